@@ -1,0 +1,177 @@
+"""ctypes binding of the fp64 CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the CPU-baseline leg of
+the benchmark import this package; the product package never does.  It shares no
+code with the HIP path: the only things both sides consume are the seeded inputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "oracle.c")
+
+BF16, F32, F64 = 0, 1, 2
+SAMPLE, GREEDY = 0, 1
+
+BAD_TOKEN = 1
+Q_ZERO = 2
+NONFINITE = 4
+BAD_GAMMA = 8
+ZERO_RESID = 16
+BAD_TEMP = 32
+INVALID_MASK = BAD_TOKEN | NONFINITE | BAD_GAMMA | BAD_TEMP
+
+_DTYPES = {"bf16": BF16, "f32": F32, "f64": F64}
+
+
+def build(verbose: bool = False) -> str:
+    """Compile oracle.c into liboracle.so (gcc, fp64, OpenMP over rows)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fopenmp", "-fPIC", "-shared",
+           SRC_PATH, "-o", LIB_PATH, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True, cwd=_HERE)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def _load(path: str):
+    L = ctypes.CDLL(path)
+    vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
+    L.oracle_softmax.argtypes = [vp, ctypes.c_int, i64, dbl, vp]
+    L.oracle_softmax.restype = ctypes.c_int
+    L.oracle_argmax.argtypes = [vp, ctypes.c_int, i64]
+    L.oracle_argmax.restype = i64
+    L.oracle_position.argtypes = [vp, vp, ctypes.c_int, i64, dbl, vp, vp, vp, vp, vp]
+    L.oracle_position.restype = ctypes.c_int
+    L.oracle_inverse_cdf.argtypes = [vp, i64, dbl, vp, vp]
+    L.oracle_inverse_cdf.restype = i64
+    L.oracle_verify.argtypes = [vp, vp, ctypes.c_int, i64, i32, i64, vp, vp, vp, vp,
+                                ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int]
+    L.oracle_verify.restype = ctypes.c_int
+    return L
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC_PATH):
+            build()
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+class using:
+    """Context manager that points this binding at another build of oracle.c (used
+    to check that planted mistakes in a copy of the oracle fail its pins)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = _lib
+        _lib = _load(self.path)
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _logits(z, dtype):
+    if dtype == "bf16":
+        return np.ascontiguousarray(z, np.uint16)
+    if dtype == "f32":
+        return np.ascontiguousarray(z, np.float32)
+    return np.ascontiguousarray(z, np.float64)
+
+
+def softmax(z, T: float, dtype: str = "f64") -> np.ndarray:
+    z = _logits(z, dtype)
+    p = np.empty(z.shape[-1], np.float64)
+    rc = lib().oracle_softmax(_ptr(z), _DTYPES[dtype], z.shape[-1], float(T), _ptr(p))
+    if rc != 0:
+        raise ValueError(f"oracle_softmax status {rc}")
+    return p
+
+
+def argmax(z, dtype: str = "f64") -> int:
+    z = _logits(z, dtype)
+    return int(lib().oracle_argmax(_ptr(z), _DTYPES[dtype], z.shape[-1]))
+
+
+def position(zt, zd, T: float, dtype: str = "f64") -> dict:
+    """p, q, alpha = sum min(p,q), residual mass and residual r at one position."""
+    zt = _logits(zt, dtype)
+    zd = _logits(zd, dtype)
+    V = zt.shape[-1]
+    p, q, r = (np.empty(V, np.float64) for _ in range(3))
+    a = np.zeros(1, np.float64)
+    w = np.zeros(1, np.float64)
+    rc = lib().oracle_position(_ptr(zt), _ptr(zd), _DTYPES[dtype], V, float(T), _ptr(p), _ptr(q),
+                               _ptr(a), _ptr(w), _ptr(r))
+    if rc != 0:
+        raise ValueError(f"oracle_position status {rc}")
+    return dict(p=p, q=q, alpha=float(a[0]), resid_mass=float(w[0]), residual=r)
+
+
+def inverse_cdf(w, u: float):
+    """(token, W, near_edge) of the inverse-CDF draw with weights w and uniform u."""
+    w = np.ascontiguousarray(w, np.float64)
+    W = np.zeros(1, np.float64)
+    near = np.zeros(1, np.int32)
+    tok = lib().oracle_inverse_cdf(_ptr(w), w.shape[0], float(u), _ptr(W), _ptr(near))
+    return int(tok), float(W[0]), bool(near[0])
+
+
+def verify(target, draft, dtype: str, vocab: int, gamma, draft_tokens, uniforms, temperature,
+           mode: str = "sample", n_target_rows=None, threads: int = 0) -> dict:
+    """One verification round over a packed batch; returns numpy arrays."""
+    gamma = np.ascontiguousarray(gamma, np.int32)
+    B = gamma.shape[0]
+    target = _logits(target, dtype)
+    draft = None if draft is None else _logits(draft, dtype)
+    tokens = np.ascontiguousarray(draft_tokens, np.int32)
+    uniforms = np.ascontiguousarray(uniforms, np.float32)
+    temperature = np.ascontiguousarray(temperature, np.float32)
+    if n_target_rows is None:
+        n_target_rows = target.shape[0] if target.ndim == 2 else target.size // vocab
+    n_draft = tokens.shape[0]
+    out = dict(
+        n_accepted=np.empty(B, np.int32),
+        emitted=np.empty(n_target_rows, np.int32),
+        p_x=np.empty(n_draft, np.float64),
+        q_x=np.empty(n_draft, np.float64),
+        resid_mass=np.empty(B, np.float64),
+        row_status=np.empty(B, np.int32),
+        flag_pos=np.empty(B, np.int32),
+    )
+    rc = lib().oracle_verify(_ptr(target), _ptr(draft), _DTYPES[dtype], int(vocab), B,
+                             int(n_target_rows), _ptr(tokens), _ptr(uniforms), _ptr(temperature),
+                             _ptr(gamma), SAMPLE if mode == "sample" else GREEDY,
+                             _ptr(out["n_accepted"]), _ptr(out["emitted"]), _ptr(out["p_x"]),
+                             _ptr(out["q_x"]), _ptr(out["resid_mass"]), _ptr(out["row_status"]),
+                             _ptr(out["flag_pos"]), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_verify status {rc}")
+    return out
+
+
+def verify_workload(w, threads: int = 0, mode: str | None = None) -> dict:
+    """verify() on any object with the packed-workload attributes."""
+    return verify(w.target, w.draft, w.dtype, w.vocab, w.gamma, w.draft_tokens, w.uniforms,
+                  w.temperature, mode=mode or w.mode, threads=threads)

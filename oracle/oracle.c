@@ -1,0 +1,450 @@
+/*
+ * fp64 CPU oracle of the speculative-sampling verification step.
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark load this file's library.  The product library never links, loads
+ * or calls it, and it shares no code, header or table with the HIP path.
+ *
+ * It computes, plainly and in float64, what one verification round computes:
+ *
+ *  - temperature softmax of every position's logits, y_i = exp(z_i/t) / sum_j exp(z_j/t)
+ *    (brunomaga.github.io "inference-distillation-speculative-decoding", section
+ *    "Knowledge distillation", the softened-output equation), with the same t for the
+ *    target distribution p and the drafter distribution q (rayaq.ca "Speculative
+ *    decoding", section "Why the output is exactly the target's", last paragraph);
+ *    evaluated with the maximum logit subtracted first, which leaves y unchanged;
+ *  - the left-to-right accept test: draft x_j is kept iff u_j < min(1, p_j(x_j)/q_j(x_j)),
+ *    stopping at the first rejection (rayaq.ca "Speculative decoding", section
+ *    "One round", step 3);
+ *  - on a rejection at position K, one draw from the residual
+ *    r = max(0, p_K - q_K) / sum max(0, p_K - q_K) (same section, step 4);
+ *  - if all drafts are kept, one bonus draw from p at the position after the last
+ *    draft (same section, step 5);
+ *  - the greedy variant: keep drafts while they equal the target's argmax, then emit
+ *    the target's argmax at the first mismatch or after the last draft (rayaq.ca
+ *    "Speculative decoding", section "The greedy case"; brunomaga.github.io, section
+ *    "Draft-model speculative decoding", greedy paragraph).
+ *
+ * Readings where the pages leave a step open (each also listed in the design notes):
+ *  - p is the target, q the drafter (the rayaq.ca and cgnarendiran.github.io naming;
+ *    brunomaga.github.io swaps the letters, not the rule);
+ *  - the test is strict, u < ratio, with u in [0, 1);
+ *  - uniforms are inputs: slot j < gamma drives accept test j, slot gamma drives the
+ *    single categorical draw (residual or bonus);
+ *  - a categorical draw is the inverse CDF in token order: with weights w,
+ *    W = sum(w), t = u * W, the token is the smallest v whose running sum exceeds t;
+ *  - q(x) = 0 gives ratio 1 if p(x) > 0, else 0 (flagged Q_ZERO);
+ *  - residual mass W = 0 at a rejection (possible only through rounding) falls back to
+ *    drawing from p_K (flagged ZERO_RESID);
+ *  - temperature t <= 0 in sampling mode makes that row greedy (the t -> 0 limit);
+ *  - greedy argmax is taken on the raw logits, lowest index on ties;
+ *  - a NaN or +inf logit, or a position whose logits are all -inf, makes the row
+ *    invalid (NONFINITE); -inf elsewhere is an ordinary zero-probability token;
+ *  - a decision whose threshold is within 1e-5 of its input (|u - ratio| < 1e-5 for a
+ *    test, |C - t| < 1e-5 * W at an interior edge of the drawn token's CDF interval
+ *    for a draw) is reported in flag_pos so comparisons can exclude it.
+ */
+#include <float.h>
+#include <math.h>
+#include <omp.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "oracle.h"
+
+/* ------------------------------------------------------------------------- */
+/* element access: exact upcast of bf16 / fp32 / fp64 logits to double       */
+/* ------------------------------------------------------------------------- */
+static double logit_at(const void *base, int dtype, int64_t idx)
+{
+    if (dtype == ORACLE_BF16) {
+        uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)base)[idx];
+    return ((const double *)base)[idx];
+}
+
+static const void *vector_ptr(const void *base, int dtype, int64_t row, int64_t V)
+{
+    size_t esz = dtype == ORACLE_BF16 ? 2 : dtype == ORACLE_F32 ? 4 : 8;
+    return (const char *)base + (size_t)row * (size_t)V * esz;
+}
+
+/* ------------------------------------------------------------------------- */
+/* temperature softmax of one position                                        */
+/* ------------------------------------------------------------------------- */
+
+/* NaN or +inf anywhere, or every element -inf: the position has no softmax. */
+static int vector_nonfinite(const void *z, int dtype, int64_t V)
+{
+    int any_above_neg_inf = 0;
+    for (int64_t v = 0; v < V; ++v) {
+        double x = logit_at(z, dtype, v);
+        if (isnan(x) || x == INFINITY)
+            return 1;
+        if (x != -INFINITY)
+            any_above_neg_inf = 1;
+    }
+    return !any_above_neg_inf;
+}
+
+/* m = max z, S = sum_v exp((z_v - m)/T), summed in index order. */
+static void vector_max_sumexp(const void *z, int dtype, int64_t V, double T, double *m_out,
+                              double *S_out)
+{
+    double m = -INFINITY;
+    for (int64_t v = 0; v < V; ++v) {
+        double x = logit_at(z, dtype, v);
+        if (x > m)
+            m = x;
+    }
+    double S = 0.0;
+    for (int64_t v = 0; v < V; ++v)
+        S += exp((logit_at(z, dtype, v) - m) / T);
+    *m_out = m;
+    *S_out = S;
+}
+
+int oracle_softmax(const void *z, int dtype, int64_t V, double T, double *p)
+{
+    if (!z || !p || V <= 0 || !(T > 0) || !isfinite(T))
+        return -1;
+    if (vector_nonfinite(z, dtype, V))
+        return ORACLE_NONFINITE;
+    double m, S;
+    vector_max_sumexp(z, dtype, V, T, &m, &S);
+    for (int64_t v = 0; v < V; ++v)
+        p[v] = exp((logit_at(z, dtype, v) - m) / T) / S;
+    return 0;
+}
+
+/* first index of the maximum of the raw logits */
+int64_t oracle_argmax(const void *z, int dtype, int64_t V)
+{
+    int64_t best = 0;
+    double bv = logit_at(z, dtype, 0);
+    for (int64_t v = 1; v < V; ++v) {
+        double x = logit_at(z, dtype, v);
+        if (x > bv) {
+            bv = x;
+            best = v;
+        }
+    }
+    return best;
+}
+
+/* ------------------------------------------------------------------------- */
+/* one position: alpha, residual mass and residual distribution               */
+/* ------------------------------------------------------------------------- */
+int oracle_position(const void *zt, const void *zd, int dtype, int64_t V, double T, double *p,
+                    double *q, double *alpha, double *resid_mass, double *residual)
+{
+    double *pp = p ? p : malloc(sizeof(double) * (size_t)V);
+    double *qq = q ? q : malloc(sizeof(double) * (size_t)V);
+    int rc = 0;
+    if (!pp || !qq) {
+        rc = -1;
+        goto out;
+    }
+    rc = oracle_softmax(zt, dtype, V, T, pp);
+    if (rc == 0)
+        rc = oracle_softmax(zd, dtype, V, T, qq);
+    if (rc != 0)
+        goto out;
+    double a = 0.0, w = 0.0;
+    for (int64_t v = 0; v < V; ++v) {
+        a += fmin(pp[v], qq[v]);
+        w += fmax(0.0, pp[v] - qq[v]);
+    }
+    if (alpha)
+        *alpha = a;
+    if (resid_mass)
+        *resid_mass = w;
+    if (residual)
+        for (int64_t v = 0; v < V; ++v)
+            residual[v] = w > 0 ? fmax(0.0, pp[v] - qq[v]) / w : 0.0;
+out:
+    if (!p)
+        free(pp);
+    if (!q)
+        free(qq);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------- */
+/* the inverse-CDF draw                                                        */
+/* ------------------------------------------------------------------------- */
+int64_t oracle_inverse_cdf(const double *w, int64_t V, double u, double *W_out, int *near_edge)
+{
+    double W = 0.0;
+    for (int64_t v = 0; v < V; ++v)
+        W += w[v];
+    double t = u * W;
+    double C = 0.0, C_prev = 0.0;
+    int64_t token = -1;
+    for (int64_t v = 0; v < V; ++v) {
+        C_prev = C;
+        C += w[v];
+        if (C > t) {
+            token = v;
+            break;
+        }
+    }
+    if (token < 0) { /* only through rounding: the last token with positive weight */
+        for (int64_t v = V - 1; v >= 0; --v)
+            if (w[v] > 0) {
+                token = v;
+                break;
+            }
+        C = W;
+        C_prev = W - (token >= 0 ? w[token] : 0.0);
+    }
+    /* only interior edges are decision boundaries: the lower edge when some earlier
+       token has weight, the upper edge when some later token has weight */
+    if (near_edge)
+        *near_edge = (C_prev > 0 && fabs(C_prev - t) < 1e-5 * W) ||
+                     (C < W && fabs(C - t) < 1e-5 * W);
+    if (W_out)
+        *W_out = W;
+    return token;
+}
+
+/* ------------------------------------------------------------------------- */
+/* the verification round, one batch                                           */
+/* ------------------------------------------------------------------------- */
+static void invalidate_row(int32_t *n_accepted, int32_t *emitted, double *p_x, double *q_x,
+                           double *resid, int64_t i, int64_t t0, int64_t d0, int g)
+{
+    n_accepted[i] = -1;
+    for (int j = 0; j <= g; ++j)
+        emitted[t0 + j] = -1;
+    if (p_x)
+        for (int j = 0; j < g; ++j)
+            p_x[d0 + j] = NAN;
+    if (q_x)
+        for (int j = 0; j < g; ++j)
+            q_x[d0 + j] = NAN;
+    if (resid)
+        resid[i] = NAN;
+}
+
+int oracle_verify(const void *target, const void *draft, int dtype, int64_t V, int32_t B,
+                  int64_t n_target_rows, const int32_t *draft_tokens, const float *uniforms,
+                  const float *temperature, const int32_t *gamma_per_row, int mode,
+                  int32_t *n_accepted, int32_t *emitted, double *p_x, double *q_x,
+                  double *resid_mass, int32_t *row_status, int32_t *flag_pos, int nthreads)
+{
+    if (!target || !gamma_per_row || !uniforms || !temperature || !n_accepted || !emitted ||
+        V <= 0 || B < 0 || n_target_rows < 0)
+        return -1;
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_F32 && dtype != ORACLE_F64)
+        return -1;
+
+    /* offsets: exclusive prefix sums of gamma+1 (target rows) and gamma (draft rows) */
+    int64_t *t_off = malloc(sizeof(int64_t) * ((size_t)B + 1));
+    int64_t *d_off = malloc(sizeof(int64_t) * ((size_t)B + 1));
+    if (!t_off || !d_off) {
+        free(t_off);
+        free(d_off);
+        return -1;
+    }
+    int bad_gamma = 0;
+    t_off[0] = d_off[0] = 0;
+    for (int32_t i = 0; i < B; ++i) {
+        int g = gamma_per_row[i];
+        if (g < 0) {
+            bad_gamma = 1;
+            g = 0;
+        }
+        t_off[i + 1] = t_off[i] + g + 1;
+        d_off[i + 1] = d_off[i] + g;
+    }
+    if (t_off[B] != n_target_rows)
+        bad_gamma = 1;
+    if (bad_gamma) {
+        for (int32_t i = 0; i < B; ++i) {
+            n_accepted[i] = -1;
+            if (row_status)
+                row_status[i] = ORACLE_BAD_GAMMA;
+            if (flag_pos)
+                flag_pos[i] = -1;
+            if (resid_mass)
+                resid_mass[i] = NAN;
+        }
+        for (int64_t k = 0; k < n_target_rows; ++k)
+            emitted[k] = -1;
+        free(t_off);
+        free(d_off);
+        return 0;
+    }
+    if (t_off[B] > B && (!draft || !draft_tokens)) {
+        free(t_off);
+        free(d_off);
+        return -1;
+    }
+
+    int rc = 0;
+    const int nth = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel num_threads(nth)
+    {
+        double *P = malloc(sizeof(double) * (size_t)V);
+        double *Q = malloc(sizeof(double) * (size_t)V);
+        double *w = malloc(sizeof(double) * (size_t)V);
+        if (!P || !Q || !w) {
+#pragma omp atomic write
+            rc = -1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int32_t i = 0; i < B; ++i) {
+            if (!P || !Q || !w)
+                continue;
+            const int g = gamma_per_row[i];
+            const int64_t t0 = t_off[i], d0 = d_off[i];
+            const double T = (double)temperature[i];
+            int status = 0, flag = -1;
+            int greedy = mode == ORACLE_GREEDY;
+            if (!greedy) {
+                if (!isfinite(T))
+                    status |= ORACLE_BAD_TEMP;
+                else if (T <= 0)
+                    greedy = 1;
+                else if (T < (double)FLT_MIN)
+                    status |= ORACLE_BAD_TEMP;
+            }
+            for (int j = 0; j < g; ++j) {
+                int32_t x = draft_tokens[d0 + j];
+                if (x < 0 || (int64_t)x >= V)
+                    status |= ORACLE_BAD_TOKEN;
+            }
+            /* validity of every position the row reads */
+            for (int j = 0; j <= g && !(status & ORACLE_NONFINITE); ++j)
+                if (vector_nonfinite(vector_ptr(target, dtype, t0 + j, V), dtype, V))
+                    status |= ORACLE_NONFINITE;
+            if (!greedy)
+                for (int j = 0; j < g && !(status & ORACLE_NONFINITE); ++j)
+                    if (vector_nonfinite(vector_ptr(draft, dtype, d0 + j, V), dtype, V))
+                        status |= ORACLE_NONFINITE;
+            if (status & ORACLE_INVALID_MASK) {
+                invalidate_row(n_accepted, emitted, p_x, q_x, resid_mass, i, t0, d0, g);
+                if (row_status)
+                    row_status[i] = status;
+                if (flag_pos)
+                    flag_pos[i] = -1;
+                continue;
+            }
+
+            if (greedy) {
+                /* keep drafts while they equal the target's argmax */
+                int K = g;
+                for (int j = 0; j < g; ++j) {
+                    int64_t a = oracle_argmax(vector_ptr(target, dtype, t0 + j, V), dtype, V);
+                    if ((int64_t)draft_tokens[d0 + j] != a) {
+                        K = j;
+                        break;
+                    }
+                }
+                int64_t aK = oracle_argmax(vector_ptr(target, dtype, t0 + K, V), dtype, V);
+                for (int j = 0; j < K; ++j)
+                    emitted[t0 + j] = draft_tokens[d0 + j];
+                emitted[t0 + K] = (int32_t)aK;
+                for (int j = K + 1; j <= g; ++j)
+                    emitted[t0 + j] = -1;
+                n_accepted[i] = K;
+                if (p_x)
+                    for (int j = 0; j < g; ++j)
+                        p_x[d0 + j] = NAN;
+                if (q_x)
+                    for (int j = 0; j < g; ++j)
+                        q_x[d0 + j] = NAN;
+                if (resid_mass)
+                    resid_mass[i] = NAN;
+                if (row_status)
+                    row_status[i] = status;
+                if (flag_pos)
+                    flag_pos[i] = -1;
+                continue;
+            }
+
+            /* p(x_j) and q(x_j) at every draft position */
+            int K = g;
+            int decided = 0;
+            for (int j = 0; j < g; ++j) {
+                const void *zt = vector_ptr(target, dtype, t0 + j, V);
+                const void *zd = vector_ptr(draft, dtype, d0 + j, V);
+                const int64_t x = draft_tokens[d0 + j];
+                double mt, St, md, Sd;
+                vector_max_sumexp(zt, dtype, V, T, &mt, &St);
+                vector_max_sumexp(zd, dtype, V, T, &md, &Sd);
+                double px = exp((logit_at(zt, dtype, x) - mt) / T) / St;
+                double qx = exp((logit_at(zd, dtype, x) - md) / T) / Sd;
+                if (p_x)
+                    p_x[d0 + j] = px;
+                if (q_x)
+                    q_x[d0 + j] = qx;
+                double ratio;
+                if (qx > 0) {
+                    ratio = px / qx;
+                    if (ratio > 1.0)
+                        ratio = 1.0;
+                } else {
+                    ratio = px > 0 ? 1.0 : 0.0;
+                    status |= ORACLE_Q_ZERO;
+                }
+                if (!decided) {
+                    double u = (double)uniforms[t0 + j];
+                    if (flag < 0 && fabs(u - ratio) < 1e-5)
+                        flag = j;
+                    if (!(u < ratio)) {
+                        K = j;
+                        decided = 1;
+                    }
+                }
+            }
+
+            /* residual at a rejection, or p at the bonus position */
+            oracle_softmax(vector_ptr(target, dtype, t0 + K, V), dtype, V, T, P);
+            if (K < g) {
+                oracle_softmax(vector_ptr(draft, dtype, d0 + K, V), dtype, V, T, Q);
+                double W = 0.0;
+                for (int64_t v = 0; v < V; ++v) {
+                    w[v] = fmax(0.0, P[v] - Q[v]);
+                    W += w[v];
+                }
+                if (W == 0.0) {
+                    memcpy(w, P, sizeof(double) * (size_t)V);
+                    status |= ORACLE_ZERO_RESID;
+                }
+            } else {
+                memcpy(w, P, sizeof(double) * (size_t)V);
+            }
+            double W;
+            int near = 0;
+            int64_t tok = oracle_inverse_cdf(w, V, (double)uniforms[t0 + g], &W, &near);
+            if (flag < 0 && near)
+                flag = g;
+            for (int j = 0; j < K; ++j)
+                emitted[t0 + j] = draft_tokens[d0 + j];
+            emitted[t0 + K] = (int32_t)tok;
+            for (int j = K + 1; j <= g; ++j)
+                emitted[t0 + j] = -1;
+            n_accepted[i] = K;
+            if (resid_mass)
+                resid_mass[i] = W;
+            if (row_status)
+                row_status[i] = status;
+            if (flag_pos)
+                flag_pos[i] = flag;
+        }
+        free(P);
+        free(Q);
+        free(w);
+    }
+    free(t_off);
+    free(d_off);
+    return rc;
+}

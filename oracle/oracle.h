@@ -1,0 +1,32 @@
+/*
+ * fp64 CPU oracle of the speculative-sampling verification step: declarations.
+ * TEST INFRASTRUCTURE ONLY (tests, smoke check, CPU baseline); see oracle.c.
+ * This header is the oracle's own and is not shared with the HIP path.
+ */
+#ifndef SPEC_VERIFY_ORACLE_H
+#define SPEC_VERIFY_ORACLE_H
+#include <stdint.h>
+
+enum { ORACLE_BF16 = 0, ORACLE_F32 = 1, ORACLE_F64 = 2 };
+enum { ORACLE_SAMPLE = 0, ORACLE_GREEDY = 1 };
+
+/* per-row status bits */
+#define ORACLE_BAD_TOKEN 1   /* a draft token outside [0, V)                        */
+#define ORACLE_Q_ZERO 2      /* q(x) == 0 at some draft position (informational)   */
+#define ORACLE_NONFINITE 4   /* NaN / +inf logit, or a position with all -inf       */
+#define ORACLE_BAD_GAMMA 8   /* gamma < 0, or sum(gamma+1) != n_target_rows        */
+#define ORACLE_ZERO_RESID 16 /* zero residual mass at a rejection (informational)  */
+#define ORACLE_BAD_TEMP 32   /* sampling row with non-finite or subnormal T         */
+#define ORACLE_INVALID_MASK (ORACLE_BAD_TOKEN | ORACLE_NONFINITE | ORACLE_BAD_GAMMA | ORACLE_BAD_TEMP)
+
+int oracle_softmax(const void *z, int dtype, int64_t V, double T, double *p);
+int64_t oracle_argmax(const void *z, int dtype, int64_t V);
+int oracle_position(const void *zt, const void *zd, int dtype, int64_t V, double T, double *p,
+                    double *q, double *alpha, double *resid_mass, double *residual);
+int64_t oracle_inverse_cdf(const double *w, int64_t V, double u, double *W_out, int *near_edge);
+int oracle_verify(const void *target, const void *draft, int dtype, int64_t V, int32_t B,
+                  int64_t n_target_rows, const int32_t *draft_tokens, const float *uniforms,
+                  const float *temperature, const int32_t *gamma_per_row, int mode,
+                  int32_t *n_accepted, int32_t *emitted, double *p_x, double *q_x,
+                  double *resid_mass, int32_t *row_status, int32_t *flag_pos, int nthreads);
+#endif

@@ -1,0 +1,671 @@
+"""Pins of the fp64 CPU oracle to things other than itself.
+
+Every function here checks the oracle against something the pages or the
+mathematics fix: values the pages print for their worked examples (under
+tests/golden, each with its citation), closed forms, identities of the method,
+special cases that reduce to a library routine (scipy's softmax, numpy's
+argmax / searchsorted), brute force on tiny inputs, and Monte Carlo against exact
+page fractions.  Each raises AssertionError on a mismatch.
+
+The same functions are run against planted mistakes in the oracle (see
+test_oracle_mutants.py), which must each fail at least one of them.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+import scipy.special
+import scipy.stats
+
+import oracle
+from pagevals import LOGP, LOGQ, MARKOV, P, P_MAT, Q, Q_MAT, ROUNDS, TOK, load
+
+U24 = 2.0 ** -24
+F32_BELOW_ONE = float(np.float32(1.0 - U24))
+
+
+def _close(a, b, tol, what):
+    assert abs(float(a) - float(b)) <= tol, f"{what}: {a!r} vs {b!r} (tol {tol})"
+
+
+def _chi2_ok(observed, probs, what, pmin=1e-3):
+    observed = np.asarray(observed, np.float64)
+    probs = np.asarray(probs, np.float64)
+    n = observed.sum()
+    exp = probs * n
+    keep = exp >= 5
+    obs_k, exp_k = list(observed[keep]), list(exp[keep])
+    if (~keep).any():  # merge thin bins
+        obs_k.append(observed[~keep].sum())
+        exp_k.append(exp[~keep].sum())
+    obs_k, exp_k = np.array(obs_k), np.array(exp_k)
+    if len(obs_k) < 2:
+        return
+    assert np.all(obs_k[exp_k == 0] == 0), f"{what}: mass where none is expected"
+    m = exp_k > 0
+    pval = scipy.stats.chisquare(obs_k[m], exp_k[m] * obs_k[m].sum() / exp_k[m].sum()).pvalue
+    assert pval > pmin, f"{what}: chi-square p = {pval:.2e}, observed {observed}, expected {exp}"
+
+
+def snapped(rng, shape):
+    return (rng.integers(0, 1 << 24, size=shape).astype(np.float64) * U24).astype(np.float32)
+
+
+# --------------------------------------------------------------------------- #
+# Markov three-token example: drafter simulation and packed rounds
+# --------------------------------------------------------------------------- #
+def markov_drafts(rng, ctx, gamma):
+    """Draft tokens from the Markov drafter q, one round per entry of ctx."""
+    cq = np.cumsum(Q_MAT, axis=1)
+    out = np.empty((len(ctx), gamma), np.int32)
+    prev = np.asarray(ctx)
+    for j in range(gamma):
+        u = rng.random(len(ctx))
+        x = np.minimum((u[:, None] >= cq[prev]).sum(axis=1), 2)
+        out[:, j] = x
+        prev = x
+    return out
+
+
+def markov_verify(ctx, drafts, uniforms):
+    """Run the oracle on rounds from contexts ctx with the given drafts and uniforms."""
+    N, g = drafts.shape
+    seq = np.concatenate([np.asarray(ctx)[:, None], drafts], axis=1)  # context of each position
+    target = LOGP[seq].reshape(-1, 3)
+    draft = LOGQ[seq[:, :g]].reshape(-1, 3)
+    return oracle.verify(target, draft, "f64", 3, np.full(N, g, np.int32), drafts.reshape(-1),
+                         np.asarray(uniforms, np.float32).reshape(-1), np.ones(N, np.float32))
+
+
+def markov_round(rng, ctx, gamma):
+    drafts = markov_drafts(rng, ctx, gamma)
+    u = snapped(rng, (len(ctx), gamma + 1))
+    r = markov_verify(ctx, drafts, u)
+    em = r["emitted"].reshape(len(ctx), gamma + 1)
+    return r["n_accepted"], em
+
+
+def markov_emit(rng, start, n_tokens, N, gamma=3):
+    """Chain rounds from `start` until n_tokens are out; returns [N, n_tokens]."""
+    seq = np.full((N, n_tokens), -1, np.int64)
+    cnt = np.zeros(N, np.int64)
+    ctx = np.full(N, start, np.int64)
+    while True:
+        idx = np.nonzero(cnt < n_tokens)[0]
+        if len(idx) == 0:
+            return seq
+        K, em = markov_round(rng, ctx[idx], gamma)
+        for k in range(gamma + 1):
+            take = (k <= K) & (cnt[idx] < n_tokens)
+            rows = idx[take]
+            seq[rows, cnt[rows]] = em[take, k]
+            cnt[rows] += 1
+        ctx[idx] = em[np.arange(len(idx)), K]
+
+
+# --------------------------------------------------------------------------- #
+# softmax and argmax
+# --------------------------------------------------------------------------- #
+def pin_softmax_constant():
+    """Constant logits give 1/V exactly (up to rounding)."""
+    for V in (1, 7, 32000):
+        p = oracle.softmax(np.full(V, 3.25), 0.7)
+        assert np.all(p == 1.0 / V), "constant logits"
+
+
+def pin_softmax_two_level():
+    """n1 logits at a, n2 at b: p(a) = 1 / (n1 + n2 exp((b-a)/T))."""
+    for (n1, n2, a, b, T) in [(1, 3, 2.0, -1.0, 1.0), (5, 11, 0.5, 1.75, 0.8), (2, 1000, 9.0, 0.0, 1.3)]:
+        z = np.array([a] * n1 + [b] * n2)
+        p = oracle.softmax(z, T)
+        pa = 1.0 / (n1 + n2 * math.exp((b - a) / T))
+        pb = 1.0 / (n2 + n1 * math.exp((a - b) / T))
+        tol = 4e-16 * (n1 + n2)  # sequential fp64 sum of n1 + n2 terms
+        _close(p[0] / pa, 1.0, tol, "two-level p(a)")
+        _close(p[-1] / pb, 1.0, tol, "two-level p(b)")
+
+
+def pin_softmax_vs_scipy():
+    """Temperature softmax equals scipy.special.softmax(z / T) for all input dtypes."""
+    rng = np.random.default_rng(11)
+    import workloads
+    for dtype in ("f64", "f32", "bf16"):
+        for T in (0.5, 0.8, 1.0, 1.5):
+            z = rng.standard_normal(4099) * 3.0
+            if dtype == "bf16":
+                zin = workloads.to_bf16_bits(z.astype(np.float32))
+                zf = workloads.bf16_bits_to_f32(zin).astype(np.float64)
+            elif dtype == "f32":
+                zin = z.astype(np.float32)
+                zf = zin.astype(np.float64)
+            else:
+                zin, zf = z, z
+            p = oracle.softmax(zin, T, dtype)
+            ref = scipy.special.softmax(zf / T)
+            assert np.max(np.abs(p - ref) / ref) < 1e-12, f"softmax vs scipy ({dtype}, T={T})"
+
+
+def pin_softmax_one_hot_and_masked():
+    """A dominant logit gives ~1; -inf logits get probability 0; all -inf is rejected."""
+    z = np.zeros(100)
+    z[17] = 1000.0
+    p = oracle.softmax(z, 1.0)
+    _close(p[17], 1.0, 1e-300, "dominant logit")
+    z = np.array([0.0, -np.inf, 0.0, -np.inf])
+    p = oracle.softmax(z, 1.0)
+    assert p[1] == 0.0 and p[3] == 0.0 and abs(p[0] - 0.5) < 1e-16, "masked logits"
+    for bad in ([-np.inf] * 3, [0.0, np.nan], [np.inf, 0.0]):
+        try:
+            oracle.softmax(np.array(bad), 1.0)
+        except ValueError:
+            continue
+        raise AssertionError(f"softmax accepted {bad}")
+
+
+def pin_argmax_first_index():
+    """Greedy argmax is numpy's argmax (first index of the maximum) on raw logits."""
+    rng = np.random.default_rng(5)
+    import workloads
+    for _ in range(50):
+        z = rng.integers(-3, 4, size=257).astype(np.float32)  # many ties
+        assert oracle.argmax(z, "f32") == int(np.argmax(z)), "argmax ties (f32)"
+        zb = workloads.to_bf16_bits(z)
+        assert oracle.argmax(zb, "bf16") == int(np.argmax(z)), "argmax ties (bf16)"
+
+
+# --------------------------------------------------------------------------- #
+# the three-token Markov example (rayaq.ca "Speculative decoding", "Worked example")
+# --------------------------------------------------------------------------- #
+def pin_markov_alpha_and_residual():
+    """alpha and the residual for previous tokens a, b, c match the page's table."""
+    for c in "abc":
+        r = oracle.position(LOGP[TOK[c]], LOGQ[TOK[c]], 1.0)
+        for v in range(3):
+            _close(r["p"][v], float(P[c][v]), 1e-15, f"p(.|{c})")
+            _close(r["q"][v], float(Q[c][v]), 1e-15, f"q(.|{c})")
+            _close(r["residual"][v], float(Fraction(MARKOV["residual"][c][v])), 1e-12,
+                   f"residual(.|{c})")
+        _close(r["alpha"], float(Fraction(MARKOV["alpha"][c])), 1e-15, f"alpha({c})")
+        _close(r["resid_mass"], 1.0 - float(Fraction(MARKOV["alpha"][c])), 1e-15, f"W({c})")
+
+
+def pin_markov_reject_round():
+    """Drafts c, c, a after 'a' with u = 0.085, 0.835: keep c (ratio 1), reject c
+    (ratio 5/7), residual gives a; the round emits 'c a' and accepts one draft."""
+    spec = ROUNDS["reject_round"]
+    drafts = np.array([[TOK[t] for t in spec["drafts"]]], np.int32)
+    for u_draw in (0.0, 0.3, 0.7, F32_BELOW_ONE):
+        for u3 in (0.0, 0.5, F32_BELOW_ONE):  # the third draft is never checked
+            u = np.array([[spec["positions"][0]["u"], spec["positions"][1]["u"], u3, u_draw]])
+            r = markov_verify([TOK["a"]], drafts, u)
+            assert r["n_accepted"][0] == spec["n_accepted"], r
+            em = [t for t in r["emitted"] if t >= 0]
+            assert em == [TOK[t] for t in spec["emitted"]], em
+            assert r["flag_pos"][0] == -1
+            _close(r["p_x"][0], float(Fraction(spec["positions"][0]["p"])), 1e-15, "p(c|a)")
+            _close(r["q_x"][0], float(Fraction(spec["positions"][0]["q"])), 1e-15, "q(c|a)")
+            _close(r["p_x"][1], float(Fraction(spec["positions"][1]["p"])), 1e-15, "p(c|c)")
+            _close(r["q_x"][1], float(Fraction(spec["positions"][1]["q"])), 1e-15, "q(c|c)")
+            _close(r["p_x"][1] / r["q_x"][1], 5 / 7, 1e-15, "ratio 5/7")
+            _close(r["resid_mass"][0], 1 - 4 / 5, 1e-15, "W after c")
+
+
+def pin_markov_all_accept_round():
+    """Drafts b, c, c after 'a' (ratios 3/4, 1, 5/7) all kept; the bonus from
+    p(.|c) = (3/10, 1/5, 1/2) gives c for u in [1/2, 1): 'b c c c'."""
+    spec = ROUNDS["all_accept_round"]
+    drafts = np.array([[TOK[t] for t in spec["drafts"]]], np.int32)
+    ratios = [Fraction(3, 10) / Fraction(2, 5), Fraction(1), Fraction(1, 2) / Fraction(7, 10)]
+    below = [float(np.nextafter(np.float32(float(x)), np.float32(0))) for x in ratios]
+    u = np.array([[below[0], F32_BELOW_ONE, below[2], 0.75]])
+    r = markov_verify([TOK["a"]], drafts, u)
+    assert r["n_accepted"][0] == 3, r
+    assert list(r["emitted"]) == [TOK[t] for t in spec["emitted"]], r["emitted"]
+    for j in range(3):
+        _close(r["p_x"][j] / r["q_x"][j], float(ratios[j]), 1e-15, f"ratio {j}")
+    for u_draw, tok in ((0.0, "a"), (0.2999, "a"), (0.3001, "b"), (0.4999, "b"), (0.5001, "c"),
+                        (F32_BELOW_ONE, "c")):
+        u[0, 3] = u_draw
+        r = markov_verify([TOK["a"]], drafts, u)
+        assert r["emitted"][3] == TOK[tok], (u_draw, r["emitted"])
+    # a uniform just above a ratio below 1 rejects there
+    for j in (0, 2):
+        uu = u.copy()
+        uu[0, j] = float(np.nextafter(np.float32(float(ratios[j])), np.float32(1)))
+        r = markov_verify([TOK["a"]], drafts, uu)
+        assert r["n_accepted"][0] == j, (j, r["n_accepted"])
+
+
+def pin_markov_distinct_sequences():
+    """Every draft and every accept-or-reject outcome from 'a' with gamma = 3 gives
+    94 distinct emitted sequences."""
+    seqs = set()
+    grid = (np.arange(256) + 0.5) / 256
+    for drafts in itertools.product(range(3), repeat=3):
+        for pattern in itertools.product((0.0, F32_BELOW_ONE), repeat=3):
+            n = len(grid)
+            u = np.empty((n, 4), np.float32)
+            u[:, :3] = pattern
+            u[:, 3] = grid
+            r = markov_verify(np.zeros(n, np.int64), np.tile(np.array(drafts, np.int32), (n, 1)), u)
+            em = r["emitted"].reshape(n, 4)
+            for row in em:
+                seqs.add(tuple(int(t) for t in row if t >= 0))
+    assert len(seqs) == ROUNDS["distinct_sequences_from_a_gamma3"], len(seqs)
+
+
+def pin_markov_accept_counts():
+    """P(K = 0..3) from 'a' is 1/10, 13/100, 61/500, 81/125, so E[tokens] = 1659/500
+    (not the 3.439 of the i.i.d. formula)."""
+    rng = np.random.default_rng(2024)
+    N = 400_000
+    K, _ = markov_round(rng, np.zeros(N, np.int64), 3)
+    probs = [float(Fraction(ROUNDS["accepted_count_from_a_gamma3"][str(k)])) for k in range(4)]
+    _chi2_ok(np.bincount(K, minlength=4), probs, "P(K) from a")
+    mean = (K + 1).mean()
+    se = (K + 1).std() / math.sqrt(N)
+    exact = float(Fraction(ROUNDS["expected_tokens_from_a_gamma3"]))
+    assert abs(mean - exact) < 4 * se, (mean, exact, se)
+    assert abs(mean - ROUNDS["iid_formula_alpha_9_10_gamma3"]) > 50 * se
+
+
+def pin_markov_joint_two_tokens():
+    """Chaining rounds from 'a' until two tokens are out reproduces the target's joint."""
+    rng = np.random.default_rng(7)
+    N = 300_000
+    seq = markov_emit(rng, TOK["a"], 2, N)
+    counts = np.zeros(9)
+    np.add.at(counts, seq[:, 0] * 3 + seq[:, 1], 1)
+    table = ROUNDS["joint_two_tokens_from_a"]
+    probs = [float(Fraction(table[a + b])) for a in "abc" for b in "abc"]
+    _chi2_ok(counts, probs, "two-token joint from a")
+
+
+def pin_markov_joint_three_tokens():
+    """From every start, three emitted tokens follow the target chain p exactly."""
+    rng = np.random.default_rng(8)
+    N = 150_000
+    for s in range(3):
+        seq = markov_emit(rng, s, 3, N)
+        counts = np.zeros(27)
+        np.add.at(counts, seq[:, 0] * 9 + seq[:, 1] * 3 + seq[:, 2], 1)
+        probs = [P_MAT[s, a] * P_MAT[a, b] * P_MAT[b, c]
+                 for a in range(3) for b in range(3) for c in range(3)]
+        _chi2_ok(counts, probs, f"three-token joint from {s}")
+
+
+# --------------------------------------------------------------------------- #
+# the four-token hand example (cgnarendiran.github.io, "The correction that makes it exact")
+# --------------------------------------------------------------------------- #
+def _four_token():
+    ex = load("four_token_example.json")
+    return ex, np.log(np.array(ex["target_p"])), np.log(np.array(ex["draft_q"]))
+
+
+def pin_four_token_alpha_residual():
+    ex, lp, lq = _four_token()
+    r = oracle.position(lp, lq, 1.0)
+    _close(r["alpha"], ex["alpha"], 1e-15, "alpha")
+    _close(1 - r["alpha"], ex["reject_probability"], 1e-15, "reject probability")
+    for v in range(4):
+        _close(r["residual"][v], float(Fraction(ex["residual"][v])), 1e-14, f"residual {v}")
+        _close(r["residual"][v], ex["residual_printed"][v], 5e-4, f"printed residual {v}")
+    # exactness: min(p, q) + (1 - alpha) r = p
+    emit = np.minimum(r["p"], r["q"]) + (1 - r["alpha"]) * r["residual"]
+    assert np.max(np.abs(emit - np.array(ex["target_p"]))) < 1e-15
+
+
+def pin_four_token_decision_and_emit():
+    """The proposed token is kept with probability 1/2, and what is emitted is p."""
+    ex, lp, lq = _four_token()
+    x = ex["tokens"].index(ex["proposed"])
+
+    def run(u):
+        u = np.asarray(u, np.float32).reshape(-1, 2)
+        n = u.shape[0]
+        target = np.tile(np.stack([lp, lp]), (n, 1))
+        draft = np.tile(lq[None], (n, 1))
+        return oracle.verify(target, draft, "f64", 4, np.ones(n, np.int32), np.full(n, x, np.int32),
+                             u, np.ones(n, np.float32))
+
+    r = run([0.4999, 0.0])
+    assert r["n_accepted"][0] == 1 and r["emitted"][0] == x
+    _close(r["p_x"][0] / r["q_x"][0], ex["accept_probability"], 1e-15, "keep probability")
+    r = run([0.5001, 0.0])
+    assert r["n_accepted"][0] == 0
+    # on rejection the residual CDF is (0, 2/3, 5/6, 1): a, my, your
+    for ud, tok in ((0.1, 1), (0.666, 1), (0.667, 2), (0.83, 2), (0.834, 3), (0.99, 3)):
+        r = run([0.9, ud])
+        assert r["emitted"][0] == tok, (ud, r["emitted"])
+    # Monte Carlo: the token emitted at the position is distributed as p
+    rng = np.random.default_rng(99)
+    N = 200_000
+    xq = rng.choice(4, size=N, p=np.array(ex["draft_q"]))
+    u = snapped(rng, (N, 2))
+    target = np.tile(np.stack([lp, lp]), (N, 1))
+    draft = np.tile(lq[None], (N, 1))
+    r = oracle.verify(target, draft, "f64", 4, np.ones(N, np.int32), xq.astype(np.int32), u,
+                      np.ones(N, np.float32))
+    em0 = r["emitted"].reshape(N, 2)[:, 0]
+    _chi2_ok(np.bincount(em0, minlength=4), ex["target_p"], "four-token emit distribution")
+    acc = (r["n_accepted"] == 1) & (xq == x)
+    _close(acc.sum() / (xq == x).sum(), 0.5, 4 * math.sqrt(0.25 / (xq == x).sum()), "keep rate")
+
+
+# --------------------------------------------------------------------------- #
+# quiz values (rayaq.ca "Speculative decoding", self-check questions)
+# --------------------------------------------------------------------------- #
+def pin_quiz_keep_probability():
+    qz = load("quiz.json")["keep_probability"]
+    lp = np.log([qz["p"], 1 - qz["p"]])
+    lq = np.log([qz["q"], 1 - qz["q"]])
+    target = np.stack([lp, lp])
+    for u, acc in ((0.2499, 1), (0.2501, 0)):
+        r = oracle.verify(target, lq[None], "f64", 2, [1], [0], [u, 0.5], [1.0])
+        _close(r["p_x"][0] / r["q_x"][0], qz["expected"], 1e-15, "keep probability")
+        assert r["n_accepted"][0] == acc
+
+
+def pin_quiz_expected_tokens():
+    """alpha = 0.8 at every position, gamma = 4: E[tokens] = (1 - 0.8^5)/0.2 = 3.3616."""
+    qz = load("quiz.json")["expected_tokens_iid"]
+    p = np.array([0.6, 0.4])
+    q = np.array([0.8, 0.2])  # sum min(p, q) = 0.8
+    assert abs(np.minimum(p, q).sum() - qz["alpha"]) < 1e-15
+    g = qz["gamma"]
+    rng = np.random.default_rng(31)
+    N = 400_000
+    x = rng.choice(2, size=(N, g), p=q).astype(np.int32)
+    u = snapped(rng, (N, g + 1))
+    target = np.tile(np.log(p), (N * (g + 1), 1))
+    draft = np.tile(np.log(q), (N * g, 1))
+    r = oracle.verify(target, draft, "f64", 2, np.full(N, g, np.int32), x.reshape(-1), u,
+                      np.ones(N, np.float32))
+    tokens = r["n_accepted"] + 1
+    se = tokens.std() / math.sqrt(N)
+    closed = (1 - qz["alpha"] ** (g + 1)) / (1 - qz["alpha"])
+    assert abs(closed - qz["expected"]) < 5e-3
+    assert abs(tokens.mean() - closed) < 4 * se, (tokens.mean(), closed, se)
+
+
+# --------------------------------------------------------------------------- #
+# identities of the method on random inputs
+# --------------------------------------------------------------------------- #
+def pin_identities_random():
+    """min(p,q) + max(0,p-q) = p; sum max(0,p-q) = 1 - alpha; alpha = 1 - TV(p, q);
+    min(p,q) + (1-alpha) r = p."""
+    import workloads
+    rng = np.random.default_rng(3)
+    for dtype in ("f32", "bf16"):
+        for T in (0.6, 1.0, 1.4):
+            zt = rng.standard_normal(2000).astype(np.float32) * 3
+            zd = (zt + rng.standard_normal(2000) * 1.0).astype(np.float32)
+            if dtype == "bf16":
+                zt, zd = workloads.to_bf16_bits(zt), workloads.to_bf16_bits(zd)
+            r = oracle.position(zt, zd, T, dtype)
+            p, q, a = r["p"], r["q"], r["alpha"]
+            lhs = np.minimum(p, q) + np.maximum(0.0, p - q)
+            assert np.all(np.abs(lhs - p) <= np.spacing(p)), "min + max(0, p-q) = p"
+            _close(r["resid_mass"], 1 - a, 1e-12, "W = 1 - alpha")
+            _close(a, 1 - 0.5 * np.abs(p - q).sum(), 1e-12, "alpha = 1 - TV")
+            emit = np.minimum(p, q) + (1 - a) * r["residual"]
+            assert np.max(np.abs(emit - p)) < 1e-12, "P(emit) = p"
+            assert abs(p.sum() - 1) < 1e-12 and abs(q.sum() - 1) < 1e-12
+
+
+def pin_px_qx_vs_scipy():
+    """p(x_j) and q(x_j) reported by a batched, ragged, tempered round equal
+    scipy's softmax(z / T) at the draft token."""
+    import workloads
+    w = workloads.small(seed=12, batch=9, vocab=301, dtype="f32", gamma=[0, 1, 2, 3, 4, 5, 6, 7, 3],
+                        temperature=[0.55, 0.8, 1.0, 1.3, 0.7, 2.0, 0.9, 1.1, 0.6])
+    r = oracle.verify_workload(w)
+    t_off, d_off = w.offsets()
+    for i in range(w.batch):
+        T = float(w.temperature[i])
+        for j in range(int(w.gamma[i])):
+            x = int(w.draft_tokens[d_off[i] + j])
+            pz = scipy.special.softmax(w.target[t_off[i] + j].astype(np.float64) / T)[x]
+            qz = scipy.special.softmax(w.draft[d_off[i] + j].astype(np.float64) / T)[x]
+            _close(r["p_x"][d_off[i] + j] / pz, 1.0, 1e-12, "p_x vs scipy")
+            _close(r["q_x"][d_off[i] + j] / qz, 1.0, 1e-12, "q_x vs scipy")
+
+
+def pin_rows_independent():
+    """Each row of a ragged batch gives what it gives alone (packed offsets)."""
+    import workloads
+    w = workloads.small(seed=13, batch=7, vocab=97, dtype="bf16", gamma=[3, 0, 5, 1, 0, 7, 2],
+                        temperature=[0.7, 1.0, 1.2, 0.9, 1.0, 0.5, 1.5])
+    full = oracle.verify_workload(w)
+    t_off, d_off = w.offsets()
+    for i in range(w.batch):
+        g = int(w.gamma[i])
+        r = oracle.verify(w.target[t_off[i]:t_off[i + 1]], w.draft[d_off[i]:d_off[i + 1]], "bf16",
+                          w.vocab, [g], w.draft_tokens[d_off[i]:d_off[i + 1]],
+                          w.uniforms[t_off[i]:t_off[i + 1]], w.temperature[i:i + 1])
+        assert r["n_accepted"][0] == full["n_accepted"][i]
+        assert np.array_equal(r["emitted"], full["emitted"][t_off[i]:t_off[i + 1]])
+
+
+# --------------------------------------------------------------------------- #
+# the draw
+# --------------------------------------------------------------------------- #
+def pin_inverse_cdf_vs_searchsorted():
+    """The draw is numpy's searchsorted(cumsum(w), u*W, side='right'); a uniform at
+    the middle of a token's CDF interval selects that token; u = 0 skips leading
+    zero weights."""
+    rng = np.random.default_rng(17)
+    for _ in range(200):
+        V = int(rng.integers(1, 300))
+        w = rng.random(V) * (rng.random(V) < 0.6)
+        if w.sum() == 0:
+            w[rng.integers(V)] = 1.0
+        C = np.cumsum(w)
+        for u in list(rng.random(5)) + [0.0]:
+            tok, W, _ = oracle.inverse_cdf(w, u)
+            assert tok == int(np.searchsorted(C, u * C[-1], side="right")), (u, tok)
+            assert w[tok] > 0
+        v = int(np.nonzero(w)[0][rng.integers(np.count_nonzero(w))])
+        mid = ((C[v] - w[v]) + C[v]) / 2 / C[-1]
+        assert oracle.inverse_cdf(w, mid)[0] == v
+
+
+def pin_gamma_zero_is_bonus():
+    """A row with no drafts emits one draw from p_0 with its single uniform."""
+    rng = np.random.default_rng(4)
+    z = rng.standard_normal((50, 64))
+    u = snapped(rng, 50)
+    r = oracle.verify(z, np.zeros((0, 64)), "f64", 64, np.zeros(50, np.int32),
+                      np.zeros(0, np.int32), u, np.full(50, 0.9, np.float32))
+    for i in range(50):
+        p = scipy.special.softmax(z[i] / np.float32(0.9).astype(np.float64))
+        assert r["n_accepted"][i] == 0
+        assert r["emitted"][i] == int(np.searchsorted(np.cumsum(p), float(u[i]) * p.sum(), side="right"))
+
+
+# --------------------------------------------------------------------------- #
+# special cases that reduce to something simpler
+# --------------------------------------------------------------------------- #
+def pin_q_equals_p_accepts_all():
+    rng = np.random.default_rng(6)
+    N, g, V = 500, 5, 40
+    z = rng.standard_normal((N * (g + 1), V))
+    d = z.reshape(N, g + 1, V)[:, :g].reshape(-1, V)
+    x = rng.integers(0, V, N * g).astype(np.int32)
+    r = oracle.verify(z, d, "f64", V, np.full(N, g, np.int32), x, snapped(rng, N * (g + 1)),
+                      np.ones(N, np.float32))
+    assert np.all(r["n_accepted"] == g)
+
+
+def pin_one_hot_draft():
+    """A one-hot q (a greedy drafter) keeps x with probability p(x) and otherwise
+    draws from p with x removed."""
+    rng = np.random.default_rng(8)
+    V, x = 12, 5
+    zt = rng.standard_normal(V)
+    zd = np.full(V, -np.inf)
+    zd[x] = 0.0
+    r = oracle.position(zt, zd, 1.0)
+    p = scipy.special.softmax(zt)
+    _close(r["alpha"], p[x], 1e-15, "alpha = p(x)")
+    expect = p.copy()
+    expect[x] = 0.0
+    expect /= 1 - p[x]
+    assert np.max(np.abs(r["residual"] - expect)) < 1e-14
+
+
+def pin_greedy_brute_force():
+    """Greedy mode keeps drafts while they equal numpy's argmax of the target logits,
+    then emits that argmax."""
+    import workloads
+    rng = np.random.default_rng(21)
+    for dtype in ("f32", "bf16"):
+        B, V = 60, 16
+        gam = rng.integers(0, 6, B).astype(np.int32)
+        nT, nD = int((gam + 1).sum()), int(gam.sum())
+        zt = rng.integers(-2, 3, (nT, V)).astype(np.float32)  # ties everywhere
+        t_off = np.concatenate([[0], np.cumsum(gam + 1)])
+        am = np.argmax(zt, axis=1)
+        x = np.empty(nD, np.int32)
+        k = 0
+        for i in range(B):
+            for j in range(gam[i]):
+                x[k] = am[t_off[i] + j] if rng.random() < 0.7 else rng.integers(V)
+                k += 1
+        zin = workloads.to_bf16_bits(zt) if dtype == "bf16" else zt
+        r = oracle.verify(zin, np.zeros((nD, V), zin.dtype), dtype, V, gam, x, np.zeros(nT, np.float32),
+                          np.ones(B, np.float32), mode="greedy")
+        d = 0
+        for i in range(B):
+            K = gam[i]
+            for j in range(gam[i]):
+                if x[d + j] != am[t_off[i] + j]:
+                    K = j
+                    break
+            assert r["n_accepted"][i] == K
+            exp = list(x[d:d + K]) + [am[t_off[i] + K]] + [-1] * (gam[i] - K)
+            assert list(r["emitted"][t_off[i]:t_off[i + 1]]) == exp
+            d += gam[i]
+
+
+def pin_low_temperature_is_greedy():
+    """At a temperature far below the logit gaps, sampling gives the greedy result
+    whatever the uniforms; T <= 0 rows are greedy rows."""
+    rng = np.random.default_rng(23)
+    B, g, V = 40, 4, 50
+    base = rng.permutation(V).astype(np.float64) * 0.5  # distinct logits, gaps >= 0.5
+    zt = np.stack([rng.permutation(base) for _ in range(B * (g + 1))])
+    zd = np.stack([rng.permutation(base) for _ in range(B * g)])
+    am = np.argmax(zt, axis=1).reshape(B, g + 1)
+    x = np.where(rng.random((B, g)) < 0.6, am[:, :g], rng.integers(0, V, (B, g))).astype(np.int32)
+    gam = np.full(B, g, np.int32)
+    greedy = oracle.verify(zt, zd, "f64", V, gam, x.reshape(-1), np.zeros(B * (g + 1), np.float32),
+                           np.ones(B, np.float32), mode="greedy")
+    for trial in range(3):
+        u = snapped(rng, B * (g + 1))
+        cold = oracle.verify(zt, zd, "f64", V, gam, x.reshape(-1), u, np.full(B, 1e-3, np.float32))
+        assert np.array_equal(cold["n_accepted"], greedy["n_accepted"])
+        assert np.array_equal(cold["emitted"], greedy["emitted"])
+        for t in (0.0, -1.0):
+            zero = oracle.verify(zt, zd, "f64", V, gam, x.reshape(-1), u, np.full(B, t, np.float32))
+            assert np.array_equal(zero["emitted"], greedy["emitted"])
+
+
+# --------------------------------------------------------------------------- #
+# decisions at a threshold
+# --------------------------------------------------------------------------- #
+def pin_strict_threshold_and_flags():
+    """The test is strict (u = ratio rejects); decisions within 1e-5 of their
+    threshold are flagged, decisions further away are not."""
+    # p = (1/2, 1/2) and q = (1, 0): the ratio at x = 0 is exactly 1/2
+    zt2, zd2 = np.array([0.0, 0.0]), np.array([0.0, -np.inf])
+    target = np.stack([zt2, zt2])
+
+    def run(u):
+        return oracle.verify(target, zd2[None], "f64", 2, [1], [0], [u, 0.25], [1.0])
+
+    r = run(0.5)
+    assert r["n_accepted"][0] == 0 and r["flag_pos"][0] == 0, "u = ratio must reject, flagged"
+    r = run(0.5 - U24)
+    assert r["n_accepted"][0] == 1 and r["flag_pos"][0] == 0
+    r = run(0.5 + 2e-5)
+    assert r["n_accepted"][0] == 0 and r["flag_pos"][0] == -1
+    r = run(0.5 - 2e-5)
+    assert r["n_accepted"][0] == 1 and r["flag_pos"][0] == -1
+    # draw near a CDF edge: residual after rejection is (0, 1) -> no edge at u=0.25;
+    # the bonus p = (1/2, 1/2) has an edge at u = 1/2
+    r = oracle.verify(target, zd2[None], "f64", 2, [1], [0], [0.1, 0.5], [1.0])
+    assert r["n_accepted"][0] == 1 and r["emitted"][1] == 1 and r["flag_pos"][0] == 1
+    r = oracle.verify(target, zd2[None], "f64", 2, [1], [0], [0.1, 0.5 - 4e-6], [1.0])
+    assert r["emitted"][1] == 0 and r["flag_pos"][0] == 1
+    r = oracle.verify(target, zd2[None], "f64", 2, [1], [0], [0.1, 0.5 - 4e-5], [1.0])
+    assert r["emitted"][1] == 0 and r["flag_pos"][0] == -1
+
+
+# --------------------------------------------------------------------------- #
+# status rules
+# --------------------------------------------------------------------------- #
+def pin_status_rules():
+    rng = np.random.default_rng(41)
+    V, g = 16, 3
+    zt = rng.standard_normal((4 * (g + 1), V))
+    zd = rng.standard_normal((4 * g, V))
+    x = rng.integers(0, V, 4 * g).astype(np.int32)
+    u = snapped(rng, 4 * (g + 1))
+    gam = np.full(4, g, np.int32)
+    T = np.ones(4, np.float32)
+
+    def run(zt=zt, zd=zd, x=x, gam=gam, T=T, n=None, mode="sample"):
+        return oracle.verify(zt, zd, "f64", V, gam, x, u, T, mode=mode, n_target_rows=n)
+
+    base = run()
+    assert np.all(base["row_status"] & oracle.INVALID_MASK == 0)
+    # draft token out of range invalidates only its row
+    xb = x.copy()
+    xb[g + 1] = V
+    r = run(x=xb)
+    assert r["row_status"][1] & oracle.BAD_TOKEN and r["n_accepted"][1] == -1
+    assert np.all(r["emitted"][g + 1:2 * (g + 1)] == -1)
+    assert np.array_equal(r["emitted"][:g + 1], base["emitted"][:g + 1])
+    # NaN / +inf / all -inf invalidate their row; a single -inf does not
+    for bad, invalid in ((np.nan, True), (np.inf, True), (-np.inf, False)):
+        zb = zd.copy()
+        zb[2 * g + 1, 3] = bad
+        r = run(zd=zb)
+        assert bool(r["row_status"][2] & oracle.NONFINITE) == invalid, bad
+        assert (r["n_accepted"][2] == -1) == invalid
+    zb = zt.copy()
+    zb[3 * (g + 1) + 2] = -np.inf
+    r = run(zt=zb)
+    assert r["row_status"][3] & oracle.NONFINITE
+    # greedy rows never read draft logits
+    zb = zd.copy()
+    zb[0, 0] = np.nan
+    r = run(zd=zb, mode="greedy")
+    assert r["row_status"][0] == 0 and r["n_accepted"][0] >= 0
+    # bad gamma: negative, or a row count that does not match
+    r = run(gam=np.array([g, -1, g, g], np.int32))
+    assert np.all(r["row_status"] == oracle.BAD_GAMMA) and np.all(r["n_accepted"] == -1)
+    r = run(n=4 * (g + 1) - 1)
+    assert np.all(r["row_status"] == oracle.BAD_GAMMA)
+    # temperature: non-finite or subnormal is invalid, <= 0 is greedy
+    Tb = np.array([np.nan, np.inf, 1e-39, 1.0], np.float32)
+    r = run(T=Tb)
+    assert np.all(r["row_status"][:3] & oracle.BAD_TEMP) and r["row_status"][3] == 0
+    # q(x) = 0 with p(x) > 0: ratio 1, flagged; q(x) = p(x) = 0 with p = q elsewhere:
+    # rejection with zero residual mass falls back to p
+    zt3 = np.array([[0.0, 0.0, -np.inf]] * 2)
+    zd3 = np.array([[0.0, 0.0, -np.inf]])
+    r = oracle.verify(zt3, zd3, "f64", 3, [1], [2], [0.3, 0.7], [1.0])
+    assert r["n_accepted"][0] == 0 and r["row_status"][0] == oracle.Q_ZERO | oracle.ZERO_RESID
+    assert r["emitted"][0] == 1  # 0.7 of (1/2, 1/2, 0)
+    zt4 = np.array([[0.0, 0.0, 0.0]] * 2)
+    zd4 = np.array([[0.0, 0.0, -np.inf]])
+    r = oracle.verify(zt4, zd4, "f64", 3, [1], [2], [F32_BELOW_ONE, 0.7], [1.0])
+    assert r["n_accepted"][0] == 1 and r["row_status"][0] == oracle.Q_ZERO
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -1,0 +1,70 @@
+"""Planted mistakes in a copy of the oracle must each fail at least one pin.
+
+Each mutant is one plausible slip (a non-strict test, an inverted ratio, a wrong
+residual sign, the wrong uniform for the draw, ...), applied textually to a
+temporary copy of oracle.c and compiled on the CPU.  The committed oracle is never
+modified.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+import pins
+
+MUTANTS = {
+    "nonstrict_accept": ("if (!(u < ratio)) {", "if (!(u <= ratio)) {"),
+    "inverted_ratio": ("ratio = px / qx;", "ratio = qx / px;"),
+    "residual_sign": ("w[v] = fmax(0.0, P[v] - Q[v]);", "w[v] = fmax(0.0, Q[v] - P[v]);"),
+    "bonus_wrong_position": (
+        "oracle_softmax(vector_ptr(target, dtype, t0 + K, V), dtype, V, T, P);",
+        "oracle_softmax(vector_ptr(target, dtype, t0 + (K == g && K > 0 ? K - 1 : K), V), dtype, V, T, P);"),
+    "draw_reuses_test_uniform": ("(double)uniforms[t0 + g], &W, &near)", "(double)uniforms[t0 + K], &W, &near)"),
+    "q_sum_without_temperature": ("vector_max_sumexp(zd, dtype, V, T, &md, &Sd);",
+                                  "vector_max_sumexp(zd, dtype, V, 1.0, &md, &Sd);"),
+    "sumexp_without_temperature": ("S += exp((logit_at(z, dtype, v) - m) / T);",
+                                   "S += exp(logit_at(z, dtype, v) - m);"),
+    "greedy_bonus_off_by_one": (
+        "int64_t aK = oracle_argmax(vector_ptr(target, dtype, t0 + K, V), dtype, V);",
+        "int64_t aK = oracle_argmax(vector_ptr(target, dtype, t0 + (K > 0 ? K - 1 : 0), V), dtype, V);"),
+    "greedy_last_index_on_ties": ("        if (x > bv) {", "        if (x >= bv) {"),
+    "cdf_nonstrict": ("        if (C > t) {", "        if (C >= t) {"),
+    "draw_unnormalized": ("    double t = u * W;", "    double t = u;"),
+    "alpha_with_max": ("a += fmin(pp[v], qq[v]);", "a += fmax(pp[v], qq[v]);"),
+    "flag_threshold_too_wide": ("if (flag < 0 && fabs(u - ratio) < 1e-5)", "if (flag < 0 && fabs(u - ratio) < 1e-3)"),
+    "no_zero_residual_fallback": ("                if (W == 0.0) {", "                if (W < 0.0) {"),
+    "neg_inf_is_nonfinite": ("if (isnan(x) || x == INFINITY)", "if (isnan(x) || isinf(x))"),
+}
+
+
+@pytest.fixture(scope="module")
+def mutant_dir(tmp_path_factory):
+    return tmp_path_factory.mktemp("oracle_mutants")
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, mutant_dir):
+    old, new = MUTANTS[name]
+    src = open(oracle.SRC_PATH).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/found"
+    d = mutant_dir / name
+    d.mkdir()
+    shutil.copy(os.path.join(os.path.dirname(oracle.SRC_PATH), "oracle.h"), d / "oracle.h")
+    (d / "oracle.c").write_text(src.replace(old, new))
+    so = str(d / "liboracle.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", str(d / "oracle.c"),
+                    "-o", so, "-lm"], check=True)
+    failed = []
+    with oracle.using(so):
+        for pin in pins.ALL_PINS:
+            try:
+                pin()
+            except AssertionError:
+                failed.append(pin.__name__)
+            except ValueError:
+                failed.append(pin.__name__)
+            if failed:
+                break
+    assert failed, f"mutant {name} passes every pin"

@@ -1,0 +1,328 @@
+"""Seeded synthetic workloads for the speculative-sampling verification step.
+
+This module only *produces inputs*: logits, draft tokens, uniforms, temperatures
+and per-row draft lengths.  It holds none of the verification arithmetic (no
+temperature softmax, no acceptance ratio, no residual, no inverse-CDF draw), so
+both the HIP path and the CPU oracle may consume what it makes.
+
+Layout (the packed layout of the library's C ABI):
+  * row i has gamma_i drafts; target rows t_off[i] .. t_off[i]+gamma_i hold the
+    target logits of the gamma_i+1 verified positions, draft rows
+    d_off[i] .. d_off[i]+gamma_i-1 hold the drafter logits of the gamma_i drafts;
+  * t_off / d_off are exclusive prefix sums of gamma_i+1 / gamma_i;
+  * logits are row-major [rows, V]; bf16 logits are stored as their uint16 bit
+    patterns (round-to-nearest-even from float32), fp32 logits as float32;
+  * uniforms[t_off[i] + j] (j < gamma_i) drives the accept test of draft j, and
+    uniforms[t_off[i] + gamma_i] drives the single residual-or-bonus draw;
+    every uniform is k * 2^-24 for an integer k in [0, 2^24), so it is exact in
+    float32 and in float64.
+
+Draft tokens are what a drafter would have produced: in sampling mode a sample
+of softmax(draft/T) drawn with the Gumbel-max construction (argmax of logits/T
+plus Gumbel noise), in greedy mode the argmax of the draft logits (the greedy
+drafter).  Both are input generation, done before and apart from verification.
+
+Every random number comes from numpy's Philox bit generator, keyed per
+(seed, workload, row) through a SeedSequence, so a workload is reproducible and
+its rows can be generated in parallel.
+
+The five workloads follow the configurations the verification step is measured
+on: a 32-token toy for the statistical checks, and bf16/fp32 batches at
+V = 32000, 128256, 152064 and 256000.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+U24 = float(2.0 ** -24)
+
+
+# --------------------------------------------------------------------------- #
+# container
+# --------------------------------------------------------------------------- #
+@dataclass
+class Workload:
+    name: str
+    dtype: str                 # "bf16" | "f32"
+    vocab: int
+    gamma: np.ndarray          # int32 [B]
+    target: np.ndarray         # uint16 bits (bf16) or float32, [n_target_rows, V]
+    draft: np.ndarray          # same dtype, [n_draft_rows, V]
+    draft_tokens: np.ndarray   # int32 [n_draft_rows]
+    uniforms: np.ndarray       # float32 [n_target_rows]
+    temperature: np.ndarray    # float32 [B]
+    mode: str = "sample"       # "sample" | "greedy"
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def batch(self) -> int:
+        return int(self.gamma.shape[0])
+
+    @property
+    def n_target_rows(self) -> int:
+        return int(self.target.shape[0])
+
+    @property
+    def n_draft_rows(self) -> int:
+        return int(self.draft.shape[0])
+
+    @property
+    def dense_gamma(self):
+        """The common draft length if every row has the same one, else None."""
+        if self.batch and np.all(self.gamma == self.gamma[0]):
+            return int(self.gamma[0])
+        return None
+
+    def offsets(self):
+        """(t_off, d_off) as int64 arrays of length B+1 (layout bookkeeping)."""
+        t = np.zeros(self.batch + 1, np.int64)
+        d = np.zeros(self.batch + 1, np.int64)
+        np.cumsum(self.gamma.astype(np.int64) + 1, out=t[1:])
+        np.cumsum(self.gamma.astype(np.int64), out=d[1:])
+        return t, d
+
+    def logit_bytes(self) -> int:
+        return int(self.target.nbytes + self.draft.nbytes)
+
+    def with_mode(self, mode: str) -> "Workload":
+        w = Workload(**{**self.__dict__})
+        w.mode = mode
+        return w
+
+
+# --------------------------------------------------------------------------- #
+# helpers (input generation only)
+# --------------------------------------------------------------------------- #
+def _rng(seed: int, stream: int, row: int) -> np.random.Generator:
+    ss = np.random.SeedSequence(entropy=int(seed), spawn_key=(int(stream), int(row)))
+    return np.random.Generator(np.random.Philox(ss))
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit pattern, round to nearest, ties to even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def logits_as_f32(arr: np.ndarray, dtype: str) -> np.ndarray:
+    return bf16_bits_to_f32(arr) if dtype == "bf16" else np.asarray(arr, np.float32)
+
+
+def snapped_uniforms(rng: np.random.Generator, n: int) -> np.ndarray:
+    k = rng.integers(0, 1 << 24, size=n, dtype=np.int64)
+    return (k.astype(np.float64) * U24).astype(np.float32)
+
+
+def gumbel_max_token(rng: np.random.Generator, logits_f32: np.ndarray, temperature: float) -> int:
+    """One draw from softmax(logits / T) by the Gumbel-max construction."""
+    g = -np.log(rng.standard_exponential(logits_f32.shape[0]))
+    return int(np.argmax(logits_f32.astype(np.float64) / float(temperature) + g))
+
+
+def _store(x_f32: np.ndarray, dtype: str) -> np.ndarray:
+    return to_bf16_bits(x_f32) if dtype == "bf16" else x_f32.astype(np.float32)
+
+
+def _workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+# --------------------------------------------------------------------------- #
+# generic builder
+# --------------------------------------------------------------------------- #
+def build(name: str, dtype: str, vocab: int, gamma, temperature, seed: int,
+          target_fn, draft_fn, mode: str = "sample", draft_tokens_fn=None,
+          meta=None) -> Workload:
+    """Assemble a packed workload row by row.
+
+    target_fn(rng, row, n_pos) -> float32 [n_pos, V]   (pre-rounding target logits)
+    draft_fn(rng, row, tgt)    -> float32 [gamma, V]    (pre-rounding draft logits)
+    draft_tokens_fn(rng, row, draft_stored_f32, T) -> int32 [gamma] (optional)
+    """
+    gamma = np.asarray(gamma, np.int32)
+    B = gamma.shape[0]
+    temperature = np.asarray(temperature, np.float32)
+    if temperature.ndim == 0:
+        temperature = np.full(B, float(temperature), np.float32)
+    t_off = np.concatenate([[0], np.cumsum(gamma.astype(np.int64) + 1)])
+    d_off = np.concatenate([[0], np.cumsum(gamma.astype(np.int64))])
+    store_dt = np.uint16 if dtype == "bf16" else np.float32
+    target = np.empty((int(t_off[-1]), vocab), store_dt)
+    draft = np.empty((int(d_off[-1]), vocab), store_dt)
+    tokens = np.empty(int(d_off[-1]), np.int32)
+    uniforms = np.empty(int(t_off[-1]), np.float32)
+
+    def one_row(i: int):
+        g = int(gamma[i])
+        rng = _rng(seed, 1, i)
+        tgt = target_fn(rng, i, g + 1)
+        target[t_off[i]:t_off[i + 1]] = _store(tgt, dtype)
+        if g > 0:
+            drf = draft_fn(rng, i, tgt[:g])
+            draft[d_off[i]:d_off[i + 1]] = _store(drf, dtype)
+            stored = logits_as_f32(draft[d_off[i]:d_off[i + 1]], dtype)
+            if draft_tokens_fn is not None:
+                tok = draft_tokens_fn(rng, i, stored, float(temperature[i]))
+            elif mode == "greedy":
+                tok = np.argmax(stored, axis=1)
+            else:
+                tok = [gumbel_max_token(rng, stored[j], float(temperature[i])) for j in range(g)]
+            tokens[d_off[i]:d_off[i + 1]] = np.asarray(tok, np.int32)
+        uniforms[t_off[i]:t_off[i + 1]] = snapped_uniforms(_rng(seed, 2, i), g + 1)
+
+    if B * vocab >= (1 << 20):
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(one_row, range(B)))
+    else:
+        for i in range(B):
+            one_row(i)
+    return Workload(name=name, dtype=dtype, vocab=vocab, gamma=gamma, target=target,
+                    draft=draft, draft_tokens=tokens, uniforms=uniforms,
+                    temperature=temperature, mode=mode, meta=dict(meta or {}, seed=seed))
+
+
+# --------------------------------------------------------------------------- #
+# logit shapes
+# --------------------------------------------------------------------------- #
+def _normal_target(vocab: int, sigma: float):
+    def fn(rng, row, n_pos):
+        return rng.standard_normal((n_pos, vocab), dtype=np.float32) * np.float32(sigma)
+    return fn
+
+
+def _boosted_target(vocab: int, sigma: float, n_boost: int, boost: float):
+    """N(0, sigma) logits with n_boost distinct random entries per position raised by +boost."""
+    def fn(rng, row, n_pos):
+        x = rng.standard_normal((n_pos, vocab), dtype=np.float32) * np.float32(sigma)
+        for j in range(n_pos):
+            idx = rng.choice(vocab, size=n_boost, replace=False)
+            x[j, idx] += np.float32(boost)
+        return x
+    return fn
+
+
+def _zipf_target(vocab: int, sigma: float, s: float):
+    """N(0, sigma) logits plus -s*ln(rank) under a fresh random token permutation per
+    position, i.e. probabilities tilted by a Zipf(s) factor rank^-s."""
+    log_rank = (-s * np.log(np.arange(1, vocab + 1, dtype=np.float64))).astype(np.float32)
+
+    def fn(rng, row, n_pos):
+        x = rng.standard_normal((n_pos, vocab), dtype=np.float32) * np.float32(sigma)
+        for j in range(n_pos):
+            x[j] += log_rank[rng.permutation(vocab)]
+        return x
+    return fn
+
+
+def _noisy_draft(scale: float, sigma):
+    """draft = scale * target + N(0, sigma_row)."""
+    def fn(rng, row, tgt):
+        sg = sigma(row) if callable(sigma) else sigma
+        return (np.float32(scale) * tgt
+                + rng.standard_normal(tgt.shape, dtype=np.float32) * np.float32(sg))
+    return fn
+
+
+# --------------------------------------------------------------------------- #
+# the five configurations
+# --------------------------------------------------------------------------- #
+def toy(seed: int = 1, rounds: int = 10_000, gamma: int = 4, vocab: int = 32,
+        shared_position: bool = False) -> Workload:
+    """B=1, gamma=4, V=32 fp32 toy: target ~ N(0,2), draft = target + N(0,0.5), T=1.
+
+    The single row's logits are fixed and replicated over `rounds` independent
+    rounds (one packed row per round); every round draws its own draft tokens
+    from q and its own uniforms.  With shared_position=True every position uses
+    the same (p, q) pair, so the acceptance rate is the same at every position.
+    """
+    base = _rng(seed, 0, 0)
+    if shared_position:
+        t1 = base.standard_normal(vocab) * 2.0
+        tgt = np.tile(t1, (gamma + 1, 1))
+        d1 = t1 + base.standard_normal(vocab) * 0.5
+        drf = np.tile(d1, (gamma, 1))
+    else:
+        tgt = base.standard_normal((gamma + 1, vocab)) * 2.0
+        drf = tgt[:gamma] + base.standard_normal((gamma, vocab)) * 0.5
+    tgt = tgt.astype(np.float32)
+    drf = drf.astype(np.float32)
+    B = rounds
+    target = np.tile(tgt, (B, 1))
+    draft = np.tile(drf, (B, 1))
+    # Gumbel-max draws of every round's drafts from softmax(draft), fp64
+    rng = _rng(seed, 3, 0)
+    g = -np.log(rng.standard_exponential((B, gamma, vocab)))
+    tokens = np.argmax(drf.astype(np.float64)[None] + g, axis=2).astype(np.int32).reshape(-1)
+    uniforms = snapped_uniforms(_rng(seed, 2, 0), B * (gamma + 1))
+    return Workload(name="toy" + ("_shared" if shared_position else ""), dtype="f32",
+                    vocab=vocab, gamma=np.full(B, gamma, np.int32), target=target,
+                    draft=draft, draft_tokens=tokens, uniforms=uniforms,
+                    temperature=np.ones(B, np.float32), mode="sample",
+                    meta=dict(seed=seed, rounds=rounds, base_target=tgt, base_draft=drf))
+
+
+def c2(seed: int = 2) -> Workload:
+    """B=8, gamma=4, V=32000 bf16; target N(0,3) with 5 logits +8 per position;
+    draft = target + N(0,1); T=1."""
+    V = 32000
+    return build("c2_b8_g4_v32000_bf16", "bf16", V, np.full(8, 4), 1.0, seed,
+                 _boosted_target(V, 3.0, 5, 8.0), _noisy_draft(1.0, 1.0))
+
+
+def c3(seed: int = 3, mode: str = "sample", batch: int = 64) -> Workload:
+    """B=64, gamma=5, V=128256 bf16; target N(0,3) + Zipf(1.1) log-boost on a random
+    permutation; draft = 0.8*target + N(0,1.5); T=0.8; sampling or greedy."""
+    V = 128256
+    return build(f"c3_b{batch}_g5_v128256_bf16_{mode}", "bf16", V, np.full(batch, 5), 0.8, seed,
+                 _zipf_target(V, 3.0, 1.1), _noisy_draft(0.8, 1.5), mode=mode)
+
+
+def c4(seed: int = 4, batch: int = 256) -> Workload:
+    """B=256, gamma=8, V=152064 bf16 as c2; per-row T ~ U[0.5,1.5]; per-row draft
+    noise sigma ~ U[0.2,3.0]."""
+    V = 152064
+    prm = _rng(seed, 9, 0)
+    temps = prm.uniform(0.5, 1.5, batch).astype(np.float32)
+    sig = prm.uniform(0.2, 3.0, batch)
+    return build(f"c4_b{batch}_g8_v152064_bf16", "bf16", V, np.full(batch, 8), temps, seed,
+                 _boosted_target(V, 3.0, 5, 8.0), _noisy_draft(1.0, lambda r: float(sig[r])),
+                 meta=dict(draft_sigma=sig))
+
+
+def c5(seed: int = 5, batch: int = 512) -> Workload:
+    """Ragged B=512, gamma_i ~ U{0..7}, V=256000 fp32; target N(0,4); draft = target + N(0,1); T=1."""
+    V = 256000
+    prm = _rng(seed, 9, 0)
+    gam = prm.integers(0, 8, batch).astype(np.int32)
+    return build(f"c5_b{batch}_ragged_v256000_f32", "f32", V, gam, 1.0, seed,
+                 _normal_target(V, 4.0), _noisy_draft(1.0, 1.0))
+
+
+def small(seed: int, batch: int, vocab: int, dtype: str, gamma, temperature=1.0,
+          sigma: float = 3.0, noise: float = 1.0, mode: str = "sample", n_boost: int = 0) -> Workload:
+    """Small generic workload for parity tests (ragged gamma allowed)."""
+    gamma = np.asarray(gamma, np.int32)
+    if gamma.ndim == 0:
+        gamma = np.full(batch, int(gamma), np.int32)
+    tf = _boosted_target(vocab, sigma, n_boost, 8.0) if n_boost else _normal_target(vocab, sigma)
+    return build(f"small_b{batch}_v{vocab}_{dtype}_{mode}", dtype, vocab, gamma, temperature, seed,
+                 tf, _noisy_draft(1.0, noise), mode=mode)
+
+
+CONFIGS = {
+    "toy": toy,
+    "c2": c2,
+    "c3": c3,
+    "c4": c4,
+    "c5": c5,
+}
