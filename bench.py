@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative-sampling verification step on one MI355X.
+
+One step = one spec_verify call over a whole batch (statistics pass over every
+logit, accept scan, residual/bonus draw), inputs already resident in HBM.  The
+default workload is B=64 rows, gamma=5, V=128256, bf16 logits, sampling mode, with
+the batch rotated over 4 device copies so that the 256 MB last-level cache cannot
+serve a step from the previous one.
+
+Prints ONE JSON line: verified positions/s (sum of gamma_i + 1 per step), plus
+rows/s, algorithmic HBM GB/s, the roofline of the dominant kernel (the statistics
+pass, timed live with HIP events recorded around it on the call's stream), and the
+CPU oracle timed on this host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, published
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "stats_kernel_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "speculative_sampling_verify_02_amd", "csrc", f)
+                  for f in ("sv_kernels.hip", "sv_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c3", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--mode", default="sample", choices=["sample", "greedy"])
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (to calibrate rocprof byte counters)")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t pairs through the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (loads the runtime)
+        self.hip = ctypes.CDLL("libamdhip64.so.7", mode=ctypes.RTLD_GLOBAL)
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+        return e.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def to_device(w, dev):
+    import numpy as np
+    import torch
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    if w.dtype == "bf16":
+        target = t(w.target.view(np.int16)).view(torch.bfloat16)
+        draft = t(w.draft.view(np.int16)).view(torch.bfloat16)
+    else:
+        target, draft = t(w.target), t(w.draft)
+    return dict(target=target, draft=draft, tokens=t(w.draft_tokens), uniforms=t(w.uniforms),
+                temperature=t(w.temperature), gamma=t(w.gamma))
+
+
+def make_workload(name, mode):
+    import workloads
+    if name == "c3":
+        return workloads.c3(mode=mode)
+    w = workloads.CONFIGS[name]()
+    return w.with_mode(mode) if mode != w.mode else w
+
+
+def cpu_baseline(w, budget_s: float, mode: str):
+    """The oracle (as it stands) on this host: whole batches, repeated until the
+    budget is spent."""
+    import oracle
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    positions = int(w.gamma.sum() + w.batch)
+    t0 = time.perf_counter()
+    calls = 0
+    while True:
+        oracle.verify_workload(w, threads=cores, mode=mode)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or calls >= 10000:
+            break
+    return {"value": positions * calls / el, "unit": "positions/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{calls} full batches of the same workload ({w.batch} rows, {positions} "
+                      f"positions each), {el:.1f} s wall, OpenMP over rows"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
+                                   "part of it (rows shard independently, see the design notes)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import speculative_sampling_verify_02_amd as sv
+
+    dev = torch.device("cuda:0")
+    w = make_workload(args.config, args.mode)
+    esz = 2 if w.dtype == "bf16" else 4
+    copies = [to_device(w, dev) for _ in range(max(1, args.copies))]
+    dense = w.dense_gamma
+    gamma_arg = dense if dense is not None else None
+    nT, nD, V, B = w.n_target_rows, w.n_draft_rows, w.vocab, w.batch
+
+    outs = [(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(nT, dtype=torch.int32, device=dev))
+            for _ in copies]
+    ws = torch.empty(sv.workspace_bytes(B, nT, V, sv.SV_BF16 if w.dtype == "bf16" else sv.SV_F32),
+                     dtype=torch.uint8, device=dev)
+
+    def step(k, d=None):
+        d = d or copies[k % len(copies)]
+        g = gamma_arg if gamma_arg is not None else d["gamma"]
+        return sv.spec_verify(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temperature"], g,
+                              mode=args.mode, workspace=ws, out=outs[k % len(copies)])
+
+    # one checked call: accepted counts drive the algorithmic pass-2 bytes
+    n_acc, _ = step(0)
+    torch.cuda.synchronize()
+    K = n_acc.cpu().numpy()
+    gam = w.gamma
+    pass1_bytes = (nT + (nD if args.mode == "sample" else 0)) * V * esz
+    pass2_bytes = 0
+    if args.mode == "sample":
+        pass2_bytes = int(sum(V * esz * (2 if K[i] < gam[i] else 1) for i in range(B) if K[i] >= 0))
+    small_bytes = nT * 4 * 2 + nD * 4 + B * 8
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    ev = HipEvents()
+    starts = [ev.create() for _ in range(args.steps)]
+    stops = [ev.create() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        sv.set_profile_events(starts[k], stops[k])
+        step(k)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sv.set_profile_events(None, None)
+    stats_ms = [ev.elapsed_ms(starts[k], stops[k]) for k in range(args.steps)]
+    for e in starts + stops:
+        ev.destroy(e)
+
+    sec_per_step = (t1 - t0) / args.steps
+    positions = nT
+    stats_avg_ms = float(np.mean(stats_ms))
+    stats_bytes = pass1_bytes  # every logit read once (the per-segment records it writes are < 0.01%)
+    achieved = stats_bytes / (stats_avg_ms * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(PROFILE_TRAFFIC):
+        try:
+            prof = json.load(open(PROFILE_TRAFFIC))
+            key = f"{args.config}_{args.mode}"
+            entry = prof.get("workloads", {}).get(key)
+            if entry and prof.get("kernel_source_hash") == kernel_source_hash():
+                traffic = entry["hbm_bytes_per_launch"]
+        except Exception:
+            traffic = None
+
+    total_bytes = pass1_bytes + pass2_bytes + small_bytes
+    res = {
+        "metric": "verified positions/sec and achieved HBM GB/s (% of peak), V=128256 bf16",
+        "value": positions / sec_per_step,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec_per_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "gamma": int(gam.max()) if dense is None else dense,
+                   "ragged": dense is None, "vocab": V, "mode": args.mode,
+                   "rotated_device_copies": len(copies)},
+        "rows_per_s": B / sec_per_step,
+        "hbm_gbps_algorithmic": total_bytes / sec_per_step / 1e9,
+        "hbm_frac_of_peak": total_bytes / sec_per_step / 1e9 / PEAK_HBM_GBPS,
+        "bytes_per_step": {"pass1_logits": pass1_bytes, "pass2_logits": pass2_bytes, "other": small_bytes},
+        "mean_accepted": float(K[K >= 0].mean()) if (K >= 0).any() else None,
+        "roofline": {"kernel": "stats_kernel", "bound": "hbm", "achieved": achieved,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": traffic, "avg_launch_ms": stats_avg_ms,
+                     "algorithmic_bytes_per_launch": stats_bytes},
+        "cpu_baseline": None,
+    }
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.mode)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,151 @@
+/*
+ * spec_verify: the verification step of speculative sampling on AMD Instinct MI355X
+ * (gfx950), as a C ABI.
+ *
+ * One call verifies a batch of drafted rows.  Row i carries gamma_i drafted tokens
+ * x_0 .. x_{gamma_i - 1}, the target model's logits at the gamma_i + 1 positions the
+ * verification pass scored, and the drafter's logits at the gamma_i drafted positions.
+ * With p_j = softmax(target_j / T_i) and q_j = softmax(draft_j / T_i) (the same
+ * temperature for both; brunomaga.github.io "inference-distillation-speculative-
+ * decoding", section "Knowledge distillation", the softened-output equation, and
+ * rayaq.ca "Speculative decoding", section "Why the output is exactly the target's"):
+ *
+ *   1. drafts are kept left to right while u_j < min(1, p_j(x_j) / q_j(x_j)); the first
+ *      failing j is K (rayaq.ca "Speculative decoding", section "One round", step 3);
+ *   2. if K < gamma_i, one token is drawn from the residual
+ *      max(0, p_K - q_K) / sum max(0, p_K - q_K) (same section, step 4);
+ *   3. if K = gamma_i, one bonus token is drawn from p_{gamma_i} (same section, step 5);
+ *   4. in greedy mode drafts are kept while they equal the target's argmax, and the
+ *      target's argmax at K is emitted (rayaq.ca "Speculative decoding", section
+ *      "The greedy case").
+ *
+ * A categorical draw with weights w is the inverse CDF in token order: t = u * sum(w),
+ * the token is the smallest v whose running sum of w exceeds t.  All randomness is
+ * supplied by the caller as uniforms, so the result is a deterministic function of
+ * the inputs.
+ *
+ * LAYOUT (packed rows).  Let t_off[i] = sum_{k<i} (gamma_k + 1) and
+ * d_off[i] = sum_{k<i} gamma_k, n_target_rows = sum (gamma_i + 1), n_draft_rows =
+ * n_target_rows - batch.  Logit matrices are row-major: target [n_target_rows, vocab],
+ * draft [n_draft_rows, vocab]; row t_off[i] + j of target holds position j of batch
+ * row i, row d_off[i] + j of draft holds draft position j.  A dense [B, gamma+1, V]
+ * target tensor and [B, gamma, V] draft tensor are this layout with a constant gamma.
+ *
+ * OWNERSHIP.  Every buffer is owned by the caller.  All array pointers are DEVICE
+ * pointers (hipMalloc'd or equivalent) unless stated otherwise.  The library keeps no
+ * pointer past the call and allocates no device memory: scratch space is the caller's
+ * `workspace`, of at least spec_verify_workspace_bytes(...) bytes, 256-byte aligned.
+ *
+ * ASYNCHRONY.  spec_verify enqueues its kernels on `hip_stream` (a hipStream_t; NULL =
+ * the null stream) and returns without synchronizing.  Outputs are valid once the
+ * stream reaches that point.  Two calls that share a workspace must be ordered on
+ * one stream.
+ *
+ * ERRORS.  Argument errors detectable on the host (null pointers, bad sizes, bad
+ * dtype or mode, a workspace that is too small or misaligned, a dense row count that
+ * does not match) return a negative sv_status and enqueue nothing.  Data-dependent
+ * problems never abort: they are reported per row through row status bits, and an
+ * invalid row gets n_accepted = -1 and -1 in all its emitted slots.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SV_OK = 0,
+    SV_EINVAL = -1,     /* bad pointer, size, mode or layout                     */
+    SV_EDTYPE = -2,     /* dtype is not SV_BF16 or SV_F32                         */
+    SV_EWORKSPACE = -3, /* workspace too small or not 256-byte aligned            */
+    SV_EHIP = -4        /* the HIP runtime reported an error while enqueueing      */
+} sv_status;
+
+typedef enum { SV_BF16 = 0, SV_F32 = 1 } sv_dtype;
+typedef enum { SV_SAMPLE = 0, SV_GREEDY = 1 } sv_mode;
+
+/* Per-row status bits (row_status).  The first four make a row invalid. */
+#define SV_ROW_BAD_TOKEN 1    /* a draft token is outside [0, vocab)                          */
+#define SV_ROW_Q_ZERO 2       /* q(x_j) == 0 at some draft position; that ratio is 1 if
+                                 p(x_j) > 0, else 0 (informational)                            */
+#define SV_ROW_NONFINITE 4    /* a NaN or +inf logit, or a position whose logits are all -inf */
+#define SV_ROW_BAD_GAMMA 8    /* some gamma_i < 0, or sum(gamma_i + 1) != n_target_rows; set
+                                 on every row of the call                                      */
+#define SV_ROW_ZERO_RESID 16  /* zero residual mass at a rejection (only through rounding);
+                                 the token was drawn from p_K instead (informational)          */
+#define SV_ROW_BAD_TEMP 32    /* sampling row whose temperature is NaN, infinite, or in
+                                 (0, FLT_MIN)                                                   */
+
+/* Optional diagnostics: every pointer may be NULL; all are device pointers. */
+typedef struct sv_diag {
+    double *p_x;         /* [n_draft_rows]: p_j(x_j) at every draft position of a valid
+                            sampling row (NaN elsewhere)                                  */
+    double *q_x;         /* [n_draft_rows]: q_j(x_j), likewise                            */
+    double *resid_mass;  /* [batch]: sum of the draw weights (residual mass at a
+                            rejection, ~1 for a bonus draw); NaN for greedy/invalid rows   */
+    int32_t *row_status; /* [batch]: SV_ROW_* bits                                        */
+} sv_diag;
+
+/*
+ * Bytes of device workspace spec_verify needs for this shape.  Returns 0 for invalid
+ * sizes (batch < 0, vocab <= 0, n_target_rows < batch, or dtype not SV_BF16/SV_F32).
+ */
+size_t spec_verify_workspace_bytes(int32_t batch, int64_t n_target_rows, int64_t vocab,
+                                   int32_t dtype);
+
+/*
+ * Verify one batch (see the file comment for what is computed and the layout).
+ *
+ *   target_logits  [n_target_rows, vocab] dtype   device
+ *   draft_logits   [n_draft_rows, vocab]  dtype   device (may be NULL if n_draft_rows == 0)
+ *   dtype          SV_BF16 (bf16 bit patterns) or SV_F32
+ *   vocab          V, 1 <= V < 2^31
+ *   batch          B >= 0 rows
+ *   n_target_rows  sum(gamma_i + 1)
+ *   draft_tokens   [n_draft_rows] int32 device: x_j of row i at d_off[i] + j
+ *   uniforms       [n_target_rows] float device, each in [0, 1): slot t_off[i] + j (j < gamma_i)
+ *                  drives accept test j, slot t_off[i] + gamma_i drives the single draw
+ *   temperature    [batch] float device: T_i; T_i <= 0 makes row i greedy in SV_SAMPLE mode
+ *   gamma_per_row  [batch] int32 device, or NULL for a dense batch where every row has
+ *                  `gamma_uniform` drafts (then n_target_rows must be batch*(gamma_uniform+1))
+ *   gamma_uniform  used only when gamma_per_row is NULL; >= 0
+ *   mode           SV_SAMPLE or SV_GREEDY (greedy ignores temperature and draft_logits)
+ *   n_accepted     [batch] int32 device out: K_i, or -1 for an invalid row
+ *   emitted_tokens [n_target_rows] int32 device out: row i at t_off[i]: the K_i kept
+ *                  drafts, then the drawn (or argmax) token, then -1 up to gamma_i
+ *   diag           optional diagnostics (NULL, or a HOST pointer to a struct of device
+ *                  pointers)
+ *   workspace      device scratch, >= spec_verify_workspace_bytes(...) bytes, 256-aligned;
+ *                  its contents need no initialization and are overwritten
+ *   hip_stream     hipStream_t to enqueue on
+ */
+sv_status spec_verify(const void *target_logits, const void *draft_logits, int32_t dtype,
+                      int64_t vocab, int32_t batch, int64_t n_target_rows,
+                      const int32_t *draft_tokens, const float *uniforms,
+                      const float *temperature, const int32_t *gamma_per_row,
+                      int32_t gamma_uniform, int32_t mode, int32_t *n_accepted,
+                      int32_t *emitted_tokens, const sv_diag *diag, void *workspace,
+                      size_t workspace_bytes, void *hip_stream);
+
+/* Static, human-readable name of an sv_status value. */
+const char *spec_verify_strerror(int32_t status);
+
+/*
+ * Profiling aid: when both are non-NULL hipEvent_t handles, every following
+ * spec_verify call records `start_event` on its stream right before its streaming
+ * statistics kernel (the pass over every logit) and `stop_event` right after it.
+ * Pass NULL, NULL to stop.  Process-wide setting, not thread-safe.
+ */
+sv_status spec_verify_set_profile_events(void *start_event, void *stop_event);
+
+/* Version string of the library. */
+const char *spec_verify_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPEC_VERIFY_H */

@@ -52,10 +52,10 @@ def _load(path: str):
     L.oracle_argmax.restype = i64
     L.oracle_position.argtypes = [vp, vp, ctypes.c_int, i64, dbl, vp, vp, vp, vp, vp]
     L.oracle_position.restype = ctypes.c_int
-    L.oracle_inverse_cdf.argtypes = [vp, i64, dbl, vp, vp]
+    L.oracle_inverse_cdf.argtypes = [vp, i64, dbl, dbl, vp, vp]
     L.oracle_inverse_cdf.restype = i64
     L.oracle_verify.argtypes = [vp, vp, ctypes.c_int, i64, i32, i64, vp, vp, vp, vp,
-                                ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int]
+                                ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, dbl, ctypes.c_int]
     L.oracle_verify.restype = ctypes.c_int
     return L
 
@@ -129,18 +129,21 @@ def position(zt, zd, T: float, dtype: str = "f64") -> dict:
     return dict(p=p, q=q, alpha=float(a[0]), resid_mass=float(w[0]), residual=r)
 
 
-def inverse_cdf(w, u: float):
+def inverse_cdf(w, u: float, eps: float = 1e-5):
     """(token, W, near_edge) of the inverse-CDF draw with weights w and uniform u."""
     w = np.ascontiguousarray(w, np.float64)
     W = np.zeros(1, np.float64)
     near = np.zeros(1, np.int32)
-    tok = lib().oracle_inverse_cdf(_ptr(w), w.shape[0], float(u), _ptr(W), _ptr(near))
+    tok = lib().oracle_inverse_cdf(_ptr(w), w.shape[0], float(u), float(eps), _ptr(W), _ptr(near))
     return int(tok), float(W[0]), bool(near[0])
 
 
 def verify(target, draft, dtype: str, vocab: int, gamma, draft_tokens, uniforms, temperature,
-           mode: str = "sample", n_target_rows=None, threads: int = 0) -> dict:
-    """One verification round over a packed batch; returns numpy arrays."""
+           mode: str = "sample", n_target_rows=None, threads: int = 0,
+           flag_eps: float = 1e-5) -> dict:
+    """One verification round over a packed batch; returns numpy arrays.  flag_pos[i] is
+    the first decision of row i within flag_eps of its threshold (accept test j, or
+    gamma_i for the draw), -1 if none."""
     gamma = np.ascontiguousarray(gamma, np.int32)
     B = gamma.shape[0]
     target = _logits(target, dtype)
@@ -165,13 +168,13 @@ def verify(target, draft, dtype: str, vocab: int, gamma, draft_tokens, uniforms,
                              _ptr(gamma), SAMPLE if mode == "sample" else GREEDY,
                              _ptr(out["n_accepted"]), _ptr(out["emitted"]), _ptr(out["p_x"]),
                              _ptr(out["q_x"]), _ptr(out["resid_mass"]), _ptr(out["row_status"]),
-                             _ptr(out["flag_pos"]), int(threads))
+                             _ptr(out["flag_pos"]), float(flag_eps), int(threads))
     if rc != 0:
         raise ValueError(f"oracle_verify status {rc}")
     return out
 
 
-def verify_workload(w, threads: int = 0, mode: str | None = None) -> dict:
+def verify_workload(w, threads: int = 0, mode: str | None = None, flag_eps: float = 1e-5) -> dict:
     """verify() on any object with the packed-workload attributes."""
     return verify(w.target, w.draft, w.dtype, w.vocab, w.gamma, w.draft_tokens, w.uniforms,
-                  w.temperature, mode=mode or w.mode, threads=threads)
+                  w.temperature, mode=mode or w.mode, threads=threads, flag_eps=flag_eps)

@@ -40,9 +40,10 @@
  *  - greedy argmax is taken on the raw logits, lowest index on ties;
  *  - a NaN or +inf logit, or a position whose logits are all -inf, makes the row
  *    invalid (NONFINITE); -inf elsewhere is an ordinary zero-probability token;
- *  - a decision whose threshold is within 1e-5 of its input (|u - ratio| < 1e-5 for a
- *    test, |C - t| < 1e-5 * W at an interior edge of the drawn token's CDF interval
- *    for a draw) is reported in flag_pos so comparisons can exclude it.
+ *  - a decision whose threshold is within eps of its input (|u - ratio| < eps for a
+ *    test, |C - t| < eps * W at an interior edge of the drawn token's CDF interval
+ *    for a draw; eps = 1e-5 unless the caller passes another) is reported in flag_pos
+ *    so comparisons can exclude it.
  */
 #include <float.h>
 #include <math.h>
@@ -179,7 +180,8 @@ out:
 /* ------------------------------------------------------------------------- */
 /* the inverse-CDF draw                                                        */
 /* ------------------------------------------------------------------------- */
-int64_t oracle_inverse_cdf(const double *w, int64_t V, double u, double *W_out, int *near_edge)
+int64_t oracle_inverse_cdf(const double *w, int64_t V, double u, double eps, double *W_out,
+                           int *near_edge)
 {
     double W = 0.0;
     for (int64_t v = 0; v < V; ++v)
@@ -207,8 +209,8 @@ int64_t oracle_inverse_cdf(const double *w, int64_t V, double u, double *W_out, 
     /* only interior edges are decision boundaries: the lower edge when some earlier
        token has weight, the upper edge when some later token has weight */
     if (near_edge)
-        *near_edge = (C_prev > 0 && fabs(C_prev - t) < 1e-5 * W) ||
-                     (C < W && fabs(C - t) < 1e-5 * W);
+        *near_edge = (C_prev > 0 && fabs(C_prev - t) < eps * W) ||
+                     (C < W && fabs(C - t) < eps * W);
     if (W_out)
         *W_out = W;
     return token;
@@ -237,8 +239,10 @@ int oracle_verify(const void *target, const void *draft, int dtype, int64_t V, i
                   int64_t n_target_rows, const int32_t *draft_tokens, const float *uniforms,
                   const float *temperature, const int32_t *gamma_per_row, int mode,
                   int32_t *n_accepted, int32_t *emitted, double *p_x, double *q_x,
-                  double *resid_mass, int32_t *row_status, int32_t *flag_pos, int nthreads)
+                  double *resid_mass, int32_t *row_status, int32_t *flag_pos, double flag_eps,
+                  int nthreads)
 {
+    const double eps = flag_eps > 0 ? flag_eps : 1e-5;
     if (!target || !gamma_per_row || !uniforms || !temperature || !n_accepted || !emitted ||
         V <= 0 || B < 0 || n_target_rows < 0)
         return -1;
@@ -397,7 +401,7 @@ int oracle_verify(const void *target, const void *draft, int dtype, int64_t V, i
                 }
                 if (!decided) {
                     double u = (double)uniforms[t0 + j];
-                    if (flag < 0 && fabs(u - ratio) < 1e-5)
+                    if (flag < 0 && fabs(u - ratio) < eps)
                         flag = j;
                     if (!(u < ratio)) {
                         K = j;
@@ -424,7 +428,7 @@ int oracle_verify(const void *target, const void *draft, int dtype, int64_t V, i
             }
             double W;
             int near = 0;
-            int64_t tok = oracle_inverse_cdf(w, V, (double)uniforms[t0 + g], &W, &near);
+            int64_t tok = oracle_inverse_cdf(w, V, (double)uniforms[t0 + g], eps, &W, &near);
             if (flag < 0 && near)
                 flag = g;
             for (int j = 0; j < K; ++j)

@@ -23,10 +23,12 @@ int oracle_softmax(const void *z, int dtype, int64_t V, double T, double *p);
 int64_t oracle_argmax(const void *z, int dtype, int64_t V);
 int oracle_position(const void *zt, const void *zd, int dtype, int64_t V, double T, double *p,
                     double *q, double *alpha, double *resid_mass, double *residual);
-int64_t oracle_inverse_cdf(const double *w, int64_t V, double u, double *W_out, int *near_edge);
+int64_t oracle_inverse_cdf(const double *w, int64_t V, double u, double eps, double *W_out,
+                           int *near_edge);
 int oracle_verify(const void *target, const void *draft, int dtype, int64_t V, int32_t B,
                   int64_t n_target_rows, const int32_t *draft_tokens, const float *uniforms,
                   const float *temperature, const int32_t *gamma_per_row, int mode,
                   int32_t *n_accepted, int32_t *emitted, double *p_x, double *q_x,
-                  double *resid_mass, int32_t *row_status, int32_t *flag_pos, int nthreads);
+                  double *resid_mass, int32_t *row_status, int32_t *flag_pos, double flag_eps,
+                  int nthreads);
 #endif

@@ -1,0 +1,215 @@
+"""spec_verify: the verification step of speculative sampling on AMD MI355X (gfx950).
+
+This module is a thin ctypes binding of the HIP library libspecverify.so: it
+marshals torch tensors into the C ABI declared in include/spec_verify.h (device
+pointers, sizes, the current HIP stream) and nothing else.  Every step of the
+computation runs in the library's kernels.  Importing this package fails loudly if
+the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+# sv_status
+SV_OK, SV_EINVAL, SV_EDTYPE, SV_EWORKSPACE, SV_EHIP = 0, -1, -2, -3, -4
+# sv_dtype / sv_mode
+SV_BF16, SV_F32 = 0, 1
+SV_SAMPLE, SV_GREEDY = 0, 1
+# row status bits
+ROW_BAD_TOKEN = 1
+ROW_Q_ZERO = 2
+ROW_NONFINITE = 4
+ROW_BAD_GAMMA = 8
+ROW_ZERO_RESID = 16
+ROW_BAD_TEMP = 32
+ROW_INVALID = ROW_BAD_TOKEN | ROW_NONFINITE | ROW_BAD_GAMMA | ROW_BAD_TEMP
+
+EXPORTED = ("spec_verify", "spec_verify_workspace_bytes", "spec_verify_strerror",
+            "spec_verify_set_profile_events", "spec_verify_version")
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"spec_verify failed ({status}): {message}")
+        self.status = status
+
+
+class Diag(ctypes.Structure):
+    _fields_ = [("p_x", ctypes.c_void_p), ("q_x", ctypes.c_void_p),
+                ("resid_mass", ctypes.c_void_p), ("row_status", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first (python -c "
+            "'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.spec_verify_workspace_bytes.argtypes = [i32, i64, i64, i32]
+    L.spec_verify_workspace_bytes.restype = sz
+    L.spec_verify.argtypes = [vp, vp, i32, i64, i32, i64, vp, vp, vp, vp, i32, i32, vp, vp,
+                              ctypes.POINTER(Diag), vp, sz, vp]
+    L.spec_verify.restype = ctypes.c_int
+    L.spec_verify_strerror.argtypes = [i32]
+    L.spec_verify_strerror.restype = ctypes.c_char_p
+    L.spec_verify_set_profile_events.argtypes = [vp, vp]
+    L.spec_verify_set_profile_events.restype = ctypes.c_int
+    L.spec_verify_version.argtypes = []
+    L.spec_verify_version.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+def strerror(status: int) -> str:
+    return lib.spec_verify_strerror(int(status)).decode()
+
+
+def version() -> str:
+    return lib.spec_verify_version().decode()
+
+
+def workspace_bytes(batch: int, n_target_rows: int, vocab: int, dtype: int) -> int:
+    return int(lib.spec_verify_workspace_bytes(batch, n_target_rows, vocab, dtype))
+
+
+def set_profile_events(start_event, stop_event) -> None:
+    """Raw hipEvent_t handles (ints) recorded around the statistics kernel of every
+    following call; (None, None) stops."""
+    rc = lib.spec_verify_set_profile_events(start_event, stop_event)
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, strerror(rc))
+
+
+_workspaces: dict = {}
+
+
+def _workspace(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
+    key = (device.index, stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtypes, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or t.device != device:
+        raise ValueError(f"{name} must be a tensor on {device}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature,
+                gamma_per_row=None, *, mode: str = "sample", diag: bool = False,
+                workspace: torch.Tensor | None = None, out=None):
+    """Verify a batch of drafted rows on the GPU.
+
+    target_logits  bf16/fp32 [n_target_rows, V] (packed) or [B, gamma+1, V] (dense)
+    draft_logits   same dtype, [n_draft_rows, V] or [B, gamma, V]; may be None in greedy mode
+    draft_tokens   int32 [n_draft_rows] (or [B, gamma])
+    uniforms       float32 [n_target_rows] (or [B, gamma+1]); slot gamma_i of a row drives
+                   the draw, the others the accept tests
+    temperature    float32 [B] tensor, or a Python float for every row
+    gamma_per_row  int32 [B] device tensor (ragged rows), an int (dense), or None (dense,
+                   gamma read from a 3-D target tensor)
+    mode           "sample" or "greedy"
+    Returns (n_accepted int32 [B], emitted int32 [n_target_rows]) and, with diag=True,
+    a third dict of p_x, q_x (float64 [n_draft_rows]), resid_mass (float64 [B]) and
+    row_status (int32 [B]).  Asynchronous on torch's current stream.
+    """
+    device = target_logits.device
+    if device.type != "cuda":
+        raise ValueError("target_logits must be a GPU tensor")
+    if target_logits.dtype == torch.bfloat16:
+        dtype = SV_BF16
+    elif target_logits.dtype == torch.float32:
+        dtype = SV_F32
+    else:
+        raise ValueError(f"unsupported logits dtype {target_logits.dtype}")
+    if mode not in ("sample", "greedy"):
+        raise ValueError("mode must be 'sample' or 'greedy'")
+    V = int(target_logits.shape[-1])
+    n_target_rows = target_logits.numel() // V if V else 0
+
+    gamma_t = None
+    if isinstance(gamma_per_row, torch.Tensor):
+        gamma_t = gamma_per_row
+        B = int(gamma_t.numel())
+        gamma_uniform = 0
+    else:
+        if gamma_per_row is None:
+            if target_logits.dim() != 3:
+                raise ValueError("pass gamma_per_row for a packed 2-D target tensor")
+            B, gp1 = int(target_logits.shape[0]), int(target_logits.shape[1])
+            gamma_uniform = gp1 - 1
+        else:
+            gamma_uniform = int(gamma_per_row)
+            B = n_target_rows // (gamma_uniform + 1)
+    if not isinstance(temperature, torch.Tensor):
+        temperature = torch.full((B,), float(temperature), dtype=torch.float32, device=device)
+
+    _check(target_logits, "target_logits", (target_logits.dtype,), device)
+    _check(draft_logits, "draft_logits", (target_logits.dtype,), device)
+    _check(draft_tokens, "draft_tokens", (torch.int32,), device)
+    _check(uniforms, "uniforms", (torch.float32,), device)
+    _check(temperature, "temperature", (torch.float32,), device)
+    _check(gamma_t, "gamma_per_row", (torch.int32,), device)
+    if temperature.numel() != B:
+        raise ValueError("temperature must have one entry per row")
+    if uniforms.numel() != n_target_rows:
+        raise ValueError("uniforms must have one entry per target row")
+    if draft_tokens is not None and draft_tokens.numel() != n_target_rows - B:
+        raise ValueError("draft_tokens must have one entry per draft row")
+
+    if out is None:
+        n_acc = torch.empty(B, dtype=torch.int32, device=device)
+        emitted = torch.empty(n_target_rows, dtype=torch.int32, device=device)
+    else:
+        n_acc, emitted = out
+        _check(n_acc, "n_accepted", (torch.int32,), device)
+        _check(emitted, "emitted", (torch.int32,), device)
+    dg = None
+    d = None
+    if diag:
+        n_draft = n_target_rows - B
+        dg = dict(p_x=torch.empty(n_draft, dtype=torch.float64, device=device),
+                  q_x=torch.empty(n_draft, dtype=torch.float64, device=device),
+                  resid_mass=torch.empty(B, dtype=torch.float64, device=device),
+                  row_status=torch.empty(B, dtype=torch.int32, device=device))
+        d = Diag(dg["p_x"].data_ptr(), dg["q_x"].data_ptr(), dg["resid_mass"].data_ptr(),
+                 dg["row_status"].data_ptr())
+
+    stream = torch.cuda.current_stream(device).cuda_stream
+    need = workspace_bytes(B, n_target_rows, V, dtype)
+    if workspace is None:
+        workspace = _workspace(device, stream, need)
+    elif workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
+
+    rc = lib.spec_verify(_ptr(target_logits), _ptr(draft_logits), dtype, V, B, n_target_rows,
+                         _ptr(draft_tokens), _ptr(uniforms), _ptr(temperature), _ptr(gamma_t),
+                         gamma_uniform, SV_SAMPLE if mode == "sample" else SV_GREEDY,
+                         _ptr(n_acc), _ptr(emitted), ctypes.byref(d) if d is not None else None,
+                         _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, strerror(rc))
+    if diag:
+        return n_acc, emitted, dg
+    return n_acc, emitted

@@ -1,0 +1,123 @@
+// Host side of the spec_verify C ABI: argument checks, workspace carving and the
+// kernel sequence on the caller's stream.  Declarations and the contract are in
+// include/spec_verify.h.
+#include <stdint.h>
+#include <string.h>
+
+#include "spec_verify.h"
+#include "sv_internal.h"
+
+namespace {
+
+hipEvent_t g_prof_start = nullptr;
+hipEvent_t g_prof_stop = nullptr;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" size_t spec_verify_workspace_bytes(int32_t batch, int64_t n_target_rows, int64_t vocab,
+                                              int32_t dtype)
+{
+    if (batch < 0 || vocab <= 0 || vocab > INT32_MAX || n_target_rows < batch ||
+        (dtype != SV_BF16 && dtype != SV_F32))
+        return 0;
+    if (2 * n_target_rows - batch > INT32_MAX) return 0;
+    return sv::make_layout(batch, n_target_rows, vocab).total;
+}
+
+extern "C" const char *spec_verify_strerror(int32_t status)
+{
+    switch (status) {
+    case SV_OK: return "ok";
+    case SV_EINVAL: return "invalid argument (pointer, size, mode or layout)";
+    case SV_EDTYPE: return "unsupported dtype (expected SV_BF16 or SV_F32)";
+    case SV_EWORKSPACE: return "workspace too small or not 256-byte aligned";
+    case SV_EHIP: return "HIP runtime error while enqueueing kernels";
+    default: return "unknown status";
+    }
+}
+
+extern "C" const char *spec_verify_version(void) { return "spec_verify 0.1 (gfx950)"; }
+
+extern "C" sv_status spec_verify_set_profile_events(void *start_event, void *stop_event)
+{
+    if ((start_event == nullptr) != (stop_event == nullptr)) return SV_EINVAL;
+    g_prof_start = static_cast<hipEvent_t>(start_event);
+    g_prof_stop = static_cast<hipEvent_t>(stop_event);
+    return SV_OK;
+}
+
+extern "C" sv_status spec_verify(const void *target_logits, const void *draft_logits, int32_t dtype,
+                                 int64_t vocab, int32_t batch, int64_t n_target_rows,
+                                 const int32_t *draft_tokens, const float *uniforms,
+                                 const float *temperature, const int32_t *gamma_per_row,
+                                 int32_t gamma_uniform, int32_t mode, int32_t *n_accepted,
+                                 int32_t *emitted_tokens, const sv_diag *diag, void *workspace,
+                                 size_t workspace_bytes, void *hip_stream)
+{
+    if (dtype != SV_BF16 && dtype != SV_F32) return SV_EDTYPE;
+    if (mode != SV_SAMPLE && mode != SV_GREEDY) return SV_EINVAL;
+    if (batch < 0 || vocab <= 0 || vocab > INT32_MAX || n_target_rows < batch) return SV_EINVAL;
+    if (2 * n_target_rows - batch > INT32_MAX) return SV_EINVAL;
+    if (gamma_per_row == nullptr) {
+        if (gamma_uniform < 0) return SV_EINVAL;
+        if (n_target_rows != (int64_t)batch * ((int64_t)gamma_uniform + 1)) return SV_EINVAL;
+    }
+    if (batch == 0) return n_target_rows == 0 ? SV_OK : SV_EINVAL;
+    const int64_t n_draft_rows = n_target_rows - batch;
+    if (!target_logits || !uniforms || !temperature || !n_accepted || !emitted_tokens || !workspace)
+        return SV_EINVAL;
+    if (n_draft_rows > 0 && (!draft_tokens || (mode == SV_SAMPLE && !draft_logits))) return SV_EINVAL;
+
+    const sv::Layout L = sv::make_layout(batch, n_target_rows, vocab);
+    if (workspace_bytes < L.total || ((uintptr_t)workspace & 255u) != 0) return SV_EWORKSPACE;
+
+    char *ws = static_cast<char *>(workspace);
+    sv::Params P{};
+    P.target = target_logits;
+    P.draft = draft_logits;
+    P.V = vocab;
+    P.B = batch;
+    P.mode = mode;
+    P.nT = n_target_rows;
+    P.nD = n_draft_rows;
+    P.nvec = 2 * n_target_rows - batch;
+    P.tokens = draft_tokens;
+    P.uniforms = uniforms;
+    P.temperature = temperature;
+    P.gamma = gamma_per_row;
+    P.gamma_uniform = gamma_per_row ? 0 : gamma_uniform;
+    P.n_accepted = n_accepted;
+    P.emitted = emitted_tokens;
+    if (diag) {
+        P.p_x = diag->p_x;
+        P.q_x = diag->q_x;
+        P.resid = diag->resid_mass;
+        P.row_status = diag->row_status;
+    }
+    P.hdr = reinterpret_cast<sv::Header *>(ws + L.hdr);
+    P.rows = reinterpret_cast<sv::RowInfo *>(ws + L.rows);
+    P.vec_row = reinterpret_cast<int32_t *>(ws + L.vec_row);
+    P.parts = reinterpret_cast<sv::Partial *>(ws + L.parts);
+    P.draws = reinterpret_cast<sv::RowDraw *>(ws + L.draws);
+    P.tiles = reinterpret_cast<sv::Sum2 *>(ws + L.tiles);
+    P.segs = reinterpret_cast<sv::Sum2 *>(ws + L.segs);
+    P.counters = reinterpret_cast<int32_t *>(ws + L.counters);
+    P.geo = sv::make_geometry(batch, n_target_rows, vocab);
+
+    // 16-byte vector loads need every logit row to start 16-byte aligned
+    const int64_t esz = dtype == SV_BF16 ? 2 : 4;
+    const bool aligned = (vocab * esz) % 16 == 0 && aligned16(target_logits) &&
+                         (n_draft_rows == 0 || draft_logits == nullptr || aligned16(draft_logits));
+
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = hipSuccess;
+    if (gamma_per_row) e = sv::launch_prepare(P, s);
+    if (e == hipSuccess && g_prof_start) e = hipEventRecord(g_prof_start, s);
+    if (e == hipSuccess) e = sv::launch_stats(P, s, dtype, aligned);
+    if (e == hipSuccess && g_prof_stop) e = hipEventRecord(g_prof_stop, s);
+    if (e == hipSuccess) e = sv::launch_scan(P, s, dtype);
+    if (e == hipSuccess && mode == SV_SAMPLE) e = sv::launch_draw(P, s, dtype, aligned);
+    return e == hipSuccess ? SV_OK : SV_EHIP;
+}

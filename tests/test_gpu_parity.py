@@ -1,0 +1,201 @@
+"""HIP path against the CPU oracle, through the C ABI, on seeded synthetic inputs."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def H():
+    import gpu_harness
+    return gpu_harness
+
+
+def _parity(H, w, mode=None, dense=False, strict_eps=1e-7):
+    _say(f"[case] {w.name} mode={mode or w.mode} dense={dense} B={w.batch} V={w.vocab}")
+    gpu = H.run_gpu(w, mode=mode, dense=dense)
+    ref = oracle.verify_workload(w, mode=mode)
+    rep = H.compare(w, gpu, ref, mode=mode)
+    if (mode or w.mode) == "sample":
+        strict = oracle.verify_workload(w, mode=mode, flag_eps=strict_eps)
+        rep["strict_checked_mismatched"] = H.check_strict(w, gpu, strict)
+    _say(f"[ok] {rep}")
+    return gpu, ref, rep
+
+
+# --------------------------------------------------------------------------- #
+# toy workload: bit parity plus the statistics of 10,000 rounds
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("shared", [False, True], ids=["per_position", "shared_position"])
+def test_toy_parity_and_statistics(H, shared):
+    import stats_checks
+    w = workloads.toy(seed=1 if not shared else 2, shared_position=shared)
+    gpu, ref, rep = _parity(H, w)
+    stats_checks.check_emitted_distribution(w, gpu["n_accepted"], gpu["emitted"])
+    stats_checks.check_accept_counts(w, gpu["n_accepted"])
+
+
+# --------------------------------------------------------------------------- #
+# small shapes: ragged, unaligned, multi-segment, degenerate vocabularies
+# --------------------------------------------------------------------------- #
+SMALL = [
+    dict(seed=21, batch=9, vocab=4096, dtype="bf16", gamma=[3, 0, 5, 2, 4, 1, 7, 0, 2],
+         temperature=[0.8, 1.0, 1.2, 0.7, 1.0, 0.0, 1.5, -1.0, 0.6]),
+    dict(seed=22, batch=7, vocab=997, dtype="bf16", gamma=[1, 2, 0, 6, 3, 3, 1]),
+    dict(seed=23, batch=5, vocab=20000, dtype="bf16", gamma=[4, 4, 4, 4, 4], n_boost=5),
+    dict(seed=24, batch=6, vocab=1024, dtype="f32", gamma=[2, 0, 3, 5, 1, 4],
+         temperature=[0.9, 1.1, 0.5, 2.0, 1.0, 0.75]),
+    dict(seed=25, batch=6, vocab=1001, dtype="f32", gamma=[3, 1, 0, 2, 6, 2]),
+    dict(seed=26, batch=4, vocab=1004, dtype="f32", gamma=[2, 2, 2, 2]),
+    dict(seed=27, batch=4, vocab=1, dtype="f32", gamma=[0, 1, 3, 2]),
+    dict(seed=28, batch=8, vocab=8, dtype="bf16", gamma=[1, 2, 3, 4, 5, 6, 7, 0]),
+    dict(seed=29, batch=5, vocab=513, dtype="bf16", gamma=[3, 3, 0, 1, 2]),
+    dict(seed=30, batch=3, vocab=40, dtype="f32", gamma=[100, 70, 0], noise=0.05),
+    dict(seed=31, batch=33, vocab=65536, dtype="bf16", gamma=[2] * 33, noise=0.3),
+    dict(seed=32, batch=4, vocab=300000, dtype="f32", gamma=[1, 3, 0, 2], sigma=4.0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_small_sample(H, case):
+    kw = dict(SMALL[case])
+    _parity(H, workloads.small(**kw))
+
+
+@pytest.mark.parametrize("case", [0, 1, 3, 4, 7, 9])
+def test_small_greedy(H, case):
+    kw = dict(SMALL[case])
+    w = workloads.small(**{**kw, "mode": "greedy"})
+    _parity(H, w, mode="greedy")
+
+
+def test_greedy_ties(H):
+    """Integer-valued bf16 logits tie everywhere: the lowest index must win."""
+    rng = np.random.default_rng(3)
+    B, g, V = 16, 4, 3000
+    gam = np.full(B, g, np.int32)
+    tgt = rng.integers(-3, 4, (B * (g + 1), V)).astype(np.float32)
+    am = np.argmax(tgt, axis=1).reshape(B, g + 1)
+    tok = np.where(rng.random((B, g)) < 0.8, am[:, :g], 0).astype(np.int32).reshape(-1)
+    w = workloads.Workload("ties", "bf16", V, gam, workloads.to_bf16_bits(tgt),
+                           workloads.to_bf16_bits(np.zeros((B * g, V), np.float32)), tok,
+                           np.zeros(B * (g + 1), np.float32), np.ones(B, np.float32), mode="greedy")
+    _parity(H, w, mode="greedy")
+
+
+def test_dense_equals_ragged(H):
+    w = workloads.small(seed=41, batch=12, vocab=8192, dtype="bf16", gamma=3)
+    a = H.run_gpu(w, dense=True)
+    b = H.run_gpu(w, dense=False)
+    for k in a:
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+
+
+def test_deterministic(H):
+    w = workloads.small(seed=42, batch=16, vocab=50000, dtype="bf16", gamma=4, n_boost=5)
+    d = H.to_device(w)
+    a = H.run_gpu(w, tensors=d)
+    b = H.run_gpu(w, tensors=d)
+    for k in a:
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+
+
+# --------------------------------------------------------------------------- #
+# status rules and special inputs
+# --------------------------------------------------------------------------- #
+def _edit(w, **kw):
+    return workloads.Workload(**{**w.__dict__, **kw})
+
+
+def test_status_rules(H):
+    base = workloads.small(seed=51, batch=10, vocab=2048, dtype="f32", gamma=3)
+    tgt = base.target.copy()
+    drf = base.draft.copy()
+    tok = base.draft_tokens.copy()
+    T = base.temperature.copy()
+    drf[1 * 3 + 1, 7] = np.nan                 # row 1: NaN in a draft position
+    tgt[2 * 4 + 3, 100] = np.inf               # row 2: +inf at the bonus position
+    tgt[3 * 4 + 0, :] = -np.inf                # row 3: a position with all -inf
+    tgt[4 * 4 + 2, :1000] = -np.inf            # row 4: masked tokens, still valid
+    drf[4 * 3 + 1, 1000:] = -np.inf
+    tok[5 * 3 + 2] = 2048                      # row 5: token out of range
+    tok[6 * 3 + 0] = -1                        # row 6: negative token
+    T[7] = np.nan                              # row 7: NaN temperature
+    T[8] = 1e-39                               # row 8: subnormal temperature
+    T[9] = 0.0                                 # row 9: greedy row
+    w = _edit(base, target=tgt, draft=drf, draft_tokens=tok, temperature=T)
+    gpu, ref, rep = _parity(H, w)
+    st = gpu["row_status"]
+    assert st[1] & oracle.NONFINITE and st[2] & oracle.NONFINITE and st[3] & oracle.NONFINITE
+    assert not st[4] & oracle.INVALID_MASK
+    assert st[5] & oracle.BAD_TOKEN and st[6] & oracle.BAD_TOKEN
+    assert st[7] & oracle.BAD_TEMP and st[8] & oracle.BAD_TEMP
+    assert st[9] == 0 and gpu["n_accepted"][9] >= 0
+    # greedy mode never reads draft logits: the NaN draft row is valid there
+    gg, rg, _ = _parity(H, w, mode="greedy")
+    assert not gg["row_status"][1] & oracle.INVALID_MASK
+
+
+def test_q_zero_and_zero_residual(H):
+    """q(x) = 0 with p(x) > 0 keeps the draft (ratio 1); q(x) = p(x) = 0 with p = q
+    elsewhere rejects with zero residual mass and draws from p."""
+    V = 16
+    z = np.zeros((2, V), np.float32)
+    tgt1 = z.copy()
+    drf1 = z[:1].copy()
+    drf1[0, 5] = -np.inf
+    tgt2 = z.copy()
+    tgt2[:, 9] = -np.inf
+    drf2 = z[:1].copy()
+    drf2[0, 9] = -np.inf
+    w = workloads.Workload("qzero", "f32", V, np.array([1, 1], np.int32), np.concatenate([tgt1, tgt2]),
+                           np.concatenate([drf1, drf2]), np.array([5, 9], np.int32),
+                           np.array([0.999, 0.3, 0.2, 0.55], np.float32), np.ones(2, np.float32))
+    gpu, ref, rep = _parity(H, w)
+    assert gpu["row_status"][0] == oracle.Q_ZERO and gpu["n_accepted"][0] == 1
+    assert gpu["row_status"][1] == oracle.Q_ZERO | oracle.ZERO_RESID and gpu["n_accepted"][1] == 0
+
+
+def test_bad_gamma(H):
+    w = workloads.small(seed=52, batch=6, vocab=512, dtype="bf16", gamma=[2, 1, 3, 0, 2, 1])
+    d = H.to_device(w)
+    import torch
+    import speculative_sampling_verify_02_amd as sv
+    for bad in ([2, 1, 3, 0, 2, 2], [2, 1, -1, 0, 2, 5]):
+        g = torch.tensor(bad, dtype=torch.int32, device=d["target"].device)
+        n, e, dg = sv.spec_verify(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temperature"],
+                                  g, diag=True)
+        torch.cuda.synchronize()
+        assert (n.cpu().numpy() == -1).all() and (e.cpu().numpy() == -1).all()
+        assert (dg["row_status"].cpu().numpy() == oracle.BAD_GAMMA).all()
+
+
+# --------------------------------------------------------------------------- #
+# the five configurations at full size
+# --------------------------------------------------------------------------- #
+def test_c2_full(H):
+    _parity(H, workloads.c2())
+
+
+@pytest.mark.parametrize("mode", ["sample", "greedy"])
+def test_c3_full(H, mode):
+    _parity(H, workloads.c3(mode=mode), mode=mode, dense=True)
+
+
+def test_c4_full(H):
+    _parity(H, workloads.c4(), dense=True)
+
+
+def test_c5_full(H):
+    _parity(H, workloads.c5())

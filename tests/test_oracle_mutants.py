@@ -21,7 +21,8 @@ MUTANTS = {
     "bonus_wrong_position": (
         "oracle_softmax(vector_ptr(target, dtype, t0 + K, V), dtype, V, T, P);",
         "oracle_softmax(vector_ptr(target, dtype, t0 + (K == g && K > 0 ? K - 1 : K), V), dtype, V, T, P);"),
-    "draw_reuses_test_uniform": ("(double)uniforms[t0 + g], &W, &near)", "(double)uniforms[t0 + K], &W, &near)"),
+    "draw_reuses_test_uniform": ("(double)uniforms[t0 + g], eps, &W, &near)",
+                                 "(double)uniforms[t0 + K], eps, &W, &near)"),
     "q_sum_without_temperature": ("vector_max_sumexp(zd, dtype, V, T, &md, &Sd);",
                                   "vector_max_sumexp(zd, dtype, V, 1.0, &md, &Sd);"),
     "sumexp_without_temperature": ("S += exp((logit_at(z, dtype, v) - m) / T);",
@@ -33,7 +34,7 @@ MUTANTS = {
     "cdf_nonstrict": ("        if (C > t) {", "        if (C >= t) {"),
     "draw_unnormalized": ("    double t = u * W;", "    double t = u;"),
     "alpha_with_max": ("a += fmin(pp[v], qq[v]);", "a += fmax(pp[v], qq[v]);"),
-    "flag_threshold_too_wide": ("if (flag < 0 && fabs(u - ratio) < 1e-5)", "if (flag < 0 && fabs(u - ratio) < 1e-3)"),
+    "flag_threshold_too_wide": ("if (flag < 0 && fabs(u - ratio) < eps)", "if (flag < 0 && fabs(u - ratio) < 100 * eps)"),
     "no_zero_residual_fallback": ("                if (W == 0.0) {", "                if (W < 0.0) {"),
     "neg_inf_is_nonfinite": ("if (isnan(x) || x == INFINITY)", "if (isnan(x) || isinf(x))"),
 }
