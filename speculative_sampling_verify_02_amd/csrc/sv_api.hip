@@ -73,6 +73,11 @@ extern "C" sv_status spec_verify(const void *target_logits, const void *draft_lo
     const sv::Layout L = sv::make_layout(batch, n_target_rows, vocab);
     if (workspace_bytes < L.total || ((uintptr_t)workspace & 255u) != 0) return SV_EWORKSPACE;
 
+    // 16-byte vector loads need every logit row to start 16-byte aligned
+    const int64_t esz = dtype == SV_BF16 ? 2 : 4;
+    const bool aligned = (vocab * esz) % 16 == 0 && aligned16(target_logits) &&
+                         (n_draft_rows == 0 || draft_logits == nullptr || aligned16(draft_logits));
+
     char *ws = static_cast<char *>(workspace);
     sv::Params P{};
     P.target = target_logits;
@@ -82,7 +87,6 @@ extern "C" sv_status spec_verify(const void *target_logits, const void *draft_lo
     P.mode = mode;
     P.nT = n_target_rows;
     P.nD = n_draft_rows;
-    P.nvec = 2 * n_target_rows - batch;
     P.tokens = draft_tokens;
     P.uniforms = uniforms;
     P.temperature = temperature;
@@ -100,16 +104,10 @@ extern "C" sv_status spec_verify(const void *target_logits, const void *draft_lo
     P.rows = reinterpret_cast<sv::RowInfo *>(ws + L.rows);
     P.vec_row = reinterpret_cast<int32_t *>(ws + L.vec_row);
     P.parts = reinterpret_cast<sv::Partial *>(ws + L.parts);
+    P.zx = reinterpret_cast<float *>(ws + L.zx);
     P.draws = reinterpret_cast<sv::RowDraw *>(ws + L.draws);
     P.tiles = reinterpret_cast<sv::Sum2 *>(ws + L.tiles);
-    P.segs = reinterpret_cast<sv::Sum2 *>(ws + L.segs);
-    P.counters = reinterpret_cast<int32_t *>(ws + L.counters);
-    P.geo = sv::make_geometry(batch, n_target_rows, vocab);
-
-    // 16-byte vector loads need every logit row to start 16-byte aligned
-    const int64_t esz = dtype == SV_BF16 ? 2 : 4;
-    const bool aligned = (vocab * esz) % 16 == 0 && aligned16(target_logits) &&
-                         (n_draft_rows == 0 || draft_logits == nullptr || aligned16(draft_logits));
+    P.geo = sv::make_geometry(batch, n_target_rows, vocab, mode, sv::stats_grid_cap(dtype, aligned));
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     hipError_t e = hipSuccess;

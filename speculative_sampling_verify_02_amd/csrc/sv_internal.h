@@ -13,14 +13,15 @@ namespace sv {
 // ---------------------------------------------------------------------------
 constexpr int kBlock = 256;              // threads per workgroup (4 wave64)
 constexpr int kWaves = kBlock / 64;
-constexpr int kUnitElems = 8;            // logits a lane handles per "unit"
-constexpr int kTileUnits = 64;           // pass-2 tile: one unit per lane of a wave
+constexpr int kUnitElems = 8;            // logits a lane loads at once (one 16-byte bf16 load)
+constexpr int kUnroll = 4;               // units in flight per thread in the streaming pass
+constexpr int kTileUnits = 64;           // draw tile: one unit per lane of a wave
 constexpr int kTileElems = kTileUnits * kUnitElems;   // 512 logits
-constexpr int kTilesPerSeg = 16;         // pass-2 segment: 16 tiles = 8192 logits
-constexpr int kUnroll = 4;               // units per thread per pass-1 iteration
+constexpr int kTilesPerWave = 4;         // draw: tiles a wave sums with all loads in flight
+constexpr int kTilesPerDrawWg = kTilesPerWave * kWaves;   // 16 tiles = 8192 logits
 constexpr int kXcds = 8;                 // MI355X: 8 XCDs, workgroups dealt round-robin
-constexpr int64_t kTargetWorkgroups = 2048;   // pass-1 grid goal (8 per CU)
-constexpr int64_t kMinSegUnits = 512;    // pass-1 segment floor (2 units per thread)
+constexpr int kMaxStatsGrid = 8192;      // cap of the streaming-pass grid
+constexpr int64_t kMinUnitsPerWg = 2048; // 8 units per thread at least
 constexpr double kLog2e = 1.44269504088896340736;
 
 // row status bits (mirror SV_ROW_* of the public header)
@@ -49,18 +50,18 @@ struct RowInfo {           // packed offsets of one row (ragged batches)
     int32_t t_off, d_off, gamma, pad;
 };
 
-struct Partial {           // pass-1 result of one (vector, segment)
-    float m;               // sampling: max logit; greedy: max logit
+struct Partial {           // streaming-pass result of one (workgroup, vector) overlap
+    float m;               // max logit (-inf: no finite logit)
     int32_t idx;           // greedy: first index of the max (INT32_MAX: none)
     double s;              // sampling: sum of 2^((z - m) c); greedy: 0, or NaN if a NaN was seen
 };
 
-struct Sum2 {              // pass-2 sums over a tile or a segment
+struct Sum2 {              // draw sums over one tile
     double w;              // draw weights (residual or bonus)
     double p;              // target probabilities (zero-residual fallback)
 };
 
-struct RowDraw {           // what pass 2 needs about one row
+struct RowDraw {           // what the draw needs about one row
     int32_t kind;          // DRAW_NONE / DRAW_RESIDUAL / DRAW_BONUS
     int32_t K;
     int32_t t_row, d_row;  // logit rows of target / draft at position K
@@ -68,53 +69,62 @@ struct RowDraw {           // what pass 2 needs about one row
     float u;               // the draw's uniform
     int32_t t_slot;        // emitted slot t_off + K
     double S_t, S_d;       // sums of 2^((z - m) c) at K
+    float T;
+    int32_t pad;
 };
 
+// Streaming pass: the vectors it reads (all target and draft positions in sampling
+// mode, target positions only in greedy mode) laid end to end as one range of
+// units, cut into G equal contiguous pieces, one per workgroup.
 struct Geometry {
     int64_t nunits;        // ceil(V / 8)
-    int64_t seg_units;     // pass-1 units per segment
-    int32_t nseg;          // pass-1 segments per vector
-    int32_t nseg2;         // pass-2 segments per row
-    int64_t ntiles;        // pass-2 tiles per vector
+    int64_t nvec;          // vectors streamed
+    int64_t total_units;   // nvec * nunits
+    int64_t R;             // units per workgroup
+    int32_t G;             // workgroups
+    int32_t ntiles;        // draw tiles per vector
+    int32_t ndraw;         // draw workgroups per row
+    int32_t pad;
 };
 
 struct Layout {
-    size_t hdr, rows, vec_row, parts, draws, tiles, segs, counters, total;
+    size_t hdr, rows, vec_row, parts, zx, draws, tiles, total;
 };
 
-// Pass-1 and pass-2 partitioning; depends only on the shape.
-inline Geometry make_geometry(int32_t B, int64_t nT, int64_t V)
+inline Geometry make_geometry(int32_t B, int64_t nT, int64_t V, int32_t mode, int32_t grid_cap)
 {
     Geometry g{};
     g.nunits = (V + kUnitElems - 1) / kUnitElems;
-    const int64_t nvec = 2 * nT - B;
-    int64_t nseg = nvec > 0 ? (kTargetWorkgroups + nvec - 1) / nvec : 1;
-    int64_t max_seg = (g.nunits + kMinSegUnits - 1) / kMinSegUnits;
-    if (nseg > max_seg) nseg = max_seg;
-    if (nseg < 1) nseg = 1;
-    g.seg_units = (g.nunits + nseg - 1) / nseg;
-    g.nseg = (int32_t)((g.nunits + g.seg_units - 1) / g.seg_units);
-    g.ntiles = (g.nunits + kTileUnits - 1) / kTileUnits;
-    g.nseg2 = (int32_t)((g.ntiles + kTilesPerSeg - 1) / kTilesPerSeg);
+    g.nvec = mode == 1 ? nT : 2 * nT - B;
+    g.total_units = g.nvec * g.nunits;
+    int64_t G = (g.total_units + kMinUnitsPerWg - 1) / kMinUnitsPerWg;
+    if (G > grid_cap) G = grid_cap;
+    if (G > kMaxStatsGrid) G = kMaxStatsGrid;
+    if (G < 1) G = 1;
+    g.R = (g.total_units + G - 1) / G;
+    if (g.R < 1) g.R = 1;
+    g.G = (int32_t)((g.total_units + g.R - 1) / g.R);
+    g.ntiles = (int32_t)((g.nunits + kTileUnits - 1) / kTileUnits);
+    g.ndraw = (g.ntiles + kTilesPerDrawWg - 1) / kTilesPerDrawWg;
     return g;
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Sized for the largest grid and for sampling mode, so it depends only on the shape.
 inline Layout make_layout(int32_t B, int64_t nT, int64_t V)
 {
-    const Geometry g = make_geometry(B, nT, V);
     const int64_t nvec = 2 * nT - B;
+    const int64_t ntiles = ((V + kUnitElems - 1) / kUnitElems + kTileUnits - 1) / kTileUnits;
     Layout L{};
     size_t off = 0;
     L.hdr = off;      off += align256(sizeof(Header));
     L.rows = off;     off += align256(sizeof(RowInfo) * (size_t)B);
     L.vec_row = off;  off += align256(sizeof(int32_t) * (size_t)nvec);
-    L.parts = off;    off += align256(sizeof(Partial) * (size_t)nvec * (size_t)g.nseg);
+    L.parts = off;    off += align256(sizeof(Partial) * ((size_t)kMaxStatsGrid + (size_t)nvec));
+    L.zx = off;       off += align256(sizeof(float) * 2 * (size_t)(nT - B));
     L.draws = off;    off += align256(sizeof(RowDraw) * (size_t)B);
-    L.tiles = off;    off += align256(sizeof(Sum2) * (size_t)B * (size_t)g.ntiles);
-    L.segs = off;     off += align256(sizeof(Sum2) * (size_t)B * (size_t)g.nseg2);
-    L.counters = off; off += align256(sizeof(int32_t) * (size_t)B);
+    L.tiles = off;    off += align256(sizeof(Sum2) * (size_t)B * (size_t)ntiles);
     L.total = off;
     return L;
 }
@@ -128,7 +138,7 @@ struct Params {
     int64_t V;
     int32_t B;
     int32_t mode;          // SV_SAMPLE / SV_GREEDY
-    int64_t nT, nD, nvec;
+    int64_t nT, nD;
     const int32_t *tokens;
     const float *uniforms;
     const float *temperature;
@@ -143,10 +153,9 @@ struct Params {
     RowInfo *rows;
     int32_t *vec_row;
     Partial *parts;
+    float *zx;             // [2 nD]: target then draft logit at each draft token
     RowDraw *draws;
     Sum2 *tiles;
-    Sum2 *segs;
-    int32_t *counters;
     Geometry geo;
 };
 
@@ -168,6 +177,13 @@ __device__ __forceinline__ RowGeom row_geom(const Params &P, int32_t row)
     return RowGeom{ri.t_off, ri.d_off, ri.gamma};
 }
 
+// First streamed vector ("slot") of a row: sampling streams the row's gamma+1 target
+// positions then its gamma draft positions; greedy streams target positions only.
+__device__ __forceinline__ int64_t row_slot0(const Params &P, const RowGeom &G)
+{
+    return P.mode == 1 ? G.t_off : G.t_off + G.d_off;
+}
+
 // Sampling, greedy, or an unusable temperature for a sampling row.
 __device__ __forceinline__ int32_t row_mode(int32_t mode, float T)
 {
@@ -179,8 +195,8 @@ __device__ __forceinline__ int32_t row_mode(int32_t mode, float T)
 }
 
 // exp((z - m) / T) = 2^((z - m) c) with c = log2(e) / T, split as c_hi + c_lo:
-// c_hi is c rounded down to fp32, c_lo >= FLT_MIN > 0 the fp32 remainder, so an
-// argument built from them carries c to ~2^-48 and -inf logits stay -inf.
+// c_hi is c rounded down to fp32 and c_lo >= FLT_MIN > 0 the fp32 remainder, so
+// arguments built from both carry c to ~2^-48 and -inf logits stay -inf.
 struct TempConst {
     float c_hi, c_lo;
     double c_eff;          // c_hi + c_lo exactly
@@ -198,50 +214,97 @@ __device__ __forceinline__ TempConst temp_const(float T)
     return tc;
 }
 
-// Logits whose scaled reference |m c_hi| is below this use the one-rounding
-// argument fma(z, c_lo, fma(z, c_hi, -M)); larger ones use (z - m) first.
-constexpr float kFastRef = 1073741824.0f;   // 2^30
+// References at or above this magnitude take the (z - m) route instead of the
+// integer reference (fp32 integers are exact below 2^24; the gap leaves room).
+constexpr float kFastRef = 1048576.0f;   // 2^20
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 2^x in fp64: x = n + f with n = rint(x), |f| <= 1/2, and 2^f from its Taylor series
+// in f ln 2 to degree 13 (truncation below 5e-18 relative); NaN propagates, very
+// negative x (and -inf) give 0.
+__host__ __device__ __forceinline__ double exp2_f64(double x)
+{
+    if (x < -1100.0) x = -1100.0;
+    if (x > 1100.0) x = 1100.0;
+    const double n = rint(x);
+    const double f = x - n;
+    double p = 0x1.816193166d0f9p-40;
+    p = fma(p, f, 0x1.c3bd650fc2986p-36);
+    p = fma(p, f, 0x1.e8cac7351bb25p-32);
+    p = fma(p, f, 0x1.e4cf5158b8ecap-28);
+    p = fma(p, f, 0x1.b5253d395e7c4p-24);
+    p = fma(p, f, 0x1.62c0223a5c824p-20);
+    p = fma(p, f, 0x1.ffcbfc588b0c7p-17);
+    p = fma(p, f, 0x1.430912f86c787p-13);
+    p = fma(p, f, 0x1.5d87fe78a6731p-10);
+    p = fma(p, f, 0x1.3b2ab6fba4e77p-7);
+    p = fma(p, f, 0x1.c6b08d704a0c0p-5);
+    p = fma(p, f, 0x1.ebfbdff82c58fp-3);
+    p = fma(p, f, 0x1.62e42fefa39efp-1);
+    p = fma(p, f, 1.0);
+    return ldexp(p, (int)n);
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Load unit `unit` (8 logits) of a vector of V logits; logits past V read as -inf.
-// ALIGNED: the vector starts 16-byte aligned and V is a multiple of the vector width.
+// Raw storage of one unit (8 logits): one 16-byte load for bf16, two for fp32.
+template <int DT> struct RawUnit;
+template <> struct RawUnit<0> { uint4 a; };
+template <> struct RawUnit<1> { float4 a, b; };
+
+// ALIGNED: the vector starts 16-byte aligned and holds a whole number of 16-byte
+// groups; otherwise logits are read one by one.  Logits past V read as -inf.
 template <int DT, bool ALIGNED>
-__device__ __forceinline__ void load_unit(const void *base, int64_t unit, int64_t V, float *x)
+__device__ __forceinline__ RawUnit<DT> load_raw(const void *base, int64_t unit, int64_t V)
 {
+    RawUnit<DT> r;
     const int64_t e0 = unit * kUnitElems;
     if constexpr (DT == 0) {
         const uint16_t *p = static_cast<const uint16_t *>(base);
         if constexpr (ALIGNED) {
-            const uint4 v = reinterpret_cast<const uint4 *>(p)[unit];
-            x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
-            x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
-            x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
-            x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+            r.a = reinterpret_cast<const uint4 *>(p)[unit];
         } else {
+            uint32_t w[4];
 #pragma unroll
-            for (int e = 0; e < kUnitElems; ++e)
-                x[e] = (e0 + e < V) ? __uint_as_float((uint32_t)p[e0 + e] << 16) : -INFINITY;
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t lo = (e0 + 2 * k < V) ? (uint32_t)p[e0 + 2 * k] : 0xff80u;
+                const uint32_t hi = (e0 + 2 * k + 1 < V) ? (uint32_t)p[e0 + 2 * k + 1] : 0xff80u;
+                w[k] = lo | (hi << 16);
+            }
+            r.a = make_uint4(w[0], w[1], w[2], w[3]);
         }
     } else {
         const float *p = static_cast<const float *>(base);
         if constexpr (ALIGNED) {
-            const float4 a = reinterpret_cast<const float4 *>(p)[2 * unit];
-            x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-            if (e0 + 4 < V) {
-                const float4 b = reinterpret_cast<const float4 *>(p)[2 * unit + 1];
-                x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-            } else {
-                x[4] = x[5] = x[6] = x[7] = -INFINITY;
-            }
+            r.a = reinterpret_cast<const float4 *>(p)[2 * unit];
+            if (e0 + 4 < V)
+                r.b = reinterpret_cast<const float4 *>(p)[2 * unit + 1];
+            else
+                r.b = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         } else {
+            float v[8];
 #pragma unroll
-            for (int e = 0; e < kUnitElems; ++e)
-                x[e] = (e0 + e < V) ? p[e0 + e] : -INFINITY;
+            for (int e = 0; e < 8; ++e) v[e] = (e0 + e < V) ? p[e0 + e] : -INFINITY;
+            r.a = make_float4(v[0], v[1], v[2], v[3]);
+            r.b = make_float4(v[4], v[5], v[6], v[7]);
         }
+    }
+    return r;
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack(const RawUnit<DT> &r, float *x)
+{
+    if constexpr (DT == 0) {
+        x[0] = bf16_lo(r.a.x); x[1] = bf16_hi(r.a.x);
+        x[2] = bf16_lo(r.a.y); x[3] = bf16_hi(r.a.y);
+        x[4] = bf16_lo(r.a.z); x[5] = bf16_hi(r.a.z);
+        x[6] = bf16_lo(r.a.w); x[7] = bf16_hi(r.a.w);
+    } else {
+        x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+        x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
     }
 }
 
@@ -296,6 +359,7 @@ __device__ __forceinline__ double wave_inclusive_sum(double v, int lane)
 }
 
 // launchers (sv_kernels.hip)
+int32_t stats_grid_cap(int dtype, bool aligned);
 hipError_t launch_prepare(const Params &P, hipStream_t s);
 hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned);
 hipError_t launch_scan(const Params &P, hipStream_t s, int dtype);

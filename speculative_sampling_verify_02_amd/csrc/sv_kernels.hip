@@ -1,30 +1,36 @@
 // HIP kernels of the speculative-sampling verification step for gfx950.
 //
-// Pass 1 (stats_kernel) streams every logit once: for every (row, position) vector
-// it produces the maximum and the sum of exp((z - m)/T) (sampling rows) or the first
-// argmax (greedy rows), split over a few segments per vector so the grid has
-// thousands of workgroups.  The temperature softmax it summarizes is the softened
-// output of brunomaga.github.io "inference-distillation-speculative-decoding",
-// section "Knowledge distillation", applied with one T to both models (rayaq.ca
-// "Speculative decoding", section "Why the output is exactly the target's").
+// stats_kernel streams every logit once.  The vectors it reads (the gamma+1 target
+// and gamma draft positions of every row, or only target positions in greedy mode)
+// are laid end to end and cut into equal contiguous pieces, one per workgroup, so
+// every workgroup does the same work and the grid ends together.  For each
+// (workgroup, vector) overlap it writes the maximum and the sum of exp((z - m)/T)
+// (sampling rows) or the first argmax (greedy rows).  The temperature softmax these
+// summarize is the softened output of brunomaga.github.io "inference-distillation-
+// speculative-decoding", section "Knowledge distillation", with one T for both
+// models (rayaq.ca "Speculative decoding", section "Why the output is exactly the
+// target's").
 //
-// The accept scan (scan_kernel) walks each row left to right, keeping x_j while
-// u_j < min(1, p_j(x_j)/q_j(x_j)) (rayaq.ca "Speculative decoding", section "One
-// round", step 3), or while x_j equals the argmax in greedy mode (section "The
-// greedy case").
+// scan_kernel gives each row one wave: it merges the pieces, computes p(x_j) and
+// q(x_j), and keeps x_j while u_j < min(1, p_j(x_j)/q_j(x_j)) (rayaq.ca
+// "Speculative decoding", section "One round", step 3), or while x_j equals the
+// argmax in greedy mode (section "The greedy case").
 //
-// Pass 2 (draw_kernel) re-reads only the position K of each sampling row: the
-// residual max(0, p - q) after a rejection (step 4) or p for the bonus token
-// (step 5), sums it per 512-logit tile and per 8192-logit segment, and the last
-// workgroup of the row walks segment sums, tile sums and one tile to the inverse-CDF
-// token.  All workgroups of a row run on one XCD so that final tile re-read hits
-// that XCD's L2.
+// draw_tiles_kernel re-reads only position K of each sampling row and sums the draw
+// weights per 512-logit tile: the residual max(0, p - q) after a rejection (step 4)
+// or p for the bonus token (step 5).  draw_final_kernel walks one row's tile sums
+// and one tile to the inverse-CDF token.
+//
+// bf16 logits are processed in fp32 (exp2 on the hardware unit, fp64 accumulation
+// of 8-logit partial sums); fp32 logits are processed in fp64 throughout.
 #include <float.h>
 #include <limits.h>
 
 #include "sv_internal.h"
 
 namespace sv {
+
+constexpr double kQNaN = __builtin_nan("");
 
 // ===========================================================================
 // prepare: packed offsets of a ragged batch
@@ -46,7 +52,7 @@ __global__ __launch_bounds__(1024) void prepare_kernel(Params P)
         int32_t g = in ? P.gamma[i] : 0;
         if (in && g < 0) bad = 1;
         if (g < 0) g = 0;
-        int64_t vt = in ? (int64_t)g + 1 : 0, vd = in ? (int64_t)g : 0;
+        const int64_t vt = in ? (int64_t)g + 1 : 0, vd = in ? (int64_t)g : 0;
         int64_t it = vt, id = vd;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -60,12 +66,12 @@ __global__ __launch_bounds__(1024) void prepare_kernel(Params P)
         const int64_t t_off = pt + it - vt, d_off = pd + id - vd;
         if (in) {
             P.rows[i] = RowInfo{(int32_t)t_off, (int32_t)d_off, g, 0};
-            // vector slots of row i: target positions then draft positions
-            const int64_t s0 = t_off + d_off;
-            if (s0 < P.nvec) {
-                int64_t n = 2 * (int64_t)g + 1;
-                if (n > P.nvec - s0) n = P.nvec - s0;
-                for (int64_t k = 0; k < n; ++k) P.vec_row[s0 + k] = (int32_t)i;
+            // streamed slots of row i (bounds-checked: totals are validated below)
+            const int64_t s0 = P.mode == 1 ? t_off : t_off + d_off;
+            const int64_t n = P.mode == 1 ? (int64_t)g + 1 : 2 * (int64_t)g + 1;
+            if (s0 < P.geo.nvec) {
+                const int64_t e = s0 + n < P.geo.nvec ? s0 + n : P.geo.nvec;
+                for (int64_t k = s0; k < e; ++k) P.vec_row[k] = (int32_t)i;
             }
         }
         __syncthreads();
@@ -76,227 +82,329 @@ __global__ __launch_bounds__(1024) void prepare_kernel(Params P)
 }
 
 // ===========================================================================
-// pass 1: per-vector statistics
+// streaming pass
 // ===========================================================================
-struct SampleState {
+
+// Sampling accumulator of one thread, fp32 arithmetic (bf16 logits).  s holds
+// sum 2^(z c - R) against an integer reference R, or, on the slow route (scaled
+// logits at or beyond 2^20 in magnitude), sum 2^((z - mref) c).  R moves to the
+// smallest integer at or above a group's scaled maximum when that maximum passes
+// it, an exact power-of-two rescale of s, so the largest terms have arguments in
+// (-1, 0].  Before any finite logit R = 0 and has_ref is false: -inf logits add 0
+// and a NaN logit makes s NaN.  Rare paths sit behind wave-uniform branches.
+struct Acc32 {
     float m;        // running maximum
-    float mref;     // logit the reference exponent was taken at (-inf: none yet)
-    float Mref;     // fp32(mref * c_hi)
-    bool fast;      // |Mref| < 2^30: single-fma argument against Mref
-    bool nan_seen;  // a NaN arrived while no finite logit had been seen
-    double R;       // s holds sum 2^(z c - R)
+    float R;        // integer reference (fast route)
+    float mref;     // reference logit (slow route)
+    bool has_ref;
+    bool slow;
     double s;
 };
 
 template <int N>
-__device__ __forceinline__ void sample_chunk(SampleState &st, const float *x, const TempConst &tc)
+__device__ __forceinline__ void acc32_group(Acc32 &a, const float *x, const TempConst &tc)
 {
     float cm = x[0];
 #pragma unroll
     for (int i = 1; i < N; ++i) cm = fmaxf(cm, x[i]);
-    st.m = fmaxf(st.m, cm);
-    // new reference only when the maximum first appears or climbs by 16 binades,
-    // so exponents stay <= 16 without a rescale per chunk
-    if (cm > st.mref && (st.mref == -INFINITY || (cm - st.mref) * tc.c_hi > 16.0f)) {
-        const float M = cm * tc.c_hi;
-        const bool fast = fabsf(M) < kFastRef;
-        const double R = fast ? (double)M : (double)cm * tc.c_eff;
-        if (st.mref != -INFINITY) st.s *= exp2(st.R - R);
-        st.mref = cm;
-        st.Mref = M;
-        st.fast = fast;
-        st.R = R;
-    }
-    if (st.mref == -INFINITY) {
-#pragma unroll
-        for (int i = 0; i < N; ++i) st.nan_seen |= (x[i] != x[i]);
-        return;
+    a.m = fmaxf(a.m, cm);
+    const bool up = a.slow ? cm > a.mref : (cm * tc.c_hi > a.R || (!a.has_ref && cm > -INFINITY));
+    if (__any(up)) {
+        if (up) {
+            const float Rn = ceilf(cm * tc.c_hi);
+            const bool slow = !(fabsf(Rn) < kFastRef);
+            if (a.has_ref) {
+                if (!a.slow && !slow) {
+                    a.s = ldexp(a.s, (int)(a.R - Rn));
+                } else {
+                    const double Rold = a.slow ? (double)a.mref * tc.c_eff : (double)a.R;
+                    const double Rnew = slow ? (double)cm * tc.c_eff : (double)Rn;
+                    a.s *= exp2_f64(Rold - Rnew);
+                }
+            }
+            a.R = slow ? 0.0f : Rn;
+            a.mref = cm;
+            a.slow = slow;
+            a.has_ref = true;
+        }
     }
     float e[N];
-    if (st.fast) {
-#pragma unroll
-        for (int i = 0; i < N; ++i) e[i] = fast_exp2(fmaf(x[i], tc.c_lo, fmaf(x[i], tc.c_hi, -st.Mref)));
-    } else {
+    if (__any(a.slow)) {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const float d = x[i] - st.mref;
-            e[i] = fast_exp2(fmaf(d, tc.c_hi, d * tc.c_lo));
+            const float d = x[i] - a.mref;
+            const float es = hw_exp2(fmaf(d, tc.c_hi, d * tc.c_lo));
+            const float ef = hw_exp2(fmaf(x[i], tc.c_lo, fmaf(x[i], tc.c_hi, -a.R)));
+            e[i] = a.slow ? es : ef;
         }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) e[i] = hw_exp2(fmaf(x[i], tc.c_lo, fmaf(x[i], tc.c_hi, -a.R)));
     }
 #pragma unroll
     for (int w = 1; w < N; w <<= 1)
 #pragma unroll
         for (int i = 0; i + w < N; i += 2 * w) e[i] += e[i + w];
-    st.s += (double)e[0];
+    a.s += (double)e[0];
 }
 
-struct GreedyState {
+// this thread's sum relative to its own maximum m: sum 2^((z - m) c)
+__device__ __forceinline__ double acc32_final(const Acc32 &a, const TempConst &tc)
+{
+    if (!a.has_ref) return a.s;   // 0, or NaN
+    const double Rd = a.slow ? (double)a.mref * tc.c_eff : (double)a.R;
+    return a.s * exp2_f64(Rd - (double)a.m * tc.c_eff);
+}
+
+// Sampling accumulator in fp64 (fp32 logits), same scheme with an fp64 reference.
+struct Acc64 {
+    float m;
+    bool has_ref;
+    double R;
+    double s;
+};
+
+template <int N>
+__device__ __forceinline__ void acc64_group(Acc64 &a, const float *x, const TempConst &tc)
+{
+    float cm = x[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) cm = fmaxf(cm, x[i]);
+    a.m = fmaxf(a.m, cm);
+    const double sc = (double)cm * tc.c_eff;
+    const bool up = sc > a.R || (!a.has_ref && cm > -INFINITY);
+    if (__any(up)) {
+        if (up) {
+            const double Rn = ceil(sc);
+            if (a.has_ref) {
+                const double sh = a.R - Rn;
+                a.s = sh < -2000.0 ? a.s * 0.0 : ldexp(a.s, (int)sh);
+            }
+            a.R = Rn;
+            a.has_ref = true;
+        }
+    }
+    double t = 0.0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) t += exp2_f64(fma((double)x[i], tc.c_eff, -a.R));
+    a.s += t;
+}
+
+__device__ __forceinline__ double acc64_final(const Acc64 &a, const TempConst &tc)
+{
+    if (!a.has_ref) return a.s;
+    return a.s * exp2_f64(a.R - (double)a.m * tc.c_eff);
+}
+
+struct AccArg {
     float best;
     int32_t idx;
     bool nan_seen;
 };
 
-template <int DT, bool AL, bool GREEDY>
-__device__ __forceinline__ Partial reduce_segment(const void *base, int64_t u0, int64_t u1, int64_t V,
-                                                  const TempConst &tc)
+// x holds kUnroll units, unit k at index u + k * kBlock
+template <int N>
+__device__ __forceinline__ void accarg_group(AccArg &a, const float *x, int64_t u)
+{
+    float cm = x[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) cm = fmaxf(cm, x[i]);
+    bool nan = false;
+#pragma unroll
+    for (int i = 0; i < N; ++i) nan |= (x[i] != x[i]);
+    a.nan_seen |= nan;
+    const bool up = cm > a.best;
+    if (__any(up)) {
+        if (up) {
+            a.best = cm;
+            int first = N - 1;
+#pragma unroll
+            for (int i = N - 1; i >= 0; --i)
+                if (x[i] == cm) first = i;
+            a.idx = (int32_t)((u + (int64_t)(first / kUnitElems) * kBlock) * kUnitElems + first % kUnitElems);
+        }
+    }
+}
+
+// A unit past the end of the piece, read as -inf logits.
+template <int DT>
+__device__ __forceinline__ RawUnit<DT> neg_inf_unit()
+{
+    RawUnit<DT> r;
+    if constexpr (DT == 0) {
+        r.a = make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
+    } else {
+        r.a = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        r.b = r.a;
+    }
+    return r;
+}
+
+// One vector piece [a, b) (units) by the whole workgroup.
+template <int DT, bool AL>
+__device__ Partial reduce_piece(const void *base, int64_t a, int64_t b, int64_t V, int rmode,
+                                const TempConst &tc)
 {
     constexpr int N = kUnroll * kUnitElems;
     __shared__ float sh_f[kWaves];
     __shared__ double sh_d[kWaves];
     __shared__ int sh_i[kWaves], sh_n[kWaves];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __syncthreads();   // the shared slots may still be read by a previous piece
 
-    SampleState st{-INFINITY, -INFINITY, 0.0f, false, false, 0.0, 0.0};
-    GreedyState gs{-INFINITY, INT32_MAX, false};
+    Acc32 a32{-INFINITY, 0.0f, 0.0f, false, false, 0.0};
+    Acc64 a64{-INFINITY, false, 0.0, 0.0};
+    AccArg ag{-INFINITY, INT32_MAX, false};
 
-    for (int64_t ub = u0 + tid; ub < u1; ub += (int64_t)kBlock * kUnroll) {
-        float x[N];
+    // software pipeline: the next group's loads are in flight while this group is
+    // reduced
+    constexpr int64_t kStride = (int64_t)kBlock * kUnroll;
+    RawUnit<DT> cur[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+        const int64_t uk = a + tid + (int64_t)k * kBlock;
+        cur[k] = uk < b ? load_raw<DT, AL>(base, uk, V) : neg_inf_unit<DT>();
+    }
+    for (int64_t u = a + tid; u < b; u += kStride) {
+        RawUnit<DT> nxt[kUnroll];
 #pragma unroll
         for (int k = 0; k < kUnroll; ++k) {
-            const int64_t u = ub + (int64_t)k * kBlock;
-            if (u < u1) {
-                load_unit<DT, AL>(base, u, V, x + k * kUnitElems);
-            } else {
-#pragma unroll
-                for (int e = 0; e < kUnitElems; ++e) x[k * kUnitElems + e] = -INFINITY;
-            }
+            const int64_t uk = u + kStride + (int64_t)k * kBlock;
+            nxt[k] = uk < b ? load_raw<DT, AL>(base, uk, V) : neg_inf_unit<DT>();
         }
-        if constexpr (GREEDY) {
-            float cm = x[0];
+        float x[N];
 #pragma unroll
-            for (int i = 1; i < N; ++i) cm = fmaxf(cm, x[i]);
-            bool nan = false;
+        for (int k = 0; k < kUnroll; ++k) unpack<DT>(cur[k], x + k * kUnitElems);
+        if (rmode == ROW_GREEDY) accarg_group<N>(ag, x, u);
+        else if (DT == 0) acc32_group<N>(a32, x, tc);
+        else acc64_group<N>(a64, x, tc);
 #pragma unroll
-            for (int i = 0; i < N; ++i) nan |= (x[i] != x[i]);
-            gs.nan_seen |= nan;
-            if (cm > gs.best) {
-                gs.best = cm;
-#pragma unroll
-                for (int i = N - 1; i >= 0; --i)
-                    if (x[i] == cm)
-                        gs.idx = (int32_t)((ub + (int64_t)(i / kUnitElems) * kBlock) * kUnitElems +
-                                           (i % kUnitElems));
-            }
-        } else {
-            sample_chunk<N>(st, x, tc);
-        }
+        for (int k = 0; k < kUnroll; ++k) cur[k] = nxt[k];
     }
 
     Partial out;
-    if constexpr (GREEDY) {
-        float b = wave_max(gs.best);
-        if (lane == 0) sh_f[wave] = b;
+    if (rmode == ROW_GREEDY) {
+        float bst = wave_max(ag.best);
+        if (lane == 0) sh_f[wave] = bst;
         __syncthreads();
-        b = sh_f[0];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) b = fmaxf(b, sh_f[w]);
-        int cand = (gs.best == b) ? gs.idx : INT32_MAX;
-        cand = wave_min_int(cand);
-        int nan = wave_or_int(gs.nan_seen ? 1 : 0);
+        bst = fmaxf(fmaxf(sh_f[0], sh_f[1]), fmaxf(sh_f[2], sh_f[3]));
+        int cand = wave_min_int(ag.best == bst ? ag.idx : INT32_MAX);
+        const int nan = wave_or_int(ag.nan_seen ? 1 : 0);
         if (lane == 0) { sh_i[wave] = cand; sh_n[wave] = nan; }
         __syncthreads();
-        int idx = sh_i[0];
-        int anynan = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) { idx = min(idx, sh_i[w]); anynan |= sh_n[w]; }
-        out.m = b;
-        out.idx = idx;
-        out.s = anynan ? __longlong_as_double(0x7ff8000000000000LL) : 0.0;
-    } else {
-        // this thread's sum relative to its own maximum
-        double s_m;
-        if (st.mref == -INFINITY)
-            s_m = 0.0;
-        else
-            s_m = st.s * exp2(st.R - (double)st.m * tc.c_eff);
-        if (st.nan_seen) s_m = __longlong_as_double(0x7ff8000000000000LL);
-        float mw = wave_max(st.m);
-        if (lane == 0) sh_f[wave] = mw;
-        __syncthreads();
-        mw = sh_f[0];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) mw = fmaxf(mw, sh_f[w]);
-        double c = (st.m == -INFINITY) ? s_m : s_m * exp2(((double)st.m - (double)mw) * tc.c_eff);
-        c = wave_sum(c);
-        if (lane == 0) sh_d[wave] = c;
-        __syncthreads();
-        double s = 0.0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) s += sh_d[w];
-        out.m = mw;
-        out.idx = 0;
-        out.s = s;
+        out.m = bst;
+        out.idx = min(min(sh_i[0], sh_i[1]), min(sh_i[2], sh_i[3]));
+        out.s = (sh_n[0] | sh_n[1] | sh_n[2] | sh_n[3]) ? kQNaN : 0.0;
+        return out;
     }
+    // this thread's sum relative to its own maximum, then the workgroup's
+    const float m = DT == 0 ? a32.m : a64.m;
+    const double s_m = DT == 0 ? acc32_final(a32, tc) : acc64_final(a64, tc);
+    float mw = wave_max(m);
+    if (lane == 0) sh_f[wave] = mw;
+    __syncthreads();
+    mw = fmaxf(fmaxf(sh_f[0], sh_f[1]), fmaxf(sh_f[2], sh_f[3]));
+    double c = (m == -INFINITY) ? s_m : s_m * exp2_f64(((double)m - (double)mw) * tc.c_eff);
+    c = wave_sum(c);
+    if (lane == 0) sh_d[wave] = c;
+    __syncthreads();
+    out.m = mw;
+    out.idx = 0;
+    out.s = (sh_d[0] + sh_d[1]) + (sh_d[2] + sh_d[3]);
     return out;
+}
+
+__device__ __forceinline__ int32_t slot_row(const Params &P, int64_t v)
+{
+    if (P.gamma != nullptr) return P.vec_row[v];
+    const int64_t per = P.mode == 1 ? (int64_t)P.gamma_uniform + 1 : 2 * (int64_t)P.gamma_uniform + 1;
+    return (int32_t)(v / per);
 }
 
 template <int DT, bool AL>
 __global__ __launch_bounds__(kBlock) void stats_kernel(Params P)
 {
-    const int64_t item = blockIdx.x;
-    const int64_t slot = item / P.geo.nseg;
-    const int32_t seg = (int32_t)(item - slot * P.geo.nseg);
-    int32_t row;
-    RowGeom G;
-    if (P.gamma != nullptr) {
-        if (P.hdr->status != 0) return;
-        row = P.vec_row[slot];
-        G = row_geom(P, row);
-    } else {
-        const int64_t per = 2 * (int64_t)P.gamma_uniform + 1;
-        row = (int32_t)(slot / per);
-        G = row_geom(P, row);
+    if (P.gamma != nullptr && P.hdr->status != 0) return;
+    const int64_t wg = blockIdx.x;
+    const int64_t nunits = P.geo.nunits;
+    const int64_t u0 = wg * P.geo.R;
+    int64_t u1 = u0 + P.geo.R;
+    if (u1 > P.geo.total_units) u1 = P.geo.total_units;
+    if (u0 >= u1) return;
+    const int64_t v0 = u0 / nunits, v1 = (u1 - 1) / nunits;
+    for (int64_t v = v0; v <= v1; ++v) {
+        const int64_t vb = v * nunits;
+        const int64_t a = (u0 > vb ? u0 : vb) - vb;
+        const int64_t b = (u1 < vb + nunits ? u1 : vb + nunits) - vb;
+        const int32_t row = slot_row(P, v);
+        const RowGeom G = row_geom(P, row);
+        const int64_t k = v - row_slot0(P, G);
+        const bool is_target = P.mode == 1 || k <= G.gamma;
+        const int64_t vrow = is_target ? G.t_off + k : G.d_off + (k - G.gamma - 1);
+        const float T = P.temperature[row];
+        const int32_t rm = row_mode(P.mode, T);
+        Partial rec{-INFINITY, INT32_MAX, 0.0};
+        if (rm != ROW_BAD_TEMP && (rm == ROW_SAMPLE || is_target)) {
+            const TempConst tc = temp_const(rm == ROW_SAMPLE ? T : 1.0f);
+            const void *base = vec_ptr(is_target ? P.target : P.draft, DT, vrow, P.V);
+            // the logit at this position's draft token, if it lies in this piece
+            // (sampling rows), saved for the accept test
+            const int64_t j = is_target ? k : k - G.gamma - 1;
+            float zx = 0.0f;
+            bool have_zx = false;
+            if (rm == ROW_SAMPLE && j < G.gamma) {
+                const int32_t x = P.tokens[G.d_off + j];
+                if (x >= 0 && (int64_t)x < P.V && x / kUnitElems >= a && x / kUnitElems < b) {
+                    zx = load_logit<DT>(base, x);
+                    have_zx = true;
+                }
+            }
+            rec = reduce_piece<DT, AL>(base, a, b, P.V, rm, tc);
+            if (have_zx && threadIdx.x == 0) P.zx[(is_target ? 0 : P.nD) + G.d_off + j] = zx;
+        }
+        if (threadIdx.x == 0) P.parts[wg + v] = rec;
     }
-    const int64_t k = slot - (G.t_off + G.d_off);
-    const bool is_target = k <= G.gamma;
-    const float T = P.temperature[row];
-    const int32_t rm = row_mode(P.mode, T);
-    if (rm == ROW_BAD_TEMP) return;
-    if (rm == ROW_GREEDY && !is_target) return;
-    const int64_t vrow = is_target ? G.t_off + k : G.d_off + (k - G.gamma - 1);
-    const void *base = vec_ptr(is_target ? P.target : P.draft, DT, vrow, P.V);
-    const int64_t u0 = (int64_t)seg * P.geo.seg_units;
-    int64_t u1 = u0 + P.geo.seg_units;
-    if (u1 > P.geo.nunits) u1 = P.geo.nunits;
-    Partial out;
-    if (rm == ROW_GREEDY) {
-        TempConst tc{1.0f, 0.0f, 1.0};
-        out = reduce_segment<DT, AL, true>(base, u0, u1, P.V, tc);
-    } else {
-        const TempConst tc = temp_const(T);
-        out = reduce_segment<DT, AL, false>(base, u0, u1, P.V, tc);
-    }
-    if (threadIdx.x == 0) P.parts[slot * P.geo.nseg + seg] = out;
 }
 
 // ===========================================================================
 // accept scan: one wave per row
 // ===========================================================================
-__device__ __forceinline__ void combine_sample(const Params &P, int64_t slot, const TempConst &tc,
-                                               float &m, double &S)
-{
-    const Partial *pp = P.parts + slot * P.geo.nseg;
-    m = -INFINITY;
-    for (int s = 0; s < P.geo.nseg; ++s) m = fmaxf(m, pp[s].m);
-    S = 0.0;
-    for (int s = 0; s < P.geo.nseg; ++s) {
-        const Partial q = pp[s];
-        S += (q.m == -INFINITY) ? q.s : q.s * exp2(((double)q.m - (double)m) * tc.c_eff);
-    }
-}
 
-__device__ __forceinline__ void combine_greedy(const Params &P, int64_t slot, float &val, int32_t &idx,
-                                               bool &nan)
+// merge the pieces of streamed vector v: max and sum 2^((z - m) c), or argmax
+__device__ __forceinline__ void merge_vector(const Params &P, int64_t v, const TempConst &tc, bool greedy,
+                                             float &m, double &S, int32_t &idx, bool &nan)
 {
-    const Partial *pp = P.parts + slot * P.geo.nseg;
-    val = -INFINITY;
-    for (int s = 0; s < P.geo.nseg; ++s) val = fmaxf(val, pp[s].m);
+    const int64_t w0 = (v * P.geo.nunits) / P.geo.R;
+    const int64_t w1 = ((v + 1) * P.geo.nunits - 1) / P.geo.R;
+    m = -INFINITY;
+    S = 0.0;
     idx = INT32_MAX;
     nan = false;
-    for (int s = 0; s < P.geo.nseg; ++s) {
-        const Partial q = pp[s];
-        if (q.m == val && q.idx < idx) idx = q.idx;
-        nan |= (q.s != q.s);
+    constexpr int kBuf = 8;
+    Partial buf[kBuf];
+    for (int64_t w = w0; w <= w1; w += kBuf) {
+#pragma unroll
+        for (int i = 0; i < kBuf; ++i)
+            buf[i] = (w + i <= w1) ? P.parts[w + i + v] : Partial{-INFINITY, INT32_MAX, 0.0};
+        if (greedy) {
+#pragma unroll
+            for (int i = 0; i < kBuf; ++i) {
+                if (buf[i].m > m || (buf[i].m == m && buf[i].idx < idx)) {
+                    idx = buf[i].m > m ? buf[i].idx : min(idx, buf[i].idx);
+                    m = buf[i].m;
+                }
+                nan |= (buf[i].s != buf[i].s);
+            }
+        } else {
+            float mm = m;
+#pragma unroll
+            for (int i = 0; i < kBuf; ++i) mm = fmaxf(mm, buf[i].m);
+            if (mm > m && m != -INFINITY) S *= exp2_f64(((double)m - (double)mm) * tc.c_eff);
+            m = mm;
+#pragma unroll
+            for (int i = 0; i < kBuf; ++i)
+                S += buf[i].m == -INFINITY ? buf[i].s : buf[i].s * exp2_f64(((double)buf[i].m - (double)m) * tc.c_eff);
+        }
     }
 }
 
@@ -305,7 +413,6 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(Params P)
 {
     const int lane = threadIdx.x & 63;
     const int32_t row = blockIdx.x * kWaves + (threadIdx.x >> 6);
-    const double qnan = __longlong_as_double(0x7ff8000000000000LL);
 
     if (P.gamma != nullptr && P.hdr->status != 0) {
         // inconsistent gamma array: every row and slot is invalid
@@ -313,24 +420,22 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(Params P)
         const int64_t nthreads = (int64_t)gridDim.x * kBlock;
         for (int64_t s = gid; s < P.nT; s += nthreads) P.emitted[s] = -1;
         for (int64_t s = gid; s < P.nD; s += nthreads) {
-            if (P.p_x) P.p_x[s] = qnan;
-            if (P.q_x) P.q_x[s] = qnan;
+            if (P.p_x) P.p_x[s] = kQNaN;
+            if (P.q_x) P.q_x[s] = kQNaN;
         }
         if (row < P.B && lane == 0) {
             P.n_accepted[row] = -1;
             if (P.row_status) P.row_status[row] = ST_BAD_GAMMA;
-            if (P.resid) P.resid[row] = qnan;
+            if (P.resid) P.resid[row] = kQNaN;
             P.draws[row].kind = DRAW_NONE;
-            P.counters[row] = 0;
         }
         return;
     }
     if (row >= P.B) return;
-    if (lane == 0) P.counters[row] = 0;
 
     const RowGeom G = row_geom(P, row);
     const int32_t g = G.gamma;
-    const int64_t slot0 = G.t_off + G.d_off;
+    const int64_t slot0 = row_slot0(P, G);
     const float T = P.temperature[row];
     const int32_t rm = row_mode(P.mode, T);
     const bool greedy = rm == ROW_GREEDY;
@@ -339,86 +444,89 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(Params P)
     int status = (rm == ROW_BAD_TEMP) ? ST_BAD_TEMP : 0;
     int32_t K = g;
     bool found = false;
+    float kmt = -INFINITY, kmd = -INFINITY;   // statistics at K (valid on every lane once known)
+    double kSt = 0.0, kSd = 0.0;
+    int32_t kidx = -1;
 
     if (rm != ROW_BAD_TEMP) {
         for (int base = 0; base <= g; base += 64) {
             const int j = base + lane;
-            bool reject = false;
-            if (j <= g) {
-                const int64_t ts = slot0 + j;
-                int32_t x = 0;
-                bool x_ok = false;
-                if (j < g) {
-                    x = P.tokens[G.d_off + j];
-                    x_ok = x >= 0 && (int64_t)x < P.V;
-                    if (!x_ok) status |= ST_BAD_TOKEN;
+            const bool has_t = j <= g, has_d = j < g;
+            int32_t x = 0;
+            float u = 0.0f, zt = 0.0f, zd = 0.0f;
+            if (has_d) {
+                x = P.tokens[G.d_off + j];
+                u = P.uniforms[G.t_off + j];
+                if (!greedy) {   // saved by the streaming pass
+                    zt = P.zx[G.d_off + j];
+                    zd = P.zx[P.nD + G.d_off + j];
                 }
-                if (greedy) {
-                    float val;
-                    int32_t idx;
-                    bool nan;
-                    combine_greedy(P, ts, val, idx, nan);
-                    if (nan || !(val > -INFINITY && val < INFINITY)) status |= ST_NONFINITE;
-                    if (j < g) reject = x != idx;
-                } else {
-                    float mt;
-                    double St;
-                    combine_sample(P, ts, tc, mt, St);
-                    if (!(St > 0.0 && St < INFINITY)) status |= ST_NONFINITE;
-                    if (j < g) {
-                        float md;
-                        double Sd;
-                        combine_sample(P, slot0 + g + 1 + j, tc, md, Sd);
-                        if (!(Sd > 0.0 && Sd < INFINITY)) status |= ST_NONFINITE;
-                        double px = qnan, qx = qnan;
-                        if (x_ok && St > 0.0 && St < INFINITY && Sd > 0.0 && Sd < INFINITY) {
-                            const float zt = load_logit<DT>(vec_ptr(P.target, DT, G.t_off + j, P.V), x);
-                            const float zd = load_logit<DT>(vec_ptr(P.draft, DT, G.d_off + j, P.V), x);
-                            px = exp(((double)zt - (double)mt) / Td) / St;
-                            qx = exp(((double)zd - (double)md) / Td) / Sd;
-                            double ratio;
-                            if (qx > 0.0) {
-                                ratio = px / qx;
-                                if (ratio > 1.0) ratio = 1.0;
-                            } else {
-                                ratio = px > 0.0 ? 1.0 : 0.0;
-                                status |= ST_Q_ZERO;
-                            }
-                            reject = !((double)P.uniforms[G.t_off + j] < ratio);
+            }
+            const bool x_ok = x >= 0 && (int64_t)x < P.V;
+            if (has_d && !x_ok) status |= ST_BAD_TOKEN;
+            float mt = -INFINITY, md = -INFINITY;
+            double St = 0.0, Sd = 0.0;
+            int32_t it = INT32_MAX, idd;
+            bool nt = false, nd = false;
+            bool reject = false;
+            if (has_t) merge_vector(P, slot0 + j, tc, greedy, mt, St, it, nt);
+            if (greedy) {
+                if (has_t && (nt || !(mt > -INFINITY && mt < INFINITY))) status |= ST_NONFINITE;
+                if (has_d) reject = x != it;
+            } else {
+                if (has_t && !(St > 0.0 && St < INFINITY)) status |= ST_NONFINITE;
+                if (has_d) {
+                    merge_vector(P, slot0 + g + 1 + j, tc, false, md, Sd, idd, nd);
+                    if (!(Sd > 0.0 && Sd < INFINITY)) status |= ST_NONFINITE;
+                    double px = kQNaN, qx = kQNaN;
+                    if (x_ok && St > 0.0 && St < INFINITY && Sd > 0.0 && Sd < INFINITY) {
+                        px = exp(((double)zt - (double)mt) / Td) / St;
+                        qx = exp(((double)zd - (double)md) / Td) / Sd;
+                        double ratio;
+                        if (qx > 0.0) {
+                            ratio = px / qx;
+                            if (ratio > 1.0) ratio = 1.0;
+                        } else {
+                            ratio = px > 0.0 ? 1.0 : 0.0;
+                            status |= ST_Q_ZERO;
                         }
-                        if (P.p_x) P.p_x[G.d_off + j] = px;
-                        if (P.q_x) P.q_x[G.d_off + j] = qx;
+                        reject = !((double)u < ratio);
                     }
+                    if (P.p_x) P.p_x[G.d_off + j] = px;
+                    if (P.q_x) P.q_x[G.d_off + j] = qx;
                 }
             }
             const unsigned long long rb = __ballot(reject);
+            int src = -1;
             if (!found && rb != 0ull) {
-                K = base + __ffsll((long long)rb) - 1;
+                src = __ffsll((long long)rb) - 1;
+                K = base + src;
                 found = true;
+            } else if (!found && g - base < 64) {
+                src = g - base;   // no rejection: the bonus position is in this chunk
+            }
+            if (src >= 0) {
+                kmt = __shfl(mt, src);
+                kSt = __shfl(St, src);
+                kmd = __shfl(md, src);
+                kSd = __shfl(Sd, src);
+                kidx = __shfl(it, src);
             }
         }
     }
     status = wave_or_int(status);
     const bool invalid = (status & ST_INVALID) != 0;
 
-    // emitted tokens, -1 past the drawn position
-    int32_t aK = -1;
-    if (!invalid && greedy && lane == 0) {
-        float val;
-        bool nan;
-        combine_greedy(P, slot0 + K, val, aK, nan);
-    }
-    aK = __shfl(aK, 0);
     for (int j = lane; j <= g; j += 64) {
         int32_t e = -1;
         if (!invalid) {
             if (j < K) e = P.tokens[G.d_off + j];
-            else if (j == K && greedy) e = aK;
+            else if (j == K && greedy) e = kidx;
         }
         P.emitted[G.t_off + j] = e;
         if (j < g && (invalid || greedy)) {
-            if (P.p_x) P.p_x[G.d_off + j] = qnan;
-            if (P.q_x) P.q_x[G.d_off + j] = qnan;
+            if (P.p_x) P.p_x[G.d_off + j] = kQNaN;
+            if (P.q_x) P.q_x[G.d_off + j] = kQNaN;
         }
     }
     if (lane == 0) {
@@ -433,229 +541,233 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(Params P)
             D.d_row = (int32_t)(G.d_off + K);
             D.u = P.uniforms[G.t_off + g];
             D.t_slot = (int32_t)(G.t_off + K);
-            combine_sample(P, slot0 + K, tc, D.m_t, D.S_t);
-            if (K < g) combine_sample(P, slot0 + g + 1 + K, tc, D.m_d, D.S_d);
+            D.m_t = kmt;
+            D.S_t = kSt;
+            D.m_d = kmd;
+            D.S_d = kSd;
+            D.T = T;
         } else if (P.resid) {
-            P.resid[row] = qnan;
+            P.resid[row] = kQNaN;
         }
         P.draws[row] = D;
     }
 }
 
 // ===========================================================================
-// pass 2: residual / bonus weights and the inverse-CDF draw
+// draw: per-tile weight sums, then the inverse CDF
 // ===========================================================================
-struct DrawConst {
+template <int DT>
+struct DrawConst;
+
+// bf16 logits: fp32 weights against an integer reference (as in the streaming pass)
+template <>
+struct DrawConst<0> {
     TempConst tc;
-    float Mt, Md, mt, md;
-    float Ft, Fd;           // unnormalized -> probability
-    bool fast_t, fast_d;
-    bool residual;
-};
+    float Rt, Rd, mt, md, Ft, Fd;
+    bool slow_t, slow_d, residual;
 
-__device__ __forceinline__ DrawConst draw_const(const RowDraw &D, float T)
-{
-    DrawConst c;
-    c.tc = temp_const(T);
-    c.residual = D.kind == DRAW_RESIDUAL;
-    c.mt = D.m_t;
-    c.Mt = D.m_t * c.tc.c_hi;
-    c.fast_t = fabsf(c.Mt) < kFastRef;
-    c.Ft = c.fast_t ? (float)(exp2((double)c.Mt - (double)D.m_t * c.tc.c_eff) / D.S_t)
-                    : (float)(1.0 / D.S_t);
-    c.md = D.m_d;
-    c.Md = D.m_d * c.tc.c_hi;
-    c.fast_d = fabsf(c.Md) < kFastRef;
-    c.Fd = 0.0f;
-    if (c.residual)
-        c.Fd = c.fast_d ? (float)(exp2((double)c.Md - (double)D.m_d * c.tc.c_eff) / D.S_d)
-                        : (float)(1.0 / D.S_d);
-    return c;
-}
-
-__device__ __forceinline__ float unnorm(float z, float M, float m, bool fast, const TempConst &tc)
-{
-    if (fast) return fast_exp2(fmaf(z, tc.c_lo, fmaf(z, tc.c_hi, -M)));
-    const float d = z - m;
-    return fast_exp2(fmaf(d, tc.c_hi, d * tc.c_lo));
-}
-
-// weights w (residual or p) and target probabilities p of one unit
-template <int DT, bool AL>
-__device__ __forceinline__ void unit_weights(const DrawConst &c, const void *tb, const void *db, int64_t unit,
-                                             int64_t V, float *w, float *p)
-{
-    float zt[kUnitElems];
-    load_unit<DT, AL>(tb, unit, V, zt);
-#pragma unroll
-    for (int e = 0; e < kUnitElems; ++e) p[e] = unnorm(zt[e], c.Mt, c.mt, c.fast_t, c.tc) * c.Ft;
-    if (c.residual) {
-        float zd[kUnitElems];
-        load_unit<DT, AL>(db, unit, V, zd);
+    __device__ __forceinline__ void init(const RowDraw &D)
+    {
+        tc = temp_const(D.T);
+        residual = D.kind == DRAW_RESIDUAL;
+        mt = D.m_t;
+        Rt = ceilf(mt * tc.c_hi);
+        slow_t = !(fabsf(Rt) < kFastRef);
+        Ft = (float)((slow_t ? 1.0 : exp2_f64((double)Rt - (double)mt * tc.c_eff)) / D.S_t);
+        md = D.m_d;
+        Rd = ceilf(md * tc.c_hi);
+        slow_d = !(fabsf(Rd) < kFastRef);
+        Fd = residual ? (float)((slow_d ? 1.0 : exp2_f64((double)Rd - (double)md * tc.c_eff)) / D.S_d) : 0.0f;
+    }
+    __device__ __forceinline__ float unnorm(float z, float R, float m, bool slow) const
+    {
+        if (!slow) return hw_exp2(fmaf(z, tc.c_lo, fmaf(z, tc.c_hi, -R)));
+        const float d = z - m;
+        return hw_exp2(fmaf(d, tc.c_hi, d * tc.c_lo));
+    }
+    // weights of one unit: w (residual or p) and p, as doubles
+    __device__ __forceinline__ void weights(const float *zt, const float *zd, double *w, double *p) const
+    {
 #pragma unroll
         for (int e = 0; e < kUnitElems; ++e) {
-            const float q = unnorm(zd[e], c.Md, c.md, c.fast_d, c.tc) * c.Fd;
-            w[e] = fmaxf(0.0f, p[e] - q);
+            const float pe = unnorm(zt[e], Rt, mt, slow_t) * Ft;
+            float we = pe;
+            if (residual) we = fmaxf(0.0f, pe - unnorm(zd[e], Rd, md, slow_d) * Fd);
+            w[e] = we;
+            p[e] = pe;
         }
-    } else {
+    }
+};
+
+// fp32 logits: fp64 weights
+template <>
+struct DrawConst<1> {
+    TempConst tc;
+    double Rt, Rd, Ft, Fd;
+    bool residual;
+
+    __device__ __forceinline__ void init(const RowDraw &D)
+    {
+        tc = temp_const(D.T);
+        residual = D.kind == DRAW_RESIDUAL;
+        Rt = ceil((double)D.m_t * tc.c_eff);
+        Ft = exp2_f64(Rt - (double)D.m_t * tc.c_eff) / D.S_t;
+        Rd = residual ? ceil((double)D.m_d * tc.c_eff) : 0.0;
+        Fd = residual ? exp2_f64(Rd - (double)D.m_d * tc.c_eff) / D.S_d : 0.0;
+    }
+    __device__ __forceinline__ void weights(const float *zt, const float *zd, double *w, double *p) const
+    {
 #pragma unroll
-        for (int e = 0; e < kUnitElems; ++e) w[e] = p[e];
-    }
-}
-
-// Within the `n` sums at arr (stride 2 doubles, field 0 = w, 1 = p), with `carry`
-// already accumulated before them, find the first index whose running sum exceeds
-// t; if none, the last index with a positive value.  Returns the index and the
-// running sum before it.  Executed by one full wave.
-__device__ __forceinline__ int find_in_sums(const Sum2 *arr, int n, bool use_p, double t, double carry,
-                                            int lane, double &before)
-{
-    int found = -1, last_pos = -1;
-    double before_found = 0.0, before_last = 0.0;
-    for (int c0 = 0; c0 < n; c0 += 64) {
-        const int i = c0 + lane;
-        const double v = i < n ? (use_p ? arr[i].p : arr[i].w) : 0.0;
-        const double incl = wave_inclusive_sum(v, lane) + carry;
-        const unsigned long long hit = __ballot(i < n && incl > t);
-        const unsigned long long pos = __ballot(i < n && v > 0.0);
-        if (pos) {
-            const int l = 63 - __clzll((long long)pos);
-            last_pos = c0 + l;
-            before_last = __shfl(incl - v, l);
+        for (int e = 0; e < kUnitElems; ++e) {
+            const double pe = exp2_f64(fma((double)zt[e], tc.c_eff, -Rt)) * Ft;
+            double we = pe;
+            if (residual) we = fmax(0.0, pe - exp2_f64(fma((double)zd[e], tc.c_eff, -Rd)) * Fd);
+            w[e] = we;
+            p[e] = pe;
         }
-        if (hit) {
-            const int l = __ffsll((long long)hit) - 1;
-            found = c0 + l;
-            before_found = __shfl(incl - v, l);
-            break;
-        }
-        carry = __shfl(incl, 63);
     }
-    if (found >= 0) {
-        before = before_found;
-        return found;
-    }
-    before = before_last;
-    return last_pos;
-}
-
-__device__ __forceinline__ double sum_all(const Sum2 *arr, int n, bool use_p, int lane)
-{
-    double carry = 0.0;
-    for (int c0 = 0; c0 < n; c0 += 64) {
-        const int i = c0 + lane;
-        const double v = i < n ? (use_p ? arr[i].p : arr[i].w) : 0.0;
-        const double incl = wave_inclusive_sum(v, lane) + carry;
-        carry = __shfl(incl, 63);
-    }
-    return carry;
-}
+};
 
 template <int DT, bool AL>
-__global__ __launch_bounds__(kBlock) void draw_kernel(Params P)
+__global__ __launch_bounds__(kBlock) void draw_tiles_kernel(Params P)
 {
-    __shared__ double sh_w[kWaves], sh_p[kWaves];
-    __shared__ int sh_last;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // all segments of a row on one XCD: workgroup w runs on XCD w % 8
-    const int64_t wg = blockIdx.x;
-    const int32_t xcd = (int32_t)(wg % kXcds);
-    const int64_t local = wg / kXcds;
-    const int64_t rk = local / P.geo.nseg2;
-    const int32_t seg = (int32_t)(local - rk * P.geo.nseg2);
-    const int64_t row64 = (int64_t)xcd + (int64_t)kXcds * rk;
-    if (row64 >= P.B) return;
-    const int32_t row = (int32_t)row64;
+    const int64_t row = blockIdx.x / P.geo.ndraw;
+    const int32_t piece = (int32_t)(blockIdx.x - row * P.geo.ndraw);
     const RowDraw D = P.draws[row];
     if (D.kind == DRAW_NONE) return;
-
-    const DrawConst c = draw_const(D, P.temperature[row]);
+    DrawConst<DT> c;
+    c.init(D);
     const void *tb = vec_ptr(P.target, DT, D.t_row, P.V);
     const void *db = c.residual ? vec_ptr(P.draft, DT, D.d_row, P.V) : nullptr;
-    Sum2 *tiles = P.tiles + (int64_t)row * P.geo.ntiles;
-    Sum2 *segs = P.segs + (int64_t)row * P.geo.nseg2;
+    const int64_t t0 = (int64_t)piece * kTilesPerDrawWg + (int64_t)wave * kTilesPerWave;
 
-    // ---- tile and segment sums ----
-    const int64_t t0 = (int64_t)seg * kTilesPerSeg;
-    int64_t t1 = t0 + kTilesPerSeg;
-    if (t1 > P.geo.ntiles) t1 = P.geo.ntiles;
-    double acc_w = 0.0, acc_p = 0.0;
-    for (int64_t tile = t0 + wave; tile < t1; tile += kWaves) {
-        const int64_t unit = tile * kTileUnits + lane;
-        float w[kUnitElems], p[kUnitElems];
-        float lw = 0.0f, lp = 0.0f;
-        if (unit < P.geo.nunits) {
-            unit_weights<DT, AL>(c, tb, db, unit, P.V, w, p);
+    RawUnit<DT> rt[kTilesPerWave], rd[kTilesPerWave];
 #pragma unroll
-            for (int e = 0; e < kUnitElems; ++e) { lw += w[e]; lp += p[e]; }
+    for (int i = 0; i < kTilesPerWave; ++i) {
+        const int64_t unit = (t0 + i) * kTileUnits + lane;
+        const bool in = t0 + i < P.geo.ntiles && unit < P.geo.nunits;
+        rt[i] = in ? load_raw<DT, AL>(tb, unit, P.V) : neg_inf_unit<DT>();
+        rd[i] = (in && c.residual) ? load_raw<DT, AL>(db, unit, P.V) : neg_inf_unit<DT>();
+    }
+    // per-lane sums of every tile first, then one interleaved cross-lane reduction
+    // (tiles past the end read -inf logits and sum to 0)
+    double lw[kTilesPerWave], lp[kTilesPerWave];
+#pragma unroll
+    for (int i = 0; i < kTilesPerWave; ++i) {
+        float zt[kUnitElems], zd[kUnitElems];
+        unpack<DT>(rt[i], zt);
+        unpack<DT>(rd[i], zd);
+        double w[kUnitElems], p[kUnitElems];
+        c.weights(zt, zd, w, p);
+        lw[i] = 0.0;
+        lp[i] = 0.0;
+#pragma unroll
+        for (int e = 0; e < kUnitElems; ++e) { lw[i] += w[e]; lp[i] += p[e]; }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+#pragma unroll
+        for (int i = 0; i < kTilesPerWave; ++i) {
+            lw[i] += __shfl_xor(lw[i], o);
+            lp[i] += __shfl_xor(lp[i], o);
         }
-        const double tw = wave_sum((double)lw), tp = wave_sum((double)lp);
-        if (lane == 0) tiles[tile] = Sum2{tw, tp};
-        acc_w += tw;
-        acc_p += tp;
     }
-    if (lane == 0) { sh_w[wave] = acc_w; sh_p[wave] = acc_p; }
-    __syncthreads();
-    if (tid == 0) {
-        double sw = 0.0, sp = 0.0;
-        for (int w = 0; w < kWaves; ++w) { sw += sh_w[w]; sp += sh_p[w]; }
-        segs[seg] = Sum2{sw, sp};
-        __threadfence();
-        const int old = atomicAdd(&P.counters[row], 1);
-        sh_last = (old == P.geo.nseg2 - 1);
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < kTilesPerWave; ++i)
+            if (t0 + i < P.geo.ntiles) P.tiles[row * P.geo.ntiles + t0 + i] = Sum2{lw[i], lp[i]};
     }
-    __syncthreads();
-    if (!sh_last || wave != 0) return;
-    __threadfence();
+}
 
-    // ---- the last workgroup of the row: inverse CDF ----
-    const int nseg2 = P.geo.nseg2;
+// one wave per row
+template <int DT, bool AL>
+__global__ __launch_bounds__(64) void draw_final_kernel(Params P)
+{
+    const int lane = threadIdx.x;
+    const int32_t row = blockIdx.x;
+    const RowDraw D = P.draws[row];
+    if (D.kind == DRAW_NONE) return;
+    const int32_t nt = P.geo.ntiles;
+    const Sum2 *tiles = P.tiles + (int64_t)row * nt;
+    const int per = (nt + 63) / 64;        // tiles per lane, contiguous
+    const int l0 = lane * per;
+    const int l1 = min(l0 + per, nt);
+
+    // total weight (residual, or p when the residual is empty)
+    double lw = 0.0, lp = 0.0;
+    for (int t = l0; t < l1; ++t) { lw += tiles[t].w; lp += tiles[t].p; }
+    const double iw = wave_inclusive_sum(lw, lane), ip = wave_inclusive_sum(lp, lane);
+    double W = __shfl(iw, 63);
     bool use_p = false;
-    double W = sum_all(segs, nseg2, false, lane);
-    if (c.residual && !(W > 0.0)) {
-        use_p = true;
-        W = sum_all(segs, nseg2, true, lane);
-    }
+    if (D.kind == DRAW_RESIDUAL && !(W > 0.0)) use_p = true;
+    if (D.kind == DRAW_BONUS) use_p = false;
+    if (use_p) W = __shfl(ip, 63);
     const double t = (double)D.u * W;
-    double before;
-    const int g = find_in_sums(segs, nseg2, use_p, t, 0.0, lane, before);
+
+    // the tile where the running sum first exceeds t
+    double cum = use_p ? ip - lp : iw - lw;
+    int cand = -1, lastpos = -1;
+    double cand_before = 0.0, last_before = 0.0;
+    for (int k = l0; k < l1; ++k) {
+        const double v = use_p ? tiles[k].p : tiles[k].w;
+        if (cand < 0 && cum + v > t) { cand = k; cand_before = cum; }
+        if (v > 0.0) { lastpos = k; last_before = cum; }
+        cum += v;
+    }
+    int tile = -1;
+    double before = 0.0;
+    const unsigned long long hit = __ballot(cand >= 0);
+    if (hit) {
+        const int l = __ffsll((long long)hit) - 1;
+        tile = __shfl(cand, l);
+        before = __shfl(cand_before, l);
+    } else {
+        const unsigned long long pos = __ballot(lastpos >= 0);
+        if (pos) {
+            const int l = 63 - __clzll((long long)pos);
+            tile = __shfl(lastpos, l);
+            before = __shfl(last_before, l);
+        }
+    }
+
     int32_t token = -1;
-    if (g >= 0) {
-        const int64_t gt0 = (int64_t)g * kTilesPerSeg;
-        int nt = kTilesPerSeg;
-        if (gt0 + nt > P.geo.ntiles) nt = (int)(P.geo.ntiles - gt0);
-        double before_tile;
-        const int tl = find_in_sums(tiles + gt0, nt, use_p, t, before, lane, before_tile);
-        if (tl >= 0) {
-            const int64_t tile = gt0 + tl;
-            const int64_t unit = tile * kTileUnits + lane;
-            float w[kUnitElems], p[kUnitElems];
+    if (tile >= 0) {
+        DrawConst<DT> c;
+        c.init(D);
+        const void *tb = vec_ptr(P.target, DT, D.t_row, P.V);
+        const void *db = c.residual ? vec_ptr(P.draft, DT, D.d_row, P.V) : nullptr;
+        const int64_t unit = (int64_t)tile * kTileUnits + lane;
+        const bool in = unit < P.geo.nunits;
+        const RawUnit<DT> rt = in ? load_raw<DT, AL>(tb, unit, P.V) : neg_inf_unit<DT>();
+        const RawUnit<DT> rd = (in && c.residual) ? load_raw<DT, AL>(db, unit, P.V) : neg_inf_unit<DT>();
+        float zt[kUnitElems], zd[kUnitElems];
+        unpack<DT>(rt, zt);
+        unpack<DT>(rd, zd);
+        double w[kUnitElems], p[kUnitElems];
+        c.weights(zt, zd, w, p);
+        double ls = 0.0;
 #pragma unroll
-            for (int e = 0; e < kUnitElems; ++e) w[e] = p[e] = 0.0f;
-            if (unit < P.geo.nunits) unit_weights<DT, AL>(c, tb, db, unit, P.V, w, p);
-            double lsum = 0.0;
+        for (int e = 0; e < kUnitElems; ++e) ls += use_p ? p[e] : w[e];
+        const double incl = wave_inclusive_sum(ls, lane);
+        double run = before + incl - ls;
+        int ce = -1, lpos = -1;
 #pragma unroll
-            for (int e = 0; e < kUnitElems; ++e) lsum += (double)(use_p ? p[e] : w[e]);
-            const double incl = wave_inclusive_sum(lsum, lane);
-            double cum = before_tile + incl - lsum;
-            int cand = -1, lastpos = -1;
-#pragma unroll
-            for (int e = 0; e < kUnitElems; ++e) {
-                const float we = use_p ? p[e] : w[e];
-                cum += (double)we;
-                if (cand < 0 && cum > t) cand = e;
-                if (we > 0.0f) lastpos = e;
-            }
-            const unsigned long long hit = __ballot(cand >= 0);
-            if (hit) {
-                const int l = __ffsll((long long)hit) - 1;
-                token = (int32_t)(__shfl((int)(unit * kUnitElems) + cand, l));
-            } else {
-                const unsigned long long pos = __ballot(lastpos >= 0);
-                if (pos) {
-                    const int l = 63 - __clzll((long long)pos);
-                    token = (int32_t)(__shfl((int)(unit * kUnitElems) + lastpos, l));
-                }
+        for (int e = 0; e < kUnitElems; ++e) {
+            const double we = use_p ? p[e] : w[e];
+            run += we;
+            if (ce < 0 && run > t) ce = e;
+            if (we > 0.0) lpos = e;
+        }
+        const unsigned long long h2 = __ballot(ce >= 0);
+        if (h2) {
+            const int l = __ffsll((long long)h2) - 1;
+            token = __shfl((int)(unit * kUnitElems) + ce, l);
+        } else {
+            const unsigned long long p2 = __ballot(lpos >= 0);
+            if (p2) {
+                const int l = 63 - __clzll((long long)p2);
+                token = __shfl((int)(unit * kUnitElems) + lpos, l);
             }
         }
     }
@@ -677,6 +789,34 @@ static hipError_t launch(const void *fn, int64_t blocks, int threads, const Para
     return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(threads), args, 0, s);
 }
 
+static const void *stats_fn(int dtype, bool aligned)
+{
+    return dtype == 0 ? (aligned ? (const void *)stats_kernel<0, true> : (const void *)stats_kernel<0, false>)
+                      : (aligned ? (const void *)stats_kernel<1, true> : (const void *)stats_kernel<1, false>);
+}
+
+// Workgroups of the streaming kernel that fit on the current device at once
+// (cached per device and kernel variant).
+int32_t stats_grid_cap(int dtype, bool aligned)
+{
+    constexpr int kMaxDev = 64;
+    static int32_t cache[kMaxDev][4] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 1024;
+    const int var = dtype * 2 + (aligned ? 1 : 0);
+    if (dev < kMaxDev && cache[dev][var] > 0) return cache[dev][var];
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stats_fn(dtype, aligned), kBlock, 0) !=
+            hipSuccess || per_cu <= 0)
+        per_cu = 4;
+    int64_t cap = (int64_t)cus * per_cu;
+    if (cap > kMaxStatsGrid) cap = kMaxStatsGrid;
+    if (dev < kMaxDev) cache[dev][var] = (int32_t)cap;
+    return (int32_t)cap;
+}
+
 hipError_t launch_prepare(const Params &P, hipStream_t s)
 {
     return launch((const void *)prepare_kernel, 1, 1024, P, s);
@@ -684,10 +824,7 @@ hipError_t launch_prepare(const Params &P, hipStream_t s)
 
 hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned)
 {
-    const int64_t blocks = P.nvec * P.geo.nseg;
-    const void *fn = dtype == 0 ? (aligned ? (const void *)stats_kernel<0, true> : (const void *)stats_kernel<0, false>)
-                                : (aligned ? (const void *)stats_kernel<1, true> : (const void *)stats_kernel<1, false>);
-    return launch(fn, blocks, kBlock, P, s);
+    return launch(stats_fn(dtype, aligned), P.geo.G, kBlock, P, s);
 }
 
 hipError_t launch_scan(const Params &P, hipStream_t s, int dtype)
@@ -699,11 +836,15 @@ hipError_t launch_scan(const Params &P, hipStream_t s, int dtype)
 
 hipError_t launch_draw(const Params &P, hipStream_t s, int dtype, bool aligned)
 {
-    const int64_t rows8 = ((int64_t)P.B + kXcds - 1) / kXcds;
-    const int64_t blocks = rows8 * kXcds * P.geo.nseg2;
-    const void *fn = dtype == 0 ? (aligned ? (const void *)draw_kernel<0, true> : (const void *)draw_kernel<0, false>)
-                                : (aligned ? (const void *)draw_kernel<1, true> : (const void *)draw_kernel<1, false>);
-    return launch(fn, blocks, kBlock, P, s);
+    const void *tiles = dtype == 0
+        ? (aligned ? (const void *)draw_tiles_kernel<0, true> : (const void *)draw_tiles_kernel<0, false>)
+        : (aligned ? (const void *)draw_tiles_kernel<1, true> : (const void *)draw_tiles_kernel<1, false>);
+    const void *fin = dtype == 0
+        ? (aligned ? (const void *)draw_final_kernel<0, true> : (const void *)draw_final_kernel<0, false>)
+        : (aligned ? (const void *)draw_final_kernel<1, true> : (const void *)draw_final_kernel<1, false>);
+    hipError_t e = launch(tiles, (int64_t)P.B * P.geo.ndraw, kBlock, P, s);
+    if (e == hipSuccess) e = launch(fin, P.B, 64, P, s);
+    return e;
 }
 
 }  // namespace sv
