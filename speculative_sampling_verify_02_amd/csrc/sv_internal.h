@@ -294,6 +294,23 @@ __device__ __forceinline__ RawUnit<DT> load_raw(const void *base, int64_t unit, 
     return r;
 }
 
+// Word 3 of a raw (untyped, offset-addressed) buffer resource on gfx9-family GPUs.
+constexpr int kBufferWord3 = 0x00020000;
+
+// One unit through a buffer resource at a byte offset (16-byte aligned data).
+template <int DT>
+__device__ __forceinline__ RawUnit<DT> buffer_unit(__amdgpu_buffer_rsrc_t rs, uint32_t off)
+{
+    RawUnit<DT> r;
+    if constexpr (DT == 0) {
+        r.a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+    } else {
+        r.a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+        r.b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 16), 0, 0));
+    }
+    return r;
+}
+
 template <int DT>
 __device__ __forceinline__ void unpack(const RawUnit<DT> &r, float *x)
 {
@@ -362,7 +379,7 @@ __device__ __forceinline__ double wave_inclusive_sum(double v, int lane)
 int32_t stats_grid_cap(int dtype, bool aligned);
 hipError_t launch_prepare(const Params &P, hipStream_t s);
 hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned);
-hipError_t launch_scan(const Params &P, hipStream_t s, int dtype);
-hipError_t launch_draw(const Params &P, hipStream_t s, int dtype, bool aligned);
+hipError_t launch_verify(const Params &P, hipStream_t s, int dtype, bool aligned);
+hipError_t launch_draw_final(const Params &P, hipStream_t s, int dtype, bool aligned);
 
 }  // namespace sv

@@ -11,15 +11,14 @@
 // models (rayaq.ca "Speculative decoding", section "Why the output is exactly the
 // target's").
 //
-// scan_kernel gives each row one wave: it merges the pieces, computes p(x_j) and
-// q(x_j), and keeps x_j while u_j < min(1, p_j(x_j)/q_j(x_j)) (rayaq.ca
-// "Speculative decoding", section "One round", step 3), or while x_j equals the
-// argmax in greedy mode (section "The greedy case").
-//
-// draw_tiles_kernel re-reads only position K of each sampling row and sums the draw
-// weights per 512-logit tile: the residual max(0, p - q) after a rejection (step 4)
-// or p for the bonus token (step 5).  draw_final_kernel walks one row's tile sums
-// and one tile to the inverse-CDF token.
+// verify_kernel gives each row one wave for the accept scan: it merges the pieces,
+// computes p(x_j) and q(x_j), and keeps x_j while u_j < min(1, p_j(x_j)/q_j(x_j))
+// (rayaq.ca "Speculative decoding", section "One round", step 3), or while x_j
+// equals the argmax in greedy mode (section "The greedy case").  The workgroups of a
+// sampling row then re-read only position K and sum the draw weights per 512-logit
+// tile: the residual max(0, p - q) after a rejection (step 4) or p for the bonus
+// token (step 5).  draw_final_kernel walks one row's tile sums and one tile to the
+// inverse-CDF token.
 //
 // bf16 logits are processed in fp32 (exp2 on the hardware unit, fp64 accumulation
 // of 8-logit partial sums); fp32 logits are processed in fp64 throughout.
@@ -106,8 +105,8 @@ __device__ __forceinline__ void acc32_group(Acc32 &a, const float *x, const Temp
 {
     float cm = x[0];
 #pragma unroll
-    for (int i = 1; i < N; ++i) cm = fmaxf(cm, x[i]);
-    a.m = fmaxf(a.m, cm);
+    for (int i = 1; i < N; ++i) cm = __builtin_elementwise_maximum(cm, x[i]);
+    a.m = __builtin_elementwise_maximum(a.m, cm);
     const bool up = a.slow ? cm > a.mref : (cm * tc.c_hi > a.R || (!a.has_ref && cm > -INFINITY));
     if (__any(up)) {
         if (up) {
@@ -169,8 +168,8 @@ __device__ __forceinline__ void acc64_group(Acc64 &a, const float *x, const Temp
 {
     float cm = x[0];
 #pragma unroll
-    for (int i = 1; i < N; ++i) cm = fmaxf(cm, x[i]);
-    a.m = fmaxf(a.m, cm);
+    for (int i = 1; i < N; ++i) cm = __builtin_elementwise_maximum(cm, x[i]);
+    a.m = __builtin_elementwise_maximum(a.m, cm);
     const double sc = (double)cm * tc.c_eff;
     const bool up = sc > a.R || (!a.has_ref && cm > -INFINITY);
     if (__any(up)) {
@@ -208,7 +207,7 @@ __device__ __forceinline__ void accarg_group(AccArg &a, const float *x, int64_t 
 {
     float cm = x[0];
 #pragma unroll
-    for (int i = 1; i < N; ++i) cm = fmaxf(cm, x[i]);
+    for (int i = 1; i < N; ++i) cm = __builtin_elementwise_maximum(cm, x[i]);
     bool nan = false;
 #pragma unroll
     for (int i = 0; i < N; ++i) nan |= (x[i] != x[i]);
@@ -245,7 +244,7 @@ template <int DT, bool AL>
 __device__ Partial reduce_piece(const void *base, int64_t a, int64_t b, int64_t V, int rmode,
                                 const TempConst &tc)
 {
-    constexpr int N = kUnroll * kUnitElems;
+    constexpr int kHalf = kUnroll / 2 * kUnitElems;
     __shared__ float sh_f[kWaves];
     __shared__ double sh_d[kWaves];
     __shared__ int sh_i[kWaves], sh_n[kWaves];
@@ -256,30 +255,70 @@ __device__ Partial reduce_piece(const void *base, int64_t a, int64_t b, int64_t 
     Acc64 a64{-INFINITY, false, 0.0, 0.0};
     AccArg ag{-INFINITY, INT32_MAX, false};
 
-    // software pipeline: the next group's loads are in flight while this group is
-    // reduced
-    constexpr int64_t kStride = (int64_t)kBlock * kUnroll;
-    RawUnit<DT> cur[kUnroll];
+    // one group = kUnroll units per thread, unit k of thread t at u + t + k * kBlock
+    auto group = [&](const RawUnit<DT> *r, int64_t u) {
+        // two halves of kHalf logits each keep fewer values live at once
 #pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-        const int64_t uk = a + tid + (int64_t)k * kBlock;
-        cur[k] = uk < b ? load_raw<DT, AL>(base, uk, V) : neg_inf_unit<DT>();
+        for (int h = 0; h < 2; ++h) {
+            float x[kHalf];
+#pragma unroll
+            for (int k = 0; k < kUnroll / 2; ++k) unpack<DT>(r[h * (kUnroll / 2) + k], x + k * kUnitElems);
+            if (rmode == ROW_GREEDY) accarg_group<kHalf>(ag, x, u + (int64_t)h * (kUnroll / 2) * kBlock);
+            else if (DT == 0) acc32_group<kHalf>(a32, x, tc);
+            else acc64_group<kHalf>(a64, x, tc);
+        }
+    };
+
+    constexpr int64_t kStride = (int64_t)kBlock * kUnroll;
+    constexpr uint32_t kUnitBytes = DT == 0 ? 16u : 32u;
+    int64_t u_tail = a;   // first group start not covered by the unpredicated loop
+    if constexpr (AL) {
+        // full groups: unpredicated buffer loads at 32-bit offsets from the piece
+        // start, the next group's loads in flight while this one is reduced
+        // (an fp32 vector whose length is not a multiple of 8 ends in a partial unit;
+        // that unit is left to the predicated loop)
+        const int64_t n = b - a - ((DT == 1 && b * kUnitElems > V) ? 1 : 0);
+        const int64_t nfull = n / kStride;
+        if (nfull > 0 && n * kUnitBytes < ((int64_t)1 << 31)) {
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<char *>(static_cast<const char *>(base) + a * kUnitBytes), 0,
+                (int)(n * kUnitBytes), kBufferWord3);
+            auto load_group = [&](RawUnit<DT> *r, uint32_t off) {
+#pragma unroll
+                for (int k = 0; k < kUnroll; ++k) r[k] = buffer_unit<DT>(rs, off + (uint32_t)k * kBlock * kUnitBytes);
+            };
+            // two alternating register buffers (no copies between them, so waiting for
+            // one group's loads leaves the next group's loads in flight)
+            const uint32_t off0 = (uint32_t)tid * kUnitBytes;
+            const uint32_t step = (uint32_t)kStride * kUnitBytes;
+            RawUnit<DT> ra[kUnroll], rb[kUnroll];
+            load_group(ra, off0);
+            int64_t it = 0;
+            for (; it + 2 < nfull; it += 2) {   // prefetches always in range here
+                load_group(rb, off0 + (uint32_t)(it + 1) * step);
+                group(ra, a + it * kStride + tid);
+                load_group(ra, off0 + (uint32_t)(it + 2) * step);
+                group(rb, a + (it + 1) * kStride + tid);
+            }
+            if (it + 1 < nfull) {
+                load_group(rb, off0 + (uint32_t)(it + 1) * step);
+                group(ra, a + it * kStride + tid);
+                group(rb, a + (it + 1) * kStride + tid);
+            } else {
+                group(ra, a + it * kStride + tid);
+            }
+            u_tail = a + nfull * kStride;
+        }
     }
-    for (int64_t u = a + tid; u < b; u += kStride) {
-        RawUnit<DT> nxt[kUnroll];
+    // remaining units, predicated (logits past b read as -inf)
+    for (int64_t u = u_tail + tid; u - tid < b; u += kStride) {
+        RawUnit<DT> r[kUnroll];
 #pragma unroll
         for (int k = 0; k < kUnroll; ++k) {
-            const int64_t uk = u + kStride + (int64_t)k * kBlock;
-            nxt[k] = uk < b ? load_raw<DT, AL>(base, uk, V) : neg_inf_unit<DT>();
+            const int64_t uk = u + (int64_t)k * kBlock;
+            r[k] = uk < b ? load_raw<DT, AL>(base, uk, V) : neg_inf_unit<DT>();
         }
-        float x[N];
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) unpack<DT>(cur[k], x + k * kUnitElems);
-        if (rmode == ROW_GREEDY) accarg_group<N>(ag, x, u);
-        else if (DT == 0) acc32_group<N>(a32, x, tc);
-        else acc64_group<N>(a64, x, tc);
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) cur[k] = nxt[k];
+        group(r, u);
     }
 
     Partial out;
@@ -369,99 +408,97 @@ __global__ __launch_bounds__(kBlock) void stats_kernel(Params P)
 // ===========================================================================
 // accept scan: one wave per row
 // ===========================================================================
+constexpr int kPre = 4;   // pieces of a vector fetched up front (more are fetched later)
 
-// merge the pieces of streamed vector v: max and sum 2^((z - m) c), or argmax
-__device__ __forceinline__ void merge_vector(const Params &P, int64_t v, const TempConst &tc, bool greedy,
-                                             float &m, double &S, int32_t &idx, bool &nan)
+struct VecRecs {
+    Partial r[kPre];
+    int64_t v, w0, w1;    // streamed vector, first and last workgroup whose piece covers it
+};
+
+__device__ __forceinline__ void fetch_recs(const Params &P, int64_t v, VecRecs &R)
 {
-    const int64_t w0 = (v * P.geo.nunits) / P.geo.R;
-    const int64_t w1 = ((v + 1) * P.geo.nunits - 1) / P.geo.R;
+    R.v = v;
+    R.w0 = (v * P.geo.nunits) / P.geo.R;
+    R.w1 = ((v + 1) * P.geo.nunits - 1) / P.geo.R;
+#pragma unroll
+    for (int i = 0; i < kPre; ++i)
+        R.r[i] = (R.w0 + i <= R.w1) ? P.parts[R.w0 + i + v] : Partial{-INFINITY, INT32_MAX, 0.0};
+}
+
+__device__ __forceinline__ void merge_one(const Partial &q, bool greedy, const TempConst &tc, float &m,
+                                          double &S, int32_t &idx, bool &nan)
+{
+    if (greedy) {
+        if (q.m > m) {
+            m = q.m;
+            idx = q.idx;
+        } else if (q.m == m && q.idx < idx) {
+            idx = q.idx;
+        }
+        nan |= (q.s != q.s);
+        return;
+    }
+    if (q.m > m) {
+        if (m != -INFINITY) S *= exp2_f64(((double)m - (double)q.m) * tc.c_eff);
+        m = q.m;
+    }
+    S += q.m == -INFINITY ? q.s : q.s * exp2_f64(((double)q.m - (double)m) * tc.c_eff);
+}
+
+// merge the pieces of a vector: max and sum 2^((z - m) c), or first argmax
+__device__ __forceinline__ void merge_recs(const Params &P, const VecRecs &R, const TempConst &tc, bool greedy,
+                                           float &m, double &S, int32_t &idx, bool &nan)
+{
     m = -INFINITY;
     S = 0.0;
     idx = INT32_MAX;
     nan = false;
-    constexpr int kBuf = 8;
-    Partial buf[kBuf];
-    for (int64_t w = w0; w <= w1; w += kBuf) {
 #pragma unroll
-        for (int i = 0; i < kBuf; ++i)
-            buf[i] = (w + i <= w1) ? P.parts[w + i + v] : Partial{-INFINITY, INT32_MAX, 0.0};
-        if (greedy) {
-#pragma unroll
-            for (int i = 0; i < kBuf; ++i) {
-                if (buf[i].m > m || (buf[i].m == m && buf[i].idx < idx)) {
-                    idx = buf[i].m > m ? buf[i].idx : min(idx, buf[i].idx);
-                    m = buf[i].m;
-                }
-                nan |= (buf[i].s != buf[i].s);
-            }
-        } else {
-            float mm = m;
-#pragma unroll
-            for (int i = 0; i < kBuf; ++i) mm = fmaxf(mm, buf[i].m);
-            if (mm > m && m != -INFINITY) S *= exp2_f64(((double)m - (double)mm) * tc.c_eff);
-            m = mm;
-#pragma unroll
-            for (int i = 0; i < kBuf; ++i)
-                S += buf[i].m == -INFINITY ? buf[i].s : buf[i].s * exp2_f64(((double)buf[i].m - (double)m) * tc.c_eff);
-        }
-    }
+    for (int i = 0; i < kPre; ++i) merge_one(R.r[i], greedy, tc, m, S, idx, nan);
+    for (int64_t w = R.w0 + kPre; w <= R.w1; ++w) merge_one(P.parts[w + R.v], greedy, tc, m, S, idx, nan);
 }
 
+// The accept scan of one row by one wave (positions across lanes).  Returns what
+// the draw needs (identical on every lane); with `write`, also stores the row's
+// outputs.
 template <int DT>
-__global__ __launch_bounds__(kBlock) void scan_kernel(Params P)
+__device__ RowDraw scan_row(const Params &P, int32_t row, bool write)
 {
     const int lane = threadIdx.x & 63;
-    const int32_t row = blockIdx.x * kWaves + (threadIdx.x >> 6);
-
-    if (P.gamma != nullptr && P.hdr->status != 0) {
-        // inconsistent gamma array: every row and slot is invalid
-        const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-        const int64_t nthreads = (int64_t)gridDim.x * kBlock;
-        for (int64_t s = gid; s < P.nT; s += nthreads) P.emitted[s] = -1;
-        for (int64_t s = gid; s < P.nD; s += nthreads) {
-            if (P.p_x) P.p_x[s] = kQNaN;
-            if (P.q_x) P.q_x[s] = kQNaN;
-        }
-        if (row < P.B && lane == 0) {
-            P.n_accepted[row] = -1;
-            if (P.row_status) P.row_status[row] = ST_BAD_GAMMA;
-            if (P.resid) P.resid[row] = kQNaN;
-            P.draws[row].kind = DRAW_NONE;
-        }
-        return;
-    }
-    if (row >= P.B) return;
-
     const RowGeom G = row_geom(P, row);
     const int32_t g = G.gamma;
     const int64_t slot0 = row_slot0(P, G);
     const float T = P.temperature[row];
     const int32_t rm = row_mode(P.mode, T);
     const bool greedy = rm == ROW_GREEDY;
-    const TempConst tc = temp_const(rm == ROW_SAMPLE ? T : 1.0f);
-    const double Td = (double)T;
     int status = (rm == ROW_BAD_TEMP) ? ST_BAD_TEMP : 0;
     int32_t K = g;
     bool found = false;
-    float kmt = -INFINITY, kmd = -INFINITY;   // statistics at K (valid on every lane once known)
+    float kmt = -INFINITY, kmd = -INFINITY;   // statistics at K (on every lane once known)
     double kSt = 0.0, kSd = 0.0;
     int32_t kidx = -1;
+    int32_t x_keep = 0;                       // this lane's draft token (rows with gamma < 64)
 
     if (rm != ROW_BAD_TEMP) {
         for (int base = 0; base <= g; base += 64) {
             const int j = base + lane;
             const bool has_t = j <= g, has_d = j < g;
+            // every load of this chunk first
             int32_t x = 0;
             float u = 0.0f, zt = 0.0f, zd = 0.0f;
+            VecRecs rt, rd;
+            if (has_t) fetch_recs(P, slot0 + j, rt);
             if (has_d) {
                 x = P.tokens[G.d_off + j];
                 u = P.uniforms[G.t_off + j];
                 if (!greedy) {   // saved by the streaming pass
                     zt = P.zx[G.d_off + j];
                     zd = P.zx[P.nD + G.d_off + j];
+                    fetch_recs(P, slot0 + g + 1 + j, rd);
                 }
             }
+            x_keep = x;
+            const TempConst tc = temp_const(rm == ROW_SAMPLE ? T : 1.0f);
             const bool x_ok = x >= 0 && (int64_t)x < P.V;
             if (has_d && !x_ok) status |= ST_BAD_TOKEN;
             float mt = -INFINITY, md = -INFINITY;
@@ -469,17 +506,18 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(Params P)
             int32_t it = INT32_MAX, idd;
             bool nt = false, nd = false;
             bool reject = false;
-            if (has_t) merge_vector(P, slot0 + j, tc, greedy, mt, St, it, nt);
+            if (has_t) merge_recs(P, rt, tc, greedy, mt, St, it, nt);
             if (greedy) {
                 if (has_t && (nt || !(mt > -INFINITY && mt < INFINITY))) status |= ST_NONFINITE;
                 if (has_d) reject = x != it;
             } else {
                 if (has_t && !(St > 0.0 && St < INFINITY)) status |= ST_NONFINITE;
                 if (has_d) {
-                    merge_vector(P, slot0 + g + 1 + j, tc, false, md, Sd, idd, nd);
+                    merge_recs(P, rd, tc, false, md, Sd, idd, nd);
                     if (!(Sd > 0.0 && Sd < INFINITY)) status |= ST_NONFINITE;
                     double px = kQNaN, qx = kQNaN;
                     if (x_ok && St > 0.0 && St < INFINITY && Sd > 0.0 && Sd < INFINITY) {
+                        const double Td = (double)T;
                         px = exp(((double)zt - (double)mt) / Td) / St;
                         qx = exp(((double)zd - (double)md) / Td) / Sd;
                         double ratio;
@@ -492,8 +530,10 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(Params P)
                         }
                         reject = !((double)u < ratio);
                     }
-                    if (P.p_x) P.p_x[G.d_off + j] = px;
-                    if (P.q_x) P.q_x[G.d_off + j] = qx;
+                    if (write) {
+                        if (P.p_x) P.p_x[G.d_off + j] = px;
+                        if (P.q_x) P.q_x[G.d_off + j] = qx;
+                    }
                 }
             }
             const unsigned long long rb = __ballot(reject);
@@ -517,39 +557,59 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(Params P)
     status = wave_or_int(status);
     const bool invalid = (status & ST_INVALID) != 0;
 
-    for (int j = lane; j <= g; j += 64) {
-        int32_t e = -1;
-        if (!invalid) {
-            if (j < K) e = P.tokens[G.d_off + j];
-            else if (j == K && greedy) e = kidx;
+    RowDraw D{};
+    D.kind = DRAW_NONE;
+    if (!invalid && !greedy) {
+        D.kind = K < g ? DRAW_RESIDUAL : DRAW_BONUS;
+        D.K = K;
+        D.t_row = (int32_t)(G.t_off + K);
+        D.d_row = (int32_t)(G.d_off + K);
+        D.u = P.uniforms[G.t_off + g];
+        D.t_slot = (int32_t)(G.t_off + K);
+        D.m_t = kmt;
+        D.S_t = kSt;
+        D.m_d = kmd;
+        D.S_d = kSd;
+        D.T = T;
+    }
+    if (write) {
+        for (int j = lane; j <= g; j += 64) {
+            int32_t e = -1;
+            if (!invalid) {
+                if (j < K) e = g < 64 ? x_keep : P.tokens[G.d_off + j];
+                else if (j == K && greedy) e = kidx;
+            }
+            P.emitted[G.t_off + j] = e;
+            if (j < g && (invalid || greedy)) {
+                if (P.p_x) P.p_x[G.d_off + j] = kQNaN;
+                if (P.q_x) P.q_x[G.d_off + j] = kQNaN;
+            }
         }
-        P.emitted[G.t_off + j] = e;
-        if (j < g && (invalid || greedy)) {
-            if (P.p_x) P.p_x[G.d_off + j] = kQNaN;
-            if (P.q_x) P.q_x[G.d_off + j] = kQNaN;
+        if (lane == 0) {
+            P.n_accepted[row] = invalid ? -1 : K;
+            if (P.row_status) P.row_status[row] = status;
+            if (D.kind == DRAW_NONE && P.resid) P.resid[row] = kQNaN;
+            P.draws[row] = D;
         }
     }
-    if (lane == 0) {
-        P.n_accepted[row] = invalid ? -1 : K;
-        if (P.row_status) P.row_status[row] = status;
-        RowDraw D{};
-        D.kind = DRAW_NONE;
-        if (!invalid && !greedy) {
-            D.kind = K < g ? DRAW_RESIDUAL : DRAW_BONUS;
-            D.K = K;
-            D.t_row = (int32_t)(G.t_off + K);
-            D.d_row = (int32_t)(G.d_off + K);
-            D.u = P.uniforms[G.t_off + g];
-            D.t_slot = (int32_t)(G.t_off + K);
-            D.m_t = kmt;
-            D.S_t = kSt;
-            D.m_d = kmd;
-            D.S_d = kSd;
-            D.T = T;
-        } else if (P.resid) {
-            P.resid[row] = kQNaN;
-        }
-        P.draws[row] = D;
+    return D;
+}
+
+// Ragged batch whose gamma array is inconsistent: every row and slot is invalid.
+__device__ void invalidate_call(const Params &P, int32_t row, bool row_writer)
+{
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t s = gid; s < P.nT; s += nthreads) P.emitted[s] = -1;
+    for (int64_t s = gid; s < P.nD; s += nthreads) {
+        if (P.p_x) P.p_x[s] = kQNaN;
+        if (P.q_x) P.q_x[s] = kQNaN;
+    }
+    if (row_writer && row < P.B) {
+        P.n_accepted[row] = -1;
+        if (P.row_status) P.row_status[row] = ST_BAD_GAMMA;
+        if (P.resid) P.resid[row] = kQNaN;
+        P.draws[row].kind = DRAW_NONE;
     }
 }
 
@@ -629,12 +689,25 @@ struct DrawConst<1> {
 };
 
 template <int DT, bool AL>
-__global__ __launch_bounds__(kBlock) void draw_tiles_kernel(Params P)
+__global__ __launch_bounds__(kBlock) void verify_kernel(Params P)
 {
+    __shared__ RowDraw sD;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t row = blockIdx.x / P.geo.ndraw;
-    const int32_t piece = (int32_t)(blockIdx.x - row * P.geo.ndraw);
-    const RowDraw D = P.draws[row];
+    const int64_t per_row = P.mode == 1 ? 1 : P.geo.ndraw;
+    const int32_t row = (int32_t)(blockIdx.x / per_row);
+    const int32_t piece = (int32_t)(blockIdx.x - (int64_t)row * per_row);
+    if (P.gamma != nullptr && P.hdr->status != 0) {
+        invalidate_call(P, row, piece == 0 && tid == 0);
+        return;
+    }
+    // every workgroup of the row runs the scan (a few hundred bytes from L2); the
+    // first one stores the row's outputs
+    if (wave == 0) {
+        const RowDraw d = scan_row<DT>(P, row, piece == 0);
+        if (lane == 0) sD = d;
+    }
+    __syncthreads();
+    const RowDraw D = sD;
     if (D.kind == DRAW_NONE) return;
     DrawConst<DT> c;
     c.init(D);
@@ -827,24 +900,21 @@ hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned)
     return launch(stats_fn(dtype, aligned), P.geo.G, kBlock, P, s);
 }
 
-hipError_t launch_scan(const Params &P, hipStream_t s, int dtype)
+hipError_t launch_verify(const Params &P, hipStream_t s, int dtype, bool aligned)
 {
-    const int64_t blocks = ((int64_t)P.B + kWaves - 1) / kWaves;
-    const void *fn = dtype == 0 ? (const void *)scan_kernel<0> : (const void *)scan_kernel<1>;
-    return launch(fn, blocks, kBlock, P, s);
+    const void *fn = dtype == 0
+        ? (aligned ? (const void *)verify_kernel<0, true> : (const void *)verify_kernel<0, false>)
+        : (aligned ? (const void *)verify_kernel<1, true> : (const void *)verify_kernel<1, false>);
+    const int64_t per_row = P.mode == 1 ? 1 : P.geo.ndraw;
+    return launch(fn, (int64_t)P.B * per_row, kBlock, P, s);
 }
 
-hipError_t launch_draw(const Params &P, hipStream_t s, int dtype, bool aligned)
+hipError_t launch_draw_final(const Params &P, hipStream_t s, int dtype, bool aligned)
 {
-    const void *tiles = dtype == 0
-        ? (aligned ? (const void *)draw_tiles_kernel<0, true> : (const void *)draw_tiles_kernel<0, false>)
-        : (aligned ? (const void *)draw_tiles_kernel<1, true> : (const void *)draw_tiles_kernel<1, false>);
-    const void *fin = dtype == 0
+    const void *fn = dtype == 0
         ? (aligned ? (const void *)draw_final_kernel<0, true> : (const void *)draw_final_kernel<0, false>)
         : (aligned ? (const void *)draw_final_kernel<1, true> : (const void *)draw_final_kernel<1, false>);
-    hipError_t e = launch(tiles, (int64_t)P.B * P.geo.ndraw, kBlock, P, s);
-    if (e == hipSuccess) e = launch(fin, P.B, 64, P, s);
-    return e;
+    return launch(fn, P.B, 64, P, s);
 }
 
 }  // namespace sv
