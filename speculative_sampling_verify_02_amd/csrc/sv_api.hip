@@ -23,7 +23,7 @@ extern "C" size_t spec_verify_workspace_bytes(int32_t batch, int64_t n_target_ro
         (dtype != SV_BF16 && dtype != SV_F32))
         return 0;
     if (2 * n_target_rows - batch > INT32_MAX) return 0;
-    return sv::make_layout(batch, n_target_rows, vocab).total;
+    return sv::make_layout(batch, n_target_rows, vocab, dtype).total;
 }
 
 extern "C" const char *spec_verify_strerror(int32_t status)
@@ -70,7 +70,7 @@ extern "C" sv_status spec_verify(const void *target_logits, const void *draft_lo
         return SV_EINVAL;
     if (n_draft_rows > 0 && (!draft_tokens || (mode == SV_SAMPLE && !draft_logits))) return SV_EINVAL;
 
-    const sv::Layout L = sv::make_layout(batch, n_target_rows, vocab);
+    const sv::Layout L = sv::make_layout(batch, n_target_rows, vocab, dtype);
     if (workspace_bytes < L.total || ((uintptr_t)workspace & 255u) != 0) return SV_EWORKSPACE;
 
     // 16-byte vector loads need every logit row to start 16-byte aligned
@@ -102,12 +102,16 @@ extern "C" sv_status spec_verify(const void *target_logits, const void *draft_lo
     }
     P.hdr = reinterpret_cast<sv::Header *>(ws + L.hdr);
     P.rows = reinterpret_cast<sv::RowInfo *>(ws + L.rows);
-    P.vec_row = reinterpret_cast<int32_t *>(ws + L.vec_row);
+    P.vinfo = reinterpret_cast<sv::VecInfo *>(ws + L.vinfo);
     P.parts = reinterpret_cast<sv::Partial *>(ws + L.parts);
     P.zx = reinterpret_cast<float *>(ws + L.zx);
     P.draws = reinterpret_cast<sv::RowDraw *>(ws + L.draws);
     P.tiles = reinterpret_cast<sv::Sum2 *>(ws + L.tiles);
-    P.geo = sv::make_geometry(batch, n_target_rows, vocab, mode, sv::stats_grid_cap(dtype, aligned));
+    P.geo = sv::make_geometry(batch, n_target_rows, vocab, mode, dtype, sv::stats_grid_cap(dtype, aligned));
+    if (!gamma_per_row) {
+        P.geo.inv_t = 1.0 / ((double)gamma_uniform + 1.0);
+        P.geo.inv_d = gamma_uniform > 0 ? 1.0 / (double)gamma_uniform : 0.0;
+    }
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     hipError_t e = hipSuccess;

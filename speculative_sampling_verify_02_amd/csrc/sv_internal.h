@@ -12,16 +12,19 @@ namespace sv {
 // geometry constants
 // ---------------------------------------------------------------------------
 constexpr int kBlock = 256;              // threads per workgroup (4 wave64)
+constexpr int kStatsBlock = 768;         // streaming pass, aligned rows: 12 waves, one workgroup per CU
 constexpr int kWaves = kBlock / 64;
-constexpr int kUnitElems = 8;            // logits a lane loads at once (one 16-byte bf16 load)
-constexpr int kUnroll = 4;               // units in flight per thread in the streaming pass
+constexpr int kUnitElems = 8;            // logits per draw-tile lane (one 16-byte bf16 load)
 constexpr int kTileUnits = 64;           // draw tile: one unit per lane of a wave
 constexpr int kTileElems = kTileUnits * kUnitElems;   // 512 logits
 constexpr int kTilesPerWave = 4;         // draw: tiles a wave sums with all loads in flight
 constexpr int kTilesPerDrawWg = kTilesPerWave * kWaves;   // 16 tiles = 8192 logits
-constexpr int kXcds = 8;                 // MI355X: 8 XCDs, workgroups dealt round-robin
-constexpr int kMaxStatsGrid = 8192;      // cap of the streaming-pass grid
-constexpr int64_t kMinUnitsPerWg = 2048; // 8 units per thread at least
+// Streaming pass: a wave reads a half piece of 8 KB as 8 loads of 16 bytes per lane
+// (lane l's k-th load at byte 1024 k + 16 l), so bf16 halves hold 4096 logits and
+// fp32 halves 2048.
+constexpr int kItemLoads = 8;
+constexpr int64_t kItemBytes = 64 * 16 * kItemLoads;
+constexpr int kMaxStatsGrid = 16384;     // cap of the streaming-pass grid
 constexpr double kLog2e = 1.44269504088896340736;
 
 // row status bits (mirror SV_ROW_* of the public header)
@@ -50,10 +53,17 @@ struct RowInfo {           // packed offsets of one row (ragged batches)
     int32_t t_off, d_off, gamma, pad;
 };
 
-struct Partial {           // streaming-pass result of one (workgroup, vector) overlap
-    float m;               // max logit (-inf: no finite logit)
-    int32_t idx;           // greedy: first index of the max (INT32_MAX: none)
-    double s;              // sampling: sum of 2^((z - m) c); greedy: 0, or NaN if a NaN was seen
+struct Partial {           // streaming-pass result of one piece
+    float m;               // max logit (NaN if the overlap holds a NaN; -inf: no finite logit)
+    int32_t idx;           // greedy: first index of the max within the vector (INT32_MAX: none)
+    double s;              // sampling: sum over the overlap of 2^(z c - E(m)), E as in rec_ref
+};
+
+struct VecInfo {           // one streamed vector of a ragged batch (filled by prepare_kernel)
+    int32_t row;           // batch row
+    int32_t slot;          // index of the position's draft token (d_off + j), -1 at j = gamma
+    int32_t x;             // that draft token (when slot >= 0)
+    float T;               // the row's temperature
 };
 
 struct Sum2 {              // draw sums over one tile
@@ -73,56 +83,70 @@ struct RowDraw {           // what the draw needs about one row
     int32_t pad;
 };
 
-// Streaming pass: the vectors it reads (all target and draft positions in sampling
-// mode, target positions only in greedy mode) laid end to end as one range of
-// units, cut into G equal contiguous pieces, one per workgroup.
+// Streaming pass.  The vectors it reads are the target rows (vectors 0 .. nT-1) and,
+// in sampling mode, the draft rows (vectors nT .. nT+nD-1).  Each vector is cut into
+// ipv pieces of two halves of kItemBytes (the last piece shorter); piece v ipv + j is
+// piece j of vector v, and its record sits at parts[v ipv + j].  Wave w of the grid
+// reduces pieces w, w + nwaves, ... .
 struct Geometry {
-    int64_t nunits;        // ceil(V / 8)
+    int64_t nunits;        // ceil(V / 8): draw tiles
     int64_t nvec;          // vectors streamed
-    int64_t total_units;   // nvec * nunits
-    int64_t R;             // units per workgroup
-    int32_t G;             // workgroups
+    int64_t ie;            // logits per half piece
+    int64_t ipv;           // pieces per vector
+    int64_t nitems;        // pieces: nvec * ipv
+    int32_t G;             // streaming workgroups
     int32_t ntiles;        // draw tiles per vector
     int32_t ndraw;         // draw workgroups per row
     int32_t pad;
+    double inv_ipv;        // 1 / ipv, 1 / (gamma + 1), 1 / gamma (dense batches): quotients
+    double inv_t, inv_d;   // are estimated in fp64 and corrected by one step
 };
 
 struct Layout {
-    size_t hdr, rows, vec_row, parts, zx, draws, tiles, total;
+    size_t hdr, rows, vinfo, parts, zx, draws, tiles, total;
 };
 
-inline Geometry make_geometry(int32_t B, int64_t nT, int64_t V, int32_t mode, int32_t grid_cap)
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline int64_t item_elems(int32_t dtype) { return kItemBytes / (dtype == 0 ? 2 : 4); }
+
+inline Geometry make_geometry(int32_t B, int64_t nT, int64_t V, int32_t mode, int32_t dtype,
+                              int32_t grid_cap)
 {
     Geometry g{};
-    g.nunits = (V + kUnitElems - 1) / kUnitElems;
-    g.nvec = mode == 1 ? nT : 2 * nT - B;
-    g.total_units = g.nvec * g.nunits;
-    int64_t G = (g.total_units + kMinUnitsPerWg - 1) / kMinUnitsPerWg;
-    if (G > grid_cap) G = grid_cap;
-    if (G > kMaxStatsGrid) G = kMaxStatsGrid;
+    const int64_t nD = nT - B;
+    g.nunits = ceil_div(V, kUnitElems);
+    g.nvec = mode == 1 ? nT : nT + nD;
+    g.ie = item_elems(dtype);
+    g.ipv = ceil_div(V, 2 * g.ie);
+    g.nitems = g.nvec * g.ipv;
+    // the workgroups that fit at once, each with an equal share of the pieces
+    int64_t G = grid_cap < kMaxStatsGrid ? grid_cap : kMaxStatsGrid;
+    if (G > g.nitems) G = g.nitems;
     if (G < 1) G = 1;
-    g.R = (g.total_units + G - 1) / G;
-    if (g.R < 1) g.R = 1;
-    g.G = (int32_t)((g.total_units + g.R - 1) / g.R);
-    g.ntiles = (int32_t)((g.nunits + kTileUnits - 1) / kTileUnits);
-    g.ndraw = (g.ntiles + kTilesPerDrawWg - 1) / kTilesPerDrawWg;
+    g.G = (int32_t)G;
+    g.ntiles = (int32_t)ceil_div(g.nunits, kTileUnits);
+    g.ndraw = (int32_t)ceil_div(g.ntiles, kTilesPerDrawWg);
+    g.inv_ipv = 1.0 / (double)g.ipv;
     return g;
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Sized for the largest grid and for sampling mode, so it depends only on the shape.
-inline Layout make_layout(int32_t B, int64_t nT, int64_t V)
+// Sized for sampling mode, so it depends only on the shape and dtype.
+inline Layout make_layout(int32_t B, int64_t nT, int64_t V, int32_t dtype)
 {
-    const int64_t nvec = 2 * nT - B;
-    const int64_t ntiles = ((V + kUnitElems - 1) / kUnitElems + kTileUnits - 1) / kTileUnits;
+    const int64_t nD = nT - B;
+    const int64_t nvec = nT + nD;
+    const int64_t nitems = nvec * ceil_div(V, 2 * item_elems(dtype));
+    const int64_t ntiles = ceil_div(ceil_div(V, kUnitElems), kTileUnits);
     Layout L{};
     size_t off = 0;
     L.hdr = off;      off += align256(sizeof(Header));
     L.rows = off;     off += align256(sizeof(RowInfo) * (size_t)B);
-    L.vec_row = off;  off += align256(sizeof(int32_t) * (size_t)nvec);
-    L.parts = off;    off += align256(sizeof(Partial) * ((size_t)kMaxStatsGrid + (size_t)nvec));
-    L.zx = off;       off += align256(sizeof(float) * 2 * (size_t)(nT - B));
+    L.vinfo = off;    off += align256(sizeof(VecInfo) * (size_t)nvec);
+    L.parts = off;    off += align256(sizeof(Partial) * (size_t)nitems);
+    L.zx = off;       off += align256(sizeof(float) * 2 * (size_t)nD);
     L.draws = off;    off += align256(sizeof(RowDraw) * (size_t)B);
     L.tiles = off;    off += align256(sizeof(Sum2) * (size_t)B * (size_t)ntiles);
     L.total = off;
@@ -151,7 +175,7 @@ struct Params {
     int32_t *row_status;
     Header *hdr;
     RowInfo *rows;
-    int32_t *vec_row;
+    VecInfo *vinfo;        // ragged batches: per-vector row, token and temperature
     Partial *parts;
     float *zx;             // [2 nD]: target then draft logit at each draft token
     RowDraw *draws;
@@ -177,13 +201,6 @@ __device__ __forceinline__ RowGeom row_geom(const Params &P, int32_t row)
     return RowGeom{ri.t_off, ri.d_off, ri.gamma};
 }
 
-// First streamed vector ("slot") of a row: sampling streams the row's gamma+1 target
-// positions then its gamma draft positions; greedy streams target positions only.
-__device__ __forceinline__ int64_t row_slot0(const Params &P, const RowGeom &G)
-{
-    return P.mode == 1 ? G.t_off : G.t_off + G.d_off;
-}
-
 // Sampling, greedy, or an unusable temperature for a sampling row.
 __device__ __forceinline__ int32_t row_mode(int32_t mode, float T)
 {
@@ -194,28 +211,37 @@ __device__ __forceinline__ int32_t row_mode(int32_t mode, float T)
     return ROW_SAMPLE;
 }
 
-// exp((z - m) / T) = 2^((z - m) c) with c = log2(e) / T, split as c_hi + c_lo:
-// c_hi is c rounded down to fp32 and c_lo >= FLT_MIN > 0 the fp32 remainder, so
-// arguments built from both carry c to ~2^-48 and -inf logits stay -inf.
+// exp((z - m) / T) = 2^((z - m) c) with c = log2(e) / T.
+//   bf16 logits (fp32 arithmetic): c_hi = c rounded to fp32 is the scale itself (a
+//     relative change of the temperature below 2^-24), c_lo = 0, c_eff = c_hi.
+//   fp32 logits (fp64 arithmetic): c_eff = c_hi + c_lo carries c to ~2^-48, c_hi
+//     rounded down and c_lo >= FLT_MIN the fp32 remainder.
 struct TempConst {
     float c_hi, c_lo;
-    double c_eff;          // c_hi + c_lo exactly
+    double c_eff;
 };
 
+template <int DT>
 __device__ __forceinline__ TempConst temp_const(float T)
 {
     const double c = kLog2e / (double)T;
     TempConst tc;
-    tc.c_hi = __double2float_rd(c);
-    float lo = (float)(c - (double)tc.c_hi);
-    if (!(lo >= 1.175494351e-38f)) lo = 1.175494351e-38f;
-    tc.c_lo = lo;
-    tc.c_eff = (double)tc.c_hi + (double)tc.c_lo;
+    if constexpr (DT == 0) {
+        tc.c_hi = (float)c;
+        tc.c_lo = 0.0f;
+        tc.c_eff = (double)tc.c_hi;
+    } else {
+        tc.c_hi = __double2float_rd(c);
+        float lo = (float)(c - (double)tc.c_hi);
+        if (!(lo >= 1.175494351e-38f)) lo = 1.175494351e-38f;
+        tc.c_lo = lo;
+        tc.c_eff = (double)tc.c_hi + (double)tc.c_lo;
+    }
     return tc;
 }
 
-// References at or above this magnitude take the (z - m) route instead of the
-// integer reference (fp32 integers are exact below 2^24; the gap leaves room).
+// fp32 references B = ref * c at or above this magnitude take the (z - m) route:
+// the rounding of B (below 2^-4 here) stays a harmless shift of the exponents.
 constexpr float kFastRef = 1048576.0f;   // 2^20
 
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -373,6 +399,78 @@ __device__ __forceinline__ double wave_inclusive_sum(double v, int lane)
         if (lane >= o) v += t;
     }
     return v;
+}
+
+// floor(a / b) for 0 <= a < 2^53 and b >= 1, given inv_b = 1 / b rounded: the fp64
+// estimate is off by at most one, which the remainder test corrects.
+__device__ __forceinline__ int64_t qdiv(int64_t a, int64_t b, double inv_b)
+{
+    int64_t q = (int64_t)((double)a * inv_b);
+    const int64_t r = a - q * b;
+    if (r < 0) --q;
+    else if (r >= b) ++q;
+    return q;
+}
+
+// --- wave64 all-reductions returning a wave-uniform value: rotations within each
+// 16-lane row (DPP row_ror 1, 2, 4, 8) leave every lane with its row's result, and
+// the four rows are combined from lanes 0, 16, 32, 48 ---
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __int_as_float(dpp_i32<CTRL>(__float_as_int(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const int lo = dpp_i32<CTRL>((int)(uint32_t)b), hi = dpp_i32<CTRL>((int)(uint32_t)(b >> 32));
+    return __longlong_as_double((long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+__device__ __forceinline__ float readlane_f32(float v, int l)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double readlane_f64(double v, int l)
+{
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// maximum that propagates NaN
+__device__ __forceinline__ float nmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+__device__ __forceinline__ float wave_umax_f32(float v)
+{
+    v = nmax(v, dpp_f32<0x121>(v));
+    v = nmax(v, dpp_f32<0x122>(v));
+    v = nmax(v, dpp_f32<0x124>(v));
+    v = nmax(v, dpp_f32<0x128>(v));
+    return nmax(nmax(readlane_f32(v, 0), readlane_f32(v, 16)), nmax(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+__device__ __forceinline__ int wave_umin_i32(int v)
+{
+    v = min(v, dpp_i32<0x121>(v));
+    v = min(v, dpp_i32<0x122>(v));
+    v = min(v, dpp_i32<0x124>(v));
+    v = min(v, dpp_i32<0x128>(v));
+    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+__device__ __forceinline__ double wave_usum_f64(double v)
+{
+    v += dpp_f64<0x121>(v);
+    v += dpp_f64<0x122>(v);
+    v += dpp_f64<0x124>(v);
+    v += dpp_f64<0x128>(v);
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
 // launchers (sv_kernels.hip)

@@ -1,27 +1,28 @@
 // HIP kernels of the speculative-sampling verification step for gfx950.
 //
-// stats_kernel streams every logit once.  The vectors it reads (the gamma+1 target
-// and gamma draft positions of every row, or only target positions in greedy mode)
-// are laid end to end and cut into equal contiguous pieces, one per workgroup, so
-// every workgroup does the same work and the grid ends together.  For each
-// (workgroup, vector) overlap it writes the maximum and the sum of exp((z - m)/T)
-// (sampling rows) or the first argmax (greedy rows).  The temperature softmax these
-// summarize is the softened output of brunomaga.github.io "inference-distillation-
-// speculative-decoding", section "Knowledge distillation", with one T for both
-// models (rayaq.ca "Speculative decoding", section "Why the output is exactly the
-// target's").
+// stats_kernel streams every logit once.  The vectors it reads are the target rows
+// and (sampling mode) the draft rows of the batch, two contiguous arrays cut into
+// 8 KB items; wave w of the grid reads items w, w + nwaves, ..., each as eight
+// 16-byte loads per lane with the next item's loads in flight while one is reduced.
+// For each (item, vector) overlap the wave writes one record: the maximum and the
+// sum of exp((z - m)/T) (sampling rows) or the first argmax (greedy rows).  The
+// temperature softmax these summarize is the softened output of brunomaga.github.io
+// "inference-distillation-speculative-decoding", section "Knowledge distillation",
+// with one T for both models (rayaq.ca "Speculative decoding", section "Why the
+// output is exactly the target's").  The wave also keeps the logit at each
+// position's draft token when it passes through its registers.
 //
-// verify_kernel gives each row one wave for the accept scan: it merges the pieces,
-// computes p(x_j) and q(x_j), and keeps x_j while u_j < min(1, p_j(x_j)/q_j(x_j))
-// (rayaq.ca "Speculative decoding", section "One round", step 3), or while x_j
-// equals the argmax in greedy mode (section "The greedy case").  The workgroups of a
-// sampling row then re-read only position K and sum the draw weights per 512-logit
-// tile: the residual max(0, p - q) after a rejection (step 4) or p for the bonus
-// token (step 5).  draw_final_kernel walks one row's tile sums and one tile to the
-// inverse-CDF token.
+// verify_kernel merges a row's records per vector (one wave per vector), then one
+// wave runs the accept scan over the positions: it keeps x_j while u_j < min(1,
+// p_j(x_j)/q_j(x_j)) (rayaq.ca "Speculative decoding", section "One round", step 3),
+// or while x_j equals the argmax in greedy mode (section "The greedy case").  The
+// workgroups of a sampling row then re-read only position K and sum the draw weights
+// per 512-logit tile: the residual max(0, p - q) after a rejection (step 4) or p for
+// the bonus token (step 5).  draw_final_kernel walks one row's tile sums and one
+// tile to the inverse-CDF token.
 //
-// bf16 logits are processed in fp32 (exp2 on the hardware unit, fp64 accumulation
-// of 8-logit partial sums); fp32 logits are processed in fp64 throughout.
+// bf16 logits are processed in fp32 (exp2 on the hardware unit, fp64 sums across
+// lanes); fp32 logits are processed in fp64 throughout.
 #include <float.h>
 #include <limits.h>
 
@@ -32,7 +33,7 @@ namespace sv {
 constexpr double kQNaN = __builtin_nan("");
 
 // ===========================================================================
-// prepare: packed offsets of a ragged batch
+// prepare: packed offsets of a ragged batch and the per-vector table
 // ===========================================================================
 __global__ __launch_bounds__(1024) void prepare_kernel(Params P)
 {
@@ -65,12 +66,14 @@ __global__ __launch_bounds__(1024) void prepare_kernel(Params P)
         const int64_t t_off = pt + it - vt, d_off = pd + id - vd;
         if (in) {
             P.rows[i] = RowInfo{(int32_t)t_off, (int32_t)d_off, g, 0};
-            // streamed slots of row i (bounds-checked: totals are validated below)
-            const int64_t s0 = P.mode == 1 ? t_off : t_off + d_off;
-            const int64_t n = P.mode == 1 ? (int64_t)g + 1 : 2 * (int64_t)g + 1;
-            if (s0 < P.geo.nvec) {
-                const int64_t e = s0 + n < P.geo.nvec ? s0 + n : P.geo.nvec;
-                for (int64_t k = s0; k < e; ++k) P.vec_row[k] = (int32_t)i;
+            // the row's vectors (bounds-checked: the totals are validated below)
+            const float T = P.temperature[i];
+            for (int64_t k = 0; k <= g && t_off + k < P.nT; ++k) {
+                const bool has_x = k < g && d_off + k < P.nD;
+                const int32_t slot = has_x ? (int32_t)(d_off + k) : -1;
+                P.vinfo[t_off + k] = VecInfo{(int32_t)i, slot, has_x ? P.tokens[d_off + k] : -1, T};
+                if (P.mode == 0 && has_x)
+                    P.vinfo[P.nT + d_off + k] = VecInfo{(int32_t)i, slot, P.tokens[d_off + k], T};
             }
         }
         __syncthreads();
@@ -84,515 +87,821 @@ __global__ __launch_bounds__(1024) void prepare_kernel(Params P)
 // streaming pass
 // ===========================================================================
 
-// Sampling accumulator of one thread, fp32 arithmetic (bf16 logits).  s holds
-// sum 2^(z c - R) against an integer reference R, or, on the slow route (scaled
-// logits at or beyond 2^20 in magnitude), sum 2^((z - mref) c).  R moves to the
-// smallest integer at or above a group's scaled maximum when that maximum passes
-// it, an exact power-of-two rescale of s, so the largest terms have arguments in
-// (-1, 0].  Before any finite logit R = 0 and has_ref is false: -inf logits add 0
-// and a NaN logit makes s NaN.  Rare paths sit behind wave-uniform branches.
-struct Acc32 {
-    float m;        // running maximum
-    float R;        // integer reference (fast route)
-    float mref;     // reference logit (slow route)
-    bool has_ref;
-    bool slow;
-    double s;
+// What the pass needs about one streamed vector.
+struct VecCtx {
+    int32_t row;
+    int32_t slot;   // index of the position's draft token, -1 if none is tested there
+    int32_t x;      // that token
+    float T;
+    bool target;    // a target row (else a draft row)
 };
 
-template <int N>
-__device__ __forceinline__ void acc32_group(Acc32 &a, const float *x, const TempConst &tc)
+// v: global vector index (target rows first, then draft rows)
+__device__ __forceinline__ VecCtx vec_ctx(const Params &P, int64_t v)
 {
-    float cm = x[0];
-#pragma unroll
-    for (int i = 1; i < N; ++i) cm = __builtin_elementwise_maximum(cm, x[i]);
-    a.m = __builtin_elementwise_maximum(a.m, cm);
-    const bool up = a.slow ? cm > a.mref : (cm * tc.c_hi > a.R || (!a.has_ref && cm > -INFINITY));
-    if (__any(up)) {
-        if (up) {
-            const float Rn = ceilf(cm * tc.c_hi);
-            const bool slow = !(fabsf(Rn) < kFastRef);
-            if (a.has_ref) {
-                if (!a.slow && !slow) {
-                    a.s = ldexp(a.s, (int)(a.R - Rn));
-                } else {
-                    const double Rold = a.slow ? (double)a.mref * tc.c_eff : (double)a.R;
-                    const double Rnew = slow ? (double)cm * tc.c_eff : (double)Rn;
-                    a.s *= exp2_f64(Rold - Rnew);
-                }
-            }
-            a.R = slow ? 0.0f : Rn;
-            a.mref = cm;
-            a.slow = slow;
-            a.has_ref = true;
-        }
+    VecCtx c;
+    c.target = v < P.nT;
+    if (P.gamma == nullptr) {
+        const bool target = c.target;
+        const int64_t vloc = target ? v : v - P.nT;
+        const int64_t g = P.gamma_uniform;
+        const int64_t per = target ? g + 1 : g;   // g > 0 whenever draft vectors exist
+        const int64_t row = qdiv(vloc, per, target ? P.geo.inv_t : P.geo.inv_d);
+        const int64_t j = vloc - row * per;
+        c.row = (int32_t)row;
+        c.slot = (P.mode == 0 && j < g) ? (int32_t)(row * g + j) : -1;
+        c.x = c.slot >= 0 ? P.tokens[c.slot] : -1;
+        c.T = P.temperature[row];
+    } else {
+        const VecInfo vi = P.vinfo[v];
+        c.row = vi.row;
+        c.slot = P.mode == 0 ? vi.slot : -1;
+        c.x = vi.x;
+        c.T = vi.T;
     }
-    float e[N];
-    if (__any(a.slow)) {
+    return c;
+}
+
+// One half-piece as this lane holds it: load k covers bytes [1024 k + 16 l, +16) of
+// the half.
+struct ItemRaw {
+    uint4 d[kItemLoads];
+};
+
+// logits per 16-byte load
+template <int DT> constexpr int kE = DT == 0 ? 8 : 4;
+
+// Logits of piece j of vector v in half h: [j 2 ie + h ie, +n), n in [0, ie].
+__device__ __forceinline__ int32_t half_len(const Params &P, int64_t j, int h)
+{
+    const int64_t e0 = (2 * j + h) * P.geo.ie;
+    const int64_t n = P.V - e0;
+    return (int32_t)(n < 0 ? 0 : (n < P.geo.ie ? n : P.geo.ie));
+}
+
+// Issue the loads of half h of piece j of vector v.  Offsets past the end of the
+// vector are clamped to its last 16 bytes (those logits are masked when the half is
+// reduced).  An empty half, or live = false (no piece left), reads an empty window at
+// the start of the vector (nothing to read, nothing used), which keeps every load of
+// the pipeline unconditional.
+template <int DT, bool AL>
+__device__ __forceinline__ void half_begin(const Params &P, int64_t v, int64_t j, int h, bool live, ItemRaw &r,
+                                           int lane)
+{
+    constexpr int64_t esz = DT == 0 ? 2 : 4;
+    if (!live) v = j = 0;
+    const int64_t n = live ? half_len(P, j, h) : 0;
+    const bool target = v < P.nT;
+    const int64_t row = target ? v : v - P.nT;
+    const int64_t e0 = n > 0 ? (2 * j + h) * P.geo.ie : 0;
+    const char *base = static_cast<const char *>(target ? P.target : P.draft) + (row * P.V + e0) * esz;
+    if constexpr (AL) {
+        const uint32_t nbytes = (uint32_t)(n * esz);   // a multiple of 16
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, (int)nbytes, kBufferWord3);
+        const uint32_t last = nbytes > 16u ? nbytes - 16u : 0u;
 #pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const float d = x[i] - a.mref;
-            const float es = hw_exp2(fmaf(d, tc.c_hi, d * tc.c_lo));
-            const float ef = hw_exp2(fmaf(x[i], tc.c_lo, fmaf(x[i], tc.c_hi, -a.R)));
-            e[i] = a.slow ? es : ef;
+        for (int k = 0; k < kItemLoads; ++k) {
+            uint32_t off = (uint32_t)k * 1024u + (uint32_t)lane * 16u;
+            off = off < last ? off : last;
+            r.d[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
         }
     } else {
+        const int64_t nl = n > 0 ? n : 1;
 #pragma unroll
-        for (int i = 0; i < N; ++i) e[i] = hw_exp2(fmaf(x[i], tc.c_lo, fmaf(x[i], tc.c_hi, -a.R)));
-    }
+        for (int k = 0; k < kItemLoads; ++k) {
+            uint32_t w[4];
+            if constexpr (DT == 0) {
+                const uint16_t *p = reinterpret_cast<const uint16_t *>(base);
 #pragma unroll
-    for (int w = 1; w < N; w <<= 1)
+                for (int t = 0; t < 4; ++t) {
+                    const int64_t e = (int64_t)k * 512 + lane * 8 + 2 * t;
+                    const int64_t e_lo = e < nl ? e : nl - 1, e_hi = e + 1 < nl ? e + 1 : nl - 1;
+                    w[t] = (uint32_t)p[e_lo] | ((uint32_t)p[e_hi] << 16);
+                }
+            } else {
+                const uint32_t *p = reinterpret_cast<const uint32_t *>(base);
 #pragma unroll
-        for (int i = 0; i + w < N; i += 2 * w) e[i] += e[i + w];
-    a.s += (double)e[0];
-}
-
-// this thread's sum relative to its own maximum m: sum 2^((z - m) c)
-__device__ __forceinline__ double acc32_final(const Acc32 &a, const TempConst &tc)
-{
-    if (!a.has_ref) return a.s;   // 0, or NaN
-    const double Rd = a.slow ? (double)a.mref * tc.c_eff : (double)a.R;
-    return a.s * exp2_f64(Rd - (double)a.m * tc.c_eff);
-}
-
-// Sampling accumulator in fp64 (fp32 logits), same scheme with an fp64 reference.
-struct Acc64 {
-    float m;
-    bool has_ref;
-    double R;
-    double s;
-};
-
-template <int N>
-__device__ __forceinline__ void acc64_group(Acc64 &a, const float *x, const TempConst &tc)
-{
-    float cm = x[0];
-#pragma unroll
-    for (int i = 1; i < N; ++i) cm = __builtin_elementwise_maximum(cm, x[i]);
-    a.m = __builtin_elementwise_maximum(a.m, cm);
-    const double sc = (double)cm * tc.c_eff;
-    const bool up = sc > a.R || (!a.has_ref && cm > -INFINITY);
-    if (__any(up)) {
-        if (up) {
-            const double Rn = ceil(sc);
-            if (a.has_ref) {
-                const double sh = a.R - Rn;
-                a.s = sh < -2000.0 ? a.s * 0.0 : ldexp(a.s, (int)sh);
+                for (int t = 0; t < 4; ++t) {
+                    const int64_t e = (int64_t)k * 256 + lane * 4 + t;
+                    w[t] = p[e < nl ? e : nl - 1];
+                }
             }
-            a.R = Rn;
-            a.has_ref = true;
+            r.d[k] = make_uint4(w[0], w[1], w[2], w[3]);
         }
     }
-    double t = 0.0;
-#pragma unroll
-    for (int i = 0; i < N; ++i) t += exp2_f64(fma((double)x[i], tc.c_eff, -a.R));
-    a.s += t;
 }
 
-__device__ __forceinline__ double acc64_final(const Acc64 &a, const TempConst &tc)
+// Logits at half offsets n and beyond become -inf (the short end of a vector).  With
+// AL the rows hold whole 16-byte loads, so the test is per load.
+template <int DT, bool AL>
+__device__ __forceinline__ void mask_tail(ItemRaw &r, int lane, int n)
 {
-    if (!a.has_ref) return a.s;
-    return a.s * exp2_f64(a.R - (double)a.m * tc.c_eff);
+    constexpr int E = kE<DT>;
+    constexpr uint32_t kNinf = DT == 0 ? 0xff80ff80u : 0xff800000u;
+#pragma unroll
+    for (int k = 0; k < kItemLoads; ++k) {
+        if constexpr (AL) {
+            if (k * 64 * E + lane * E >= n) r.d[k] = make_uint4(kNinf, kNinf, kNinf, kNinf);
+        } else {
+            uint32_t w[4] = {r.d[k].x, r.d[k].y, r.d[k].z, r.d[k].w};
+#pragma unroll
+            for (int t = 0; t < E; ++t) {
+                if (k * 64 * E + lane * E + t < n) continue;
+                if constexpr (DT == 0) w[t / 2] = (t & 1) ? ((w[t / 2] & 0xffffu) | 0xff800000u) : ((w[t / 2] & 0xffff0000u) | 0xff80u);
+                else w[t] = 0xff800000u;
+            }
+            r.d[k] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
 }
 
-struct AccArg {
-    float best;
-    int32_t idx;
-    bool nan_seen;
+// bf16 pairs to fp32 by byte permutes (two operand orders): other ways of unpacking,
+// so that a pass that re-reads the registers recomputes the values instead of keeping
+// an earlier pass's (or another branch's) values live
+template <int FORM>
+__device__ __forceinline__ float bf16_lo_f(uint32_t w)
+{
+    return __uint_as_float(FORM == 1 ? __builtin_amdgcn_perm(0u, w, 0x01000c0cu) : __builtin_amdgcn_perm(w, 0u, 0x05040c0cu));
+}
+template <int FORM>
+__device__ __forceinline__ float bf16_hi_f(uint32_t w)
+{
+    return __uint_as_float(FORM == 1 ? __builtin_amdgcn_perm(0u, w, 0x03020c0cu) : __builtin_amdgcn_perm(w, 0u, 0x07060c0cu));
+}
+
+// The logits of load k on this lane (FORM picks the bf16 unpacking: 0 shifts and
+// masks, 1 and 2 byte permutes).
+template <int DT, int FORM = 0>
+__device__ __forceinline__ void lane_vals(const ItemRaw &r, int k, float *x)
+{
+    const uint4 w = r.d[k];
+    if constexpr (DT == 0 && FORM != 0) {
+        x[0] = bf16_lo_f<FORM>(w.x); x[1] = bf16_hi_f<FORM>(w.x);
+        x[2] = bf16_lo_f<FORM>(w.y); x[3] = bf16_hi_f<FORM>(w.y);
+        x[4] = bf16_lo_f<FORM>(w.z); x[5] = bf16_hi_f<FORM>(w.z);
+        x[6] = bf16_lo_f<FORM>(w.w); x[7] = bf16_hi_f<FORM>(w.w);
+    } else if constexpr (DT == 0) {
+        x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
+        x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+        x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z);
+        x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+    } else {
+        x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y);
+        x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ float lane_max(const ItemRaw &r)
+{
+    constexpr int E = kE<DT>;
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kItemLoads; ++k) {
+        float x[E];
+        lane_vals<DT>(r, k, x);
+#pragma unroll
+        for (int t = 0; t < E; ++t) m = nmax(m, x[t]);
+    }
+    return m;
+}
+
+__device__ __forceinline__ float wave_usum_f32(float v)
+{
+    v += dpp_f32<0x121>(v);
+    v += dpp_f32<0x122>(v);
+    v += dpp_f32<0x124>(v);
+    v += dpp_f32<0x128>(v);
+    return v;
+}
+
+// fp64 total of a wave of fp32 lane values (fp32 within rows of 16 lanes)
+__device__ __forceinline__ double wave_total(float v)
+{
+    v = wave_usum_f32(v);
+    return ((double)readlane_f32(v, 0) + (double)readlane_f32(v, 16)) +
+           ((double)readlane_f32(v, 32) + (double)readlane_f32(v, 48));
+}
+
+// 2^d for a double d in fp32: the integer part exactly, the fraction on the hardware unit
+__device__ __forceinline__ float exp2_split(double d)
+{
+    const double n = rint(d);
+    return ldexpf(hw_exp2((float)(d - n)), (int)n);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 sampling piece.  Every lane sums 2^(z c - E) over its logits against its
+// own reference E: E = B = fl(R c) for a reference logit R (E = B + fma(R, c, -B),
+// the exact R c, when |B| >= 2^30, where the rounding of B would matter).  R starts
+// as the largest logit of the lane's first load; when a lane's sum over a half
+// overflows (a logit far above R) the half is summed again, from registers, against
+// the lane's maximum.  The epilogue brings the lanes to the piece maximum M.
+// ---------------------------------------------------------------------------
+struct LaneSum {
+    float m;      // maximum so far (NaN-propagating)
+    float s;      // sum 2^(z c - E) so far (0 while m = -inf)
+    float Bhi;    // fl(R c)
+    float Blo;    // R c - Bhi (used when huge)
+    double E;     // the reference of s
+    bool huge;    // wave-uniform: the two-part reference is in use
 };
 
-// x holds kUnroll units, unit k at index u + k * kBlock
-template <int N>
-__device__ __forceinline__ void accarg_group(AccArg &a, const float *x, int64_t u)
+__device__ __forceinline__ void set_ref(LaneSum &a, float R, float c)
 {
-    float cm = x[0];
+    a.Bhi = R * c;
+    a.Blo = fmaf(R, c, -a.Bhi);
+    a.huge = __any(!(fabsf(a.Bhi) < 0x1p30f));
+    a.E = a.huge ? (double)a.Bhi + (double)a.Blo : (double)a.Bhi;
+}
+
+// add one half (first: the piece's first half, which sets the references)
+__device__ __forceinline__ void sample_half(const ItemRaw &r, float c, LaneSum &a, bool first)
+{
+    if (first) {
+        float x[8];
+        lane_vals<0>(r, 0, x);
+        float R = x[0];
 #pragma unroll
-    for (int i = 1; i < N; ++i) cm = __builtin_elementwise_maximum(cm, x[i]);
+        for (int t = 1; t < 8; ++t) R = nmax(R, x[t]);
+        a.m = -INFINITY;
+        a.s = 0.0f;
+        set_ref(a, R, c);
+    }
+    const float m_prev = a.m, s_prev = a.s;
+    const double E_prev = a.E;
+    float acc[kItemLoads];
+#pragma unroll
+    for (int k = 0; k < kItemLoads; ++k) {
+        float x[8];
+        lane_vals<0, 1>(r, k, x);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) a.m = nmax(a.m, x[t]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) x[t] = hw_exp2(fmaf(x[t], c, -a.Bhi));
+#pragma unroll
+        for (int w = 1; w < 8; w <<= 1)
+#pragma unroll
+            for (int t = 0; t + w < 8; t += 2 * w) x[t] += x[t + w];
+        acc[k] = x[0];
+    }
+#pragma unroll
+    for (int w = 1; w < kItemLoads; w <<= 1)
+#pragma unroll
+        for (int k = 0; k + w < kItemLoads; k += 2 * w) acc[k] += acc[k + w];
+    // a lane whose logits are finite but whose sum is not, or a two-part reference: the
+    // references move to the lanes' maxima, the earlier sum is rescaled, and the half is
+    // summed again (from registers) with the two-part reference when needed
+    const bool over = !(acc[0] <= 3.402823466e38f) && fabsf(a.m) <= 3.402823466e38f;
+    if (__any(over) || a.huge) {
+        const float R = fabsf(a.m) <= 3.402823466e38f ? a.m : 0.0f;
+        set_ref(a, R, c);
+        a.s = m_prev == -INFINITY ? 0.0f : s_prev * (float)exp2_f64(E_prev - a.E);
+        const float Blo = a.huge ? a.Blo : 0.0f;
+        float acc2[kItemLoads];
+#pragma unroll
+        for (int k = 0; k < kItemLoads; ++k) {
+            float x[8];
+            lane_vals<0, 2>(r, k, x);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) x[t] = hw_exp2(fmaf(x[t], c, -a.Bhi) - Blo);
+#pragma unroll
+            for (int w = 1; w < 8; w <<= 1)
+#pragma unroll
+                for (int t = 0; t + w < 8; t += 2 * w) x[t] += x[t + w];
+            acc2[k] = x[0];
+        }
+#pragma unroll
+        for (int w = 1; w < kItemLoads; w <<= 1)
+#pragma unroll
+            for (int k = 0; k + w < kItemLoads; k += 2 * w) acc2[k] += acc2[k + w];
+        acc[0] = acc2[0];
+    }
+    a.s += acc[0];
+    if (a.m == -INFINITY) a.s = 0.0f;
+}
+
+// The piece's record from the lane sums: m = M, s = sum 2^(z c - E_M) with
+// E_M = fl(M c) (ref = M, in idx) or, when |fl(M c)| >= 2^30, the exact M c (ref = NaN).
+__device__ __forceinline__ Partial sample_record(const LaneSum &a, float c)
+{
+    const float M = wave_umax_f32(a.m);
+    Partial p{M, 0, 0.0};
+    if (M == -INFINITY) return p;
+    if (!(fabsf(M) <= 3.402823466e38f)) {   // a NaN or +inf logit
+        p.idx = __float_as_int(__builtin_nanf(""));
+        p.s = (double)__builtin_nanf("");
+        return p;
+    }
+    const float BM = M * c;
+    const bool exact = !(fabsf(BM) < 0x1p30f);
+    const double EM = exact ? (double)M * (double)c : (double)BM;
+    const float t = a.m == -INFINITY ? 0.0f : a.s * exp2_split(a.E - EM);
+    p.idx = __float_as_int(exact ? __builtin_nanf("") : M);
+    p.s = wave_total(t);
+    return p;
+}
+
+// ---------------------------------------------------------------------------
+// greedy piece: first index of the maximum (per lane, then across the wave)
+// ---------------------------------------------------------------------------
+struct LaneArg {
+    float best;
+    int32_t idx;   // piece offset
+    bool nan;
+};
+
+template <int DT>
+__device__ __forceinline__ void argmax_half(const ItemRaw &r, int lane, int base, LaneArg &a)
+{
+    constexpr int E = kE<DT>;
+    // per load maximum, then the first load holding the half's lane maximum (strictly
+    // greater wins, so the earliest load keeps ties)
+    float mh = -INFINITY;
+    int kb = 0;
     bool nan = false;
 #pragma unroll
-    for (int i = 0; i < N; ++i) nan |= (x[i] != x[i]);
-    a.nan_seen |= nan;
-    const bool up = cm > a.best;
-    if (__any(up)) {
-        if (up) {
-            a.best = cm;
-            int first = N - 1;
+    for (int k = 0; k < kItemLoads; ++k) {
+        float x[E];
+        lane_vals<DT>(r, k, x);
+        float lm = x[0];
 #pragma unroll
-            for (int i = N - 1; i >= 0; --i)
-                if (x[i] == cm) first = i;
-            a.idx = (int32_t)((u + (int64_t)(first / kUnitElems) * kBlock) * kUnitElems + first % kUnitElems);
+        for (int t = 1; t < E; ++t) lm = nmax(lm, x[t]);
+        nan |= lm != lm;
+        if (lm > mh) {
+            mh = lm;
+            kb = k;
         }
+    }
+    a.nan |= nan;
+    // the first logit of that load equal to it
+    uint4 w = r.d[0];
+#pragma unroll
+    for (int k = 1; k < kItemLoads; ++k)
+        if (k == kb) w = r.d[k];
+    ItemRaw one;
+    one.d[0] = w;
+    float x[E];
+    lane_vals<DT, 1>(one, 0, x);
+    int t0 = E - 1;
+#pragma unroll
+    for (int t = E - 2; t >= 0; --t)
+        if (x[t] == mh) t0 = t;
+    if (mh > a.best) {
+        a.best = mh;
+        a.idx = base + kb * 64 * E + lane * E + t0;
     }
 }
 
-// A unit past the end of the piece, read as -inf logits.
-template <int DT>
-__device__ __forceinline__ RawUnit<DT> neg_inf_unit()
+__device__ __forceinline__ Partial argmax_record(const LaneArg &a)
 {
-    RawUnit<DT> r;
-    if constexpr (DT == 0) {
-        r.a = make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
-    } else {
-        r.a = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        r.b = r.a;
-    }
-    return r;
+    const float M = wave_umax_f32(a.nan ? __builtin_nanf("") : a.best);
+    return Partial{M, wave_umin_i32(a.best == M ? a.idx : INT32_MAX), 0.0};
 }
 
-// One vector piece [a, b) (units) by the whole workgroup.
-template <int DT, bool AL>
-__device__ Partial reduce_piece(const void *base, int64_t a, int64_t b, int64_t V, int rmode,
-                                const TempConst &tc)
-{
-    constexpr int kHalf = kUnroll / 2 * kUnitElems;
-    __shared__ float sh_f[kWaves];
-    __shared__ double sh_d[kWaves];
-    __shared__ int sh_i[kWaves], sh_n[kWaves];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    __syncthreads();   // the shared slots may still be read by a previous piece
-
-    Acc32 a32{-INFINITY, 0.0f, 0.0f, false, false, 0.0};
-    Acc64 a64{-INFINITY, false, 0.0, 0.0};
-    AccArg ag{-INFINITY, INT32_MAX, false};
-
-    // one group = kUnroll units per thread, unit k of thread t at u + t + k * kBlock
-    auto group = [&](const RawUnit<DT> *r, int64_t u) {
-        // two halves of kHalf logits each keep fewer values live at once
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            float x[kHalf];
-#pragma unroll
-            for (int k = 0; k < kUnroll / 2; ++k) unpack<DT>(r[h * (kUnroll / 2) + k], x + k * kUnitElems);
-            if (rmode == ROW_GREEDY) accarg_group<kHalf>(ag, x, u + (int64_t)h * (kUnroll / 2) * kBlock);
-            else if (DT == 0) acc32_group<kHalf>(a32, x, tc);
-            else acc64_group<kHalf>(a64, x, tc);
-        }
-    };
-
-    constexpr int64_t kStride = (int64_t)kBlock * kUnroll;
-    constexpr uint32_t kUnitBytes = DT == 0 ? 16u : 32u;
-    int64_t u_tail = a;   // first group start not covered by the unpredicated loop
-    if constexpr (AL) {
-        // full groups: unpredicated buffer loads at 32-bit offsets from the piece
-        // start, the next group's loads in flight while this one is reduced
-        // (an fp32 vector whose length is not a multiple of 8 ends in a partial unit;
-        // that unit is left to the predicated loop)
-        const int64_t n = b - a - ((DT == 1 && b * kUnitElems > V) ? 1 : 0);
-        const int64_t nfull = n / kStride;
-        if (nfull > 0 && n * kUnitBytes < ((int64_t)1 << 31)) {
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<char *>(static_cast<const char *>(base) + a * kUnitBytes), 0,
-                (int)(n * kUnitBytes), kBufferWord3);
-            auto load_group = [&](RawUnit<DT> *r, uint32_t off) {
-#pragma unroll
-                for (int k = 0; k < kUnroll; ++k) r[k] = buffer_unit<DT>(rs, off + (uint32_t)k * kBlock * kUnitBytes);
-            };
-            // two alternating register buffers (no copies between them, so waiting for
-            // one group's loads leaves the next group's loads in flight)
-            const uint32_t off0 = (uint32_t)tid * kUnitBytes;
-            const uint32_t step = (uint32_t)kStride * kUnitBytes;
-            RawUnit<DT> ra[kUnroll], rb[kUnroll];
-            load_group(ra, off0);
-            int64_t it = 0;
-            for (; it + 2 < nfull; it += 2) {   // prefetches always in range here
-                load_group(rb, off0 + (uint32_t)(it + 1) * step);
-                group(ra, a + it * kStride + tid);
-                load_group(ra, off0 + (uint32_t)(it + 2) * step);
-                group(rb, a + (it + 1) * kStride + tid);
-            }
-            if (it + 1 < nfull) {
-                load_group(rb, off0 + (uint32_t)(it + 1) * step);
-                group(ra, a + it * kStride + tid);
-                group(rb, a + (it + 1) * kStride + tid);
-            } else {
-                group(ra, a + it * kStride + tid);
-            }
-            u_tail = a + nfull * kStride;
-        }
-    }
-    // remaining units, predicated (logits past b read as -inf)
-    for (int64_t u = u_tail + tid; u - tid < b; u += kStride) {
-        RawUnit<DT> r[kUnroll];
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t uk = u + (int64_t)k * kBlock;
-            r[k] = uk < b ? load_raw<DT, AL>(base, uk, V) : neg_inf_unit<DT>();
-        }
-        group(r, u);
-    }
-
-    Partial out;
-    if (rmode == ROW_GREEDY) {
-        float bst = wave_max(ag.best);
-        if (lane == 0) sh_f[wave] = bst;
-        __syncthreads();
-        bst = fmaxf(fmaxf(sh_f[0], sh_f[1]), fmaxf(sh_f[2], sh_f[3]));
-        int cand = wave_min_int(ag.best == bst ? ag.idx : INT32_MAX);
-        const int nan = wave_or_int(ag.nan_seen ? 1 : 0);
-        if (lane == 0) { sh_i[wave] = cand; sh_n[wave] = nan; }
-        __syncthreads();
-        out.m = bst;
-        out.idx = min(min(sh_i[0], sh_i[1]), min(sh_i[2], sh_i[3]));
-        out.s = (sh_n[0] | sh_n[1] | sh_n[2] | sh_n[3]) ? kQNaN : 0.0;
-        return out;
-    }
-    // this thread's sum relative to its own maximum, then the workgroup's
-    const float m = DT == 0 ? a32.m : a64.m;
-    const double s_m = DT == 0 ? acc32_final(a32, tc) : acc64_final(a64, tc);
-    float mw = wave_max(m);
-    if (lane == 0) sh_f[wave] = mw;
-    __syncthreads();
-    mw = fmaxf(fmaxf(sh_f[0], sh_f[1]), fmaxf(sh_f[2], sh_f[3]));
-    double c = (m == -INFINITY) ? s_m : s_m * exp2_f64(((double)m - (double)mw) * tc.c_eff);
-    c = wave_sum(c);
-    if (lane == 0) sh_d[wave] = c;
-    __syncthreads();
-    out.m = mw;
-    out.idx = 0;
-    out.s = (sh_d[0] + sh_d[1]) + (sh_d[2] + sh_d[3]);
-    return out;
-}
-
-__device__ __forceinline__ int32_t slot_row(const Params &P, int64_t v)
-{
-    if (P.gamma != nullptr) return P.vec_row[v];
-    const int64_t per = P.mode == 1 ? (int64_t)P.gamma_uniform + 1 : 2 * (int64_t)P.gamma_uniform + 1;
-    return (int32_t)(v / per);
-}
-
-template <int DT, bool AL>
-__global__ __launch_bounds__(kBlock) void stats_kernel(Params P)
-{
-    if (P.gamma != nullptr && P.hdr->status != 0) return;
-    const int64_t wg = blockIdx.x;
-    const int64_t nunits = P.geo.nunits;
-    const int64_t u0 = wg * P.geo.R;
-    int64_t u1 = u0 + P.geo.R;
-    if (u1 > P.geo.total_units) u1 = P.geo.total_units;
-    if (u0 >= u1) return;
-    const int64_t v0 = u0 / nunits, v1 = (u1 - 1) / nunits;
-    for (int64_t v = v0; v <= v1; ++v) {
-        const int64_t vb = v * nunits;
-        const int64_t a = (u0 > vb ? u0 : vb) - vb;
-        const int64_t b = (u1 < vb + nunits ? u1 : vb + nunits) - vb;
-        const int32_t row = slot_row(P, v);
-        const RowGeom G = row_geom(P, row);
-        const int64_t k = v - row_slot0(P, G);
-        const bool is_target = P.mode == 1 || k <= G.gamma;
-        const int64_t vrow = is_target ? G.t_off + k : G.d_off + (k - G.gamma - 1);
-        const float T = P.temperature[row];
-        const int32_t rm = row_mode(P.mode, T);
-        Partial rec{-INFINITY, INT32_MAX, 0.0};
-        if (rm != ROW_BAD_TEMP && (rm == ROW_SAMPLE || is_target)) {
-            const TempConst tc = temp_const(rm == ROW_SAMPLE ? T : 1.0f);
-            const void *base = vec_ptr(is_target ? P.target : P.draft, DT, vrow, P.V);
-            // the logit at this position's draft token, if it lies in this piece
-            // (sampling rows), saved for the accept test
-            const int64_t j = is_target ? k : k - G.gamma - 1;
-            float zx = 0.0f;
-            bool have_zx = false;
-            if (rm == ROW_SAMPLE && j < G.gamma) {
-                const int32_t x = P.tokens[G.d_off + j];
-                if (x >= 0 && (int64_t)x < P.V && x / kUnitElems >= a && x / kUnitElems < b) {
-                    zx = load_logit<DT>(base, x);
-                    have_zx = true;
-                }
-            }
-            rec = reduce_piece<DT, AL>(base, a, b, P.V, rm, tc);
-            if (have_zx && threadIdx.x == 0) P.zx[(is_target ? 0 : P.nD) + G.d_off + j] = zx;
-        }
-        if (threadIdx.x == 0) P.parts[wg + v] = rec;
-    }
-}
-
-// ===========================================================================
-// accept scan: one wave per row
-// ===========================================================================
-constexpr int kPre = 4;   // pieces of a vector fetched up front (more are fetched later)
-
-struct VecRecs {
-    Partial r[kPre];
-    int64_t v, w0, w1;    // streamed vector, first and last workgroup whose piece covers it
+// ---------------------------------------------------------------------------
+// fp32 sampling piece (fp64 arithmetic): maximum first, then the sum against it
+// ---------------------------------------------------------------------------
+struct LaneSum64 {
+    float m;
+    double s;
 };
 
-__device__ __forceinline__ void fetch_recs(const Params &P, int64_t v, VecRecs &R)
-{
-    R.v = v;
-    R.w0 = (v * P.geo.nunits) / P.geo.R;
-    R.w1 = ((v + 1) * P.geo.nunits - 1) / P.geo.R;
-#pragma unroll
-    for (int i = 0; i < kPre; ++i)
-        R.r[i] = (R.w0 + i <= R.w1) ? P.parts[R.w0 + i + v] : Partial{-INFINITY, INT32_MAX, 0.0};
-}
-
-__device__ __forceinline__ void merge_one(const Partial &q, bool greedy, const TempConst &tc, float &m,
-                                          double &S, int32_t &idx, bool &nan)
-{
-    if (greedy) {
-        if (q.m > m) {
-            m = q.m;
-            idx = q.idx;
-        } else if (q.m == m && q.idx < idx) {
-            idx = q.idx;
-        }
-        nan |= (q.s != q.s);
-        return;
-    }
-    if (q.m > m) {
-        if (m != -INFINITY) S *= exp2_f64(((double)m - (double)q.m) * tc.c_eff);
-        m = q.m;
-    }
-    S += q.m == -INFINITY ? q.s : q.s * exp2_f64(((double)q.m - (double)m) * tc.c_eff);
-}
-
-// merge the pieces of a vector: max and sum 2^((z - m) c), or first argmax
-__device__ __forceinline__ void merge_recs(const Params &P, const VecRecs &R, const TempConst &tc, bool greedy,
-                                           float &m, double &S, int32_t &idx, bool &nan)
-{
-    m = -INFINITY;
-    S = 0.0;
-    idx = INT32_MAX;
-    nan = false;
-#pragma unroll
-    for (int i = 0; i < kPre; ++i) merge_one(R.r[i], greedy, tc, m, S, idx, nan);
-    for (int64_t w = R.w0 + kPre; w <= R.w1; ++w) merge_one(P.parts[w + R.v], greedy, tc, m, S, idx, nan);
-}
-
-// The accept scan of one row by one wave (positions across lanes).  Returns what
-// the draw needs (identical on every lane); with `write`, also stores the row's
-// outputs.
+// ---------------------------------------------------------------------------
+// the logit at the position's draft token
+// ---------------------------------------------------------------------------
+// The logit at half offset o (on the lane that loaded it): the raw word is picked
+// with constant indices (the half stays in registers) and unpacked alone.
 template <int DT>
-__device__ RowDraw scan_row(const Params &P, int32_t row, bool write)
+__device__ __forceinline__ float half_value(const ItemRaw &r, int lane, int o)
 {
+    constexpr int E = kE<DT>;
+    uint32_t wsel = 0u;
+    bool hi = false;
+#pragma unroll
+    for (int k = 0; k < kItemLoads; ++k) {
+        const uint32_t w[4] = {r.d[k].x, r.d[k].y, r.d[k].z, r.d[k].w};
+#pragma unroll
+        for (int t = 0; t < E; ++t) {
+            if (k * 64 * E + lane * E + t == o) {
+                wsel = w[DT == 0 ? t / 2 : t];
+                hi = (t & 1) != 0;
+            }
+        }
+    }
+    if constexpr (DT == 0) return hi ? bf16_hi(wsel) : bf16_lo(wsel);
+    else return __uint_as_float(wsel);
+}
+
+// What one piece's reduction carries between its two halves.
+template <int DT>
+struct PieceAcc {
+    LaneSum ls;
+    LaneSum64 l64;
+    LaneArg la;
+};
+
+template <int DT, bool AL>
+__device__ __forceinline__ void piece_half(const Params &P, const VecCtx &vc, int32_t rm, const TempConst &tc,
+                                           int64_t j, int h, int n, ItemRaw &r, PieceAcc<DT> &acc, int lane)
+{
+    constexpr int E = kE<DT>;
+    if (n != (int)P.geo.ie) mask_tail<DT, AL>(r, lane, n);
+    if (rm == ROW_SAMPLE) {
+        if constexpr (DT == 0) {
+            sample_half(r, tc.c_hi, acc.ls, h == 0);
+        } else {
+            // fp32 logits: the half's maximum, then its sum against the running maximum
+            const float mh = lane_max<DT>(r);
+            const float mn = nmax(h == 0 ? -INFINITY : acc.l64.m, mh);
+            double s = h == 0 ? 0.0 : acc.l64.s;
+            if (h == 1 && acc.l64.m != -INFINITY && mn != acc.l64.m)
+                s *= exp2_f64(((double)acc.l64.m - (double)mn) * tc.c_eff);
+            if (mn > -INFINITY) {
+#pragma unroll
+                for (int k = 0; k < kItemLoads; ++k) {
+                    float x[E];
+                    lane_vals<DT>(r, k, x);
+#pragma unroll
+                    for (int t = 0; t < E; ++t) s += exp2_f64(((double)x[t] - (double)mn) * tc.c_eff);
+                }
+            }
+            acc.l64.m = mn;
+            acc.l64.s = s;
+        }
+        // the logit at the position's draft token, if this half holds it
+        if (vc.slot >= 0 && vc.x >= 0 && (int64_t)vc.x < P.V) {
+            const int64_t o = (int64_t)vc.x - (2 * j + h) * P.geo.ie;
+            if (o >= 0 && o < n) {
+                const float z = half_value<DT>(r, lane, (int)o);
+                if (lane == (int)((o % (64 * E)) / E)) P.zx[(vc.target ? 0 : P.nD) + vc.slot] = z;
+            }
+        }
+    } else if (rm == ROW_GREEDY && vc.target) {
+        if (h == 0) acc.la = LaneArg{-INFINITY, INT32_MAX, false};
+        argmax_half<DT>(r, lane, h * (int)P.geo.ie, acc.la);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void piece_finish(const Params &P, const VecCtx &vc, int32_t rm, const TempConst &tc,
+                                             int64_t v, int64_t j, PieceAcc<DT> &acc)
+{
+    Partial rec{-INFINITY, INT32_MAX, 0.0};
+    if (rm == ROW_SAMPLE) {
+        if constexpr (DT == 0) {
+            rec = sample_record(acc.ls, tc.c_hi);
+        } else {
+            // lanes to the piece maximum
+            const float M = wave_umax_f32(acc.l64.m);
+            rec.m = M;
+            const double t = acc.l64.m == -INFINITY ? 0.0 : acc.l64.s * exp2_f64(((double)acc.l64.m - (double)M) * tc.c_eff);
+            rec.s = wave_usum_f64(t);
+        }
+    } else if (rm == ROW_GREEDY && vc.target) {
+        rec = argmax_record(acc.la);
+        if (rec.idx != INT32_MAX) rec.idx += (int32_t)(j * 2 * P.geo.ie);
+    }
+    if ((threadIdx.x & 63) == 0) P.parts[v * P.geo.ipv + j] = rec;
+}
+
+// Workgroup b owns pieces [b N / G, (b + 1) N / G) of the N pieces.  Its waves take
+// them in order from a counter in LDS (each wave's first piece is fixed), so a wave
+// the CU's arbiter serves less takes fewer pieces and the workgroup's waves finish
+// together; with one workgroup per CU the CUs finish together too.
+template <int DT, bool AL>
+__device__ __forceinline__ void stats_body(const Params &P)
+{
+    __shared__ uint32_t s_next;
+    if (threadIdx.x == 0) s_next = 0u;
+    __syncthreads();
+    if (P.gamma != nullptr && P.hdr->status != 0) return;
     const int lane = threadIdx.x & 63;
+    const int64_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nwb = blockDim.x >> 6;
+    const int64_t N = P.geo.nitems, G = gridDim.x;
+    const int64_t p0 = (int64_t)blockIdx.x * N / G, p1 = ((int64_t)blockIdx.x + 1) * N / G;
+    int64_t p = p0 + wave;
+    if (p >= p1) return;
+    auto grab = [&]() -> int64_t {
+        uint32_t t = 0u;
+        if (lane == 0) t = atomicAdd(&s_next, 1u);
+        return p0 + nwb + (int64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)t);
+    };
+    const int64_t ipv = P.geo.ipv;
+    int64_t v = qdiv(p, ipv, P.geo.inv_ipv), j = p - v * ipv;
+    int64_t pn = grab();   // the piece after this one
+    // the two halves of a piece in two register buffers: the next piece's first half
+    // is loaded while this piece's second half is reduced, and so on (every load
+    // unconditional, no copies between the buffers)
+    ItemRaw ra, rb;
+    half_begin<DT, AL>(P, v, j, 0, true, ra, lane);
+    half_begin<DT, AL>(P, v, j, 1, true, rb, lane);
+    VecCtx vc = vec_ctx(P, v);
+    float cached_T = __builtin_nanf("");
+    TempConst tc{};
+    for (;;) {
+        const int64_t cv = v, cj = j;
+        const bool live = pn < p1;
+        int64_t pnn = p1;
+        if (live) {
+            v = qdiv(pn, ipv, P.geo.inv_ipv);
+            j = pn - v * ipv;
+            pnn = grab();
+        }
+        const int32_t rm = row_mode(P.mode, vc.T);
+        if (rm == ROW_SAMPLE && vc.T != cached_T) {
+            tc = temp_const<DT>(vc.T);
+            cached_T = vc.T;
+        }
+        PieceAcc<DT> acc;
+        piece_half<DT, AL>(P, vc, rm, tc, cj, 0, half_len(P, cj, 0), ra, acc, lane);
+        half_begin<DT, AL>(P, v, j, 0, live, ra, lane);
+        const int n1 = half_len(P, cj, 1);
+        if (n1 > 0) piece_half<DT, AL>(P, vc, rm, tc, cj, 1, n1, rb, acc, lane);
+        half_begin<DT, AL>(P, v, j, 1, live, rb, lane);
+        const VecCtx vn = vec_ctx(P, live ? v : 0);
+        piece_finish<DT>(P, vc, rm, tc, cv, cj, acc);
+        if (!live) break;
+        vc = vn;
+        pn = pnn;
+    }
+}
+
+// log2 of the factor that takes a record's sum to sum 2^((z - m) c) over its logits
+// (0 for records of -inf or NaN logits, and for references stored as NaN: exact m c).
+template <int DT>
+__device__ __forceinline__ double rec_shift(const Partial &q, const TempConst &tc)
+{
+    if (!(q.m > -INFINITY && q.m < INFINITY)) return 0.0;
+    if constexpr (DT == 0) {
+        const float ref = __int_as_float(q.idx);
+        if (ref != ref) return 0.0;
+        return (double)(ref * tc.c_hi) - (double)q.m * tc.c_eff;
+    } else {
+        return 0.0;
+    }
+}
+
+// 16-byte aligned rows (the usual case): one workgroup of 12 waves per CU, 3 per SIMD
+template <int DT>
+__global__ __launch_bounds__(kStatsBlock) void stats_kernel(Params P)
+{
+    stats_body<DT, true>(P);
+}
+
+// rows read logit by logit
+template <int DT>
+__global__ __launch_bounds__(kBlock) void stats_kernel_unaligned(Params P)
+{
+    stats_body<DT, false>(P);
+}
+
+// ===========================================================================
+// accept scan: the whole workgroup merges records, one wave tests positions
+// ===========================================================================
+constexpr int kScanBatch = 4;   // vectors per wave with their record loads in flight together
+
+struct ScanLds {
+    float m[2][64];        // per position of the chunk: target, draft maximum
+    double S[2][64];       // sums 2^((z - m) c)
+    int32_t idx[64];       // target first argmax (greedy rows)
+    RowDraw D;
+};
+
+// Records of global vector v: items [v ipv, (v + 1) ipv).
+__device__ __forceinline__ void vec_records(const Params &P, int64_t v, int64_t &i0, int64_t &i1)
+{
+    i0 = v * P.geo.ipv;
+    i1 = i0 + P.geo.ipv - 1;
+}
+
+template <int DT>
+__device__ __forceinline__ void wave_merge(const Params &P, const Partial &q0, int64_t i0, int64_t i1, bool greedy,
+                                           const TempConst &tc, int lane, float &M, double &S, int32_t &idx)
+{
+    float m = q0.m;
+    double s = greedy ? 0.0 : q0.s;
+    double sh = greedy ? 0.0 : rec_shift<DT>(q0, tc);   // s 2^sh: sum 2^((z - m) c) of this lane's logits
+    int32_t id = (m != m) ? INT32_MAX : q0.idx;
+    for (int64_t i = i0 + 64 + lane; i <= i1; i += 64) {   // vectors of more than 64 items
+        const Partial q = P.parts[i];
+        if (greedy) {
+            if (q.m != q.m) {
+                m = q.m;
+            } else if (q.m > m) {
+                m = q.m;
+                id = q.idx;
+            } else if (q.m == m && q.idx < id) {
+                id = q.idx;
+            }
+            continue;
+        }
+        s *= exp2_f64(sh);
+        sh = 0.0;
+        const double qs = q.s * exp2_f64(rec_shift<DT>(q, tc));
+        if (q.m > m) {
+            if (m != -INFINITY) s *= exp2_f64(((double)m - (double)q.m) * tc.c_eff);
+            m = q.m;
+        }
+        s += q.m == -INFINITY ? qs : qs * exp2_f64(((double)q.m - (double)m) * tc.c_eff);
+        if (q.m != q.m) m = q.m;
+    }
+    M = wave_umax_f32(m);
+    if (greedy) {
+        S = 0.0;
+        idx = wave_umin_i32(m == M ? id : INT32_MAX);
+    } else {
+        // NaN anywhere gives M = NaN and S = NaN
+        const double t = m == -INFINITY ? s : s * exp2_f64(sh + ((double)m - (double)M) * tc.c_eff);
+        S = wave_usum_f64(t);
+        idx = INT32_MAX;
+    }
+}
+
+// Per-vector statistics of positions [base, base + nt) (target) and [base, base + nd)
+// (draft) of a row into LDS, every wave taking every fourth vector.
+template <int DT>
+__device__ __forceinline__ void scan_merge(const Params &P, const RowGeom &G, int64_t base, int nt, int nd,
+                                           bool greedy, const TempConst &tc, ScanLds &sh)
+{
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nq = nt + nd;
+    for (int q0 = wave; q0 < nq; q0 += kWaves * kScanBatch) {
+        Partial rec[kScanBatch];
+        int64_t vv[kScanBatch], i0[kScanBatch], i1[kScanBatch];
+#pragma unroll
+        for (int b = 0; b < kScanBatch; ++b) {
+            const int q = q0 + b * kWaves;
+            rec[b] = Partial{-INFINITY, INT32_MAX, 0.0};
+            vv[b] = -1;
+            if (q < nq) {
+                vv[b] = q < nt ? G.t_off + base + q : P.nT + G.d_off + base + (q - nt);
+                vec_records(P, vv[b], i0[b], i1[b]);
+                if (i0[b] + lane <= i1[b]) rec[b] = P.parts[i0[b] + lane];
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < kScanBatch; ++b) {
+            const int q = q0 + b * kWaves;
+            if (q >= nq) break;
+            float M;
+            double S;
+            int32_t idx;
+            wave_merge<DT>(P, rec[b], i0[b], i1[b], greedy && q < nt, tc, lane, M, S, idx);
+            if (lane == 0) {
+                const int side = q < nt ? 0 : 1, j = q < nt ? q : q - nt;
+                sh.m[side][j] = M;
+                sh.S[side][j] = S;
+                if (side == 0) sh.idx[j] = idx;
+            }
+        }
+    }
+}
+
+// The accept scan of one row by the whole workgroup.  Returns what the draw needs
+// (on every thread); with `write`, wave 0 also stores the row's outputs.
+template <int DT>
+__device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &sh)
+{
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const RowGeom G = row_geom(P, row);
     const int32_t g = G.gamma;
-    const int64_t slot0 = row_slot0(P, G);
     const float T = P.temperature[row];
     const int32_t rm = row_mode(P.mode, T);
     const bool greedy = rm == ROW_GREEDY;
+    const TempConst tc = temp_const<DT>(rm == ROW_SAMPLE ? T : 1.0f);
     int status = (rm == ROW_BAD_TEMP) ? ST_BAD_TEMP : 0;
     int32_t K = g;
     bool found = false;
-    float kmt = -INFINITY, kmd = -INFINITY;   // statistics at K (on every lane once known)
+    float kmt = -INFINITY, kmd = -INFINITY;   // statistics at K (wave 0, every lane once known)
     double kSt = 0.0, kSd = 0.0;
     int32_t kidx = -1;
     int32_t x_keep = 0;                       // this lane's draft token (rows with gamma < 64)
 
     if (rm != ROW_BAD_TEMP) {
-        for (int base = 0; base <= g; base += 64) {
-            const int j = base + lane;
+        for (int64_t base = 0; base <= g; base += 64) {
+            const int nt = (int)(g + 1 - base < 64 ? g + 1 - base : 64);
+            const int nd = greedy ? 0 : (int)(g - base < 64 ? g - base : 64);
+            const int64_t j = base + lane;
             const bool has_t = j <= g, has_d = j < g;
-            // every load of this chunk first
+            // this chunk's per-position inputs (wave 0), in flight during the merge
             int32_t x = 0;
             float u = 0.0f, zt = 0.0f, zd = 0.0f;
-            VecRecs rt, rd;
-            if (has_t) fetch_recs(P, slot0 + j, rt);
-            if (has_d) {
+            if (wave == 0 && has_d) {
                 x = P.tokens[G.d_off + j];
                 u = P.uniforms[G.t_off + j];
-                if (!greedy) {   // saved by the streaming pass
+                if (!greedy) {
                     zt = P.zx[G.d_off + j];
                     zd = P.zx[P.nD + G.d_off + j];
-                    fetch_recs(P, slot0 + g + 1 + j, rd);
                 }
             }
-            x_keep = x;
-            const TempConst tc = temp_const(rm == ROW_SAMPLE ? T : 1.0f);
-            const bool x_ok = x >= 0 && (int64_t)x < P.V;
-            if (has_d && !x_ok) status |= ST_BAD_TOKEN;
-            float mt = -INFINITY, md = -INFINITY;
-            double St = 0.0, Sd = 0.0;
-            int32_t it = INT32_MAX, idd;
-            bool nt = false, nd = false;
-            bool reject = false;
-            if (has_t) merge_recs(P, rt, tc, greedy, mt, St, it, nt);
-            if (greedy) {
-                if (has_t && (nt || !(mt > -INFINITY && mt < INFINITY))) status |= ST_NONFINITE;
-                if (has_d) reject = x != it;
-            } else {
-                if (has_t && !(St > 0.0 && St < INFINITY)) status |= ST_NONFINITE;
-                if (has_d) {
-                    merge_recs(P, rd, tc, false, md, Sd, idd, nd);
-                    if (!(Sd > 0.0 && Sd < INFINITY)) status |= ST_NONFINITE;
-                    double px = kQNaN, qx = kQNaN;
-                    if (x_ok && St > 0.0 && St < INFINITY && Sd > 0.0 && Sd < INFINITY) {
-                        const double Td = (double)T;
-                        px = exp(((double)zt - (double)mt) / Td) / St;
-                        qx = exp(((double)zd - (double)md) / Td) / Sd;
-                        double ratio;
-                        if (qx > 0.0) {
-                            ratio = px / qx;
-                            if (ratio > 1.0) ratio = 1.0;
-                        } else {
-                            ratio = px > 0.0 ? 1.0 : 0.0;
-                            status |= ST_Q_ZERO;
+            scan_merge<DT>(P, G, base, nt, nd, greedy, tc, sh);
+            __syncthreads();
+            if (wave == 0) {
+                x_keep = x;
+                const bool x_ok = x >= 0 && (int64_t)x < P.V;
+                if (has_d && !x_ok) status |= ST_BAD_TOKEN;
+                const float mt = has_t ? sh.m[0][lane] : -INFINITY;
+                const double St = has_t ? sh.S[0][lane] : 0.0;
+                const int32_t it = has_t ? sh.idx[lane] : INT32_MAX;
+                float md = -INFINITY;
+                double Sd = 0.0;
+                bool reject = false;
+                if (greedy) {
+                    if (has_t && !(mt > -INFINITY && mt < INFINITY)) status |= ST_NONFINITE;
+                    if (has_d) reject = x != it;
+                } else {
+                    if (has_t && !(St > 0.0 && St < INFINITY)) status |= ST_NONFINITE;
+                    if (has_d) {
+                        md = sh.m[1][lane];
+                        Sd = sh.S[1][lane];
+                        if (!(Sd > 0.0 && Sd < INFINITY)) status |= ST_NONFINITE;
+                        double px = kQNaN, qx = kQNaN;
+                        if (x_ok && St > 0.0 && St < INFINITY && Sd > 0.0 && Sd < INFINITY) {
+                            px = exp2_f64(((double)zt - (double)mt) * tc.c_eff) / St;
+                            qx = exp2_f64(((double)zd - (double)md) * tc.c_eff) / Sd;
+                            double ratio;
+                            if (qx > 0.0) {
+                                ratio = px / qx;
+                                if (ratio > 1.0) ratio = 1.0;
+                            } else {
+                                ratio = px > 0.0 ? 1.0 : 0.0;
+                                status |= ST_Q_ZERO;
+                            }
+                            reject = !((double)u < ratio);
                         }
-                        reject = !((double)u < ratio);
-                    }
-                    if (write) {
-                        if (P.p_x) P.p_x[G.d_off + j] = px;
-                        if (P.q_x) P.q_x[G.d_off + j] = qx;
+                        if (write) {
+                            if (P.p_x) P.p_x[G.d_off + j] = px;
+                            if (P.q_x) P.q_x[G.d_off + j] = qx;
+                        }
                     }
                 }
+                const unsigned long long rb = __ballot(reject);
+                int src = -1;
+                if (!found && rb != 0ull) {
+                    src = __ffsll((long long)rb) - 1;
+                    K = (int32_t)(base + src);
+                    found = true;
+                } else if (!found && g - base < 64) {
+                    src = (int)(g - base);   // no rejection: the bonus position is in this chunk
+                }
+                if (src >= 0) {
+                    kmt = __shfl(mt, src);
+                    kSt = __shfl(St, src);
+                    kmd = __shfl(md, src);
+                    kSd = __shfl(Sd, src);
+                    kidx = __shfl(it, src);
+                }
             }
-            const unsigned long long rb = __ballot(reject);
-            int src = -1;
-            if (!found && rb != 0ull) {
-                src = __ffsll((long long)rb) - 1;
-                K = base + src;
-                found = true;
-            } else if (!found && g - base < 64) {
-                src = g - base;   // no rejection: the bonus position is in this chunk
-            }
-            if (src >= 0) {
-                kmt = __shfl(mt, src);
-                kSt = __shfl(St, src);
-                kmd = __shfl(md, src);
-                kSd = __shfl(Sd, src);
-                kidx = __shfl(it, src);
-            }
+            // every chunk is scanned (statuses and diagnostics cover all positions)
+            __syncthreads();   // sh is rewritten by the next chunk
         }
     }
-    status = wave_or_int(status);
-    const bool invalid = (status & ST_INVALID) != 0;
 
-    RowDraw D{};
-    D.kind = DRAW_NONE;
-    if (!invalid && !greedy) {
-        D.kind = K < g ? DRAW_RESIDUAL : DRAW_BONUS;
-        D.K = K;
-        D.t_row = (int32_t)(G.t_off + K);
-        D.d_row = (int32_t)(G.d_off + K);
-        D.u = P.uniforms[G.t_off + g];
-        D.t_slot = (int32_t)(G.t_off + K);
-        D.m_t = kmt;
-        D.S_t = kSt;
-        D.m_d = kmd;
-        D.S_d = kSd;
-        D.T = T;
-    }
-    if (write) {
-        for (int j = lane; j <= g; j += 64) {
-            int32_t e = -1;
-            if (!invalid) {
-                if (j < K) e = g < 64 ? x_keep : P.tokens[G.d_off + j];
-                else if (j == K && greedy) e = kidx;
+    if (wave == 0) {
+        status = wave_or_int(status);
+        const bool invalid = (status & ST_INVALID) != 0;
+        RowDraw D{};
+        D.kind = DRAW_NONE;
+        if (!invalid && !greedy) {
+            D.kind = K < g ? DRAW_RESIDUAL : DRAW_BONUS;
+            D.K = K;
+            D.t_row = (int32_t)(G.t_off + K);
+            D.d_row = (int32_t)(G.d_off + K);
+            D.u = P.uniforms[G.t_off + g];
+            D.t_slot = (int32_t)(G.t_off + K);
+            D.m_t = kmt;
+            D.S_t = kSt;
+            D.m_d = kmd;
+            D.S_d = kSd;
+            D.T = T;
+        }
+        if (write) {
+            for (int64_t j = lane; j <= g; j += 64) {
+                int32_t e = -1;
+                if (!invalid) {
+                    if (j < K) e = g < 64 ? x_keep : P.tokens[G.d_off + j];
+                    else if (j == K && greedy) e = kidx;
+                }
+                P.emitted[G.t_off + j] = e;
+                if (j < g && (invalid || greedy)) {
+                    if (P.p_x) P.p_x[G.d_off + j] = kQNaN;
+                    if (P.q_x) P.q_x[G.d_off + j] = kQNaN;
+                }
             }
-            P.emitted[G.t_off + j] = e;
-            if (j < g && (invalid || greedy)) {
-                if (P.p_x) P.p_x[G.d_off + j] = kQNaN;
-                if (P.q_x) P.q_x[G.d_off + j] = kQNaN;
+            if (lane == 0) {
+                P.n_accepted[row] = invalid ? -1 : K;
+                if (P.row_status) P.row_status[row] = status;
+                if (D.kind == DRAW_NONE && P.resid) P.resid[row] = kQNaN;
+                P.draws[row] = D;
             }
         }
-        if (lane == 0) {
-            P.n_accepted[row] = invalid ? -1 : K;
-            if (P.row_status) P.row_status[row] = status;
-            if (D.kind == DRAW_NONE && P.resid) P.resid[row] = kQNaN;
-            P.draws[row] = D;
-        }
+        if (lane == 0) sh.D = D;
     }
-    return D;
+    __syncthreads();
+    return sh.D;
 }
 
 // Ragged batch whose gamma array is inconsistent: every row and slot is invalid.
@@ -616,43 +925,56 @@ __device__ void invalidate_call(const Params &P, int32_t row, bool row_writer)
 // ===========================================================================
 // draw: per-tile weight sums, then the inverse CDF
 // ===========================================================================
+// A unit past the end of a vector, read as -inf logits.
+template <int DT>
+__device__ __forceinline__ RawUnit<DT> neg_inf_unit()
+{
+    RawUnit<DT> r;
+    if constexpr (DT == 0) {
+        r.a = make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
+    } else {
+        r.a = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        r.b = r.a;
+    }
+    return r;
+}
+
 template <int DT>
 struct DrawConst;
 
-// bf16 logits: fp32 weights against an integer reference (as in the streaming pass)
+// bf16 logits: fp32 weights 2^(z c - B) F with B = m c rounded to fp32 and
+// F = 2^(B - m c) / S (the (z - m) route when |B| >= 2^20, as in the streaming pass)
 template <>
 struct DrawConst<0> {
-    TempConst tc;
-    float Rt, Rd, mt, md, Ft, Fd;
+    float c, Bt, Bd, mt, md, Ft, Fd;
     bool slow_t, slow_d, residual;
 
     __device__ __forceinline__ void init(const RowDraw &D)
     {
-        tc = temp_const(D.T);
+        const TempConst tc = temp_const<0>(D.T);
+        c = tc.c_hi;
         residual = D.kind == DRAW_RESIDUAL;
         mt = D.m_t;
-        Rt = ceilf(mt * tc.c_hi);
-        slow_t = !(fabsf(Rt) < kFastRef);
-        Ft = (float)((slow_t ? 1.0 : exp2_f64((double)Rt - (double)mt * tc.c_eff)) / D.S_t);
+        Bt = mt * c;
+        slow_t = !(fabsf(Bt) < kFastRef);
+        Ft = (float)((slow_t ? 1.0 : exp2_f64((double)Bt - (double)mt * (double)c)) / D.S_t);
         md = D.m_d;
-        Rd = ceilf(md * tc.c_hi);
-        slow_d = !(fabsf(Rd) < kFastRef);
-        Fd = residual ? (float)((slow_d ? 1.0 : exp2_f64((double)Rd - (double)md * tc.c_eff)) / D.S_d) : 0.0f;
+        Bd = md * c;
+        slow_d = !(fabsf(Bd) < kFastRef);
+        Fd = residual ? (float)((slow_d ? 1.0 : exp2_f64((double)Bd - (double)md * (double)c)) / D.S_d) : 0.0f;
     }
-    __device__ __forceinline__ float unnorm(float z, float R, float m, bool slow) const
+    __device__ __forceinline__ float unnorm(float z, float B, float m, bool slow) const
     {
-        if (!slow) return hw_exp2(fmaf(z, tc.c_lo, fmaf(z, tc.c_hi, -R)));
-        const float d = z - m;
-        return hw_exp2(fmaf(d, tc.c_hi, d * tc.c_lo));
+        return slow ? hw_exp2((z - m) * c) : hw_exp2(fmaf(z, c, -B));
     }
     // weights of one unit: w (residual or p) and p, as doubles
     __device__ __forceinline__ void weights(const float *zt, const float *zd, double *w, double *p) const
     {
 #pragma unroll
         for (int e = 0; e < kUnitElems; ++e) {
-            const float pe = unnorm(zt[e], Rt, mt, slow_t) * Ft;
+            const float pe = unnorm(zt[e], Bt, mt, slow_t) * Ft;
             float we = pe;
-            if (residual) we = fmaxf(0.0f, pe - unnorm(zd[e], Rd, md, slow_d) * Fd);
+            if (residual) we = fmaxf(0.0f, pe - unnorm(zd[e], Bd, md, slow_d) * Fd);
             w[e] = we;
             p[e] = pe;
         }
@@ -668,7 +990,7 @@ struct DrawConst<1> {
 
     __device__ __forceinline__ void init(const RowDraw &D)
     {
-        tc = temp_const(D.T);
+        tc = temp_const<1>(D.T);
         residual = D.kind == DRAW_RESIDUAL;
         Rt = ceil((double)D.m_t * tc.c_eff);
         Ft = exp2_f64(Rt - (double)D.m_t * tc.c_eff) / D.S_t;
@@ -691,8 +1013,8 @@ struct DrawConst<1> {
 template <int DT, bool AL>
 __global__ __launch_bounds__(kBlock) void verify_kernel(Params P)
 {
-    __shared__ RowDraw sD;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ ScanLds sh;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t per_row = P.mode == 1 ? 1 : P.geo.ndraw;
     const int32_t row = (int32_t)(blockIdx.x / per_row);
     const int32_t piece = (int32_t)(blockIdx.x - (int64_t)row * per_row);
@@ -700,14 +1022,9 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(Params P)
         invalidate_call(P, row, piece == 0 && tid == 0);
         return;
     }
-    // every workgroup of the row runs the scan (a few hundred bytes from L2); the
-    // first one stores the row's outputs
-    if (wave == 0) {
-        const RowDraw d = scan_row<DT>(P, row, piece == 0);
-        if (lane == 0) sD = d;
-    }
-    __syncthreads();
-    const RowDraw D = sD;
+    // every workgroup of the row runs the scan (its records come from L2); the first
+    // one stores the row's outputs
+    const RowDraw D = scan_row<DT>(P, row, piece == 0, sh);
     if (D.kind == DRAW_NONE) return;
     DrawConst<DT> c;
     c.init(D);
@@ -862,10 +1179,12 @@ static hipError_t launch(const void *fn, int64_t blocks, int threads, const Para
     return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(threads), args, 0, s);
 }
 
+static int stats_block(bool aligned) { return aligned ? kStatsBlock : kBlock; }
+
 static const void *stats_fn(int dtype, bool aligned)
 {
-    return dtype == 0 ? (aligned ? (const void *)stats_kernel<0, true> : (const void *)stats_kernel<0, false>)
-                      : (aligned ? (const void *)stats_kernel<1, true> : (const void *)stats_kernel<1, false>);
+    return dtype == 0 ? (aligned ? (const void *)stats_kernel<0> : (const void *)stats_kernel_unaligned<0>)
+                      : (aligned ? (const void *)stats_kernel<1> : (const void *)stats_kernel_unaligned<1>);
 }
 
 // Workgroups of the streaming kernel that fit on the current device at once
@@ -881,9 +1200,9 @@ int32_t stats_grid_cap(int dtype, bool aligned)
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stats_fn(dtype, aligned), kBlock, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stats_fn(dtype, aligned), stats_block(aligned), 0) !=
             hipSuccess || per_cu <= 0)
-        per_cu = 4;
+        per_cu = 1;
     int64_t cap = (int64_t)cus * per_cu;
     if (cap > kMaxStatsGrid) cap = kMaxStatsGrid;
     if (dev < kMaxDev) cache[dev][var] = (int32_t)cap;
@@ -897,7 +1216,7 @@ hipError_t launch_prepare(const Params &P, hipStream_t s)
 
 hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned)
 {
-    return launch(stats_fn(dtype, aligned), P.geo.G, kBlock, P, s);
+    return launch(stats_fn(dtype, aligned), P.geo.G, stats_block(aligned), P, s);
 }
 
 hipError_t launch_verify(const Params &P, hipStream_t s, int dtype, bool aligned)
