@@ -661,7 +661,7 @@ __global__ __launch_bounds__(kBlock) void stats_kernel_unaligned(Params P)
 // ===========================================================================
 // accept scan: the whole workgroup merges records, one wave tests positions
 // ===========================================================================
-constexpr int kScanBatch = 4;   // vectors per wave with their record loads in flight together
+constexpr int kScanBatch = 3;   // vectors per wave with their record loads in flight together
 
 struct ScanLds {
     float m[2][64];        // per position of the chunk: target, draft maximum
@@ -720,28 +720,44 @@ __device__ __forceinline__ void wave_merge(const Params &P, const Partial &q0, i
     }
 }
 
+// One wave's record loads for vectors q0, q0 + 4, ... of a position chunk (vectors
+// q < nt are target positions base + q, the others draft positions base + q - nt).
+struct ScanBatch {
+    Partial rec[kScanBatch];
+    int64_t i0[kScanBatch], i1[kScanBatch];
+};
+
+__device__ __forceinline__ void load_batch(const Params &P, const RowGeom &G, int64_t base, int nt, int nq, int q0,
+                                           int lane, ScanBatch &B)
+{
+#pragma unroll
+    for (int b = 0; b < kScanBatch; ++b) {
+        const int q = q0 + b * kWaves;
+        B.rec[b] = Partial{-INFINITY, INT32_MAX, 0.0};
+        B.i0[b] = 0;
+        B.i1[b] = -1;
+        if (q < nq) {
+            const int64_t v = q < nt ? G.t_off + base + q : P.nT + G.d_off + base + (q - nt);
+            vec_records(P, v, B.i0[b], B.i1[b]);
+            if (B.i0[b] + lane <= B.i1[b]) B.rec[b] = P.parts[B.i0[b] + lane];
+        }
+    }
+}
+
 // Per-vector statistics of positions [base, base + nt) (target) and [base, base + nd)
-// (draft) of a row into LDS, every wave taking every fourth vector.
+// (draft) of a row into LDS, every wave taking every fourth vector (first: this wave's
+// first batch, already loaded).
 template <int DT>
 __device__ __forceinline__ void scan_merge(const Params &P, const RowGeom &G, int64_t base, int nt, int nd,
-                                           bool greedy, const TempConst &tc, ScanLds &sh)
+                                           bool greedy, const TempConst &tc, ScanLds &sh, const ScanBatch &first,
+                                           bool have_first)
 {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nq = nt + nd;
     for (int q0 = wave; q0 < nq; q0 += kWaves * kScanBatch) {
-        Partial rec[kScanBatch];
-        int64_t vv[kScanBatch], i0[kScanBatch], i1[kScanBatch];
-#pragma unroll
-        for (int b = 0; b < kScanBatch; ++b) {
-            const int q = q0 + b * kWaves;
-            rec[b] = Partial{-INFINITY, INT32_MAX, 0.0};
-            vv[b] = -1;
-            if (q < nq) {
-                vv[b] = q < nt ? G.t_off + base + q : P.nT + G.d_off + base + (q - nt);
-                vec_records(P, vv[b], i0[b], i1[b]);
-                if (i0[b] + lane <= i1[b]) rec[b] = P.parts[i0[b] + lane];
-            }
-        }
+        ScanBatch B;
+        if (have_first && q0 == wave) B = first;
+        else load_batch(P, G, base, nt, nq, q0, lane, B);
 #pragma unroll
         for (int b = 0; b < kScanBatch; ++b) {
             const int q = q0 + b * kWaves;
@@ -749,7 +765,7 @@ __device__ __forceinline__ void scan_merge(const Params &P, const RowGeom &G, in
             float M;
             double S;
             int32_t idx;
-            wave_merge<DT>(P, rec[b], i0[b], i1[b], greedy && q < nt, tc, lane, M, S, idx);
+            wave_merge<DT>(P, B.rec[b], B.i0[b], B.i1[b], greedy && q < nt, tc, lane, M, S, idx);
             if (lane == 0) {
                 const int side = q < nt ? 0 : 1, j = q < nt ? q : q - nt;
                 sh.m[side][j] = M;
@@ -768,7 +784,27 @@ __device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &s
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const RowGeom G = row_geom(P, row);
     const int32_t g = G.gamma;
+    // every load that does not depend on the temperature first: the temperature, the
+    // draw's uniform, the first position chunk's tokens, uniforms and logits at the
+    // tokens (wave 0), and each wave's first batch of records
     const float T = P.temperature[row];
+    const float u_draw = P.uniforms[G.t_off + g];
+    int32_t x0 = 0;
+    float u0 = 0.0f, zt0 = 0.0f, zd0 = 0.0f;
+    if (wave == 0 && lane < g) {
+        x0 = P.tokens[G.d_off + lane];
+        u0 = P.uniforms[G.t_off + lane];
+        if (P.mode == 0) {
+            zt0 = P.zx[G.d_off + lane];
+            zd0 = P.zx[P.nD + G.d_off + lane];
+        }
+    }
+    ScanBatch first;
+    {
+        const int nt0 = g + 1 < 64 ? g + 1 : 64;
+        const int nd0 = P.mode == 1 ? 0 : (g < 64 ? g : 64);
+        load_batch(P, G, 0, nt0, nt0 + nd0, wave, lane, first);
+    }
     const int32_t rm = row_mode(P.mode, T);
     const bool greedy = rm == ROW_GREEDY;
     const TempConst tc = temp_const<DT>(rm == ROW_SAMPLE ? T : 1.0f);
@@ -787,9 +823,9 @@ __device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &s
             const int64_t j = base + lane;
             const bool has_t = j <= g, has_d = j < g;
             // this chunk's per-position inputs (wave 0), in flight during the merge
-            int32_t x = 0;
-            float u = 0.0f, zt = 0.0f, zd = 0.0f;
-            if (wave == 0 && has_d) {
+            int32_t x = x0;
+            float u = u0, zt = zt0, zd = zd0;
+            if (base > 0 && wave == 0 && has_d) {
                 x = P.tokens[G.d_off + j];
                 u = P.uniforms[G.t_off + j];
                 if (!greedy) {
@@ -797,7 +833,7 @@ __device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &s
                     zd = P.zx[P.nD + G.d_off + j];
                 }
             }
-            scan_merge<DT>(P, G, base, nt, nd, greedy, tc, sh);
+            scan_merge<DT>(P, G, base, nt, nd, greedy, tc, sh, first, base == 0);
             __syncthreads();
             if (wave == 0) {
                 x_keep = x;
@@ -870,7 +906,7 @@ __device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &s
             D.K = K;
             D.t_row = (int32_t)(G.t_off + K);
             D.d_row = (int32_t)(G.d_off + K);
-            D.u = P.uniforms[G.t_off + g];
+            D.u = u_draw;
             D.t_slot = (int32_t)(G.t_off + K);
             D.m_t = kmt;
             D.S_t = kSt;
@@ -967,8 +1003,9 @@ struct DrawConst<0> {
     {
         return slow ? hw_exp2((z - m) * c) : hw_exp2(fmaf(z, c, -B));
     }
-    // weights of one unit: w (residual or p) and p, as doubles
-    __device__ __forceinline__ void weights(const float *zt, const float *zd, double *w, double *p) const
+    using W = float;
+    // weights of one unit: w (residual or p) and p
+    __device__ __forceinline__ void weights(const float *zt, const float *zd, float *w, float *p) const
     {
 #pragma unroll
         for (int e = 0; e < kUnitElems; ++e) {
@@ -997,6 +1034,7 @@ struct DrawConst<1> {
         Rd = residual ? ceil((double)D.m_d * tc.c_eff) : 0.0;
         Fd = residual ? exp2_f64(Rd - (double)D.m_d * tc.c_eff) / D.S_d : 0.0;
     }
+    using W = double;
     __device__ __forceinline__ void weights(const float *zt, const float *zd, double *w, double *p) const
     {
 #pragma unroll
@@ -1011,7 +1049,7 @@ struct DrawConst<1> {
 };
 
 template <int DT, bool AL>
-__global__ __launch_bounds__(kBlock) void verify_kernel(Params P)
+__device__ __forceinline__ void verify_body(const Params &P)
 {
     __shared__ ScanLds sh;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1048,7 +1086,7 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(Params P)
         float zt[kUnitElems], zd[kUnitElems];
         unpack<DT>(rt[i], zt);
         unpack<DT>(rd[i], zd);
-        double w[kUnitElems], p[kUnitElems];
+        typename DrawConst<DT>::W w[kUnitElems], p[kUnitElems];
         c.weights(zt, zd, w, p);
         lw[i] = 0.0;
         lp[i] = 0.0;
@@ -1068,6 +1106,19 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(Params P)
         for (int i = 0; i < kTilesPerWave; ++i)
             if (t0 + i < P.geo.ntiles) P.tiles[row * P.geo.ntiles + t0 + i] = Sum2{lw[i], lp[i]};
     }
+}
+
+// bf16 logits: four workgroups per CU (all of a typical call's workgroups at once)
+template <bool AL>
+__global__ __launch_bounds__(kBlock, 4) void verify_kernel(Params P)
+{
+    verify_body<0, AL>(P);
+}
+
+template <bool AL>
+__global__ __launch_bounds__(kBlock) void verify_kernel_f32(Params P)
+{
+    verify_body<1, AL>(P);
 }
 
 // one wave per row
@@ -1134,7 +1185,7 @@ __global__ __launch_bounds__(64) void draw_final_kernel(Params P)
         float zt[kUnitElems], zd[kUnitElems];
         unpack<DT>(rt, zt);
         unpack<DT>(rd, zd);
-        double w[kUnitElems], p[kUnitElems];
+        typename DrawConst<DT>::W w[kUnitElems], p[kUnitElems];
         c.weights(zt, zd, w, p);
         double ls = 0.0;
 #pragma unroll
@@ -1222,8 +1273,8 @@ hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned)
 hipError_t launch_verify(const Params &P, hipStream_t s, int dtype, bool aligned)
 {
     const void *fn = dtype == 0
-        ? (aligned ? (const void *)verify_kernel<0, true> : (const void *)verify_kernel<0, false>)
-        : (aligned ? (const void *)verify_kernel<1, true> : (const void *)verify_kernel<1, false>);
+        ? (aligned ? (const void *)verify_kernel<true> : (const void *)verify_kernel<false>)
+        : (aligned ? (const void *)verify_kernel_f32<true> : (const void *)verify_kernel_f32<false>);
     const int64_t per_row = P.mode == 1 ? 1 : P.geo.ndraw;
     return launch(fn, (int64_t)P.B * per_row, kBlock, P, s);
 }
