@@ -119,7 +119,8 @@ extern "C" sv_status spec_verify(const void *target_logits, const void *draft_lo
     if (e == hipSuccess && g_prof_start) e = hipEventRecord(g_prof_start, s);
     if (e == hipSuccess) e = sv::launch_stats(P, s, dtype, aligned);
     if (e == hipSuccess && g_prof_stop) e = hipEventRecord(g_prof_stop, s);
-    if (e == hipSuccess) e = sv::launch_verify(P, s, dtype, aligned);
+    if (e == hipSuccess) e = sv::launch_scan(P, s, dtype);
+    if (e == hipSuccess && mode == SV_SAMPLE) e = sv::launch_verify(P, s, dtype, aligned);
     if (e == hipSuccess && mode == SV_SAMPLE) e = sv::launch_draw_final(P, s, dtype, aligned);
     return e == hipSuccess ? SV_OK : SV_EHIP;
 }

@@ -477,6 +477,7 @@ __device__ __forceinline__ double wave_usum_f64(double v)
 int32_t stats_grid_cap(int dtype, bool aligned);
 hipError_t launch_prepare(const Params &P, hipStream_t s);
 hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned);
+hipError_t launch_scan(const Params &P, hipStream_t s, int dtype);
 hipError_t launch_verify(const Params &P, hipStream_t s, int dtype, bool aligned);
 hipError_t launch_draw_final(const Params &P, hipStream_t s, int dtype, bool aligned);
 

@@ -1048,21 +1048,36 @@ struct DrawConst<1> {
     }
 };
 
+// The accept scan, one workgroup per row; it stores the row's outputs and what the
+// draw needs.
+template <int DT>
+__device__ __forceinline__ void scan_body(const Params &P)
+{
+    __shared__ ScanLds sh;
+    const int32_t row = (int32_t)blockIdx.x;
+    if (P.gamma != nullptr && P.hdr->status != 0) {
+        invalidate_call(P, row, threadIdx.x == 0);
+        return;
+    }
+    scan_row<DT>(P, row, true, sh);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void scan_kernel(Params P)
+{
+    scan_body<DT>(P);
+}
+
+// The draw's tile sums: workgroup `piece` of a row sums its slice of position K.
 template <int DT, bool AL>
 __device__ __forceinline__ void verify_body(const Params &P)
 {
-    __shared__ ScanLds sh;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t per_row = P.mode == 1 ? 1 : P.geo.ndraw;
+    const int64_t per_row = P.geo.ndraw;
     const int32_t row = (int32_t)(blockIdx.x / per_row);
     const int32_t piece = (int32_t)(blockIdx.x - (int64_t)row * per_row);
-    if (P.gamma != nullptr && P.hdr->status != 0) {
-        invalidate_call(P, row, piece == 0 && tid == 0);
-        return;
-    }
-    // every workgroup of the row runs the scan (its records come from L2); the first
-    // one stores the row's outputs
-    const RowDraw D = scan_row<DT>(P, row, piece == 0, sh);
+    if (P.gamma != nullptr && P.hdr->status != 0) return;
+    const RowDraw D = P.draws[row];
     if (D.kind == DRAW_NONE) return;
     DrawConst<DT> c;
     c.init(D);
@@ -1108,9 +1123,8 @@ __device__ __forceinline__ void verify_body(const Params &P)
     }
 }
 
-// bf16 logits: four workgroups per CU (all of a typical call's workgroups at once)
 template <bool AL>
-__global__ __launch_bounds__(kBlock, 4) void verify_kernel(Params P)
+__global__ __launch_bounds__(kBlock) void verify_kernel(Params P)
 {
     verify_body<0, AL>(P);
 }
@@ -1270,13 +1284,18 @@ hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned)
     return launch(stats_fn(dtype, aligned), P.geo.G, stats_block(aligned), P, s);
 }
 
+hipError_t launch_scan(const Params &P, hipStream_t s, int dtype)
+{
+    const void *fn = dtype == 0 ? (const void *)scan_kernel<0> : (const void *)scan_kernel<1>;
+    return launch(fn, (int64_t)P.B, kBlock, P, s);
+}
+
 hipError_t launch_verify(const Params &P, hipStream_t s, int dtype, bool aligned)
 {
     const void *fn = dtype == 0
         ? (aligned ? (const void *)verify_kernel<true> : (const void *)verify_kernel<false>)
         : (aligned ? (const void *)verify_kernel_f32<true> : (const void *)verify_kernel_f32<false>);
-    const int64_t per_row = P.mode == 1 ? 1 : P.geo.ndraw;
-    return launch(fn, (int64_t)P.B * per_row, kBlock, P, s);
+    return launch(fn, (int64_t)P.B * P.geo.ndraw, kBlock, P, s);
 }
 
 hipError_t launch_draw_final(const Params &P, hipStream_t s, int dtype, bool aligned)
