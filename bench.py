@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, published
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "stats_kernel_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "speculative_sampling_verify_02_amd", "csrc", f)
-                  for f in ("sv_kernels.hip", "sv_internal.h")]
+                  for f in ("sv_stats.hip", "sv_internal.h")]
 
 
 def kernel_source_hash() -> str:

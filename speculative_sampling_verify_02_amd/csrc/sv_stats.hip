@@ -1,0 +1,630 @@
+// The streaming pass of the speculative-sampling verification step for gfx950.
+//
+// Every logit of every target and draft vector is read exactly once.  The vectors
+// are cut into pieces of two 8 KB halves; one workgroup per CU owns a contiguous
+// range of pieces and its waves take them in order from a counter in LDS, each half
+// as eight 16-byte loads per lane with the next half's loads in flight while one is
+// reduced.  Per piece a wave writes one record: the maximum and the sum of
+// 2^((z - m) c), c = log2(e)/T, over the piece (sampling rows) or the first argmax
+// (greedy rows).  The temperature softmax these summarize is the softened output of
+// brunomaga.github.io "inference-distillation-speculative-decoding", section
+// "Knowledge distillation", with one T for both models (rayaq.ca "Speculative
+// decoding", section "Why the output is exactly the target's").  The wave also keeps
+// the logit at each position's draft token when it passes through its registers.
+//
+// bf16 logits are processed in fp32 (exp2 on the hardware unit, fp64 sums across
+// lanes); fp32 logits are processed in fp64.
+#include <float.h>
+#include <limits.h>
+
+#include "sv_internal.h"
+
+namespace sv {
+
+// ===========================================================================
+// streaming pass
+// ===========================================================================
+
+// What the pass needs about one streamed vector.
+struct VecCtx {
+    int32_t row;
+    int32_t slot;   // index of the position's draft token, -1 if none is tested there
+    int32_t x;      // that token
+    float T;
+    bool target;    // a target row (else a draft row)
+};
+
+// v: global vector index (target rows first, then draft rows)
+__device__ __forceinline__ VecCtx vec_ctx(const Params &P, int64_t v)
+{
+    VecCtx c;
+    c.target = v < P.nT;
+    if (P.gamma == nullptr) {
+        const bool target = c.target;
+        const int64_t vloc = target ? v : v - P.nT;
+        const int64_t g = P.gamma_uniform;
+        const int64_t per = target ? g + 1 : g;   // g > 0 whenever draft vectors exist
+        const int64_t row = qdiv(vloc, per, target ? P.geo.inv_t : P.geo.inv_d);
+        const int64_t j = vloc - row * per;
+        c.row = (int32_t)row;
+        c.slot = (P.mode == 0 && j < g) ? (int32_t)(row * g + j) : -1;
+        c.x = c.slot >= 0 ? P.tokens[c.slot] : -1;
+        c.T = P.temperature[row];
+    } else {
+        const VecInfo vi = P.vinfo[v];
+        c.row = vi.row;
+        c.slot = P.mode == 0 ? vi.slot : -1;
+        c.x = vi.x;
+        c.T = vi.T;
+    }
+    return c;
+}
+
+// One half-piece as this lane holds it: load k covers bytes [1024 k + 16 l, +16) of
+// the half.
+struct ItemRaw {
+    uint4 d[kItemLoads];
+};
+
+// logits per 16-byte load
+template <int DT> constexpr int kE = DT == 0 ? 8 : 4;
+
+// Logits of piece j of vector v in half h: [j 2 ie + h ie, +n), n in [0, ie].
+__device__ __forceinline__ int32_t half_len(const Params &P, int64_t j, int h)
+{
+    const int64_t e0 = (2 * j + h) * P.geo.ie;
+    const int64_t n = P.V - e0;
+    return (int32_t)(n < 0 ? 0 : (n < P.geo.ie ? n : P.geo.ie));
+}
+
+// Issue the loads of half h of piece j of vector v.  Offsets past the end of the
+// vector are clamped to its last 16 bytes (those logits are masked when the half is
+// reduced).  An empty half, or live = false (no piece left), reads an empty window at
+// the start of the vector (nothing to read, nothing used), which keeps every load of
+// the pipeline unconditional.
+template <int DT, bool AL>
+__device__ __forceinline__ void half_begin(const Params &P, int64_t v, int64_t j, int h, bool live, ItemRaw &r,
+                                           int lane)
+{
+    constexpr int64_t esz = DT == 0 ? 2 : 4;
+    if (!live) v = j = 0;
+    const int64_t n = live ? half_len(P, j, h) : 0;
+    const bool target = v < P.nT;
+    const int64_t row = target ? v : v - P.nT;
+    const int64_t e0 = n > 0 ? (2 * j + h) * P.geo.ie : 0;
+    const char *base = static_cast<const char *>(target ? P.target : P.draft) + (row * P.V + e0) * esz;
+    if constexpr (AL) {
+        const uint32_t nbytes = (uint32_t)(n * esz);   // a multiple of 16
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, (int)nbytes, kBufferWord3);
+        const uint32_t last = nbytes > 16u ? nbytes - 16u : 0u;
+#pragma unroll
+        for (int k = 0; k < kItemLoads; ++k) {
+            uint32_t off = (uint32_t)k * 1024u + (uint32_t)lane * 16u;
+            off = off < last ? off : last;
+            r.d[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+        }
+    } else {
+        const int64_t nl = n > 0 ? n : 1;
+#pragma unroll
+        for (int k = 0; k < kItemLoads; ++k) {
+            uint32_t w[4];
+            if constexpr (DT == 0) {
+                const uint16_t *p = reinterpret_cast<const uint16_t *>(base);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int64_t e = (int64_t)k * 512 + lane * 8 + 2 * t;
+                    const int64_t e_lo = e < nl ? e : nl - 1, e_hi = e + 1 < nl ? e + 1 : nl - 1;
+                    w[t] = (uint32_t)p[e_lo] | ((uint32_t)p[e_hi] << 16);
+                }
+            } else {
+                const uint32_t *p = reinterpret_cast<const uint32_t *>(base);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int64_t e = (int64_t)k * 256 + lane * 4 + t;
+                    w[t] = p[e < nl ? e : nl - 1];
+                }
+            }
+            r.d[k] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+}
+
+// Logits at half offsets n and beyond become -inf (the short end of a vector).  With
+// AL the rows hold whole 16-byte loads, so the test is per load.
+template <int DT, bool AL>
+__device__ __forceinline__ void mask_tail(ItemRaw &r, int lane, int n)
+{
+    constexpr int E = kE<DT>;
+    constexpr uint32_t kNinf = DT == 0 ? 0xff80ff80u : 0xff800000u;
+#pragma unroll
+    for (int k = 0; k < kItemLoads; ++k) {
+        if constexpr (AL) {
+            if (k * 64 * E + lane * E >= n) r.d[k] = make_uint4(kNinf, kNinf, kNinf, kNinf);
+        } else {
+            uint32_t w[4] = {r.d[k].x, r.d[k].y, r.d[k].z, r.d[k].w};
+#pragma unroll
+            for (int t = 0; t < E; ++t) {
+                if (k * 64 * E + lane * E + t < n) continue;
+                if constexpr (DT == 0) w[t / 2] = (t & 1) ? ((w[t / 2] & 0xffffu) | 0xff800000u) : ((w[t / 2] & 0xffff0000u) | 0xff80u);
+                else w[t] = 0xff800000u;
+            }
+            r.d[k] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+}
+
+// bf16 pairs to fp32 by byte permutes (two operand orders): other ways of unpacking,
+// so that a pass that re-reads the registers recomputes the values instead of keeping
+// an earlier pass's (or another branch's) values live
+template <int FORM>
+__device__ __forceinline__ float bf16_lo_f(uint32_t w)
+{
+    return __uint_as_float(FORM == 1 ? __builtin_amdgcn_perm(0u, w, 0x01000c0cu) : __builtin_amdgcn_perm(w, 0u, 0x05040c0cu));
+}
+template <int FORM>
+__device__ __forceinline__ float bf16_hi_f(uint32_t w)
+{
+    return __uint_as_float(FORM == 1 ? __builtin_amdgcn_perm(0u, w, 0x03020c0cu) : __builtin_amdgcn_perm(w, 0u, 0x07060c0cu));
+}
+
+// The logits of load k on this lane (FORM picks the bf16 unpacking: 0 shifts and
+// masks, 1 and 2 byte permutes).
+template <int DT, int FORM = 0>
+__device__ __forceinline__ void lane_vals(const ItemRaw &r, int k, float *x)
+{
+    const uint4 w = r.d[k];
+    if constexpr (DT == 0 && FORM != 0) {
+        x[0] = bf16_lo_f<FORM>(w.x); x[1] = bf16_hi_f<FORM>(w.x);
+        x[2] = bf16_lo_f<FORM>(w.y); x[3] = bf16_hi_f<FORM>(w.y);
+        x[4] = bf16_lo_f<FORM>(w.z); x[5] = bf16_hi_f<FORM>(w.z);
+        x[6] = bf16_lo_f<FORM>(w.w); x[7] = bf16_hi_f<FORM>(w.w);
+    } else if constexpr (DT == 0) {
+        x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
+        x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+        x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z);
+        x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+    } else {
+        x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y);
+        x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ float lane_max(const ItemRaw &r)
+{
+    constexpr int E = kE<DT>;
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kItemLoads; ++k) {
+        float x[E];
+        lane_vals<DT>(r, k, x);
+#pragma unroll
+        for (int t = 0; t < E; ++t) m = nmax(m, x[t]);
+    }
+    return m;
+}
+
+__device__ __forceinline__ float wave_usum_f32(float v)
+{
+    v += dpp_f32<0x121>(v);
+    v += dpp_f32<0x122>(v);
+    v += dpp_f32<0x124>(v);
+    v += dpp_f32<0x128>(v);
+    return v;
+}
+
+// fp64 total of a wave of fp32 lane values (fp32 within rows of 16 lanes)
+__device__ __forceinline__ double wave_total(float v)
+{
+    v = wave_usum_f32(v);
+    return ((double)readlane_f32(v, 0) + (double)readlane_f32(v, 16)) +
+           ((double)readlane_f32(v, 32) + (double)readlane_f32(v, 48));
+}
+
+// 2^d for a double d in fp32: the integer part exactly, the fraction on the hardware unit
+__device__ __forceinline__ float exp2_split(double d)
+{
+    const double n = rint(d);
+    return ldexpf(hw_exp2((float)(d - n)), (int)n);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 sampling piece.  Every lane sums 2^(z c - E) over its logits against its
+// own reference E: E = B = fl(R c) for a reference logit R (E = B + fma(R, c, -B),
+// the exact R c, when |B| >= 2^30, where the rounding of B would matter).  R starts
+// as the largest logit of the lane's first load; when a lane's sum over a half
+// overflows (a logit far above R) the half is summed again, from registers, against
+// the lane's maximum.  The epilogue brings the lanes to the piece maximum M.
+// ---------------------------------------------------------------------------
+struct LaneSum {
+    float m;      // maximum so far (NaN-propagating)
+    float s;      // sum 2^(z c - E) so far (0 while m = -inf)
+    float Bhi;    // fl(R c)
+    float Blo;    // R c - Bhi (used when huge)
+    double E;     // the reference of s
+    bool huge;    // wave-uniform: the two-part reference is in use
+};
+
+__device__ __forceinline__ void set_ref(LaneSum &a, float R, float c)
+{
+    a.Bhi = R * c;
+    a.Blo = fmaf(R, c, -a.Bhi);
+    a.huge = __any(!(fabsf(a.Bhi) < 0x1p30f));
+    a.E = a.huge ? (double)a.Bhi + (double)a.Blo : (double)a.Bhi;
+}
+
+// add one half (first: the piece's first half, which sets the references)
+__device__ __forceinline__ void sample_half(const ItemRaw &r, float c, LaneSum &a, bool first)
+{
+    if (first) {
+        float x[8];
+        lane_vals<0>(r, 0, x);
+        float R = x[0];
+#pragma unroll
+        for (int t = 1; t < 8; ++t) R = nmax(R, x[t]);
+        a.m = -INFINITY;
+        a.s = 0.0f;
+        set_ref(a, R, c);
+    }
+    const float m_prev = a.m, s_prev = a.s;
+    const double E_prev = a.E;
+    float acc[kItemLoads];
+#pragma unroll
+    for (int k = 0; k < kItemLoads; ++k) {
+        float x[8];
+        lane_vals<0, 1>(r, k, x);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) a.m = nmax(a.m, x[t]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) x[t] = hw_exp2(fmaf(x[t], c, -a.Bhi));
+#pragma unroll
+        for (int w = 1; w < 8; w <<= 1)
+#pragma unroll
+            for (int t = 0; t + w < 8; t += 2 * w) x[t] += x[t + w];
+        acc[k] = x[0];
+    }
+#pragma unroll
+    for (int w = 1; w < kItemLoads; w <<= 1)
+#pragma unroll
+        for (int k = 0; k + w < kItemLoads; k += 2 * w) acc[k] += acc[k + w];
+    // a lane whose logits are finite but whose sum is not, or a two-part reference: the
+    // references move to the lanes' maxima, the earlier sum is rescaled, and the half is
+    // summed again (from registers) with the two-part reference when needed
+    const bool over = !(acc[0] <= 3.402823466e38f) && fabsf(a.m) <= 3.402823466e38f;
+    if (__any(over) || a.huge) {
+        const float R = fabsf(a.m) <= 3.402823466e38f ? a.m : 0.0f;
+        set_ref(a, R, c);
+        a.s = m_prev == -INFINITY ? 0.0f : s_prev * (float)exp2_f64(E_prev - a.E);
+        const float Blo = a.huge ? a.Blo : 0.0f;
+        float acc2[kItemLoads];
+#pragma unroll
+        for (int k = 0; k < kItemLoads; ++k) {
+            float x[8];
+            lane_vals<0, 2>(r, k, x);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) x[t] = hw_exp2(fmaf(x[t], c, -a.Bhi) - Blo);
+#pragma unroll
+            for (int w = 1; w < 8; w <<= 1)
+#pragma unroll
+                for (int t = 0; t + w < 8; t += 2 * w) x[t] += x[t + w];
+            acc2[k] = x[0];
+        }
+#pragma unroll
+        for (int w = 1; w < kItemLoads; w <<= 1)
+#pragma unroll
+            for (int k = 0; k + w < kItemLoads; k += 2 * w) acc2[k] += acc2[k + w];
+        acc[0] = acc2[0];
+    }
+    a.s += acc[0];
+    if (a.m == -INFINITY) a.s = 0.0f;
+}
+
+// The piece's record from the lane sums: m = M, s = sum 2^(z c - E_M) with
+// E_M = fl(M c) (ref = M, in idx) or, when |fl(M c)| >= 2^30, the exact M c (ref = NaN).
+__device__ __forceinline__ Partial sample_record(const LaneSum &a, float c)
+{
+    const float M = wave_umax_f32(a.m);
+    Partial p{M, 0, 0.0};
+    if (M == -INFINITY) return p;
+    if (!(fabsf(M) <= 3.402823466e38f)) {   // a NaN or +inf logit
+        p.idx = __float_as_int(__builtin_nanf(""));
+        p.s = (double)__builtin_nanf("");
+        return p;
+    }
+    const float BM = M * c;
+    const bool exact = !(fabsf(BM) < 0x1p30f);
+    const double EM = exact ? (double)M * (double)c : (double)BM;
+    const float t = a.m == -INFINITY ? 0.0f : a.s * exp2_split(a.E - EM);
+    p.idx = __float_as_int(exact ? __builtin_nanf("") : M);
+    p.s = wave_total(t);
+    return p;
+}
+
+// ---------------------------------------------------------------------------
+// greedy piece: first index of the maximum (per lane, then across the wave)
+// ---------------------------------------------------------------------------
+struct LaneArg {
+    float best;
+    int32_t idx;   // piece offset
+    bool nan;
+};
+
+template <int DT>
+__device__ __forceinline__ void argmax_half(const ItemRaw &r, int lane, int base, LaneArg &a)
+{
+    constexpr int E = kE<DT>;
+    // per load maximum, then the first load holding the half's lane maximum (strictly
+    // greater wins, so the earliest load keeps ties)
+    float mh = -INFINITY;
+    int kb = 0;
+    bool nan = false;
+#pragma unroll
+    for (int k = 0; k < kItemLoads; ++k) {
+        float x[E];
+        lane_vals<DT>(r, k, x);
+        float lm = x[0];
+#pragma unroll
+        for (int t = 1; t < E; ++t) lm = nmax(lm, x[t]);
+        nan |= lm != lm;
+        if (lm > mh) {
+            mh = lm;
+            kb = k;
+        }
+    }
+    a.nan |= nan;
+    // the first logit of that load equal to it
+    uint4 w = r.d[0];
+#pragma unroll
+    for (int k = 1; k < kItemLoads; ++k)
+        if (k == kb) w = r.d[k];
+    ItemRaw one;
+    one.d[0] = w;
+    float x[E];
+    lane_vals<DT, 1>(one, 0, x);
+    int t0 = E - 1;
+#pragma unroll
+    for (int t = E - 2; t >= 0; --t)
+        if (x[t] == mh) t0 = t;
+    if (mh > a.best) {
+        a.best = mh;
+        a.idx = base + kb * 64 * E + lane * E + t0;
+    }
+}
+
+__device__ __forceinline__ Partial argmax_record(const LaneArg &a)
+{
+    const float M = wave_umax_f32(a.nan ? __builtin_nanf("") : a.best);
+    return Partial{M, wave_umin_i32(a.best == M ? a.idx : INT32_MAX), 0.0};
+}
+
+// ---------------------------------------------------------------------------
+// fp32 sampling piece (fp64 arithmetic): maximum first, then the sum against it
+// ---------------------------------------------------------------------------
+struct LaneSum64 {
+    float m;
+    double s;
+};
+
+// ---------------------------------------------------------------------------
+// the logit at the position's draft token
+// ---------------------------------------------------------------------------
+// The logit at half offset o (on the lane that loaded it): the raw word is picked
+// with constant indices (the half stays in registers) and unpacked alone.
+template <int DT>
+__device__ __forceinline__ float half_value(const ItemRaw &r, int lane, int o)
+{
+    constexpr int E = kE<DT>;
+    uint32_t wsel = 0u;
+    bool hi = false;
+#pragma unroll
+    for (int k = 0; k < kItemLoads; ++k) {
+        const uint32_t w[4] = {r.d[k].x, r.d[k].y, r.d[k].z, r.d[k].w};
+#pragma unroll
+        for (int t = 0; t < E; ++t) {
+            if (k * 64 * E + lane * E + t == o) {
+                wsel = w[DT == 0 ? t / 2 : t];
+                hi = (t & 1) != 0;
+            }
+        }
+    }
+    if constexpr (DT == 0) return hi ? bf16_hi(wsel) : bf16_lo(wsel);
+    else return __uint_as_float(wsel);
+}
+
+// What one piece's reduction carries between its two halves.
+template <int DT>
+struct PieceAcc {
+    LaneSum ls;
+    LaneSum64 l64;
+    LaneArg la;
+};
+
+template <int DT, bool AL>
+__device__ __forceinline__ void piece_half(const Params &P, const VecCtx &vc, int32_t rm, const TempConst &tc,
+                                           int64_t j, int h, int n, ItemRaw &r, PieceAcc<DT> &acc, int lane)
+{
+    constexpr int E = kE<DT>;
+    if (n != (int)P.geo.ie) mask_tail<DT, AL>(r, lane, n);
+    if (rm == ROW_SAMPLE) {
+        if constexpr (DT == 0) {
+            sample_half(r, tc.c_hi, acc.ls, h == 0);
+        } else {
+            // fp32 logits: the half's maximum, then its sum against the running maximum
+            const float mh = lane_max<DT>(r);
+            const float mn = nmax(h == 0 ? -INFINITY : acc.l64.m, mh);
+            double s = h == 0 ? 0.0 : acc.l64.s;
+            if (h == 1 && acc.l64.m != -INFINITY && mn != acc.l64.m)
+                s *= exp2_f64(((double)acc.l64.m - (double)mn) * tc.c_eff);
+            if (mn > -INFINITY) {
+#pragma unroll
+                for (int k = 0; k < kItemLoads; ++k) {
+                    float x[E];
+                    lane_vals<DT>(r, k, x);
+#pragma unroll
+                    for (int t = 0; t < E; ++t) s += exp2_f64(((double)x[t] - (double)mn) * tc.c_eff);
+                }
+            }
+            acc.l64.m = mn;
+            acc.l64.s = s;
+        }
+        // the logit at the position's draft token, if this half holds it
+        if (vc.slot >= 0 && vc.x >= 0 && (int64_t)vc.x < P.V) {
+            const int64_t o = (int64_t)vc.x - (2 * j + h) * P.geo.ie;
+            if (o >= 0 && o < n) {
+                const float z = half_value<DT>(r, lane, (int)o);
+                if (lane == (int)((o % (64 * E)) / E)) P.zx[(vc.target ? 0 : P.nD) + vc.slot] = z;
+            }
+        }
+    } else if (rm == ROW_GREEDY && vc.target) {
+        if (h == 0) acc.la = LaneArg{-INFINITY, INT32_MAX, false};
+        argmax_half<DT>(r, lane, h * (int)P.geo.ie, acc.la);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void piece_finish(const Params &P, const VecCtx &vc, int32_t rm, const TempConst &tc,
+                                             int64_t v, int64_t j, PieceAcc<DT> &acc)
+{
+    Partial rec{-INFINITY, INT32_MAX, 0.0};
+    if (rm == ROW_SAMPLE) {
+        if constexpr (DT == 0) {
+            rec = sample_record(acc.ls, tc.c_hi);
+        } else {
+            // lanes to the piece maximum
+            const float M = wave_umax_f32(acc.l64.m);
+            rec.m = M;
+            const double t = acc.l64.m == -INFINITY ? 0.0 : acc.l64.s * exp2_f64(((double)acc.l64.m - (double)M) * tc.c_eff);
+            rec.s = wave_usum_f64(t);
+        }
+    } else if (rm == ROW_GREEDY && vc.target) {
+        rec = argmax_record(acc.la);
+        if (rec.idx != INT32_MAX) rec.idx += (int32_t)(j * 2 * P.geo.ie);
+    }
+    if ((threadIdx.x & 63) == 0) P.parts[v * P.geo.ipv + j] = rec;
+}
+
+// Workgroup b owns pieces [b N / G, (b + 1) N / G) of the N pieces.  Its waves take
+// them in order from a counter in LDS (each wave's first piece is fixed), so a wave
+// the CU's arbiter serves less takes fewer pieces and the workgroup's waves finish
+// together; with one workgroup per CU the CUs finish together too.
+template <int DT, bool AL>
+__device__ __forceinline__ void stats_body(const Params &P)
+{
+    __shared__ uint32_t s_next;
+    if (threadIdx.x == 0) s_next = 0u;
+    __syncthreads();
+    if (P.gamma != nullptr && P.hdr->status != 0) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nwb = blockDim.x >> 6;
+    const int64_t N = P.geo.nitems, G = gridDim.x;
+    const int64_t p0 = (int64_t)blockIdx.x * N / G, p1 = ((int64_t)blockIdx.x + 1) * N / G;
+    int64_t p = p0 + wave;
+    if (p >= p1) return;
+    auto grab = [&]() -> int64_t {
+        uint32_t t = 0u;
+        if (lane == 0) t = atomicAdd(&s_next, 1u);
+        return p0 + nwb + (int64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)t);
+    };
+    const int64_t ipv = P.geo.ipv;
+    int64_t v = qdiv(p, ipv, P.geo.inv_ipv), j = p - v * ipv;
+    int64_t pn = grab();   // the piece after this one
+    // the two halves of a piece in two register buffers: the next piece's first half
+    // is loaded while this piece's second half is reduced, and so on (every load
+    // unconditional, no copies between the buffers)
+    ItemRaw ra, rb;
+    half_begin<DT, AL>(P, v, j, 0, true, ra, lane);
+    half_begin<DT, AL>(P, v, j, 1, true, rb, lane);
+    VecCtx vc = vec_ctx(P, v);
+    float cached_T = __builtin_nanf("");
+    TempConst tc{};
+    for (;;) {
+        const int64_t cv = v, cj = j;
+        const bool live = pn < p1;
+        int64_t pnn = p1;
+        if (live) {
+            v = qdiv(pn, ipv, P.geo.inv_ipv);
+            j = pn - v * ipv;
+            pnn = grab();
+        }
+        const int32_t rm = row_mode(P.mode, vc.T);
+        if (rm == ROW_SAMPLE && vc.T != cached_T) {
+            tc = temp_const<DT>(vc.T);
+            cached_T = vc.T;
+        }
+        PieceAcc<DT> acc;
+        piece_half<DT, AL>(P, vc, rm, tc, cj, 0, half_len(P, cj, 0), ra, acc, lane);
+        half_begin<DT, AL>(P, v, j, 0, live, ra, lane);
+        const int n1 = half_len(P, cj, 1);
+        if (n1 > 0) piece_half<DT, AL>(P, vc, rm, tc, cj, 1, n1, rb, acc, lane);
+        half_begin<DT, AL>(P, v, j, 1, live, rb, lane);
+        const VecCtx vn = vec_ctx(P, live ? v : 0);
+        piece_finish<DT>(P, vc, rm, tc, cv, cj, acc);
+        if (!live) break;
+        vc = vn;
+        pn = pnn;
+    }
+}
+
+// 16-byte aligned rows (the usual case): one workgroup of 12 waves per CU, 3 per SIMD
+template <int DT>
+__global__ __launch_bounds__(kStatsBlock) void stats_kernel(Params P)
+{
+    stats_body<DT, true>(P);
+}
+
+// rows read logit by logit
+template <int DT>
+__global__ __launch_bounds__(kBlock) void stats_kernel_unaligned(Params P)
+{
+    stats_body<DT, false>(P);
+}
+
+// ===========================================================================
+// launchers
+// ===========================================================================
+static hipError_t launch(const void *fn, int64_t blocks, int threads, const Params &P, hipStream_t s)
+{
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    void *args[] = {const_cast<Params *>(&P)};
+    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(threads), args, 0, s);
+}
+
+static int stats_block(bool aligned) { return aligned ? kStatsBlock : kBlock; }
+
+static const void *stats_fn(int dtype, bool aligned)
+{
+    return dtype == 0 ? (aligned ? (const void *)stats_kernel<0> : (const void *)stats_kernel_unaligned<0>)
+                      : (aligned ? (const void *)stats_kernel<1> : (const void *)stats_kernel_unaligned<1>);
+}
+
+// Workgroups of the streaming kernel that fit on the current device at once
+// (cached per device and kernel variant).
+int32_t stats_grid_cap(int dtype, bool aligned)
+{
+    constexpr int kMaxDev = 64;
+    static int32_t cache[kMaxDev][4] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 1024;
+    const int var = dtype * 2 + (aligned ? 1 : 0);
+    if (dev < kMaxDev && cache[dev][var] > 0) return cache[dev][var];
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stats_fn(dtype, aligned), stats_block(aligned), 0) !=
+            hipSuccess || per_cu <= 0)
+        per_cu = 1;
+    int64_t cap = (int64_t)cus * per_cu;
+    if (cap > kMaxStatsGrid) cap = kMaxStatsGrid;
+    if (dev < kMaxDev) cache[dev][var] = (int32_t)cap;
+    return (int32_t)cap;
+}
+
+hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned)
+{
+    return launch(stats_fn(dtype, aligned), P.geo.G, stats_block(aligned), P, s);
+}
+
+}  // namespace sv
