@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c3", choices=["c2", "c3", "c4", "c5"])
     ap.add_argument("--mode", default="sample", choices=["sample", "greedy"])
+    ap.add_argument("--op", default="verify", choices=["verify", "sample"],
+                    help="verify: the verification step (default); sample: the drafter's draw "
+                         "over the configuration's draft logit vectors")
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
@@ -126,6 +129,105 @@ def cpu_baseline(w, budget_s: float, mode: str):
                       f"positions each), {el:.1f} s wall, OpenMP over rows"}
 
 
+def timed_steps(step, steps: int, sv):
+    """Wall time of `steps` calls, then the same calls again with HIP events around
+    each call's streaming kernel; returns (sec per step, stats kernel ms per launch,
+    ms per step with the events)."""
+    import numpy as np
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(k)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ev = HipEvents()
+    starts = [ev.create() for _ in range(steps)]
+    stops = [ev.create() for _ in range(steps)]
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for k in range(steps):
+        sv.set_profile_events(starts[k], stops[k])
+        step(k)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    sv.set_profile_events(None, None)
+    stats_ms = [ev.elapsed_ms(starts[k], stops[k]) for k in range(steps)]
+    for e in starts + stops:
+        ev.destroy(e)
+    return (t1 - t0) / steps, float(np.mean(stats_ms)), (t3 - t2) / steps * 1e3
+
+
+def bench_sample(args):
+    """The drafter's draw x ~ softmax(z/T) over every draft logit vector of the
+    configuration (for the V = 128256 batch: 320 vectors), one call per step."""
+    import numpy as np
+    import torch
+
+    import speculative_sampling_verify_02_amd as sv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    w = make_workload(args.config, "sample")
+    si = workloads.sample_inputs(w, seed=11, side="draft")
+    esz = 2 if si.dtype == "bf16" else 4
+
+    def dev_logits():
+        if si.dtype == "bf16":
+            return torch.from_numpy(si.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(si.logits).to(dev)
+    copies = [dict(z=dev_logits(), u=torch.from_numpy(si.uniforms).to(dev),
+                   T=torch.from_numpy(si.temperature).to(dev)) for _ in range(max(1, args.copies))]
+    n, V = si.n, si.vocab
+    outs = [torch.empty(n, dtype=torch.int32, device=dev) for _ in copies]
+    ws = torch.empty(sv.sample_workspace_bytes(n, V, sv.SV_BF16 if si.dtype == "bf16" else sv.SV_F32),
+                     dtype=torch.uint8, device=dev)
+
+    def step(k):
+        d = copies[k % len(copies)]
+        return sv.spec_sample(d["z"], d["u"], d["T"], workspace=ws, out=outs[k % len(copies)])
+
+    step(0)
+    torch.cuda.synchronize()
+    for k in range(args.warmup):
+        step(k)
+    sec, stats_ms, ms_ev = timed_steps(step, args.steps, sv)
+    pass1 = n * V * esz
+    piece = 2 * 8192  # the draw re-reads one 16 KB piece per vector
+    total = pass1 + n * min(piece, V * esz) + n * 12
+    achieved = pass1 / (stats_ms * 1e-3) / 1e9
+    res = {
+        "metric": "sampled vectors/sec (drafter's draw x ~ softmax(z/T)) and achieved HBM GB/s",
+        "value": n / sec, "unit": "vectors/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": sec * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": si.dtype, "data": "synthetic",
+        "config": {"workload": si.name, "vectors": n, "vocab": V, "rotated_device_copies": len(copies)},
+        "hbm_gbps_algorithmic": total / sec / 1e9,
+        "hbm_frac_of_peak": total / sec / 1e9 / PEAK_HBM_GBPS,
+        "roofline": {"kernel": "stats_kernel", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+                     "avg_launch_ms": stats_ms, "algorithmic_bytes_per_launch": pass1,
+                     "timed_steps": args.steps, "ms_per_step_with_events": ms_ev},
+        "cpu_baseline": None,
+    }
+    if args.cpu_seconds > 0:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        t0 = time.perf_counter()
+        calls = 0
+        while True:
+            oracle.sample(si.logits, si.dtype, V, si.temperature, si.uniforms, threads=cores)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or calls >= 10000:
+                break
+        res["cpu_baseline"] = {"value": n * calls / el, "unit": "vectors/s", "cores": int(cores),
+                               "kind": "oracle",
+                               "sample": f"{calls} full calls ({n} vectors each), {el:.1f} s wall, "
+                                         f"OpenMP over vectors"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -133,6 +235,9 @@ def main():
                                    "part of it (rows shard independently, see the design notes)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.op == "sample":
+        bench_sample(args)
+        return
     import numpy as np
     import torch
 
@@ -165,7 +270,10 @@ def main():
     pass1_bytes = (nT + (nD if args.mode == "sample" else 0)) * V * esz
     pass2_bytes = 0
     if args.mode == "sample":
-        pass2_bytes = int(sum(V * esz * (2 if K[i] < gam[i] else 1) for i in range(B) if K[i] >= 0))
+        # a rejection re-reads position K of both models; a bonus draw re-reads one
+        # 16 KB piece of p_gamma (its piece sums come from the streaming pass)
+        pass2_bytes = int(sum(2 * V * esz if K[i] < gam[i] else min(2 * 8192, V * esz)
+                              for i in range(B) if K[i] >= 0))
     small_bytes = nT * 4 * 2 + nD * 4 + B * 8
 
     if args.copy_calibration:
@@ -180,34 +288,11 @@ def main():
         step(k)
     torch.cuda.synchronize()
 
-    # timed region 1: the whole job, nothing else on the stream
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(k)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-
-    # timed region 2: the same steps with HIP events recorded around the streaming
-    # kernel on the call's stream (event records add their own gaps to the step)
-    ev = HipEvents()
-    starts = [ev.create() for _ in range(args.steps)]
-    stops = [ev.create() for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for k in range(args.steps):
-        sv.set_profile_events(starts[k], stops[k])
-        step(k)
-    torch.cuda.synchronize()
-    t3 = time.perf_counter()
-    sv.set_profile_events(None, None)
-    stats_ms = [ev.elapsed_ms(starts[k], stops[k]) for k in range(args.steps)]
-    for e in starts + stops:
-        ev.destroy(e)
-
-    sec_per_step = (t1 - t0) / args.steps
+    # the whole job with nothing else on the stream, then the same steps with HIP
+    # events recorded around the streaming kernel on the call's stream (the event
+    # records add their own gaps to the step)
+    sec_per_step, stats_avg_ms, ms_events = timed_steps(step, args.steps, sv)
     positions = nT
-    stats_avg_ms = float(np.mean(stats_ms))
     stats_bytes = pass1_bytes  # every logit read once (the per-segment records it writes are < 0.01%)
     achieved = stats_bytes / (stats_avg_ms * 1e-3) / 1e9
 
@@ -249,7 +334,7 @@ def main():
                      "traffic": traffic, "avg_launch_ms": stats_avg_ms,
                      "algorithmic_bytes_per_launch": stats_bytes,
                      "timed_steps": args.steps,
-                     "ms_per_step_with_events": (t3 - t2) / args.steps * 1e3},
+                     "ms_per_step_with_events": ms_events},
         "cpu_baseline": None,
     }
     if args.cpu_seconds > 0:

@@ -131,13 +131,47 @@ sv_status spec_verify(const void *target_logits, const void *draft_logits, int32
                       int32_t *emitted_tokens, const sv_diag *diag, void *workspace,
                       size_t workspace_bytes, void *hip_stream);
 
+/*
+ * The drafter's draw: one token per logit vector, x_i ~ q_i = softmax(logits_i / T_i)
+ * (rayaq.ca "Speculative decoding", section "One round", step 1, and the drafter loop
+ * of section "Implementation", which applies the temperature softmax and then a
+ * categorical draw).  The draw is the same inverse CDF as the verification's: with
+ * t = u_i * sum_v q_i(v), the token is the smallest v whose running sum of q_i
+ * exceeds t.  T_i <= 0 takes the first argmax of the raw logits instead (a greedy
+ * drafter, brunomaga.github.io "inference-distillation-speculative-decoding",
+ * section "Draft-model speculative decoding").  The logits are read once.
+ *
+ *   logits       [n, vocab] dtype device, row-major (row i = vector i)
+ *   dtype        SV_BF16 or SV_F32
+ *   vocab        V, 1 <= V < 2^31
+ *   n            vectors, 0 <= n < 2^31
+ *   temperature  [n] float device: T_i
+ *   uniforms     [n] float device, each in [0, 1): u_i
+ *   tokens       [n] int32 device out: the drawn token, or -1 for an invalid vector
+ *   row_status   [n] int32 device out, or NULL: SV_ROW_NONFINITE (a NaN or +inf logit,
+ *                or all logits -inf) or SV_ROW_BAD_TEMP (T_i NaN, infinite or in
+ *                (0, FLT_MIN)); both make the vector invalid
+ *   workspace    device scratch, >= spec_sample_workspace_bytes(n, vocab, dtype) bytes,
+ *                256-byte aligned, contents overwritten
+ *   hip_stream   hipStream_t to enqueue on; asynchronous like spec_verify
+ *
+ * Host-detectable argument errors return a negative sv_status and enqueue nothing;
+ * the caller owns every buffer.
+ */
+size_t spec_sample_workspace_bytes(int64_t n, int64_t vocab, int32_t dtype);
+sv_status spec_sample(const void *logits, int32_t dtype, int64_t vocab, int64_t n,
+                      const float *temperature, const float *uniforms, int32_t *tokens,
+                      int32_t *row_status, void *workspace, size_t workspace_bytes,
+                      void *hip_stream);
+
 /* Static, human-readable name of an sv_status value. */
 const char *spec_verify_strerror(int32_t status);
 
 /*
  * Profiling aid: when both are non-NULL hipEvent_t handles, every following
- * spec_verify call records `start_event` on its stream right before its streaming
- * statistics kernel (the pass over every logit) and `stop_event` right after it.
+ * spec_verify or spec_sample call records `start_event` on its stream right before
+ * its streaming statistics kernel (the pass over every logit) and `stop_event`
+ * right after it.
  * Pass NULL, NULL to stop.  Process-wide setting, not thread-safe.
  */
 sv_status spec_verify_set_profile_events(void *start_event, void *stop_event);

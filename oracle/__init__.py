@@ -57,6 +57,8 @@ def _load(path: str):
     L.oracle_verify.argtypes = [vp, vp, ctypes.c_int, i64, i32, i64, vp, vp, vp, vp,
                                 ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, dbl, ctypes.c_int]
     L.oracle_verify.restype = ctypes.c_int
+    L.oracle_sample.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, vp, dbl, ctypes.c_int]
+    L.oracle_sample.restype = ctypes.c_int
     return L
 
 
@@ -171,6 +173,27 @@ def verify(target, draft, dtype: str, vocab: int, gamma, draft_tokens, uniforms,
                              _ptr(out["flag_pos"]), float(flag_eps), int(threads))
     if rc != 0:
         raise ValueError(f"oracle_verify status {rc}")
+    return out
+
+
+def sample(logits, dtype: str, vocab: int, temperature, uniforms, threads: int = 0,
+           flag_eps: float = 1e-5) -> dict:
+    """The drafter's draw: one token per logit vector (x ~ softmax(z/T) by inverse CDF
+    with that vector's uniform; argmax where T <= 0).  Returns tokens, status and
+    flags (1 where the draw's threshold is within flag_eps * W of an interior edge)."""
+    z = _logits(logits, dtype)
+    n = z.size // vocab
+    temperature = np.ascontiguousarray(temperature, np.float32)
+    uniforms = np.ascontiguousarray(uniforms, np.float32)
+    if temperature.shape[0] != n or uniforms.shape[0] != n:
+        raise ValueError("one temperature and one uniform per vector")
+    out = dict(tokens=np.empty(n, np.int32), status=np.empty(n, np.int32),
+               flags=np.empty(n, np.int32))
+    rc = lib().oracle_sample(_ptr(z), _DTYPES[dtype], int(vocab), int(n), _ptr(temperature),
+                             _ptr(uniforms), _ptr(out["tokens"]), _ptr(out["status"]),
+                             _ptr(out["flags"]), float(flag_eps), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_sample status {rc}")
     return out
 
 

@@ -452,3 +452,64 @@ int oracle_verify(const void *target, const void *draft, int dtype, int64_t V, i
     free(d_off);
     return rc;
 }
+
+/* ------------------------------------------------------------------------- */
+/* the drafter's draw: one token per logit vector                              */
+/* ------------------------------------------------------------------------- */
+/* x ~ q with q = softmax(z / T): the drafting step of a round (rayaq.ca
+ * "Speculative decoding", section "One round", step 1; the drafter loop of section
+ * "Implementation" applies the temperature softmax, then a categorical draw).  The
+ * draw is the same inverse CDF as the verification's draws, with the vector's own
+ * uniform u_i.  T <= 0 takes the argmax (the greedy drafter of brunomaga.github.io,
+ * section "Draft-model speculative decoding"); a non-finite or subnormal positive T
+ * and a vector without a softmax make the entry invalid (token -1).  flags[i] = 1
+ * when the draw's threshold lies within eps * W of an interior edge of the drawn
+ * token's CDF interval. */
+int oracle_sample(const void *logits, int dtype, int64_t V, int64_t n, const float *temperature,
+                  const float *uniforms, int32_t *tokens, int32_t *status_out, int32_t *flags,
+                  double flag_eps, int nthreads)
+{
+    const double eps = flag_eps > 0 ? flag_eps : 1e-5;
+    if (!logits || !temperature || !uniforms || !tokens || V <= 0 || n < 0)
+        return -1;
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_F32 && dtype != ORACLE_F64)
+        return -1;
+    int rc = 0;
+    const int nth = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel num_threads(nth)
+    {
+        double *w = malloc(sizeof(double) * (size_t)V);
+        if (!w) {
+#pragma omp atomic write
+            rc = -1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < n; ++i) {
+            if (!w)
+                continue;
+            const void *z = vector_ptr(logits, dtype, i, V);
+            const double T = (double)temperature[i];
+            int status = 0, near = 0;
+            int64_t tok = -1;
+            if (!isfinite(T) || (T > 0 && T < (double)FLT_MIN))
+                status |= ORACLE_BAD_TEMP;
+            if (vector_nonfinite(z, dtype, V))
+                status |= ORACLE_NONFINITE;
+            if (!status) {
+                if (T <= 0) {
+                    tok = oracle_argmax(z, dtype, V);
+                } else {
+                    oracle_softmax(z, dtype, V, T, w);
+                    tok = oracle_inverse_cdf(w, V, (double)uniforms[i], eps, NULL, &near);
+                }
+            }
+            tokens[i] = (int32_t)tok;
+            if (status_out)
+                status_out[i] = status;
+            if (flags)
+                flags[i] = near;
+        }
+        free(w);
+    }
+    return rc;
+}

@@ -31,4 +31,7 @@ int oracle_verify(const void *target, const void *draft, int dtype, int64_t V, i
                   int32_t *n_accepted, int32_t *emitted, double *p_x, double *q_x,
                   double *resid_mass, int32_t *row_status, int32_t *flag_pos, double flag_eps,
                   int nthreads);
+int oracle_sample(const void *logits, int dtype, int64_t V, int64_t n, const float *temperature,
+                  const float *uniforms, int32_t *tokens, int32_t *status_out, int32_t *flags,
+                  double flag_eps, int nthreads);
 #endif

@@ -31,7 +31,8 @@ ROW_BAD_TEMP = 32
 ROW_INVALID = ROW_BAD_TOKEN | ROW_NONFINITE | ROW_BAD_GAMMA | ROW_BAD_TEMP
 
 EXPORTED = ("spec_verify", "spec_verify_workspace_bytes", "spec_verify_strerror",
-            "spec_verify_set_profile_events", "spec_verify_version")
+            "spec_verify_set_profile_events", "spec_verify_version", "spec_sample",
+            "spec_sample_workspace_bytes")
 
 
 class SpecVerifyError(RuntimeError):
@@ -63,6 +64,10 @@ def _load():
     L.spec_verify_set_profile_events.restype = ctypes.c_int
     L.spec_verify_version.argtypes = []
     L.spec_verify_version.restype = ctypes.c_char_p
+    L.spec_sample_workspace_bytes.argtypes = [i64, i64, i32]
+    L.spec_sample_workspace_bytes.restype = sz
+    L.spec_sample.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp, vp, sz, vp]
+    L.spec_sample.restype = ctypes.c_int
     return L
 
 
@@ -79,6 +84,10 @@ def version() -> str:
 
 def workspace_bytes(batch: int, n_target_rows: int, vocab: int, dtype: int) -> int:
     return int(lib.spec_verify_workspace_bytes(batch, n_target_rows, vocab, dtype))
+
+
+def sample_workspace_bytes(n: int, vocab: int, dtype: int) -> int:
+    return int(lib.spec_sample_workspace_bytes(n, vocab, dtype))
 
 
 def set_profile_events(start_event, stop_event) -> None:
@@ -213,3 +222,52 @@ def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature
     if diag:
         return n_acc, emitted, dg
     return n_acc, emitted
+
+
+def spec_sample(logits, uniforms, temperature, *, status: bool = False,
+                workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """The drafter's draw on the GPU: one token per logit vector, x ~ softmax(z/T) by
+    inverse CDF with that vector's uniform (first argmax where T <= 0).
+
+    logits       bf16/fp32 [n, V] (or any shape [..., V]: every vector is one draw)
+    uniforms     float32, one per vector
+    temperature  float32 tensor with one entry per vector, or a Python float
+    Returns int32 tokens [n] (-1 for an invalid vector) and, with status=True, also
+    the int32 status bits per vector.  Asynchronous on torch's current stream.
+    """
+    device = logits.device
+    if device.type != "cuda":
+        raise ValueError("logits must be a GPU tensor")
+    if logits.dtype == torch.bfloat16:
+        dtype = SV_BF16
+    elif logits.dtype == torch.float32:
+        dtype = SV_F32
+    else:
+        raise ValueError(f"unsupported logits dtype {logits.dtype}")
+    V = int(logits.shape[-1])
+    n = logits.numel() // V if V else 0
+    if not isinstance(temperature, torch.Tensor):
+        temperature = torch.full((n,), float(temperature), dtype=torch.float32, device=device)
+    _check(logits, "logits", (logits.dtype,), device)
+    _check(uniforms, "uniforms", (torch.float32,), device)
+    _check(temperature, "temperature", (torch.float32,), device)
+    if uniforms.numel() != n or temperature.numel() != n:
+        raise ValueError("one uniform and one temperature per vector")
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=device)
+    else:
+        _check(out, "out", (torch.int32,), device)
+        if out.numel() != n:
+            raise ValueError("out must hold one token per vector")
+    st = torch.empty(n, dtype=torch.int32, device=device) if status else None
+    stream = torch.cuda.current_stream(device).cuda_stream
+    need = sample_workspace_bytes(n, V, dtype)
+    if workspace is None:
+        workspace = _workspace(device, stream, need)
+    elif workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
+    rc = lib.spec_sample(_ptr(logits), dtype, V, n, _ptr(temperature), _ptr(uniforms), _ptr(out),
+                         _ptr(st), _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, strerror(rc))
+    return (out, st) if status else out

@@ -124,3 +124,65 @@ extern "C" sv_status spec_verify(const void *target_logits, const void *draft_lo
     if (e == hipSuccess && mode == SV_SAMPLE) e = sv::launch_draw_final(P, s, dtype, aligned);
     return e == hipSuccess ? SV_OK : SV_EHIP;
 }
+
+extern "C" size_t spec_sample_workspace_bytes(int64_t n, int64_t vocab, int32_t dtype)
+{
+    if (n < 0 || n > INT32_MAX || vocab <= 0 || vocab > INT32_MAX || (dtype != SV_BF16 && dtype != SV_F32))
+        return 0;
+    const sv::Layout L = sv::make_layout((int32_t)n, n, vocab, dtype);
+    return L.total + ((sizeof(int32_t) * (size_t)n + 255) & ~(size_t)255);
+}
+
+// The drafter's draw is a verification of rows without drafts: every row is one
+// position, whose bonus draw from p_0 = softmax(z / T) with the row's uniform is the
+// sampled token (or its argmax when T <= 0).  No second pass over the logits runs:
+// the draw reuses the streaming pass's piece sums.
+extern "C" sv_status spec_sample(const void *logits, int32_t dtype, int64_t vocab, int64_t n,
+                                 const float *temperature, const float *uniforms, int32_t *tokens,
+                                 int32_t *row_status, void *workspace, size_t workspace_bytes,
+                                 void *hip_stream)
+{
+    if (dtype != SV_BF16 && dtype != SV_F32) return SV_EDTYPE;
+    if (n < 0 || n > INT32_MAX || vocab <= 0 || vocab > INT32_MAX) return SV_EINVAL;
+    if (n == 0) return SV_OK;
+    if (!logits || !temperature || !uniforms || !tokens || !workspace) return SV_EINVAL;
+    const size_t need = spec_sample_workspace_bytes(n, vocab, dtype);
+    if (workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) return SV_EWORKSPACE;
+
+    const sv::Layout L = sv::make_layout((int32_t)n, n, vocab, dtype);
+    const int64_t esz = dtype == SV_BF16 ? 2 : 4;
+    const bool aligned = (vocab * esz) % 16 == 0 && aligned16(logits);
+    char *ws = static_cast<char *>(workspace);
+    sv::Params P{};
+    P.target = logits;
+    P.V = vocab;
+    P.B = (int32_t)n;
+    P.mode = SV_SAMPLE;
+    P.nT = n;
+    P.nD = 0;
+    P.uniforms = uniforms;
+    P.temperature = temperature;
+    P.gamma_uniform = 0;
+    P.n_accepted = reinterpret_cast<int32_t *>(ws + L.total);
+    P.emitted = tokens;
+    P.row_status = row_status;
+    P.hdr = reinterpret_cast<sv::Header *>(ws + L.hdr);
+    P.rows = reinterpret_cast<sv::RowInfo *>(ws + L.rows);
+    P.vinfo = reinterpret_cast<sv::VecInfo *>(ws + L.vinfo);
+    P.parts = reinterpret_cast<sv::Partial *>(ws + L.parts);
+    P.zx = reinterpret_cast<float *>(ws + L.zx);
+    P.draws = reinterpret_cast<sv::RowDraw *>(ws + L.draws);
+    P.tiles = reinterpret_cast<sv::Sum2 *>(ws + L.tiles);
+    P.geo = sv::make_geometry((int32_t)n, n, vocab, SV_SAMPLE, dtype, sv::stats_grid_cap(dtype, aligned));
+    P.geo.inv_t = 1.0;
+    P.geo.inv_d = 0.0;
+
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = hipSuccess;
+    if (g_prof_start) e = hipEventRecord(g_prof_start, s);
+    if (e == hipSuccess) e = sv::launch_stats(P, s, dtype, aligned);
+    if (e == hipSuccess && g_prof_stop) e = hipEventRecord(g_prof_stop, s);
+    if (e == hipSuccess) e = sv::launch_scan(P, s, dtype);
+    if (e == hipSuccess) e = sv::launch_draw_final(P, s, dtype, aligned);
+    return e == hipSuccess ? SV_OK : SV_EHIP;
+}

@@ -6,10 +6,11 @@
 // positions: it keeps x_j while u_j < min(1, p_j(x_j)/q_j(x_j)) (rayaq.ca
 // "Speculative decoding", section "One round", step 3), or while x_j equals the
 // argmax in greedy mode (section "The greedy case"), writes the row's outputs and
-// what its draw needs.  verify_kernel re-reads only position K of each sampling row
-// and sums the draw weights per 512-logit tile: the residual max(0, p - q) after a
-// rejection (step 4) or p for the bonus token (step 5).  draw_final_kernel walks
-// one row's tile sums and one tile to the inverse-CDF token.
+// what its draw needs.  After a rejection verify_kernel re-reads position K of the
+// row and sums the residual max(0, p - q) (step 4) per 512-logit tile, and
+// draw_final_kernel walks the tile sums and one tile to the inverse-CDF token.  The
+// bonus token (step 5) is drawn from p, whose sums per piece the streaming pass
+// already holds: draw_final_kernel walks those and re-reads one piece.
 //
 // bf16 logits are processed in fp32 (exp2 on the hardware unit, fp64 sums across
 // lanes); fp32 logits are processed in fp64 throughout.
@@ -203,6 +204,7 @@ __device__ __forceinline__ void scan_merge(const Params &P, const RowGeom &G, in
                 sh.S[side][j] = S;
                 if (side == 0) sh.idx[j] = idx;
             }
+
         }
     }
 }
@@ -432,7 +434,7 @@ struct DrawConst<0> {
     }
     __device__ __forceinline__ float unnorm(float z, float B, float m, bool slow) const
     {
-        return slow ? hw_exp2((z - m) * c) : hw_exp2(fmaf(z, c, -B));
+        return hw_exp2(slow ? (z - m) * c : fmaf(z, c, -B));
     }
     using W = float;
     // weights of one unit: w (residual or p) and p
@@ -499,7 +501,8 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(Params P)
     scan_body<DT>(P);
 }
 
-// The draw's tile sums: workgroup `piece` of a row sums its slice of position K.
+// The residual's tile sums: workgroup `piece` of a row that rejected sums its slice of
+// position K.
 template <int DT, bool AL>
 __device__ __forceinline__ void verify_body(const Params &P)
 {
@@ -509,7 +512,7 @@ __device__ __forceinline__ void verify_body(const Params &P)
     const int32_t piece = (int32_t)(blockIdx.x - (int64_t)row * per_row);
     if (P.gamma != nullptr && P.hdr->status != 0) return;
     const RowDraw D = P.draws[row];
-    if (D.kind == DRAW_NONE) return;
+    if (D.kind != DRAW_RESIDUAL) return;
     DrawConst<DT> c;
     c.init(D);
     const void *tb = vec_ptr(P.target, DT, D.t_row, P.V);
@@ -566,14 +569,230 @@ __global__ __launch_bounds__(kBlock) void verify_kernel_f32(Params P)
     verify_body<1, AL>(P);
 }
 
-// one wave per row
-template <int DT, bool AL>
-__global__ __launch_bounds__(64) void draw_final_kernel(Params P)
+// ---------------------------------------------------------------------------
+// bonus draw from the streaming pass's records: the weights are p at position K, so
+// the piece sums are already known (the sum 2^((z - M_j) c) of piece j, taken to the
+// vector maximum m and divided by S).  One wave per row finds the piece where the
+// running sum first exceeds t = u W, then re-reads that piece only: its tiles'
+// sums, the tile, the token.
+// ---------------------------------------------------------------------------
+
+// logits per draw piece (two halves of the streaming pass) and tiles per piece
+template <int DT> constexpr int kPieceTiles = 2 * kItemBytes / (DT == 0 ? 2 : 4) / kTileElems;
+
+// Sum of p over piece q of a vector whose maximum is m and sum 2^((z - m) c) is S.
+template <int DT>
+__device__ __forceinline__ double piece_weight(const Partial &q, const TempConst &tc, float m, double S)
 {
-    const int lane = threadIdx.x;
-    const int32_t row = blockIdx.x;
-    const RowDraw D = P.draws[row];
-    if (D.kind == DRAW_NONE) return;
+    if (!(q.m > -INFINITY)) return 0.0;
+    return q.s * exp2_f64(rec_shift<DT>(q, tc) + ((double)q.m - (double)m) * tc.c_eff) / S;
+}
+
+// The bonus draw's piece from the pieces' p sums (lane j holds piece j): the first
+// piece where the running sum exceeds t = u W, else the last one with weight.
+template <int DT>
+__device__ __forceinline__ void bonus_piece(const Partial &q, const TempConst &tc, float m, double S, float u,
+                                            int lane, int32_t &piece, double &before, double &W)
+{
+    const double w = (m == m && S > 0.0) ? piece_weight<DT>(q, tc, m, S) : 0.0;
+    const double incl = wave_inclusive_sum(w, lane);
+    W = __shfl(incl, 63);
+    const double t = (double)u * W;
+    const unsigned long long hit = __ballot(incl > t && w > 0.0);
+    const unsigned long long pos = __ballot(w > 0.0);
+    const int l = hit ? __ffsll((long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : -1);
+    piece = l;
+    before = l >= 0 ? __shfl(incl - w, l) : 0.0;
+}
+
+// Totals over the 64 lanes of N per-lane values (N a power of two, at most 64), in
+// every lane: a butterfly where each exchange also halves the values a lane carries
+// (log2 N steps leave lane l the partial total of value bitrev(l mod N) over its
+// group of N lanes), then the groups are added, and the totals read back per value.
+template <int N>
+__device__ __forceinline__ void wave_totals(double (&v)[N], int lane)
+{
+    constexpr int LOGN = N == 1 ? 0 : N == 2 ? 1 : N == 4 ? 2 : N == 8 ? 3 : N == 16 ? 4 : N == 32 ? 5 : 6;
+    static_assert((1 << LOGN) == N, "N must be a power of two up to 64");
+    double x[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) x[k] = v[k];
+#pragma unroll
+    for (int st = 0; st < LOGN; ++st) {
+        const int half = N >> (st + 1);
+        const bool up = (lane >> st) & 1;
+#pragma unroll
+        for (int k = 0; k < half; ++k) {
+            const double send = up ? x[k] : x[k + half];
+            const double keep = up ? x[k + half] : x[k];
+            x[k] = keep + __shfl_xor(send, 1 << st);
+        }
+    }
+    double t = x[0];
+#pragma unroll
+    for (int m = N; m < 64; m <<= 1) t += __shfl_xor(t, m);
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        int r = 0;   // the lane holding value k: k with its LOGN bits reversed
+#pragma unroll
+        for (int bit = 0; bit < LOGN; ++bit) r |= ((k >> bit) & 1) << (LOGN - 1 - bit);
+        v[k] = readlane_f64(t, r);
+    }
+}
+
+// The bonus draw by the workgroup's four waves: the piece (chosen by the scan, or
+// here for vectors of more than 64 pieces), each wave's quarter of its tiles summed,
+// the tile, the token.
+template <int DT, bool AL>
+__device__ __forceinline__ void draw_bonus_row(const Params &P, const RowDraw &D, int32_t row, int lane, int wave,
+                                               double *s_ts)
+{
+    const TempConst tc = temp_const<DT>(D.T);
+    int64_t piece = -1;
+    double before = 0.0, W = 0.0;
+    // the piece from the records (every wave computes the same): one per lane when the
+    // vector has at most 64 pieces, else contiguous runs per lane
+    if (P.geo.ipv <= 64) {
+        const Partial q = lane < P.geo.ipv ? P.parts[(int64_t)D.t_row * P.geo.ipv + lane]
+                                           : Partial{-INFINITY, INT32_MAX, 0.0};
+        int32_t pc;
+        bonus_piece<DT>(q, tc, D.m_t, D.S_t, D.u, lane, pc, before, W);
+        piece = pc;
+    } else {
+        const int64_t ipv = P.geo.ipv;
+        const Partial *rec = P.parts + (int64_t)D.t_row * ipv;
+        const int64_t per = (ipv + 63) / 64;
+        const int64_t l0 = lane * per;
+        const int64_t l1 = min(l0 + per, ipv);
+        double lw = 0.0;
+        for (int64_t j = l0; j < l1; ++j) lw += piece_weight<DT>(rec[j], tc, D.m_t, D.S_t);
+        const double iw = wave_inclusive_sum(lw, lane);
+        W = __shfl(iw, 63);
+        const double t = (double)D.u * W;
+        double cum = iw - lw;
+        int64_t cand = -1, lastpos = -1;
+        double cand_before = 0.0, last_before = 0.0;
+        for (int64_t j = l0; j < l1; ++j) {
+            const double v = piece_weight<DT>(rec[j], tc, D.m_t, D.S_t);
+            if (cand < 0 && cum + v > t) { cand = j; cand_before = cum; }
+            if (v > 0.0) { lastpos = j; last_before = cum; }
+            cum += v;
+        }
+        const unsigned long long hit = __ballot(cand >= 0);
+        if (hit) {
+            const int l = __ffsll((long long)hit) - 1;
+            piece = __shfl(cand, l);
+            before = __shfl(cand_before, l);
+        } else {
+            const unsigned long long pos = __ballot(lastpos >= 0);
+            if (pos) {
+                const int l = 63 - __clzll((long long)pos);
+                piece = __shfl(lastpos, l);
+                before = __shfl(last_before, l);
+            }
+        }
+    }
+    const double t = (double)D.u * W;
+    constexpr int NT = kPieceTiles<DT>;
+    constexpr int NW = NT / kWaves;   // tiles per wave
+    if (piece < 0) {   // no piece has weight (cannot happen for a valid row)
+        if (wave == 0 && lane == 0) {
+            P.emitted[D.t_slot] = -1;
+            if (P.resid) P.resid[row] = W;
+        }
+        return;
+    }
+    DrawConst<DT> c;
+    c.init(D);
+    const void *tb = vec_ptr(P.target, DT, D.t_row, P.V);
+    const int64_t tile0 = piece * NT + wave * NW;
+    RawUnit<DT> r[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+        const int64_t unit = (tile0 + k) * kTileUnits + lane;
+        r[k] = unit < P.geo.nunits ? load_raw<DT, AL>(tb, unit, P.V) : neg_inf_unit<DT>();
+    }
+    double ls[NW], ts[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+        float z[kUnitElems];
+        unpack<DT>(r[k], z);
+        typename DrawConst<DT>::W w[kUnitElems], pe[kUnitElems];
+        c.weights(z, z, w, pe);
+        ls[k] = 0.0;
+#pragma unroll
+        for (int e = 0; e < kUnitElems; ++e) ls[k] += pe[e];
+        ts[k] = ls[k];
+    }
+    wave_totals<NW>(ts, lane);
+    if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < NW; ++k) s_ts[wave * NW + k] = ts[k];
+    }
+    __syncthreads();
+    // the tile where the running sum first exceeds t, else the last tile of the piece
+    // with weight (a crossing lost to rounding between the two sums)
+    int kt = -1, kl = -1;
+    double tb_hit = 0.0, tb_last = 0.0, run = before;
+    for (int k = 0; k < NT; ++k) {
+        const double v = s_ts[k];
+        if (kt < 0 && run + v > t) { kt = k; tb_hit = run; }
+        if (v > 0.0) { kl = k; tb_last = run; }
+        run += v;
+    }
+    const int k_sel = kt >= 0 ? kt : kl;
+    int32_t token = -1;
+    if (k_sel >= 0 && k_sel / NW == wave) {
+        const double tile_before = kt >= 0 ? tb_hit : tb_last;
+        const int ks = k_sel - wave * NW;
+        double my = 0.0;
+        RawUnit<DT> rs = r[0];
+#pragma unroll
+        for (int k = 0; k < NW; ++k)
+            if (k == ks) { my = ls[k]; rs = r[k]; }
+        float z[kUnitElems];
+        unpack<DT>(rs, z);
+        typename DrawConst<DT>::W w[kUnitElems], pe[kUnitElems];
+        c.weights(z, z, w, pe);
+        const double incl = wave_inclusive_sum(my, lane);
+        double rr = tile_before + incl - my;
+        int ce = -1, lpos = -1;
+#pragma unroll
+        for (int e = 0; e < kUnitElems; ++e) {
+            const double we = pe[e];
+            rr += we;
+            if (ce < 0 && rr > t) ce = e;
+            if (we > 0.0) lpos = e;
+        }
+        const int64_t unit = (tile0 + ks) * kTileUnits + lane;
+        const unsigned long long h2 = __ballot(ce >= 0);
+        if (h2) {
+            const int l = __ffsll((long long)h2) - 1;
+            token = __shfl((int)(unit * kUnitElems) + ce, l);
+        } else {
+            const unsigned long long p2 = __ballot(lpos >= 0);
+            if (p2) {
+                const int l = 63 - __clzll((long long)p2);
+                token = __shfl((int)(unit * kUnitElems) + lpos, l);
+            }
+        }
+        // no logit of the piece has a weight in fp32 although its record does (its
+        // probability is below 2^-126): the piece's first logit stands in
+        if (token < 0) token = (int32_t)(piece * NT * kTileElems);
+        if (lane == 0) {
+            P.emitted[D.t_slot] = token;
+            if (P.resid) P.resid[row] = W;
+        }
+    } else if (k_sel < 0 && wave == 0 && lane == 0) {
+        P.emitted[D.t_slot] = (int32_t)(piece * NT * kTileElems);
+        if (P.resid) P.resid[row] = W;
+    }
+}
+
+// The residual draw from the tile sums of the row's position K.
+template <int DT, bool AL>
+__device__ __forceinline__ void draw_residual_row(const Params &P, const RowDraw &D, int32_t row, int lane)
+{
     const int32_t nt = P.geo.ntiles;
     const Sum2 *tiles = P.tiles + (int64_t)row * nt;
     const int per = (nt + 63) / 64;        // tiles per lane, contiguous
@@ -587,7 +806,6 @@ __global__ __launch_bounds__(64) void draw_final_kernel(Params P)
     double W = __shfl(iw, 63);
     bool use_p = false;
     if (D.kind == DRAW_RESIDUAL && !(W > 0.0)) use_p = true;
-    if (D.kind == DRAW_BONUS) use_p = false;
     if (use_p) W = __shfl(ip, 63);
     const double t = (double)D.u * W;
 
@@ -664,6 +882,22 @@ __global__ __launch_bounds__(64) void draw_final_kernel(Params P)
     }
 }
 
+// One workgroup of four waves per row: the residual walk runs on wave 0, the bonus
+// draw on all four.
+template <int DT, bool AL>
+__global__ __launch_bounds__(kBlock) void draw_final_kernel(Params P)
+{
+    __shared__ double s_ts[kPieceTiles<DT>];
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int32_t row = blockIdx.x;
+    const RowDraw D = P.draws[row];
+    if (D.kind == DRAW_RESIDUAL) {
+        if (wave == 0) draw_residual_row<DT, AL>(P, D, row, lane);
+    } else if (D.kind == DRAW_BONUS) {
+        draw_bonus_row<DT, AL>(P, D, row, lane, wave, s_ts);
+    }
+}
+
 // ===========================================================================
 // launchers
 // ===========================================================================
@@ -699,7 +933,7 @@ hipError_t launch_draw_final(const Params &P, hipStream_t s, int dtype, bool ali
     const void *fn = dtype == 0
         ? (aligned ? (const void *)draw_final_kernel<0, true> : (const void *)draw_final_kernel<0, false>)
         : (aligned ? (const void *)draw_final_kernel<1, true> : (const void *)draw_final_kernel<1, false>);
-    return launch(fn, P.B, 64, P, s);
+    return launch(fn, P.B, kBlock, P, s);
 }
 
 }  // namespace sv

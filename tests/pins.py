@@ -668,4 +668,55 @@ def pin_status_rules():
     assert r["n_accepted"][0] == 1 and r["row_status"][0] == oracle.Q_ZERO
 
 
+
+# --------------------------------------------------------------------------- #
+# the drafter's draw (x ~ q)
+# --------------------------------------------------------------------------- #
+def pin_sample_closed_form():
+    """Hand-computed draws: logits (0, ln 3, 0, 0) give (1, 3, 1, 1)/6 at T = 1 and
+    (1, 9, 1, 1)/12 at T = 1/2; bf16 logits (0, 1, 0, 0) give (1, e, 1, 1)/(3 + e)."""
+    z = np.array([0.0, math.log(3.0), 0.0, 0.0])
+    cases = [(1.0, [0.1, 0.2, 0.6, 0.7, 0.95], [0, 1, 1, 2, 3]),
+             (0.5, [0.05, 0.5, 0.85, 0.99], [0, 1, 2, 3])]
+    for T, us, want in cases:
+        r = oracle.sample(np.tile(z, (len(us), 1)), "f64", 4, [T] * len(us), us)
+        assert list(r["tokens"]) == want, (T, r["tokens"])
+        assert not r["status"].any()
+    zb = np.tile(np.array([0x0000, 0x3F80, 0x0000, 0x0000], np.uint16), (5, 1))
+    # edges 1/(3+e) = 0.1749, (1+e)/(3+e) = 0.6501, (2+e)/(3+e) = 0.8251
+    r = oracle.sample(zb, "bf16", 4, [1.0] * 5, [0.17, 0.18, 0.65, 0.66, 0.83])
+    assert list(r["tokens"]) == [0, 1, 1, 2, 3], r["tokens"]
+
+
+def pin_sample_stratified_counts():
+    """Uniforms on a regular grid (k + 1/2)/N hit every token v within one count of
+    N p_v, with p = scipy's softmax of z/T."""
+    rng = np.random.default_rng(23)
+    V, N = 10, 20000
+    z = rng.standard_normal(V) * 2.0
+    T = 0.7
+    u = ((np.arange(N) + 0.5) / N).astype(np.float32)
+    r = oracle.sample(np.tile(z, (N, 1)), "f64", V, np.full(N, T, np.float32), u)
+    p = scipy.special.softmax(z / np.float64(np.float32(T)))
+    counts = np.bincount(r["tokens"], minlength=V)
+    assert np.all(np.abs(counts - N * p) <= 1.0 + 1e-9), (counts, N * p)
+
+
+def pin_sample_greedy_and_status():
+    """T <= 0 takes the first argmax; a bad temperature or a vector without a softmax
+    gives token -1 with its status bit; -inf logits are never drawn."""
+    z = np.array([[1.0, 3.0, 3.0, 2.0]] * 6)
+    z[4, 2] = np.nan
+    z[5, :] = -np.inf
+    T = np.array([0.0, -1.0, np.nan, 1e-39, 1.0, 1.0], np.float32)
+    r = oracle.sample(z, "f64", 4, T, np.full(6, 0.5, np.float32))
+    assert list(r["tokens"][:2]) == [1, 1]
+    assert r["status"][2] & oracle.BAD_TEMP and r["status"][3] & oracle.BAD_TEMP
+    assert r["status"][4] & oracle.NONFINITE and r["status"][5] & oracle.NONFINITE
+    assert np.all(r["tokens"][2:] == -1)
+    zm = np.array([[-np.inf, 0.0, -np.inf, 0.0]] * 4)
+    r = oracle.sample(zm, "f64", 4, np.ones(4, np.float32), [0.0, 0.49, 0.51, F32_BELOW_ONE])
+    assert list(r["tokens"]) == [1, 1, 3, 3] and not r["status"].any()
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -17,7 +17,7 @@ def _declared():
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         for m in re.finditer(r"\b([a-z_][a-z0-9_]*)\s*\(", text):
             name = m.group(1)
-            if name.startswith("spec_verify"):
+            if name.startswith("spec_"):
                 names.add(name)
     return names
 
@@ -85,3 +85,33 @@ def test_host_argument_errors(sv):
     assert _call(sv, ws=(1 << 27) + 64) == sv.SV_EWORKSPACE  # misaligned
     assert _call(sv, batch=0, nT=0) == sv.SV_OK              # empty batch: nothing to do
     assert sv.lib.spec_verify_set_profile_events(ctypes.c_void_p(1), None) == sv.SV_EINVAL
+
+
+def _call_sample(sv, **kw):
+    args = dict(logits=1 << 20, dtype=sv.SV_BF16, vocab=32, n=4, temperature=1 << 24,
+                uniforms=1 << 23, tokens=1 << 25, status=None, ws=1 << 27, ws_bytes=1 << 30)
+    args.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return sv.lib.spec_sample(vp(args["logits"]), args["dtype"], args["vocab"], args["n"],
+                              vp(args["temperature"]), vp(args["uniforms"]), vp(args["tokens"]),
+                              vp(args["status"]), vp(args["ws"]), args["ws_bytes"], None)
+
+
+def test_sample_host_argument_errors(sv):
+    assert _call_sample(sv, dtype=5) == sv.SV_EDTYPE
+    assert _call_sample(sv, vocab=0) == sv.SV_EINVAL
+    assert _call_sample(sv, n=-1) == sv.SV_EINVAL
+    assert _call_sample(sv, n=1 << 31) == sv.SV_EINVAL
+    assert _call_sample(sv, logits=None) == sv.SV_EINVAL
+    assert _call_sample(sv, uniforms=None) == sv.SV_EINVAL
+    assert _call_sample(sv, temperature=None) == sv.SV_EINVAL
+    assert _call_sample(sv, tokens=None) == sv.SV_EINVAL
+    assert _call_sample(sv, ws=None) == sv.SV_EINVAL
+    assert _call_sample(sv, ws_bytes=100) == sv.SV_EWORKSPACE
+    assert _call_sample(sv, ws=(1 << 27) + 64) == sv.SV_EWORKSPACE
+    assert _call_sample(sv, n=0) == sv.SV_OK
+    a = sv.sample_workspace_bytes(320, 128256, sv.SV_BF16)
+    assert 0 < a < 64 << 20 and a % 256 == 0
+    assert sv.sample_workspace_bytes(-1, 10, sv.SV_BF16) == 0
+    assert sv.sample_workspace_bytes(4, 0, sv.SV_F32) == 0
+    assert sv.sample_workspace_bytes(4, 10, 7) == 0

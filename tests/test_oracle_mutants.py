@@ -36,6 +36,10 @@ MUTANTS = {
     "alpha_with_max": ("a += fmin(pp[v], qq[v]);", "a += fmax(pp[v], qq[v]);"),
     "flag_threshold_too_wide": ("if (flag < 0 && fabs(u - ratio) < eps)", "if (flag < 0 && fabs(u - ratio) < 100 * eps)"),
     "no_zero_residual_fallback": ("                if (W == 0.0) {", "                if (W < 0.0) {"),
+    "sample_without_temperature": ("oracle_softmax(z, dtype, V, T, w);", "oracle_softmax(z, dtype, V, 1.0, w);"),
+    "sample_first_uniform": ("tok = oracle_inverse_cdf(w, V, (double)uniforms[i], eps, NULL, &near);",
+                             "tok = oracle_inverse_cdf(w, V, (double)uniforms[0], eps, NULL, &near);"),
+    "sample_greedy_below_one": ("                if (T <= 0) {", "                if (T < 1) {"),
     "neg_inf_is_nonfinite": ("if (isnan(x) || x == INFINITY)", "if (isnan(x) || isinf(x))"),
 }
 

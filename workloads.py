@@ -319,6 +319,39 @@ def small(seed: int, batch: int, vocab: int, dtype: str, gamma, temperature=1.0,
                  tf, _noisy_draft(1.0, noise), mode=mode)
 
 
+@dataclass
+class SampleInputs:
+    """Inputs of the drafter's draw: n logit vectors, one temperature and one uniform
+    each."""
+    name: str
+    dtype: str
+    vocab: int
+    logits: np.ndarray         # uint16 bits (bf16) or float32, [n, V]
+    temperature: np.ndarray    # float32 [n]
+    uniforms: np.ndarray       # float32 [n], k * 2^-24
+
+    @property
+    def n(self) -> int:
+        return int(self.logits.shape[0])
+
+
+def sample_inputs(w: Workload, seed: int, side: str = "draft", limit: int | None = None) -> SampleInputs:
+    """The vectors of one side of a workload (its draft rows, or its target rows), each
+    with its row's temperature and a fresh uniform from its own Philox stream."""
+    t_off, d_off = w.offsets()
+    if side == "draft":
+        logits = w.draft
+        temp = np.repeat(w.temperature, w.gamma)
+    else:
+        logits = w.target
+        temp = np.repeat(w.temperature, w.gamma + 1)
+    if limit is not None:
+        logits, temp = logits[:limit], temp[:limit]
+    u = snapped_uniforms(_rng(seed, 7, 0), logits.shape[0])
+    return SampleInputs(f"{w.name}_{side}", w.dtype, w.vocab, np.ascontiguousarray(logits),
+                        np.ascontiguousarray(temp, np.float32), u)
+
+
 CONFIGS = {
     "toy": toy,
     "c2": c2,
