@@ -46,9 +46,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c3", choices=["c2", "c3", "c4", "c5"])
     ap.add_argument("--mode", default="sample", choices=["sample", "greedy"])
-    ap.add_argument("--op", default="verify", choices=["verify", "sample"],
+    ap.add_argument("--op", default="verify", choices=["verify", "sample", "tree"],
                     help="verify: the verification step (default); sample: the drafter's draw "
-                         "over the configuration's draft logit vectors")
+                         "over the configuration's draft logit vectors; tree: greedy verification "
+                         "of 16 Medusa trees (top-2 candidates, 5 heads: 63 nodes) at V = 128256 bf16")
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
@@ -228,6 +229,71 @@ def bench_sample(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_tree(args):
+    """Greedy verification of candidate trees: 16 Medusa-shaped trees of 63 nodes
+    (top-2 candidates from each of 5 heads) over V = 128256 bf16 logits."""
+    import numpy as np
+    import torch
+
+    import speculative_sampling_verify_02_amd as sv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    tr = workloads.trees(21, 16, 128256, "bf16", top_k=2, heads=5)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    copies = [dict(z=torch.from_numpy(tr.logits.view(np.int16)).to(dev).view(torch.bfloat16),
+                   c=t(tr.counts), k=t(tr.tokens), p=t(tr.parents)) for _ in range(max(1, args.copies))]
+    n, V, B = tr.n_nodes, tr.vocab, int(tr.counts.shape[0])
+    outs = [(torch.empty(B, dtype=torch.int32, device=dev), torch.empty(n, dtype=torch.int32, device=dev),
+             torch.empty(n, dtype=torch.int32, device=dev)) for _ in copies]
+    ws = torch.empty(sv.tree_workspace_bytes(n, V, sv.SV_BF16), dtype=torch.uint8, device=dev)
+
+    def step(k):
+        d = copies[k % len(copies)]
+        return sv.spec_tree_verify_greedy(d["z"], d["c"], d["k"], d["p"], workspace=ws, out=outs[k % len(copies)])
+
+    n_acc = step(0)[0]
+    torch.cuda.synchronize()
+    K = n_acc.cpu().numpy()
+    for k in range(args.warmup):
+        step(k)
+    sec, stats_ms, ms_ev = timed_steps(step, args.steps, sv)
+    pass1 = n * V * 2
+    total = pass1 + n * 16
+    achieved = pass1 / (stats_ms * 1e-3) / 1e9
+    res = {
+        "metric": "verified tree nodes/sec (greedy tree verification) and achieved HBM GB/s",
+        "value": n / sec, "unit": "nodes/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": sec * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": tr.name, "trees": B, "nodes": n, "vocab": V, "rotated_device_copies": len(copies)},
+        "trees_per_s": B / sec,
+        "mean_kept_drafts": float(K[K >= 0].mean()),
+        "hbm_gbps_algorithmic": total / sec / 1e9,
+        "hbm_frac_of_peak": total / sec / 1e9 / PEAK_HBM_GBPS,
+        "roofline": {"kernel": "stats_kernel", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+                     "avg_launch_ms": stats_ms, "algorithmic_bytes_per_launch": pass1,
+                     "timed_steps": args.steps, "ms_per_step_with_events": ms_ev},
+        "cpu_baseline": None,
+    }
+    if args.cpu_seconds > 0:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        t0 = time.perf_counter()
+        calls = 0
+        while True:
+            oracle.tree_greedy(tr.logits, "bf16", V, tr.counts, tr.tokens, tr.parents, threads=cores)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or calls >= 10000:
+                break
+        res["cpu_baseline"] = {"value": n * calls / el, "unit": "nodes/s", "cores": int(cores), "kind": "oracle",
+                               "sample": f"{calls} full calls ({B} trees, {n} nodes each), {el:.1f} s wall, "
+                                         f"OpenMP over trees"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -237,6 +303,9 @@ def main():
         sys.exit(2)
     if args.op == "sample":
         bench_sample(args)
+        return
+    if args.op == "tree":
+        bench_tree(args)
         return
     import numpy as np
     import torch

@@ -79,6 +79,9 @@ typedef enum { SV_SAMPLE = 0, SV_GREEDY = 1 } sv_mode;
                                  the token was drawn from p_K instead (informational)          */
 #define SV_ROW_BAD_TEMP 32    /* sampling row whose temperature is NaN, infinite, or in
                                  (0, FLT_MIN)                                                   */
+#define SV_ROW_BAD_TREE 64    /* spec_tree_verify_greedy: a tree with no node, more than 2048
+                                 nodes, a root with a parent, or a node whose parent is not an
+                                 earlier node of its tree                                      */
 
 /* Optional diagnostics: every pointer may be NULL; all are device pointers. */
 typedef struct sv_diag {
@@ -164,12 +167,63 @@ sv_status spec_sample(const void *logits, int32_t dtype, int64_t vocab, int64_t 
                       int32_t *row_status, void *workspace, size_t workspace_bytes,
                       void *hip_stream);
 
+/*
+ * Greedy verification of candidate trees (brunomaga.github.io "inference-distillation-
+ * speculative-decoding", section "Medusa": the candidates of several positions form
+ * a tree, one forward pass with tree attention scores every node, and the longest
+ * accepted path is kept).  Node k's prediction is the first argmax of the target's
+ * raw logits at k; a node is kept when its parent is kept and its token equals the
+ * parent's prediction; the root (node 0 of a tree, parent -1) is the target's own
+ * last token and is always kept.  The result per tree is the longest kept path from
+ * the root (the one ending at the lowest node index among equally long ones),
+ * followed by the prediction at its last node, the target's next token.
+ *
+ * LAYOUT.  Trees are packed: tree i holds nodes [off_i, off_i + node_counts[i]),
+ * off_i = sum_{j<i} node_counts[j]; row off_i + k of target_logits holds node k of
+ * tree i.  parents[] are tree-local node indices, each parent listed before its
+ * children (parent < node); the root's parent is -1.
+ *
+ *   target_logits  [n_nodes, vocab] dtype device
+ *   dtype          SV_BF16 or SV_F32
+ *   vocab          V, 1 <= V < 2^31
+ *   n_trees        B >= 0
+ *   n_nodes        sum(node_counts), < 2^31
+ *   node_counts    [B] int32 device, each in [1, 2048]
+ *   tokens         [n_nodes] int32 device: each node's token (the root's is not tested)
+ *   parents        [n_nodes] int32 device
+ *   n_accepted     [B] int32 device out: kept drafts on the path (path length - 1), or -1
+ *                  for an invalid tree
+ *   path           [n_nodes] int32 device out: at off_i + d the tree-local node at depth d
+ *                  of the path, then -1
+ *   emitted        [n_nodes] int32 device out: at off_i the tokens of the path's nodes
+ *                  after the root, then the prediction at its last node, then -1
+ *   row_status     [B] int32 device out, or NULL: SV_ROW_BAD_TREE, SV_ROW_BAD_TOKEN (a
+ *                  token outside [0, vocab)), SV_ROW_NONFINITE (a node whose logits hold
+ *                  NaN or +inf, or are all -inf), SV_ROW_BAD_GAMMA on every tree when the
+ *                  counts do not add up to n_nodes; each makes the tree invalid (-1 in all
+ *                  its outputs)
+ *   workspace      device scratch of spec_tree_verify_greedy_workspace_bytes(...) bytes,
+ *                  256-byte aligned, contents overwritten
+ *   hip_stream     hipStream_t to enqueue on; asynchronous like spec_verify
+ *
+ * Every logit is read once.  Host-detectable argument errors return a negative
+ * sv_status and enqueue nothing; the caller owns every buffer.
+ */
+size_t spec_tree_verify_greedy_workspace_bytes(int64_t n_nodes, int64_t vocab, int32_t dtype);
+sv_status spec_tree_verify_greedy(const void *target_logits, int32_t dtype, int64_t vocab,
+                                  int32_t n_trees, int64_t n_nodes, const int32_t *node_counts,
+                                  const int32_t *tokens, const int32_t *parents,
+                                  int32_t *n_accepted, int32_t *path, int32_t *emitted,
+                                  int32_t *row_status, void *workspace, size_t workspace_bytes,
+                                  void *hip_stream);
+
 /* Static, human-readable name of an sv_status value. */
 const char *spec_verify_strerror(int32_t status);
 
 /*
  * Profiling aid: when both are non-NULL hipEvent_t handles, every following
- * spec_verify or spec_sample call records `start_event` on its stream right before
+ * spec_verify, spec_sample or spec_tree_verify_greedy call records `start_event` on its
+ * stream right before
  * its streaming statistics kernel (the pass over every logit) and `stop_event`
  * right after it.
  * Pass NULL, NULL to stop.  Process-wide setting, not thread-safe.

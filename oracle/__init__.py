@@ -25,7 +25,8 @@ NONFINITE = 4
 BAD_GAMMA = 8
 ZERO_RESID = 16
 BAD_TEMP = 32
-INVALID_MASK = BAD_TOKEN | NONFINITE | BAD_GAMMA | BAD_TEMP
+BAD_TREE = 64
+INVALID_MASK = BAD_TOKEN | NONFINITE | BAD_GAMMA | BAD_TEMP | BAD_TREE
 
 _DTYPES = {"bf16": BF16, "f32": F32, "f64": F64}
 
@@ -59,6 +60,9 @@ def _load(path: str):
     L.oracle_verify.restype = ctypes.c_int
     L.oracle_sample.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, vp, dbl, ctypes.c_int]
     L.oracle_sample.restype = ctypes.c_int
+    L.oracle_tree_greedy.argtypes = [vp, ctypes.c_int, i64, i32, i64, vp, vp, vp, vp, vp, vp, vp,
+                                     ctypes.c_int]
+    L.oracle_tree_greedy.restype = ctypes.c_int
     return L
 
 
@@ -194,6 +198,28 @@ def sample(logits, dtype: str, vocab: int, temperature, uniforms, threads: int =
                              _ptr(out["flags"]), float(flag_eps), int(threads))
     if rc != 0:
         raise ValueError(f"oracle_sample status {rc}")
+    return out
+
+
+def tree_greedy(logits, dtype: str, vocab: int, counts, tokens, parents, threads: int = 0) -> dict:
+    """Greedy verification of a batch of candidate trees (nodes packed tree after tree,
+    parents tree-local and listed before their children).  Returns n_accepted [B],
+    path, emitted [n_nodes] and status [B]."""
+    z = _logits(logits, dtype)
+    counts = np.ascontiguousarray(counts, np.int32)
+    tokens = np.ascontiguousarray(tokens, np.int32)
+    parents = np.ascontiguousarray(parents, np.int32)
+    n = tokens.shape[0]
+    if parents.shape[0] != n or z.size // vocab != n:
+        raise ValueError("one token, one parent and one logit vector per node")
+    B = counts.shape[0]
+    out = dict(n_accepted=np.empty(B, np.int32), path=np.empty(n, np.int32),
+               emitted=np.empty(n, np.int32), status=np.empty(B, np.int32))
+    rc = lib().oracle_tree_greedy(_ptr(z), _DTYPES[dtype], int(vocab), B, n, _ptr(counts), _ptr(tokens),
+                                  _ptr(parents), _ptr(out["n_accepted"]), _ptr(out["path"]),
+                                  _ptr(out["emitted"]), _ptr(out["status"]), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_tree_greedy status {rc}")
     return out
 
 

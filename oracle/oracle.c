@@ -513,3 +513,131 @@ int oracle_sample(const void *logits, int dtype, int64_t V, int64_t n, const flo
     }
     return rc;
 }
+
+/* ------------------------------------------------------------------------- */
+/* greedy verification of a candidate tree                                     */
+/* ------------------------------------------------------------------------- */
+/* One forward pass scores every node of a tree of candidate continuations; node
+ * k's prediction is the argmax of the target's logits at k, and a node is kept when
+ * its parent is kept and its token equals its parent's prediction.  The root (node
+ * 0, parent -1) is the target's own token and is always kept.  The result is the
+ * longest kept path from the root (brunomaga.github.io "inference-distillation-
+ * speculative-decoding", section "Medusa", the tree-verification description), the
+ * first such path in node order when several are equally long, followed by the
+ * prediction at its last node, the target's next token.  Nodes are listed parents
+ * first (parent < node).
+ *
+ * Tree i holds nodes [off_i, off_i + count_i), off_i = sum_{j<i} count_j; parents[]
+ * are tree-local.  Outputs per tree: n_accepted[i] = path length - 1 (the kept
+ * drafts); path[off_i + d] = the tree-local node at depth d of the path, -1 after
+ * it; emitted[off_i + d] = the path's tokens after the root, then the prediction at
+ * its last node, -1 after it.  A tree whose count is below 1, whose root has a
+ * parent, or whose node k >= 1 has a parent outside [0, k) is invalid (BAD_TREE);
+ * a token outside [0, V) (BAD_TOKEN) or a node vector without a maximum (NaN, +inf,
+ * all -inf: NONFINITE) also invalidates the tree; counts that do not add up to
+ * n_nodes invalidate every tree (BAD_GAMMA).  An invalid tree gets n_accepted = -1
+ * and -1 in every slot. */
+int oracle_tree_greedy(const void *logits, int dtype, int64_t V, int32_t B, int64_t n_nodes,
+                       const int32_t *counts, const int32_t *tokens, const int32_t *parents,
+                       int32_t *n_accepted, int32_t *path, int32_t *emitted, int32_t *status_out,
+                       int nthreads)
+{
+    if (!logits || !counts || !tokens || !parents || !n_accepted || !path || !emitted || V <= 0 ||
+        B < 0 || n_nodes < 0)
+        return -1;
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_F32 && dtype != ORACLE_F64)
+        return -1;
+    int64_t *off = malloc(sizeof(int64_t) * ((size_t)B + 1));
+    if (!off)
+        return -1;
+    off[0] = 0;
+    int bad_total = 0;
+    for (int32_t i = 0; i < B; ++i) {
+        int64_t c = counts[i] > 0 ? counts[i] : 0;
+        off[i + 1] = off[i] + c;
+    }
+    if (off[B] != n_nodes)
+        bad_total = 1;
+    for (int64_t k = 0; k < n_nodes; ++k) {
+        path[k] = -1;
+        emitted[k] = -1;
+    }
+    if (bad_total) {
+        for (int32_t i = 0; i < B; ++i) {
+            n_accepted[i] = -1;
+            if (status_out)
+                status_out[i] = ORACLE_BAD_GAMMA;
+        }
+        free(off);
+        return 0;
+    }
+    int rc = 0;
+    const int nth = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel num_threads(nth)
+    {
+        int64_t cap = 0;
+        int64_t *pred = NULL, *len = NULL;
+#pragma omp for schedule(dynamic, 1)
+        for (int32_t i = 0; i < B; ++i) {
+            const int64_t o = off[i];
+            const int64_t n = off[i + 1] - o;
+            int status = 0;
+            if (counts[i] < 1 || parents[o] != -1)
+                status |= ORACLE_BAD_TREE;
+            for (int64_t k = 1; k < n; ++k)
+                if (parents[o + k] < 0 || parents[o + k] >= k)
+                    status |= ORACLE_BAD_TREE;
+            for (int64_t k = 0; k < n; ++k) {
+                if (tokens[o + k] < 0 || (int64_t)tokens[o + k] >= V)
+                    status |= ORACLE_BAD_TOKEN;
+                if (vector_nonfinite(vector_ptr(logits, dtype, o + k, V), dtype, V))
+                    status |= ORACLE_NONFINITE;
+            }
+            if (status_out)
+                status_out[i] = status;
+            n_accepted[i] = -1;
+            if (status)
+                continue;
+            if (n > cap) {
+                free(pred);
+                free(len);
+                pred = malloc(sizeof(int64_t) * (size_t)n);
+                len = malloc(sizeof(int64_t) * (size_t)n);
+                cap = n;
+                if (!pred || !len) {
+#pragma omp atomic write
+                    rc = -1;
+                    cap = 0;
+                    continue;
+                }
+            }
+            /* predictions, then kept nodes in node order: len[k] = kept path length to
+               k (0 = not kept) */
+            for (int64_t k = 0; k < n; ++k)
+                pred[k] = oracle_argmax(vector_ptr(logits, dtype, o + k, V), dtype, V);
+            len[0] = 1;
+            int64_t best = 0;
+            for (int64_t k = 1; k < n; ++k) {
+                const int64_t par = parents[o + k];
+                len[k] = (len[par] > 0 && (int64_t)tokens[o + k] == pred[par]) ? len[par] + 1 : 0;
+                if (len[k] > len[best])
+                    best = k;
+            }
+            /* the path, root first: walk up from its last node */
+            const int64_t L = len[best];
+            int64_t k = best;
+            for (int64_t d = L - 1; d >= 0; --d) {
+                path[o + d] = (int32_t)k;
+                k = parents[o + k];
+            }
+            for (int64_t d = 1; d < L; ++d)
+                emitted[o + d - 1] = tokens[o + path[o + d]];
+            emitted[o + L - 1] = (int32_t)pred[best];
+            n_accepted[i] = (int32_t)(L - 1);
+        }
+        free(pred);
+        free(len);
+    }
+    free(off);
+    return rc;
+}

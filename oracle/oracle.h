@@ -17,7 +17,8 @@ enum { ORACLE_SAMPLE = 0, ORACLE_GREEDY = 1 };
 #define ORACLE_BAD_GAMMA 8   /* gamma < 0, or sum(gamma+1) != n_target_rows        */
 #define ORACLE_ZERO_RESID 16 /* zero residual mass at a rejection (informational)  */
 #define ORACLE_BAD_TEMP 32   /* sampling row with non-finite or subnormal T         */
-#define ORACLE_INVALID_MASK (ORACLE_BAD_TOKEN | ORACLE_NONFINITE | ORACLE_BAD_GAMMA | ORACLE_BAD_TEMP)
+#define ORACLE_BAD_TREE 64   /* a tree whose parents are not listed before children */
+#define ORACLE_INVALID_MASK (ORACLE_BAD_TOKEN | ORACLE_NONFINITE | ORACLE_BAD_GAMMA | ORACLE_BAD_TEMP | ORACLE_BAD_TREE)
 
 int oracle_softmax(const void *z, int dtype, int64_t V, double T, double *p);
 int64_t oracle_argmax(const void *z, int dtype, int64_t V);
@@ -34,4 +35,8 @@ int oracle_verify(const void *target, const void *draft, int dtype, int64_t V, i
 int oracle_sample(const void *logits, int dtype, int64_t V, int64_t n, const float *temperature,
                   const float *uniforms, int32_t *tokens, int32_t *status_out, int32_t *flags,
                   double flag_eps, int nthreads);
+int oracle_tree_greedy(const void *logits, int dtype, int64_t V, int32_t B, int64_t n_nodes,
+                       const int32_t *counts, const int32_t *tokens, const int32_t *parents,
+                       int32_t *n_accepted, int32_t *path, int32_t *emitted, int32_t *status_out,
+                       int nthreads);
 #endif

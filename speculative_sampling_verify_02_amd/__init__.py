@@ -28,11 +28,13 @@ ROW_NONFINITE = 4
 ROW_BAD_GAMMA = 8
 ROW_ZERO_RESID = 16
 ROW_BAD_TEMP = 32
-ROW_INVALID = ROW_BAD_TOKEN | ROW_NONFINITE | ROW_BAD_GAMMA | ROW_BAD_TEMP
+ROW_BAD_TREE = 64
+ROW_INVALID = ROW_BAD_TOKEN | ROW_NONFINITE | ROW_BAD_GAMMA | ROW_BAD_TEMP | ROW_BAD_TREE
 
 EXPORTED = ("spec_verify", "spec_verify_workspace_bytes", "spec_verify_strerror",
             "spec_verify_set_profile_events", "spec_verify_version", "spec_sample",
-            "spec_sample_workspace_bytes")
+            "spec_sample_workspace_bytes", "spec_tree_verify_greedy",
+            "spec_tree_verify_greedy_workspace_bytes")
 
 
 class SpecVerifyError(RuntimeError):
@@ -68,6 +70,10 @@ def _load():
     L.spec_sample_workspace_bytes.restype = sz
     L.spec_sample.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp, vp, sz, vp]
     L.spec_sample.restype = ctypes.c_int
+    L.spec_tree_verify_greedy_workspace_bytes.argtypes = [i64, i64, i32]
+    L.spec_tree_verify_greedy_workspace_bytes.restype = sz
+    L.spec_tree_verify_greedy.argtypes = [vp, i32, i64, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.spec_tree_verify_greedy.restype = ctypes.c_int
     return L
 
 
@@ -88,6 +94,10 @@ def workspace_bytes(batch: int, n_target_rows: int, vocab: int, dtype: int) -> i
 
 def sample_workspace_bytes(n: int, vocab: int, dtype: int) -> int:
     return int(lib.spec_sample_workspace_bytes(n, vocab, dtype))
+
+
+def tree_workspace_bytes(n_nodes: int, vocab: int, dtype: int) -> int:
+    return int(lib.spec_tree_verify_greedy_workspace_bytes(n_nodes, vocab, dtype))
 
 
 def set_profile_events(start_event, stop_event) -> None:
@@ -271,3 +281,53 @@ def spec_sample(logits, uniforms, temperature, *, status: bool = False,
     if rc != SV_OK:
         raise SpecVerifyError(rc, strerror(rc))
     return (out, st) if status else out
+
+
+def spec_tree_verify_greedy(target_logits, node_counts, tokens, parents, *, status: bool = False,
+                            workspace: torch.Tensor | None = None, out=None):
+    """Greedy verification of packed candidate trees on the GPU.
+
+    target_logits  bf16/fp32 [n_nodes, V]: node k of tree i at row off_i + k
+    node_counts    int32 [B] device tensor (each in [1, 2048])
+    tokens         int32 [n_nodes]; parents int32 [n_nodes], tree-local, -1 for roots,
+                   parents before children
+    Returns (n_accepted [B], path [n_nodes], emitted [n_nodes]) and, with status=True,
+    also the int32 status bits per tree.  Asynchronous on torch's current stream.
+    """
+    device = target_logits.device
+    if device.type != "cuda":
+        raise ValueError("target_logits must be a GPU tensor")
+    if target_logits.dtype == torch.bfloat16:
+        dtype = SV_BF16
+    elif target_logits.dtype == torch.float32:
+        dtype = SV_F32
+    else:
+        raise ValueError(f"unsupported logits dtype {target_logits.dtype}")
+    V = int(target_logits.shape[-1])
+    n = target_logits.numel() // V if V else 0
+    for t, name in ((target_logits, "target_logits"), (node_counts, "node_counts"), (tokens, "tokens"),
+                    (parents, "parents")):
+        _check(t, name, (t.dtype,) if name == "target_logits" else (torch.int32,), device)
+    if tokens.numel() != n or parents.numel() != n:
+        raise ValueError("one token and one parent per node")
+    B = int(node_counts.numel())
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=device), torch.empty(n, dtype=torch.int32, device=device),
+               torch.empty(n, dtype=torch.int32, device=device))
+    else:
+        for t in out:
+            _check(t, "out", (torch.int32,), device)
+    n_acc, path, emitted = out
+    st = torch.empty(B, dtype=torch.int32, device=device) if status else None
+    stream = torch.cuda.current_stream(device).cuda_stream
+    need = tree_workspace_bytes(n, V, dtype)
+    if workspace is None:
+        workspace = _workspace(device, stream, need)
+    elif workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
+    rc = lib.spec_tree_verify_greedy(_ptr(target_logits), dtype, V, B, n, _ptr(node_counts), _ptr(tokens),
+                                     _ptr(parents), _ptr(n_acc), _ptr(path), _ptr(emitted), _ptr(st),
+                                     _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, strerror(rc))
+    return (n_acc, path, emitted, st) if status else (n_acc, path, emitted)

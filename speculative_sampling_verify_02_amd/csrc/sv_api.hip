@@ -186,3 +186,72 @@ extern "C" sv_status spec_sample(const void *logits, int32_t dtype, int64_t voca
     if (e == hipSuccess) e = sv::launch_draw_final(P, s, dtype, aligned);
     return e == hipSuccess ? SV_OK : SV_EHIP;
 }
+
+extern "C" size_t spec_tree_verify_greedy_workspace_bytes(int64_t n_nodes, int64_t vocab, int32_t dtype)
+{
+    if (n_nodes < 0 || n_nodes > INT32_MAX || vocab <= 0 || vocab > INT32_MAX ||
+        (dtype != SV_BF16 && dtype != SV_F32))
+        return 0;
+    return sv::make_layout((int32_t)n_nodes, n_nodes, vocab, dtype).total;
+}
+
+// Greedy tree verification: the streaming pass in greedy mode over every node's
+// vector (a call whose rows are the nodes, each without drafts), then one workgroup
+// per tree.
+extern "C" sv_status spec_tree_verify_greedy(const void *target_logits, int32_t dtype, int64_t vocab,
+                                             int32_t n_trees, int64_t n_nodes, const int32_t *node_counts,
+                                             const int32_t *tokens, const int32_t *parents,
+                                             int32_t *n_accepted, int32_t *path, int32_t *emitted,
+                                             int32_t *row_status, void *workspace, size_t workspace_bytes,
+                                             void *hip_stream)
+{
+    if (dtype != SV_BF16 && dtype != SV_F32) return SV_EDTYPE;
+    if (n_trees < 0 || n_nodes < 0 || n_nodes > INT32_MAX || vocab <= 0 || vocab > INT32_MAX) return SV_EINVAL;
+    if (n_trees == 0) return n_nodes == 0 ? SV_OK : SV_EINVAL;
+    if (!target_logits && n_nodes > 0) return SV_EINVAL;
+    if (!node_counts || !tokens || !parents || !n_accepted || !path || !emitted || !workspace) return SV_EINVAL;
+    const size_t need = spec_tree_verify_greedy_workspace_bytes(n_nodes, vocab, dtype);
+    if (workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) return SV_EWORKSPACE;
+
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const int64_t esz = dtype == SV_BF16 ? 2 : 4;
+    const bool aligned = (vocab * esz) % 16 == 0 && aligned16(target_logits);
+    const sv::Layout L = sv::make_layout((int32_t)n_nodes, n_nodes, vocab, dtype);
+    char *ws = static_cast<char *>(workspace);
+    hipError_t e = hipSuccess;
+    if (n_nodes > 0) {
+        sv::Params P{};
+        P.target = target_logits;
+        P.V = vocab;
+        P.B = (int32_t)n_nodes;
+        P.mode = SV_GREEDY;
+        P.nT = n_nodes;
+        P.nD = 0;
+        P.gamma_uniform = 0;
+        P.hdr = reinterpret_cast<sv::Header *>(ws + L.hdr);
+        P.parts = reinterpret_cast<sv::Partial *>(ws + L.parts);
+        P.zx = reinterpret_cast<float *>(ws + L.zx);
+        P.geo = sv::make_geometry((int32_t)n_nodes, n_nodes, vocab, SV_GREEDY, dtype,
+                                  sv::stats_grid_cap(dtype, aligned));
+        P.geo.inv_t = 1.0;
+        P.geo.inv_d = 0.0;
+        if (g_prof_start) e = hipEventRecord(g_prof_start, s);
+        if (e == hipSuccess) e = sv::launch_stats(P, s, dtype, aligned);
+        if (e == hipSuccess && g_prof_stop) e = hipEventRecord(g_prof_stop, s);
+    }
+    sv::TreeParams T{};
+    T.parts = reinterpret_cast<const sv::Partial *>(ws + L.parts);
+    T.ipv = sv::ceil_div(vocab, 2 * sv::item_elems(dtype));
+    T.V = vocab;
+    T.n_nodes = n_nodes;
+    T.B = n_trees;
+    T.counts = node_counts;
+    T.tokens = tokens;
+    T.parents = parents;
+    T.n_accepted = n_accepted;
+    T.path = path;
+    T.emitted = emitted;
+    T.row_status = row_status;
+    if (e == hipSuccess) e = sv::launch_tree(T, s);
+    return e == hipSuccess ? SV_OK : SV_EHIP;
+}

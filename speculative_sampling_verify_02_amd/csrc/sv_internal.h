@@ -35,7 +35,8 @@ enum : int32_t {
     ST_BAD_GAMMA = 8,
     ST_ZERO_RESID = 16,
     ST_BAD_TEMP = 32,
-    ST_INVALID = ST_BAD_TOKEN | ST_NONFINITE | ST_BAD_GAMMA | ST_BAD_TEMP,
+    ST_BAD_TREE = 64,
+    ST_INVALID = ST_BAD_TOKEN | ST_NONFINITE | ST_BAD_GAMMA | ST_BAD_TEMP | ST_BAD_TREE,
 };
 
 enum : int32_t { ROW_SAMPLE = 0, ROW_GREEDY = 1, ROW_BAD_TEMP = 2 };
@@ -181,6 +182,25 @@ struct Params {
     RowDraw *draws;
     Sum2 *tiles;
     Geometry geo;
+};
+
+// Greedy verification of candidate trees: the streaming pass has left one argmax
+// record per piece of every node's vector (nodes packed tree after tree).
+constexpr int kMaxTreeNodes = 2048;
+struct TreeParams {
+    const Partial *parts;
+    int64_t ipv;              // records per node vector
+    int64_t V;
+    int64_t n_nodes;
+    int32_t B;                // trees
+    int32_t pad;
+    const int32_t *counts;    // [B] nodes per tree
+    const int32_t *tokens;    // [n_nodes]
+    const int32_t *parents;   // [n_nodes], tree-local, -1 for the root
+    int32_t *n_accepted;      // [B]
+    int32_t *path;            // [n_nodes]
+    int32_t *emitted;         // [n_nodes]
+    int32_t *row_status;      // [B] or null
 };
 
 // ---------------------------------------------------------------------------
@@ -480,5 +500,6 @@ hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned)
 hipError_t launch_scan(const Params &P, hipStream_t s, int dtype);
 hipError_t launch_verify(const Params &P, hipStream_t s, int dtype, bool aligned);
 hipError_t launch_draw_final(const Params &P, hipStream_t s, int dtype, bool aligned);
+hipError_t launch_tree(const TreeParams &T, hipStream_t s);
 
 }  // namespace sv

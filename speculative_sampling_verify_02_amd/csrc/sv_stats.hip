@@ -49,7 +49,7 @@ __device__ __forceinline__ VecCtx vec_ctx(const Params &P, int64_t v)
         c.row = (int32_t)row;
         c.slot = (P.mode == 0 && j < g) ? (int32_t)(row * g + j) : -1;
         c.x = c.slot >= 0 ? P.tokens[c.slot] : -1;
-        c.T = P.temperature[row];
+        c.T = P.mode == 0 ? P.temperature[row] : 0.0f;   // greedy calls may pass no temperatures
     } else {
         const VecInfo vi = P.vinfo[v];
         c.row = vi.row;

@@ -719,4 +719,141 @@ def pin_sample_greedy_and_status():
     assert list(r["tokens"]) == [1, 1, 3, 3] and not r["status"].any()
 
 
+
+# --------------------------------------------------------------------------- #
+# greedy verification of a candidate tree
+# --------------------------------------------------------------------------- #
+def _tree_brute(z, counts, tokens, parents):
+    """Every node's root path by walking parents; a node is kept when every edge on
+    it has the child's token equal to numpy's first argmax at the parent; the deepest
+    kept node wins, the lowest index on ties."""
+    out_n, out_path, out_emit = [], [], []
+    o = 0
+    for c in counts:
+        pred = [int(np.argmax(z[o + k])) for k in range(c)]
+        best, best_len = 0, 1
+        for k in range(c):
+            chain = [k]
+            while parents[o + chain[-1]] >= 0:
+                chain.append(int(parents[o + chain[-1]]))
+            chain.reverse()
+            ok = all(tokens[o + chain[d]] == pred[chain[d - 1]] for d in range(1, len(chain)))
+            if ok and len(chain) > best_len:
+                best, best_len = k, len(chain)
+        chain = [best]
+        while parents[o + chain[-1]] >= 0:
+            chain.append(int(parents[o + chain[-1]]))
+        chain.reverse()
+        out_n.append(len(chain) - 1)
+        out_path.append(chain + [-1] * (c - len(chain)))
+        out_emit.append([int(tokens[o + j]) for j in chain[1:]] + [pred[best]] + [-1] * (c - len(chain)))
+        o += c
+    return np.array(out_n), np.concatenate(out_path), np.concatenate(out_emit)
+
+
+def _random_trees(rng, B, nmax, V):
+    counts = rng.integers(1, nmax + 1, B).astype(np.int32)
+    parents, tokens = [], []
+    for c in counts:
+        parents += [-1] + [int(rng.integers(0, k)) for k in range(1, c)]
+    n = int(counts.sum())
+    # small integer logits: ties everywhere, so the lowest-index rule is exercised
+    z = rng.integers(-2, 3, (n, V)).astype(np.float64)
+    o = 0
+    for c in counts:
+        for k in range(c):
+            par = parents[o + k]
+            if par < 0 or rng.random() < 0.3:
+                tokens.append(int(rng.integers(0, V)))
+            else:
+                tokens.append(int(np.argmax(z[o + par])))   # a child that will be kept
+        o += c
+    return z, counts, np.array(tokens, np.int32), np.array(parents, np.int32)
+
+
+def pin_tree_brute_force():
+    rng = np.random.default_rng(31)
+    for _ in range(30):
+        z, counts, tokens, parents = _random_trees(rng, 6, 12, 5)
+        r = oracle.tree_greedy(z, "f64", 5, counts, tokens, parents)
+        n, path, emit = _tree_brute(z, counts, tokens, parents)
+        assert not r["status"].any()
+        assert np.array_equal(r["n_accepted"], n), (r["n_accepted"], n)
+        assert np.array_equal(r["path"], path)
+        assert np.array_equal(r["emitted"], emit)
+
+
+def pin_tree_chain_is_linear_greedy():
+    """A chain (node k's parent is k - 1) is a row of drafts: the result is the linear
+    greedy verification of tokens 1 .. n-1 against the nodes' logits."""
+    rng = np.random.default_rng(32)
+    B, V = 40, 30
+    counts = rng.integers(1, 9, B).astype(np.int32)
+    n = int(counts.sum())
+    z = rng.standard_normal((n, V))
+    parents, tokens = [], []
+    o = 0
+    for c in counts:
+        am = np.argmax(z[o:o + c], axis=1)
+        for k in range(c):
+            parents.append(k - 1)
+            tokens.append(int(am[k - 1]) if k > 0 and rng.random() < 0.75 else int(rng.integers(0, V)))
+        o += c
+    tokens = np.array(tokens, np.int32)
+    r = oracle.tree_greedy(z, "f64", V, counts, tokens, parents)
+    drafts = np.concatenate([tokens[o + 1:o + c] for o, c in zip(np.cumsum(counts) - counts, counts)])
+    lin = oracle.verify(z, np.zeros((n - B, V)), "f64", V, counts - 1, drafts.astype(np.int32),
+                        np.zeros(n, np.float32), np.ones(B, np.float32), mode="greedy")
+    assert np.array_equal(r["n_accepted"], lin["n_accepted"])
+    assert np.array_equal(r["emitted"], lin["emitted"])
+    for i, (o, c) in enumerate(zip(np.cumsum(counts) - counts, counts)):
+        K = lin["n_accepted"][i]
+        assert list(r["path"][o:o + c]) == list(range(K + 1)) + [-1] * (c - K - 1)
+
+
+def pin_tree_hand_example():
+    """Root 0 with children 1 (token 3) and 2 (token 1); node 3 (token 0) under 1,
+    nodes 4 (token 2) and 5 (token 4) under 2, node 6 (token 0) under 4.  The argmax
+    is 1 at the root, 2 at node 2, 0 at node 4 and 3 at node 6, so the kept path is
+    0 -> 2 -> 4 -> 6 and the next token is 3."""
+    parents = np.array([-1, 0, 0, 1, 2, 2, 4], np.int32)
+    tokens = np.array([9, 3, 1, 0, 2, 4, 0], np.int32)
+    am = [1, 4, 2, 0, 0, 1, 3]
+    z = np.zeros((7, 10))
+    for k, a in enumerate(am):
+        z[k, a] = 5.0
+    r = oracle.tree_greedy(z, "f64", 10, [7], tokens, parents)
+    assert r["n_accepted"][0] == 3
+    assert list(r["path"]) == [0, 2, 4, 6, -1, -1, -1]
+    assert list(r["emitted"]) == [1, 2, 0, 3, -1, -1, -1]
+    # two kept paths of equal length: the one ending at the lower node index wins
+    tokens2 = np.array([9, 1, 1, 4, 4, 2, 0], np.int32)
+    am2 = [1, 4, 4, 7, 8, 1, 3]
+    z2 = np.zeros((7, 10))
+    for k, a in enumerate(am2):
+        z2[k, a] = 5.0
+    r = oracle.tree_greedy(z2, "f64", 10, [7], tokens2, parents)
+    assert r["n_accepted"][0] == 2 and list(r["path"][:3]) == [0, 1, 3]
+    assert list(r["emitted"][:3]) == [1, 4, 7]
+
+
+def pin_tree_status():
+    z = np.zeros((5, 4))
+    z[:, 1] = 1.0
+    ok = oracle.tree_greedy(z, "f64", 4, [2, 3], [0, 1, 0, 1, 1], [-1, 0, -1, 0, 1])
+    assert list(ok["n_accepted"]) == [1, 2] and not ok["status"].any()
+    r = oracle.tree_greedy(z, "f64", 4, [2, 3], [0, 1, 0, 1, 1], [-1, 0, -1, 0, 2])   # parent not earlier
+    assert r["status"][1] & oracle.BAD_TREE and r["n_accepted"][1] == -1 and r["status"][0] == 0
+    r = oracle.tree_greedy(z, "f64", 4, [2, 3], [0, 1, 0, 1, 1], [0, 0, -1, 0, 1])    # root with a parent
+    assert r["status"][0] & oracle.BAD_TREE
+    r = oracle.tree_greedy(z, "f64", 4, [2, 3], [0, 7, 0, 1, 1], [-1, 0, -1, 0, 1])   # token out of range
+    assert r["status"][0] & oracle.BAD_TOKEN and np.all(r["emitted"][:2] == -1)
+    zn = z.copy()
+    zn[3, 2] = np.nan
+    r = oracle.tree_greedy(zn, "f64", 4, [2, 3], [0, 1, 0, 1, 1], [-1, 0, -1, 0, 1])
+    assert r["status"][1] & oracle.NONFINITE and r["status"][0] == 0
+    r = oracle.tree_greedy(z, "f64", 4, [2, 2], [0, 1, 0, 1, 1], [-1, 0, -1, 0, 1])   # counts != nodes
+    assert np.all(r["status"] == oracle.BAD_GAMMA) and np.all(r["emitted"] == -1)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -115,3 +115,29 @@ def test_sample_host_argument_errors(sv):
     assert sv.sample_workspace_bytes(-1, 10, sv.SV_BF16) == 0
     assert sv.sample_workspace_bytes(4, 0, sv.SV_F32) == 0
     assert sv.sample_workspace_bytes(4, 10, 7) == 0
+
+
+def test_tree_host_argument_errors(sv):
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def call(**kw):
+        a = dict(logits=1 << 20, dtype=sv.SV_BF16, vocab=32, B=2, n=6, counts=1 << 21, tokens=1 << 22,
+                 parents=1 << 23, n_acc=1 << 24, path=1 << 25, emitted=1 << 26, status=None, ws=1 << 27,
+                 ws_bytes=1 << 30)
+        a.update(kw)
+        return sv.lib.spec_tree_verify_greedy(vp(a["logits"]), a["dtype"], a["vocab"], a["B"], a["n"],
+                                              vp(a["counts"]), vp(a["tokens"]), vp(a["parents"]),
+                                              vp(a["n_acc"]), vp(a["path"]), vp(a["emitted"]),
+                                              vp(a["status"]), vp(a["ws"]), a["ws_bytes"], None)
+    assert call(dtype=9) == sv.SV_EDTYPE
+    assert call(vocab=0) == sv.SV_EINVAL
+    assert call(B=-1) == sv.SV_EINVAL
+    assert call(n=-1) == sv.SV_EINVAL
+    assert call(B=0, n=3) == sv.SV_EINVAL
+    assert call(B=0, n=0) == sv.SV_OK
+    for k in ("logits", "counts", "tokens", "parents", "n_acc", "path", "emitted", "ws"):
+        assert call(**{k: None}) == sv.SV_EINVAL, k
+    assert call(ws_bytes=10) == sv.SV_EWORKSPACE
+    assert call(ws=(1 << 27) + 8) == sv.SV_EWORKSPACE
+    assert sv.tree_workspace_bytes(4032, 128256, sv.SV_BF16) > 0
+    assert sv.tree_workspace_bytes(-1, 10, sv.SV_BF16) == 0

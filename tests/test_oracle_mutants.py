@@ -40,6 +40,9 @@ MUTANTS = {
     "sample_first_uniform": ("tok = oracle_inverse_cdf(w, V, (double)uniforms[i], eps, NULL, &near);",
                              "tok = oracle_inverse_cdf(w, V, (double)uniforms[0], eps, NULL, &near);"),
     "sample_greedy_below_one": ("                if (T <= 0) {", "                if (T < 1) {"),
+    "tree_own_prediction": ("(int64_t)tokens[o + k] == pred[par]", "(int64_t)tokens[o + k] == pred[k]"),
+    "tree_last_longest": ("                if (len[k] > len[best])", "                if (len[k] >= len[best])"),
+    "tree_ignores_parent": ("len[k] = (len[par] > 0 && ", "len[k] = (len[par] >= 0 && "),
     "neg_inf_is_nonfinite": ("if (isnan(x) || x == INFINITY)", "if (isnan(x) || isinf(x))"),
 }
 

@@ -352,6 +352,86 @@ def sample_inputs(w: Workload, seed: int, side: str = "draft", limit: int | None
                         np.ascontiguousarray(temp, np.float32), u)
 
 
+@dataclass
+class TreeInputs:
+    """Candidate trees for greedy tree verification, packed tree after tree: node k of
+    tree i is row off_i + k of `logits`; parents are tree-local, -1 for the root,
+    listed before their children."""
+    name: str
+    dtype: str
+    vocab: int
+    counts: np.ndarray         # int32 [B]
+    tokens: np.ndarray         # int32 [n_nodes]
+    parents: np.ndarray        # int32 [n_nodes]
+    logits: np.ndarray         # uint16 bits (bf16) or float32, [n_nodes, V]
+
+    @property
+    def n_nodes(self) -> int:
+        return int(self.tokens.shape[0])
+
+
+def medusa_shape(top_k: int, heads: int):
+    """Parents and depths of a Medusa candidate tree: the root, then per level every
+    node of the previous level gets top_k children, level by level."""
+    parents, depths, level = [-1], [0], [0]
+    for d in range(1, heads + 1):
+        nxt = []
+        for par in level:
+            for _ in range(top_k):
+                nxt.append(len(parents))
+                parents.append(par)
+                depths.append(d)
+        level = nxt
+    return np.array(parents, np.int32), np.array(depths, np.int32)
+
+
+def trees(seed: int, batch: int, vocab: int, dtype: str, top_k=2, heads=5, accept: float = 0.7,
+          sigma: float = 3.0, random_shape: bool = False) -> TreeInputs:
+    """Medusa-shaped trees (or, with random_shape, random trees in parents-first
+    order) over normal logits.  Every level has top_k candidate tokens shared by all
+    its nodes, as when each level's tokens come from one head.  With probability
+    `accept` a node's logits are shaped so that their argmax is one of the next
+    level's candidates (so that child is kept), else a random token."""
+    counts, toks, pars, rows = [], [], [], []
+    tk = np.atleast_1d(np.asarray(top_k))
+    hd = np.atleast_1d(np.asarray(heads))
+    for i in range(batch):
+        rng = _rng(seed, 11, i)
+        k_i, h_i = int(tk[i % tk.size]), int(hd[i % hd.size])
+        if random_shape:
+            n = int(rng.integers(1, max(2, k_i ** h_i) + 1))
+            par = np.array([-1] + [int(rng.integers(0, j)) for j in range(1, n)], np.int32)
+            dep = np.zeros(n, np.int32)
+            for j in range(1, n):
+                dep[j] = dep[par[j]] + 1
+        else:
+            par, dep = medusa_shape(k_i, h_i)
+        n = par.shape[0]
+        dmax = int(dep.max())
+        cand = [rng.choice(vocab, size=min(k_i, vocab), replace=False) for _ in range(dmax + 2)]
+        tok = np.empty(n, np.int32)
+        tok[0] = rng.integers(0, vocab)
+        slot = np.zeros(n, np.int64)
+        for j in range(1, n):
+            c = cand[dep[j]]
+            # children of one parent take the level's candidates in order
+            sib = int(np.sum(par[:j] == par[j]))
+            slot[j] = sib % c.shape[0]
+            tok[j] = c[slot[j]]
+        z = rng.standard_normal((n, vocab)).astype(np.float32) * np.float32(sigma)
+        for j in range(n):
+            if rng.random() < accept:
+                t = int(rng.choice(cand[dep[j] + 1]))
+                z[j, t] = z[j].max() + np.float32(1.0)
+        counts.append(n)
+        toks.append(tok)
+        pars.append(par)
+        rows.append(_store(z, dtype))
+    name = f"trees_b{batch}_{'random' if random_shape else f'k{top_k}_h{heads}'}_v{vocab}_{dtype}"
+    return TreeInputs(name, dtype, vocab, np.array(counts, np.int32), np.concatenate(toks),
+                      np.concatenate(pars), np.ascontiguousarray(np.concatenate(rows)))
+
+
 CONFIGS = {
     "toy": toy,
     "c2": c2,
