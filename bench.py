@@ -46,9 +46,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c3", choices=["c2", "c3", "c4", "c5"])
     ap.add_argument("--mode", default="sample", choices=["sample", "greedy"])
-    ap.add_argument("--op", default="verify", choices=["verify", "sample", "tree"],
+    ap.add_argument("--op", default="verify", choices=["verify", "early", "sample", "tree"],
                     help="verify: the verification step (default); sample: the drafter's draw "
-                         "over the configuration's draft logit vectors; tree: greedy verification "
+                         "over the configuration's draft logit vectors; early: the verification step "
+                         "with early exit (positions left to right); tree: greedy verification "
                          "of 16 Medusa trees (top-2 candidates, 5 heads: 63 nodes) at V = 128256 bf16")
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -205,7 +206,8 @@ def bench_sample(args):
         "config": {"workload": si.name, "vectors": n, "vocab": V, "rotated_device_copies": len(copies)},
         "hbm_gbps_algorithmic": total / sec / 1e9,
         "hbm_frac_of_peak": total / sec / 1e9 / PEAK_HBM_GBPS,
-        "roofline": {"kernel": "stats_kernel", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
+        "roofline": {"kernel": "stats_list_kernel + ee_step_kernel steps" if early else "stats_kernel",
+                     "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
                      "avg_launch_ms": stats_ms, "algorithmic_bytes_per_launch": pass1,
                      "timed_steps": args.steps, "ms_per_step_with_events": ms_ev},
@@ -271,7 +273,8 @@ def bench_tree(args):
         "mean_kept_drafts": float(K[K >= 0].mean()),
         "hbm_gbps_algorithmic": total / sec / 1e9,
         "hbm_frac_of_peak": total / sec / 1e9 / PEAK_HBM_GBPS,
-        "roofline": {"kernel": "stats_kernel", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
+        "roofline": {"kernel": "stats_list_kernel + ee_step_kernel steps" if early else "stats_kernel",
+                     "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
                      "avg_launch_ms": stats_ms, "algorithmic_bytes_per_launch": pass1,
                      "timed_steps": args.steps, "ms_per_step_with_events": ms_ev},
@@ -325,18 +328,32 @@ def main():
     ws = torch.empty(sv.workspace_bytes(B, nT, V, sv.SV_BF16 if w.dtype == "bf16" else sv.SV_F32),
                      dtype=torch.uint8, device=dev)
 
+    early = args.op == "early"
+    if early:
+        ws = torch.empty(sv.early_exit_workspace_bytes(B, nT, V, sv.SV_BF16 if w.dtype == "bf16" else sv.SV_F32),
+                         dtype=torch.uint8, device=dev)
+    gmax = int(w.gamma.max())
+
     def step(k, d=None):
         d = d or copies[k % len(copies)]
         g = gamma_arg if gamma_arg is not None else d["gamma"]
+        if early:
+            return sv.spec_verify_early_exit(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temperature"],
+                                             g, gamma_max=gmax, mode=args.mode, workspace=ws,
+                                             out=outs[k % len(copies)])
         return sv.spec_verify(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temperature"], g,
                               mode=args.mode, workspace=ws, out=outs[k % len(copies)])
 
     # one checked call: accepted counts drive the algorithmic pass-2 bytes
-    n_acc, _ = step(0)
+    n_acc = step(0)[0]
     torch.cuda.synchronize()
     K = n_acc.cpu().numpy()
     gam = w.gamma
     pass1_bytes = (nT + (nD if args.mode == "sample" else 0)) * V * esz
+    if early:
+        # positions 0..K of the target, and 0..min(K, gamma-1) of the draft in sampling mode
+        pass1_bytes = int(sum((K[i] + 1 + (min(K[i], gam_i - 1) + 1 if args.mode == "sample" else 0)) * V * esz
+                              for i, gam_i in enumerate(w.gamma) if K[i] >= 0))
     pass2_bytes = 0
     if args.mode == "sample":
         # a rejection re-reads position K of both models; a bonus draw re-reads one
@@ -392,13 +409,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "gamma": int(gam.max()) if dense is None else dense,
                    "ragged": dense is None, "vocab": V, "mode": args.mode,
+                   "variant": "early exit" if early else "all positions in parallel",
                    "rotated_device_copies": len(copies)},
         "rows_per_s": B / sec_per_step,
         "hbm_gbps_algorithmic": total_bytes / sec_per_step / 1e9,
         "hbm_frac_of_peak": total_bytes / sec_per_step / 1e9 / PEAK_HBM_GBPS,
         "bytes_per_step": {"pass1_logits": pass1_bytes, "pass2_logits": pass2_bytes, "other": small_bytes},
         "mean_accepted": float(K[K >= 0].mean()) if (K >= 0).any() else None,
-        "roofline": {"kernel": "stats_kernel", "bound": "hbm", "achieved": achieved,
+        "roofline": {"kernel": "stats_list_kernel + ee_step_kernel steps" if early else "stats_kernel",
+                     "bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic, "avg_launch_ms": stats_avg_ms,
                      "algorithmic_bytes_per_launch": stats_bytes,

@@ -217,6 +217,43 @@ sv_status spec_tree_verify_greedy(const void *target_logits, int32_t dtype, int6
                                   int32_t *row_status, void *workspace, size_t workspace_bytes,
                                   void *hip_stream);
 
+/*
+ * The verification round with early exit: positions are read left to right and,
+ * for each row, nothing after its first rejection is read (rayaq.ca "Speculative
+ * decoding", section "One round", step 3, which stops at the first rejection).  One
+ * step per position: the rows still undecided read position j of both models, then
+ * decide it.  Kept drafts, drawn tokens and the residual mass are those of
+ * spec_verify on the same inputs; what differs is what a row can see: positions
+ * after its rejection are not checked for non-finite logits (a NaN there leaves the
+ * row valid) and their p(x_j), q(x_j) diagnostics are NaN.  Draft tokens are all
+ * range-checked.  Fewer logits are read (2(K_i + 1) vectors of row i after a
+ * rejection instead of 2 gamma_i + 1), at the price of gamma_max + 1 sequential steps.
+ *
+ * The cache rollback (rayaq.ca "Speculative decoding", section "Verification
+ * attention and the cache"): a round that keeps K_i drafts over a cached prefix of
+ * n_i entries keeps n_i + K_i + 1 entries (the prefix, the last token, the kept
+ * drafts) in both models' caches; crop_len[i] receives that length.
+ *
+ * Arguments as for spec_verify, plus:
+ *   gamma_max   ragged batches (gamma_per_row != NULL): a host-side bound on every
+ *               gamma_i, >= 0, the number of steps run is gamma_max + 1; a row with
+ *               gamma_i > gamma_max is invalid (SV_ROW_BAD_GAMMA).  Ignored for dense
+ *               batches (gamma_uniform is the bound).
+ *   cache_len   [batch] int32 device, or NULL for n_i = 0: cache entries before the round
+ *   crop_len    [batch] int32 device out, or NULL: n_i + K_i + 1, or -1 for an invalid row
+ *   workspace   >= spec_verify_early_exit_workspace_bytes(...) bytes, 256-byte aligned
+ */
+size_t spec_verify_early_exit_workspace_bytes(int32_t batch, int64_t n_target_rows, int64_t vocab,
+                                              int32_t dtype);
+sv_status spec_verify_early_exit(const void *target_logits, const void *draft_logits, int32_t dtype,
+                                 int64_t vocab, int32_t batch, int64_t n_target_rows,
+                                 const int32_t *draft_tokens, const float *uniforms,
+                                 const float *temperature, const int32_t *gamma_per_row,
+                                 int32_t gamma_uniform, int32_t gamma_max, int32_t mode,
+                                 const int32_t *cache_len, int32_t *n_accepted,
+                                 int32_t *emitted_tokens, int32_t *crop_len, const sv_diag *diag,
+                                 void *workspace, size_t workspace_bytes, void *hip_stream);
+
 /* Static, human-readable name of an sv_status value. */
 const char *spec_verify_strerror(int32_t status);
 

@@ -58,6 +58,10 @@ def _load(path: str):
     L.oracle_verify.argtypes = [vp, vp, ctypes.c_int, i64, i32, i64, vp, vp, vp, vp,
                                 ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, dbl, ctypes.c_int]
     L.oracle_verify.restype = ctypes.c_int
+    L.oracle_verify_ex.argtypes = [vp, vp, ctypes.c_int, i64, i32, i64, vp, vp, vp, vp,
+                                   ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, dbl, ctypes.c_int,
+                                   ctypes.c_int, vp, vp]
+    L.oracle_verify_ex.restype = ctypes.c_int
     L.oracle_sample.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, vp, dbl, ctypes.c_int]
     L.oracle_sample.restype = ctypes.c_int
     L.oracle_tree_greedy.argtypes = [vp, ctypes.c_int, i64, i32, i64, vp, vp, vp, vp, vp, vp, vp,
@@ -146,10 +150,11 @@ def inverse_cdf(w, u: float, eps: float = 1e-5):
 
 def verify(target, draft, dtype: str, vocab: int, gamma, draft_tokens, uniforms, temperature,
            mode: str = "sample", n_target_rows=None, threads: int = 0,
-           flag_eps: float = 1e-5) -> dict:
+           flag_eps: float = 1e-5, early_exit: bool = False, cache_len=None) -> dict:
     """One verification round over a packed batch; returns numpy arrays.  flag_pos[i] is
     the first decision of row i within flag_eps of its threshold (accept test j, or
-    gamma_i for the draw), -1 if none."""
+    gamma_i for the draw), -1 if none.  early_exit reads positions left to right and
+    stops at the first rejection; crop_len[i] = cache_len[i] + K_i + 1 (-1 if invalid)."""
     gamma = np.ascontiguousarray(gamma, np.int32)
     B = gamma.shape[0]
     target = _logits(target, dtype)
@@ -169,12 +174,15 @@ def verify(target, draft, dtype: str, vocab: int, gamma, draft_tokens, uniforms,
         row_status=np.empty(B, np.int32),
         flag_pos=np.empty(B, np.int32),
     )
-    rc = lib().oracle_verify(_ptr(target), _ptr(draft), _DTYPES[dtype], int(vocab), B,
-                             int(n_target_rows), _ptr(tokens), _ptr(uniforms), _ptr(temperature),
-                             _ptr(gamma), SAMPLE if mode == "sample" else GREEDY,
-                             _ptr(out["n_accepted"]), _ptr(out["emitted"]), _ptr(out["p_x"]),
-                             _ptr(out["q_x"]), _ptr(out["resid_mass"]), _ptr(out["row_status"]),
-                             _ptr(out["flag_pos"]), float(flag_eps), int(threads))
+    out["crop_len"] = np.empty(B, np.int32)
+    cl = None if cache_len is None else np.ascontiguousarray(cache_len, np.int32)
+    rc = lib().oracle_verify_ex(_ptr(target), _ptr(draft), _DTYPES[dtype], int(vocab), B,
+                                int(n_target_rows), _ptr(tokens), _ptr(uniforms), _ptr(temperature),
+                                _ptr(gamma), SAMPLE if mode == "sample" else GREEDY,
+                                _ptr(out["n_accepted"]), _ptr(out["emitted"]), _ptr(out["p_x"]),
+                                _ptr(out["q_x"]), _ptr(out["resid_mass"]), _ptr(out["row_status"]),
+                                _ptr(out["flag_pos"]), float(flag_eps), int(threads), int(bool(early_exit)),
+                                _ptr(cl), _ptr(out["crop_len"]))
     if rc != 0:
         raise ValueError(f"oracle_verify status {rc}")
     return out
@@ -223,7 +231,9 @@ def tree_greedy(logits, dtype: str, vocab: int, counts, tokens, parents, threads
     return out
 
 
-def verify_workload(w, threads: int = 0, mode: str | None = None, flag_eps: float = 1e-5) -> dict:
+def verify_workload(w, threads: int = 0, mode: str | None = None, flag_eps: float = 1e-5,
+                    early_exit: bool = False, cache_len=None) -> dict:
     """verify() on any object with the packed-workload attributes."""
     return verify(w.target, w.draft, w.dtype, w.vocab, w.gamma, w.draft_tokens, w.uniforms,
-                  w.temperature, mode=mode or w.mode, threads=threads, flag_eps=flag_eps)
+                  w.temperature, mode=mode or w.mode, threads=threads, flag_eps=flag_eps,
+                  early_exit=early_exit, cache_len=cache_len)

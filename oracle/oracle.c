@@ -219,6 +219,41 @@ int64_t oracle_inverse_cdf(const double *w, int64_t V, double u, double eps, dou
 /* ------------------------------------------------------------------------- */
 /* the verification round, one batch                                           */
 /* ------------------------------------------------------------------------- */
+/* Cache entries to keep after a round that kept K drafts over a prefix of n: the
+ * prefix, the last token and the kept drafts (rayaq.ca "Speculative decoding",
+ * section "Verification attention and the cache"). */
+static int32_t kept_cache_entries(const int32_t *cache_len, int32_t i, int K)
+{
+    const int32_t n = cache_len ? cache_len[i] : 0;
+    return n + K + 1;
+}
+
+/* The acceptance probability min(1, p(x)/q(x)) of draft token x at one position
+ * (rayaq.ca "Speculative decoding", section "One round", step 3), with p(x) and q(x)
+ * from the temperature softmax; q(x) = 0 gives 1 if p(x) > 0, else 0 (*q_zero = 1). */
+static double accept_ratio(const void *zt, const void *zd, int dtype, int64_t V, double T, int64_t x,
+                           double *px_out, double *qx_out, int *q_zero)
+{
+    double mt, St, md, Sd;
+    vector_max_sumexp(zt, dtype, V, T, &mt, &St);
+    vector_max_sumexp(zd, dtype, V, T, &md, &Sd);
+    double px = exp((logit_at(zt, dtype, x) - mt) / T) / St;
+    double qx = exp((logit_at(zd, dtype, x) - md) / T) / Sd;
+    *px_out = px;
+    *qx_out = qx;
+    *q_zero = 0;
+    double ratio;
+    if (qx > 0) {
+        ratio = px / qx;
+        if (ratio > 1.0)
+            ratio = 1.0;
+    } else {
+        ratio = px > 0 ? 1.0 : 0.0;
+        *q_zero = 1;
+    }
+    return ratio;
+}
+
 static void invalidate_row(int32_t *n_accepted, int32_t *emitted, double *p_x, double *q_x,
                            double *resid, int64_t i, int64_t t0, int64_t d0, int g)
 {
@@ -240,7 +275,24 @@ int oracle_verify(const void *target, const void *draft, int dtype, int64_t V, i
                   const float *temperature, const int32_t *gamma_per_row, int mode,
                   int32_t *n_accepted, int32_t *emitted, double *p_x, double *q_x,
                   double *resid_mass, int32_t *row_status, int32_t *flag_pos, double flag_eps,
-                  int nthreads)
+                  int nthreads);
+
+/* The round with early exit: positions are read left to right and nothing after the
+ * first rejection is read (rayaq.ca "Speculative decoding", section "One round",
+ * step 3 stops at the first rejection, and so does the verify loop of section
+ * "Implementation").  The kept drafts and the drawn token are those of the full
+ * round; what differs is only what the round can see: a position after the
+ * rejection is never checked for non-finite logits, and its p(x_j), q(x_j) are NaN.
+ * Draft tokens are still all range-checked.  crop_len[i] = n_i + K_i + 1 is the
+ * number of cache entries to keep after the round, n_i = cache_len[i] (0 when
+ * cache_len is NULL): the prefix, the last token and the kept drafts (section
+ * "Verification attention and the cache"); -1 for an invalid row. */
+int oracle_verify_ex(const void *target, const void *draft, int dtype, int64_t V, int32_t B,
+                     int64_t n_target_rows, const int32_t *draft_tokens, const float *uniforms,
+                     const float *temperature, const int32_t *gamma_per_row, int mode,
+                     int32_t *n_accepted, int32_t *emitted, double *p_x, double *q_x,
+                     double *resid_mass, int32_t *row_status, int32_t *flag_pos, double flag_eps,
+                     int nthreads, int early_exit, const int32_t *cache_len, int32_t *crop_len)
 {
     const double eps = flag_eps > 0 ? flag_eps : 1e-5;
     if (!target || !gamma_per_row || !uniforms || !temperature || !n_accepted || !emitted ||
@@ -279,6 +331,8 @@ int oracle_verify(const void *target, const void *draft, int dtype, int64_t V, i
                 flag_pos[i] = -1;
             if (resid_mass)
                 resid_mass[i] = NAN;
+            if (crop_len)
+                crop_len[i] = -1;
         }
         for (int64_t k = 0; k < n_target_rows; ++k)
             emitted[k] = -1;
@@ -325,14 +379,42 @@ int oracle_verify(const void *target, const void *draft, int dtype, int64_t V, i
                 if (x < 0 || (int64_t)x >= V)
                     status |= ORACLE_BAD_TOKEN;
             }
-            /* validity of every position the row reads */
-            for (int j = 0; j <= g && !(status & ORACLE_NONFINITE); ++j)
+            /* validity of every position the row reads: all of them, or (early exit) those
+               up to the first rejection */
+            int K_read = g;
+            if (early_exit && !(status & ORACLE_INVALID_MASK)) {
+                for (int j = 0; j < g; ++j) {
+                    const void *zt = vector_ptr(target, dtype, t0 + j, V);
+                    int reject;
+                    if (greedy) {
+                        reject = (int64_t)draft_tokens[d0 + j] != oracle_argmax(zt, dtype, V);
+                    } else {
+                        const void *zd = vector_ptr(draft, dtype, d0 + j, V);
+                        if (vector_nonfinite(zd, dtype, V)) {
+                            K_read = j; /* flagged below, at this position */
+                            break;
+                        }
+                        double px, qx;
+                        int q_zero;
+                        const double ratio = accept_ratio(zt, zd, dtype, V, T, draft_tokens[d0 + j], &px,
+                                                          &qx, &q_zero);
+                        reject = !((double)uniforms[t0 + j] < ratio);
+                    }
+                    if (vector_nonfinite(zt, dtype, V) || reject) {
+                        K_read = j;
+                        break;
+                    }
+                }
+            }
+            for (int j = 0; j <= K_read && !(status & ORACLE_NONFINITE); ++j)
                 if (vector_nonfinite(vector_ptr(target, dtype, t0 + j, V), dtype, V))
                     status |= ORACLE_NONFINITE;
             if (!greedy)
-                for (int j = 0; j < g && !(status & ORACLE_NONFINITE); ++j)
+                for (int j = 0; j < g && j <= K_read && !(status & ORACLE_NONFINITE); ++j)
                     if (vector_nonfinite(vector_ptr(draft, dtype, d0 + j, V), dtype, V))
                         status |= ORACLE_NONFINITE;
+            if (crop_len)
+                crop_len[i] = -1;
             if (status & ORACLE_INVALID_MASK) {
                 invalidate_row(n_accepted, emitted, p_x, q_x, resid_mass, i, t0, d0, g);
                 if (row_status)
@@ -359,6 +441,8 @@ int oracle_verify(const void *target, const void *draft, int dtype, int64_t V, i
                 for (int j = K + 1; j <= g; ++j)
                     emitted[t0 + j] = -1;
                 n_accepted[i] = K;
+                if (crop_len)
+                    crop_len[i] = kept_cache_entries(cache_len, i, K);
                 if (p_x)
                     for (int j = 0; j < g; ++j)
                         p_x[d0 + j] = NAN;
@@ -377,28 +461,27 @@ int oracle_verify(const void *target, const void *draft, int dtype, int64_t V, i
             /* p(x_j) and q(x_j) at every draft position */
             int K = g;
             int decided = 0;
+            if (early_exit)
+                for (int j = 0; j < g; ++j) {
+                    if (p_x)
+                        p_x[d0 + j] = NAN;
+                    if (q_x)
+                        q_x[d0 + j] = NAN;
+                }
             for (int j = 0; j < g; ++j) {
-                const void *zt = vector_ptr(target, dtype, t0 + j, V);
-                const void *zd = vector_ptr(draft, dtype, d0 + j, V);
-                const int64_t x = draft_tokens[d0 + j];
-                double mt, St, md, Sd;
-                vector_max_sumexp(zt, dtype, V, T, &mt, &St);
-                vector_max_sumexp(zd, dtype, V, T, &md, &Sd);
-                double px = exp((logit_at(zt, dtype, x) - mt) / T) / St;
-                double qx = exp((logit_at(zd, dtype, x) - md) / T) / Sd;
+                if (early_exit && decided)
+                    break;
+                double px, qx;
+                int q_zero;
+                const double ratio = accept_ratio(vector_ptr(target, dtype, t0 + j, V),
+                                                  vector_ptr(draft, dtype, d0 + j, V), dtype, V, T,
+                                                  draft_tokens[d0 + j], &px, &qx, &q_zero);
                 if (p_x)
                     p_x[d0 + j] = px;
                 if (q_x)
                     q_x[d0 + j] = qx;
-                double ratio;
-                if (qx > 0) {
-                    ratio = px / qx;
-                    if (ratio > 1.0)
-                        ratio = 1.0;
-                } else {
-                    ratio = px > 0 ? 1.0 : 0.0;
+                if (q_zero)
                     status |= ORACLE_Q_ZERO;
-                }
                 if (!decided) {
                     double u = (double)uniforms[t0 + j];
                     if (flag < 0 && fabs(u - ratio) < eps)
@@ -437,6 +520,8 @@ int oracle_verify(const void *target, const void *draft, int dtype, int64_t V, i
             for (int j = K + 1; j <= g; ++j)
                 emitted[t0 + j] = -1;
             n_accepted[i] = K;
+            if (crop_len)
+                crop_len[i] = kept_cache_entries(cache_len, i, K);
             if (resid_mass)
                 resid_mass[i] = W;
             if (row_status)
@@ -640,4 +725,16 @@ int oracle_tree_greedy(const void *logits, int dtype, int64_t V, int32_t B, int6
     }
     free(off);
     return rc;
+}
+
+int oracle_verify(const void *target, const void *draft, int dtype, int64_t V, int32_t B,
+                  int64_t n_target_rows, const int32_t *draft_tokens, const float *uniforms,
+                  const float *temperature, const int32_t *gamma_per_row, int mode,
+                  int32_t *n_accepted, int32_t *emitted, double *p_x, double *q_x,
+                  double *resid_mass, int32_t *row_status, int32_t *flag_pos, double flag_eps,
+                  int nthreads)
+{
+    return oracle_verify_ex(target, draft, dtype, V, B, n_target_rows, draft_tokens, uniforms,
+                            temperature, gamma_per_row, mode, n_accepted, emitted, p_x, q_x,
+                            resid_mass, row_status, flag_pos, flag_eps, nthreads, 0, NULL, NULL);
 }

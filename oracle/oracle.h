@@ -39,4 +39,10 @@ int oracle_tree_greedy(const void *logits, int dtype, int64_t V, int32_t B, int6
                        const int32_t *counts, const int32_t *tokens, const int32_t *parents,
                        int32_t *n_accepted, int32_t *path, int32_t *emitted, int32_t *status_out,
                        int nthreads);
+int oracle_verify_ex(const void *target, const void *draft, int dtype, int64_t V, int32_t B,
+                     int64_t n_target_rows, const int32_t *draft_tokens, const float *uniforms,
+                     const float *temperature, const int32_t *gamma_per_row, int mode,
+                     int32_t *n_accepted, int32_t *emitted, double *p_x, double *q_x,
+                     double *resid_mass, int32_t *row_status, int32_t *flag_pos, double flag_eps,
+                     int nthreads, int early_exit, const int32_t *cache_len, int32_t *crop_len);
 #endif

@@ -34,7 +34,8 @@ ROW_INVALID = ROW_BAD_TOKEN | ROW_NONFINITE | ROW_BAD_GAMMA | ROW_BAD_TEMP | ROW
 EXPORTED = ("spec_verify", "spec_verify_workspace_bytes", "spec_verify_strerror",
             "spec_verify_set_profile_events", "spec_verify_version", "spec_sample",
             "spec_sample_workspace_bytes", "spec_tree_verify_greedy",
-            "spec_tree_verify_greedy_workspace_bytes")
+            "spec_tree_verify_greedy_workspace_bytes", "spec_verify_early_exit",
+            "spec_verify_early_exit_workspace_bytes")
 
 
 class SpecVerifyError(RuntimeError):
@@ -74,6 +75,11 @@ def _load():
     L.spec_tree_verify_greedy_workspace_bytes.restype = sz
     L.spec_tree_verify_greedy.argtypes = [vp, i32, i64, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.spec_tree_verify_greedy.restype = ctypes.c_int
+    L.spec_verify_early_exit_workspace_bytes.argtypes = [i32, i64, i64, i32]
+    L.spec_verify_early_exit_workspace_bytes.restype = sz
+    L.spec_verify_early_exit.argtypes = [vp, vp, i32, i64, i32, i64, vp, vp, vp, vp, i32, i32, i32, vp, vp,
+                                         vp, vp, ctypes.POINTER(Diag), vp, sz, vp]
+    L.spec_verify_early_exit.restype = ctypes.c_int
     return L
 
 
@@ -94,6 +100,10 @@ def workspace_bytes(batch: int, n_target_rows: int, vocab: int, dtype: int) -> i
 
 def sample_workspace_bytes(n: int, vocab: int, dtype: int) -> int:
     return int(lib.spec_sample_workspace_bytes(n, vocab, dtype))
+
+
+def early_exit_workspace_bytes(batch: int, n_target_rows: int, vocab: int, dtype: int) -> int:
+    return int(lib.spec_verify_early_exit_workspace_bytes(batch, n_target_rows, vocab, dtype))
 
 
 def tree_workspace_bytes(n_nodes: int, vocab: int, dtype: int) -> int:
@@ -138,6 +148,27 @@ def _check(t, name, dtypes, device):
 def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature,
                 gamma_per_row=None, *, mode: str = "sample", diag: bool = False,
                 workspace: torch.Tensor | None = None, out=None):
+    return _verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, gamma_per_row,
+                   mode=mode, diag=diag, workspace=workspace, out=out)
+
+
+def spec_verify_early_exit(target_logits, draft_logits, draft_tokens, uniforms, temperature,
+                           gamma_per_row=None, *, gamma_max: int | None = None, cache_len=None,
+                           mode: str = "sample", diag: bool = False, workspace: torch.Tensor | None = None,
+                           out=None):
+    """spec_verify with early exit (positions read left to right, nothing after a row's
+    first rejection).  gamma_max bounds gamma_i of a ragged batch (default: read from
+    gamma_per_row, which synchronizes).  cache_len: int32 [B] device tensor of cached
+    prefix lengths (None: 0).  Returns (n_accepted, emitted, crop_len) and, with
+    diag=True, the diagnostics dict; crop_len[i] = cache_len[i] + n_accepted[i] + 1."""
+    return _verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, gamma_per_row,
+                   mode=mode, diag=diag, workspace=workspace, out=out, early_exit=True,
+                   gamma_max=gamma_max, cache_len=cache_len)
+
+
+def _verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, gamma_per_row=None, *,
+            mode="sample", diag=False, workspace=None, out=None, early_exit=False, gamma_max=None,
+            cache_len=None):
     """Verify a batch of drafted rows on the GPU.
 
     target_logits  bf16/fp32 [n_target_rows, V] (packed) or [B, gamma+1, V] (dense)
@@ -216,22 +247,37 @@ def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature
                  dg["row_status"].data_ptr())
 
     stream = torch.cuda.current_stream(device).cuda_stream
-    need = workspace_bytes(B, n_target_rows, V, dtype)
+    need = (early_exit_workspace_bytes if early_exit else workspace_bytes)(B, n_target_rows, V, dtype)
     if workspace is None:
         workspace = _workspace(device, stream, need)
     elif workspace.numel() < need:
         raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
+    md = SV_SAMPLE if mode == "sample" else SV_GREEDY
+    dptr = ctypes.byref(d) if d is not None else None
 
-    rc = lib.spec_verify(_ptr(target_logits), _ptr(draft_logits), dtype, V, B, n_target_rows,
-                         _ptr(draft_tokens), _ptr(uniforms), _ptr(temperature), _ptr(gamma_t),
-                         gamma_uniform, SV_SAMPLE if mode == "sample" else SV_GREEDY,
-                         _ptr(n_acc), _ptr(emitted), ctypes.byref(d) if d is not None else None,
-                         _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
+    if not early_exit:
+        rc = lib.spec_verify(_ptr(target_logits), _ptr(draft_logits), dtype, V, B, n_target_rows,
+                             _ptr(draft_tokens), _ptr(uniforms), _ptr(temperature), _ptr(gamma_t),
+                             gamma_uniform, md, _ptr(n_acc), _ptr(emitted), dptr,
+                             _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
+        if rc != SV_OK:
+            raise SpecVerifyError(rc, strerror(rc))
+        return (n_acc, emitted, dg) if diag else (n_acc, emitted)
+
+    _check(cache_len, "cache_len", (torch.int32,), device)
+    if cache_len is not None and cache_len.numel() != B:
+        raise ValueError("cache_len must have one entry per row")
+    if gamma_t is not None and gamma_max is None:
+        gamma_max = int(gamma_t.max().item()) if B else 0
+    crop = torch.empty(B, dtype=torch.int32, device=device)
+    rc = lib.spec_verify_early_exit(_ptr(target_logits), _ptr(draft_logits), dtype, V, B, n_target_rows,
+                                    _ptr(draft_tokens), _ptr(uniforms), _ptr(temperature), _ptr(gamma_t),
+                                    gamma_uniform, int(gamma_max or 0), md, _ptr(cache_len), _ptr(n_acc),
+                                    _ptr(emitted), _ptr(crop), dptr, _ptr(workspace), workspace.numel(),
+                                    ctypes.c_void_p(stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, strerror(rc))
-    if diag:
-        return n_acc, emitted, dg
-    return n_acc, emitted
+    return (n_acc, emitted, crop, dg) if diag else (n_acc, emitted, crop)
 
 
 def spec_sample(logits, uniforms, temperature, *, status: bool = False,
@@ -331,3 +377,6 @@ def spec_tree_verify_greedy(target_logits, node_counts, tokens, parents, *, stat
     if rc != SV_OK:
         raise SpecVerifyError(rc, strerror(rc))
     return (n_acc, path, emitted, st) if status else (n_acc, path, emitted)
+
+
+spec_verify.__doc__ = _verify.__doc__

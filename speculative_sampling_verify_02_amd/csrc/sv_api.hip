@@ -255,3 +255,109 @@ extern "C" sv_status spec_tree_verify_greedy(const void *target_logits, int32_t 
     if (e == hipSuccess) e = sv::launch_tree(T, s);
     return e == hipSuccess ? SV_OK : SV_EHIP;
 }
+
+extern "C" size_t spec_verify_early_exit_workspace_bytes(int32_t batch, int64_t n_target_rows, int64_t vocab,
+                                                         int32_t dtype)
+{
+    const size_t base = spec_verify_workspace_bytes(batch, n_target_rows, vocab, dtype);
+    return base == 0 ? 0 : base + sv::early_exit_extra_bytes(batch);
+}
+
+// The round with early exit: step j reads position j of the rows still undecided
+// (a listed-vector streaming kernel), then decides it (one wave per listed row);
+// the draws follow as in spec_verify.
+extern "C" sv_status spec_verify_early_exit(const void *target_logits, const void *draft_logits, int32_t dtype,
+                                            int64_t vocab, int32_t batch, int64_t n_target_rows,
+                                            const int32_t *draft_tokens, const float *uniforms,
+                                            const float *temperature, const int32_t *gamma_per_row,
+                                            int32_t gamma_uniform, int32_t gamma_max, int32_t mode,
+                                            const int32_t *cache_len, int32_t *n_accepted,
+                                            int32_t *emitted_tokens, int32_t *crop_len, const sv_diag *diag,
+                                            void *workspace, size_t workspace_bytes, void *hip_stream)
+{
+    if (dtype != SV_BF16 && dtype != SV_F32) return SV_EDTYPE;
+    if (mode != SV_SAMPLE && mode != SV_GREEDY) return SV_EINVAL;
+    if (batch < 0 || vocab <= 0 || vocab > INT32_MAX || n_target_rows < batch) return SV_EINVAL;
+    if (2 * n_target_rows - batch > INT32_MAX) return SV_EINVAL;
+    if (gamma_per_row == nullptr) {
+        if (gamma_uniform < 0) return SV_EINVAL;
+        if (n_target_rows != (int64_t)batch * ((int64_t)gamma_uniform + 1)) return SV_EINVAL;
+        gamma_max = gamma_uniform;
+    } else if (gamma_max < 0) {
+        return SV_EINVAL;
+    }
+    if (batch == 0) return n_target_rows == 0 ? SV_OK : SV_EINVAL;
+    const int64_t n_draft_rows = n_target_rows - batch;
+    if (!target_logits || !uniforms || !temperature || !n_accepted || !emitted_tokens || !workspace)
+        return SV_EINVAL;
+    if (n_draft_rows > 0 && (!draft_tokens || (mode == SV_SAMPLE && !draft_logits))) return SV_EINVAL;
+    const size_t need = spec_verify_early_exit_workspace_bytes(batch, n_target_rows, vocab, dtype);
+    if (workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) return SV_EWORKSPACE;
+
+    const int64_t esz = dtype == SV_BF16 ? 2 : 4;
+    const bool aligned = (vocab * esz) % 16 == 0 && aligned16(target_logits) &&
+                         (n_draft_rows == 0 || draft_logits == nullptr || aligned16(draft_logits));
+    const sv::Layout L = sv::make_layout(batch, n_target_rows, vocab, dtype);
+    char *ws = static_cast<char *>(workspace);
+    sv::Params P{};
+    P.target = target_logits;
+    P.draft = draft_logits;
+    P.V = vocab;
+    P.B = batch;
+    P.mode = mode;
+    P.nT = n_target_rows;
+    P.nD = n_draft_rows;
+    P.tokens = draft_tokens;
+    P.uniforms = uniforms;
+    P.temperature = temperature;
+    P.gamma = gamma_per_row;
+    P.gamma_uniform = gamma_per_row ? 0 : gamma_uniform;
+    P.n_accepted = n_accepted;
+    P.emitted = emitted_tokens;
+    if (diag) {
+        P.p_x = diag->p_x;
+        P.q_x = diag->q_x;
+        P.resid = diag->resid_mass;
+        P.row_status = diag->row_status;
+    }
+    P.hdr = reinterpret_cast<sv::Header *>(ws + L.hdr);
+    P.rows = reinterpret_cast<sv::RowInfo *>(ws + L.rows);
+    P.vinfo = reinterpret_cast<sv::VecInfo *>(ws + L.vinfo);
+    P.parts = reinterpret_cast<sv::Partial *>(ws + L.parts);
+    P.zx = reinterpret_cast<float *>(ws + L.zx);
+    P.draws = reinterpret_cast<sv::RowDraw *>(ws + L.draws);
+    P.tiles = reinterpret_cast<sv::Sum2 *>(ws + L.tiles);
+    P.geo = sv::make_geometry(batch, n_target_rows, vocab, mode, dtype, sv::stats_grid_cap(dtype, aligned));
+    if (!gamma_per_row) {
+        P.geo.inv_t = 1.0 / ((double)gamma_uniform + 1.0);
+        P.geo.inv_d = gamma_uniform > 0 ? 1.0 / (double)gamma_uniform : 0.0;
+    }
+    char *ex = ws + L.total;
+    const size_t rows_b = sv::align256(sizeof(int32_t) * 2 * (size_t)batch);
+    const size_t vecs_b = sv::align256(sizeof(int32_t) * 4 * (size_t)batch);
+    const size_t cnt_b = sv::align256(sizeof(int32_t) * 4);
+    P.ee_rows[0] = reinterpret_cast<int32_t *>(ex);
+    P.ee_rows[1] = P.ee_rows[0] + batch;
+    P.ee_vecs[0] = reinterpret_cast<int32_t *>(ex + rows_b);
+    P.ee_vecs[1] = P.ee_vecs[0] + 2 * (size_t)batch;
+    P.ee_count = reinterpret_cast<int32_t *>(ex + rows_b + vecs_b);
+    P.ee_status = reinterpret_cast<int32_t *>(ex + rows_b + vecs_b + cnt_b);
+    P.cache_len = cache_len;
+    P.crop_len = crop_len;
+    P.gamma_max = gamma_max;
+
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = hipSuccess;
+    if (gamma_per_row) e = sv::launch_prepare(P, s);
+    if (e == hipSuccess) e = sv::launch_ee_init(P, s);
+    if (e == hipSuccess && g_prof_start) e = hipEventRecord(g_prof_start, s);
+    for (int32_t j = 0; j <= gamma_max && e == hipSuccess; ++j) {
+        P.step = j;
+        e = sv::launch_stats_list(P, s, dtype, aligned);
+        if (e == hipSuccess) e = sv::launch_ee_step(P, s, dtype);
+    }
+    if (e == hipSuccess && g_prof_stop) e = hipEventRecord(g_prof_stop, s);
+    if (e == hipSuccess && mode == SV_SAMPLE) e = sv::launch_verify(P, s, dtype, aligned);
+    if (e == hipSuccess && mode == SV_SAMPLE) e = sv::launch_draw_final(P, s, dtype, aligned);
+    return e == hipSuccess ? SV_OK : SV_EHIP;
+}

@@ -182,7 +182,24 @@ struct Params {
     RowDraw *draws;
     Sum2 *tiles;
     Geometry geo;
+    // early exit (positions read left to right): the rows still undecided at the
+    // current step and the vectors they read there, double-buffered by step parity
+    int32_t *ee_rows[2];      // [B] row ids
+    int32_t *ee_vecs[2];      // [2 B] per listed row: its target vector, its draft vector or -1
+    int32_t *ee_count;        // [4]: rows listed in buffer 0, (unused), rows in buffer 1, (unused)
+    int32_t *ee_status;       // [B] status bits gathered so far
+    const int32_t *cache_len; // [B] or null: cache entries before the round
+    int32_t *crop_len;        // [B] or null: cache entries to keep after it
+    int32_t step;             // position being decided
+    int32_t gamma_max;        // bound on gamma_i given by the caller
 };
+
+// Early-exit scratch after the verification workspace.
+inline size_t early_exit_extra_bytes(int32_t B)
+{
+    return align256(sizeof(int32_t) * 2 * (size_t)B) + align256(sizeof(int32_t) * 4 * (size_t)B) +
+           align256(sizeof(int32_t) * 4) + align256(sizeof(int32_t) * (size_t)B);
+}
 
 // Greedy verification of candidate trees: the streaming pass has left one argmax
 // record per piece of every node's vector (nodes packed tree after tree).
@@ -501,5 +518,8 @@ hipError_t launch_scan(const Params &P, hipStream_t s, int dtype);
 hipError_t launch_verify(const Params &P, hipStream_t s, int dtype, bool aligned);
 hipError_t launch_draw_final(const Params &P, hipStream_t s, int dtype, bool aligned);
 hipError_t launch_tree(const TreeParams &T, hipStream_t s);
+hipError_t launch_stats_list(const Params &P, hipStream_t s, int dtype, bool aligned);
+hipError_t launch_ee_init(const Params &P, hipStream_t s);
+hipError_t launch_ee_step(const Params &P, hipStream_t s, int dtype);
 
 }  // namespace sv

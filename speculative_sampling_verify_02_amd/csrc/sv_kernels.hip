@@ -392,6 +392,190 @@ __device__ void invalidate_call(const Params &P, int32_t row, bool row_writer)
 }
 
 // ===========================================================================
+// early exit: the positions of each row one at a time, left to right
+// ===========================================================================
+// The first list: every row, with its position-0 vectors; every output slot
+// starts invalid (-1, NaN) and is filled as the steps decide.
+__global__ __launch_bounds__(kBlock) void ee_init_kernel(Params P)
+{
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    if (gid == 0) {
+        P.ee_count[0] = 0;
+        P.ee_count[2] = 0;
+    }
+    const bool bad_call = P.gamma != nullptr && P.hdr->status != 0;
+    if (bad_call) {
+        for (int64_t s = gid; s < P.nT; s += nth) P.emitted[s] = -1;
+        for (int64_t s = gid; s < P.nD; s += nth) {
+            if (P.p_x) P.p_x[s] = kQNaN;
+            if (P.q_x) P.q_x[s] = kQNaN;
+        }
+    }
+    for (int64_t i = gid; i < P.B; i += nth) {
+        P.draws[i].kind = DRAW_NONE;
+        if (bad_call) {
+            P.n_accepted[i] = -1;
+            if (P.row_status) P.row_status[i] = ST_BAD_GAMMA;
+            if (P.resid) P.resid[i] = kQNaN;
+            if (P.crop_len) P.crop_len[i] = -1;
+            continue;
+        }
+        const RowGeom G = row_geom(P, (int32_t)i);
+        const int32_t g = G.gamma;
+        P.ee_status[i] = g > P.gamma_max ? ST_BAD_GAMMA : 0;
+        P.ee_rows[0][i] = (int32_t)i;
+        P.ee_vecs[0][2 * i] = (int32_t)G.t_off;
+        P.ee_vecs[0][2 * i + 1] = (P.mode == 0 && g > 0) ? (int32_t)(P.nT + G.d_off) : -1;
+        for (int32_t k = 0; k <= g; ++k) P.emitted[G.t_off + k] = -1;
+        for (int32_t k = 0; k < g; ++k) {
+            if (P.p_x) P.p_x[G.d_off + k] = kQNaN;
+            if (P.q_x) P.q_x[G.d_off + k] = kQNaN;
+        }
+        if (P.resid) P.resid[i] = kQNaN;
+    }
+    if (gid == 0 && !bad_call) P.ee_count[0] = P.B;
+}
+
+// One wave per listed row decides position P.step from the records of the vectors
+// just read: the accept test of draft j (or its argmax match), else the bonus at
+// j = gamma.  A row that is kept going is listed for the next position.
+template <int DT>
+__global__ __launch_bounds__(64) void ee_step_kernel(Params P)
+{
+    const int lane = threadIdx.x;
+    const int buf = P.step & 1;
+    if (P.gamma != nullptr && P.hdr->status != 0) return;
+    const int32_t slot = (int32_t)blockIdx.x;
+    if (slot >= P.ee_count[2 * buf]) return;
+    const int32_t row = P.ee_rows[buf][slot];
+    const RowGeom G = row_geom(P, row);
+    const int32_t g = G.gamma, j = P.step;
+    const float T = P.temperature[row];
+    const int32_t rm = row_mode(P.mode, T);
+    const bool greedy = rm == ROW_GREEDY;
+    int status = P.ee_status[row];
+    // this position's inputs and records, all loads first
+    int32_t x = -1;
+    float u = 0.0f, zt = 0.0f, zd = 0.0f;
+    if (j < g) {
+        x = P.tokens[G.d_off + j];
+        u = P.uniforms[G.t_off + j];
+        if (!greedy) {
+            zt = P.zx[G.d_off + j];
+            zd = P.zx[P.nD + G.d_off + j];
+        }
+    }
+    const float u_draw = P.uniforms[G.t_off + g];
+    int64_t ti0, ti1, di0 = 0, di1 = -1;
+    vec_records(P, G.t_off + j, ti0, ti1);
+    if (!greedy && j < g) vec_records(P, P.nT + G.d_off + j, di0, di1);
+    const Partial none{-INFINITY, INT32_MAX, 0.0};
+    const Partial qt = ti0 + lane <= ti1 ? P.parts[ti0 + lane] : none;
+    const Partial qd = di0 + lane <= di1 ? P.parts[di0 + lane] : none;
+    if (j == 0) {
+        if (rm == ROW_BAD_TEMP) status |= ST_BAD_TEMP;
+        int bad = 0;
+        for (int32_t k = lane; k < g; k += 64) {
+            const int32_t xk = P.tokens[G.d_off + k];
+            if (xk < 0 || (int64_t)xk >= P.V) bad = 1;
+        }
+        if (wave_or_int(bad)) status |= ST_BAD_TOKEN;
+    }
+    const TempConst tc = temp_const<DT>(rm == ROW_SAMPLE ? T : 1.0f);
+    float mt = -INFINITY, md = -INFINITY;
+    double St = 0.0, Sd = 0.0;
+    int32_t at = INT32_MAX, unused;
+    if (!(status & ST_INVALID)) {
+        wave_merge<DT>(P, qt, ti0, ti1, greedy, tc, lane, mt, St, at);
+        if (greedy ? !(mt > -INFINITY && mt < INFINITY) : !(St > 0.0 && St < INFINITY)) status |= ST_NONFINITE;
+        if (!greedy && j < g) {
+            wave_merge<DT>(P, qd, di0, di1, false, tc, lane, md, Sd, unused);
+            if (!(Sd > 0.0 && Sd < INFINITY)) status |= ST_NONFINITE;
+        }
+    }
+    const int64_t n_cache = P.cache_len ? P.cache_len[row] : 0;
+    if (status & ST_INVALID) {
+        for (int32_t k = lane; k <= g; k += 64) P.emitted[G.t_off + k] = -1;
+        for (int32_t k = lane; k < g; k += 64) {
+            if (P.p_x) P.p_x[G.d_off + k] = kQNaN;
+            if (P.q_x) P.q_x[G.d_off + k] = kQNaN;
+        }
+        if (lane == 0) {
+            P.n_accepted[row] = -1;
+            if (P.row_status) P.row_status[row] = status;
+            if (P.resid) P.resid[row] = kQNaN;
+            if (P.crop_len) P.crop_len[row] = -1;
+        }
+        return;
+    }
+    int32_t K = -1;
+    RowDraw D{};
+    D.kind = DRAW_NONE;
+    if (greedy) {
+        if (j < g && x == at) {
+            if (lane == 0) P.emitted[G.t_off + j] = x;
+        } else {
+            K = j;
+            if (lane == 0) P.emitted[G.t_off + j] = at;
+        }
+    } else if (j < g) {
+        double px = kQNaN, qx = kQNaN, ratio = 0.0;
+        px = exp2_f64(((double)zt - (double)mt) * tc.c_eff) / St;
+        qx = exp2_f64(((double)zd - (double)md) * tc.c_eff) / Sd;
+        if (qx > 0.0) {
+            ratio = px / qx;
+            if (ratio > 1.0) ratio = 1.0;
+        } else {
+            ratio = px > 0.0 ? 1.0 : 0.0;
+            status |= ST_Q_ZERO;
+        }
+        if (lane == 0) {
+            if (P.p_x) P.p_x[G.d_off + j] = px;
+            if (P.q_x) P.q_x[G.d_off + j] = qx;
+        }
+        if (!((double)u < ratio)) {
+            K = j;
+            D.kind = DRAW_RESIDUAL;
+        } else if (lane == 0) {
+            P.emitted[G.t_off + j] = x;
+        }
+    } else {
+        K = g;
+        D.kind = DRAW_BONUS;
+    }
+    if (K >= 0) {
+        if (D.kind != DRAW_NONE) {
+            D.K = K;
+            D.t_row = (int32_t)(G.t_off + K);
+            D.d_row = (int32_t)(G.d_off + K);
+            D.u = u_draw;
+            D.t_slot = (int32_t)(G.t_off + K);
+            D.m_t = mt;
+            D.S_t = St;
+            D.m_d = md;
+            D.S_d = Sd;
+            D.T = T;
+        }
+        if (lane == 0) {
+            P.n_accepted[row] = K;
+            if (P.row_status) P.row_status[row] = status;
+            if (P.crop_len) P.crop_len[row] = (int32_t)(n_cache + K + 1);
+            P.draws[row] = D;
+        }
+        return;
+    }
+    // kept: listed for the next position
+    if (lane == 0) {
+        P.ee_status[row] = status;
+        const int32_t s2 = atomicAdd(&P.ee_count[2 * (buf ^ 1)], 1);
+        P.ee_rows[buf ^ 1][s2] = row;
+        P.ee_vecs[buf ^ 1][2 * s2] = (int32_t)(G.t_off + j + 1);
+        P.ee_vecs[buf ^ 1][2 * s2 + 1] = (!greedy && j + 1 < g) ? (int32_t)(P.nT + G.d_off + j + 1) : -1;
+    }
+}
+
+// ===========================================================================
 // draw: per-tile weight sums, then the inverse CDF
 // ===========================================================================
 // A unit past the end of a vector, read as -inf logits.
@@ -926,6 +1110,20 @@ hipError_t launch_verify(const Params &P, hipStream_t s, int dtype, bool aligned
         ? (aligned ? (const void *)verify_kernel<true> : (const void *)verify_kernel<false>)
         : (aligned ? (const void *)verify_kernel_f32<true> : (const void *)verify_kernel_f32<false>);
     return launch(fn, (int64_t)P.B * P.geo.ndraw, kBlock, P, s);
+}
+
+hipError_t launch_ee_init(const Params &P, hipStream_t s)
+{
+    int64_t blocks = ((int64_t)P.B + kBlock - 1) / kBlock;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 1024) blocks = 1024;
+    return launch((const void *)ee_init_kernel, blocks, kBlock, P, s);
+}
+
+hipError_t launch_ee_step(const Params &P, hipStream_t s, int dtype)
+{
+    const void *fn = dtype == 0 ? (const void *)ee_step_kernel<0> : (const void *)ee_step_kernel<1>;
+    return launch(fn, P.B, 64, P, s);
 }
 
 hipError_t launch_draw_final(const Params &P, hipStream_t s, int dtype, bool aligned)

@@ -567,6 +567,40 @@ __device__ __forceinline__ void stats_body(const Params &P)
     }
 }
 
+// One piece of a listed vector per wave: the early-exit steps read only the vectors
+// of the rows still undecided at the current position (two list slots per row).
+// Workgroup b takes piece b mod ipv of list slot b / ipv; slots past the list's
+// length, and holes (-1), do nothing.  Thread 0 of workgroup 0 also clears the other
+// list buffer's counts, which the step kernel after this one fills.
+template <int DT, bool AL>
+__global__ __launch_bounds__(64) void stats_list_kernel(Params P)
+{
+    const int lane = threadIdx.x;
+    const int buf = P.step & 1;
+    if (blockIdx.x == 0 && lane == 0) {
+        P.ee_count[2 * (buf ^ 1)] = 0;
+        P.ee_count[2 * (buf ^ 1) + 1] = 0;
+    }
+    if (P.gamma != nullptr && P.hdr->status != 0) return;
+    const int64_t ipv = P.geo.ipv;
+    const int64_t slot = (int64_t)blockIdx.x / ipv;
+    const int64_t j = (int64_t)blockIdx.x - slot * ipv;
+    if (slot >= 2 * (int64_t)P.ee_count[2 * buf]) return;
+    const int64_t v = P.ee_vecs[buf][slot];
+    if (v < 0) return;
+    ItemRaw ra, rb;
+    half_begin<DT, AL>(P, v, j, 0, true, ra, lane);
+    half_begin<DT, AL>(P, v, j, 1, true, rb, lane);
+    const VecCtx vc = vec_ctx(P, v);
+    const int32_t rm = row_mode(P.mode, vc.T);
+    const TempConst tc = rm == ROW_SAMPLE ? temp_const<DT>(vc.T) : TempConst{};
+    PieceAcc<DT> acc;
+    piece_half<DT, AL>(P, vc, rm, tc, j, 0, half_len(P, j, 0), ra, acc, lane);
+    const int n1 = half_len(P, j, 1);
+    if (n1 > 0) piece_half<DT, AL>(P, vc, rm, tc, j, 1, n1, rb, acc, lane);
+    piece_finish<DT>(P, vc, rm, tc, v, j, acc);
+}
+
 // 16-byte aligned rows (the usual case): one workgroup of 12 waves per CU, 3 per SIMD
 template <int DT>
 __global__ __launch_bounds__(kStatsBlock) void stats_kernel(Params P)
@@ -620,6 +654,14 @@ int32_t stats_grid_cap(int dtype, bool aligned)
     if (cap > kMaxStatsGrid) cap = kMaxStatsGrid;
     if (dev < kMaxDev) cache[dev][var] = (int32_t)cap;
     return (int32_t)cap;
+}
+
+hipError_t launch_stats_list(const Params &P, hipStream_t s, int dtype, bool aligned)
+{
+    const void *fn = dtype == 0
+        ? (aligned ? (const void *)stats_list_kernel<0, true> : (const void *)stats_list_kernel<0, false>)
+        : (aligned ? (const void *)stats_list_kernel<1, true> : (const void *)stats_list_kernel<1, false>);
+    return launch(fn, 2 * (int64_t)P.B * P.geo.ipv, 64, P, s);
 }
 
 hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned)

@@ -70,14 +70,14 @@ def markov_drafts(rng, ctx, gamma):
     return out
 
 
-def markov_verify(ctx, drafts, uniforms):
+def markov_verify(ctx, drafts, uniforms, **kw):
     """Run the oracle on rounds from contexts ctx with the given drafts and uniforms."""
     N, g = drafts.shape
     seq = np.concatenate([np.asarray(ctx)[:, None], drafts], axis=1)  # context of each position
     target = LOGP[seq].reshape(-1, 3)
     draft = LOGQ[seq[:, :g]].reshape(-1, 3)
     return oracle.verify(target, draft, "f64", 3, np.full(N, g, np.int32), drafts.reshape(-1),
-                         np.asarray(uniforms, np.float32).reshape(-1), np.ones(N, np.float32))
+                         np.asarray(uniforms, np.float32).reshape(-1), np.ones(N, np.float32), **kw)
 
 
 def markov_round(rng, ctx, gamma):
@@ -854,6 +854,95 @@ def pin_tree_status():
     assert r["status"][1] & oracle.NONFINITE and r["status"][0] == 0
     r = oracle.tree_greedy(z, "f64", 4, [2, 2], [0, 1, 0, 1, 1], [-1, 0, -1, 0, 1])   # counts != nodes
     assert np.all(r["status"] == oracle.BAD_GAMMA) and np.all(r["emitted"] == -1)
+
+
+
+# --------------------------------------------------------------------------- #
+# early exit and the cache entries to keep
+# --------------------------------------------------------------------------- #
+def pin_early_exit_page_round():
+    """The page's round with a rejection, read left to right: the same decisions and
+    page values, nothing computed after the rejection, and n + K + 1 = n + 2 cache
+    entries kept."""
+    spec = ROUNDS["reject_round"]
+    drafts = np.array([[TOK[t] for t in spec["drafts"]]], np.int32)
+    u = np.array([[spec["positions"][0]["u"], spec["positions"][1]["u"], 0.5, 0.3]])
+    r = markov_verify([TOK["a"]], drafts, u, early_exit=True, cache_len=[7])
+    assert r["n_accepted"][0] == spec["n_accepted"] == 1
+    assert [t for t in r["emitted"] if t >= 0] == [TOK[t] for t in spec["emitted"]]
+    _close(r["p_x"][1] / r["q_x"][1], 5 / 7, 1e-15, "ratio 5/7")
+    assert np.isnan(r["p_x"][2]) and np.isnan(r["q_x"][2])
+    assert r["crop_len"][0] == 7 + 1 + 1
+    full = markov_verify([TOK["a"]], drafts, u, cache_len=[7])
+    assert not np.isnan(full["p_x"][2])
+    assert full["crop_len"][0] == 9
+
+
+def pin_early_exit_matches_full_round():
+    """On finite logits the early-exit round keeps the same drafts, draws the same
+    token with the same mass, and agrees on p(x_j), q(x_j) up to the rejection."""
+    rng = np.random.default_rng(41)
+    B, V = 60, 50
+    gam = rng.integers(0, 7, B).astype(np.int32)
+    nT = int(gam.sum() + B)
+    zt = rng.standard_normal((nT, V)) * 2
+    zd = np.concatenate([zt[o:o + g] for o, g in zip(np.cumsum(gam + 1) - gam - 1, gam)]) + \
+        rng.standard_normal((int(gam.sum()), V)) * 0.7
+    x = rng.integers(0, V, int(gam.sum())).astype(np.int32)
+    u = snapped(rng, nT)
+    T = (0.5 + rng.random(B)).astype(np.float32)
+    n = rng.integers(0, 1000, B).astype(np.int32)
+    a = oracle.verify(zt, zd, "f64", V, gam, x, u, T, cache_len=n)
+    b = oracle.verify(zt, zd, "f64", V, gam, x, u, T, early_exit=True, cache_len=n)
+    for k in ("n_accepted", "emitted", "row_status", "flag_pos", "resid_mass", "crop_len"):
+        assert np.array_equal(a[k], b[k]), k
+    assert np.array_equal(b["crop_len"], n + a["n_accepted"] + 1)
+    d0 = np.cumsum(gam) - gam
+    for i in range(B):
+        K = a["n_accepted"][i]
+        for j in range(gam[i]):
+            if j <= K:
+                assert b["p_x"][d0[i] + j] == a["p_x"][d0[i] + j]
+            else:
+                assert np.isnan(b["p_x"][d0[i] + j]) and np.isnan(b["q_x"][d0[i] + j])
+
+
+def pin_early_exit_reads_only_up_to_the_rejection():
+    """A NaN logit after the first rejection leaves the early-exit row valid (the full
+    round flags it); one at or before the rejection invalidates both; greedy rows
+    likewise; a bad token anywhere invalidates both."""
+    V, g = 6, 4
+    zt = np.zeros((g + 1, V))
+    zt[:, 2] = 3.0
+    zd = np.zeros((g, V))
+    zd[:, 2] = 3.0
+    zd[1, 2] = -3.0               # position 1: q(2) small, p(2) large: kept
+    x = np.array([2, 2, 4, 2], np.int32)   # position 2: token 4 with p < q: rejected at u = 0.99
+    u = np.array([0.5, 0.5, 0.99, 0.5, 0.5], np.float32)
+    run = lambda zt_, zd_, xx=x, **kw: oracle.verify(zt_, zd_, "f64", V, [g], xx, u, [1.0], **kw)
+    zd4 = zd.copy()
+    zd4[2, 4] = 4.0
+    assert run(zt, zd4)["n_accepted"][0] == 2
+    for early, ok in ((True, True), (False, False)):
+        zt_nan = zt.copy()
+        zt_nan[3, 0] = np.nan
+        r = run(zt_nan, zd4, early_exit=early)
+        assert (r["row_status"][0] == 0) == ok and (r["n_accepted"][0] == 2) == ok
+        zd_nan = zd4.copy()
+        zd_nan[3, 1] = np.nan
+        assert (run(zt, zd_nan, early_exit=early)["row_status"][0] == 0) == ok
+        zt_nan2 = zt.copy()
+        zt_nan2[2, 0] = np.nan
+        assert run(zt_nan2, zd4, early_exit=early)["row_status"][0] & oracle.NONFINITE
+        bad = x.copy()
+        bad[3] = V
+        assert run(zt, zd4, bad, early_exit=early)["row_status"][0] & oracle.BAD_TOKEN
+    # greedy: the argmax is 2 everywhere, so the draft 4 at position 2 is the mismatch
+    zt_nan = zt.copy()
+    zt_nan[4, 0] = np.nan
+    r = run(zt_nan, zd4, mode="greedy", early_exit=True)
+    assert r["row_status"][0] == 0 and r["n_accepted"][0] == 2 and r["emitted"][2] == 2
+    assert run(zt_nan, zd4, mode="greedy")["row_status"][0] & oracle.NONFINITE
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -141,3 +141,30 @@ def test_tree_host_argument_errors(sv):
     assert call(ws=(1 << 27) + 8) == sv.SV_EWORKSPACE
     assert sv.tree_workspace_bytes(4032, 128256, sv.SV_BF16) > 0
     assert sv.tree_workspace_bytes(-1, 10, sv.SV_BF16) == 0
+
+
+def test_early_exit_host_argument_errors(sv):
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def call(**kw):
+        a = dict(target=1 << 20, draft=1 << 21, dtype=sv.SV_BF16, vocab=32, batch=2, nT=6, tokens=1 << 22,
+                 uniforms=1 << 23, temperature=1 << 24, gamma=None, gamma_u=2, gamma_max=2, mode=sv.SV_SAMPLE,
+                 cache=None, n_acc=1 << 25, emitted=1 << 26, crop=None, ws=1 << 27, ws_bytes=1 << 30)
+        a.update(kw)
+        return sv.lib.spec_verify_early_exit(vp(a["target"]), vp(a["draft"]), a["dtype"], a["vocab"], a["batch"],
+                                             a["nT"], vp(a["tokens"]), vp(a["uniforms"]), vp(a["temperature"]),
+                                             vp(a["gamma"]), a["gamma_u"], a["gamma_max"], a["mode"],
+                                             vp(a["cache"]), vp(a["n_acc"]), vp(a["emitted"]), vp(a["crop"]),
+                                             None, vp(a["ws"]), a["ws_bytes"], None)
+    assert call(dtype=4) == sv.SV_EDTYPE
+    assert call(mode=2) == sv.SV_EINVAL
+    assert call(nT=7) == sv.SV_EINVAL
+    assert call(gamma_u=-1) == sv.SV_EINVAL
+    assert call(gamma=1 << 28, gamma_max=-1) == sv.SV_EINVAL   # ragged needs a bound
+    assert call(target=None) == sv.SV_EINVAL
+    assert call(draft=None) == sv.SV_EINVAL
+    assert call(ws_bytes=64) == sv.SV_EWORKSPACE
+    assert call(ws=(1 << 27) + 16) == sv.SV_EWORKSPACE
+    assert call(batch=0, nT=0) == sv.SV_OK
+    a = sv.early_exit_workspace_bytes(64, 384, 128256, sv.SV_BF16)
+    assert a > sv.workspace_bytes(64, 384, 128256, sv.SV_BF16) and a % 256 == 0

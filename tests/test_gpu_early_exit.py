@@ -1,0 +1,103 @@
+"""The early-exit round (spec_verify_early_exit) against the CPU oracle's early-exit
+round and against the GPU's full round, through the C ABI."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from test_gpu_parity import SMALL
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def H():
+    import gpu_harness
+    return gpu_harness
+
+
+def run_early(H, w, mode=None, dense=False, cache_len=None, tensors=None):
+    import speculative_sampling_verify_02_amd as sv
+    d = tensors or H.to_device(w)
+    gamma = w.dense_gamma if dense else d["gamma"]
+    cl = None if cache_len is None else torch.from_numpy(np.ascontiguousarray(cache_len, np.int32)).cuda()
+    n, e, crop, dg = sv.spec_verify_early_exit(d["target"], d["draft"], d["tokens"], d["uniforms"],
+                                               d["temperature"], gamma, gamma_max=int(w.gamma.max()),
+                                               cache_len=cl, mode=mode or w.mode, diag=True)
+    torch.cuda.synchronize()
+    out = dict(n_accepted=n.cpu().numpy(), emitted=e.cpu().numpy(), crop_len=crop.cpu().numpy())
+    for k, v in dg.items():
+        out[k] = v.cpu().numpy()
+    return out
+
+
+def parity(H, w, mode=None, dense=False, seed=0):
+    mode = mode or w.mode
+    _say(f"[case] early exit {w.name} mode={mode} dense={dense} B={w.batch} V={w.vocab}")
+    cache = np.random.default_rng(seed).integers(0, 4096, w.batch).astype(np.int32)
+    g = run_early(H, w, mode=mode, dense=dense, cache_len=cache)
+    ref = oracle.verify_workload(w, mode=mode, early_exit=True, cache_len=cache)
+    rep = H.compare(w, g, ref, mode=mode)
+    assert np.array_equal(g["crop_len"], ref["crop_len"]), "crop lengths differ"
+    # the full round on the GPU keeps the same drafts and draws the same tokens
+    full = H.run_gpu(w, mode=mode, dense=dense)
+    ok = full["row_status"] == 0
+    assert np.array_equal(full["n_accepted"][ok], g["n_accepted"][ok])
+    t_off, _ = w.offsets()
+    for i in np.nonzero(ok)[0]:
+        a, b = t_off[i], t_off[i + 1]
+        assert np.array_equal(full["emitted"][a:b], g["emitted"][a:b]), i
+    _say(f"[ok] {rep}")
+    return g, ref
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_small_sample(H, case):
+    parity(H, workloads.small(**SMALL[case]), seed=case)
+
+
+@pytest.mark.parametrize("case", [0, 1, 3, 7, 9])
+def test_small_greedy(H, case):
+    w = workloads.small(**{**SMALL[case], "mode": "greedy"})
+    parity(H, w, mode="greedy", seed=case)
+
+
+def test_dense(H):
+    parity(H, workloads.small(seed=71, batch=24, vocab=8192, dtype="bf16", gamma=4, noise=0.4), dense=True)
+
+
+def test_nan_after_the_rejection(H):
+    """A NaN logit beyond a row's rejection is never read: the row stays valid (the
+    full round marks it invalid)."""
+    w = workloads.small(seed=72, batch=16, vocab=4096, dtype="f32", gamma=6, noise=2.0)
+    ref = oracle.verify_workload(w)
+    t_off, d_off = w.offsets()
+    tgt, dft = w.target.copy(), w.draft.copy()
+    rows = []
+    for i in range(w.batch):
+        K = ref["n_accepted"][i]
+        if 0 <= K < w.gamma[i] - 1:
+            tgt[t_off[i] + K + 1, 5] = np.nan
+            dft[d_off[i] + K + 1, 7] = np.nan
+            rows.append(i)
+    assert rows, "no row rejects early enough"
+    w2 = workloads.Workload(**{**w.__dict__, "target": tgt, "draft": dft})
+    g, _ = parity(H, w2)
+    assert np.all(g["row_status"][rows] == 0)
+
+
+def test_c3_full(H):
+    parity(H, workloads.c3(), dense=True, seed=3)
+
+
+def test_c5_full(H):
+    parity(H, workloads.c5(), seed=5)

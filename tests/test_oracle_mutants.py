@@ -43,6 +43,9 @@ MUTANTS = {
     "tree_own_prediction": ("(int64_t)tokens[o + k] == pred[par]", "(int64_t)tokens[o + k] == pred[k]"),
     "tree_last_longest": ("                if (len[k] > len[best])", "                if (len[k] >= len[best])"),
     "tree_ignores_parent": ("len[k] = (len[par] > 0 && ", "len[k] = (len[par] >= 0 && "),
+    "early_exit_keeps_reading": ("                if (early_exit && decided)\n                    break;",
+                                 "                if (early_exit && decided && 0)\n                    break;"),
+    "crop_without_last_token": ("    return n + K + 1;", "    return n + K;"),
     "neg_inf_is_nonfinite": ("if (isnan(x) || x == INFINITY)", "if (isnan(x) || isinf(x))"),
 }
 
