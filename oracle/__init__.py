@@ -60,8 +60,10 @@ def _load(path: str):
     L.oracle_verify.restype = ctypes.c_int
     L.oracle_verify_ex.argtypes = [vp, vp, ctypes.c_int, i64, i32, i64, vp, vp, vp, vp,
                                    ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, dbl, ctypes.c_int,
-                                   ctypes.c_int, vp, vp]
+                                   ctypes.c_int, vp, vp, vp, vp]
     L.oracle_verify_ex.restype = ctypes.c_int
+    L.oracle_filter_threshold.argtypes = [vp, ctypes.c_int, i64, dbl, i64, dbl, dbl, vp, vp]
+    L.oracle_filter_threshold.restype = ctypes.c_int
     L.oracle_sample.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, vp, dbl, ctypes.c_int]
     L.oracle_sample.restype = ctypes.c_int
     L.oracle_tree_greedy.argtypes = [vp, ctypes.c_int, i64, i32, i64, vp, vp, vp, vp, vp, vp, vp,
@@ -150,11 +152,14 @@ def inverse_cdf(w, u: float, eps: float = 1e-5):
 
 def verify(target, draft, dtype: str, vocab: int, gamma, draft_tokens, uniforms, temperature,
            mode: str = "sample", n_target_rows=None, threads: int = 0,
-           flag_eps: float = 1e-5, early_exit: bool = False, cache_len=None) -> dict:
+           flag_eps: float = 1e-5, early_exit: bool = False, cache_len=None, top_k=None,
+           top_p=None) -> dict:
     """One verification round over a packed batch; returns numpy arrays.  flag_pos[i] is
     the first decision of row i within flag_eps of its threshold (accept test j, or
     gamma_i for the draw), -1 if none.  early_exit reads positions left to right and
-    stops at the first rejection; crop_len[i] = cache_len[i] + K_i + 1 (-1 if invalid)."""
+    stops at the first rejection; crop_len[i] = cache_len[i] + K_i + 1 (-1 if invalid).
+    top_k (int32 [B]) and top_p (float32 [B]) filter p and q of each sampling row
+    (see filter_threshold)."""
     gamma = np.ascontiguousarray(gamma, np.int32)
     B = gamma.shape[0]
     target = _logits(target, dtype)
@@ -176,16 +181,31 @@ def verify(target, draft, dtype: str, vocab: int, gamma, draft_tokens, uniforms,
     )
     out["crop_len"] = np.empty(B, np.int32)
     cl = None if cache_len is None else np.ascontiguousarray(cache_len, np.int32)
+    tk = None if top_k is None else np.ascontiguousarray(top_k, np.int32)
+    tp = None if top_p is None else np.ascontiguousarray(top_p, np.float32)
     rc = lib().oracle_verify_ex(_ptr(target), _ptr(draft), _DTYPES[dtype], int(vocab), B,
                                 int(n_target_rows), _ptr(tokens), _ptr(uniforms), _ptr(temperature),
                                 _ptr(gamma), SAMPLE if mode == "sample" else GREEDY,
                                 _ptr(out["n_accepted"]), _ptr(out["emitted"]), _ptr(out["p_x"]),
                                 _ptr(out["q_x"]), _ptr(out["resid_mass"]), _ptr(out["row_status"]),
                                 _ptr(out["flag_pos"]), float(flag_eps), int(threads), int(bool(early_exit)),
-                                _ptr(cl), _ptr(out["crop_len"]))
+                                _ptr(cl), _ptr(out["crop_len"]), _ptr(tk), _ptr(tp))
     if rc != 0:
         raise ValueError(f"oracle_verify status {rc}")
     return out
+
+
+def filter_threshold(z, T: float, top_k: int = 0, top_p: float = 1.0, dtype: str = "f64",
+                     eps: float = 1e-10):
+    """(theta, near): tokens with logit >= theta survive top-k then top-p filtering."""
+    z = _logits(z, dtype)
+    th = np.zeros(1, np.float64)
+    near = np.zeros(1, np.int32)
+    rc = lib().oracle_filter_threshold(_ptr(z), _DTYPES[dtype], z.shape[-1], float(T), int(top_k),
+                                       float(top_p), float(eps), _ptr(th), _ptr(near))
+    if rc != 0:
+        raise ValueError(f"oracle_filter_threshold status {rc}")
+    return float(th[0]), bool(near[0])
 
 
 def sample(logits, dtype: str, vocab: int, temperature, uniforms, threads: int = 0,
@@ -232,8 +252,8 @@ def tree_greedy(logits, dtype: str, vocab: int, counts, tokens, parents, threads
 
 
 def verify_workload(w, threads: int = 0, mode: str | None = None, flag_eps: float = 1e-5,
-                    early_exit: bool = False, cache_len=None) -> dict:
+                    early_exit: bool = False, cache_len=None, top_k=None, top_p=None) -> dict:
     """verify() on any object with the packed-workload attributes."""
     return verify(w.target, w.draft, w.dtype, w.vocab, w.gamma, w.draft_tokens, w.uniforms,
                   w.temperature, mode=mode or w.mode, threads=threads, flag_eps=flag_eps,
-                  early_exit=early_exit, cache_len=cache_len)
+                  early_exit=early_exit, cache_len=cache_len, top_k=top_k, top_p=top_p)

@@ -95,8 +95,17 @@ static int vector_nonfinite(const void *z, int dtype, int64_t V)
 }
 
 /* m = max z, S = sum_v exp((z_v - m)/T), summed in index order. */
-static void vector_max_sumexp(const void *z, int dtype, int64_t V, double T, double *m_out,
-                              double *S_out)
+/* The logit of token v after filtering at theta: tokens below it drop out (their
+ * probability is 0, as for a logit of -inf). */
+static double kept_logit(const void *z, int dtype, int64_t v, double theta)
+{
+    const double x = logit_at(z, dtype, v);
+    return x >= theta ? x : -INFINITY;
+}
+
+/* m = max z, S = sum_v exp((z_v - m)/T) over the tokens kept at theta, in index order. */
+static void vector_max_sumexp(const void *z, int dtype, int64_t V, double T, double theta,
+                              double *m_out, double *S_out)
 {
     double m = -INFINITY;
     for (int64_t v = 0; v < V; ++v) {
@@ -106,21 +115,91 @@ static void vector_max_sumexp(const void *z, int dtype, int64_t V, double T, dou
     }
     double S = 0.0;
     for (int64_t v = 0; v < V; ++v)
-        S += exp((logit_at(z, dtype, v) - m) / T);
+        S += exp((kept_logit(z, dtype, v, theta) - m) / T);
     *m_out = m;
     *S_out = S;
 }
 
-int oracle_softmax(const void *z, int dtype, int64_t V, double T, double *p)
+static int softmax_kept(const void *z, int dtype, int64_t V, double T, double theta, double *p)
 {
     if (!z || !p || V <= 0 || !(T > 0) || !isfinite(T))
         return -1;
     if (vector_nonfinite(z, dtype, V))
         return ORACLE_NONFINITE;
     double m, S;
-    vector_max_sumexp(z, dtype, V, T, &m, &S);
+    vector_max_sumexp(z, dtype, V, T, theta, &m, &S);
     for (int64_t v = 0; v < V; ++v)
-        p[v] = exp((logit_at(z, dtype, v) - m) / T) / S;
+        p[v] = exp((kept_logit(z, dtype, v, theta) - m) / T) / S;
+    return 0;
+}
+
+int oracle_softmax(const void *z, int dtype, int64_t V, double T, double *p)
+{
+    return softmax_kept(z, dtype, V, T, -INFINITY, p);
+}
+
+/* ------------------------------------------------------------------------- */
+/* top-k and top-p filtering                                                   */
+/* ------------------------------------------------------------------------- */
+static int cmp_desc(const void *a, const void *b)
+{
+    const double x = *(const double *)a, y = *(const double *)b;
+    return x > y ? -1 : (x < y ? 1 : 0);
+}
+
+/* The logit threshold theta of a filtered distribution: a token is kept iff its logit
+ * is >= theta (-inf: no filtering).  The pages require any such filter to be applied
+ * to both p and q before the test (rayaq.ca "Speculative decoding", section "Why the
+ * output is exactly the target's", last paragraph; section "Tradeoffs").
+ *  - top-k (0 < top_k < V): theta_k = the top_k-th largest logit, counted with
+ *    multiplicity; every token tied with it is kept too;
+ *  - top-p (0 < top_p < 1), on the distribution left by top-k: tokens are taken in
+ *    decreasing logit order, a whole group of equal logits at a time, until their
+ *    probability reaches top_p; theta_p = the logit of the last group taken;
+ *  - theta = max(theta_k, theta_p).
+ * *near = 1 when top_p lies within eps of the cumulative probability on either side
+ * of the last group's step. */
+int oracle_filter_threshold(const void *z, int dtype, int64_t V, double T, int64_t top_k, double top_p,
+                            double eps, double *theta_out, int *near)
+{
+    *theta_out = -INFINITY;
+    if (near)
+        *near = 0;
+    if (!z || V <= 0 || !(T > 0) || !isfinite(T))
+        return -1;
+    const int use_k = top_k > 0 && top_k < V;
+    const int use_p = top_p > 0 && top_p < 1;
+    if ((!use_k && !use_p) || vector_nonfinite(z, dtype, V))
+        return 0;
+    double *s = malloc(sizeof(double) * (size_t)V);
+    if (!s)
+        return -1;
+    for (int64_t v = 0; v < V; ++v)
+        s[v] = logit_at(z, dtype, v);
+    qsort(s, (size_t)V, sizeof(double), cmp_desc);
+    double theta = use_k ? s[top_k - 1] : -INFINITY;
+    if (use_p) {
+        const double m = s[0];
+        double S = 0.0;
+        for (int64_t i = 0; i < V && s[i] >= theta; ++i)
+            S += exp((s[i] - m) / T);
+        const double target = top_p * S;
+        double cum = 0.0;
+        for (int64_t i = 0; i < V && s[i] >= theta;) {
+            const double val = s[i];
+            const double before = cum;
+            for (; i < V && s[i] == val; ++i)
+                cum += exp((s[i] - m) / T);
+            if (cum >= target) {
+                if (near)
+                    *near = (cum - target < eps * S) || (target - before < eps * S);
+                theta = val;
+                break;
+            }
+        }
+    }
+    free(s);
+    *theta_out = theta;
     return 0;
 }
 
@@ -230,15 +309,16 @@ static int32_t kept_cache_entries(const int32_t *cache_len, int32_t i, int K)
 
 /* The acceptance probability min(1, p(x)/q(x)) of draft token x at one position
  * (rayaq.ca "Speculative decoding", section "One round", step 3), with p(x) and q(x)
- * from the temperature softmax; q(x) = 0 gives 1 if p(x) > 0, else 0 (*q_zero = 1). */
+ * from the temperature softmax of the tokens kept at theta_t and theta_d; q(x) = 0
+ * gives 1 if p(x) > 0, else 0 (*q_zero = 1). */
 static double accept_ratio(const void *zt, const void *zd, int dtype, int64_t V, double T, int64_t x,
-                           double *px_out, double *qx_out, int *q_zero)
+                           double theta_t, double theta_d, double *px_out, double *qx_out, int *q_zero)
 {
     double mt, St, md, Sd;
-    vector_max_sumexp(zt, dtype, V, T, &mt, &St);
-    vector_max_sumexp(zd, dtype, V, T, &md, &Sd);
-    double px = exp((logit_at(zt, dtype, x) - mt) / T) / St;
-    double qx = exp((logit_at(zd, dtype, x) - md) / T) / Sd;
+    vector_max_sumexp(zt, dtype, V, T, theta_t, &mt, &St);
+    vector_max_sumexp(zd, dtype, V, T, theta_d, &md, &Sd);
+    double px = exp((kept_logit(zt, dtype, x, theta_t) - mt) / T) / St;
+    double qx = exp((kept_logit(zd, dtype, x, theta_d) - md) / T) / Sd;
     *px_out = px;
     *qx_out = qx;
     *q_zero = 0;
@@ -292,7 +372,8 @@ int oracle_verify_ex(const void *target, const void *draft, int dtype, int64_t V
                      const float *temperature, const int32_t *gamma_per_row, int mode,
                      int32_t *n_accepted, int32_t *emitted, double *p_x, double *q_x,
                      double *resid_mass, int32_t *row_status, int32_t *flag_pos, double flag_eps,
-                     int nthreads, int early_exit, const int32_t *cache_len, int32_t *crop_len)
+                     int nthreads, int early_exit, const int32_t *cache_len, int32_t *crop_len,
+                     const int32_t *top_k, const float *top_p)
 {
     const double eps = flag_eps > 0 ? flag_eps : 1e-5;
     if (!target || !gamma_per_row || !uniforms || !temperature || !n_accepted || !emitted ||
@@ -379,6 +460,36 @@ int oracle_verify_ex(const void *target, const void *draft, int dtype, int64_t V
                 if (x < 0 || (int64_t)x >= V)
                     status |= ORACLE_BAD_TOKEN;
             }
+            /* the filters' thresholds at every position (sampling rows with top-k or top-p);
+               a top-p boundary within 1e-10 of top_p flags that position */
+            double *th_t = NULL, *th_d = NULL;
+            const int64_t row_k = top_k ? top_k[i] : 0;
+            const double row_p = top_p ? (double)top_p[i] : 1.0;
+            if (!greedy && !(status & ORACLE_INVALID_MASK) &&
+                ((row_k > 0 && row_k < V) || (row_p > 0 && row_p < 1))) {
+                th_t = malloc(sizeof(double) * ((size_t)g + 1));
+                th_d = malloc(sizeof(double) * ((size_t)g + 1));
+                if (!th_t || !th_d) {
+#pragma omp atomic write
+                    rc = -1;
+                    free(th_t);
+                    free(th_d);
+                    continue;
+                }
+                for (int j = 0; j <= g; ++j) {
+                    int nt = 0, nd = 0;
+                    oracle_filter_threshold(vector_ptr(target, dtype, t0 + j, V), dtype, V, T, row_k, row_p,
+                                            1e-10, &th_t[j], &nt);
+                    th_d[j] = -INFINITY;
+                    if (j < g)
+                        oracle_filter_threshold(vector_ptr(draft, dtype, d0 + j, V), dtype, V, T, row_k,
+                                                row_p, 1e-10, &th_d[j], &nd);
+                    if ((nt || nd) && flag < 0)
+                        flag = j;
+                }
+            }
+#define THETA_T(j) (th_t ? th_t[j] : -INFINITY)
+#define THETA_D(j) (th_d ? th_d[j] : -INFINITY)
             /* validity of every position the row reads: all of them, or (early exit) those
                up to the first rejection */
             int K_read = g;
@@ -396,8 +507,8 @@ int oracle_verify_ex(const void *target, const void *draft, int dtype, int64_t V
                         }
                         double px, qx;
                         int q_zero;
-                        const double ratio = accept_ratio(zt, zd, dtype, V, T, draft_tokens[d0 + j], &px,
-                                                          &qx, &q_zero);
+                        const double ratio = accept_ratio(zt, zd, dtype, V, T, draft_tokens[d0 + j],
+                                                          THETA_T(j), THETA_D(j), &px, &qx, &q_zero);
                         reject = !((double)uniforms[t0 + j] < ratio);
                     }
                     if (vector_nonfinite(zt, dtype, V) || reject) {
@@ -421,6 +532,8 @@ int oracle_verify_ex(const void *target, const void *draft, int dtype, int64_t V
                     row_status[i] = status;
                 if (flag_pos)
                     flag_pos[i] = -1;
+                free(th_t);
+                free(th_d);
                 continue;
             }
 
@@ -475,7 +588,8 @@ int oracle_verify_ex(const void *target, const void *draft, int dtype, int64_t V
                 int q_zero;
                 const double ratio = accept_ratio(vector_ptr(target, dtype, t0 + j, V),
                                                   vector_ptr(draft, dtype, d0 + j, V), dtype, V, T,
-                                                  draft_tokens[d0 + j], &px, &qx, &q_zero);
+                                                  draft_tokens[d0 + j], THETA_T(j), THETA_D(j), &px, &qx,
+                                                  &q_zero);
                 if (p_x)
                     p_x[d0 + j] = px;
                 if (q_x)
@@ -494,9 +608,9 @@ int oracle_verify_ex(const void *target, const void *draft, int dtype, int64_t V
             }
 
             /* residual at a rejection, or p at the bonus position */
-            oracle_softmax(vector_ptr(target, dtype, t0 + K, V), dtype, V, T, P);
+            softmax_kept(vector_ptr(target, dtype, t0 + K, V), dtype, V, T, THETA_T(K), P);
             if (K < g) {
-                oracle_softmax(vector_ptr(draft, dtype, d0 + K, V), dtype, V, T, Q);
+                softmax_kept(vector_ptr(draft, dtype, d0 + K, V), dtype, V, T, THETA_D(K), Q);
                 double W = 0.0;
                 for (int64_t v = 0; v < V; ++v) {
                     w[v] = fmax(0.0, P[v] - Q[v]);
@@ -528,6 +642,10 @@ int oracle_verify_ex(const void *target, const void *draft, int dtype, int64_t V
                 row_status[i] = status;
             if (flag_pos)
                 flag_pos[i] = flag;
+            free(th_t);
+            free(th_d);
+#undef THETA_T
+#undef THETA_D
         }
         free(P);
         free(Q);
@@ -736,5 +854,6 @@ int oracle_verify(const void *target, const void *draft, int dtype, int64_t V, i
 {
     return oracle_verify_ex(target, draft, dtype, V, B, n_target_rows, draft_tokens, uniforms,
                             temperature, gamma_per_row, mode, n_accepted, emitted, p_x, q_x,
-                            resid_mass, row_status, flag_pos, flag_eps, nthreads, 0, NULL, NULL);
+                            resid_mass, row_status, flag_pos, flag_eps, nthreads, 0, NULL, NULL, NULL,
+                            NULL);
 }

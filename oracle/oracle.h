@@ -44,5 +44,8 @@ int oracle_verify_ex(const void *target, const void *draft, int dtype, int64_t V
                      const float *temperature, const int32_t *gamma_per_row, int mode,
                      int32_t *n_accepted, int32_t *emitted, double *p_x, double *q_x,
                      double *resid_mass, int32_t *row_status, int32_t *flag_pos, double flag_eps,
-                     int nthreads, int early_exit, const int32_t *cache_len, int32_t *crop_len);
+                     int nthreads, int early_exit, const int32_t *cache_len, int32_t *crop_len,
+                     const int32_t *top_k, const float *top_p);
+int oracle_filter_threshold(const void *z, int dtype, int64_t V, double T, int64_t top_k, double top_p,
+                            double eps, double *theta_out, int *near);
 #endif

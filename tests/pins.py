@@ -945,4 +945,109 @@ def pin_early_exit_reads_only_up_to_the_rejection():
     assert run(zt_nan, zd4, mode="greedy")["row_status"][0] & oracle.NONFINITE
 
 
+
+# --------------------------------------------------------------------------- #
+# top-k and top-p filtering of p and q
+# --------------------------------------------------------------------------- #
+def pin_filter_closed_forms():
+    """Hand-counted thresholds: probabilities (0.5, 0.3, 0.15, 0.05) keep 1, 2, 3, 4
+    tokens at top-p 0.49, 0.79, 0.81, 0.96; top-k counts ties; top-k = 3 before top-p
+    renormalizes (0.4, 0.3, 0.2, 0.1) to (4, 3, 2)/9, so top-p 0.75 keeps 2 tokens
+    instead of 3."""
+    z = np.log([0.5, 0.3, 0.15, 0.05])
+    for tp, kept in ((0.49, 1), (0.79, 2), (0.81, 3), (0.96, 4)):
+        th, near = oracle.filter_threshold(z, 1.0, top_p=tp)
+        assert np.sum(z >= th) == kept and not near, (tp, th)
+    zt = np.array([3.0, 1.0, 1.0, 1.0, 0.0])
+    assert oracle.filter_threshold(zt, 1.0, top_k=2)[0] == 1.0          # keeps 4 (ties)
+    assert oracle.filter_threshold(zt, 1.0, top_k=1)[0] == 3.0
+    assert oracle.filter_threshold(zt, 1.0, top_k=5)[0] == -np.inf      # k >= V: no filter
+    z4 = np.log([0.4, 0.3, 0.2, 0.1])
+    assert np.sum(z4 >= oracle.filter_threshold(z4, 1.0, top_p=0.75)[0]) == 3
+    assert np.sum(z4 >= oracle.filter_threshold(z4, 1.0, top_k=3, top_p=0.75)[0]) == 2
+    # temperature sharpens before top-p: T = 1/2 squares the odds, (25, 9, 2.25, 0.25)/36.5
+    assert np.sum(z >= oracle.filter_threshold(z, 0.5, top_p=0.9)[0]) == 2
+    # bf16 logits (2, 1, 1, 0): e^(z) = (7.389, 2.718, 2.718, 1) over 13.825
+    zb = np.array([[0x4000, 0x3F80, 0x3F80, 0x0000]], np.uint16)
+    th, _ = oracle.filter_threshold(zb, 1.0, top_p=0.6, dtype="bf16")
+    assert th == 1.0                                                   # 0.534 < 0.6 <= 0.928
+
+
+def pin_filter_vs_sorting():
+    """Thresholds against numpy: the top_k-th largest value, then the first group of
+    equal logits (in decreasing order) where scipy's softmax over the kept tokens
+    reaches top_p."""
+    rng = np.random.default_rng(43)
+    for _ in range(300):
+        V = int(rng.integers(2, 60))
+        z = rng.integers(-6, 7, V).astype(np.float64) * 0.5   # many ties
+        T = float(rng.choice([0.5, 1.0, 1.7]))
+        k = int(rng.integers(0, V + 2))
+        tp = float(rng.choice([1.0, rng.random()]))
+        th, near = oracle.filter_threshold(z, T, top_k=k, top_p=tp)
+        desc = np.sort(z)[::-1]
+        want = desc[k - 1] if 0 < k < V else -np.inf
+        if 0 < tp < 1:
+            kept = z[z >= want]
+            p = scipy.special.softmax(kept / T)
+            vals = np.unique(kept)[::-1]
+            cum = np.cumsum([p[kept == v].sum() for v in vals])
+            i = int(np.argmax(cum >= tp)) if (cum >= tp).any() else len(vals) - 1
+            if abs(cum[i] - tp) < 1e-9 or (i > 0 and abs(tp - cum[i - 1]) < 1e-9):
+                continue
+            want = vals[i]
+        assert th == want, (z, T, k, tp, th, want)
+
+
+def pin_top1_sampling_is_greedy():
+    """top_k = 1 on both models makes p and q one-hot at their argmaxes: with drafts
+    equal to the drafter's argmax, the sampling round is the greedy round whatever the
+    uniforms."""
+    rng = np.random.default_rng(44)
+    B, V = 50, 40
+    gam = rng.integers(0, 6, B).astype(np.int32)
+    nT, nD = int(gam.sum() + B), int(gam.sum())
+    zt = rng.standard_normal((nT, V))
+    d_off = np.cumsum(gam) - gam
+    t_off = np.cumsum(gam + 1) - gam - 1
+    zd = np.concatenate([zt[o:o + g] for o, g in zip(t_off, gam)]) + rng.standard_normal((nD, V)) * 0.8
+    x = np.argmax(zd, axis=1).astype(np.int32)
+    u = snapped(rng, nT)
+    T = np.full(B, 0.9, np.float32)
+    a = oracle.verify(zt, zd, "f64", V, gam, x, u, T, top_k=np.ones(B, np.int32))
+    g = oracle.verify(zt, zd, "f64", V, gam, x, u, T, mode="greedy")
+    assert np.array_equal(a["n_accepted"], g["n_accepted"])
+    assert np.array_equal(a["emitted"], g["emitted"])
+    # and no filter (top_k >= V, top_p >= 1) is the plain round
+    b = oracle.verify(zt, zd, "f64", V, gam, x, u, T, top_k=np.full(B, V, np.int32),
+                      top_p=np.ones(B, np.float32))
+    c = oracle.verify(zt, zd, "f64", V, gam, x, u, T)
+    for k in ("n_accepted", "emitted", "p_x", "q_x", "resid_mass"):
+        assert np.array_equal(b[k], c[k], equal_nan=True), k
+
+
+def pin_filtered_output_distribution():
+    """With p and q both filtered (top-k 5, top-p 0.8) and drafts drawn from the
+    filtered q, the token emitted at the first position is distributed as the filtered
+    p (chi-square over 40,000 rounds)."""
+    rng = np.random.default_rng(45)
+    V, g, N = 10, 2, 40000
+    zt1 = rng.standard_normal(V) * 1.5
+    zd1 = zt1 + rng.standard_normal(V)
+    zt = np.tile(zt1, (g + 1, 1))
+    zd = np.tile(zd1, (g, 1))
+    def filtered(z):
+        th, _ = oracle.filter_threshold(z, 1.0, top_k=5, top_p=0.8)
+        p = np.where(z >= th, np.exp(z - z.max()), 0.0)
+        return p / p.sum()
+    pf, qf = filtered(zt1), filtered(zd1)
+    x = rng.choice(V, size=(N, g), p=qf).astype(np.int32)
+    u = snapped(rng, N * (g + 1))
+    r = oracle.verify(np.tile(zt, (N, 1)), np.tile(zd, (N, 1)), "f64", V, np.full(N, g, np.int32),
+                      x.reshape(-1), u, np.ones(N, np.float32), top_k=np.full(N, 5, np.int32),
+                      top_p=np.full(N, 0.8, np.float32))
+    first = r["emitted"].reshape(N, g + 1)[:, 0]
+    _chi2_ok(np.bincount(first, minlength=V), pf, "filtered emission")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

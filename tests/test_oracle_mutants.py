@@ -19,14 +19,14 @@ MUTANTS = {
     "inverted_ratio": ("ratio = px / qx;", "ratio = qx / px;"),
     "residual_sign": ("w[v] = fmax(0.0, P[v] - Q[v]);", "w[v] = fmax(0.0, Q[v] - P[v]);"),
     "bonus_wrong_position": (
-        "oracle_softmax(vector_ptr(target, dtype, t0 + K, V), dtype, V, T, P);",
-        "oracle_softmax(vector_ptr(target, dtype, t0 + (K == g && K > 0 ? K - 1 : K), V), dtype, V, T, P);"),
+        "softmax_kept(vector_ptr(target, dtype, t0 + K, V), dtype, V, T, THETA_T(K), P);",
+        "softmax_kept(vector_ptr(target, dtype, t0 + (K == g && K > 0 ? K - 1 : K), V), dtype, V, T, THETA_T(K), P);"),
     "draw_reuses_test_uniform": ("(double)uniforms[t0 + g], eps, &W, &near)",
                                  "(double)uniforms[t0 + K], eps, &W, &near)"),
-    "q_sum_without_temperature": ("vector_max_sumexp(zd, dtype, V, T, &md, &Sd);",
-                                  "vector_max_sumexp(zd, dtype, V, 1.0, &md, &Sd);"),
-    "sumexp_without_temperature": ("S += exp((logit_at(z, dtype, v) - m) / T);",
-                                   "S += exp(logit_at(z, dtype, v) - m);"),
+    "q_sum_without_temperature": ("vector_max_sumexp(zd, dtype, V, T, theta_d, &md, &Sd);",
+                                  "vector_max_sumexp(zd, dtype, V, 1.0, theta_d, &md, &Sd);"),
+    "sumexp_without_temperature": ("S += exp((kept_logit(z, dtype, v, theta) - m) / T);",
+                                   "S += exp(kept_logit(z, dtype, v, theta) - m);"),
     "greedy_bonus_off_by_one": (
         "int64_t aK = oracle_argmax(vector_ptr(target, dtype, t0 + K, V), dtype, V);",
         "int64_t aK = oracle_argmax(vector_ptr(target, dtype, t0 + (K > 0 ? K - 1 : 0), V), dtype, V);"),
@@ -46,6 +46,13 @@ MUTANTS = {
     "early_exit_keeps_reading": ("                if (early_exit && decided)\n                    break;",
                                  "                if (early_exit && decided && 0)\n                    break;"),
     "crop_without_last_token": ("    return n + K + 1;", "    return n + K;"),
+    "top_k_off_by_one": ("double theta = use_k ? s[top_k - 1] : -INFINITY;",
+                         "double theta = use_k ? s[top_k] : -INFINITY;"),
+    "top_p_before_top_k": ("for (int64_t i = 0; i < V && s[i] >= theta; ++i)\n            S += exp",
+                           "for (int64_t i = 0; i < V; ++i)\n            S += exp"),
+    "top_p_overshoots": ("            if (cum >= target) {", "            if (cum > target * 1.05) {"),
+    "filter_only_target": ("                        oracle_filter_threshold(vector_ptr(draft, dtype, d0 + j, V), dtype, V, T, row_k,",
+                           "                        oracle_filter_threshold(vector_ptr(draft, dtype, d0 + j, V), dtype, V, T, 0 * row_k,"),
     "neg_inf_is_nonfinite": ("if (isnan(x) || x == INFINITY)", "if (isnan(x) || isinf(x))"),
 }
 
