@@ -46,10 +46,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c3", choices=["c2", "c3", "c4", "c5"])
     ap.add_argument("--mode", default="sample", choices=["sample", "greedy"])
-    ap.add_argument("--op", default="verify", choices=["verify", "early", "sample", "tree"],
+    ap.add_argument("--op", default="verify", choices=["verify", "early", "filtered", "sample", "tree"],
                     help="verify: the verification step (default); sample: the drafter's draw "
                          "over the configuration's draft logit vectors; early: the verification step "
-                         "with early exit (positions left to right); tree: greedy verification "
+                         "with early exit (positions left to right); filtered: the verification step "
+                         "with top-k 50 and top-p 0.9 on p and q; tree: greedy verification "
                          "of 16 Medusa trees (top-2 candidates, 5 heads: 63 nodes) at V = 128256 bf16")
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -206,8 +207,7 @@ def bench_sample(args):
         "config": {"workload": si.name, "vectors": n, "vocab": V, "rotated_device_copies": len(copies)},
         "hbm_gbps_algorithmic": total / sec / 1e9,
         "hbm_frac_of_peak": total / sec / 1e9 / PEAK_HBM_GBPS,
-        "roofline": {"kernel": "stats_list_kernel + ee_step_kernel steps" if early else "stats_kernel",
-                     "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
+        "roofline": {"kernel": "stats_kernel", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
                      "avg_launch_ms": stats_ms, "algorithmic_bytes_per_launch": pass1,
                      "timed_steps": args.steps, "ms_per_step_with_events": ms_ev},
@@ -273,8 +273,7 @@ def bench_tree(args):
         "mean_kept_drafts": float(K[K >= 0].mean()),
         "hbm_gbps_algorithmic": total / sec / 1e9,
         "hbm_frac_of_peak": total / sec / 1e9 / PEAK_HBM_GBPS,
-        "roofline": {"kernel": "stats_list_kernel + ee_step_kernel steps" if early else "stats_kernel",
-                     "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
+        "roofline": {"kernel": "stats_kernel", "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
                      "avg_launch_ms": stats_ms, "algorithmic_bytes_per_launch": pass1,
                      "timed_steps": args.steps, "ms_per_step_with_events": ms_ev},
@@ -329,6 +328,12 @@ def main():
                      dtype=torch.uint8, device=dev)
 
     early = args.op == "early"
+    filt = args.op == "filtered"
+    if filt:
+        ws = torch.empty(sv.filtered_workspace_bytes(B, nT, V, sv.SV_BF16 if w.dtype == "bf16" else sv.SV_F32),
+                         dtype=torch.uint8, device=dev)
+        fk = torch.full((B,), 50, dtype=torch.int32, device=dev)
+        fp = torch.full((B,), 0.9, dtype=torch.float32, device=dev)
     if early:
         ws = torch.empty(sv.early_exit_workspace_bytes(B, nT, V, sv.SV_BF16 if w.dtype == "bf16" else sv.SV_F32),
                          dtype=torch.uint8, device=dev)
@@ -337,6 +342,9 @@ def main():
     def step(k, d=None):
         d = d or copies[k % len(copies)]
         g = gamma_arg if gamma_arg is not None else d["gamma"]
+        if filt:
+            return sv.spec_verify_filtered(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temperature"],
+                                           g, top_k=fk, top_p=fp, workspace=ws, out=outs[k % len(copies)])
         if early:
             return sv.spec_verify_early_exit(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temperature"],
                                              g, gamma_max=gmax, mode=args.mode, workspace=ws,
@@ -409,7 +417,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "gamma": int(gam.max()) if dense is None else dense,
                    "ragged": dense is None, "vocab": V, "mode": args.mode,
-                   "variant": "early exit" if early else "all positions in parallel",
+                   "variant": "early exit" if early else (
+                       "top-k 50, top-p 0.9 on p and q" if filt else "all positions in parallel"),
                    "rotated_device_copies": len(copies)},
         "rows_per_s": B / sec_per_step,
         "hbm_gbps_algorithmic": total_bytes / sec_per_step / 1e9,

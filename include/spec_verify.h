@@ -254,6 +254,39 @@ sv_status spec_verify_early_exit(const void *target_logits, const void *draft_lo
                                  int32_t *emitted_tokens, int32_t *crop_len, const sv_diag *diag,
                                  void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/*
+ * The verification round on filtered distributions: each sampling row's top-k and
+ * top-p filter is applied to both p and q at every position before the test (rayaq.ca
+ * "Speculative decoding", section "Why the output is exactly the target's", last
+ * paragraph: the rule preserves exactly the p it is given, so a filter used for
+ * sampling must reach both distributions).  A filter keeps the tokens whose logit is
+ * at least a threshold theta, and the kept probabilities are renormalized:
+ *   top-k (0 < top_k[i] < vocab): theta_k is the top_k-th largest logit counted with
+ *         multiplicity, tokens tied with it are kept;
+ *   top-p (0 < top_p[i] < 1), applied after top-k: groups of equal logits are taken in
+ *         decreasing order until their probability reaches top_p[i]; theta_p is the
+ *         logit of the last group taken;
+ *   theta = max(theta_k, theta_p); other values of top_k / top_p do not filter.
+ * The thresholds are exact (the probability sums behind top-p are taken in fp64 at
+ * the exact temperature scale).  A draft token outside the drafter's kept set has
+ * q(x) = 0 (SV_ROW_Q_ZERO); one outside the target's kept set has p(x) = 0 and is
+ * rejected.  Greedy rows (temperature <= 0) are not filtered.
+ *
+ * Arguments as for spec_verify in SV_SAMPLE mode, plus:
+ *   top_k       [batch] int32 device, or NULL (no top-k)
+ *   top_p       [batch] float device, or NULL (no top-p); one of the two must be given
+ *   workspace   >= spec_verify_filtered_workspace_bytes(...) bytes, 256-byte aligned
+ */
+size_t spec_verify_filtered_workspace_bytes(int32_t batch, int64_t n_target_rows, int64_t vocab,
+                                            int32_t dtype);
+sv_status spec_verify_filtered(const void *target_logits, const void *draft_logits, int32_t dtype,
+                               int64_t vocab, int32_t batch, int64_t n_target_rows,
+                               const int32_t *draft_tokens, const float *uniforms,
+                               const float *temperature, const int32_t *gamma_per_row,
+                               int32_t gamma_uniform, const int32_t *top_k, const float *top_p,
+                               int32_t *n_accepted, int32_t *emitted_tokens, const sv_diag *diag,
+                               void *workspace, size_t workspace_bytes, void *hip_stream);
+
 /* Static, human-readable name of an sv_status value. */
 const char *spec_verify_strerror(int32_t status);
 

@@ -35,7 +35,8 @@ EXPORTED = ("spec_verify", "spec_verify_workspace_bytes", "spec_verify_strerror"
             "spec_verify_set_profile_events", "spec_verify_version", "spec_sample",
             "spec_sample_workspace_bytes", "spec_tree_verify_greedy",
             "spec_tree_verify_greedy_workspace_bytes", "spec_verify_early_exit",
-            "spec_verify_early_exit_workspace_bytes")
+            "spec_verify_early_exit_workspace_bytes", "spec_verify_filtered",
+            "spec_verify_filtered_workspace_bytes")
 
 
 class SpecVerifyError(RuntimeError):
@@ -80,6 +81,11 @@ def _load():
     L.spec_verify_early_exit.argtypes = [vp, vp, i32, i64, i32, i64, vp, vp, vp, vp, i32, i32, i32, vp, vp,
                                          vp, vp, ctypes.POINTER(Diag), vp, sz, vp]
     L.spec_verify_early_exit.restype = ctypes.c_int
+    L.spec_verify_filtered_workspace_bytes.argtypes = [i32, i64, i64, i32]
+    L.spec_verify_filtered_workspace_bytes.restype = sz
+    L.spec_verify_filtered.argtypes = [vp, vp, i32, i64, i32, i64, vp, vp, vp, vp, i32, vp, vp, vp, vp,
+                                       ctypes.POINTER(Diag), vp, sz, vp]
+    L.spec_verify_filtered.restype = ctypes.c_int
     return L
 
 
@@ -104,6 +110,10 @@ def sample_workspace_bytes(n: int, vocab: int, dtype: int) -> int:
 
 def early_exit_workspace_bytes(batch: int, n_target_rows: int, vocab: int, dtype: int) -> int:
     return int(lib.spec_verify_early_exit_workspace_bytes(batch, n_target_rows, vocab, dtype))
+
+
+def filtered_workspace_bytes(batch: int, n_target_rows: int, vocab: int, dtype: int) -> int:
+    return int(lib.spec_verify_filtered_workspace_bytes(batch, n_target_rows, vocab, dtype))
 
 
 def tree_workspace_bytes(n_nodes: int, vocab: int, dtype: int) -> int:
@@ -166,9 +176,20 @@ def spec_verify_early_exit(target_logits, draft_logits, draft_tokens, uniforms, 
                    gamma_max=gamma_max, cache_len=cache_len)
 
 
+def spec_verify_filtered(target_logits, draft_logits, draft_tokens, uniforms, temperature,
+                         gamma_per_row=None, *, top_k=None, top_p=None, diag: bool = False,
+                         workspace: torch.Tensor | None = None, out=None):
+    """spec_verify (sampling) with each row's top-k / top-p filter applied to both p and
+    q.  top_k: int32 [B] device tensor or None; top_p: float32 [B] device tensor or
+    None (one of the two is required)."""
+    return _verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, gamma_per_row,
+                   mode="sample", diag=diag, workspace=workspace, out=out, top_k=top_k, top_p=top_p,
+                   filtered=True)
+
+
 def _verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, gamma_per_row=None, *,
             mode="sample", diag=False, workspace=None, out=None, early_exit=False, gamma_max=None,
-            cache_len=None):
+            cache_len=None, top_k=None, top_p=None, filtered=False):
     """Verify a batch of drafted rows on the GPU.
 
     target_logits  bf16/fp32 [n_target_rows, V] (packed) or [B, gamma+1, V] (dense)
@@ -247,13 +268,28 @@ def _verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, ga
                  dg["row_status"].data_ptr())
 
     stream = torch.cuda.current_stream(device).cuda_stream
-    need = (early_exit_workspace_bytes if early_exit else workspace_bytes)(B, n_target_rows, V, dtype)
+    need = (early_exit_workspace_bytes if early_exit else
+            filtered_workspace_bytes if filtered else workspace_bytes)(B, n_target_rows, V, dtype)
     if workspace is None:
         workspace = _workspace(device, stream, need)
     elif workspace.numel() < need:
         raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
     md = SV_SAMPLE if mode == "sample" else SV_GREEDY
     dptr = ctypes.byref(d) if d is not None else None
+
+    if filtered:
+        _check(top_k, "top_k", (torch.int32,), device)
+        _check(top_p, "top_p", (torch.float32,), device)
+        for t, name in ((top_k, "top_k"), (top_p, "top_p")):
+            if t is not None and t.numel() != B:
+                raise ValueError(f"{name} must have one entry per row")
+        rc = lib.spec_verify_filtered(_ptr(target_logits), _ptr(draft_logits), dtype, V, B, n_target_rows,
+                                      _ptr(draft_tokens), _ptr(uniforms), _ptr(temperature), _ptr(gamma_t),
+                                      gamma_uniform, _ptr(top_k), _ptr(top_p), _ptr(n_acc), _ptr(emitted), dptr,
+                                      _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
+        if rc != SV_OK:
+            raise SpecVerifyError(rc, strerror(rc))
+        return (n_acc, emitted, dg) if diag else (n_acc, emitted)
 
     if not early_exit:
         rc = lib.spec_verify(_ptr(target_logits), _ptr(draft_logits), dtype, V, B, n_target_rows,

@@ -48,13 +48,14 @@ extern "C" sv_status spec_verify_set_profile_events(void *start_event, void *sto
     return SV_OK;
 }
 
-extern "C" sv_status spec_verify(const void *target_logits, const void *draft_logits, int32_t dtype,
-                                 int64_t vocab, int32_t batch, int64_t n_target_rows,
-                                 const int32_t *draft_tokens, const float *uniforms,
-                                 const float *temperature, const int32_t *gamma_per_row,
-                                 int32_t gamma_uniform, int32_t mode, int32_t *n_accepted,
-                                 int32_t *emitted_tokens, const sv_diag *diag, void *workspace,
-                                 size_t workspace_bytes, void *hip_stream)
+static sv_status verify_impl(const void *target_logits, const void *draft_logits, int32_t dtype,
+                             int64_t vocab, int32_t batch, int64_t n_target_rows,
+                             const int32_t *draft_tokens, const float *uniforms,
+                             const float *temperature, const int32_t *gamma_per_row,
+                             int32_t gamma_uniform, int32_t mode, int32_t *n_accepted,
+                             int32_t *emitted_tokens, const sv_diag *diag, void *workspace,
+                             size_t workspace_bytes, void *hip_stream, const int32_t *top_k,
+                             const float *top_p)
 {
     if (dtype != SV_BF16 && dtype != SV_F32) return SV_EDTYPE;
     if (mode != SV_SAMPLE && mode != SV_GREEDY) return SV_EINVAL;
@@ -71,7 +72,10 @@ extern "C" sv_status spec_verify(const void *target_logits, const void *draft_lo
     if (n_draft_rows > 0 && (!draft_tokens || (mode == SV_SAMPLE && !draft_logits))) return SV_EINVAL;
 
     const sv::Layout L = sv::make_layout(batch, n_target_rows, vocab, dtype);
-    if (workspace_bytes < L.total || ((uintptr_t)workspace & 255u) != 0) return SV_EWORKSPACE;
+    const bool filtered = top_k != nullptr || top_p != nullptr;
+    const size_t theta_bytes = filtered ? sv::align256(sizeof(float) * (size_t)(2 * n_target_rows - batch)) : 0;
+    if (filtered && mode != SV_SAMPLE) return SV_EINVAL;
+    if (workspace_bytes < L.total + theta_bytes || ((uintptr_t)workspace & 255u) != 0) return SV_EWORKSPACE;
 
     // 16-byte vector loads need every logit row to start 16-byte aligned
     const int64_t esz = dtype == SV_BF16 ? 2 : 4;
@@ -112,6 +116,11 @@ extern "C" sv_status spec_verify(const void *target_logits, const void *draft_lo
         P.geo.inv_t = 1.0 / ((double)gamma_uniform + 1.0);
         P.geo.inv_d = gamma_uniform > 0 ? 1.0 / (double)gamma_uniform : 0.0;
     }
+    if (filtered) {
+        P.top_k = top_k;
+        P.top_p = top_p;
+        P.theta = reinterpret_cast<float *>(ws + L.total);
+    }
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     hipError_t e = hipSuccess;
@@ -119,10 +128,48 @@ extern "C" sv_status spec_verify(const void *target_logits, const void *draft_lo
     if (e == hipSuccess && g_prof_start) e = hipEventRecord(g_prof_start, s);
     if (e == hipSuccess) e = sv::launch_stats(P, s, dtype, aligned);
     if (e == hipSuccess && g_prof_stop) e = hipEventRecord(g_prof_stop, s);
+    if (e == hipSuccess && filtered) e = sv::launch_filter(P, s, dtype, aligned);
     if (e == hipSuccess) e = sv::launch_scan(P, s, dtype);
     if (e == hipSuccess && mode == SV_SAMPLE) e = sv::launch_verify(P, s, dtype, aligned);
     if (e == hipSuccess && mode == SV_SAMPLE) e = sv::launch_draw_final(P, s, dtype, aligned);
     return e == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+extern "C" sv_status spec_verify(const void *target_logits, const void *draft_logits, int32_t dtype,
+                                 int64_t vocab, int32_t batch, int64_t n_target_rows,
+                                 const int32_t *draft_tokens, const float *uniforms,
+                                 const float *temperature, const int32_t *gamma_per_row,
+                                 int32_t gamma_uniform, int32_t mode, int32_t *n_accepted,
+                                 int32_t *emitted_tokens, const sv_diag *diag, void *workspace,
+                                 size_t workspace_bytes, void *hip_stream)
+{
+    return verify_impl(target_logits, draft_logits, dtype, vocab, batch, n_target_rows, draft_tokens, uniforms,
+                       temperature, gamma_per_row, gamma_uniform, mode, n_accepted, emitted_tokens, diag,
+                       workspace, workspace_bytes, hip_stream, nullptr, nullptr);
+}
+
+extern "C" size_t spec_verify_filtered_workspace_bytes(int32_t batch, int64_t n_target_rows, int64_t vocab,
+                                                       int32_t dtype)
+{
+    const size_t base = spec_verify_workspace_bytes(batch, n_target_rows, vocab, dtype);
+    return base == 0 ? 0 : base + sv::align256(sizeof(float) * (size_t)(2 * n_target_rows - batch));
+}
+
+// The round on filtered distributions: after the streaming pass, the vectors of rows
+// that filter get their thresholds and filtered statistics (filter_kernel); the scan
+// and the draws then see the filtered p and q.
+extern "C" sv_status spec_verify_filtered(const void *target_logits, const void *draft_logits, int32_t dtype,
+                                          int64_t vocab, int32_t batch, int64_t n_target_rows,
+                                          const int32_t *draft_tokens, const float *uniforms,
+                                          const float *temperature, const int32_t *gamma_per_row,
+                                          int32_t gamma_uniform, const int32_t *top_k, const float *top_p,
+                                          int32_t *n_accepted, int32_t *emitted_tokens, const sv_diag *diag,
+                                          void *workspace, size_t workspace_bytes, void *hip_stream)
+{
+    if (top_k == nullptr && top_p == nullptr) return SV_EINVAL;
+    return verify_impl(target_logits, draft_logits, dtype, vocab, batch, n_target_rows, draft_tokens, uniforms,
+                       temperature, gamma_per_row, gamma_uniform, SV_SAMPLE, n_accepted, emitted_tokens, diag,
+                       workspace, workspace_bytes, hip_stream, top_k, top_p);
 }
 
 extern "C" size_t spec_sample_workspace_bytes(int64_t n, int64_t vocab, int32_t dtype)

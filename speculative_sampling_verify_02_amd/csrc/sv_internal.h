@@ -81,6 +81,8 @@ struct RowDraw {           // what the draw needs about one row
     int32_t t_slot;        // emitted slot t_off + K
     double S_t, S_d;       // sums of 2^((z - m) c) at K
     float T;
+    float theta_t;         // filtering thresholds of target / draft at K (-inf: none)
+    float theta_d;
     int32_t pad;
 };
 
@@ -192,6 +194,10 @@ struct Params {
     int32_t *crop_len;        // [B] or null: cache entries to keep after it
     int32_t step;             // position being decided
     int32_t gamma_max;        // bound on gamma_i given by the caller
+    // top-k / top-p filtering of p and q
+    const int32_t *top_k;     // [B] or null
+    const float *top_p;       // [B] or null
+    float *theta;             // [nT + nD] or null: per-vector logit threshold
 };
 
 // Early-exit scratch after the verification workspace.
@@ -449,6 +455,42 @@ __device__ __forceinline__ int64_t qdiv(int64_t a, int64_t b, double inv_b)
     return q;
 }
 
+// What the pass needs about one streamed vector.
+struct VecCtx {
+    int32_t row;
+    int32_t slot;   // index of the position's draft token, -1 if none is tested there
+    int32_t x;      // that token
+    float T;
+    bool target;    // a target row (else a draft row)
+};
+
+// v: global vector index (target rows first, then draft rows)
+__device__ __forceinline__ VecCtx vec_ctx(const Params &P, int64_t v)
+{
+    VecCtx c;
+    c.target = v < P.nT;
+    if (P.gamma == nullptr) {
+        const bool target = c.target;
+        const int64_t vloc = target ? v : v - P.nT;
+        const int64_t g = P.gamma_uniform;
+        const int64_t per = target ? g + 1 : g;   // g > 0 whenever draft vectors exist
+        const int64_t row = qdiv(vloc, per, target ? P.geo.inv_t : P.geo.inv_d);
+        const int64_t j = vloc - row * per;
+        c.row = (int32_t)row;
+        c.slot = (P.mode == 0 && j < g) ? (int32_t)(row * g + j) : -1;
+        c.x = c.slot >= 0 ? P.tokens[c.slot] : -1;
+        c.T = P.mode == 0 ? P.temperature[row] : 0.0f;   // greedy calls may pass no temperatures
+    } else {
+        const VecInfo vi = P.vinfo[v];
+        c.row = vi.row;
+        c.slot = P.mode == 0 ? vi.slot : -1;
+        c.x = vi.x;
+        c.T = vi.T;
+    }
+    return c;
+}
+
+
 // --- wave64 all-reductions returning a wave-uniform value: rotations within each
 // 16-lane row (DPP row_ror 1, 2, 4, 8) leave every lane with its row's result, and
 // the four rows are combined from lanes 0, 16, 32, 48 ---
@@ -521,5 +563,6 @@ hipError_t launch_tree(const TreeParams &T, hipStream_t s);
 hipError_t launch_stats_list(const Params &P, hipStream_t s, int dtype, bool aligned);
 hipError_t launch_ee_init(const Params &P, hipStream_t s);
 hipError_t launch_ee_step(const Params &P, hipStream_t s, int dtype);
+hipError_t launch_filter(const Params &P, hipStream_t s, int dtype, bool aligned);
 
 }  // namespace sv

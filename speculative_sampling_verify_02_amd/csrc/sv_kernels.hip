@@ -346,6 +346,8 @@ __device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &s
             D.m_d = kmd;
             D.S_d = kSd;
             D.T = T;
+            D.theta_t = P.theta ? P.theta[D.t_row] : -INFINITY;
+            D.theta_d = (P.theta && K < g) ? P.theta[P.nT + D.d_row] : -INFINITY;
         }
         if (write) {
             for (int64_t j = lane; j <= g; j += 64) {
@@ -556,6 +558,8 @@ __global__ __launch_bounds__(64) void ee_step_kernel(Params P)
             D.m_d = md;
             D.S_d = Sd;
             D.T = T;
+            D.theta_t = -INFINITY;
+            D.theta_d = -INFINITY;
         }
         if (lane == 0) {
             P.n_accepted[row] = K;
@@ -595,30 +599,24 @@ __device__ __forceinline__ RawUnit<DT> neg_inf_unit()
 template <int DT>
 struct DrawConst;
 
-// bf16 logits: fp32 weights 2^(z c - B) F with B = m c rounded to fp32 and
-// F = 2^(B - m c) / S (the (z - m) route when |B| >= 2^20, as in the streaming pass)
+// bf16 logits: fp32 weights 2^((z - m) c) / S.  The difference z - m of two bf16
+// values is exact in fp32, so the maximum gets exactly 1 / S: a distribution that
+// keeps one token (a top-k 1 filter) has weight exactly 1 there on both models.
 template <>
 struct DrawConst<0> {
-    float c, Bt, Bd, mt, md, Ft, Fd;
-    bool slow_t, slow_d, residual;
+    float c, mt, md, Ft, Fd, tht, thd;
+    bool residual;
 
     __device__ __forceinline__ void init(const RowDraw &D)
     {
-        const TempConst tc = temp_const<0>(D.T);
-        c = tc.c_hi;
+        tht = D.theta_t;
+        thd = D.theta_d;
+        c = temp_const<0>(D.T).c_hi;
         residual = D.kind == DRAW_RESIDUAL;
         mt = D.m_t;
-        Bt = mt * c;
-        slow_t = !(fabsf(Bt) < kFastRef);
-        Ft = (float)((slow_t ? 1.0 : exp2_f64((double)Bt - (double)mt * (double)c)) / D.S_t);
+        Ft = (float)(1.0 / D.S_t);
         md = D.m_d;
-        Bd = md * c;
-        slow_d = !(fabsf(Bd) < kFastRef);
-        Fd = residual ? (float)((slow_d ? 1.0 : exp2_f64((double)Bd - (double)md * (double)c)) / D.S_d) : 0.0f;
-    }
-    __device__ __forceinline__ float unnorm(float z, float B, float m, bool slow) const
-    {
-        return hw_exp2(slow ? (z - m) * c : fmaf(z, c, -B));
+        Fd = residual ? (float)(1.0 / D.S_d) : 0.0f;
     }
     using W = float;
     // weights of one unit: w (residual or p) and p
@@ -626,39 +624,47 @@ struct DrawConst<0> {
     {
 #pragma unroll
         for (int e = 0; e < kUnitElems; ++e) {
-            const float pe = unnorm(zt[e], Bt, mt, slow_t) * Ft;
+            // logits below a filter's threshold drop out
+            const float zte = zt[e] < tht ? -INFINITY : zt[e];
+            const float zde = zd[e] < thd ? -INFINITY : zd[e];
+            const float pe = hw_exp2((zte - mt) * c) * Ft;
             float we = pe;
-            if (residual) we = fmaxf(0.0f, pe - unnorm(zd[e], Bd, md, slow_d) * Fd);
+            if (residual) we = fmaxf(0.0f, pe - hw_exp2((zde - md) * c) * Fd);
             w[e] = we;
             p[e] = pe;
         }
     }
 };
 
-// fp32 logits: fp64 weights
+// fp32 logits: fp64 weights 2^((z - m) c) / S (z - m exact in fp64)
 template <>
 struct DrawConst<1> {
     TempConst tc;
-    double Rt, Rd, Ft, Fd;
+    double mt, md, Ft, Fd;
+    float tht, thd;
     bool residual;
 
     __device__ __forceinline__ void init(const RowDraw &D)
     {
+        tht = D.theta_t;
+        thd = D.theta_d;
         tc = temp_const<1>(D.T);
         residual = D.kind == DRAW_RESIDUAL;
-        Rt = ceil((double)D.m_t * tc.c_eff);
-        Ft = exp2_f64(Rt - (double)D.m_t * tc.c_eff) / D.S_t;
-        Rd = residual ? ceil((double)D.m_d * tc.c_eff) : 0.0;
-        Fd = residual ? exp2_f64(Rd - (double)D.m_d * tc.c_eff) / D.S_d : 0.0;
+        mt = (double)D.m_t;
+        Ft = 1.0 / D.S_t;
+        md = (double)D.m_d;
+        Fd = residual ? 1.0 / D.S_d : 0.0;
     }
     using W = double;
     __device__ __forceinline__ void weights(const float *zt, const float *zd, double *w, double *p) const
     {
 #pragma unroll
         for (int e = 0; e < kUnitElems; ++e) {
-            const double pe = exp2_f64(fma((double)zt[e], tc.c_eff, -Rt)) * Ft;
+            const float zte = zt[e] < tht ? -INFINITY : zt[e];
+            const float zde = zd[e] < thd ? -INFINITY : zd[e];
+            const double pe = exp2_f64(((double)zte - mt) * tc.c_eff) * Ft;
             double we = pe;
-            if (residual) we = fmax(0.0, pe - exp2_f64(fma((double)zd[e], tc.c_eff, -Rd)) * Fd);
+            if (residual) we = fmax(0.0, pe - exp2_f64(((double)zde - md) * tc.c_eff) * Fd);
             w[e] = we;
             p[e] = pe;
         }
@@ -696,7 +702,8 @@ __device__ __forceinline__ void verify_body(const Params &P)
     const int32_t piece = (int32_t)(blockIdx.x - (int64_t)row * per_row);
     if (P.gamma != nullptr && P.hdr->status != 0) return;
     const RowDraw D = P.draws[row];
-    if (D.kind != DRAW_RESIDUAL) return;
+    // bonus draws use the streaming pass's piece sums, except when p is filtered
+    if (!(D.kind == DRAW_RESIDUAL || (P.theta && D.kind == DRAW_BONUS))) return;
     DrawConst<DT> c;
     c.init(D);
     const void *tb = vec_ptr(P.target, DT, D.t_row, P.V);
@@ -1075,7 +1082,7 @@ __global__ __launch_bounds__(kBlock) void draw_final_kernel(Params P)
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int32_t row = blockIdx.x;
     const RowDraw D = P.draws[row];
-    if (D.kind == DRAW_RESIDUAL) {
+    if (D.kind == DRAW_RESIDUAL || (P.theta && D.kind == DRAW_BONUS)) {
         if (wave == 0) draw_residual_row<DT, AL>(P, D, row, lane);
     } else if (D.kind == DRAW_BONUS) {
         draw_bonus_row<DT, AL>(P, D, row, lane, wave, s_ts);

@@ -25,41 +25,6 @@ namespace sv {
 // streaming pass
 // ===========================================================================
 
-// What the pass needs about one streamed vector.
-struct VecCtx {
-    int32_t row;
-    int32_t slot;   // index of the position's draft token, -1 if none is tested there
-    int32_t x;      // that token
-    float T;
-    bool target;    // a target row (else a draft row)
-};
-
-// v: global vector index (target rows first, then draft rows)
-__device__ __forceinline__ VecCtx vec_ctx(const Params &P, int64_t v)
-{
-    VecCtx c;
-    c.target = v < P.nT;
-    if (P.gamma == nullptr) {
-        const bool target = c.target;
-        const int64_t vloc = target ? v : v - P.nT;
-        const int64_t g = P.gamma_uniform;
-        const int64_t per = target ? g + 1 : g;   // g > 0 whenever draft vectors exist
-        const int64_t row = qdiv(vloc, per, target ? P.geo.inv_t : P.geo.inv_d);
-        const int64_t j = vloc - row * per;
-        c.row = (int32_t)row;
-        c.slot = (P.mode == 0 && j < g) ? (int32_t)(row * g + j) : -1;
-        c.x = c.slot >= 0 ? P.tokens[c.slot] : -1;
-        c.T = P.mode == 0 ? P.temperature[row] : 0.0f;   // greedy calls may pass no temperatures
-    } else {
-        const VecInfo vi = P.vinfo[v];
-        c.row = vi.row;
-        c.slot = P.mode == 0 ? vi.slot : -1;
-        c.x = vi.x;
-        c.T = vi.T;
-    }
-    return c;
-}
-
 // One half-piece as this lane holds it: load k covers bytes [1024 k + 16 l, +16) of
 // the half.
 struct ItemRaw {

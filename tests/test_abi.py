@@ -168,3 +168,24 @@ def test_early_exit_host_argument_errors(sv):
     assert call(batch=0, nT=0) == sv.SV_OK
     a = sv.early_exit_workspace_bytes(64, 384, 128256, sv.SV_BF16)
     assert a > sv.workspace_bytes(64, 384, 128256, sv.SV_BF16) and a % 256 == 0
+
+
+def test_filtered_host_argument_errors(sv):
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def call(**kw):
+        a = dict(target=1 << 20, draft=1 << 21, dtype=sv.SV_BF16, vocab=32, batch=2, nT=6, tokens=1 << 22,
+                 uniforms=1 << 23, temperature=1 << 24, gamma=None, gamma_u=2, top_k=1 << 28, top_p=None,
+                 n_acc=1 << 25, emitted=1 << 26, ws=1 << 27, ws_bytes=1 << 30)
+        a.update(kw)
+        return sv.lib.spec_verify_filtered(vp(a["target"]), vp(a["draft"]), a["dtype"], a["vocab"], a["batch"],
+                                           a["nT"], vp(a["tokens"]), vp(a["uniforms"]), vp(a["temperature"]),
+                                           vp(a["gamma"]), a["gamma_u"], vp(a["top_k"]), vp(a["top_p"]),
+                                           vp(a["n_acc"]), vp(a["emitted"]), None, vp(a["ws"]), a["ws_bytes"], None)
+    assert call(top_k=None, top_p=None) == sv.SV_EINVAL
+    assert call(dtype=3) == sv.SV_EDTYPE
+    assert call(nT=5) == sv.SV_EINVAL
+    assert call(draft=None) == sv.SV_EINVAL
+    assert call(ws_bytes=sv.workspace_bytes(2, 6, 32, sv.SV_BF16)) == sv.SV_EWORKSPACE   # no room for thresholds
+    assert call(batch=0, nT=0) == sv.SV_OK
+    assert sv.filtered_workspace_bytes(2, 6, 32, sv.SV_BF16) > sv.workspace_bytes(2, 6, 32, sv.SV_BF16)

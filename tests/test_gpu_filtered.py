@@ -1,0 +1,105 @@
+"""Verification on top-k / top-p filtered distributions (spec_verify_filtered)
+against the CPU oracle, through the C ABI."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from test_gpu_parity import SMALL
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def H():
+    import gpu_harness
+    return gpu_harness
+
+
+def filters(w, seed, kinds=("k", "p", "kp", "none", "k1")):
+    """Per-row top-k / top-p settings cycling through the given kinds."""
+    rng = np.random.default_rng(seed)
+    B, V = w.batch, w.vocab
+    k = np.zeros(B, np.int32)
+    p = np.ones(B, np.float32)
+    for i in range(B):
+        kind = kinds[i % len(kinds)]
+        if "k" in kind:
+            k[i] = 1 if kind == "k1" else int(rng.integers(1, max(2, min(V, 200))))
+        if "p" in kind:
+            p[i] = float(rng.choice([0.5, 0.8, 0.9, 0.95, 0.99]))
+    return k, p
+
+
+def run_filtered(H, w, k, p, dense=False):
+    import speculative_sampling_verify_02_amd as sv
+    d = H.to_device(w)
+    gamma = w.dense_gamma if dense else d["gamma"]
+    n, e, dg = sv.spec_verify_filtered(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temperature"],
+                                       gamma, top_k=torch.from_numpy(k).cuda(), top_p=torch.from_numpy(p).cuda(),
+                                       diag=True)
+    torch.cuda.synchronize()
+    out = dict(n_accepted=n.cpu().numpy(), emitted=e.cpu().numpy())
+    for key, v in dg.items():
+        out[key] = v.cpu().numpy()
+    return out
+
+
+def parity(H, w, k, p, dense=False):
+    _say(f"[case] filtered {w.name} B={w.batch} V={w.vocab} top_k={k[:4]} top_p={p[:4]}")
+    g = run_filtered(H, w, k, p, dense=dense)
+    ref = oracle.verify_workload(w, top_k=k, top_p=p)
+    rep = H.compare(w, g, ref)
+    _say(f"[ok] {rep}")
+    return g, ref
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_small(H, case):
+    w = workloads.small(**SMALL[case])
+    k, p = filters(w, seed=200 + case)
+    parity(H, w, k, p)
+
+
+def test_ties_and_tiny_vocabularies(H):
+    """Integer-valued logits (ties at every threshold) and V = 8."""
+    rng = np.random.default_rng(5)
+    w = workloads.small(seed=81, batch=10, vocab=3000, dtype="bf16", gamma=3)
+    tgt = workloads.to_bf16_bits(rng.integers(-4, 5, w.target.shape).astype(np.float32))
+    dft = workloads.to_bf16_bits(rng.integers(-4, 5, w.draft.shape).astype(np.float32))
+    w2 = workloads.Workload(**{**w.__dict__, "target": tgt, "draft": dft})
+    k, p = filters(w2, seed=6)
+    parity(H, w2, k, p)
+    w3 = workloads.small(seed=82, batch=8, vocab=8, dtype="bf16", gamma=[1, 2, 3, 4, 5, 6, 7, 0])
+    parity(H, w3, *filters(w3, seed=7))
+
+
+def test_top1_is_greedy(H):
+    """top_k = 1 on both models with drafts at the drafter's argmax: the greedy round."""
+    w = workloads.small(seed=83, batch=16, vocab=4096, dtype="f32", gamma=4, mode="greedy")
+    k = np.ones(w.batch, np.int32)
+    p = np.ones(w.batch, np.float32)
+    g = run_filtered(H, w.with_mode("sample"), k, p)
+    ref = oracle.verify_workload(w, mode="greedy")
+    assert np.array_equal(g["n_accepted"], ref["n_accepted"])
+    assert np.array_equal(g["emitted"], ref["emitted"])
+
+
+def test_c3_full(H):
+    """The V = 128256 bf16 batch with top-k 50 and top-p 0.9 on every row."""
+    w = workloads.c3()
+    parity(H, w, np.full(w.batch, 50, np.int32), np.full(w.batch, 0.9, np.float32), dense=True)
+
+
+def test_c3_full_top_p_only(H):
+    w = workloads.c3()
+    parity(H, w, np.zeros(w.batch, np.int32), np.full(w.batch, 0.95, np.float32), dense=True)
