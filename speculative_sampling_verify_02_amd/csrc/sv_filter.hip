@@ -12,8 +12,12 @@
 //          logit of the last group taken;
 //   theta = max(theta_k, theta_p).
 //
-// filter_kernel runs one workgroup of 1024 threads per vector whose row filters.  A
-// threshold is found by a bucket search over the logit values: 256 buckets of equal
+// filter_kernel runs one workgroup of 1024 threads per vector whose row filters.  With
+// top-k (k <= 1024) the k-th largest of the threads' maxima bounds theta_k from below;
+// the logits above that bound are gathered in LDS (usually little more than k) and
+// every later search runs there, so the vector is read twice.  Otherwise a threshold
+// is found on the vector itself.  A threshold is found by a bucket search over the
+// logit values: 256 buckets of equal
 // width over the current value range [lo, hi] take the count (top-k) or the fp64
 // probability mass (top-p, exp at the exact scale log2(e)/T) of their logits in LDS;
 // the bucket where the running total from the top reaches the target becomes the
@@ -44,7 +48,12 @@ __device__ __forceinline__ float fkey_val(uint32_t k)
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+constexpr int kMaxCand = 4096;   // logits kept in LDS by the top-k candidate path
+
 struct FilterLds {
+    float tmax[kFilterBlock];        // per-thread maxima
+    float cand[kMaxCand];            // logits at or above a lower bound of theta_k
+    uint32_t ncand;
     uint32_t cnt[kBins];
     double mass[kBins];
     uint32_t kmin[kBins], kmax[kBins];
@@ -84,9 +93,9 @@ __device__ __forceinline__ void each_logit(const void *base, int64_t V, int64_t 
 
 // The largest logit value t in [lo, hi] whose metric over {z >= t} reaches target,
 // where `above` is the metric over {z > hi} (count, or fp64 mass 2^((z - m) c64)).
-template <int DT, bool AL, bool MASS>
-__device__ float bucket_search(const void *base, int64_t V, int64_t nunits, float lo, float hi, double above,
-                               double target, float m, double c64, FilterLds &sh)
+template <bool MASS, class Src>
+__device__ float bucket_search(Src &&each, float lo, float hi, double above, double target, float m, double c64,
+                               FilterLds &sh)
 {
     const int tid = threadIdx.x, lane = tid & 63;
     for (int level = 0; level < 64; ++level) {   // each level leaves fewer distinct values
@@ -99,7 +108,7 @@ __device__ float bucket_search(const void *base, int64_t V, int64_t nunits, floa
             sh.kmax[tid] = 0u;
         }
         __syncthreads();
-        each_logit<DT, AL>(base, V, nunits, [&](float z) {
+        each([&](float z) {
             if (z >= lo && z <= hi) {
                 const float q = (hi - z) / width;   // NaN only for z == hi with width 0
                 const int d = q != q ? 0 : (q >= (float)(kBins - 1) ? kBins - 1 : (int)q);
@@ -193,6 +202,7 @@ __global__ __launch_bounds__(kFilterBlock) void filter_kernel(Params P)
             ++nfin;
         }
     });
+    const float tmx = mx;   // this thread's maximum
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         mx = fmaxf(mx, __shfl_xor(mx, o));
@@ -223,26 +233,68 @@ __global__ __launch_bounds__(kFilterBlock) void filter_kernel(Params P)
     }
     const double c64 = 1.4426950408889634 / (double)vc.T;
 
+    auto from_hbm = [&](auto &&f) { each_logit<DT, AL>(base, P.V, nunits, f); };
+    auto from_cand = [&](auto &&f) {
+        for (uint32_t i = tid; i < sh.ncand; i += kFilterBlock) f(sh.cand[i]);
+    };
     float theta = -INFINITY;
-    if (use_k && (uint64_t)k <= nfin)
-        theta = bucket_search<DT, AL, false>(base, P.V, nunits, mn, mx, 0.0, (double)k, mx, c64, sh);
-    if (use_p) {
-        const float lower = theta > -INFINITY ? theta : mn;
-        double s = 0.0;
-        each_logit<DT, AL>(base, P.V, nunits, [&](float z) {
-            if (z >= lower) s += exp2_f64(((double)z - (double)mx) * c64);
+    double S = 0.0;
+    bool in_lds = false;
+    // threads whose maximum is finite (each such maximum is a different logit)
+    const int nmax_fin = __syncthreads_count(tmx > -INFINITY);
+    if (use_k && (uint64_t)k <= nfin && k <= nmax_fin) {
+        // top-k candidates: the k-th largest of the per-thread maxima is a lower bound L
+        // of theta_k (those maxima are logits of the vector); the logits >= L, at
+        // least k of them, usually fit in LDS and every later step runs there
+        sh.tmax[tid] = tmx;
+        if (tid == 0) sh.ncand = 0u;
+        __syncthreads();
+        auto from_tmax = [&](auto &&f) { f(sh.tmax[tid]); };
+        const float L = bucket_search<false>(from_tmax, mn, mx, 0.0, (double)k, mx, c64, sh);
+        from_hbm([&](float z) {
+            if (z >= L) {
+                const uint32_t i = atomicAdd(&sh.ncand, 1u);
+                if (i < (uint32_t)kMaxCand) sh.cand[i] = z;
+            }
         });
-        const double Sk = fblock_sum(s, sh);
-        const float tpv = bucket_search<DT, AL, true>(base, P.V, nunits, lower, mx, 0.0, (double)tp * Sk, mx, c64,
-                                                      sh);
-        theta = fmaxf(theta, tpv);
+        __syncthreads();
+        in_lds = sh.ncand <= (uint32_t)kMaxCand;
     }
-    // the filtered statistics: the maximum and the exact sum over the kept logits
-    double s = 0.0;
-    each_logit<DT, AL>(base, P.V, nunits, [&](float z) {
-        if (z >= theta) s += exp2_f64(((double)z - (double)mx) * c64);
-    });
-    const double S = fblock_sum(s, sh);
+    if (in_lds) {
+        theta = bucket_search<false>(from_cand, mn, mx, 0.0, (double)k, mx, c64, sh);
+        if (use_p) {
+            const float lower = theta;
+            double s = 0.0;
+            from_cand([&](float z) {
+                if (z >= lower) s += exp2_f64(((double)z - (double)mx) * c64);
+            });
+            const double Sk = fblock_sum(s, sh);
+            theta = fmaxf(theta, bucket_search<true>(from_cand, lower, mx, 0.0, (double)tp * Sk, mx, c64, sh));
+        }
+        double s = 0.0;
+        from_cand([&](float z) {
+            if (z >= theta) s += exp2_f64(((double)z - (double)mx) * c64);
+        });
+        S = fblock_sum(s, sh);
+    } else {
+        if (use_k && (uint64_t)k <= nfin)
+            theta = bucket_search<false>(from_hbm, mn, mx, 0.0, (double)k, mx, c64, sh);
+        if (use_p) {
+            const float lower = theta > -INFINITY ? theta : mn;
+            double s = 0.0;
+            from_hbm([&](float z) {
+                if (z >= lower) s += exp2_f64(((double)z - (double)mx) * c64);
+            });
+            const double Sk = fblock_sum(s, sh);
+            theta = fmaxf(theta, bucket_search<true>(from_hbm, lower, mx, 0.0, (double)tp * Sk, mx, c64, sh));
+        }
+        // the filtered statistics: the maximum and the exact sum over the kept logits
+        double s = 0.0;
+        from_hbm([&](float z) {
+            if (z >= theta) s += exp2_f64(((double)z - (double)mx) * c64);
+        });
+        S = fblock_sum(s, sh);
+    }
     const int64_t ipv = P.geo.ipv;
     for (int64_t j = tid; j < ipv; j += kFilterBlock)
         P.parts[v * ipv + j] = j == 0 ? Partial{mx, __float_as_int(__builtin_nanf("")), S}

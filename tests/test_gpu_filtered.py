@@ -103,3 +103,18 @@ def test_c3_full(H):
 def test_c3_full_top_p_only(H):
     w = workloads.c3()
     parity(H, w, np.zeros(w.batch, np.int32), np.full(w.batch, 0.95, np.float32), dense=True)
+
+
+def test_large_k_and_crowded_tops(H):
+    """top-k above 1024 and more than 4096 logits tied at the top, beyond what the
+    kernel gathers in LDS: the thresholds come from searches over the whole vector."""
+    rng = np.random.default_rng(8)
+    w = workloads.small(seed=84, batch=6, vocab=20000, dtype="bf16", gamma=2)
+    tgt = workloads.to_bf16_bits(rng.integers(0, 2, w.target.shape).astype(np.float32))
+    dft = workloads.to_bf16_bits(rng.integers(0, 2, w.draft.shape).astype(np.float32))
+    w2 = workloads.Workload(**{**w.__dict__, "target": tgt, "draft": dft})
+    k = np.array([50, 2000, 5, 3000, 100, 1], np.int32)
+    p = np.array([1.0, 0.9, 0.5, 1.0, 0.99, 1.0], np.float32)
+    parity(H, w2, k, p)
+    w3 = workloads.small(seed=85, batch=6, vocab=20000, dtype="f32", gamma=2)
+    parity(H, w3, k, p)
