@@ -68,7 +68,9 @@ typedef enum {
 typedef enum { SV_BF16 = 0, SV_F32 = 1 } sv_dtype;
 typedef enum { SV_SAMPLE = 0, SV_GREEDY = 1 } sv_mode;
 
-/* Per-row status bits (row_status).  The first four make a row invalid. */
+/* Per-row status bits (row_status).  BAD_TOKEN, NONFINITE, BAD_GAMMA, BAD_TEMP and
+ * BAD_TREE make a row invalid, and an invalid row carries only those; Q_ZERO and
+ * ZERO_RESID describe the decisions of a valid row. */
 #define SV_ROW_BAD_TOKEN 1    /* a draft token is outside [0, vocab)                          */
 #define SV_ROW_Q_ZERO 2       /* q(x_j) == 0 at some draft position; that ratio is 1 if
                                  p(x_j) > 0, else 0 (informational)                            */

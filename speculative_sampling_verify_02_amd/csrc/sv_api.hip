@@ -125,10 +125,13 @@ static sv_status verify_impl(const void *target_logits, const void *draft_logits
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     hipError_t e = hipSuccess;
     if (gamma_per_row) e = sv::launch_prepare(P, s);
+    // filtered calls on aligned bf16 rows: one kernel reads each vector once and does
+    // both the streaming pass and the threshold search
+    const int fused_units = filtered ? sv::filter_stats_units(dtype, aligned, vocab) : 0;
     if (e == hipSuccess && g_prof_start) e = hipEventRecord(g_prof_start, s);
-    if (e == hipSuccess) e = sv::launch_stats(P, s, dtype, aligned);
+    if (e == hipSuccess) e = fused_units ? sv::launch_filter_stats(P, s, fused_units) : sv::launch_stats(P, s, dtype, aligned);
     if (e == hipSuccess && g_prof_stop) e = hipEventRecord(g_prof_stop, s);
-    if (e == hipSuccess && filtered) e = sv::launch_filter(P, s, dtype, aligned);
+    if (e == hipSuccess && filtered && !fused_units) e = sv::launch_filter(P, s, dtype, aligned);
     if (e == hipSuccess) e = sv::launch_scan(P, s, dtype);
     if (e == hipSuccess && mode == SV_SAMPLE) e = sv::launch_verify(P, s, dtype, aligned);
     if (e == hipSuccess && mode == SV_SAMPLE) e = sv::launch_draw_final(P, s, dtype, aligned);
@@ -155,9 +158,11 @@ extern "C" size_t spec_verify_filtered_workspace_bytes(int32_t batch, int64_t n_
     return base == 0 ? 0 : base + sv::align256(sizeof(float) * (size_t)(2 * n_target_rows - batch));
 }
 
-// The round on filtered distributions: after the streaming pass, the vectors of rows
-// that filter get their thresholds and filtered statistics (filter_kernel); the scan
-// and the draws then see the filtered p and q.
+// The round on filtered distributions: the vectors of rows that filter get their
+// thresholds and filtered statistics, in the same pass as every vector's statistics
+// for 16-byte-aligned bf16 rows of up to 163840 logits (filter_stats_kernel), else
+// after the streaming pass (filter_kernel); the scan and the draws then see the
+// filtered p and q.
 extern "C" sv_status spec_verify_filtered(const void *target_logits, const void *draft_logits, int32_t dtype,
                                           int64_t vocab, int32_t batch, int64_t n_target_rows,
                                           const int32_t *draft_tokens, const float *uniforms,

@@ -564,5 +564,7 @@ hipError_t launch_stats_list(const Params &P, hipStream_t s, int dtype, bool ali
 hipError_t launch_ee_init(const Params &P, hipStream_t s);
 hipError_t launch_ee_step(const Params &P, hipStream_t s, int dtype);
 hipError_t launch_filter(const Params &P, hipStream_t s, int dtype, bool aligned);
+int filter_stats_units(int dtype, bool aligned, int64_t V);
+hipError_t launch_filter_stats(const Params &P, hipStream_t s, int nu);
 
 }  // namespace sv

@@ -332,6 +332,7 @@ __device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &s
     if (wave == 0) {
         status = wave_or_int(status);
         const bool invalid = (status & ST_INVALID) != 0;
+        if (invalid) status &= ST_INVALID;   // an invalid row makes no decision to describe
         RowDraw D{};
         D.kind = DRAW_NONE;
         if (!invalid && !greedy) {
@@ -505,7 +506,7 @@ __global__ __launch_bounds__(64) void ee_step_kernel(Params P)
         }
         if (lane == 0) {
             P.n_accepted[row] = -1;
-            if (P.row_status) P.row_status[row] = status;
+            if (P.row_status) P.row_status[row] = status & ST_INVALID;
             if (P.resid) P.resid[row] = kQNaN;
             if (P.crop_len) P.crop_len[row] = -1;
         }

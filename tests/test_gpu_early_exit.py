@@ -95,6 +95,26 @@ def test_nan_after_the_rejection(H):
     assert np.all(g["row_status"][rows] == 0)
 
 
+def test_q_zero_then_nan(H):
+    """q(x) = 0 with p(x) > 0 at position 0 (kept, ratio 1), then a NaN target logit
+    at position 1: the row is invalid and reports only NONFINITE, like the full
+    round."""
+    V = 64
+    rng = np.random.default_rng(11)
+    tgt = rng.normal(0.0, 1.0, (2 * 4, V)).astype(np.float32)
+    drf = rng.normal(0.0, 1.0, (2 * 3, V)).astype(np.float32)
+    tok = np.array([5, 6, 7, 5, 6, 7], np.int32)
+    drf[0, 5] = -np.inf          # row 0, position 0: q(x) = 0
+    tgt[1, 9] = np.nan           # row 0, position 1: NaN
+    drf[3, 5] = -np.inf          # row 1, position 0: q(x) = 0, and the row stays valid
+    u = np.full(8, 0.5, np.float32)
+    w = workloads.Workload("qzero_nan", "f32", V, np.array([3, 3], np.int32), tgt, drf, tok, u,
+                           np.ones(2, np.float32))
+    g, ref = parity(H, w)
+    assert g["row_status"][0] == oracle.NONFINITE
+    assert g["row_status"][1] & oracle.Q_ZERO
+
+
 def test_c3_full(H):
     parity(H, workloads.c3(), dense=True, seed=3)
 
