@@ -29,11 +29,15 @@ PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, published
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "stats_kernel_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "speculative_sampling_verify_02_amd", "csrc", f)
                   for f in ("sv_stats.hip", "sv_internal.h")]
+# filtered calls on aligned bf16 rows of up to 163840 logits: one fused kernel
+PROFILE_TRAFFIC_FILTER = os.path.join(ROOT, "profiles", "filter_stats_kernel_traffic.json")
+FILTER_SOURCES = [os.path.join(ROOT, "speculative_sampling_verify_02_amd", "csrc", f)
+                  for f in ("sv_filter.hip", "sv_internal.h")]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -365,9 +369,11 @@ def main():
     pass2_bytes = 0
     if args.mode == "sample":
         # a rejection re-reads position K of both models; a bonus draw re-reads one
-        # 16 KB piece of p_gamma (its piece sums come from the streaming pass)
-        pass2_bytes = int(sum(2 * V * esz if K[i] < gam[i] else min(2 * 8192, V * esz)
+        # 16 KB piece of p_gamma (its piece sums come from the streaming pass), or all
+        # of p_gamma when p is filtered
+        pass2_bytes = int(sum(2 * V * esz if K[i] < gam[i] else (V * esz if filt else min(2 * 8192, V * esz))
                               for i in range(B) if K[i] >= 0))
+    fused = filt and w.dtype == "bf16" and V % 8 == 0 and V <= 163840
     small_bytes = nT * 4 * 2 + nD * 4 + B * 8
 
     if args.copy_calibration:
@@ -391,12 +397,13 @@ def main():
     achieved = stats_bytes / (stats_avg_ms * 1e-3) / 1e9
 
     traffic = None
-    if os.path.exists(PROFILE_TRAFFIC):
+    prof_path, sources = (PROFILE_TRAFFIC_FILTER, FILTER_SOURCES) if fused else (PROFILE_TRAFFIC, KERNEL_SOURCES)
+    if os.path.exists(prof_path) and not early and (fused or not filt):
         try:
-            prof = json.load(open(PROFILE_TRAFFIC))
+            prof = json.load(open(prof_path))
             key = f"{args.config}_{args.mode}"
             entry = prof.get("workloads", {}).get(key)
-            if entry and prof.get("kernel_source_hash") == kernel_source_hash():
+            if entry and prof.get("kernel_source_hash") == kernel_source_hash(sources):
                 traffic = entry["hbm_bytes_per_launch"]
         except Exception:
             traffic = None
@@ -425,7 +432,8 @@ def main():
         "hbm_frac_of_peak": total_bytes / sec_per_step / 1e9 / PEAK_HBM_GBPS,
         "bytes_per_step": {"pass1_logits": pass1_bytes, "pass2_logits": pass2_bytes, "other": small_bytes},
         "mean_accepted": float(K[K >= 0].mean()) if (K >= 0).any() else None,
-        "roofline": {"kernel": "stats_list_kernel + ee_step_kernel steps" if early else "stats_kernel",
+        "roofline": {"kernel": "stats_list_kernel + ee_step_kernel steps" if early else (
+                         "filter_stats_kernel" if fused else "stats_kernel"),
                      "bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic, "avg_launch_ms": stats_avg_ms,

@@ -12,20 +12,28 @@
 //          logit of the last group taken;
 //   theta = max(theta_k, theta_p).
 //
-// filter_kernel runs one workgroup of 1024 threads per vector whose row filters.  With
-// top-k (k <= 1024) the k-th largest of the threads' maxima bounds theta_k from below;
-// the logits above that bound are gathered in LDS (usually little more than k) and
-// every later search runs there, so the vector is read twice.  Otherwise a threshold
-// is found on the vector itself.  A threshold is found by a bucket search over the
-// logit values: 256 buckets of equal
-// width over the current value range [lo, hi] take the count (top-k) or the fp64
-// probability mass (top-p, exp at the exact scale log2(e)/T) of their logits in LDS;
-// the bucket where the running total from the top reaches the target becomes the
-// next range, narrowed to its smallest and largest logit, until one value remains.
-// Every level reads the vector once (bucket index (hi - z)/width is monotone in z,
-// so buckets are value intervals).  The vector's statistics record is then replaced
-// by the filtered one (maximum, exact sum over the kept tokens) and the logit at the
-// position's draft token is dropped when it falls below theta.
+// Both thresholds come from a radix select over keys that sort like the logits: the
+// largest key t whose metric over {key >= t} reaches a target, where the metric is
+// the count of logits (theta_k, target k) or their fp64 probability mass 2^((z - m) c)
+// at the exact scale c = log2(e)/T (theta_p, target top_p times the mass left by
+// top-k).  Each level histograms one 8-bit digit of the keys that share the digits
+// chosen so far (LDS atomics) and one wave picks the digit where the running total
+// from the top reaches the target: two levels for bf16 logits (16-bit keys), four
+// for fp32.  Since the metric over {key >= t} only changes at keys of logits, the
+// key found is a logit's.
+//
+// With top-k (k at most the number of threads holding a finite logit) a lower bound
+// L of theta_k comes from the threads' own maxima (per wave, with ballots); the
+// logits >= L, at least k of them and usually a few times k, are gathered in LDS and
+// every later select runs there, in one wave when they are at most 256 (the same
+// selects a key bit at a time, with ballots).  Otherwise the selects run over the
+// whole vector.
+//
+// filter_stats_kernel (16-byte-aligned bf16 rows of up to 163840 logits) holds the
+// vector in registers and produces the vector's statistics record, theta and the
+// logit at the position's draft token in one pass; filter_kernel runs after the
+// streaming pass otherwise, reading the vector from memory in every pass, and
+// replaces the record of each vector that filters.
 #include <float.h>
 #include <limits.h>
 
@@ -35,7 +43,8 @@ namespace sv {
 
 constexpr int kFilterBlock = 1024;
 constexpr int kFilterWaves = kFilterBlock / 64;
-constexpr int kBins = 256;
+constexpr int kBins = 256;       // one 8-bit digit
+constexpr int kMaxCand = 4096;   // logits kept in LDS by the top-k candidate path
 
 // A finite or infinite float as an unsigned key that sorts like the float.
 __device__ __forceinline__ uint32_t fkey(float x)
@@ -43,25 +52,29 @@ __device__ __forceinline__ uint32_t fkey(float x)
     const uint32_t b = __float_as_uint(x);
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
-__device__ __forceinline__ float fkey_val(uint32_t k)
+
+// The float of key t whose bits below LOW are those of a logit of the data (bf16
+// logits, LOW = 16: the low 16 bits of the float are zero).
+template <int LOW>
+__device__ __forceinline__ float key_val(uint32_t t)
 {
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+    if constexpr (LOW > 0)
+        if (!(t & 0x80000000u)) t |= (1u << LOW) - 1u;   // negative values: low key bits set
+    return __uint_as_float((t & 0x80000000u) ? (t & 0x7fffffffu) : ~t);
 }
 
-constexpr int kMaxCand = 4096;   // logits kept in LDS by the top-k candidate path
-
 struct FilterLds {
-    float tmax[kFilterBlock];        // per-thread maxima
-    float cand[kMaxCand];            // logits at or above a lower bound of theta_k
+    float cand[kMaxCand];   // logits at or above a lower bound of theta_k
     uint32_t ncand;
     uint32_t cnt[kBins];
     double mass[kBins];
-    uint32_t kmin[kBins], kmax[kBins];
     double rd[kFilterWaves];
-    float rf[kFilterWaves][2];
+    float rf[kFilterWaves];
     uint32_t ru[kFilterWaves];
-    int32_t sel;
-    double sel_above;
+    uint32_t rsel;          // radix select: key prefix so far
+    double rabove;          // and the metric above it
+    float wtheta;           // one-wave select results
+    double wS;
 };
 
 __device__ __forceinline__ double fblock_sum(double v, FilterLds &sh)
@@ -78,6 +91,19 @@ __device__ __forceinline__ double fblock_sum(double v, FilterLds &sh)
     return t;
 }
 
+// Block-wide maximum of the threads' values, NaN if any is NaN.
+__device__ __forceinline__ float block_nmax(float v, FilterLds &sh)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_umax_f32(v);
+    if (lane == 0) sh.rf[wave] = v;
+    __syncthreads();
+    float m = -INFINITY;
+    for (int w = 0; w < kFilterWaves; ++w) m = nmax(m, sh.rf[w]);
+    __syncthreads();
+    return m;
+}
+
 // Every logit of the vector through f(z), 8 per thread per step.
 template <int DT, bool AL, class F>
 __device__ __forceinline__ void each_logit(const void *base, int64_t V, int64_t nunits, F &&f)
@@ -91,189 +117,252 @@ __device__ __forceinline__ void each_logit(const void *base, int64_t V, int64_t 
     }
 }
 
-// The largest logit value t in [lo, hi] whose metric over {z >= t} reaches target,
-// where `above` is the metric over {z > hi} (count, or fp64 mass 2^((z - m) c64)).
-template <bool MASS, class Src>
-__device__ __forceinline__ float bucket_search(Src &&each, float lo, float hi, double above, double target, float m, double c64,
-                               FilterLds &sh)
+// The largest key t (bits >= LOW) whose metric over {key >= t} reaches target > 0:
+// the count of the logits `each` passes (MASS false), or the sum of their weights
+// 2^((z - m) c64) (MASS true).  The total metric must reach the target.
+template <bool MASS, int LOW, class Src>
+__device__ __forceinline__ uint32_t radix_select(Src &&each, double target, float m, double c64, FilterLds &sh)
 {
     const int tid = threadIdx.x, lane = tid & 63;
-    for (int level = 0; level < 64; ++level) {   // each level leaves fewer distinct values
-        if (!(lo < hi)) break;
-        const float width = (hi - lo) * (1.0f / kBins);
-        const float inv_w = 1.0f / width;
+    uint32_t prefix = 0u;
+    double above = 0.0;
+#pragma unroll
+    for (int shift = 24; shift >= LOW; shift -= 8) {
         if (tid < kBins) {
-            sh.cnt[tid] = 0u;
-            sh.mass[tid] = 0.0;
-            sh.kmin[tid] = 0xffffffffu;
-            sh.kmax[tid] = 0u;
+            if constexpr (MASS) sh.mass[tid] = 0.0;
+            else sh.cnt[tid] = 0u;
         }
         __syncthreads();
+        // keys whose digits above this one are the prefix's
+        const uint32_t hi_mask = shift == 24 ? 0u : ~((1u << (shift + 8)) - 1u);
         each([&](float z) __attribute__((always_inline)) {
-            if (z >= lo && z <= hi) {
-                const float q = (hi - z) * inv_w;   // NaN only for z == hi with width 0
-                const int d = q != q ? 0 : (q >= (float)(kBins - 1) ? kBins - 1 : (int)q);
-                atomicAdd(&sh.cnt[d], 1u);
+            const uint32_t key = fkey(z);
+            if ((key & hi_mask) == prefix) {
+                const int d = (int)((key >> shift) & 255u);
                 if constexpr (MASS) atomicAdd(&sh.mass[d], exp2_f64(((double)z - (double)m) * c64));
-                atomicMin(&sh.kmin[d], fkey(z));
-                atomicMax(&sh.kmax[d], fkey(z));
+                else atomicAdd(&sh.cnt[d], 1u);
             }
         });
         __syncthreads();
         if (tid < 64) {
-            // four bins per lane, in order; the first bin where the running total
-            // reaches the target (else the last non-empty one)
+            // lane l holds digits 255 - 4l down to 252 - 4l; the highest digit where
+            // the running total from the top reaches the target
             double v[4], lsum = 0.0;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int d = lane * 4 + k;
-                v[k] = MASS ? sh.mass[d] : (double)sh.cnt[d];
-                lsum += v[k];
+            for (int q = 0; q < 4; ++q) {
+                const int d = kBins - 1 - (lane * 4 + q);
+                v[q] = MASS ? sh.mass[d] : (double)sh.cnt[d];
+                lsum += v[q];
             }
             const double incl = wave_inclusive_sum(lsum, lane);
             double run = above + incl - lsum;
-            int hit = -1, lastne = -1;
-            double hit_before = 0.0, last_before = 0.0;
+            int hit = -1;
+            double hit_above = 0.0;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int d = lane * 4 + k;
-                if (hit < 0 && run + v[k] >= target && sh.cnt[d] > 0u) { hit = d; hit_before = run; }
-                if (sh.cnt[d] > 0u) { lastne = d; last_before = run; }
-                run += v[k];
+            for (int q = 0; q < 4; ++q) {
+                if (hit < 0 && run + v[q] >= target) {
+                    hit = kBins - 1 - (lane * 4 + q);
+                    hit_above = run;
+                }
+                run += v[q];
             }
             const unsigned long long hb = __ballot(hit >= 0);
-            int dsel;
-            double before;
-            if (hb) {
-                const int l = __ffsll((long long)hb) - 1;
-                dsel = __shfl(hit, l);
-                before = __shfl(hit_before, l);
-            } else {
-                const unsigned long long nb = __ballot(lastne >= 0);
-                const int l = nb ? 63 - __clzll((long long)nb) : 0;
-                dsel = nb ? __shfl(lastne, l) : 0;
-                before = nb ? __shfl(last_before, l) : above;
-            }
+            // (the total reaches the target, so some lane hits; digit 0 otherwise)
+            const int l = hb ? __ffsll((long long)hb) - 1 : 0;
+            const int d = hb ? __shfl(hit, l) : 0;
+            const double a = hb ? __shfl(hit_above, l) : above;
             if (lane == 0) {
-                sh.sel = dsel;
-                sh.sel_above = before;
+                sh.rsel = prefix | ((uint32_t)d << shift);
+                sh.rabove = a;
             }
         }
         __syncthreads();
-        const int d = sh.sel;
-        above = sh.sel_above;
-        const float nlo = fkey_val(sh.kmin[d]), nhi = fkey_val(sh.kmax[d]);
-        __syncthreads();
-        lo = nlo;
-        hi = nhi;
+        prefix = sh.rsel;
+        above = sh.rabove;
     }
-    return hi;
+    return prefix;
 }
 
-// Block-wide maximum of the threads' values, NaN if any is NaN.
-__device__ __forceinline__ float block_nmax(float v, FilterLds &sh)
+// ---------------------------------------------------------------------------
+// One-wave selects over N keys per lane (key 0: no value), a key bit at a time with
+// ballots: the same results as radix_select, without barriers or atomics.
+// ---------------------------------------------------------------------------
+// The largest t (bits >= LOW) with at least k keys >= t.
+template <int LOW, int N>
+__device__ __forceinline__ uint32_t wave_select_count(const uint32_t (&key)[N], int64_t k)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = wave_umax_f32(v);
-    if (lane == 0) sh.rf[wave][0] = v;
-    __syncthreads();
-    float m = -INFINITY;
-    for (int w = 0; w < kFilterWaves; ++w) m = nmax(m, sh.rf[w][0]);
-    __syncthreads();
-    return m;
-}
-
-// Block-wide minimum of the threads' values (no NaN among them).
-__device__ __forceinline__ float block_min(float v, FilterLds &sh)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t t = 0u;
+    for (int b = 31; b >= LOW; --b) {
+        const uint32_t c = t | (1u << b);
+        int n = 0;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
-    if (lane == 0) sh.rf[wave][1] = v;
-    __syncthreads();
-    float m = INFINITY;
-    for (int w = 0; w < kFilterWaves; ++w) m = fminf(m, sh.rf[w][1]);
-    __syncthreads();
-    return m;
+        for (int s = 0; s < N; ++s) n += __popcll(__ballot(key[s] >= c));
+        if (n >= k) t = c;
+    }
+    return t;
 }
+
+// The largest t (bits >= LOW) whose keys >= t carry a total weight >= target.
+template <int LOW, int N>
+__device__ __forceinline__ uint32_t wave_select_mass(const uint32_t (&key)[N], const double (&w)[N], double target)
+{
+    uint32_t t = 0u;
+    for (int b = 31; b >= LOW; --b) {
+        const uint32_t c = t | (1u << b);
+        double m = 0.0;
+#pragma unroll
+        for (int s = 0; s < N; ++s) m += key[s] >= c ? w[s] : 0.0;
+        if (wave_usum_f64(m) >= target) t = c;
+    }
+    return t;
+}
+
+constexpr int kWaveCand = 4;   // candidates per lane of the one-wave path (256 in all)
+
 
 // theta = max(theta_k, theta_p) of one vector whose logits are finite or -inf, with
 // maximum mx > -inf, and the fp64 sum over the kept logits of 2^((z - mx) c64).
-// `gather(f)` and `each(f)` both pass every logit of the vector to f (spread over
-// the threads, any order): the first once, to gather top-k candidates, the second
-// for the searches over the whole vector; `part_sum(lower)` is this thread's share
-// of the sum over the logits >= lower.  tmx is this thread's maximum under `gather`.
-template <class Gather, class Each, class PartSum>
-__device__ __forceinline__ void thresholds(Gather &&gather, Each &&each, PartSum &&part_sum, float tmx, float mx,
-                                           int64_t k, float tp, bool use_k, bool use_p, double c64, FilterLds &sh,
-                                           float &theta_out, double &S_out)
+// `each(f)` passes every logit of the vector to f (spread over the threads, any
+// order); `gather_ge(L, f)` passes every logit >= L; `part_sum(lower)` is this
+// thread's share of the sum over the logits >= lower.  tmx is this thread's maximum
+// under `gather_ge`.
+template <int LOW, class Each, class GatherGe, class PartSum>
+__device__ __forceinline__ void thresholds(Each &&each, GatherGe &&gather_ge, PartSum &&part_sum, float tmx,
+                                           float mx, int64_t k, float tp, bool use_k, bool use_p, double c64,
+                                           FilterLds &sh, float &theta_out, double &S_out)
 {
-    const int tid = threadIdx.x;
-    auto from_cand = [&](auto &&f) {
-        for (uint32_t i = tid; i < sh.ncand; i += kFilterBlock) f(sh.cand[i]);
-    };
-    float theta = -INFINITY;
-    double S = 0.0;
-    bool in_lds = false;
-    float L = -INFINITY;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // threads whose maximum is finite (each such maximum is a different logit)
     const int nmax_fin = __syncthreads_count(tmx > -INFINITY);
     if (use_k && k <= nmax_fin) {
-        // top-k candidates: the k-th largest of the per-thread maxima is a lower bound L
-        // of theta_k (those maxima are logits of the vector); the logits >= L, at
-        // least k of them, usually fit in LDS and every later step runs there
-        const float tlo = block_min(tmx > -INFINITY ? tmx : INFINITY, sh);
-        sh.tmax[tid] = tmx;
+        // top-k candidates, above a lower bound L of theta_k: every wave with at least
+        // m = ceil(k / 16) finite thread maxima takes its m-th largest, and L is the
+        // least of them; n such waves hold at least n m logits >= L, so L bounds
+        // theta_k from below when n m >= k (else L is the k-th largest of all thread
+        // maxima, by a block-wide select)
+        const int64_t m = (k + kFilterWaves - 1) / kFilterWaves;
         if (tid == 0) sh.ncand = 0u;
-        __syncthreads();
-        auto from_tmax = [&](auto &&f) { f(sh.tmax[tid]); };
-        L = bucket_search<false>(from_tmax, tlo, mx, 0.0, (double)k, mx, c64, sh);
-        if (tmx >= L) {   // only threads holding a logit >= L
-            gather([&](float z) __attribute__((always_inline)) {
-                if (z >= L) {
-                    const uint32_t i = atomicAdd(&sh.ncand, 1u);
-                    if (i < (uint32_t)kMaxCand) sh.cand[i] = z;
-                }
-            });
+        {
+            const uint32_t key[1] = {tmx > -INFINITY ? fkey(tmx) : 0u};
+            float Lw = INFINITY;
+            if (__popcll(__ballot(key[0] != 0u)) >= m) Lw = key_val<LOW>(wave_select_count<LOW, 1>(key, m));
+            if (lane == 0) sh.rf[wave] = Lw;
         }
         __syncthreads();
-        in_lds = sh.ncand <= (uint32_t)kMaxCand;
-    }
-    if (in_lds) {
-        theta = bucket_search<false>(from_cand, L, mx, 0.0, (double)k, mx, c64, sh);
-        if (use_p) {
-            const float lower = theta;
-            double s = 0.0;
-            from_cand([&](float z) {
-                if (z >= lower) s += exp2_f64(((double)z - (double)mx) * c64);
-            });
-            const double Sk = fblock_sum(s, sh);
-            theta = fmaxf(theta, bucket_search<true>(from_cand, lower, mx, 0.0, (double)tp * Sk, mx, c64, sh));
-        }
-        double s = 0.0;
-        from_cand([&](float z) {
-            if (z >= theta) s += exp2_f64(((double)z - (double)mx) * c64);
-        });
-        S = fblock_sum(s, sh);
-    } else {
-        // searches over the whole vector: its smallest finite logit and finite count first
-        float mn = INFINITY;
-        uint32_t nfin = 0u;
-        each([&](float z) {
-            if (z > -INFINITY) {
-                mn = fminf(mn, z);
-                ++nfin;
+        float L = INFINITY;
+        int nw = 0;
+        for (int w = 0; w < kFilterWaves; ++w) {
+            const float lw = sh.rf[w];
+            if (lw < INFINITY) {
+                L = fminf(L, lw);
+                ++nw;
             }
-        });
-        mn = block_min(mn, sh);
-        nfin = (uint32_t)fblock_sum((double)nfin, sh);
-        if (use_k && (uint64_t)k <= nfin) theta = bucket_search<false>(each, mn, mx, 0.0, (double)k, mx, c64, sh);
-        if (use_p) {
-            const float lower = theta > -INFINITY ? theta : mn;
-            const double Sk = fblock_sum(part_sum(lower), sh);
-            theta = fmaxf(theta, bucket_search<true>(each, lower, mx, 0.0, (double)tp * Sk, mx, c64, sh));
         }
-        S = fblock_sum(part_sum(theta), sh);
+        if ((int64_t)nw * m < k) {
+            auto from_tmax = [&](auto &&f) __attribute__((always_inline)) { f(tmx); };
+            L = key_val<LOW>(radix_select<false, LOW>(from_tmax, (double)k, mx, c64, sh));
+        }
+        if (tmx >= L) {   // only threads holding a logit >= L
+            gather_ge(L, [&](float z) __attribute__((always_inline)) {
+                const uint32_t i = atomicAdd(&sh.ncand, 1u);
+                if (i < (uint32_t)kMaxCand) sh.cand[i] = z;
+            });
+        }
+        __syncthreads();
+        const uint32_t ncand = sh.ncand;
+        if (ncand <= (uint32_t)(kWaveCand * 64)) {
+            // few candidates: theta_k, the masses, theta_p and the sum in one wave
+            if (wave == 0) {
+                uint32_t key[kWaveCand];
+                float z[kWaveCand];
+#pragma unroll
+                for (int s = 0; s < kWaveCand; ++s) {
+                    const uint32_t i = (uint32_t)(s * 64 + lane);
+                    z[s] = i < ncand ? sh.cand[i] : -INFINITY;
+                    key[s] = i < ncand ? fkey(z[s]) : 0u;
+                }
+                const uint32_t tk = wave_select_count<LOW, kWaveCand>(key, k);
+                double w[kWaveCand], ws = 0.0;
+#pragma unroll
+                for (int s = 0; s < kWaveCand; ++s) {
+                    w[s] = key[s] >= tk ? exp2_f64(((double)z[s] - (double)mx) * c64) : 0.0;
+                    ws += w[s];
+                }
+                const double Sk = wave_usum_f64(ws);
+                uint32_t tt = tk;
+                double St = Sk;
+                if (use_p) {
+                    const uint32_t tpk = wave_select_mass<LOW, kWaveCand>(key, w, (double)tp * Sk);
+                    if (tpk > tk) {
+                        tt = tpk;
+                        ws = 0.0;
+#pragma unroll
+                        for (int s = 0; s < kWaveCand; ++s) ws += key[s] >= tt ? w[s] : 0.0;
+                        St = wave_usum_f64(ws);
+                    }
+                }
+                if (lane == 0) {
+                    sh.wtheta = key_val<LOW>(tt);
+                    sh.wS = St;
+                }
+            }
+            __syncthreads();
+            theta_out = sh.wtheta;
+            S_out = sh.wS;
+            return;
+        }
+        if (ncand <= (uint32_t)kMaxCand) {
+            auto from_cand = [&](auto &&f) __attribute__((always_inline)) {
+                for (uint32_t i = tid; i < ncand; i += kFilterBlock) f(sh.cand[i]);
+            };
+            float theta = key_val<LOW>(radix_select<false, LOW>(from_cand, (double)k, mx, c64, sh));
+            auto cand_sum = [&](float lower) {
+                double s = 0.0;
+                from_cand([&](float z) {
+                    if (z >= lower) s += exp2_f64(((double)z - (double)mx) * c64);
+                });
+                return fblock_sum(s, sh);
+            };
+            double S = cand_sum(theta);
+            if (use_p) {
+                const float lk = theta;
+                auto kept = [&](auto &&f) __attribute__((always_inline)) {
+                    from_cand([&](float z) __attribute__((always_inline)) {
+                        if (z >= lk) f(z);
+                    });
+                };
+                const float tp_val = key_val<LOW>(radix_select<true, LOW>(kept, (double)tp * S, mx, c64, sh));
+                if (tp_val > theta) {
+                    theta = tp_val;
+                    S = cand_sum(theta);
+                }
+            }
+            theta_out = theta;
+            S_out = S;
+            return;
+        }
+    }
+    // selects over the whole vector; theta_k needs at least k finite logits
+    uint32_t nfin = 0u;
+    each([&](float z) {
+        if (z > -INFINITY) ++nfin;
+    });
+    nfin = (uint32_t)fblock_sum((double)nfin, sh);
+    float theta = -INFINITY;
+    if (use_k && (uint64_t)k <= nfin) theta = key_val<LOW>(radix_select<false, LOW>(each, (double)k, mx, c64, sh));
+    double S = fblock_sum(part_sum(theta), sh);
+    if (use_p) {
+        const float lk = theta;
+        auto kept = [&](auto &&f) {
+            each([&](float z) {
+                if (z >= lk) f(z);
+            });
+        };
+        const float tp_val = key_val<LOW>(radix_select<true, LOW>(kept, (double)tp * S, mx, c64, sh));
+        if (tp_val > theta) {
+            theta = tp_val;
+            S = fblock_sum(part_sum(theta), sh);
+        }
     }
     theta_out = theta;
     S_out = S;
@@ -321,6 +410,11 @@ __global__ __launch_bounds__(kFilterBlock) void filter_kernel(Params P)
     }
     const double c64 = kLog2e / (double)vc.T;
     auto from_hbm = [&](auto &&f) { each_logit<DT, AL>(base, P.V, nunits, f); };
+    auto gather_ge = [&](float L, auto &&f) {
+        from_hbm([&](float z) {
+            if (z >= L) f(z);
+        });
+    };
     auto part_sum = [&](float lower) {
         double s = 0.0;
         from_hbm([&](float z) {
@@ -330,7 +424,7 @@ __global__ __launch_bounds__(kFilterBlock) void filter_kernel(Params P)
     };
     float theta;
     double S;
-    thresholds(from_hbm, from_hbm, part_sum, tmx, mx, k, tp, use_k, use_p, c64, sh, theta, S);
+    thresholds<DT == 0 ? 16 : 0>(from_hbm, gather_ge, part_sum, tmx, mx, k, tp, use_k, use_p, c64, sh, theta, S);
     write_records(P, v, Partial{mx, __float_as_int(__builtin_nanf("")), S});
     if (tid == 0) {
         P.theta[v] = theta;
@@ -385,10 +479,17 @@ __global__ __launch_bounds__(kFilterBlock) void filter_stats_kernel(Params P)
         r[i] = in ? make_uint4(w[0], w[1], w[2], w[3]) : make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
     }
     if (P.gamma != nullptr && P.hdr->status != 0) return;
-    const VecCtx vc = vec_ctx(P, v);
+    // the vector's context, the same on every thread: kept in scalar registers
+    VecCtx vc = vec_ctx(P, v);
+    vc.row = __builtin_amdgcn_readfirstlane(vc.row);
+    vc.slot = __builtin_amdgcn_readfirstlane(vc.slot);
+    vc.x = __builtin_amdgcn_readfirstlane(vc.x);
+    vc.T = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vc.T)));
     const bool has_x = vc.slot >= 0 && vc.x >= 0 && (int64_t)vc.x < P.V;
     const float zx = (tid == 0 && has_x) ? load_logit<0>(base, vc.x) : -INFINITY;
     const int32_t rm = row_mode(P.mode, vc.T);
+    const int64_t k = __builtin_amdgcn_readfirstlane(P.top_k ? P.top_k[vc.row] : 0);
+    const float tp = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(P.top_p ? P.top_p[vc.row] : 1.0f)));
 
     // f(z, i) for every logit z of this thread, i its index in the vector
     auto each_idx = [&](auto &&f) __attribute__((always_inline)) {
@@ -408,9 +509,26 @@ __global__ __launch_bounds__(kFilterBlock) void filter_stats_kernel(Params P)
         each_idx([&](float z, int32_t) __attribute__((always_inline)) { f(z); });
     };
 
-    // the maximum, NaN if any logit is
+    // the maximum, NaN if any logit is, and (up to 16 units per thread, where the
+    // registers allow) the maximum of every unit (bf16 values, two to a register) for
+    // the top-k gather
+    constexpr bool kKeepUnitMax = NU <= 16;
     float tmx = -INFINITY;
-    each([&](float z) __attribute__((always_inline)) { tmx = nmax(tmx, z); });
+    uint32_t um2[(NU + 1) / 2];
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+        uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+        opaque(w);
+        float um = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) um = nmax(um, nmax(bf16_lo(w[t]), bf16_hi(w[t])));
+        tmx = nmax(tmx, um);
+        if constexpr (kKeepUnitMax) {
+            const uint32_t ub = __float_as_uint(um) >> 16;
+            if (i & 1) um2[i / 2] |= ub << 16;
+            else um2[i / 2] = ub;
+        }
+    }
     const float mx = block_nmax(tmx, sh);
 
     if (rm != ROW_SAMPLE) {
@@ -448,14 +566,35 @@ __global__ __launch_bounds__(kFilterBlock) void filter_stats_kernel(Params P)
     } else {
         const double c64 = kLog2e / (double)vc.T;
         const float c32 = (float)c64;
-        const int64_t k = P.top_k ? P.top_k[vc.row] : 0;
-        const float tp = P.top_p ? P.top_p[vc.row] : 1.0f;
         const bool use_k = k > 0 && k < P.V, use_p = tp > 0.0f && tp < 1.0f;
         double S;
         if (use_k || use_p) {
-            // searches that do not run on top-k candidates in LDS read the vector from
-            // memory again, in fp64 like filter_kernel (the vector's registers are
-            // free by then)
+            // the candidates come from the registers, a unit at a time (units whose
+            // maximum is below L are skipped); selects that do not run on candidates
+            // in LDS read the vector from memory again, in fp64 like filter_kernel
+            auto gather_ge = [&](float L, auto &&f) __attribute__((always_inline)) {
+#pragma unroll
+                for (int i = 0; i < NU; ++i) {
+                    uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+                    opaque(w);
+                    float um;
+                    if constexpr (kKeepUnitMax) {
+                        um = (i & 1) ? bf16_hi(um2[i / 2]) : bf16_lo(um2[i / 2]);
+                    } else {
+                        um = -INFINITY;
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) um = fmaxf(um, fmaxf(bf16_lo(w[t]), bf16_hi(w[t])));
+                    }
+                    if (um >= L) {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const float zl = bf16_lo(w[t]), zh = bf16_hi(w[t]);
+                            if (zl >= L) f(zl);
+                            if (zh >= L) f(zh);
+                        }
+                    }
+                }
+            };
             auto from_hbm = [&](auto &&f) { each_logit<0, true>(base, P.V, nunits, f); };
             auto part_sum = [&](float lower) {
                 double s = 0.0;
@@ -464,7 +603,7 @@ __global__ __launch_bounds__(kFilterBlock) void filter_stats_kernel(Params P)
                 });
                 return s;
             };
-            thresholds(each, from_hbm, part_sum, tmx, mx, k, tp, use_k, use_p, c64, sh, theta, S);
+            thresholds<16>(from_hbm, gather_ge, part_sum, tmx, mx, k, tp, use_k, use_p, c64, sh, theta, S);
         } else {
             // this thread's sum over all logits: fp32 per unit, fp64 across units
             double s = 0.0;

@@ -118,6 +118,16 @@ def test_large_k_and_crowded_tops(H):
     parity(H, w2, k, p)
     w3 = workloads.small(seed=85, batch=6, vocab=20000, dtype="f32", gamma=2)
     parity(H, w3, k, p)
+    # about 2000 logits tied at the top: more candidates than one wave selects from,
+    # few enough for the searches in LDS
+    for dt, seed in (("bf16", 86), ("f32", 87)):
+        w4 = workloads.small(seed=seed, batch=6, vocab=20000, dtype=dt, gamma=2)
+        conv = workloads.to_bf16_bits if dt == "bf16" else (lambda a: a)
+        t4 = conv(rng.integers(0, 10, w4.target.shape).astype(np.float32))
+        d4 = conv(rng.integers(0, 10, w4.draft.shape).astype(np.float32))
+        w4 = workloads.Workload(**{**w4.__dict__, "target": t4, "draft": d4})
+        parity(H, w4, np.array([300, 1000, 7, 1024, 50, 2], np.int32),
+               np.array([0.9, 1.0, 0.5, 0.99, 1.0, 0.7], np.float32))
 
 
 def test_vocab_sizes_around_the_register_budget(H):
