@@ -46,6 +46,27 @@ constexpr int kFilterWaves = kFilterBlock / 64;
 constexpr int kBins = 256;       // one 8-bit digit
 constexpr int kMaxCand = 4096;   // logits kept in LDS by the top-k candidate path
 
+// The thread index as a value the compiler must take as new at every call: what the
+// helpers derive from it (lane, wave, LDS offsets) is recomputed where used, not kept
+// in registers across the loop of filter_stats_kernel.
+__device__ __forceinline__ int tid_now()
+{
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
+// 2^x in fp64 (exp2_f64) with the series' coefficients read from constant memory:
+// scalar registers, rather than vector registers held across the loop of
+// filter_stats_kernel.
+static __constant__ double kExp2Table[14] = {kExp2Coef[0], kExp2Coef[1], kExp2Coef[2],  kExp2Coef[3],  kExp2Coef[4],
+                                             kExp2Coef[5], kExp2Coef[6], kExp2Coef[7],  kExp2Coef[8],  kExp2Coef[9],
+                                             kExp2Coef[10], kExp2Coef[11], kExp2Coef[12], kExp2Coef[13]};
+__device__ __forceinline__ double fexp2(double x)
+{
+    return exp2_f64_by(x, [](int j) { return kExp2Table[j]; });
+}
+
 // A finite or infinite float as an unsigned key that sorts like the float.
 __device__ __forceinline__ uint32_t fkey(float x)
 {
@@ -79,7 +100,7 @@ struct FilterLds {
 
 __device__ __forceinline__ double fblock_sum(double v, FilterLds &sh)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = tid_now(), lane = tid & 63, wave = tid >> 6;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
     __syncthreads();
@@ -94,7 +115,7 @@ __device__ __forceinline__ double fblock_sum(double v, FilterLds &sh)
 // Block-wide maximum of the threads' values, NaN if any is NaN.
 __device__ __forceinline__ float block_nmax(float v, FilterLds &sh)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = tid_now(), lane = tid & 63, wave = tid >> 6;
     v = wave_umax_f32(v);
     if (lane == 0) sh.rf[wave] = v;
     __syncthreads();
@@ -108,7 +129,7 @@ __device__ __forceinline__ float block_nmax(float v, FilterLds &sh)
 template <int DT, bool AL, class F>
 __device__ __forceinline__ void each_logit(const void *base, int64_t V, int64_t nunits, F &&f)
 {
-    for (int64_t u = threadIdx.x; u < nunits; u += kFilterBlock) {
+    for (int64_t u = tid_now(); u < nunits; u += kFilterBlock) {
         const RawUnit<DT> r = load_raw<DT, AL>(base, u, V);
         float z[kUnitElems];
         unpack<DT>(r, z);
@@ -123,7 +144,7 @@ __device__ __forceinline__ void each_logit(const void *base, int64_t V, int64_t 
 template <bool MASS, int LOW, class Src>
 __device__ __forceinline__ uint32_t radix_select(Src &&each, double target, float m, double c64, FilterLds &sh)
 {
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = tid_now(), lane = tid & 63;
     uint32_t prefix = 0u;
     double above = 0.0;
 #pragma unroll
@@ -139,7 +160,7 @@ __device__ __forceinline__ uint32_t radix_select(Src &&each, double target, floa
             const uint32_t key = fkey(z);
             if ((key & hi_mask) == prefix) {
                 const int d = (int)((key >> shift) & 255u);
-                if constexpr (MASS) atomicAdd(&sh.mass[d], exp2_f64(((double)z - (double)m) * c64));
+                if constexpr (MASS) atomicAdd(&sh.mass[d], fexp2(((double)z - (double)m) * c64));
                 else atomicAdd(&sh.cnt[d], 1u);
             }
         });
@@ -220,95 +241,117 @@ __device__ __forceinline__ uint32_t wave_select_mass(const uint32_t (&key)[N], c
 constexpr int kWaveCand = 4;   // candidates per lane of the one-wave path (256 in all)
 
 
-// theta = max(theta_k, theta_p) of one vector whose logits are finite or -inf, with
-// maximum mx > -inf, and the fp64 sum over the kept logits of 2^((z - mx) c64).
-// `each(f)` passes every logit of the vector to f (spread over the threads, any
-// order); `gather_ge(L, f)` passes every logit >= L; `part_sum(lower)` is this
-// thread's share of the sum over the logits >= lower.  tmx is this thread's maximum
-// under `gather_ge`.
-template <int LOW, class Each, class GatherGe, class PartSum>
-__device__ __forceinline__ void thresholds(Each &&each, GatherGe &&gather_ge, PartSum &&part_sum, float tmx,
-                                           float mx, int64_t k, float tp, bool use_k, bool use_p, double c64,
-                                           FilterLds &sh, float &theta_out, double &S_out)
+// theta and the kept sum from at most 256 candidates in LDS, in one wave (the other
+// waves wait at the barrier).
+template <int LOW>
+__device__ __forceinline__ void one_wave_thresholds(uint32_t ncand, float mx, int64_t k, float tp, bool use_p,
+                                                    double c64, FilterLds &sh, float &theta_out, double &S_out)
 {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = tid_now(), lane = tid & 63, wave = tid >> 6;
+    if (wave == 0) {
+        uint32_t key[kWaveCand];
+        float z[kWaveCand];
+#pragma unroll
+        for (int s = 0; s < kWaveCand; ++s) {
+            const uint32_t i = (uint32_t)(s * 64 + lane);
+            z[s] = i < ncand ? sh.cand[i] : -INFINITY;
+            key[s] = i < ncand ? fkey(z[s]) : 0u;
+        }
+        const uint32_t tk = wave_select_count<LOW, kWaveCand>(key, k);
+        double w[kWaveCand], ws = 0.0;
+#pragma unroll
+        for (int s = 0; s < kWaveCand; ++s) {
+            w[s] = key[s] >= tk ? fexp2(((double)z[s] - (double)mx) * c64) : 0.0;
+            ws += w[s];
+        }
+        const double Sk = wave_usum_f64(ws);
+        uint32_t tt = tk;
+        double St = Sk;
+        if (use_p) {
+            const uint32_t tpk = wave_select_mass<LOW, kWaveCand>(key, w, (double)tp * Sk);
+            if (tpk > tk) {
+                tt = tpk;
+                ws = 0.0;
+#pragma unroll
+                for (int s = 0; s < kWaveCand; ++s) ws += key[s] >= tt ? w[s] : 0.0;
+                St = wave_usum_f64(ws);
+            }
+        }
+        if (lane == 0) {
+            sh.wtheta = key_val<LOW>(tt);
+            sh.wS = St;
+        }
+    }
+    __syncthreads();
+    theta_out = sh.wtheta;
+    S_out = sh.wS;
+}
+
+constexpr uint32_t kNoCand = 0xffffffffu;
+
+// Thresholds of one vector whose logits are finite or -inf, with maximum mx > -inf,
+// in two steps.  gather_candidates: with top-k, the logits of a superset of the
+// kept ones into LDS (`gather_ge(L, f)` passes every logit >= L to f, spread over the
+// threads; tmx is this thread's maximum under it); it returns their number, or
+// kNoCand when the top-k bound does not apply.
+template <int LOW, class GatherGe>
+__device__ __forceinline__ uint32_t gather_candidates(GatherGe &&gather_ge, float tmx, float mx, int64_t k,
+                                                      bool use_k, double c64, FilterLds &sh)
+{
+    const int tid = tid_now(), lane = tid & 63, wave = tid >> 6;
     // threads whose maximum is finite (each such maximum is a different logit)
     const int nmax_fin = __syncthreads_count(tmx > -INFINITY);
-    if (use_k && k <= nmax_fin) {
-        // top-k candidates, above a lower bound L of theta_k: every wave with at least
-        // m = ceil(k / 16) finite thread maxima takes its m-th largest, and L is the
-        // least of them; n such waves hold at least n m logits >= L, so L bounds
-        // theta_k from below when n m >= k (else L is the k-th largest of all thread
-        // maxima, by a block-wide select)
-        const int64_t m = (k + kFilterWaves - 1) / kFilterWaves;
-        if (tid == 0) sh.ncand = 0u;
-        {
-            const uint32_t key[1] = {tmx > -INFINITY ? fkey(tmx) : 0u};
-            float Lw = INFINITY;
-            if (__popcll(__ballot(key[0] != 0u)) >= m) Lw = key_val<LOW>(wave_select_count<LOW, 1>(key, m));
-            if (lane == 0) sh.rf[wave] = Lw;
+    if (!(use_k && k <= nmax_fin)) return kNoCand;
+    // top-k candidates, above a lower bound L of theta_k: every wave with at least
+    // m = ceil(k / 16) finite thread maxima takes its m-th largest, and L is the
+    // least of them; n such waves hold at least n m logits >= L, so L bounds theta_k
+    // from below when n m >= k (else L is the k-th largest of all thread maxima, by
+    // a block-wide select)
+    const int64_t m = (k + kFilterWaves - 1) / kFilterWaves;
+    if (tid == 0) sh.ncand = 0u;
+    {
+        const uint32_t key[1] = {tmx > -INFINITY ? fkey(tmx) : 0u};
+        float Lw = INFINITY;
+        if (__popcll(__ballot(key[0] != 0u)) >= m) Lw = key_val<LOW>(wave_select_count<LOW, 1>(key, m));
+        if (lane == 0) sh.rf[wave] = Lw;
+    }
+    __syncthreads();
+    float L = INFINITY;
+    int nw = 0;
+    for (int w = 0; w < kFilterWaves; ++w) {
+        const float lw = sh.rf[w];
+        if (lw < INFINITY) {
+            L = fminf(L, lw);
+            ++nw;
         }
-        __syncthreads();
-        float L = INFINITY;
-        int nw = 0;
-        for (int w = 0; w < kFilterWaves; ++w) {
-            const float lw = sh.rf[w];
-            if (lw < INFINITY) {
-                L = fminf(L, lw);
-                ++nw;
-            }
-        }
-        if ((int64_t)nw * m < k) {
-            auto from_tmax = [&](auto &&f) __attribute__((always_inline)) { f(tmx); };
-            L = key_val<LOW>(radix_select<false, LOW>(from_tmax, (double)k, mx, c64, sh));
-        }
-        if (tmx >= L) {   // only threads holding a logit >= L
-            gather_ge(L, [&](float z) __attribute__((always_inline)) {
-                const uint32_t i = atomicAdd(&sh.ncand, 1u);
-                if (i < (uint32_t)kMaxCand) sh.cand[i] = z;
-            });
-        }
-        __syncthreads();
-        const uint32_t ncand = sh.ncand;
+    }
+    if ((int64_t)nw * m < k) {
+        auto from_tmax = [&](auto &&f) __attribute__((always_inline)) { f(tmx); };
+        L = key_val<LOW>(radix_select<false, LOW>(from_tmax, (double)k, mx, c64, sh));
+    }
+    if (tmx >= L) {   // only threads holding a logit >= L
+        gather_ge(L, [&](float z) __attribute__((always_inline)) {
+            const uint32_t i = atomicAdd(&sh.ncand, 1u);
+            if (i < (uint32_t)kMaxCand) sh.cand[i] = z;
+        });
+    }
+    __syncthreads();
+    return sh.ncand;
+}
+
+// finish_thresholds: theta = max(theta_k, theta_p) and the fp64 sum over the kept
+// logits of 2^((z - mx) c64), from the candidates when they fit in LDS, else from the
+// whole vector (`each(f)` passes every logit to f, spread over the threads;
+// `part_sum(lower)` is this thread's share of the sum over the logits >= lower).
+template <int LOW, class Each, class PartSum>
+__device__ __forceinline__ void finish_thresholds(Each &&each, PartSum &&part_sum, uint32_t ncand, float mx,
+                                                  int64_t k, float tp, bool use_k, bool use_p, double c64,
+                                                  FilterLds &sh, float &theta_out, double &S_out)
+{
+    const int tid = tid_now(), lane = tid & 63, wave = tid >> 6;
+    if (ncand != kNoCand) {
         if (ncand <= (uint32_t)(kWaveCand * 64)) {
-            // few candidates: theta_k, the masses, theta_p and the sum in one wave
-            if (wave == 0) {
-                uint32_t key[kWaveCand];
-                float z[kWaveCand];
-#pragma unroll
-                for (int s = 0; s < kWaveCand; ++s) {
-                    const uint32_t i = (uint32_t)(s * 64 + lane);
-                    z[s] = i < ncand ? sh.cand[i] : -INFINITY;
-                    key[s] = i < ncand ? fkey(z[s]) : 0u;
-                }
-                const uint32_t tk = wave_select_count<LOW, kWaveCand>(key, k);
-                double w[kWaveCand], ws = 0.0;
-#pragma unroll
-                for (int s = 0; s < kWaveCand; ++s) {
-                    w[s] = key[s] >= tk ? exp2_f64(((double)z[s] - (double)mx) * c64) : 0.0;
-                    ws += w[s];
-                }
-                const double Sk = wave_usum_f64(ws);
-                uint32_t tt = tk;
-                double St = Sk;
-                if (use_p) {
-                    const uint32_t tpk = wave_select_mass<LOW, kWaveCand>(key, w, (double)tp * Sk);
-                    if (tpk > tk) {
-                        tt = tpk;
-                        ws = 0.0;
-#pragma unroll
-                        for (int s = 0; s < kWaveCand; ++s) ws += key[s] >= tt ? w[s] : 0.0;
-                        St = wave_usum_f64(ws);
-                    }
-                }
-                if (lane == 0) {
-                    sh.wtheta = key_val<LOW>(tt);
-                    sh.wS = St;
-                }
-            }
-            __syncthreads();
-            theta_out = sh.wtheta;
-            S_out = sh.wS;
+            one_wave_thresholds<LOW>(ncand, mx, k, tp, use_p, c64, sh, theta_out, S_out);
             return;
         }
         if (ncand <= (uint32_t)kMaxCand) {
@@ -319,7 +362,7 @@ __device__ __forceinline__ void thresholds(Each &&each, GatherGe &&gather_ge, Pa
             auto cand_sum = [&](float lower) {
                 double s = 0.0;
                 from_cand([&](float z) {
-                    if (z >= lower) s += exp2_f64(((double)z - (double)mx) * c64);
+                    if (z >= lower) s += fexp2(((double)z - (double)mx) * c64);
                 });
                 return fblock_sum(s, sh);
             };
@@ -372,7 +415,7 @@ __device__ __forceinline__ void thresholds(Each &&each, GatherGe &&gather_ge, Pa
 __device__ __forceinline__ void write_records(const Params &P, int64_t v, const Partial &rec0)
 {
     const int64_t ipv = P.geo.ipv;
-    for (int64_t j = threadIdx.x; j < ipv; j += kFilterBlock)
+    for (int64_t j = tid_now(); j < ipv; j += kFilterBlock)
         P.parts[v * ipv + j] = j == 0 ? rec0 : Partial{-INFINITY, INT32_MAX, 0.0};
 }
 
@@ -383,7 +426,7 @@ template <int DT, bool AL>
 __global__ __launch_bounds__(kFilterBlock) void filter_kernel(Params P)
 {
     __shared__ FilterLds sh;
-    const int tid = threadIdx.x;
+    const int tid = tid_now();
     const int64_t v = blockIdx.x;
     if (P.gamma != nullptr && P.hdr->status != 0) return;
     const VecCtx vc = vec_ctx(P, v);
@@ -418,13 +461,15 @@ __global__ __launch_bounds__(kFilterBlock) void filter_kernel(Params P)
     auto part_sum = [&](float lower) {
         double s = 0.0;
         from_hbm([&](float z) {
-            if (z >= lower) s += exp2_f64(((double)z - (double)mx) * c64);
+            if (z >= lower) s += fexp2(((double)z - (double)mx) * c64);
         });
         return s;
     };
     float theta;
     double S;
-    thresholds<DT == 0 ? 16 : 0>(from_hbm, gather_ge, part_sum, tmx, mx, k, tp, use_k, use_p, c64, sh, theta, S);
+    constexpr int LOW = DT == 0 ? 16 : 0;
+    const uint32_t ncand = gather_candidates<LOW>(gather_ge, tmx, mx, k, use_k, c64, sh);
+    finish_thresholds<LOW>(from_hbm, part_sum, ncand, mx, k, tp, use_k, use_p, c64, sh, theta, S);
     write_records(P, v, Partial{mx, __float_as_int(__builtin_nanf("")), S});
     if (tid == 0) {
         P.theta[v] = theta;
@@ -453,24 +498,27 @@ __device__ __forceinline__ void opaque(uint32_t (&w)[4])
     asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
 }
 
+// NU units of vector v into registers, every load unconditional (a unit past the end
+// reads the last unit); land_vector then waits for them and makes those units -inf.
 template <int NU>
-__global__ __launch_bounds__(kFilterBlock) void filter_stats_kernel(Params P)
+__device__ __forceinline__ void load_vector(const Params &P, int64_t v, int32_t nunits, uint4 (&r)[NU])
 {
-    __shared__ FilterLds sh;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t v = blockIdx.x;
     const bool target = v < P.nT;
-    const uint16_t *base =
-        static_cast<const uint16_t *>(vec_ptr(target ? P.target : P.draft, 0, target ? v : v - P.nT, P.V));
-    const int32_t nunits = (int32_t)(P.V / kUnitElems);   // aligned rows: V is a multiple of 8
-    // every load of the vector first, unconditional (a unit past the end reads the
-    // last unit and becomes -inf once loaded)
-    uint4 r[NU];
+    const uint4 *base =
+        static_cast<const uint4 *>(vec_ptr(target ? P.target : P.draft, 0, target ? v : v - P.nT, P.V));
+    // the lane's unit offsets are recomputed here on every call (32-bit, from a thread
+    // index the compiler must take as new), not kept live across the calls
+    const uint32_t tid = (uint32_t)tid_now();
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
-        const int32_t u = tid + i * kFilterBlock;
-        r[i] = reinterpret_cast<const uint4 *>(base)[u < nunits ? u : nunits - 1];
+        const uint32_t u = tid + (uint32_t)(i * kFilterBlock);
+        r[i] = base[u < (uint32_t)nunits ? u : (uint32_t)nunits - 1u];
     }
+}
+
+template <int NU>
+__device__ __forceinline__ void land_vector(int32_t nunits, uint4 (&r)[NU], int32_t tid)
+{
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
         uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
@@ -478,156 +526,202 @@ __global__ __launch_bounds__(kFilterBlock) void filter_stats_kernel(Params P)
         const bool in = tid + i * kFilterBlock < nunits;
         r[i] = in ? make_uint4(w[0], w[1], w[2], w[3]) : make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
     }
+}
+
+// One workgroup per CU takes vectors blockIdx.x, + gridDim.x, ...; the loads of its
+// next vector are issued as soon as the current one's registers are no longer read
+// (after the top-k gather, usually), so they overlap the rest of its work.
+template <int NU>
+__global__ __launch_bounds__(kFilterBlock) void filter_stats_kernel(Params P)
+{
+    __shared__ FilterLds sh;
+    const int tid = tid_now(), lane = tid & 63, wave = tid >> 6;
+    const int64_t nvec = P.nT + P.nD;
+    const int32_t nunits = (int32_t)(P.V / kUnitElems);   // aligned rows: V is a multiple of 8
+    int64_t v = blockIdx.x;
+    if (v >= nvec) return;
+    uint4 r[NU];
+    load_vector<NU>(P, v, nunits, r);
     if (P.gamma != nullptr && P.hdr->status != 0) return;
-    // the vector's context, the same on every thread: kept in scalar registers
-    VecCtx vc = vec_ctx(P, v);
-    vc.row = __builtin_amdgcn_readfirstlane(vc.row);
-    vc.slot = __builtin_amdgcn_readfirstlane(vc.slot);
-    vc.x = __builtin_amdgcn_readfirstlane(vc.x);
-    vc.T = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vc.T)));
-    const bool has_x = vc.slot >= 0 && vc.x >= 0 && (int64_t)vc.x < P.V;
-    const float zx = (tid == 0 && has_x) ? load_logit<0>(base, vc.x) : -INFINITY;
-    const int32_t rm = row_mode(P.mode, vc.T);
-    const int64_t k = __builtin_amdgcn_readfirstlane(P.top_k ? P.top_k[vc.row] : 0);
-    const float tp = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(P.top_p ? P.top_p[vc.row] : 1.0f)));
+    for (;;) {
+        const int64_t vn = v + gridDim.x;
+        const bool has_next = vn < nvec;
+        bool issued = false;   // the next vector's loads are in flight
+        // the thread index as a new value in every iteration: what derives from it is
+        // recomputed where used instead of held in registers across the loop
+        const int32_t tid = tid_now();
+        land_vector<NU>(nunits, r, tid);
+        const bool target = v < P.nT;
+        const uint16_t *base =
+            static_cast<const uint16_t *>(vec_ptr(target ? P.target : P.draft, 0, target ? v : v - P.nT, P.V));
+        // the vector's context, the same on every thread: kept in scalar registers
+        VecCtx vc = vec_ctx(P, v);
+        vc.row = __builtin_amdgcn_readfirstlane(vc.row);
+        vc.slot = __builtin_amdgcn_readfirstlane(vc.slot);
+        vc.x = __builtin_amdgcn_readfirstlane(vc.x);
+        vc.T = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vc.T)));
+        const bool has_x = vc.slot >= 0 && vc.x >= 0 && (int64_t)vc.x < P.V;
+        const float zx = (tid == 0 && has_x) ? load_logit<0>(base, vc.x) : -INFINITY;
+        const int32_t rm = row_mode(P.mode, vc.T);
+        const int64_t k = __builtin_amdgcn_readfirstlane(P.top_k ? P.top_k[vc.row] : 0);
+        const float tp =
+            __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(P.top_p ? P.top_p[vc.row] : 1.0f)));
 
-    // f(z, i) for every logit z of this thread, i its index in the vector
-    auto each_idx = [&](auto &&f) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < NU; ++i) {
-            uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
-            opaque(w);
-            const int32_t e0 = (tid + i * kFilterBlock) * kUnitElems;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                f(bf16_lo(w[t]), e0 + 2 * t);
-                f(bf16_hi(w[t]), e0 + 2 * t + 1);
-            }
-        }
-    };
-    auto each = [&](auto &&f) __attribute__((always_inline)) {
-        each_idx([&](float z, int32_t) __attribute__((always_inline)) { f(z); });
-    };
-
-    // the maximum, NaN if any logit is, and (up to 16 units per thread, where the
-    // registers allow) the maximum of every unit (bf16 values, two to a register) for
-    // the top-k gather
-    constexpr bool kKeepUnitMax = NU <= 16;
-    float tmx = -INFINITY;
-    uint32_t um2[(NU + 1) / 2];
-#pragma unroll
-    for (int i = 0; i < NU; ++i) {
-        uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
-        opaque(w);
-        float um = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) um = nmax(um, nmax(bf16_lo(w[t]), bf16_hi(w[t])));
-        tmx = nmax(tmx, um);
-        if constexpr (kKeepUnitMax) {
-            const uint32_t ub = __float_as_uint(um) >> 16;
-            if (i & 1) um2[i / 2] |= ub << 16;
-            else um2[i / 2] = ub;
-        }
-    }
-    const float mx = block_nmax(tmx, sh);
-
-    if (rm != ROW_SAMPLE) {
-        // greedy rows: the target vectors' first argmax (NaN: no index); bad
-        // temperatures: nothing
-        Partial rec{-INFINITY, INT32_MAX, 0.0};
-        if (rm == ROW_GREEDY && target) {
-            rec.m = mx;
-            if (mx > -INFINITY) {   // not NaN, not -inf
-                int32_t first = INT32_MAX;
-                if (tmx == mx) {
-                    each_idx([&](float z, int32_t i) __attribute__((always_inline)) {
-                        if (z == mx && i < first) first = i;
-                    });
-                }
-                first = wave_umin_i32(first);
-                if (lane == 0) sh.ru[wave] = (uint32_t)first;
-                __syncthreads();
-                for (int w = 0; w < kFilterWaves; ++w) first = min(first, (int32_t)sh.ru[w]);
-                rec.idx = first;
-            }
-        }
-        write_records(P, v, rec);
-        if (tid == 0) P.theta[v] = -INFINITY;
-        return;
-    }
-
-    float theta = -INFINITY;
-    Partial rec{mx, __float_as_int(__builtin_nanf("")), 0.0};
-    if (!(mx < INFINITY)) {
-        // a NaN or +inf logit: the row is reported non-finite
-        rec.s = (double)__builtin_nanf("");
-    } else if (mx == -INFINITY) {
-        rec = Partial{-INFINITY, 0, 0.0};
-    } else {
-        const double c64 = kLog2e / (double)vc.T;
-        const float c32 = (float)c64;
-        const bool use_k = k > 0 && k < P.V, use_p = tp > 0.0f && tp < 1.0f;
-        double S;
-        if (use_k || use_p) {
-            // the candidates come from the registers, a unit at a time (units whose
-            // maximum is below L are skipped); selects that do not run on candidates
-            // in LDS read the vector from memory again, in fp64 like filter_kernel
-            auto gather_ge = [&](float L, auto &&f) __attribute__((always_inline)) {
-#pragma unroll
-                for (int i = 0; i < NU; ++i) {
-                    uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
-                    opaque(w);
-                    float um;
-                    if constexpr (kKeepUnitMax) {
-                        um = (i & 1) ? bf16_hi(um2[i / 2]) : bf16_lo(um2[i / 2]);
-                    } else {
-                        um = -INFINITY;
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) um = fmaxf(um, fmaxf(bf16_lo(w[t]), bf16_hi(w[t])));
-                    }
-                    if (um >= L) {
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            const float zl = bf16_lo(w[t]), zh = bf16_hi(w[t]);
-                            if (zl >= L) f(zl);
-                            if (zh >= L) f(zh);
-                        }
-                    }
-                }
-            };
-            auto from_hbm = [&](auto &&f) { each_logit<0, true>(base, P.V, nunits, f); };
-            auto part_sum = [&](float lower) {
-                double s = 0.0;
-                from_hbm([&](float z) {
-                    if (z >= lower) s += exp2_f64(((double)z - (double)mx) * c64);
-                });
-                return s;
-            };
-            thresholds<16>(from_hbm, gather_ge, part_sum, tmx, mx, k, tp, use_k, use_p, c64, sh, theta, S);
-        } else {
-            // this thread's sum over all logits: fp32 per unit, fp64 across units
-            double s = 0.0;
+        // f(z, i) for every logit z of this thread, i its index in the vector
+        auto each_idx = [&](auto &&f) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < NU; ++i) {
                 uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
                 opaque(w);
-                float a = 0.0f;
+                const int32_t e0 = (tid + i * kFilterBlock) * kUnitElems;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    a += hw_exp2((bf16_lo(w[t]) - mx) * c32);
-                    a += hw_exp2((bf16_hi(w[t]) - mx) * c32);
+                    f(bf16_lo(w[t]), e0 + 2 * t);
+                    f(bf16_hi(w[t]), e0 + 2 * t + 1);
                 }
-                s += (double)a;
             }
-            S = fblock_sum(s, sh);
+        };
+
+        // the maximum, NaN if any logit is, and (up to 16 units per thread, where the
+        // registers allow) the maximum of every unit (bf16 values, two to a register)
+        // for the top-k gather
+        constexpr bool kKeepUnitMax = NU <= 16;
+        float tmx = -INFINITY;
+        uint32_t um2[(NU + 1) / 2];
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+            opaque(w);
+            float um = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) um = nmax(um, nmax(bf16_lo(w[t]), bf16_hi(w[t])));
+            tmx = nmax(tmx, um);
+            if constexpr (kKeepUnitMax) {
+                const uint32_t ub = __float_as_uint(um) >> 16;
+                if (i & 1) um2[i / 2] |= ub << 16;
+                else um2[i / 2] = ub;
+            }
         }
-        rec.s = S;
+        const float mx = block_nmax(tmx, sh);
+
+        float theta = -INFINITY;
+        Partial rec{-INFINITY, INT32_MAX, 0.0};
+        if (rm != ROW_SAMPLE) {
+            // greedy rows: the target vectors' first argmax (NaN: no index); bad
+            // temperatures: nothing
+            if (rm == ROW_GREEDY && target) {
+                rec.m = mx;
+                if (mx > -INFINITY) {   // not NaN, not -inf
+                    int32_t first = INT32_MAX;
+                    if (tmx == mx) {
+                        each_idx([&](float z, int32_t i) __attribute__((always_inline)) {
+                            if (z == mx && i < first) first = i;
+                        });
+                    }
+                    first = wave_umin_i32(first);
+                    if (lane == 0) sh.ru[wave] = (uint32_t)first;
+                    __syncthreads();
+                    for (int w = 0; w < kFilterWaves; ++w) first = min(first, (int32_t)sh.ru[w]);
+                    rec.idx = first;
+                }
+            }
+        } else if (!(mx < INFINITY)) {
+            // a NaN or +inf logit: the row is reported non-finite
+            rec = Partial{mx, __float_as_int(__builtin_nanf("")), (double)__builtin_nanf("")};
+        } else if (mx == -INFINITY) {
+            rec = Partial{-INFINITY, 0, 0.0};
+        } else {
+            const double c64 = kLog2e / (double)vc.T;
+            const float c32 = (float)c64;
+            const bool use_k = k > 0 && k < P.V, use_p = tp > 0.0f && tp < 1.0f;
+            double S;
+            if (use_k || use_p) {
+                // the candidates come from the registers, a unit at a time (units whose
+                // maximum is below L are skipped); selects that do not run on
+                // candidates in LDS read the vector from memory again, in fp64 like
+                // filter_kernel
+                auto gather_ge = [&](float L, auto &&f) __attribute__((always_inline)) {
+#pragma unroll
+                    for (int i = 0; i < NU; ++i) {
+                        uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+                        opaque(w);
+                        float um;
+                        if constexpr (kKeepUnitMax) {
+                            um = (i & 1) ? bf16_hi(um2[i / 2]) : bf16_lo(um2[i / 2]);
+                        } else {
+                            um = -INFINITY;
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) um = fmaxf(um, fmaxf(bf16_lo(w[t]), bf16_hi(w[t])));
+                        }
+                        if (um >= L) {
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) {
+                                const float zl = bf16_lo(w[t]), zh = bf16_hi(w[t]);
+                                if (zl >= L) f(zl);
+                                if (zh >= L) f(zh);
+                            }
+                        }
+                    }
+                };
+                auto from_hbm = [&](auto &&f) { each_logit<0, true>(base, P.V, nunits, f); };
+                auto part_sum = [&](float lower) {
+                    double s = 0.0;
+                    from_hbm([&](float z) {
+                        if (z >= lower) s += fexp2(((double)z - (double)mx) * c64);
+                    });
+                    return s;
+                };
+                const uint32_t ncand = gather_candidates<16>(gather_ge, tmx, mx, k, use_k, c64, sh);
+                if (ncand <= (uint32_t)(kWaveCand * 64)) {
+                    // the registers are free from here on: the next vector's loads go
+                    // out while one wave finishes this one
+                    if (has_next) {
+                        load_vector<NU>(P, vn, nunits, r);
+                        issued = true;
+                    }
+                    one_wave_thresholds<16>(ncand, mx, k, tp, use_p, c64, sh, theta, S);
+                } else {
+                    finish_thresholds<16>(from_hbm, part_sum, ncand, mx, k, tp, use_k, use_p, c64, sh, theta, S);
+                }
+            } else {
+                // this thread's sum over all logits: fp32 per unit, fp64 across units
+                double s = 0.0;
+#pragma unroll
+                for (int i = 0; i < NU; ++i) {
+                    uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+                    opaque(w);
+                    float a = 0.0f;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        a += hw_exp2((bf16_lo(w[t]) - mx) * c32);
+                        a += hw_exp2((bf16_hi(w[t]) - mx) * c32);
+                    }
+                    s += (double)a;
+                }
+                S = fblock_sum(s, sh);
+            }
+            rec = Partial{mx, __float_as_int(__builtin_nanf("")), S};
+        }
+        write_records(P, v, rec);
+        if (tid == 0) {
+            P.theta[v] = theta;
+            if (rm == ROW_SAMPLE && has_x) P.zx[(target ? 0 : P.nD) + vc.slot] = zx < theta ? -INFINITY : zx;
+        }
+        if (!has_next) break;
+        if (!issued) load_vector<NU>(P, vn, nunits, r);
+        v = vn;
     }
-    write_records(P, v, rec);
-    if (tid == 0) {
-        P.theta[v] = theta;
-        if (has_x) P.zx[(target ? 0 : P.nD) + vc.slot] = zx < theta ? -INFINITY : zx;
-    }
+}
+
+// Workgroups of filter_stats_kernel<nu> that fit on the current device at once.
+static int32_t filter_grid_cap(const void *fn)
+{
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kFilterBlock, 0) != hipSuccess || per_cu <= 0)
+        per_cu = 1;
+    return cus * per_cu;
 }
 
 hipError_t launch_filter(const Params &P, hipStream_t s, int dtype, bool aligned)
@@ -666,8 +760,18 @@ hipError_t launch_filter_stats(const Params &P, hipStream_t s, int nu)
     case 20: fn = (const void *)filter_stats_kernel<20>; break;
     default: return hipErrorInvalidValue;
     }
+    static int32_t cap[5][64] = {};   // per kernel variant and device
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    const int var = nu / 4 - 1;
+    int32_t grid = dev < 64 ? cap[var][dev] : 0;
+    if (grid <= 0) {
+        grid = filter_grid_cap(fn);
+        if (dev < 64) cap[var][dev] = grid;
+    }
+    const int64_t blocks = nvec < grid ? nvec : grid;
     void *args[] = {const_cast<Params *>(&P)};
-    return hipLaunchKernel(fn, dim3((unsigned)nvec), dim3(kFilterBlock), args, 0, s);
+    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kFilterBlock), args, 0, s);
 }
 
 }  // namespace sv

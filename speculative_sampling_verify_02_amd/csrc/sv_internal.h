@@ -291,29 +291,33 @@ __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2
 
 // 2^x in fp64: x = n + f with n = rint(x), |f| <= 1/2, and 2^f from its Taylor series
 // in f ln 2 to degree 13 (truncation below 5e-18 relative); NaN propagates, very
-// negative x (and -inf) give 0.
-__host__ __device__ __forceinline__ double exp2_f64(double x)
+// negative x (and -inf) give 0.  kExp2Coef holds the series' coefficients (ln 2)^j / j!,
+// highest degree first; exp2_f64_by takes them from coef(j), so a kernel can read them
+// from constant memory (scalar registers) instead of materializing them.
+constexpr double kExp2Coef[14] = {
+    0x1.816193166d0f9p-40, 0x1.c3bd650fc2986p-36, 0x1.e8cac7351bb25p-32, 0x1.e4cf5158b8ecap-28,
+    0x1.b5253d395e7c4p-24, 0x1.62c0223a5c824p-20, 0x1.ffcbfc588b0c7p-17, 0x1.430912f86c787p-13,
+    0x1.5d87fe78a6731p-10, 0x1.3b2ab6fba4e77p-7,  0x1.c6b08d704a0c0p-5,  0x1.ebfbdff82c58fp-3,
+    0x1.62e42fefa39efp-1,  1.0};
+
+template <class Coef>
+__host__ __device__ __forceinline__ double exp2_f64_by(double x, Coef &&coef)
 {
     if (x < -1100.0) x = -1100.0;
     if (x > 1100.0) x = 1100.0;
     const double n = rint(x);
     const double f = x - n;
-    double p = 0x1.816193166d0f9p-40;
-    p = fma(p, f, 0x1.c3bd650fc2986p-36);
-    p = fma(p, f, 0x1.e8cac7351bb25p-32);
-    p = fma(p, f, 0x1.e4cf5158b8ecap-28);
-    p = fma(p, f, 0x1.b5253d395e7c4p-24);
-    p = fma(p, f, 0x1.62c0223a5c824p-20);
-    p = fma(p, f, 0x1.ffcbfc588b0c7p-17);
-    p = fma(p, f, 0x1.430912f86c787p-13);
-    p = fma(p, f, 0x1.5d87fe78a6731p-10);
-    p = fma(p, f, 0x1.3b2ab6fba4e77p-7);
-    p = fma(p, f, 0x1.c6b08d704a0c0p-5);
-    p = fma(p, f, 0x1.ebfbdff82c58fp-3);
-    p = fma(p, f, 0x1.62e42fefa39efp-1);
-    p = fma(p, f, 1.0);
+    double p = coef(0);
+#pragma unroll
+    for (int j = 1; j < 14; ++j) p = fma(p, f, coef(j));
     return ldexp(p, (int)n);
 }
+
+struct Exp2Literal {
+    __host__ __device__ double operator()(int j) const { return kExp2Coef[j]; }
+};
+
+__host__ __device__ __forceinline__ double exp2_f64(double x) { return exp2_f64_by(x, Exp2Literal{}); }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
