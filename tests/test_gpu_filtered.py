@@ -100,6 +100,13 @@ def test_c3_full(H):
     parity(H, w, np.full(w.batch, 50, np.int32), np.full(w.batch, 0.9, np.float32), dense=True)
 
 
+def test_c4_full(H):
+    """The V = 152064 bf16 batch (B = 256, gamma = 8) with top-k 50 and top-p 0.9: the
+    one-pass kernel at 20 units per thread, looping over 4352 vectors."""
+    w = workloads.c4()
+    parity(H, w, np.full(w.batch, 50, np.int32), np.full(w.batch, 0.9, np.float32), dense=True)
+
+
 def test_c3_full_top_p_only(H):
     w = workloads.c3()
     parity(H, w, np.zeros(w.batch, np.int32), np.full(w.batch, 0.95, np.float32), dense=True)
@@ -181,3 +188,18 @@ def test_bad_gamma(H):
         torch.cuda.synchronize()
         assert (n.cpu().numpy() == -1).all() and (e.cpu().numpy() == -1).all()
         assert (dg["row_status"].cpu().numpy() == oracle.BAD_GAMMA).all()
+
+
+def test_many_vectors_mixed_rows(H):
+    """More vectors than workgroups, so each workgroup of the one-pass kernel takes
+    several in turn, with rows of every kind interleaved: top-k, top-p, both, neither,
+    top-k 1, greedy (T = 0), a bad temperature and a NaN logit."""
+    w = workloads.small(seed=91, batch=100, vocab=32000, dtype="bf16", gamma=4)
+    T = w.temperature.copy()
+    T[7::10] = 0.0
+    T[13] = np.nan
+    tgt = w.target.copy()
+    tgt[5 * 5 + 2, 99] = 0x7FC0                # row 5: NaN logit
+    w2 = workloads.Workload(**{**w.__dict__, "temperature": T, "target": tgt})
+    g, ref = parity(H, w2, *filters(w2, seed=12))
+    assert g["row_status"][5] & oracle.NONFINITE and g["row_status"][13] & oracle.BAD_TEMP
