@@ -398,6 +398,82 @@ __device__ __forceinline__ void unpack(const RawUnit<DT> &r, float *x)
     }
 }
 
+// The 16 bytes at byte offset `sb` (0..15) of the 32 bytes lo:hi, dword shift Q.
+template <int Q>
+__device__ __forceinline__ uint4 funnel16(const uint4 &lo, const uint4 &hi, uint32_t rb)
+{
+    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    return make_uint4(__builtin_amdgcn_alignbyte(w[Q + 1], w[Q], rb), __builtin_amdgcn_alignbyte(w[Q + 2], w[Q + 1], rb),
+                      __builtin_amdgcn_alignbyte(w[Q + 3], w[Q + 2], rb), __builtin_amdgcn_alignbyte(w[Q + 4], w[Q + 3], rb));
+}
+
+__device__ __forceinline__ uint32_t wave_next_lane(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x130, 0xf, 0xf, false);   // lane l <- lane l + 1
+}
+
+// Unit tile * 64 + lane of a row that may not start 16-byte aligned (row_base), every
+// lane of the wave taking part: aligned 16-byte loads, each clamped to the last aligned
+// 16 bytes holding a byte of the array [arr, arr + arr_bytes) (such a block lies in a
+// mapped page; what the clamp replaces lies past the row), the bytes moved into place
+// with the next lane's block, and logits at V and beyond set to -inf.
+__device__ __forceinline__ uint4 funnel16_rt(const uint4 &lo, const uint4 &hi, uint32_t sb)
+{
+    const uint32_t rb = sb & 3u;
+    switch (sb >> 2) {
+    case 0: return rb ? funnel16<0>(lo, hi, rb) : lo;
+    case 1: return funnel16<1>(lo, hi, rb);
+    case 2: return funnel16<2>(lo, hi, rb);
+    default: return funnel16<3>(lo, hi, rb);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ RawUnit<DT> load_tile_unit(const void *row_base, int64_t tile, int64_t V, const void *arr,
+                                                      uint64_t arr_bytes, int lane)
+{
+    constexpr uint64_t ub = DT == 0 ? 16u : 32u;   // bytes per unit
+    const uint64_t a = reinterpret_cast<uint64_t>(row_base) + (uint64_t)tile * 64u * ub;
+    const uint64_t a0 = a & ~(uint64_t)15;
+    const uint32_t sb = (uint32_t)__builtin_amdgcn_readfirstlane((int)(a - a0));
+    const uint64_t last = (reinterpret_cast<uint64_t>(arr) + arr_bytes - 1) & ~(uint64_t)15;
+    auto blk = [&](uint64_t q) { return *reinterpret_cast<const uint4 *>(q < last ? q : last); };
+    RawUnit<DT> r;
+    if constexpr (DT == 0) {
+        const uint4 b0 = blk(a0 + (uint64_t)lane * 16u);
+        const uint4 ext = blk(a0 + 64u * 16u);
+        uint4 nx = make_uint4(wave_next_lane(b0.x), wave_next_lane(b0.y), wave_next_lane(b0.z), wave_next_lane(b0.w));
+        if (lane == 63) nx = ext;
+        r.a = funnel16_rt(b0, nx, sb);
+    } else {
+        const uint4 b0 = blk(a0 + (uint64_t)lane * 32u), b1 = blk(a0 + (uint64_t)lane * 32u + 16u);
+        const uint4 ext = blk(a0 + 64u * 32u);
+        uint4 nx = make_uint4(wave_next_lane(b0.x), wave_next_lane(b0.y), wave_next_lane(b0.z), wave_next_lane(b0.w));
+        if (lane == 63) nx = ext;
+        r.a = __builtin_bit_cast(float4, funnel16_rt(b0, b1, sb));
+        r.b = __builtin_bit_cast(float4, funnel16_rt(b1, nx, sb));
+    }
+    // logits at V and beyond
+    const int64_t e0 = (tile * 64 + lane) * kUnitElems;
+    if (e0 + kUnitElems > V) {
+        if constexpr (DT == 0) {
+            uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                if (e0 + t >= V) w[t / 2] = (t & 1) ? ((w[t / 2] & 0xffffu) | 0xff800000u) : ((w[t / 2] & 0xffff0000u) | 0xff80u);
+            r.a = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+            float v[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                if (e0 + t >= V) v[t] = -INFINITY;
+            r.a = make_float4(v[0], v[1], v[2], v[3]);
+            r.b = make_float4(v[4], v[5], v[6], v[7]);
+        }
+    }
+    return r;
+}
+
 template <int DT>
 __device__ __forceinline__ float load_logit(const void *base, int64_t idx)
 {

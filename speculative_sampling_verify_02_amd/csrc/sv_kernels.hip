@@ -583,6 +583,12 @@ __global__ __launch_bounds__(64) void ee_step_kernel(Params P)
 // ===========================================================================
 // draw: per-tile weight sums, then the inverse CDF
 // ===========================================================================
+// Bytes of the target (or draft) logit array.
+__device__ __forceinline__ uint64_t array_bytes(const Params &P, int DT, bool target)
+{
+    return (uint64_t)(target ? P.nT : P.nD) * (uint64_t)P.V * (DT == 0 ? 2u : 4u);
+}
+
 // A unit past the end of a vector, read as -inf logits.
 template <int DT>
 __device__ __forceinline__ RawUnit<DT> neg_inf_unit()
@@ -716,8 +722,14 @@ __device__ __forceinline__ void verify_body(const Params &P)
     for (int i = 0; i < kTilesPerWave; ++i) {
         const int64_t unit = (t0 + i) * kTileUnits + lane;
         const bool in = t0 + i < P.geo.ntiles && unit < P.geo.nunits;
-        rt[i] = in ? load_raw<DT, AL>(tb, unit, P.V) : neg_inf_unit<DT>();
-        rd[i] = (in && c.residual) ? load_raw<DT, AL>(db, unit, P.V) : neg_inf_unit<DT>();
+        if constexpr (AL) {
+            rt[i] = in ? load_raw<DT, AL>(tb, unit, P.V) : neg_inf_unit<DT>();
+            rd[i] = (in && c.residual) ? load_raw<DT, AL>(db, unit, P.V) : neg_inf_unit<DT>();
+        } else {
+            rt[i] = load_tile_unit<DT>(tb, t0 + i, P.V, P.target, array_bytes(P, DT, true), lane);
+            rd[i] = c.residual ? load_tile_unit<DT>(db, t0 + i, P.V, P.draft, array_bytes(P, DT, false), lane)
+                               : neg_inf_unit<DT>();
+        }
     }
     // per-lane sums of every tile first, then one interleaved cross-lane reduction
     // (tiles past the end read -inf logits and sum to 0)
@@ -902,7 +914,8 @@ __device__ __forceinline__ void draw_bonus_row(const Params &P, const RowDraw &D
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
         const int64_t unit = (tile0 + k) * kTileUnits + lane;
-        r[k] = unit < P.geo.nunits ? load_raw<DT, AL>(tb, unit, P.V) : neg_inf_unit<DT>();
+        if constexpr (AL) r[k] = unit < P.geo.nunits ? load_raw<DT, AL>(tb, unit, P.V) : neg_inf_unit<DT>();
+        else r[k] = load_tile_unit<DT>(tb, tile0 + k, P.V, P.target, array_bytes(P, DT, true), lane);
     }
     double ls[NW], ts[NW];
 #pragma unroll
@@ -1035,8 +1048,15 @@ __device__ __forceinline__ void draw_residual_row(const Params &P, const RowDraw
         const void *db = c.residual ? vec_ptr(P.draft, DT, D.d_row, P.V) : nullptr;
         const int64_t unit = (int64_t)tile * kTileUnits + lane;
         const bool in = unit < P.geo.nunits;
-        const RawUnit<DT> rt = in ? load_raw<DT, AL>(tb, unit, P.V) : neg_inf_unit<DT>();
-        const RawUnit<DT> rd = (in && c.residual) ? load_raw<DT, AL>(db, unit, P.V) : neg_inf_unit<DT>();
+        RawUnit<DT> rt, rd;
+        if constexpr (AL) {
+            rt = in ? load_raw<DT, AL>(tb, unit, P.V) : neg_inf_unit<DT>();
+            rd = (in && c.residual) ? load_raw<DT, AL>(db, unit, P.V) : neg_inf_unit<DT>();
+        } else {
+            rt = load_tile_unit<DT>(tb, tile, P.V, P.target, array_bytes(P, DT, true), lane);
+            rd = c.residual ? load_tile_unit<DT>(db, tile, P.V, P.draft, array_bytes(P, DT, false), lane)
+                            : neg_inf_unit<DT>();
+        }
         float zt[kUnitElems], zd[kUnitElems];
         unpack<DT>(rt, zt);
         unpack<DT>(rd, zd);

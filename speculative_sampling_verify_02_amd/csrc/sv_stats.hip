@@ -26,9 +26,13 @@ namespace sv {
 // ===========================================================================
 
 // One half-piece as this lane holds it: load k covers bytes [1024 k + 16 l, +16) of
-// the half.
+// the half.  Rows that do not start 16-byte aligned are loaded from the aligned
+// address below the half's start: sb is the offset of the half's first byte there,
+// and e the aligned 16 bytes after the last load's (for lane 63 of that load).
 struct ItemRaw {
     uint4 d[kItemLoads];
+    uint4 e;
+    uint32_t sb;
 };
 
 // logits per 16-byte load
@@ -70,28 +74,58 @@ __device__ __forceinline__ void half_begin(const Params &P, int64_t v, int64_t j
             r.d[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
         }
     } else {
-        const int64_t nl = n > 0 ? n : 1;
+        // aligned 16-byte loads from the aligned address at or below the half's start,
+        // each clamped to the last aligned 16 bytes that hold a byte of the array (a
+        // 16-byte block holding a valid byte lies in a mapped page; what the clamp
+        // replaces lies past the array, hence past the row, and is masked); the bytes
+        // are moved into place by realign before the half is reduced
+        const char *arr = static_cast<const char *>(target ? P.target : P.draft);
+        const uint64_t arr_bytes = (uint64_t)(target ? P.nT : P.nD) * (uint64_t)P.V * (uint64_t)esz;
+        const uint64_t a = reinterpret_cast<uint64_t>(base);
+        const uint64_t a0 = a & ~(uint64_t)15;
+        const uint64_t last = (reinterpret_cast<uint64_t>(arr) + arr_bytes - 1) & ~(uint64_t)15;
+        r.sb = (uint32_t)__builtin_amdgcn_readfirstlane((int)(a - a0));
 #pragma unroll
         for (int k = 0; k < kItemLoads; ++k) {
-            uint32_t w[4];
-            if constexpr (DT == 0) {
-                const uint16_t *p = reinterpret_cast<const uint16_t *>(base);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int64_t e = (int64_t)k * 512 + lane * 8 + 2 * t;
-                    const int64_t e_lo = e < nl ? e : nl - 1, e_hi = e + 1 < nl ? e + 1 : nl - 1;
-                    w[t] = (uint32_t)p[e_lo] | ((uint32_t)p[e_hi] << 16);
-                }
-            } else {
-                const uint32_t *p = reinterpret_cast<const uint32_t *>(base);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int64_t e = (int64_t)k * 256 + lane * 4 + t;
-                    w[t] = p[e < nl ? e : nl - 1];
-                }
-            }
-            r.d[k] = make_uint4(w[0], w[1], w[2], w[3]);
+            uint64_t q = a0 + (uint64_t)(k * 64 + lane) * 16u;
+            q = q < last ? q : last;
+            r.d[k] = *reinterpret_cast<const uint4 *>(q);
         }
+        uint64_t qe = a0 + (uint64_t)kItemLoads * 1024u;
+        qe = qe < last ? qe : last;
+        r.e = *reinterpret_cast<const uint4 *>(qe);
+    }
+}
+
+// Moves an unaligned half's bytes into the aligned layout: lane l of load k takes the
+// 16 bytes at offset sb of its own aligned block and the next one (lane l + 1's, or
+// for lane 63 lane 0's of load k + 1, or e after the last load).
+template <int Q>
+__device__ __forceinline__ void realign_q(ItemRaw &r, int lane, uint32_t rb)
+{
+#pragma unroll
+    for (int k = 0; k < kItemLoads; ++k) {
+        uint4 nx = make_uint4(wave_next_lane(r.d[k].x), wave_next_lane(r.d[k].y), wave_next_lane(r.d[k].z),
+                              wave_next_lane(r.d[k].w));
+        const uint4 l0 = k + 1 < kItemLoads
+            ? make_uint4((uint32_t)__builtin_amdgcn_readlane((int)r.d[k + 1].x, 0),
+                         (uint32_t)__builtin_amdgcn_readlane((int)r.d[k + 1].y, 0),
+                         (uint32_t)__builtin_amdgcn_readlane((int)r.d[k + 1].z, 0),
+                         (uint32_t)__builtin_amdgcn_readlane((int)r.d[k + 1].w, 0))
+            : r.e;
+        if (lane == 63) nx = l0;
+        r.d[k] = funnel16<Q>(r.d[k], nx, rb);
+    }
+}
+
+__device__ __forceinline__ void realign(ItemRaw &r, int lane)
+{
+    const uint32_t rb = r.sb & 3u;
+    switch (r.sb >> 2) {
+    case 0: if (rb != 0) realign_q<0>(r, lane, rb); break;
+    case 1: realign_q<1>(r, lane, rb); break;
+    case 2: realign_q<2>(r, lane, rb); break;
+    default: realign_q<3>(r, lane, rb); break;
     }
 }
 
@@ -410,6 +444,7 @@ __device__ __forceinline__ void piece_half(const Params &P, const VecCtx &vc, in
                                            int64_t j, int h, int n, ItemRaw &r, PieceAcc<DT> &acc, int lane)
 {
     constexpr int E = kE<DT>;
+    if constexpr (!AL) realign(r, lane);
     if (n != (int)P.geo.ie) mask_tail<DT, AL>(r, lane, n);
     if (rm == ROW_SAMPLE) {
         if constexpr (DT == 0) {
@@ -573,9 +608,11 @@ __global__ __launch_bounds__(kStatsBlock) void stats_kernel(Params P)
     stats_body<DT, true>(P);
 }
 
-// rows read logit by logit
+// rows that do not start 16-byte aligned: aligned loads, realigned in registers; 8
+// waves per CU (the realignment needs registers of its own)
+constexpr int kStatsBlockUnaligned = 512;
 template <int DT>
-__global__ __launch_bounds__(kBlock) void stats_kernel_unaligned(Params P)
+__global__ __launch_bounds__(kStatsBlockUnaligned) void stats_kernel_unaligned(Params P)
 {
     stats_body<DT, false>(P);
 }
@@ -591,7 +628,7 @@ static hipError_t launch(const void *fn, int64_t blocks, int threads, const Para
     return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(threads), args, 0, s);
 }
 
-static int stats_block(bool aligned) { return aligned ? kStatsBlock : kBlock; }
+static int stats_block(bool aligned) { return aligned ? kStatsBlock : kStatsBlockUnaligned; }
 
 static const void *stats_fn(int dtype, bool aligned)
 {

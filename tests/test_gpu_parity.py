@@ -94,6 +94,38 @@ def test_greedy_ties(H):
     _parity(H, w, mode="greedy")
 
 
+def _offset_copy(t, elems):
+    """The same values in a buffer whose first element sits `elems` elements past an
+    allocation's start (a base address that is not 16-byte aligned)."""
+    import torch
+    flat = torch.empty(t.numel() + elems, dtype=t.dtype, device=t.device)
+    view = flat[elems:].view(t.shape)
+    view.copy_(t)
+    return view
+
+
+@pytest.mark.parametrize("vocab,dtype,gamma,offset", [
+    (128257, "bf16", [2, 0, 3, 1, 4], 0),
+    (50257, "bf16", [3, 3, 2, 0], 0),
+    (32001, "f32", [2, 1, 0], 0),
+    (8192, "bf16", [2, 3], 3),
+    (4096, "f32", [1, 2], 1),
+])
+def test_unaligned_rows(H, vocab, dtype, gamma, offset):
+    """Rows that start at every 2- or 4-byte offset within 16 bytes (vocabularies
+    that are not a multiple of 16 bytes, or a base address past an aligned one): the
+    streaming pass loads aligned blocks and moves the bytes into place."""
+    w = workloads.small(seed=60 + len(gamma), batch=len(gamma), vocab=vocab, dtype=dtype, gamma=gamma)
+    d = H.to_device(w)
+    if offset:
+        d["target"] = _offset_copy(d["target"], offset)
+        d["draft"] = _offset_copy(d["draft"], offset)
+    for mode in ("sample", "greedy"):
+        g = H.run_gpu(w, mode=mode, tensors=d)
+        ref = oracle.verify_workload(w, mode=mode)
+        H.compare(w, g, ref, mode=mode)
+
+
 def test_dense_equals_ragged(H):
     w = workloads.small(seed=41, batch=12, vocab=8192, dtype="bf16", gamma=3)
     a = H.run_gpu(w, dense=True)
