@@ -328,7 +328,8 @@ template <> struct RawUnit<0> { uint4 a; };
 template <> struct RawUnit<1> { float4 a, b; };
 
 // ALIGNED: the vector starts 16-byte aligned and holds a whole number of 16-byte
-// groups; otherwise logits are read one by one.  Logits past V read as -inf.
+// groups; otherwise logits are read one by one (load_tile_unit reads whole tiles of
+// such rows with aligned loads).  Logits past V read as -inf.
 template <int DT, bool ALIGNED>
 __device__ __forceinline__ RawUnit<DT> load_raw(const void *base, int64_t unit, int64_t V)
 {

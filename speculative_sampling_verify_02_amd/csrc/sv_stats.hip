@@ -46,11 +46,12 @@ __device__ __forceinline__ int32_t half_len(const Params &P, int64_t j, int h)
     return (int32_t)(n < 0 ? 0 : (n < P.geo.ie ? n : P.geo.ie));
 }
 
-// Issue the loads of half h of piece j of vector v.  Offsets past the end of the
-// vector are clamped to its last 16 bytes (those logits are masked when the half is
-// reduced).  An empty half, or live = false (no piece left), reads an empty window at
-// the start of the vector (nothing to read, nothing used), which keeps every load of
-// the pipeline unconditional.
+// Issue the loads of half h of piece j of vector v.  Aligned rows: offsets past the
+// end of the vector are clamped to its last 16 bytes (those logits are masked when
+// the half is reduced).  Other rows: aligned blocks from below the half's start,
+// moved into place by realign.  An empty half, or live = false (no piece left), reads
+// an empty window at the start of the vector (nothing to read, nothing used), which
+// keeps every load of the pipeline unconditional.
 template <int DT, bool AL>
 __device__ __forceinline__ void half_begin(const Params &P, int64_t v, int64_t j, int h, bool live, ItemRaw &r,
                                            int lane)
