@@ -125,16 +125,31 @@ __device__ __forceinline__ float block_nmax(float v, FilterLds &sh)
     return m;
 }
 
-// Every logit of the vector through f(z), 8 per thread per step.
+// Every logit of the vector through f(z), 8 per thread per step.  Rows that are not
+// 16-byte aligned are read a 512-logit tile per wave with aligned loads shifted into
+// place (load_tile_unit), the logits past V as -inf (arr, arr_bytes: the array the
+// row lies in).
 template <int DT, bool AL, class F>
-__device__ __forceinline__ void each_logit(const void *base, int64_t V, int64_t nunits, F &&f)
+__device__ __forceinline__ void each_logit(const void *base, int64_t V, int64_t nunits, const void *arr,
+                                           uint64_t arr_bytes, F &&f)
 {
-    for (int64_t u = tid_now(); u < nunits; u += kFilterBlock) {
-        const RawUnit<DT> r = load_raw<DT, AL>(base, u, V);
-        float z[kUnitElems];
-        unpack<DT>(r, z);
+    if constexpr (AL) {
+        for (int64_t u = tid_now(); u < nunits; u += kFilterBlock) {
+            const RawUnit<DT> r = load_raw<DT, AL>(base, u, V);
+            float z[kUnitElems];
+            unpack<DT>(r, z);
 #pragma unroll
-        for (int e = 0; e < kUnitElems; ++e) f(z[e]);
+            for (int e = 0; e < kUnitElems; ++e) f(z[e]);
+        }
+    } else {
+        const int tid = tid_now(), lane = tid & 63, wave = tid >> 6;
+        for (int64_t tile = wave; tile * kTileUnits < nunits; tile += kFilterWaves) {
+            const RawUnit<DT> r = load_tile_unit<DT>(base, tile, V, arr, arr_bytes, lane);
+            float z[kUnitElems];
+            unpack<DT>(r, z);
+#pragma unroll
+            for (int e = 0; e < kUnitElems; ++e) f(z[e]);
+        }
     }
 }
 
@@ -329,12 +344,11 @@ __device__ __forceinline__ uint32_t gather_candidates(GatherGe &&gather_ge, floa
         auto from_tmax = [&](auto &&f) __attribute__((always_inline)) { f(tmx); };
         L = key_val<LOW>(radix_select<false, LOW>(from_tmax, (double)k, mx, c64, sh));
     }
-    if (tmx >= L) {   // only threads holding a logit >= L
-        gather_ge(L, [&](float z) __attribute__((always_inline)) {
-            const uint32_t i = atomicAdd(&sh.ncand, 1u);
-            if (i < (uint32_t)kMaxCand) sh.cand[i] = z;
-        });
-    }
+    // (every thread calls gather_ge: a source may need the whole wave for its loads)
+    gather_ge(L, [&](float z) __attribute__((always_inline)) {
+        const uint32_t i = atomicAdd(&sh.ncand, 1u);
+        if (i < (uint32_t)kMaxCand) sh.cand[i] = z;
+    });
     __syncthreads();
     return sh.ncand;
 }
@@ -441,18 +455,20 @@ __global__ __launch_bounds__(kFilterBlock) void filter_kernel(Params P)
     const bool target = v < P.nT;
     const void *base = vec_ptr(target ? P.target : P.draft, DT, target ? v : v - P.nT, P.V);
     const int64_t nunits = (P.V + kUnitElems - 1) / kUnitElems;
+    const void *arr = target ? P.target : P.draft;
+    const uint64_t arr_bytes = (uint64_t)(target ? P.nT : P.nD) * (uint64_t)P.V * (DT == 0 ? 2u : 4u);
 
     // the maximum (NaN if any logit is); NaN, +inf or no finite logit leaves the
     // vector unfiltered (its row is reported non-finite)
     float tmx = -INFINITY;
-    each_logit<DT, AL>(base, P.V, nunits, [&](float z) { tmx = nmax(tmx, z); });
+    each_logit<DT, AL>(base, P.V, nunits, arr, arr_bytes, [&](float z) { tmx = nmax(tmx, z); });
     const float mx = block_nmax(tmx, sh);
     if (!(mx > -INFINITY && mx < INFINITY)) {
         if (tid == 0) P.theta[v] = -INFINITY;
         return;
     }
     const double c64 = kLog2e / (double)vc.T;
-    auto from_hbm = [&](auto &&f) { each_logit<DT, AL>(base, P.V, nunits, f); };
+    auto from_hbm = [&](auto &&f) { each_logit<DT, AL>(base, P.V, nunits, arr, arr_bytes, f); };
     auto gather_ge = [&](float L, auto &&f) {
         from_hbm([&](float z) {
             if (z >= L) f(z);
@@ -641,6 +657,7 @@ __global__ __launch_bounds__(kFilterBlock) void filter_stats_kernel(Params P)
                 // candidates in LDS read the vector from memory again, in fp64 like
                 // filter_kernel
                 auto gather_ge = [&](float L, auto &&f) __attribute__((always_inline)) {
+                    if (!(tmx >= L)) return;   // no logit of this thread reaches L
 #pragma unroll
                     for (int i = 0; i < NU; ++i) {
                         uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
@@ -663,7 +680,7 @@ __global__ __launch_bounds__(kFilterBlock) void filter_stats_kernel(Params P)
                         }
                     }
                 };
-                auto from_hbm = [&](auto &&f) { each_logit<0, true>(base, P.V, nunits, f); };
+                auto from_hbm = [&](auto &&f) { each_logit<0, true>(base, P.V, nunits, nullptr, 0, f); };
                 auto part_sum = [&](float lower) {
                     double s = 0.0;
                     from_hbm([&](float z) {

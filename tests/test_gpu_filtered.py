@@ -203,3 +203,11 @@ def test_many_vectors_mixed_rows(H):
     w2 = workloads.Workload(**{**w.__dict__, "temperature": T, "target": tgt})
     g, ref = parity(H, w2, *filters(w2, seed=12))
     assert g["row_status"][5] & oracle.NONFINITE and g["row_status"][13] & oracle.BAD_TEMP
+
+
+@pytest.mark.parametrize("vocab,dtype", [(50257, "bf16"), (32001, "f32"), (128257, "bf16")])
+def test_unaligned_vocabularies(H, vocab, dtype):
+    """Rows that do not start 16-byte aligned: the streaming pass and the threshold
+    kernel read them with aligned loads shifted into place."""
+    w = workloads.small(seed=93, batch=5, vocab=vocab, dtype=dtype, gamma=[2, 3, 0, 1, 2])
+    parity(H, w, *filters(w, seed=13))
