@@ -57,7 +57,8 @@ struct RowInfo {           // packed offsets of one row (ragged batches)
 struct Partial {           // streaming-pass result of one piece
     float m;               // max logit (NaN if the overlap holds a NaN; -inf: no finite logit)
     int32_t idx;           // greedy: first index of the max within the vector (INT32_MAX: none)
-    double s;              // sampling: sum over the overlap of 2^(z c - E(m)), E as in rec_ref
+    double s;              // sampling: sum over the piece of 2^(z c - fl(ref c_hi)) (idx holds ref), or
+                           // of 2^((z - m) c) when idx holds a NaN
 };
 
 struct VecInfo {           // one streamed vector of a ragged batch (filled by prepare_kernel)
@@ -257,8 +258,9 @@ __device__ __forceinline__ int32_t row_mode(int32_t mode, float T)
 // exp((z - m) / T) = 2^((z - m) c) with c = log2(e) / T.
 //   bf16 logits (fp32 arithmetic): c_hi = c rounded to fp32 is the scale itself (a
 //     relative change of the temperature below 2^-24), c_lo = 0, c_eff = c_hi.
-//   fp32 logits (fp64 arithmetic): c_eff = c_hi + c_lo carries c to ~2^-48, c_hi
-//     rounded down and c_lo >= FLT_MIN the fp32 remainder.
+//   fp32 logits: c_eff = c_hi + c_lo carries c to ~2^-48, c_hi rounded down and
+//     c_lo >= FLT_MIN the fp32 remainder (the streaming pass adds z c_lo with a
+//     second fma; the fp64 steps use c_eff).
 struct TempConst {
     float c_hi, c_lo;
     double c_eff;

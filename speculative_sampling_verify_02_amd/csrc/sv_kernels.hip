@@ -76,17 +76,14 @@ __global__ __launch_bounds__(1024) void prepare_kernel(Params P)
 
 // log2 of the factor that takes a record's sum to sum 2^((z - m) c) over its logits
 // (0 for records of -inf or NaN logits, and for references stored as NaN: exact m c).
+// A record's sum is taken against fl(ref c_hi); c_eff is the full scale.
 template <int DT>
 __device__ __forceinline__ double rec_shift(const Partial &q, const TempConst &tc)
 {
     if (!(q.m > -INFINITY && q.m < INFINITY)) return 0.0;
-    if constexpr (DT == 0) {
-        const float ref = __int_as_float(q.idx);
-        if (ref != ref) return 0.0;
-        return (double)(ref * tc.c_hi) - (double)q.m * tc.c_eff;
-    } else {
-        return 0.0;
-    }
+    const float ref = __int_as_float(q.idx);
+    if (ref != ref) return 0.0;
+    return (double)(ref * tc.c_hi) - (double)q.m * tc.c_eff;
 }
 
 

@@ -12,8 +12,9 @@
 // decoding", section "Why the output is exactly the target's").  The wave also keeps
 // the logit at each position's draft token when it passes through its registers.
 //
-// bf16 logits are processed in fp32 (exp2 on the hardware unit, fp64 sums across
-// lanes); fp32 logits are processed in fp64.
+// The sums are taken in fp32 (exp2 on the hardware unit, the exponent from one fma
+// for bf16 logits and two for fp32 logits, which also carry the scale's low part)
+// and added across lanes in fp64.
 #include <float.h>
 #include <limits.h>
 
@@ -240,6 +241,7 @@ __device__ __forceinline__ float exp2_split(double d)
 struct LaneSum {
     float m;      // maximum so far (NaN-propagating)
     float s;      // sum 2^(z c - E) so far (0 while m = -inf)
+    double s64;   // fp32 logits: the same sum in fp64
     float Bhi;    // fl(R c)
     float Blo;    // R c - Bhi (used when huge)
     double E;     // the reference of s
@@ -254,15 +256,26 @@ __device__ __forceinline__ void set_ref(LaneSum &a, float R, float c)
     a.E = a.huge ? (double)a.Bhi + (double)a.Blo : (double)a.Bhi;
 }
 
-// add one half (first: the piece's first half, which sets the references)
-__device__ __forceinline__ void sample_half(const ItemRaw &r, float c, LaneSum &a, bool first)
+// 2^(x c - B) for a logit x against the reference B = Bhi (+ Blo): one fma for bf16
+// logits (c is the scale itself), two for fp32 logits (the scale's low part c_lo too).
+template <int DT>
+__device__ __forceinline__ float lane_arg(float x, float c, float c_lo, float Bhi)
 {
+    const float t = fmaf(x, c, -Bhi);
+    return DT == 0 ? t : fmaf(x, c_lo, t);
+}
+
+// add one half (first: the piece's first half, which sets the references)
+template <int DT>
+__device__ __forceinline__ void sample_half(const ItemRaw &r, float c, float c_lo, LaneSum &a, bool first)
+{
+    constexpr int E = kE<DT>;
     if (first) {
-        float x[8];
-        lane_vals<0>(r, 0, x);
+        float x[E];
+        lane_vals<DT>(r, 0, x);
         float R = x[0];
 #pragma unroll
-        for (int t = 1; t < 8; ++t) R = nmax(R, x[t]);
+        for (int t = 1; t < E; ++t) R = nmax(R, x[t]);
         a.m = -INFINITY;
         a.s = 0.0f;
         set_ref(a, R, c);
@@ -272,16 +285,16 @@ __device__ __forceinline__ void sample_half(const ItemRaw &r, float c, LaneSum &
     float acc[kItemLoads];
 #pragma unroll
     for (int k = 0; k < kItemLoads; ++k) {
-        float x[8];
-        lane_vals<0, 1>(r, k, x);
+        float x[E];
+        lane_vals<DT, 1>(r, k, x);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) a.m = nmax(a.m, x[t]);
+        for (int t = 0; t < E; ++t) a.m = nmax(a.m, x[t]);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) x[t] = hw_exp2(fmaf(x[t], c, -a.Bhi));
+        for (int t = 0; t < E; ++t) x[t] = hw_exp2(lane_arg<DT>(x[t], c, c_lo, a.Bhi));
 #pragma unroll
-        for (int w = 1; w < 8; w <<= 1)
+        for (int w = 1; w < E; w <<= 1)
 #pragma unroll
-            for (int t = 0; t + w < 8; t += 2 * w) x[t] += x[t + w];
+            for (int t = 0; t + w < E; t += 2 * w) x[t] += x[t + w];
         acc[k] = x[0];
     }
 #pragma unroll
@@ -300,14 +313,14 @@ __device__ __forceinline__ void sample_half(const ItemRaw &r, float c, LaneSum &
         float acc2[kItemLoads];
 #pragma unroll
         for (int k = 0; k < kItemLoads; ++k) {
-            float x[8];
-            lane_vals<0, 2>(r, k, x);
+            float x[E];
+            lane_vals<DT, 2>(r, k, x);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) x[t] = hw_exp2(fmaf(x[t], c, -a.Bhi) - Blo);
+            for (int t = 0; t < E; ++t) x[t] = hw_exp2(lane_arg<DT>(x[t], c, c_lo, a.Bhi) - Blo);
 #pragma unroll
-            for (int w = 1; w < 8; w <<= 1)
+            for (int w = 1; w < E; w <<= 1)
 #pragma unroll
-                for (int t = 0; t + w < 8; t += 2 * w) x[t] += x[t + w];
+                for (int t = 0; t + w < E; t += 2 * w) x[t] += x[t + w];
             acc2[k] = x[0];
         }
 #pragma unroll
@@ -320,9 +333,51 @@ __device__ __forceinline__ void sample_half(const ItemRaw &r, float c, LaneSum &
     if (a.m == -INFINITY) a.s = 0.0f;
 }
 
-// The piece's record from the lane sums: m = M, s = sum 2^(z c - E_M) with
-// E_M = fl(M c) (ref = M, in idx) or, when |fl(M c)| >= 2^30, the exact M c (ref = NaN).
-__device__ __forceinline__ Partial sample_record(const LaneSum &a, float c)
+// fp32 logits (relative error of the sums well below 1e-6): the half's lane maximum
+// first, the reference follows the running lane maximum (the sum so far rescaled),
+// so every exponent is <= 0 and the terms that matter have small arguments; each
+// load's four terms are added in fp32, the loads in fp64.
+__device__ __forceinline__ void sample_half_f32(const ItemRaw &r, float c, float c_lo, LaneSum &a, bool first)
+{
+    float mh = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kItemLoads; ++k) {
+        float x[4];
+        lane_vals<1>(r, k, x);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) mh = nmax(mh, x[t]);
+    }
+    const float mprev = first ? -INFINITY : a.m;
+    const float mnew = nmax(mprev, mh);
+    if (first) {
+        a.s64 = 0.0;
+        set_ref(a, fabsf(mnew) <= 3.402823466e38f ? mnew : 0.0f, c);
+    } else if (fabsf(mnew) <= 3.402823466e38f && mnew > mprev) {
+        const double E_old = a.E;
+        set_ref(a, mnew, c);
+        a.s64 = mprev == -INFINITY ? 0.0 : a.s64 * exp2_f64(E_old - a.E);
+    }
+    a.m = mnew;
+    if (!(fabsf(mnew) <= 3.402823466e38f)) return;   // -inf so far (nothing to add), or NaN / +inf
+    const float Blo = a.huge ? a.Blo : 0.0f;
+    double s = 0.0;
+#pragma unroll
+    for (int k = 0; k < kItemLoads; ++k) {
+        float x[4];
+        lane_vals<1, 1>(r, k, x);
+        float t4 = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) t4 += hw_exp2(lane_arg<1>(x[t], c, c_lo, a.Bhi) - Blo);
+        s += (double)t4;
+    }
+    a.s64 += s;
+}
+
+// The piece's record from the lane sums: m = M, s = sum 2^(z c' - E_M) (c' = c + c_lo,
+// the scale) with E_M = fl(M c) (ref = M, in idx) or, when |fl(M c)| >= 2^30, the
+// exact M c' (ref = NaN).
+template <int DT>
+__device__ __forceinline__ Partial sample_record(const LaneSum &a, float c, float c_lo)
 {
     const float M = wave_umax_f32(a.m);
     Partial p{M, 0, 0.0};
@@ -334,10 +389,15 @@ __device__ __forceinline__ Partial sample_record(const LaneSum &a, float c)
     }
     const float BM = M * c;
     const bool exact = !(fabsf(BM) < 0x1p30f);
-    const double EM = exact ? (double)M * (double)c : (double)BM;
-    const float t = a.m == -INFINITY ? 0.0f : a.s * exp2_split(a.E - EM);
+    const double EM = exact ? (double)M * (double)c + (double)M * (double)c_lo : (double)BM;
     p.idx = __float_as_int(exact ? __builtin_nanf("") : M);
-    p.s = wave_total(t);
+    if constexpr (DT == 0) {
+        const float t = a.m == -INFINITY ? 0.0f : a.s * exp2_split(a.E - EM);
+        p.s = wave_total(t);
+    } else {
+        const double t = a.m == -INFINITY ? 0.0 : a.s64 * exp2_f64(a.E - EM);
+        p.s = wave_usum_f64(t);
+    }
     return p;
 }
 
@@ -398,13 +458,6 @@ __device__ __forceinline__ Partial argmax_record(const LaneArg &a)
     return Partial{M, wave_umin_i32(a.best == M ? a.idx : INT32_MAX), 0.0};
 }
 
-// ---------------------------------------------------------------------------
-// fp32 sampling piece (fp64 arithmetic): maximum first, then the sum against it
-// ---------------------------------------------------------------------------
-struct LaneSum64 {
-    float m;
-    double s;
-};
 
 // ---------------------------------------------------------------------------
 // the logit at the position's draft token
@@ -436,7 +489,6 @@ __device__ __forceinline__ float half_value(const ItemRaw &r, int lane, int o)
 template <int DT>
 struct PieceAcc {
     LaneSum ls;
-    LaneSum64 l64;
     LaneArg la;
 };
 
@@ -448,27 +500,8 @@ __device__ __forceinline__ void piece_half(const Params &P, const VecCtx &vc, in
     if constexpr (!AL) realign(r, lane);
     if (n != (int)P.geo.ie) mask_tail<DT, AL>(r, lane, n);
     if (rm == ROW_SAMPLE) {
-        if constexpr (DT == 0) {
-            sample_half(r, tc.c_hi, acc.ls, h == 0);
-        } else {
-            // fp32 logits: the half's maximum, then its sum against the running maximum
-            const float mh = lane_max<DT>(r);
-            const float mn = nmax(h == 0 ? -INFINITY : acc.l64.m, mh);
-            double s = h == 0 ? 0.0 : acc.l64.s;
-            if (h == 1 && acc.l64.m != -INFINITY && mn != acc.l64.m)
-                s *= exp2_f64(((double)acc.l64.m - (double)mn) * tc.c_eff);
-            if (mn > -INFINITY) {
-#pragma unroll
-                for (int k = 0; k < kItemLoads; ++k) {
-                    float x[E];
-                    lane_vals<DT>(r, k, x);
-#pragma unroll
-                    for (int t = 0; t < E; ++t) s += exp2_f64(((double)x[t] - (double)mn) * tc.c_eff);
-                }
-            }
-            acc.l64.m = mn;
-            acc.l64.s = s;
-        }
+        if constexpr (DT == 0) sample_half<0>(r, tc.c_hi, tc.c_lo, acc.ls, h == 0);
+        else sample_half_f32(r, tc.c_hi, tc.c_lo, acc.ls, h == 0);
         // the logit at the position's draft token, if this half holds it
         if (vc.slot >= 0 && vc.x >= 0 && (int64_t)vc.x < P.V) {
             const int64_t o = (int64_t)vc.x - (2 * j + h) * P.geo.ie;
@@ -489,15 +522,7 @@ __device__ __forceinline__ void piece_finish(const Params &P, const VecCtx &vc, 
 {
     Partial rec{-INFINITY, INT32_MAX, 0.0};
     if (rm == ROW_SAMPLE) {
-        if constexpr (DT == 0) {
-            rec = sample_record(acc.ls, tc.c_hi);
-        } else {
-            // lanes to the piece maximum
-            const float M = wave_umax_f32(acc.l64.m);
-            rec.m = M;
-            const double t = acc.l64.m == -INFINITY ? 0.0 : acc.l64.s * exp2_f64(((double)acc.l64.m - (double)M) * tc.c_eff);
-            rec.s = wave_usum_f64(t);
-        }
+        rec = sample_record<DT>(acc.ls, tc.c_hi, tc.c_lo);
     } else if (rm == ROW_GREEDY && vc.target) {
         rec = argmax_record(acc.la);
         if (rec.idx != INT32_MAX) rec.idx += (int32_t)(j * 2 * P.geo.ie);
