@@ -12,8 +12,9 @@
 // bonus token (step 5) is drawn from p, whose sums per piece the streaming pass
 // already holds: draw_final_kernel walks those and re-reads one piece.
 //
-// bf16 logits are processed in fp32 (exp2 on the hardware unit, fp64 sums across
-// lanes); fp32 logits are processed in fp64 throughout.
+// The draw's weights are fp32 from the hardware exp2 for both logit types (fp32
+// logits form the exponent in two parts to keep fp32-level accuracy), with fp64 sums
+// across lanes and tiles; the merges of the streaming pass's records are fp64.
 #include <float.h>
 #include <limits.h>
 
@@ -640,35 +641,78 @@ struct DrawConst<0> {
     }
 };
 
-// fp32 logits: fp64 weights 2^((z - m) c) / S (z - m exact in fp64)
+// 1 - 2^y for y <= 0.  Near 0, where 2^y is close to 1 and the difference would
+// lose its relative accuracy, from the series -sum_k (y ln 2)^k / k! to degree 8
+// (y > -1/2: truncation below 1e-9 relative); below, from the hardware exp2.
+__device__ __forceinline__ float one_minus_exp2(float y)
+{
+    float s = (float)kExp2Coef[5];   // (ln 2)^8 / 8!; kExp2Coef[13 - k] = (ln 2)^k / k!
+#pragma unroll
+    for (int k = 7; k >= 1; --k) s = fmaf(s, y, (float)kExp2Coef[13 - k]);
+    return y > -0.5f ? -y * s : 1.0f - hw_exp2(y);
+}
+
+// fp32 logits: fp32 weights from the hardware exp2, p = 2^(u c_hi + u c_lo - B) with the
+// vector's normalisation in the exponent: B = m c + log2 S held as two fp32 parts
+// (~2^-48 relative), so no per-vector factor is rounded to fp32.  When |fl(m c_hi)| <
+// 2^20, u = z; otherwise u = z - m, which is exact for every logit whose weight is not
+// 0 (it lies within a factor 2 of m), and B = log2 S.  The residual is taken as
+// p (1 - q/p) with log2(q/p) = (z_d - z_t) c + (B_t - B_d) formed directly (the
+// constant again in two parts), so where q is close to p the residual keeps the
+// relative accuracy of its factors instead of the absolute accuracy of p and q.
 template <>
 struct DrawConst<1> {
-    TempConst tc;
-    double mt, md, Ft, Fd;
-    float tht, thd;
+    float ch, cl, ut, Bht, Blt, Kh, Kl, tht, thd;
     bool residual;
 
+    // route and exponent constant of one vector; returns m c + log2 S in fp64
+    __device__ __forceinline__ static double vector_const(float m, double S, const TempConst &tc, float &sub,
+                                                         float &Bh, float &Bl)
+    {
+        const double L = log2(S), mc = (double)m * tc.c_eff;
+        double B = L;
+        sub = m;
+        if (fabsf(m * tc.c_hi) < kFastRef) {
+            sub = 0.0f;
+            B += mc;
+        }
+        Bh = (float)B;
+        Bl = (float)(B - (double)Bh);
+        return mc + L;
+    }
     __device__ __forceinline__ void init(const RowDraw &D)
     {
         tht = D.theta_t;
         thd = D.theta_d;
-        tc = temp_const<1>(D.T);
+        const TempConst tc = temp_const<1>(D.T);
+        ch = tc.c_hi;
+        cl = tc.c_lo;
         residual = D.kind == DRAW_RESIDUAL;
-        mt = (double)D.m_t;
-        Ft = 1.0 / D.S_t;
-        md = (double)D.m_d;
-        Fd = residual ? 1.0 / D.S_d : 0.0;
+        const double Bt = vector_const(D.m_t, D.S_t, tc, ut, Bht, Blt);
+        Kh = 0.0f;
+        Kl = 0.0f;
+        if (residual) {
+            float sd, bh, bl;
+            const double K = Bt - vector_const(D.m_d, D.S_d, tc, sd, bh, bl);
+            Kh = (float)K;
+            Kl = (float)(K - (double)Kh);
+        }
     }
-    using W = double;
-    __device__ __forceinline__ void weights(const float *zt, const float *zd, double *w, double *p) const
+    using W = float;
+    __device__ __forceinline__ void weights(const float *zt, const float *zd, float *w, float *p) const
     {
 #pragma unroll
         for (int e = 0; e < kUnitElems; ++e) {
             const float zte = zt[e] < tht ? -INFINITY : zt[e];
-            const float zde = zd[e] < thd ? -INFINITY : zd[e];
-            const double pe = exp2_f64(((double)zte - mt) * tc.c_eff) * Ft;
-            double we = pe;
-            if (residual) we = fmax(0.0, pe - exp2_f64(((double)zde - md) * tc.c_eff) * Fd);
+            const float xt = zte - ut;
+            const float pe = hw_exp2(fmaf(xt, cl, fmaf(xt, ch, -Bht)) - Blt);
+            float we = pe;
+            if (residual) {
+                // y = log2(q / p); NaN (both -inf) and y >= 0 give no residual
+                const float d = (zd[e] < thd ? -INFINITY : zd[e]) - zte;
+                const float y = fmaf(d, ch, Kh) + fmaf(d, cl, Kl);
+                we = y < 0.0f ? pe * one_minus_exp2(y) : 0.0f;
+            }
             w[e] = we;
             p[e] = pe;
         }
