@@ -17,8 +17,8 @@ constexpr int kWaves = kBlock / 64;
 constexpr int kUnitElems = 8;            // logits per draw-tile lane (one 16-byte bf16 load)
 constexpr int kTileUnits = 64;           // draw tile: one unit per lane of a wave
 constexpr int kTileElems = kTileUnits * kUnitElems;   // 512 logits
-constexpr int kTilesPerWave = 4;         // draw: tiles a wave sums with all loads in flight
-constexpr int kTilesPerDrawWg = kTilesPerWave * kWaves;   // 16 tiles = 8192 logits
+constexpr int kTilesPerWave = 2;         // draw: tiles a wave sums with all loads in flight
+constexpr int kTilesPerDrawWg = kTilesPerWave * kWaves;   // 8 tiles = 4096 logits
 // Streaming pass: a wave reads a half piece of 8 KB as 8 loads of 16 bytes per lane
 // (lane l's k-th load at byte 1024 k + 16 l), so bf16 halves hold 4096 logits and
 // fp32 halves 2048.
@@ -259,8 +259,8 @@ __device__ __forceinline__ int32_t row_mode(int32_t mode, float T)
 //   bf16 logits (fp32 arithmetic): c_hi = c rounded to fp32 is the scale itself (a
 //     relative change of the temperature below 2^-24), c_lo = 0, c_eff = c_hi.
 //   fp32 logits: c_eff = c_hi + c_lo carries c to ~2^-48, c_hi rounded down and
-//     c_lo >= FLT_MIN the fp32 remainder (the streaming pass adds z c_lo with a
-//     second fma; the fp64 steps use c_eff).
+//     c_lo >= FLT_MIN the fp32 remainder (the draw's fp32 weights add z c_lo with a
+//     second fma; the streaming pass and the other fp64 steps use c_eff).
 struct TempConst {
     float c_hi, c_lo;
     double c_eff;

@@ -652,33 +652,33 @@ __device__ __forceinline__ float one_minus_exp2(float y)
     return y > -0.5f ? -y * s : 1.0f - hw_exp2(y);
 }
 
+// The sum a + b as hi + lo exactly (Knuth's branch-free two-sum; finite inputs).
+__device__ __forceinline__ void two_sum(float a, float b, float &hi, float &lo)
+{
+    hi = a + b;
+    const float bb = hi - a;
+    lo = (a - (hi - bb)) + (b - bb);
+}
+
 // fp32 logits: fp32 weights from the hardware exp2, p = 2^(u c_hi + u c_lo - B) with the
 // vector's normalisation in the exponent: B = m c + log2 S held as two fp32 parts
 // (~2^-48 relative), so no per-vector factor is rounded to fp32.  When |fl(m c_hi)| <
 // 2^20, u = z; otherwise u = z - m, which is exact for every logit whose weight is not
-// 0 (it lies within a factor 2 of m), and B = log2 S.  The residual is taken as
-// p (1 - q/p) with log2(q/p) = (z_d - z_t) c + (B_t - B_d) formed directly (the
-// constant again in two parts), so where q is close to p the residual keeps the
-// relative accuracy of its factors instead of the absolute accuracy of p and q.
+// 0 (it lies within a factor 2 of m), and B = log2 S.
+// The residual is taken as p (1 - 2^y) with y = log2(q/p) = ((z_d - z_t) + (m_t - m_d)) c
+// + log2(S_t / S_d), both differences carried exactly in two fp32 parts: y keeps its
+// relative accuracy where q is close to p (a difference p - q would keep only the
+// absolute accuracy of p and q), and it is exactly log2(S_t / S_d), 0 for equal sums,
+// wherever z_t - m_t = z_d - m_d, as for a distribution that keeps one token.
 template <>
 struct DrawConst<1> {
-    float ch, cl, ut, Bht, Blt, Kh, Kl, tht, thd;
+    float ch, cl, ut, Bht, Blt, Mh, Ml, Lh, Ll, tht, thd;
     bool residual;
 
-    // route and exponent constant of one vector; returns m c + log2 S in fp64
-    __device__ __forceinline__ static double vector_const(float m, double S, const TempConst &tc, float &sub,
-                                                         float &Bh, float &Bl)
+    __device__ __forceinline__ static void split(double x, float &hi, float &lo)
     {
-        const double L = log2(S), mc = (double)m * tc.c_eff;
-        double B = L;
-        sub = m;
-        if (fabsf(m * tc.c_hi) < kFastRef) {
-            sub = 0.0f;
-            B += mc;
-        }
-        Bh = (float)B;
-        Bl = (float)(B - (double)Bh);
-        return mc + L;
+        hi = (float)x;
+        lo = (float)(x - (double)hi);
     }
     __device__ __forceinline__ void init(const RowDraw &D)
     {
@@ -688,14 +688,18 @@ struct DrawConst<1> {
         ch = tc.c_hi;
         cl = tc.c_lo;
         residual = D.kind == DRAW_RESIDUAL;
-        const double Bt = vector_const(D.m_t, D.S_t, tc, ut, Bht, Blt);
-        Kh = 0.0f;
-        Kl = 0.0f;
+        const double Lt = log2(D.S_t);
+        double B = Lt;
+        ut = D.m_t;
+        if (fabsf(D.m_t * tc.c_hi) < kFastRef) {
+            ut = 0.0f;
+            B += (double)D.m_t * tc.c_eff;
+        }
+        split(B, Bht, Blt);
+        Mh = Ml = Lh = Ll = 0.0f;
         if (residual) {
-            float sd, bh, bl;
-            const double K = Bt - vector_const(D.m_d, D.S_d, tc, sd, bh, bl);
-            Kh = (float)K;
-            Kl = (float)(K - (double)Kh);
+            split((double)D.m_t - (double)D.m_d, Mh, Ml);   // exact: both are fp32
+            split(Lt - log2(D.S_d), Lh, Ll);
         }
     }
     using W = float;
@@ -708,10 +712,13 @@ struct DrawConst<1> {
             const float pe = hw_exp2(fmaf(xt, cl, fmaf(xt, ch, -Bht)) - Blt);
             float we = pe;
             if (residual) {
-                // y = log2(q / p); NaN (both -inf) and y >= 0 give no residual
-                const float d = (zd[e] < thd ? -INFINITY : zd[e]) - zte;
-                const float y = fmaf(d, ch, Kh) + fmaf(d, cl, Kl);
-                we = y < 0.0f ? pe * one_minus_exp2(y) : 0.0f;
+                const float zde = zd[e] < thd ? -INFINITY : zd[e];
+                float dh, dl;
+                two_sum(zde, -zte, dh, dl);
+                const float g = (dh + Mh) + (dl + Ml);
+                const float y = fmaf(g, ch, Lh) + fmaf(g, cl, Ll);
+                // q = 0 keeps all of p; y >= 0 (q >= p) and NaN (p = 0) keep nothing
+                we = zde == -INFINITY ? pe : (y < 0.0f ? pe * one_minus_exp2(y) : 0.0f);
             }
             w[e] = we;
             p[e] = pe;
@@ -748,8 +755,8 @@ __device__ __forceinline__ void verify_body(const Params &P)
     const int64_t per_row = P.geo.ndraw;
     const int32_t row = (int32_t)(blockIdx.x / per_row);
     const int32_t piece = (int32_t)(blockIdx.x - (int64_t)row * per_row);
+    const RowDraw D = P.draws[row];   // loaded together with the status word
     if (P.gamma != nullptr && P.hdr->status != 0) return;
-    const RowDraw D = P.draws[row];
     // bonus draws use the streaming pass's piece sums, except when p is filtered
     if (!(D.kind == DRAW_RESIDUAL || (P.theta && D.kind == DRAW_BONUS))) return;
     DrawConst<DT> c;

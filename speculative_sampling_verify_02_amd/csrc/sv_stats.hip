@@ -12,9 +12,10 @@
 // decoding", section "Why the output is exactly the target's").  The wave also keeps
 // the logit at each position's draft token when it passes through its registers.
 //
-// The sums are taken in fp32 (exp2 on the hardware unit, the exponent from one fma
-// for bf16 logits and two for fp32 logits, which also carry the scale's low part)
-// and added across lanes in fp64.
+// bf16 logits are summed in fp32 (exp2 on the hardware unit, the exponent from one
+// fma) and added across lanes in fp64.  fp32 logits are summed term by term in fp64
+// (a table-driven exp2): the residual mass of a draft close to the target depends on
+// the ratio of the two sums to ~1e-9 relative, below what an fp32 exp can give.
 #include <float.h>
 #include <limits.h>
 
@@ -256,19 +257,11 @@ __device__ __forceinline__ void set_ref(LaneSum &a, float R, float c)
     a.E = a.huge ? (double)a.Bhi + (double)a.Blo : (double)a.Bhi;
 }
 
-// 2^(x c - B) for a logit x against the reference B = Bhi (+ Blo): one fma for bf16
-// logits (c is the scale itself), two for fp32 logits (the scale's low part c_lo too).
-template <int DT>
-__device__ __forceinline__ float lane_arg(float x, float c, float c_lo, float Bhi)
+// add one bf16 half (first: the piece's first half, which sets the references); the
+// term of logit x is 2^(x c - Bhi), one fma and the hardware exp2
+__device__ __forceinline__ void sample_half(const ItemRaw &r, float c, LaneSum &a, bool first)
 {
-    const float t = fmaf(x, c, -Bhi);
-    return DT == 0 ? t : fmaf(x, c_lo, t);
-}
-
-// add one half (first: the piece's first half, which sets the references)
-template <int DT>
-__device__ __forceinline__ void sample_half(const ItemRaw &r, float c, float c_lo, LaneSum &a, bool first)
-{
+    constexpr int DT = 0;
     constexpr int E = kE<DT>;
     if (first) {
         float x[E];
@@ -290,7 +283,7 @@ __device__ __forceinline__ void sample_half(const ItemRaw &r, float c, float c_l
 #pragma unroll
         for (int t = 0; t < E; ++t) a.m = nmax(a.m, x[t]);
 #pragma unroll
-        for (int t = 0; t < E; ++t) x[t] = hw_exp2(lane_arg<DT>(x[t], c, c_lo, a.Bhi));
+        for (int t = 0; t < E; ++t) x[t] = hw_exp2(fmaf(x[t], c, -a.Bhi));
 #pragma unroll
         for (int w = 1; w < E; w <<= 1)
 #pragma unroll
@@ -316,7 +309,7 @@ __device__ __forceinline__ void sample_half(const ItemRaw &r, float c, float c_l
             float x[E];
             lane_vals<DT, 2>(r, k, x);
 #pragma unroll
-            for (int t = 0; t < E; ++t) x[t] = hw_exp2(lane_arg<DT>(x[t], c, c_lo, a.Bhi) - Blo);
+            for (int t = 0; t < E; ++t) x[t] = hw_exp2(fmaf(x[t], c, -a.Bhi) - Blo);
 #pragma unroll
             for (int w = 1; w < E; w <<= 1)
 #pragma unroll
@@ -333,11 +326,68 @@ __device__ __forceinline__ void sample_half(const ItemRaw &r, float c, float c_l
     if (a.m == -INFINITY) a.s = 0.0f;
 }
 
-// fp32 logits (relative error of the sums well below 1e-6): the half's lane maximum
-// first, the reference follows the running lane maximum (the sum so far rescaled),
-// so every exponent is <= 0 and the terms that matter have small arguments; each
-// load's four terms are added in fp32, the loads in fp64.
-__device__ __forceinline__ void sample_half_f32(const ItemRaw &r, float c, float c_lo, LaneSum &a, bool first)
+// 2^(a/L) in fp64 from a table of the L = 64 values 2^(j/L) in LDS (exp2_tab_read,
+// then exp2_tab_finish): a = k + r with
+// k = rint(a), so |r| <= 1/2 and 2^(a/L) = 2^floor(k/L) 2^((k mod L)/L) 2^(r/L), with
+// 2^(r/L) from its Taylor series in r ln 2 / L to degree 3 (truncation below 4e-11
+// relative).  The power 2^floor(k/L) is added to the exponent field of the product,
+// which lies in [0.99, 2.02): the caller keeps a >= -1000 L (2^-1000, a term that
+// cannot register next to the maximum's 1), so the result stays normal.  Entry j of
+// the lane's copy is at col[j << sh] (sh = 6: one column per lane, which no two lanes
+// of a wave share, so the reads meet no bank conflicts; sh = 0: a single shared copy).
+constexpr int kTabBits = 6;
+constexpr int kTabLen = 1 << kTabBits;
+
+struct Exp2Tab {
+    const double *col;
+    int sh;
+};
+
+// (ln 2 / L)^j / j!  (kExp2Coef[13 - j] = (ln 2)^j / j!, scaled by L^-j exactly)
+constexpr double kTabC1 = kExp2Coef[12] / kTabLen;
+constexpr double kTabC2 = kExp2Coef[11] / kTabLen / kTabLen;
+constexpr double kTabC3 = kExp2Coef[10] / kTabLen / kTabLen / kTabLen;
+
+// The two halves of exp2_tab, so that a caller can issue the table reads of several
+// terms before it waits for the first: the rounding and the read, then the series.
+struct TabTerm {
+    double r;   // a - rint(a)
+    double T;   // 2^((k mod L)/L)
+    int ki;     // rint(a)
+};
+
+__device__ __forceinline__ TabTerm exp2_tab_read(double a, const Exp2Tab &t)
+{
+    const double k = rint(a);
+    TabTerm u;
+    u.r = a - k;   // exact
+    u.ki = (int)k;
+    u.T = t.col[(u.ki & (kTabLen - 1)) << t.sh];
+    return u;
+}
+
+__device__ __forceinline__ double exp2_tab_finish(const TabTerm &u)
+{
+    const double q = fma(fma(fma(kTabC3, u.r, kTabC2), u.r, kTabC1), u.r, 1.0);
+    const double v = u.T * q;
+    return __hiloint2double(__double2hiint(v) + (u.ki >> kTabBits) * 1048576, __double2loint(v));
+}
+
+// Fill a table of 2^(j/L) for exp2_tab_read: kTabLen entries, each repeated `copies`
+// times (64: one column per lane; 1: a single copy).  The caller synchronises after it.
+__device__ __forceinline__ void fill_exp2_tab(double *tab, int copies)
+{
+    for (int i = threadIdx.x; i < kTabLen * copies; i += blockDim.x)
+        tab[i] = exp2_f64((double)(i / copies) * (1.0 / kTabLen));
+}
+
+// fp32 logits: the sums feed log2(S_t / S_d), which the residual mass of a draft close
+// to the target needs to ~1e-9 relative, so every term is an fp64 2^(x c - E): the
+// exponent from one fp64 fma (c the full scale), the power from the table.  The half's lane maximum comes first and the reference follows the
+// running lane maximum (the sum so far rescaled), so every exponent is <= 0 up to
+// rounding.
+__device__ __forceinline__ void sample_half_f32(const ItemRaw &r, float c, double c_eff, LaneSum &a, bool first,
+                                                const Exp2Tab &tab)
 {
     float mh = -INFINITY;
 #pragma unroll
@@ -359,16 +409,18 @@ __device__ __forceinline__ void sample_half_f32(const ItemRaw &r, float c, float
     }
     a.m = mnew;
     if (!(fabsf(mnew) <= 3.402823466e38f)) return;   // -inf so far (nothing to add), or NaN / +inf
-    const float Blo = a.huge ? a.Blo : 0.0f;
+    // exponents scaled by L (exact) and kept >= -1000 L (-inf logits included)
+    const double cs = (double)kTabLen * c_eff, Es = (double)kTabLen * a.E;
     double s = 0.0;
 #pragma unroll
     for (int k = 0; k < kItemLoads; ++k) {
         float x[4];
         lane_vals<1, 1>(r, k, x);
-        float t4 = 0.0f;
+        TabTerm u[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) t4 += hw_exp2(lane_arg<1>(x[t], c, c_lo, a.Bhi) - Blo);
-        s += (double)t4;
+        for (int t = 0; t < 4; ++t) u[t] = exp2_tab_read(fmax(fma((double)x[t], cs, -Es), -1000.0 * kTabLen), tab);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) s += exp2_tab_finish(u[t]);
     }
     a.s64 += s;
 }
@@ -494,14 +546,15 @@ struct PieceAcc {
 
 template <int DT, bool AL>
 __device__ __forceinline__ void piece_half(const Params &P, const VecCtx &vc, int32_t rm, const TempConst &tc,
-                                           int64_t j, int h, int n, ItemRaw &r, PieceAcc<DT> &acc, int lane)
+                                           int64_t j, int h, int n, ItemRaw &r, PieceAcc<DT> &acc, int lane,
+                                           const Exp2Tab &tab)
 {
     constexpr int E = kE<DT>;
     if constexpr (!AL) realign(r, lane);
     if (n != (int)P.geo.ie) mask_tail<DT, AL>(r, lane, n);
     if (rm == ROW_SAMPLE) {
-        if constexpr (DT == 0) sample_half<0>(r, tc.c_hi, tc.c_lo, acc.ls, h == 0);
-        else sample_half_f32(r, tc.c_hi, tc.c_lo, acc.ls, h == 0);
+        if constexpr (DT == 0) sample_half(r, tc.c_hi, acc.ls, h == 0);
+        else sample_half_f32(r, tc.c_hi, tc.c_eff, acc.ls, h == 0, tab);
         // the logit at the position's draft token, if this half holds it
         if (vc.slot >= 0 && vc.x >= 0 && (int64_t)vc.x < P.V) {
             const int64_t o = (int64_t)vc.x - (2 * j + h) * P.geo.ie;
@@ -538,10 +591,16 @@ template <int DT, bool AL>
 __device__ __forceinline__ void stats_body(const Params &P)
 {
     __shared__ uint32_t s_next;
+    const int lane = threadIdx.x & 63;
+    Exp2Tab tab{nullptr, 6};
+    if constexpr (DT == 1) {
+        __shared__ double s_tab[kTabLen * 64];
+        fill_exp2_tab(s_tab, 64);
+        tab.col = s_tab + lane;
+    }
     if (threadIdx.x == 0) s_next = 0u;
     __syncthreads();
     if (P.gamma != nullptr && P.hdr->status != 0) return;
-    const int lane = threadIdx.x & 63;
     const int64_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nwb = blockDim.x >> 6;
     const int64_t N = P.geo.nitems, G = gridDim.x;
@@ -580,10 +639,10 @@ __device__ __forceinline__ void stats_body(const Params &P)
             cached_T = vc.T;
         }
         PieceAcc<DT> acc;
-        piece_half<DT, AL>(P, vc, rm, tc, cj, 0, half_len(P, cj, 0), ra, acc, lane);
+        piece_half<DT, AL>(P, vc, rm, tc, cj, 0, half_len(P, cj, 0), ra, acc, lane, tab);
         half_begin<DT, AL>(P, v, j, 0, live, ra, lane);
         const int n1 = half_len(P, cj, 1);
-        if (n1 > 0) piece_half<DT, AL>(P, vc, rm, tc, cj, 1, n1, rb, acc, lane);
+        if (n1 > 0) piece_half<DT, AL>(P, vc, rm, tc, cj, 1, n1, rb, acc, lane, tab);
         half_begin<DT, AL>(P, v, j, 1, live, rb, lane);
         const VecCtx vn = vec_ctx(P, live ? v : 0);
         piece_finish<DT>(P, vc, rm, tc, cv, cj, acc);
@@ -603,6 +662,13 @@ __global__ __launch_bounds__(64) void stats_list_kernel(Params P)
 {
     const int lane = threadIdx.x;
     const int buf = P.step & 1;
+    Exp2Tab tab{nullptr, 0};
+    if constexpr (DT == 1) {   // one shared copy: 64 copies would limit the one-wave workgroups per CU
+        __shared__ double s_tab[kTabLen];
+        fill_exp2_tab(s_tab, 1);
+        __syncthreads();
+        tab.col = s_tab;
+    }
     if (blockIdx.x == 0 && lane == 0) {
         P.ee_count[2 * (buf ^ 1)] = 0;
         P.ee_count[2 * (buf ^ 1) + 1] = 0;
@@ -621,9 +687,9 @@ __global__ __launch_bounds__(64) void stats_list_kernel(Params P)
     const int32_t rm = row_mode(P.mode, vc.T);
     const TempConst tc = rm == ROW_SAMPLE ? temp_const<DT>(vc.T) : TempConst{};
     PieceAcc<DT> acc;
-    piece_half<DT, AL>(P, vc, rm, tc, j, 0, half_len(P, j, 0), ra, acc, lane);
+    piece_half<DT, AL>(P, vc, rm, tc, j, 0, half_len(P, j, 0), ra, acc, lane, tab);
     const int n1 = half_len(P, j, 1);
-    if (n1 > 0) piece_half<DT, AL>(P, vc, rm, tc, j, 1, n1, rb, acc, lane);
+    if (n1 > 0) piece_half<DT, AL>(P, vc, rm, tc, j, 1, n1, rb, acc, lane, tab);
     piece_finish<DT>(P, vc, rm, tc, v, j, acc);
 }
 

@@ -64,6 +64,10 @@ SMALL = [
     dict(seed=30, batch=3, vocab=40, dtype="f32", gamma=[100, 70, 0], noise=0.05),
     dict(seed=31, batch=33, vocab=65536, dtype="bf16", gamma=[2] * 33, noise=0.3),
     dict(seed=32, batch=4, vocab=300000, dtype="f32", gamma=[1, 3, 0, 2], sigma=4.0),
+    # drafts very close to the target: the residual is a small difference of near-equal
+    # probabilities, which the fp32 weights must resolve to the 1e-6 relative bound
+    dict(seed=33, batch=5, vocab=2003, dtype="f32", gamma=[3, 2, 4, 1, 6], noise=0.01),
+    dict(seed=34, batch=3, vocab=60001, dtype="f32", gamma=[2, 5, 3], noise=0.02, temperature=0.7),
 ]
 
 
@@ -197,6 +201,23 @@ def test_q_zero_and_zero_residual(H):
     gpu, ref, rep = _parity(H, w)
     assert gpu["row_status"][0] == oracle.Q_ZERO and gpu["n_accepted"][0] == 1
     assert gpu["row_status"][1] == oracle.Q_ZERO | oracle.ZERO_RESID and gpu["n_accepted"][1] == 0
+
+
+@pytest.mark.parametrize("vocab,dtype", [(40, "f32"), (2003, "f32"), (60001, "f32"), (4096, "bf16")])
+def test_near_equal_rejections(H, vocab, dtype):
+    """Drafts within about 1 % of the target and test uniforms just below 1: rows reject
+    where p(x) is a hair below q(x), so the residual max(0, p - q) is a small
+    difference of near-equal probabilities, its mass a few percent at most."""
+    w = workloads.small(seed=70 + vocab % 7, batch=12, vocab=vocab, dtype=dtype, gamma=3, noise=0.01)
+    u = w.uniforms.copy()
+    off = np.concatenate([[0], np.cumsum(w.gamma.astype(np.int64) + 1)])
+    for i in range(w.batch):
+        u[off[i]:off[i] + w.gamma[i]] = np.float32(0.999999)
+    w2 = _edit(w, uniforms=u)
+    gpu, ref, rep = _parity(H, w2)
+    assert (ref["n_accepted"] < w2.gamma).sum() >= w.batch // 2
+    W = ref["resid_mass"][ref["n_accepted"] < w2.gamma]
+    assert np.nanmax(W) < 0.1
 
 
 def test_bad_gamma(H):
