@@ -9,8 +9,8 @@ serve a step from the previous one.
 
 Prints ONE JSON line: verified positions/s (sum of gamma_i + 1 per step), plus
 rows/s, algorithmic HBM GB/s, the roofline of the dominant kernel (the statistics
-pass, timed live with HIP events recorded around it on the call's stream), and the
-CPU oracle timed on this host as a baseline.
+pass, timed live with HIP events attached to its dispatch on the call's stream), and
+the CPU oracle timed on this host as a baseline.
 """
 from __future__ import annotations
 
@@ -137,8 +137,8 @@ def cpu_baseline(w, budget_s: float, mode: str):
 
 
 def timed_steps(step, steps: int, sv):
-    """Wall time of `steps` calls, then the same calls again with HIP events around
-    each call's streaming kernel; returns (sec per step, stats kernel ms per launch,
+    """Wall time of `steps` calls, then the same calls again with HIP events attached
+    to each call's streaming-kernel dispatch; returns (sec per step, stats kernel ms per launch,
     ms per step with the events)."""
     import numpy as np
     import torch
@@ -389,8 +389,7 @@ def main():
     torch.cuda.synchronize()
 
     # the whole job with nothing else on the stream, then the same steps with HIP
-    # events recorded around the streaming kernel on the call's stream (the event
-    # records add their own gaps to the step)
+    # events attached to the streaming kernel's dispatch on the call's stream
     sec_per_step, stats_avg_ms, ms_events = timed_steps(step, args.steps, sv)
     positions = nT
     stats_bytes = pass1_bytes  # every logit read once (the per-segment records it writes are < 0.01%)

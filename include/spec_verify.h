@@ -294,10 +294,11 @@ const char *spec_verify_strerror(int32_t status);
 
 /*
  * Profiling aid: when both are non-NULL hipEvent_t handles, every following
- * spec_verify, spec_sample or spec_tree_verify_greedy call records `start_event` on its
- * stream right before
- * its streaming statistics kernel (the pass over every logit) and `stop_event`
- * right after it.
+ * spec_verify, spec_sample, spec_verify_filtered or spec_tree_verify_greedy call
+ * attaches them to the dispatch of its streaming kernel (the pass over every logit:
+ * the streaming statistics kernel, or the fused filter kernel), so that
+ * hipEventElapsedTime(start_event, stop_event) gives that kernel's own duration;
+ * spec_verify_early_exit records them on its stream around its position steps.
  * Pass NULL, NULL to stop.  Process-wide setting, not thread-safe.
  */
 sv_status spec_verify_set_profile_events(void *start_event, void *stop_event);

@@ -121,8 +121,9 @@ def tree_workspace_bytes(n_nodes: int, vocab: int, dtype: int) -> int:
 
 
 def set_profile_events(start_event, stop_event) -> None:
-    """Raw hipEvent_t handles (ints) recorded around the statistics kernel of every
-    following call; (None, None) stops."""
+    """Raw hipEvent_t handles (ints) attached to the streaming kernel's dispatch in
+    every following call (around the position steps for early exit); (None, None)
+    stops."""
     rc = lib.spec_verify_set_profile_events(start_event, stop_event)
     if rc != SV_OK:
         raise SpecVerifyError(rc, strerror(rc))

@@ -128,9 +128,9 @@ static sv_status verify_impl(const void *target_logits, const void *draft_logits
     // filtered calls on aligned bf16 rows: one kernel reads each vector once and does
     // both the streaming pass and the threshold search
     const int fused_units = filtered ? sv::filter_stats_units(dtype, aligned, vocab) : 0;
-    if (e == hipSuccess && g_prof_start) e = hipEventRecord(g_prof_start, s);
-    if (e == hipSuccess) e = fused_units ? sv::launch_filter_stats(P, s, fused_units) : sv::launch_stats(P, s, dtype, aligned);
-    if (e == hipSuccess && g_prof_stop) e = hipEventRecord(g_prof_stop, s);
+    if (e == hipSuccess)
+        e = fused_units ? sv::launch_filter_stats(P, s, fused_units, g_prof_start, g_prof_stop)
+                        : sv::launch_stats(P, s, dtype, aligned, g_prof_start, g_prof_stop);
     if (e == hipSuccess && filtered && !fused_units) e = sv::launch_filter(P, s, dtype, aligned);
     if (e == hipSuccess) e = sv::launch_scan(P, s, dtype);
     if (e == hipSuccess && mode == SV_SAMPLE) e = sv::launch_verify(P, s, dtype, aligned);
@@ -230,10 +230,7 @@ extern "C" sv_status spec_sample(const void *logits, int32_t dtype, int64_t voca
     P.geo.inv_d = 0.0;
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    hipError_t e = hipSuccess;
-    if (g_prof_start) e = hipEventRecord(g_prof_start, s);
-    if (e == hipSuccess) e = sv::launch_stats(P, s, dtype, aligned);
-    if (e == hipSuccess && g_prof_stop) e = hipEventRecord(g_prof_stop, s);
+    hipError_t e = sv::launch_stats(P, s, dtype, aligned, g_prof_start, g_prof_stop);
     if (e == hipSuccess) e = sv::launch_scan(P, s, dtype);
     if (e == hipSuccess) e = sv::launch_draw_final(P, s, dtype, aligned);
     return e == hipSuccess ? SV_OK : SV_EHIP;
@@ -287,9 +284,7 @@ extern "C" sv_status spec_tree_verify_greedy(const void *target_logits, int32_t 
                                   sv::stats_grid_cap(dtype, aligned));
         P.geo.inv_t = 1.0;
         P.geo.inv_d = 0.0;
-        if (g_prof_start) e = hipEventRecord(g_prof_start, s);
-        if (e == hipSuccess) e = sv::launch_stats(P, s, dtype, aligned);
-        if (e == hipSuccess && g_prof_stop) e = hipEventRecord(g_prof_stop, s);
+        e = sv::launch_stats(P, s, dtype, aligned, g_prof_start, g_prof_stop);
     }
     sv::TreeParams T{};
     T.parts = reinterpret_cast<const sv::Partial *>(ws + L.parts);

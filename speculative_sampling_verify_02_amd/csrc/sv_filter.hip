@@ -528,7 +528,7 @@ __device__ __forceinline__ void load_vector(const Params &P, int64_t v, int32_t 
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
         const uint32_t u = tid + (uint32_t)(i * kFilterBlock);
-        r[i] = base[u < (uint32_t)nunits ? u : (uint32_t)nunits - 1u];
+        r[i] = load_nt16(base + (u < (uint32_t)nunits ? u : (uint32_t)nunits - 1u));
     }
 }
 
@@ -763,10 +763,10 @@ int filter_stats_units(int dtype, bool aligned, int64_t V)
     return 0;
 }
 
-hipError_t launch_filter_stats(const Params &P, hipStream_t s, int nu)
+hipError_t launch_filter_stats(const Params &P, hipStream_t s, int nu, hipEvent_t start, hipEvent_t stop)
 {
     const int64_t nvec = P.nT + P.nD;
-    if (nvec <= 0) return hipSuccess;
+    if (nvec <= 0) return launch_timed(nullptr, 0, kFilterBlock, P, s, start, stop);
     if (nvec > INT32_MAX) return hipErrorInvalidConfiguration;
     const void *fn = nullptr;
     switch (nu) {
@@ -787,8 +787,7 @@ hipError_t launch_filter_stats(const Params &P, hipStream_t s, int nu)
         if (dev < 64) cap[var][dev] = grid;
     }
     const int64_t blocks = nvec < grid ? nvec : grid;
-    void *args[] = {const_cast<Params *>(&P)};
-    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kFilterBlock), args, 0, s);
+    return launch_timed(fn, blocks, kFilterBlock, P, s, start, stop);
 }
 
 }  // namespace sv

@@ -74,7 +74,7 @@ __device__ __forceinline__ void half_begin(const Params &P, int64_t v, int64_t j
         for (int k = 0; k < kItemLoads; ++k) {
             uint32_t off = (uint32_t)k * 1024u + (uint32_t)lane * 16u;
             off = off < last ? off : last;
-            r.d[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+            r.d[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, kLoadNT));
         }
     } else {
         // aligned 16-byte loads from the aligned address at or below the half's start,
@@ -92,11 +92,11 @@ __device__ __forceinline__ void half_begin(const Params &P, int64_t v, int64_t j
         for (int k = 0; k < kItemLoads; ++k) {
             uint64_t q = a0 + (uint64_t)(k * 64 + lane) * 16u;
             q = q < last ? q : last;
-            r.d[k] = *reinterpret_cast<const uint4 *>(q);
+            r.d[k] = load_nt16(reinterpret_cast<const void *>(q));
         }
         uint64_t qe = a0 + (uint64_t)kItemLoads * 1024u;
         qe = qe < last ? qe : last;
-        r.e = *reinterpret_cast<const uint4 *>(qe);
+        r.e = load_nt16(reinterpret_cast<const void *>(qe));
     }
 }
 
@@ -758,9 +758,9 @@ hipError_t launch_stats_list(const Params &P, hipStream_t s, int dtype, bool ali
     return launch(fn, 2 * (int64_t)P.B * P.geo.ipv, 64, P, s);
 }
 
-hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned)
+hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned, hipEvent_t start, hipEvent_t stop)
 {
-    return launch(stats_fn(dtype, aligned), P.geo.G, stats_block(aligned), P, s);
+    return launch_timed(stats_fn(dtype, aligned), P.geo.G, stats_block(aligned), P, s, start, stop);
 }
 
 }  // namespace sv
