@@ -220,6 +220,31 @@ def test_near_equal_rejections(H, vocab, dtype):
     assert np.nanmax(W) < 0.1
 
 
+def test_extreme_scales_f32(H):
+    """fp32 logits at extreme scales: temperatures from 1e-3 to 1e30 (a near-uniform
+    distribution), rows shifted by +1e7 (their exponents m c lie far beyond 2^20, so
+    the draw subtracts m first and the streaming pass works against large
+    references), a draft shifted by -1e6 against its target (the same softmax from
+    very different maxima), and rows with -inf entries away from the drafted tokens."""
+    g = 3
+    w = workloads.small(seed=91, batch=8, vocab=5000, dtype="f32", gamma=g)
+    T = np.array([1e-3, 0.05, 1.0, 1e3, 1e30, 1.0, 0.5, 2.0], np.float32)
+    tgt, drf = w.target.copy(), w.draft.copy()
+    tr = lambda i: slice(i * (g + 1), (i + 1) * (g + 1))
+    dr = lambda i: slice(i * g, (i + 1) * g)
+    tgt[tr(5)] += np.float32(1e7)
+    drf[dr(5)] += np.float32(1e7)
+    rng = np.random.default_rng(92)
+    drafted = set(w.draft_tokens[dr(6)].tolist())
+    holes = np.array([v for v in rng.choice(w.vocab, 150, replace=False) if v not in drafted][:100])
+    tgt[tr(6), holes[:50, None].T] = -np.inf
+    drf[dr(6), holes[50:, None].T] = -np.inf
+    drf[dr(7)] -= np.float32(1e6)
+    w2 = _edit(w, target=tgt, draft=drf, temperature=T)
+    _parity(H, w2)
+    _parity(H, w2, mode="greedy")
+
+
 def test_bad_gamma(H):
     w = workloads.small(seed=52, batch=6, vocab=512, dtype="bf16", gamma=[2, 1, 3, 0, 2, 1])
     d = H.to_device(w)
