@@ -277,3 +277,12 @@ def test_c4_full(H):
 
 def test_c5_full(H):
     _parity(H, workloads.c5())
+
+
+@pytest.mark.parametrize("seed", [13, 23])
+def test_c3_more_seeds(H, seed):
+    _parity(H, workloads.c3(seed=seed), dense=True)
+
+
+def test_c4_second_seed(H):
+    _parity(H, workloads.c4(seed=14), dense=True)
