@@ -383,10 +383,10 @@ __device__ __forceinline__ void fill_exp2_tab(double *tab, int copies)
 
 // fp32 logits: the sums feed log2(S_t / S_d), which the residual mass of a draft close
 // to the target needs to ~1e-9 relative, so every term is an fp64 2^(x c - E): the
-// exponent from one fp64 fma (c the full scale), the power from the table.  The half's lane maximum comes first and the reference follows the
-// running lane maximum (the sum so far rescaled), so every exponent is <= 0 up to
-// rounding.
-__device__ __forceinline__ void sample_half_f32(const ItemRaw &r, float c, double c_eff, LaneSum &a, bool first,
+// exponent from one fp64 fma (c the full scale), the power from the table.  The half's
+// lane maximum comes first and the reference follows the running lane maximum (the
+// sum so far rescaled), so every exponent is <= 0 up to rounding.
+__device__ __forceinline__ void sample_half_f32(const ItemRaw &r, double c_eff, LaneSum &a, bool first,
                                                 const Exp2Tab &tab)
 {
     float mh = -INFINITY;
@@ -399,12 +399,14 @@ __device__ __forceinline__ void sample_half_f32(const ItemRaw &r, float c, doubl
     }
     const float mprev = first ? -INFINITY : a.m;
     const float mnew = nmax(mprev, mh);
+    // the reference is R c with the full scale, in fp64 (against R c_hi alone the term
+    // of R itself would be 2^(R c_lo), which overflows once R c passes ~2^33)
     if (first) {
         a.s64 = 0.0;
-        set_ref(a, fabsf(mnew) <= 3.402823466e38f ? mnew : 0.0f, c);
+        a.E = (double)(fabsf(mnew) <= 3.402823466e38f ? mnew : 0.0f) * c_eff;
     } else if (fabsf(mnew) <= 3.402823466e38f && mnew > mprev) {
         const double E_old = a.E;
-        set_ref(a, mnew, c);
+        a.E = (double)mnew * c_eff;
         a.s64 = mprev == -INFINITY ? 0.0 : a.s64 * exp2_f64(E_old - a.E);
     }
     a.m = mnew;
@@ -554,7 +556,7 @@ __device__ __forceinline__ void piece_half(const Params &P, const VecCtx &vc, in
     if (n != (int)P.geo.ie) mask_tail<DT, AL>(r, lane, n);
     if (rm == ROW_SAMPLE) {
         if constexpr (DT == 0) sample_half(r, tc.c_hi, acc.ls, h == 0);
-        else sample_half_f32(r, tc.c_hi, tc.c_eff, acc.ls, h == 0, tab);
+        else sample_half_f32(r, tc.c_eff, acc.ls, h == 0, tab);
         // the logit at the position's draft token, if this half holds it
         if (vc.slot >= 0 && vc.x >= 0 && (int64_t)vc.x < P.V) {
             const int64_t o = (int64_t)vc.x - (2 * j + h) * P.geo.ie;

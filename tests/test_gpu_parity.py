@@ -225,10 +225,12 @@ def test_extreme_scales_f32(H):
     distribution), rows shifted by +1e7 (their exponents m c lie far beyond 2^20, so
     the draw subtracts m first and the streaming pass works against large
     references), a draft shifted by -1e6 against its target (the same softmax from
-    very different maxima), and rows with -inf entries away from the drafted tokens."""
+    very different maxima), rows with -inf entries away from the drafted tokens, and a
+    row shifted by 1e6 at T = 1e-4, whose m c ~ 1.4e10 is far beyond where a reference
+    taken with the scale's fp32 part alone would overflow the sums."""
     g = 3
-    w = workloads.small(seed=91, batch=8, vocab=5000, dtype="f32", gamma=g)
-    T = np.array([1e-3, 0.05, 1.0, 1e3, 1e30, 1.0, 0.5, 2.0], np.float32)
+    w = workloads.small(seed=91, batch=9, vocab=5000, dtype="f32", gamma=g)
+    T = np.array([1e-3, 0.05, 1.0, 1e3, 1e30, 1.0, 0.5, 2.0, 1e-4], np.float32)
     tgt, drf = w.target.copy(), w.draft.copy()
     tr = lambda i: slice(i * (g + 1), (i + 1) * (g + 1))
     dr = lambda i: slice(i * g, (i + 1) * g)
@@ -240,6 +242,8 @@ def test_extreme_scales_f32(H):
     tgt[tr(6), holes[:50, None].T] = -np.inf
     drf[dr(6), holes[50:, None].T] = -np.inf
     drf[dr(7)] -= np.float32(1e6)
+    tgt[tr(8)] += np.float32(1e6)   # m c ~ 1.4e10 at T = 1e-4
+    drf[dr(8)] += np.float32(1e6)
     w2 = _edit(w, target=tgt, draft=drf, temperature=T)
     _parity(H, w2)
     _parity(H, w2, mode="greedy")
