@@ -290,3 +290,12 @@ def test_c3_more_seeds(H, seed):
 
 def test_c4_second_seed(H):
     _parity(H, workloads.c4(seed=14), dense=True)
+
+
+def test_many_rows(H):
+    """3000 ragged rows (gamma 0..7): the packed offsets are scanned over several
+    1024-row chunks, and every per-row kernel runs thousands of workgroups."""
+    gam = np.random.default_rng(95).integers(0, 8, 3000).astype(np.int32)
+    _parity(H, workloads.small(seed=95, batch=3000, vocab=2048, dtype="bf16", gamma=gam))
+    wg = workloads.small(seed=96, batch=3000, vocab=2048, dtype="bf16", gamma=gam, mode="greedy")
+    _parity(H, wg, mode="greedy")
