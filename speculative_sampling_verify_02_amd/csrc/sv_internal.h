@@ -391,20 +391,6 @@ __device__ __forceinline__ RawUnit<DT> load_raw(const void *base, int64_t unit, 
 // Word 3 of a raw (untyped, offset-addressed) buffer resource on gfx9-family GPUs.
 constexpr int kBufferWord3 = 0x00020000;
 
-// One unit through a buffer resource at a byte offset (16-byte aligned data).
-template <int DT>
-__device__ __forceinline__ RawUnit<DT> buffer_unit(__amdgpu_buffer_rsrc_t rs, uint32_t off)
-{
-    RawUnit<DT> r;
-    if constexpr (DT == 0) {
-        r.a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, kLoadNT));
-    } else {
-        r.a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, kLoadNT));
-        r.b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 16), 0, kLoadNT));
-    }
-    return r;
-}
-
 template <int DT>
 __device__ __forceinline__ void unpack(const RawUnit<DT> &r, float *x)
 {
