@@ -231,8 +231,7 @@ extern "C" sv_status spec_sample(const void *logits, int32_t dtype, int64_t voca
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     hipError_t e = sv::launch_stats(P, s, dtype, aligned, g_prof_start, g_prof_stop);
-    if (e == hipSuccess) e = sv::launch_scan(P, s, dtype);
-    if (e == hipSuccess) e = sv::launch_draw_final(P, s, dtype, aligned);
+    if (e == hipSuccess) e = sv::launch_scan_draw(P, s, dtype, aligned);
     return e == hipSuccess ? SV_OK : SV_EHIP;
 }
 

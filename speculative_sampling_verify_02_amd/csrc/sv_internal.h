@@ -666,6 +666,7 @@ hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned,
 hipError_t launch_scan(const Params &P, hipStream_t s, int dtype);
 hipError_t launch_verify(const Params &P, hipStream_t s, int dtype, bool aligned);
 hipError_t launch_draw_final(const Params &P, hipStream_t s, int dtype, bool aligned);
+hipError_t launch_scan_draw(const Params &P, hipStream_t s, int dtype, bool aligned);
 hipError_t launch_tree(const TreeParams &T, hipStream_t s);
 hipError_t launch_stats_list(const Params &P, hipStream_t s, int dtype, bool aligned);
 hipError_t launch_ee_init(const Params &P, hipStream_t s);

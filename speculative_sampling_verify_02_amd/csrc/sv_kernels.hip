@@ -1158,6 +1158,19 @@ __global__ __launch_bounds__(kBlock) void draw_final_kernel(Params P)
     }
 }
 
+// The drafter's draw (every row a single position, no drafts): the scan and the draw
+// in one workgroup per vector, so the draw's inputs never pass through memory.
+template <int DT, bool AL>
+__global__ __launch_bounds__(kBlock) void scan_draw_kernel(Params P)
+{
+    __shared__ ScanLds sh;
+    __shared__ double s_ts[kPieceTiles<DT>];
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int32_t row = blockIdx.x;
+    const RowDraw D = scan_row<DT>(P, row, true, sh);
+    if (D.kind == DRAW_BONUS) draw_bonus_row<DT, AL>(P, D, row, lane, wave, s_ts);
+}
+
 // ===========================================================================
 // launchers
 // ===========================================================================
@@ -1200,6 +1213,14 @@ hipError_t launch_ee_step(const Params &P, hipStream_t s, int dtype)
 {
     const void *fn = dtype == 0 ? (const void *)ee_step_kernel<0> : (const void *)ee_step_kernel<1>;
     return launch(fn, P.B, 64, P, s);
+}
+
+hipError_t launch_scan_draw(const Params &P, hipStream_t s, int dtype, bool aligned)
+{
+    const void *fn = dtype == 0
+        ? (aligned ? (const void *)scan_draw_kernel<0, true> : (const void *)scan_draw_kernel<0, false>)
+        : (aligned ? (const void *)scan_draw_kernel<1, true> : (const void *)scan_draw_kernel<1, false>);
+    return launch(fn, P.B, kBlock, P, s);
 }
 
 hipError_t launch_draw_final(const Params &P, hipStream_t s, int dtype, bool aligned)
