@@ -303,8 +303,9 @@ def bench_tree(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
-                                   "part of it (rows shard independently, see the design notes)",
+        print(json.dumps({"error": "one GPU only: rows are independent, so a job on several GPUs "
+                                   "runs one call per GPU on its own rows; no multi-GPU run is "
+                                   "implemented or measured",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if args.op == "sample":

@@ -189,3 +189,18 @@ def test_filtered_host_argument_errors(sv):
     assert call(ws_bytes=sv.workspace_bytes(2, 6, 32, sv.SV_BF16)) == sv.SV_EWORKSPACE   # no room for thresholds
     assert call(batch=0, nT=0) == sv.SV_OK
     assert sv.filtered_workspace_bytes(2, 6, 32, sv.SV_BF16) > sv.workspace_bytes(2, 6, 32, sv.SV_BF16)
+
+
+def test_bench_refuses_several_gpus():
+    """The benchmark runs on one GPU: asking for more exits with status 2 and one JSON
+    line that says so, before anything touches a GPU."""
+    import json
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300, cwd=root)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == 2 and "one GPU only" in line["error"]
