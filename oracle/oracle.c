@@ -25,7 +25,7 @@
  *    "Speculative decoding", section "The greedy case"; brunomaga.github.io, section
  *    "Draft-model speculative decoding", greedy paragraph).
  *
- * Readings where the pages leave a step open (each also listed in the design notes):
+ * Readings where the pages leave a step open:
  *  - p is the target, q the drafter (the rayaq.ca and cgnarendiran.github.io naming;
  *    brunomaga.github.io swaps the letters, not the rule);
  *  - the test is strict, u < ratio, with u in [0, 1);
