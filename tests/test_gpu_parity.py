@@ -299,3 +299,31 @@ def test_many_rows(H):
     _parity(H, workloads.small(seed=95, batch=3000, vocab=2048, dtype="bf16", gamma=gam))
     wg = workloads.small(seed=96, batch=3000, vocab=2048, dtype="bf16", gamma=gam, mode="greedy")
     _parity(H, wg, mode="greedy")
+
+
+def test_profile_events(H):
+    """Events handed to spec_verify_set_profile_events are attached to the streaming
+    kernel's dispatch: after a call they bound a short, positive interval."""
+    import torch
+    import bench
+    import speculative_sampling_verify_02_amd as sv
+    ev = bench.HipEvents()
+    a, b = ev.create(), ev.create()
+    w = workloads.small(seed=97, batch=6, vocab=8192, dtype="bf16", gamma=3)
+    d = H.to_device(w)
+    dev = d["target"].device
+    try:
+        sv.set_profile_events(a, b)
+        sv.spec_verify(d["target"], d["draft"], d["tokens"], d["uniforms"], d["temperature"], int(w.gamma[0]))
+        torch.cuda.synchronize()
+        t_verify = ev.elapsed_ms(a, b)
+        n = d["target"].shape[0]
+        sv.spec_sample(d["target"], torch.rand(n, device=dev), torch.ones(n, device=dev))
+        torch.cuda.synchronize()
+        t_sample = ev.elapsed_ms(a, b)
+    finally:
+        sv.set_profile_events(None, None)
+        ev.destroy(a)
+        ev.destroy(b)
+    _say(f"[ok] streaming kernel {t_verify * 1e3:.1f} us (verify), {t_sample * 1e3:.1f} us (sample)")
+    assert 0.0 < t_verify < 50.0 and 0.0 < t_sample < 50.0
