@@ -31,6 +31,7 @@ __device__ __forceinline__ uint32_t order_key(float x)
 struct TreeLds {
     unsigned long long key[kMaxTreeNodes];   // per node: value key << 32 | (INT32_MAX - index)
     int32_t anc[kMaxTreeNodes];
+    int32_t par[kMaxTreeNodes];                // tree-local parent (-1 at the root)
     int32_t dep[kMaxTreeNodes];
     int32_t acc[kMaxTreeNodes];
     int32_t tok[kMaxTreeNodes];
@@ -94,16 +95,19 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeParams T)
         if (k == 0 ? par != -1 : (par < 0 || par >= k)) st |= ST_BAD_TREE;
         if (tk < 0 || (int64_t)tk >= T.V) st |= ST_BAD_TOKEN;
         sh.anc[k] = k == 0 ? -1 : par;
+        sh.par[k] = k == 0 ? -1 : par;
         sh.tok[k] = tk;
         sh.key[k] = 0ull;
     }
     __syncthreads();
     // predictions: every record of the tree's vectors into its node's key
-    const int64_t nrec = (int64_t)n * T.ipv;
+    // (n <= kMaxTreeNodes nodes of ipv records each: the indices fit 32 bits)
+    const uint32_t ipv32 = (uint32_t)T.ipv;
+    const uint32_t nrec = (uint32_t)n * ipv32;
     const Partial *rec = T.parts + off * T.ipv;
-    for (int64_t r = tid; r < nrec; r += kBlock) {
+    for (uint32_t r = tid; r < nrec; r += kBlock) {
         const Partial q = rec[r];
-        const int64_t k = r / T.ipv;
+        const uint32_t k = r / ipv32;
         const uint32_t idx = q.idx == INT32_MAX ? 0u : (uint32_t)(INT32_MAX - q.idx);
         atomicMax(&sh.key[k], ((unsigned long long)order_key(q.m) << 32) | idx);
     }
@@ -167,14 +171,14 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeParams T)
         __syncthreads();
         const int best = INT32_MAX - (int32_t)(uint32_t)(sh.best & 0xffffffffu);
         const int depth = (int)(sh.best >> 32);
-        // the path, root first: one thread walks up the parents into the anc array
-        // (free again), then every slot is written in parallel
+        // the path, root first: one thread walks up the parents (held in LDS) into the
+        // anc array (free again), then every slot is written in parallel
         __syncthreads();
         if (tid == 0) {
             int k = best;
             for (int d = depth; d >= 0; --d) {
                 sh.anc[d] = k;
-                k = T.parents[off + k];   // tree-local parent (the anc array is reused)
+                k = sh.par[k];
             }
         }
         __syncthreads();
