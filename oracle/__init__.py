@@ -27,6 +27,9 @@ ZERO_RESID = 16
 BAD_TEMP = 32
 BAD_TREE = 64
 INVALID_MASK = BAD_TOKEN | NONFINITE | BAD_GAMMA | BAD_TEMP | BAD_TREE
+# per-decision flags (verify()["flags"])
+FLAG_NEAR = 1     # the decision lies within flag_eps of its threshold
+FLAG_FILTER = 2   # a top-p boundary within 1e-10 at this position
 
 _DTYPES = {"bf16": BF16, "f32": F32, "f64": F64}
 
@@ -55,16 +58,18 @@ def _load(path: str):
     L.oracle_position.restype = ctypes.c_int
     L.oracle_inverse_cdf.argtypes = [vp, i64, dbl, dbl, vp, vp]
     L.oracle_inverse_cdf.restype = i64
+    L.oracle_inverse_cdf_range.argtypes = [vp, i64, dbl, dbl, vp, vp, vp, vp]
+    L.oracle_inverse_cdf_range.restype = i64
     L.oracle_verify.argtypes = [vp, vp, ctypes.c_int, i64, i32, i64, vp, vp, vp, vp,
                                 ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, dbl, ctypes.c_int]
     L.oracle_verify.restype = ctypes.c_int
     L.oracle_verify_ex.argtypes = [vp, vp, ctypes.c_int, i64, i32, i64, vp, vp, vp, vp,
                                    ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, dbl, ctypes.c_int,
-                                   ctypes.c_int, vp, vp, vp, vp]
+                                   ctypes.c_int, vp, vp, vp, vp, vp, vp, vp]
     L.oracle_verify_ex.restype = ctypes.c_int
     L.oracle_filter_threshold.argtypes = [vp, ctypes.c_int, i64, dbl, i64, dbl, dbl, vp, vp]
     L.oracle_filter_threshold.restype = ctypes.c_int
-    L.oracle_sample.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, vp, dbl, ctypes.c_int]
+    L.oracle_sample.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, vp, dbl, ctypes.c_int, vp, vp]
     L.oracle_sample.restype = ctypes.c_int
     L.oracle_tree_greedy.argtypes = [vp, ctypes.c_int, i64, i32, i64, vp, vp, vp, vp, vp, vp, vp,
                                      ctypes.c_int]
@@ -150,13 +155,30 @@ def inverse_cdf(w, u: float, eps: float = 1e-5):
     return int(tok), float(W[0]), bool(near[0])
 
 
+def inverse_cdf_range(w, u: float, eps: float = 1e-5):
+    """(token, W, near_edge, lo, hi): the draw, and the first and last tokens with
+    weight whose CDF interval comes within eps * W of the threshold u * W (lo = hi =
+    token when the draw is not near an edge)."""
+    w = np.ascontiguousarray(w, np.float64)
+    W = np.zeros(1, np.float64)
+    near = np.zeros(1, np.int32)
+    lo = np.zeros(1, np.int64)
+    hi = np.zeros(1, np.int64)
+    tok = lib().oracle_inverse_cdf_range(_ptr(w), w.shape[0], float(u), float(eps), _ptr(W), _ptr(near),
+                                         _ptr(lo), _ptr(hi))
+    return int(tok), float(W[0]), bool(near[0]), int(lo[0]), int(hi[0])
+
+
 def verify(target, draft, dtype: str, vocab: int, gamma, draft_tokens, uniforms, temperature,
            mode: str = "sample", n_target_rows=None, threads: int = 0,
            flag_eps: float = 1e-5, early_exit: bool = False, cache_len=None, top_k=None,
            top_p=None) -> dict:
     """One verification round over a packed batch; returns numpy arrays.  flag_pos[i] is
     the first decision of row i within flag_eps of its threshold (accept test j, or
-    gamma_i for the draw), -1 if none.  early_exit reads positions left to right and
+    gamma_i for the draw), -1 if none; flags[t_off[i] + j] has FLAG_NEAR for every
+    such decision (test j < gamma_i, or the draw at j = gamma_i) and FLAG_FILTER where
+    a top-p boundary lies within 1e-10; [draw_lo[i], draw_hi[i]] are the tokens a near
+    draw could return (both equal the drawn token otherwise).  early_exit reads positions left to right and
     stops at the first rejection; crop_len[i] = cache_len[i] + K_i + 1 (-1 if invalid).
     top_k (int32 [B]) and top_p (float32 [B]) filter p and q of each sampling row
     (see filter_threshold)."""
@@ -178,6 +200,9 @@ def verify(target, draft, dtype: str, vocab: int, gamma, draft_tokens, uniforms,
         resid_mass=np.empty(B, np.float64),
         row_status=np.empty(B, np.int32),
         flag_pos=np.empty(B, np.int32),
+        flags=np.empty(n_target_rows, np.int32),
+        draw_lo=np.empty(B, np.int32),
+        draw_hi=np.empty(B, np.int32),
     )
     out["crop_len"] = np.empty(B, np.int32)
     cl = None if cache_len is None else np.ascontiguousarray(cache_len, np.int32)
@@ -189,7 +214,8 @@ def verify(target, draft, dtype: str, vocab: int, gamma, draft_tokens, uniforms,
                                 _ptr(out["n_accepted"]), _ptr(out["emitted"]), _ptr(out["p_x"]),
                                 _ptr(out["q_x"]), _ptr(out["resid_mass"]), _ptr(out["row_status"]),
                                 _ptr(out["flag_pos"]), float(flag_eps), int(threads), int(bool(early_exit)),
-                                _ptr(cl), _ptr(out["crop_len"]), _ptr(tk), _ptr(tp))
+                                _ptr(cl), _ptr(out["crop_len"]), _ptr(tk), _ptr(tp), _ptr(out["flags"]),
+                                _ptr(out["draw_lo"]), _ptr(out["draw_hi"]))
     if rc != 0:
         raise ValueError(f"oracle_verify status {rc}")
     return out
@@ -212,7 +238,8 @@ def sample(logits, dtype: str, vocab: int, temperature, uniforms, threads: int =
            flag_eps: float = 1e-5) -> dict:
     """The drafter's draw: one token per logit vector (x ~ softmax(z/T) by inverse CDF
     with that vector's uniform; argmax where T <= 0).  Returns tokens, status and
-    flags (1 where the draw's threshold is within flag_eps * W of an interior edge)."""
+    flags (1 where the draw's threshold is within flag_eps * W of an interior edge),
+    and lo / hi, the tokens such a draw could return (both = the token otherwise)."""
     z = _logits(logits, dtype)
     n = z.size // vocab
     temperature = np.ascontiguousarray(temperature, np.float32)
@@ -220,10 +247,11 @@ def sample(logits, dtype: str, vocab: int, temperature, uniforms, threads: int =
     if temperature.shape[0] != n or uniforms.shape[0] != n:
         raise ValueError("one temperature and one uniform per vector")
     out = dict(tokens=np.empty(n, np.int32), status=np.empty(n, np.int32),
-               flags=np.empty(n, np.int32))
+               flags=np.empty(n, np.int32), lo=np.empty(n, np.int32), hi=np.empty(n, np.int32))
     rc = lib().oracle_sample(_ptr(z), _DTYPES[dtype], int(vocab), int(n), _ptr(temperature),
                              _ptr(uniforms), _ptr(out["tokens"]), _ptr(out["status"]),
-                             _ptr(out["flags"]), float(flag_eps), int(threads))
+                             _ptr(out["flags"]), float(flag_eps), int(threads), _ptr(out["lo"]),
+                             _ptr(out["hi"]))
     if rc != 0:
         raise ValueError(f"oracle_sample status {rc}")
     return out

@@ -42,8 +42,12 @@
  *    invalid (NONFINITE); -inf elsewhere is an ordinary zero-probability token;
  *  - a decision whose threshold is within eps of its input (|u - ratio| < eps for a
  *    test, |C - t| < eps * W at an interior edge of the drawn token's CDF interval
- *    for a draw; eps = 1e-5 unless the caller passes another) is reported in flag_pos
- *    so comparisons can exclude it.
+ *    for a draw; eps = 1e-5 unless the caller passes another) is "near": flag_pos
+ *    holds a row's first near decision, flags[] marks every one (slot t_off + j for
+ *    test j, slot t_off + gamma for the draw), and [draw_lo, draw_hi] bound the tokens
+ *    a near draw could return (those whose CDF interval comes within eps * W of the
+ *    threshold), so that a comparison with arithmetic of another precision can hold
+ *    each decision to exactly what its input fixes.
  */
 #include <float.h>
 #include <math.h>
@@ -259,8 +263,14 @@ out:
 /* ------------------------------------------------------------------------- */
 /* the inverse-CDF draw                                                        */
 /* ------------------------------------------------------------------------- */
-int64_t oracle_inverse_cdf(const double *w, int64_t V, double u, double eps, double *W_out,
-                           int *near_edge)
+/* The draw with weights w: W = sum(w), t = u * W, the token is the smallest v whose
+ * running sum C_v exceeds t.  *near_edge = 1 when t lies within eps * W of an interior
+ * edge of that token's interval [C_{v-1}, C_v); then [*lo, *hi] are the first and last
+ * tokens with positive weight whose interval comes within eps * W of t (the tokens a
+ * draw could return whose threshold or running sums were off by eps * W).  Otherwise
+ * *lo = *hi = the token. */
+int64_t oracle_inverse_cdf_range(const double *w, int64_t V, double u, double eps, double *W_out,
+                                 int *near_edge, int64_t *lo, int64_t *hi)
 {
     double W = 0.0;
     for (int64_t v = 0; v < V; ++v)
@@ -287,12 +297,38 @@ int64_t oracle_inverse_cdf(const double *w, int64_t V, double u, double eps, dou
     }
     /* only interior edges are decision boundaries: the lower edge when some earlier
        token has weight, the upper edge when some later token has weight */
+    const int near = (C_prev > 0 && fabs(C_prev - t) < eps * W) || (C < W && fabs(C - t) < eps * W);
+    int64_t a = token, b = token;
+    if (near) {
+        double c = 0.0;
+        a = b = -1;
+        for (int64_t v = 0; v < V; ++v) {
+            const double before = c;
+            c += w[v];
+            if (w[v] > 0 && c >= t - eps * W && before <= t + eps * W) {
+                if (a < 0)
+                    a = v;
+                b = v;
+            }
+        }
+        if (a < 0)
+            a = b = token;
+    }
     if (near_edge)
-        *near_edge = (C_prev > 0 && fabs(C_prev - t) < eps * W) ||
-                     (C < W && fabs(C - t) < eps * W);
+        *near_edge = near;
+    if (lo)
+        *lo = a;
+    if (hi)
+        *hi = b;
     if (W_out)
         *W_out = W;
     return token;
+}
+
+int64_t oracle_inverse_cdf(const double *w, int64_t V, double u, double eps, double *W_out,
+                           int *near_edge)
+{
+    return oracle_inverse_cdf_range(w, V, u, eps, W_out, near_edge, NULL, NULL);
 }
 
 /* ------------------------------------------------------------------------- */
@@ -373,7 +409,8 @@ int oracle_verify_ex(const void *target, const void *draft, int dtype, int64_t V
                      int32_t *n_accepted, int32_t *emitted, double *p_x, double *q_x,
                      double *resid_mass, int32_t *row_status, int32_t *flag_pos, double flag_eps,
                      int nthreads, int early_exit, const int32_t *cache_len, int32_t *crop_len,
-                     const int32_t *top_k, const float *top_p)
+                     const int32_t *top_k, const float *top_p, int32_t *flags, int32_t *draw_lo,
+                     int32_t *draw_hi)
 {
     const double eps = flag_eps > 0 ? flag_eps : 1e-5;
     if (!target || !gamma_per_row || !uniforms || !temperature || !n_accepted || !emitted ||
@@ -414,9 +451,16 @@ int oracle_verify_ex(const void *target, const void *draft, int dtype, int64_t V
                 resid_mass[i] = NAN;
             if (crop_len)
                 crop_len[i] = -1;
+            if (draw_lo)
+                draw_lo[i] = -1;
+            if (draw_hi)
+                draw_hi[i] = -1;
         }
-        for (int64_t k = 0; k < n_target_rows; ++k)
+        for (int64_t k = 0; k < n_target_rows; ++k) {
             emitted[k] = -1;
+            if (flags)
+                flags[k] = 0;
+        }
         free(t_off);
         free(d_off);
         return 0;
@@ -447,6 +491,13 @@ int oracle_verify_ex(const void *target, const void *draft, int dtype, int64_t V
             const double T = (double)temperature[i];
             int status = 0, flag = -1;
             int greedy = mode == ORACLE_GREEDY;
+            if (flags)
+                for (int j = 0; j <= g; ++j)
+                    flags[t0 + j] = 0;
+            if (draw_lo)
+                draw_lo[i] = -1;
+            if (draw_hi)
+                draw_hi[i] = -1;
             if (!greedy) {
                 if (!isfinite(T))
                     status |= ORACLE_BAD_TEMP;
@@ -484,8 +535,12 @@ int oracle_verify_ex(const void *target, const void *draft, int dtype, int64_t V
                     if (j < g)
                         oracle_filter_threshold(vector_ptr(draft, dtype, d0 + j, V), dtype, V, T, row_k,
                                                 row_p, 1e-10, &th_d[j], &nd);
-                    if ((nt || nd) && flag < 0)
-                        flag = j;
+                    if (nt || nd) {
+                        if (flag < 0)
+                            flag = j;
+                        if (flags)
+                            flags[t0 + j] |= ORACLE_FLAG_FILTER;
+                    }
                 }
             }
 #define THETA_T(j) (th_t ? th_t[j] : -INFINITY)
@@ -553,6 +608,10 @@ int oracle_verify_ex(const void *target, const void *draft, int dtype, int64_t V
                 emitted[t0 + K] = (int32_t)aK;
                 for (int j = K + 1; j <= g; ++j)
                     emitted[t0 + j] = -1;
+                if (draw_lo)
+                    draw_lo[i] = (int32_t)aK;
+                if (draw_hi)
+                    draw_hi[i] = (int32_t)aK;
                 n_accepted[i] = K;
                 if (crop_len)
                     crop_len[i] = kept_cache_entries(cache_len, i, K);
@@ -598,8 +657,12 @@ int oracle_verify_ex(const void *target, const void *draft, int dtype, int64_t V
                     status |= ORACLE_Q_ZERO;
                 if (!decided) {
                     double u = (double)uniforms[t0 + j];
-                    if (flag < 0 && fabs(u - ratio) < eps)
-                        flag = j;
+                    if (fabs(u - ratio) < eps) {
+                        if (flag < 0)
+                            flag = j;
+                        if (flags)
+                            flags[t0 + j] |= ORACLE_FLAG_NEAR;
+                    }
                     if (!(u < ratio)) {
                         K = j;
                         decided = 1;
@@ -625,9 +688,18 @@ int oracle_verify_ex(const void *target, const void *draft, int dtype, int64_t V
             }
             double W;
             int near = 0;
-            int64_t tok = oracle_inverse_cdf(w, V, (double)uniforms[t0 + g], eps, &W, &near);
-            if (flag < 0 && near)
-                flag = g;
+            int64_t lo, hi;
+            int64_t tok = oracle_inverse_cdf_range(w, V, (double)uniforms[t0 + g], eps, &W, &near, &lo, &hi);
+            if (near) {
+                if (flag < 0)
+                    flag = g;
+                if (flags)
+                    flags[t0 + g] |= ORACLE_FLAG_NEAR;
+            }
+            if (draw_lo)
+                draw_lo[i] = (int32_t)lo;
+            if (draw_hi)
+                draw_hi[i] = (int32_t)hi;
             for (int j = 0; j < K; ++j)
                 emitted[t0 + j] = draft_tokens[d0 + j];
             emitted[t0 + K] = (int32_t)tok;
@@ -667,10 +739,11 @@ int oracle_verify_ex(const void *target, const void *draft, int dtype, int64_t V
  * section "Draft-model speculative decoding"); a non-finite or subnormal positive T
  * and a vector without a softmax make the entry invalid (token -1).  flags[i] = 1
  * when the draw's threshold lies within eps * W of an interior edge of the drawn
- * token's CDF interval. */
+ * token's CDF interval; [lo[i], hi[i]] are then the tokens whose interval comes within
+ * eps * W of it (lo = hi = the token otherwise). */
 int oracle_sample(const void *logits, int dtype, int64_t V, int64_t n, const float *temperature,
                   const float *uniforms, int32_t *tokens, int32_t *status_out, int32_t *flags,
-                  double flag_eps, int nthreads)
+                  double flag_eps, int nthreads, int32_t *lo, int32_t *hi)
 {
     const double eps = flag_eps > 0 ? flag_eps : 1e-5;
     if (!logits || !temperature || !uniforms || !tokens || V <= 0 || n < 0)
@@ -693,20 +766,24 @@ int oracle_sample(const void *logits, int dtype, int64_t V, int64_t n, const flo
             const void *z = vector_ptr(logits, dtype, i, V);
             const double T = (double)temperature[i];
             int status = 0, near = 0;
-            int64_t tok = -1;
+            int64_t tok = -1, a = -1, b = -1;
             if (!isfinite(T) || (T > 0 && T < (double)FLT_MIN))
                 status |= ORACLE_BAD_TEMP;
             if (vector_nonfinite(z, dtype, V))
                 status |= ORACLE_NONFINITE;
             if (!status) {
                 if (T <= 0) {
-                    tok = oracle_argmax(z, dtype, V);
+                    tok = a = b = oracle_argmax(z, dtype, V);
                 } else {
                     oracle_softmax(z, dtype, V, T, w);
-                    tok = oracle_inverse_cdf(w, V, (double)uniforms[i], eps, NULL, &near);
+                    tok = oracle_inverse_cdf_range(w, V, (double)uniforms[i], eps, NULL, &near, &a, &b);
                 }
             }
             tokens[i] = (int32_t)tok;
+            if (lo)
+                lo[i] = (int32_t)a;
+            if (hi)
+                hi[i] = (int32_t)b;
             if (status_out)
                 status_out[i] = status;
             if (flags)
@@ -855,5 +932,5 @@ int oracle_verify(const void *target, const void *draft, int dtype, int64_t V, i
     return oracle_verify_ex(target, draft, dtype, V, B, n_target_rows, draft_tokens, uniforms,
                             temperature, gamma_per_row, mode, n_accepted, emitted, p_x, q_x,
                             resid_mass, row_status, flag_pos, flag_eps, nthreads, 0, NULL, NULL, NULL,
-                            NULL);
+                            NULL, NULL, NULL, NULL);
 }

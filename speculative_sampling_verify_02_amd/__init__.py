@@ -249,6 +249,19 @@ def _verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, ga
         raise ValueError("uniforms must have one entry per target row")
     if draft_tokens is not None and draft_tokens.numel() != n_target_rows - B:
         raise ValueError("draft_tokens must have one entry per draft row")
+    n_draft_rows = n_target_rows - B
+    if draft_logits is not None:
+        # the kernels read n_draft_rows rows of V logits from this pointer
+        if draft_logits.dim() < 1 or int(draft_logits.shape[-1]) != V:
+            raise ValueError(f"draft_logits has {int(draft_logits.shape[-1]) if draft_logits.dim() else 0} "
+                             f"logits per row, the target {V}")
+        if draft_logits.numel() != n_draft_rows * V:
+            raise ValueError(f"draft_logits holds {draft_logits.numel() // max(V, 1)} rows, "
+                             f"{n_draft_rows} draft rows expected")
+    elif mode == "sample" and n_draft_rows > 0:
+        raise ValueError("draft_logits is required in sampling mode when rows have drafts")
+    if n_draft_rows > 0 and draft_tokens is None:
+        raise ValueError("draft_tokens is required when rows have drafts")
 
     if out is None:
         n_acc = torch.empty(B, dtype=torch.int32, device=device)

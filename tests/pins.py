@@ -605,6 +605,62 @@ def pin_strict_threshold_and_flags():
     assert r["emitted"][1] == 0 and r["flag_pos"][0] == -1
 
 
+def pin_every_near_decision_flagged():
+    """Each decision within 1e-5 of its threshold is flagged, not only the first, and
+    only decisions are: the page's all-accept round (ratios 3/4, 1, 5/7, bonus from
+    p(.|c) = (3/10, 1/5, 1/2)) with uniforms just below 3/4 and 5/7, far from 1, and
+    a draw 3e-6 above the CDF edge 1/2 between b and c; then the page's rejection
+    round with a uniform just above 5/7 and one near the unread third ratio."""
+    spec = ROUNDS["all_accept_round"]
+    drafts = np.array([[TOK[t] for t in spec["drafts"]]], np.int32)
+    below = lambda x: float(np.nextafter(np.float32(x), np.float32(0)))
+    u = np.array([[below(3 / 4), 0.5, below(5 / 7), float(np.float32(0.5 + 3e-6))]])
+    r = markov_verify([TOK["a"]], drafts, u)
+    assert r["n_accepted"][0] == 3 and r["emitted"][3] == TOK["c"], r
+    assert list(r["flags"]) == [oracle.FLAG_NEAR, 0, oracle.FLAG_NEAR, oracle.FLAG_NEAR], r["flags"]
+    assert r["flag_pos"][0] == 0
+    # the tokens a draw within 1e-5 of the edge could return: b and c
+    assert (r["draw_lo"][0], r["draw_hi"][0]) == (TOK["b"], TOK["c"])
+    u[0, 3] = 0.75
+    r = markov_verify([TOK["a"]], drafts, u)
+    assert r["flags"][3] == 0 and r["draw_lo"][0] == r["draw_hi"][0] == TOK["c"]
+    rej = ROUNDS["reject_round"]
+    drafts = np.array([[TOK[t] for t in rej["drafts"]]], np.int32)
+    above = float(np.nextafter(np.float32(5 / 7), np.float32(1)))
+    r = markov_verify([TOK["a"]], drafts, np.array([[0.085, above, F32_BELOW_ONE, 0.4]]))
+    assert r["n_accepted"][0] == 1 and r["emitted"][1] == TOK["a"], r
+    # the residual after c is (1, 0, 0): one token, no interior edge
+    assert list(r["flags"]) == [0, oracle.FLAG_NEAR, 0, 0], r["flags"]
+    assert r["draw_lo"][0] == r["draw_hi"][0] == TOK["a"]
+
+
+def pin_draw_range_by_perturbation():
+    """[lo, hi] of a draw are the first and last tokens that the plain inverse CDF
+    returns for thresholds within eps * W of t = u W: the draw is repeated over a
+    grid of uniforms in [u - eps, u + eps], with windows of one to several tokens."""
+    rng = np.random.default_rng(29)
+    for trial in range(300):
+        V = int(rng.integers(2, 60))
+        w = rng.random(V) * (rng.random(V) < 0.7)
+        if np.count_nonzero(w) < 2:
+            w[:2] = [0.3, 0.7]
+        C = np.cumsum(w) / w.sum()
+        eps = float(rng.choice([1e-5, 1e-3, 0.05]))
+        # uniforms near an interior edge, and anywhere
+        edges = C[:-1][(C[:-1] > 0) & (C[:-1] < 1)]
+        u = float(rng.choice(edges) + rng.uniform(-0.9, 0.9) * eps) if trial % 3 and edges.size else float(rng.random())
+        u = min(max(u, 0.0), 1.0 - 1e-12)
+        tok, W, near, lo, hi = oracle.inverse_cdf_range(w, u, eps)
+        assert tok == oracle.inverse_cdf(w, u, eps)[0]
+        grid = np.clip(np.linspace(u - eps, u + eps, 4001), 0.0, 1.0 - 1e-12)
+        seen = sorted({oracle.inverse_cdf(w, g)[0] for g in grid})
+        if not near:
+            assert lo == hi == tok
+            continue
+        assert seen[0] == lo and seen[-1] == hi, (trial, u, eps, seen, lo, hi)
+        assert w[lo] > 0 and w[hi] > 0 and lo <= tok <= hi
+
+
 # --------------------------------------------------------------------------- #
 # status rules
 # --------------------------------------------------------------------------- #
@@ -862,20 +918,25 @@ def pin_tree_status():
 # --------------------------------------------------------------------------- #
 def pin_early_exit_page_round():
     """The page's round with a rejection, read left to right: the same decisions and
-    page values, nothing computed after the rejection, and n + K + 1 = n + 2 cache
-    entries kept."""
+    page values, nothing computed after the rejection, and the page's cache counts:
+    5 entries before the round, 9 after the verification pass wrote the last token and
+    the three drafts, 7 kept once one draft is accepted (rayaq.ca "Speculative
+    decoding", section "A round with a rejection")."""
     spec = ROUNDS["reject_round"]
     drafts = np.array([[TOK[t] for t in spec["drafts"]]], np.int32)
     u = np.array([[spec["positions"][0]["u"], spec["positions"][1]["u"], 0.5, 0.3]])
-    r = markov_verify([TOK["a"]], drafts, u, early_exit=True, cache_len=[7])
+    before = spec["cache_entries_before"]
+    # the fixture is the page's: the verification pass adds the last token and gamma drafts
+    assert before + 1 + spec["gamma"] == spec["cache_entries_after_verify"]
+    r = markov_verify([TOK["a"]], drafts, u, early_exit=True, cache_len=[before])
     assert r["n_accepted"][0] == spec["n_accepted"] == 1
     assert [t for t in r["emitted"] if t >= 0] == [TOK[t] for t in spec["emitted"]]
     _close(r["p_x"][1] / r["q_x"][1], 5 / 7, 1e-15, "ratio 5/7")
     assert np.isnan(r["p_x"][2]) and np.isnan(r["q_x"][2])
-    assert r["crop_len"][0] == 7 + 1 + 1
-    full = markov_verify([TOK["a"]], drafts, u, cache_len=[7])
+    assert r["crop_len"][0] == spec["cache_entries_kept"], r["crop_len"]
+    full = markov_verify([TOK["a"]], drafts, u, cache_len=[before])
     assert not np.isnan(full["p_x"][2])
-    assert full["crop_len"][0] == 9
+    assert full["crop_len"][0] == spec["cache_entries_kept"]
 
 
 def pin_early_exit_matches_full_round():

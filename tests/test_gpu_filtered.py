@@ -58,7 +58,7 @@ def parity(H, w, k, p, dense=False):
     _say(f"[case] filtered {w.name} B={w.batch} V={w.vocab} top_k={k[:4]} top_p={p[:4]}")
     g = run_filtered(H, w, k, p, dense=dense)
     ref = oracle.verify_workload(w, top_k=k, top_p=p)
-    rep = H.compare(w, g, ref)
+    rep = H.compare(w, g, ref, oracle_kw=dict(top_k=k, top_p=p))
     _say(f"[ok] {rep}")
     return g, ref
 
@@ -94,17 +94,44 @@ def test_top1_is_greedy(H):
     assert np.array_equal(g["emitted"], ref["emitted"])
 
 
+def _filtered_path_exercised(w, ref, min_bonus=0):
+    """The drafts come from the drafter's top-k set, so the filtered ratio and residual
+    path runs on most positions: few rows see q(x) = 0, most reject with a residual of
+    positive mass, and (where asked) rows reach the filtered bonus draw."""
+    st, K = ref["row_status"], ref["n_accepted"]
+    q_zero = float(((st & oracle.Q_ZERO) != 0).mean())
+    rejects = int(((K >= 0) & (K < w.gamma) & (ref["resid_mass"] > 0)).sum())
+    bonus = int((K == w.gamma).sum())
+    _say(f"[ok] q(x)=0 on {q_zero:.3f} of rows, {rejects} residual draws, {bonus} bonus draws")
+    assert q_zero < 0.10
+    assert rejects >= min(w.batch // 2, 20) or bonus >= 0.3 * w.batch
+    assert bonus >= min_bonus
+
+
 def test_c3_full(H):
-    """The V = 128256 bf16 batch with top-k 50 and top-p 0.9 on every row."""
-    w = workloads.c3()
-    parity(H, w, np.full(w.batch, 50, np.int32), np.full(w.batch, 0.9, np.float32), dense=True)
+    """The V = 128256 bf16 batch with top-k 50 and top-p 0.9 on every row, drafts drawn
+    from the drafter's 20 largest logits (inside its kept set on nearly every
+    position, as a drafter that samples from filtered q would draw them)."""
+    w = workloads.c3(draft_top_k=20)
+    g, ref = parity(H, w, np.full(w.batch, 50, np.int32), np.full(w.batch, 0.9, np.float32), dense=True)
+    _filtered_path_exercised(w, ref)
+
+
+def test_c3_full_near_target_bonus(H):
+    """The same filter on the V = 128256 batch with a draft close to its target: most
+    rows keep every draft and draw the bonus from the filtered p at full size."""
+    w = workloads.c3(seed=33, draft_scale=1.0, draft_sigma=0.2, draft_top_k=20)
+    g, ref = parity(H, w, np.full(w.batch, 50, np.int32), np.full(w.batch, 0.9, np.float32), dense=True)
+    _filtered_path_exercised(w, ref, min_bonus=int(0.3 * w.batch))
 
 
 def test_c4_full(H):
     """The V = 152064 bf16 batch (B = 256, gamma = 8) with top-k 50 and top-p 0.9: the
-    one-pass kernel at 20 units per thread, looping over 4352 vectors."""
-    w = workloads.c4()
-    parity(H, w, np.full(w.batch, 50, np.int32), np.full(w.batch, 0.9, np.float32), dense=True)
+    one-pass kernel at 20 units per thread, looping over 4352 vectors; drafts from the
+    drafter's 20 largest logits."""
+    w = workloads.c4(draft_top_k=20)
+    g, ref = parity(H, w, np.full(w.batch, 50, np.int32), np.full(w.batch, 0.9, np.float32), dense=True)
+    _filtered_path_exercised(w, ref, min_bonus=1)
 
 
 def test_c3_full_top_p_only(H):

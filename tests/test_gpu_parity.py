@@ -22,7 +22,10 @@ def H():
     return gpu_harness
 
 
-def _parity(H, w, mode=None, dense=False, strict_eps=1e-7):
+def _parity(H, w, mode=None, dense=False, strict_eps=1e-7, assert_strict=False):
+    """Parity with the oracle (see gpu_harness.compare).  Also counts the rows whose
+    decisions all lie further than strict_eps from their thresholds but differ; with
+    assert_strict that count must be 0."""
     _say(f"[case] {w.name} mode={mode or w.mode} dense={dense} B={w.batch} V={w.vocab}")
     gpu = H.run_gpu(w, mode=mode, dense=dense)
     ref = oracle.verify_workload(w, mode=mode)
@@ -30,6 +33,8 @@ def _parity(H, w, mode=None, dense=False, strict_eps=1e-7):
     if (mode or w.mode) == "sample":
         strict = oracle.verify_workload(w, mode=mode, flag_eps=strict_eps)
         rep["strict_checked_mismatched"] = H.check_strict(w, gpu, strict)
+        if assert_strict:
+            assert rep["strict_checked_mismatched"][1] == 0, rep
     _say(f"[ok] {rep}")
     return gpu, ref, rep
 
@@ -272,24 +277,36 @@ def test_c2_full(H):
 
 @pytest.mark.parametrize("mode", ["sample", "greedy"])
 def test_c3_full(H, mode):
-    _parity(H, workloads.c3(mode=mode), mode=mode, dense=True)
+    _parity(H, workloads.c3(mode=mode), mode=mode, dense=True, assert_strict=True)
 
 
 def test_c4_full(H):
-    _parity(H, workloads.c4(), dense=True)
+    _parity(H, workloads.c4(), dense=True, assert_strict=True)
 
 
 def test_c5_full(H):
-    _parity(H, workloads.c5())
+    _parity(H, workloads.c5(), assert_strict=True)
 
 
 @pytest.mark.parametrize("seed", [13, 23])
 def test_c3_more_seeds(H, seed):
-    _parity(H, workloads.c3(seed=seed), dense=True)
+    _parity(H, workloads.c3(seed=seed), dense=True, assert_strict=True)
 
 
 def test_c4_second_seed(H):
-    _parity(H, workloads.c4(seed=14), dense=True)
+    _parity(H, workloads.c4(seed=14), dense=True, assert_strict=True)
+
+
+def test_c3_near_target_draft_reaches_bonus(H):
+    """The V = 128256 batch with a draft close to its target (draft = target + N(0, 0.2)):
+    most rows keep every draft, so the bonus draw from the streaming pass's piece sums
+    runs on most rows at full size (rayaq.ca "Speculative decoding", section "One
+    round", step 5)."""
+    w = workloads.c3(seed=33, draft_scale=1.0, draft_sigma=0.2)
+    gpu, ref, rep = _parity(H, w, dense=True, assert_strict=True)
+    bonus = int((ref["n_accepted"] == w.gamma).sum())
+    _say(f"[ok] bonus rows {bonus} of {w.batch}")
+    assert bonus >= 0.3 * w.batch
 
 
 def test_many_rows(H):
@@ -327,3 +344,27 @@ def test_profile_events(H):
         ev.destroy(b)
     _say(f"[ok] streaming kernel {t_verify * 1e3:.1f} us (verify), {t_sample * 1e3:.1f} us (sample)")
     assert 0.0 < t_verify < 50.0 and 0.0 < t_sample < 50.0
+
+
+def test_binding_rejects_mismatched_draft_logits(H):
+    """A drafter whose vocabulary or row count does not match the target's is refused
+    by the binding before anything is launched (the kernels would read past the
+    draft tensor or stride the wrong rows)."""
+    import torch
+    import speculative_sampling_verify_02_amd as sv
+    w = workloads.small(seed=98, batch=4, vocab=1000, dtype="bf16", gamma=2)
+    d = H.to_device(w)
+    padded = torch.zeros((w.n_draft_rows, 1024), dtype=torch.bfloat16, device=d["draft"].device)
+    short = d["draft"][:-1]
+    for bad, msg in ((padded, "logits per row"), (short, "draft rows expected")):
+        with pytest.raises(ValueError, match=msg):
+            sv.spec_verify(d["target"], bad, d["tokens"], d["uniforms"], d["temperature"], d["gamma"])
+        with pytest.raises(ValueError, match=msg):
+            sv.spec_verify_filtered(d["target"], bad, d["tokens"], d["uniforms"], d["temperature"], d["gamma"],
+                                    top_k=torch.full((4,), 5, dtype=torch.int32, device=bad.device))
+        with pytest.raises(ValueError, match=msg):
+            sv.spec_verify_early_exit(d["target"], bad, d["tokens"], d["uniforms"], d["temperature"],
+                                      d["gamma"], gamma_max=2)
+    with pytest.raises(ValueError, match="required in sampling mode"):
+        sv.spec_verify(d["target"], None, d["tokens"], d["uniforms"], d["temperature"], d["gamma"])
+    torch.cuda.synchronize()

@@ -2,7 +2,8 @@
 
 Parity rule: status bits identical on every vector; the token identical wherever
 the oracle finds the draw's threshold farther than 1e-5 W from an interior edge of
-the drawn token's CDF interval; elsewhere a valid token.  Greedy vectors (T <= 0)
+the drawn token's CDF interval; elsewhere one of the tokens whose CDF interval comes
+within 1e-5 W of the threshold (the oracle's [lo, hi]).  Greedy vectors (T <= 0)
 match bit for bit.
 """
 from __future__ import annotations
@@ -46,7 +47,9 @@ def check(si, tok, st, ref):
     diff = np.nonzero(free & (tok != ref["tokens"]))[0]
     assert diff.size == 0, f"tokens differ at {diff[:10]}: gpu {tok[diff[:10]]} oracle {ref['tokens'][diff[:10]]}"
     flagged = np.nonzero(~free)[0]
-    assert np.all((tok[flagged] >= 0) & (tok[flagged] < si.vocab))
+    out = flagged[(tok[flagged] < ref["lo"][flagged]) | (tok[flagged] > ref["hi"][flagged])]
+    assert out.size == 0, (f"near draws outside the oracle's admissible tokens at {out[:10]}: gpu {tok[out[:10]]} "
+                           f"range {ref['lo'][out[:10]]}..{ref['hi'][out[:10]]}")
     return dict(n=si.n, flagged=int(flagged.size), flagged_differ=int((tok[flagged] != ref["tokens"][flagged]).sum()))
 
 

@@ -21,8 +21,8 @@ MUTANTS = {
     "bonus_wrong_position": (
         "softmax_kept(vector_ptr(target, dtype, t0 + K, V), dtype, V, T, THETA_T(K), P);",
         "softmax_kept(vector_ptr(target, dtype, t0 + (K == g && K > 0 ? K - 1 : K), V), dtype, V, T, THETA_T(K), P);"),
-    "draw_reuses_test_uniform": ("(double)uniforms[t0 + g], eps, &W, &near)",
-                                 "(double)uniforms[t0 + K], eps, &W, &near)"),
+    "draw_reuses_test_uniform": ("(double)uniforms[t0 + g], eps, &W, &near, &lo, &hi)",
+                                 "(double)uniforms[t0 + K], eps, &W, &near, &lo, &hi)"),
     "q_sum_without_temperature": ("vector_max_sumexp(zd, dtype, V, T, theta_d, &md, &Sd);",
                                   "vector_max_sumexp(zd, dtype, V, 1.0, theta_d, &md, &Sd);"),
     "sumexp_without_temperature": ("S += exp((kept_logit(z, dtype, v, theta) - m) / T);",
@@ -34,11 +34,11 @@ MUTANTS = {
     "cdf_nonstrict": ("        if (C > t) {", "        if (C >= t) {"),
     "draw_unnormalized": ("    double t = u * W;", "    double t = u;"),
     "alpha_with_max": ("a += fmin(pp[v], qq[v]);", "a += fmax(pp[v], qq[v]);"),
-    "flag_threshold_too_wide": ("if (flag < 0 && fabs(u - ratio) < eps)", "if (flag < 0 && fabs(u - ratio) < 100 * eps)"),
+    "flag_threshold_too_wide": ("if (fabs(u - ratio) < eps) {", "if (fabs(u - ratio) < 100 * eps) {"),
     "no_zero_residual_fallback": ("                if (W == 0.0) {", "                if (W < 0.0) {"),
     "sample_without_temperature": ("oracle_softmax(z, dtype, V, T, w);", "oracle_softmax(z, dtype, V, 1.0, w);"),
-    "sample_first_uniform": ("tok = oracle_inverse_cdf(w, V, (double)uniforms[i], eps, NULL, &near);",
-                             "tok = oracle_inverse_cdf(w, V, (double)uniforms[0], eps, NULL, &near);"),
+    "sample_first_uniform": ("oracle_inverse_cdf_range(w, V, (double)uniforms[i], eps, NULL, &near, &a, &b);",
+                             "oracle_inverse_cdf_range(w, V, (double)uniforms[0], eps, NULL, &near, &a, &b);"),
     "sample_greedy_below_one": ("                if (T <= 0) {", "                if (T < 1) {"),
     "tree_own_prediction": ("(int64_t)tokens[o + k] == pred[par]", "(int64_t)tokens[o + k] == pred[k]"),
     "tree_last_longest": ("                if (len[k] > len[best])", "                if (len[k] >= len[best])"),
@@ -53,6 +53,10 @@ MUTANTS = {
     "top_p_overshoots": ("            if (cum >= target) {", "            if (cum > target * 1.05) {"),
     "filter_only_target": ("                        oracle_filter_threshold(vector_ptr(draft, dtype, d0 + j, V), dtype, V, T, row_k,",
                            "                        oracle_filter_threshold(vector_ptr(draft, dtype, d0 + j, V), dtype, V, T, 0 * row_k,"),
+    "flags_only_first_near": ("                        if (flags)\n                            flags[t0 + j] |= ORACLE_FLAG_NEAR;",
+                              "                        if (flags && flag == j)\n                            flags[t0 + j] |= ORACLE_FLAG_NEAR;"),
+    "draw_range_drops_lower": ("if (w[v] > 0 && c >= t - eps * W && before <= t + eps * W) {",
+                               "if (w[v] > 0 && c > t && before <= t + eps * W) {"),
     "neg_inf_is_nonfinite": ("if (isnan(x) || x == INFINITY)", "if (isnan(x) || isinf(x))"),
 }
 

@@ -123,10 +123,24 @@ def snapped_uniforms(rng: np.random.Generator, n: int) -> np.ndarray:
     return (k.astype(np.float64) * U24).astype(np.float32)
 
 
-def gumbel_max_token(rng: np.random.Generator, logits_f32: np.ndarray, temperature: float) -> int:
-    """One draw from softmax(logits / T) by the Gumbel-max construction."""
-    g = -np.log(rng.standard_exponential(logits_f32.shape[0]))
-    return int(np.argmax(logits_f32.astype(np.float64) / float(temperature) + g))
+def gumbel_max_token(rng: np.random.Generator, logits_f32: np.ndarray, temperature: float,
+                     top_k: int = 0) -> int:
+    """One draw from softmax(logits / T) by the Gumbel-max construction; with top_k > 0,
+    from the top_k largest logits only (Gumbel-max over that index set: a draw from the
+    distribution restricted to them, chosen by rank alone).  T <= 0 is a greedy drafter:
+    the first argmax of the raw logits (the Gumbel noise is still drawn, so the stream
+    stays aligned)."""
+    z = logits_f32.astype(np.float64)
+    idx = None
+    if 0 < top_k < z.shape[0]:
+        idx = np.sort(np.argpartition(-z, top_k - 1)[:top_k])
+        z = z[idx]
+    g = -np.log(rng.standard_exponential(z.shape[0]))
+    if not (float(temperature) > 0.0):
+        pick = int(np.argmax(z))
+    else:
+        pick = int(np.argmax(z / float(temperature) + g))
+    return int(idx[pick]) if idx is not None else pick
 
 
 def _store(x_f32: np.ndarray, dtype: str) -> np.ndarray:
@@ -142,12 +156,14 @@ def _workers() -> int:
 # --------------------------------------------------------------------------- #
 def build(name: str, dtype: str, vocab: int, gamma, temperature, seed: int,
           target_fn, draft_fn, mode: str = "sample", draft_tokens_fn=None,
-          meta=None) -> Workload:
+          meta=None, draft_top_k: int = 0) -> Workload:
     """Assemble a packed workload row by row.
 
     target_fn(rng, row, n_pos) -> float32 [n_pos, V]   (pre-rounding target logits)
     draft_fn(rng, row, tgt)    -> float32 [gamma, V]    (pre-rounding draft logits)
     draft_tokens_fn(rng, row, draft_stored_f32, T) -> int32 [gamma] (optional)
+    draft_top_k > 0: sampled drafts come from the draft_top_k largest draft logits of
+    their position (a drafter that samples from its own top-k set)
     """
     gamma = np.asarray(gamma, np.int32)
     B = gamma.shape[0]
@@ -176,7 +192,7 @@ def build(name: str, dtype: str, vocab: int, gamma, temperature, seed: int,
             elif mode == "greedy":
                 tok = np.argmax(stored, axis=1)
             else:
-                tok = [gumbel_max_token(rng, stored[j], float(temperature[i])) for j in range(g)]
+                tok = [gumbel_max_token(rng, stored[j], float(temperature[i]), draft_top_k) for j in range(g)]
             tokens[d_off[i]:d_off[i + 1]] = np.asarray(tok, np.int32)
         uniforms[t_off[i]:t_off[i + 1]] = snapped_uniforms(_rng(seed, 2, i), g + 1)
 
@@ -279,24 +295,33 @@ def c2(seed: int = 2) -> Workload:
                  _boosted_target(V, 3.0, 5, 8.0), _noisy_draft(1.0, 1.0))
 
 
-def c3(seed: int = 3, mode: str = "sample", batch: int = 64) -> Workload:
+def c3(seed: int = 3, mode: str = "sample", batch: int = 64, draft_scale: float = 0.8,
+       draft_sigma: float = 1.5, draft_top_k: int = 0) -> Workload:
     """B=64, gamma=5, V=128256 bf16; target N(0,3) + Zipf(1.1) log-boost on a random
-    permutation; draft = 0.8*target + N(0,1.5); T=0.8; sampling or greedy."""
+    permutation; draft = 0.8*target + N(0,1.5); T=0.8; sampling or greedy.  draft_scale
+    and draft_sigma change the draft (1.0 and 0.2: a draft close to its target, whose
+    rows mostly keep every draft); draft_top_k > 0 samples the drafts from the draft's
+    top-k set."""
     V = 128256
-    return build(f"c3_b{batch}_g5_v128256_bf16_{mode}", "bf16", V, np.full(batch, 5), 0.8, seed,
-                 _zipf_target(V, 3.0, 1.1), _noisy_draft(0.8, 1.5), mode=mode)
+    tag = "" if (draft_scale, draft_sigma, draft_top_k) == (0.8, 1.5, 0) else \
+        f"_d{draft_scale:g}x_n{draft_sigma:g}" + (f"_dk{draft_top_k}" if draft_top_k else "")
+    return build(f"c3_b{batch}_g5_v128256_bf16_{mode}{tag}", "bf16", V, np.full(batch, 5), 0.8, seed,
+                 _zipf_target(V, 3.0, 1.1), _noisy_draft(draft_scale, draft_sigma), mode=mode,
+                 draft_top_k=draft_top_k)
 
 
-def c4(seed: int = 4, batch: int = 256) -> Workload:
+def c4(seed: int = 4, batch: int = 256, draft_top_k: int = 0) -> Workload:
     """B=256, gamma=8, V=152064 bf16 as c2; per-row T ~ U[0.5,1.5]; per-row draft
-    noise sigma ~ U[0.2,3.0]."""
+    noise sigma ~ U[0.2,3.0].  draft_top_k > 0 samples the drafts from the draft's
+    top-k set."""
     V = 152064
     prm = _rng(seed, 9, 0)
     temps = prm.uniform(0.5, 1.5, batch).astype(np.float32)
     sig = prm.uniform(0.2, 3.0, batch)
-    return build(f"c4_b{batch}_g8_v152064_bf16", "bf16", V, np.full(batch, 8), temps, seed,
+    return build(f"c4_b{batch}_g8_v152064_bf16" + (f"_dk{draft_top_k}" if draft_top_k else ""), "bf16", V,
+                 np.full(batch, 8), temps, seed,
                  _boosted_target(V, 3.0, 5, 8.0), _noisy_draft(1.0, lambda r: float(sig[r])),
-                 meta=dict(draft_sigma=sig))
+                 meta=dict(draft_sigma=sig), draft_top_k=draft_top_k)
 
 
 def c5(seed: int = 5, batch: int = 512) -> Workload:
