@@ -34,7 +34,8 @@
  * OWNERSHIP.  Every buffer is owned by the caller.  All array pointers are DEVICE
  * pointers (hipMalloc'd or equivalent) unless stated otherwise.  The library keeps no
  * pointer past the call and allocates no device memory: scratch space is the caller's
- * `workspace`, of at least spec_verify_workspace_bytes(...) bytes, 256-byte aligned.
+ * `workspace`, of at least spec_verify_workspace_bytes(...) bytes, 256-byte aligned
+ * (spec_verify_noalloc takes it from a fixed device array of the library instead).
  *
  * ASYNCHRONY.  spec_verify enqueues its kernels on `hip_stream` (a hipStream_t; NULL =
  * the null stream) and returns without synchronizing.  Outputs are valid once the
@@ -62,7 +63,9 @@ typedef enum {
     SV_EINVAL = -1,     /* bad pointer, size, mode or layout                     */
     SV_EDTYPE = -2,     /* dtype is not SV_BF16 or SV_F32                         */
     SV_EWORKSPACE = -3, /* workspace too small or not 256-byte aligned            */
-    SV_EHIP = -4        /* the HIP runtime reported an error while enqueueing      */
+    SV_EHIP = -4,       /* the HIP runtime reported an error while enqueueing      */
+    SV_ESCRATCH = -5    /* spec_verify_noalloc: the shape needs more workspace than
+                           its fixed scratch array holds                           */
 } sv_status;
 
 typedef enum { SV_BF16 = 0, SV_F32 = 1 } sv_dtype;
@@ -288,6 +291,32 @@ sv_status spec_verify_filtered(const void *target_logits, const void *draft_logi
                                int32_t gamma_uniform, const int32_t *top_k, const float *top_p,
                                int32_t *n_accepted, int32_t *emitted_tokens, const sv_diag *diag,
                                void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * spec_verify without a workspace argument, for callers that cannot allocate device
+ * memory: code being captured into a HIP graph, tight serving loops, harnesses that
+ * forbid hipMalloc.  It enqueues exactly spec_verify's kernels, with the workspace
+ * taken from a file-scope device array of SPEC_VERIFY_NOALLOC_SCRATCH_BYTES bytes
+ * that the library holds on every GPU it runs on until the process ends (one copy
+ * per device; its address is looked up with hipGetSymbolAddress on the first call on
+ * a device).  It calls no hipMalloc, hipFree or other allocating routine.
+ *
+ * Arguments, layout, outputs and errors as for spec_verify; the workspace and its
+ * size are not passed.  A shape whose spec_verify_workspace_bytes(...) exceeds
+ * SPEC_VERIFY_NOALLOC_SCRATCH_BYTES returns SV_ESCRATCH and enqueues nothing.
+ *
+ * Every call on one GPU shares that GPU's scratch array, whose contents need no
+ * initialization and are overwritten by each call.  Calls ordered on one stream are
+ * safe; calls that may overlap on one GPU (different streams, or different host
+ * threads without ordering) race on the array and give undefined results.
+ */
+#define SPEC_VERIFY_NOALLOC_SCRATCH_BYTES (16u << 20)
+sv_status spec_verify_noalloc(const void *target_logits, const void *draft_logits, int32_t dtype,
+                              int64_t vocab, int32_t batch, int64_t n_target_rows,
+                              const int32_t *draft_tokens, const float *uniforms,
+                              const float *temperature, const int32_t *gamma_per_row,
+                              int32_t gamma_uniform, int32_t mode, int32_t *n_accepted,
+                              int32_t *emitted_tokens, const sv_diag *diag, void *hip_stream);
 
 /* Static, human-readable name of an sv_status value. */
 const char *spec_verify_strerror(int32_t status);

@@ -17,7 +17,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 # sv_status
-SV_OK, SV_EINVAL, SV_EDTYPE, SV_EWORKSPACE, SV_EHIP = 0, -1, -2, -3, -4
+SV_OK, SV_EINVAL, SV_EDTYPE, SV_EWORKSPACE, SV_EHIP, SV_ESCRATCH = 0, -1, -2, -3, -4, -5
+# fixed scratch array of spec_verify_noalloc (bytes)
+NOALLOC_SCRATCH_BYTES = 16 << 20
 # sv_dtype / sv_mode
 SV_BF16, SV_F32 = 0, 1
 SV_SAMPLE, SV_GREEDY = 0, 1
@@ -36,7 +38,7 @@ EXPORTED = ("spec_verify", "spec_verify_workspace_bytes", "spec_verify_strerror"
             "spec_sample_workspace_bytes", "spec_tree_verify_greedy",
             "spec_tree_verify_greedy_workspace_bytes", "spec_verify_early_exit",
             "spec_verify_early_exit_workspace_bytes", "spec_verify_filtered",
-            "spec_verify_filtered_workspace_bytes")
+            "spec_verify_filtered_workspace_bytes", "spec_verify_noalloc")
 
 
 class SpecVerifyError(RuntimeError):
@@ -86,6 +88,9 @@ def _load():
     L.spec_verify_filtered.argtypes = [vp, vp, i32, i64, i32, i64, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                                        ctypes.POINTER(Diag), vp, sz, vp]
     L.spec_verify_filtered.restype = ctypes.c_int
+    L.spec_verify_noalloc.argtypes = [vp, vp, i32, i64, i32, i64, vp, vp, vp, vp, i32, i32, vp, vp,
+                                      ctypes.POINTER(Diag), vp]
+    L.spec_verify_noalloc.restype = ctypes.c_int
     return L
 
 
@@ -427,6 +432,41 @@ def spec_tree_verify_greedy(target_logits, node_counts, tokens, parents, *, stat
     if rc != SV_OK:
         raise SpecVerifyError(rc, strerror(rc))
     return (n_acc, path, emitted, st) if status else (n_acc, path, emitted)
+
+
+def spec_verify_noalloc(target_logits, draft_logits, draft_tokens, uniforms, temperature, gamma_per_row, *,
+                        mode: str = "sample", out=None):
+    """spec_verify through the entry point that allocates nothing on the device: the
+    workspace is the library's fixed scratch array (NOALLOC_SCRATCH_BYTES per GPU).
+    gamma_per_row is an int32 [B] device tensor or an int (dense); out, if given, is
+    (n_accepted, emitted).  Calls that overlap on one GPU race on the scratch array."""
+    device = target_logits.device
+    dtype = SV_BF16 if target_logits.dtype == torch.bfloat16 else SV_F32
+    if target_logits.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"unsupported logits dtype {target_logits.dtype}")
+    V = int(target_logits.shape[-1])
+    nT = target_logits.numel() // V
+    gamma_t = gamma_per_row if isinstance(gamma_per_row, torch.Tensor) else None
+    gu = 0 if gamma_t is not None else int(gamma_per_row)
+    B = int(gamma_t.numel()) if gamma_t is not None else nT // (gu + 1)
+    for t, name, dts in ((target_logits, "target_logits", (target_logits.dtype,)),
+                         (draft_logits, "draft_logits", (target_logits.dtype,)),
+                         (draft_tokens, "draft_tokens", (torch.int32,)), (uniforms, "uniforms", (torch.float32,)),
+                         (temperature, "temperature", (torch.float32,)), (gamma_t, "gamma_per_row", (torch.int32,))):
+        _check(t, name, dts, device)
+    if draft_logits is not None and draft_logits.numel() != (nT - B) * V:
+        raise ValueError("draft_logits must hold one row of V logits per draft row")
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=device), torch.empty(nT, dtype=torch.int32, device=device))
+    n_acc, emitted = out
+    md = SV_SAMPLE if mode == "sample" else SV_GREEDY
+    stream = torch.cuda.current_stream(device).cuda_stream
+    rc = lib.spec_verify_noalloc(_ptr(target_logits), _ptr(draft_logits), dtype, V, B, nT, _ptr(draft_tokens),
+                                 _ptr(uniforms), _ptr(temperature), _ptr(gamma_t), gu, md, _ptr(n_acc),
+                                 _ptr(emitted), None, ctypes.c_void_p(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, strerror(rc))
+    return n_acc, emitted
 
 
 spec_verify.__doc__ = _verify.__doc__

@@ -34,6 +34,7 @@ extern "C" const char *spec_verify_strerror(int32_t status)
     case SV_EDTYPE: return "unsupported dtype (expected SV_BF16 or SV_F32)";
     case SV_EWORKSPACE: return "workspace too small or not 256-byte aligned";
     case SV_EHIP: return "HIP runtime error while enqueueing kernels";
+    case SV_ESCRATCH: return "shape needs more workspace than spec_verify_noalloc's fixed scratch array";
     default: return "unknown status";
     }
 }

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(sv):
 
 
 def test_strerror_and_version(sv):
-    for code in (sv.SV_OK, sv.SV_EINVAL, sv.SV_EDTYPE, sv.SV_EWORKSPACE, sv.SV_EHIP):
+    for code in (sv.SV_OK, sv.SV_EINVAL, sv.SV_EDTYPE, sv.SV_EWORKSPACE, sv.SV_EHIP, sv.SV_ESCRATCH):
         assert sv.strerror(code) and sv.strerror(code) != "unknown status"
     assert sv.strerror(12345) == "unknown status"
     assert "gfx950" in sv.version()
@@ -204,3 +204,20 @@ def test_bench_refuses_several_gpus():
     assert r.returncode == 2
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert line["n_gpus"] == 2 and "one GPU only" in line["error"]
+
+
+def test_noalloc_host_argument_errors(sv):
+    """spec_verify_noalloc refuses, before touching a device, a shape whose workspace
+    exceeds its fixed scratch array, and bad dtypes or sizes."""
+    L = sv.lib
+    p = 1 << 20
+
+    def call(dtype, V, B, nT, gu):
+        return L.spec_verify_noalloc(p, p, dtype, V, B, nT, p, p, p, None, gu, sv.SV_SAMPLE, p, p, None, None)
+
+    # 4096 rows of 8 drafts over V = 256000 fp32: beyond 16 MiB of workspace
+    assert sv.workspace_bytes(4096, 4096 * 9, 256000, sv.SV_F32) > sv.NOALLOC_SCRATCH_BYTES
+    assert call(sv.SV_F32, 256000, 4096, 4096 * 9, 8) == sv.SV_ESCRATCH
+    assert call(7, 1000, 2, 6, 2) == sv.SV_EDTYPE
+    assert call(sv.SV_BF16, 0, 2, 6, 2) == sv.SV_EINVAL
+    assert call(sv.SV_BF16, 1000, 2, 1, 2) == sv.SV_EINVAL
