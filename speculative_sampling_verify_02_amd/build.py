@@ -8,7 +8,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", f) for f in ("sv_stats.hip", "sv_kernels.hip", "sv_tree.hip", "sv_filter.hip", "sv_api.hip", "sv_noalloc.hip")]
-HEADERS = [os.path.join(HERE, "csrc", "sv_internal.h"), os.path.join(ROOT, "include", "spec_verify.h")]
+HEADERS = [os.path.join(HERE, "csrc", h) for h in ("sv_internal.h", "sv_stream.h", "sv_draw.h")] + \
+    [os.path.join(ROOT, "include", "spec_verify.h")]
 OUT = os.path.join(HERE, "libspecverify.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

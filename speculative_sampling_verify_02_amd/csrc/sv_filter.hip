@@ -624,7 +624,8 @@ __global__ __launch_bounds__(kFilterBlock) void filter_stats_kernel(Params P)
         Partial rec{-INFINITY, INT32_MAX, 0.0};
         if (rm != ROW_SAMPLE) {
             // greedy rows: the target vectors' first argmax (NaN: no index); bad
-            // temperatures: nothing
+            // temperatures: the maximum alone (which tells the row non-finite)
+            if (rm == ROW_BAD_TEMP) rec.m = mx;
             if (rm == ROW_GREEDY && target) {
                 rec.m = mx;
                 if (mx > -INFINITY) {   // not NaN, not -inf

@@ -15,14 +15,9 @@
 // The draw's weights are fp32 from the hardware exp2 for both logit types (fp32
 // logits form the exponent in two parts to keep fp32-level accuracy), with fp64 sums
 // across lanes and tiles; the merges of the streaming pass's records are fp64.
-#include <float.h>
-#include <limits.h>
-
-#include "sv_internal.h"
+#include "sv_draw.h"
 
 namespace sv {
-
-constexpr double kQNaN = __builtin_nan("");
 
 // ===========================================================================
 // prepare: packed offsets of a ragged batch and the per-vector table
@@ -75,19 +70,6 @@ __global__ __launch_bounds__(1024) void prepare_kernel(Params P)
     if (tid == 0) P.hdr->status = (bad || carry_t != P.nT) ? ST_BAD_GAMMA : 0;
 }
 
-// log2 of the factor that takes a record's sum to sum 2^((z - m) c) over its logits
-// (0 for records of -inf or NaN logits, and for references stored as NaN: exact m c).
-// A record's sum is taken against fl(ref c_hi); c_eff is the full scale.
-template <int DT>
-__device__ __forceinline__ double rec_shift(const Partial &q, const TempConst &tc)
-{
-    if (!(q.m > -INFINITY && q.m < INFINITY)) return 0.0;
-    const float ref = __int_as_float(q.idx);
-    if (ref != ref) return 0.0;
-    return (double)(ref * tc.c_hi) - (double)q.m * tc.c_eff;
-}
-
-
 // ===========================================================================
 // accept scan: the whole workgroup merges records, one wave tests positions
 // ===========================================================================
@@ -99,56 +81,6 @@ struct ScanLds {
     int32_t idx[64];       // target first argmax (greedy rows)
     RowDraw D;
 };
-
-// Records of global vector v: items [v ipv, (v + 1) ipv).
-__device__ __forceinline__ void vec_records(const Params &P, int64_t v, int64_t &i0, int64_t &i1)
-{
-    i0 = v * P.geo.ipv;
-    i1 = i0 + P.geo.ipv - 1;
-}
-
-template <int DT>
-__device__ __forceinline__ void wave_merge(const Params &P, const Partial &q0, int64_t i0, int64_t i1, bool greedy,
-                                           const TempConst &tc, int lane, float &M, double &S, int32_t &idx)
-{
-    float m = q0.m;
-    double s = greedy ? 0.0 : q0.s;
-    double sh = greedy ? 0.0 : rec_shift<DT>(q0, tc);   // s 2^sh: sum 2^((z - m) c) of this lane's logits
-    int32_t id = (m != m) ? INT32_MAX : q0.idx;
-    for (int64_t i = i0 + 64 + lane; i <= i1; i += 64) {   // vectors of more than 64 items
-        const Partial q = P.parts[i];
-        if (greedy) {
-            if (q.m != q.m) {
-                m = q.m;
-            } else if (q.m > m) {
-                m = q.m;
-                id = q.idx;
-            } else if (q.m == m && q.idx < id) {
-                id = q.idx;
-            }
-            continue;
-        }
-        s *= exp2_f64(sh);
-        sh = 0.0;
-        const double qs = q.s * exp2_f64(rec_shift<DT>(q, tc));
-        if (q.m > m) {
-            if (m != -INFINITY) s *= exp2_f64(((double)m - (double)q.m) * tc.c_eff);
-            m = q.m;
-        }
-        s += q.m == -INFINITY ? qs : qs * exp2_f64(((double)q.m - (double)m) * tc.c_eff);
-        if (q.m != q.m) m = q.m;
-    }
-    M = wave_umax_f32(m);
-    if (greedy) {
-        S = 0.0;
-        idx = wave_umin_i32(m == M ? id : INT32_MAX);
-    } else {
-        // NaN anywhere gives M = NaN and S = NaN
-        const double t = m == -INFINITY ? s : s * exp2_f64(sh + ((double)m - (double)M) * tc.c_eff);
-        S = wave_usum_f64(t);
-        idx = INT32_MAX;
-    }
-}
 
 // One wave's record loads for vectors q0, q0 + 4, ... of a position chunk (vectors
 // q < nt are target positions base + q, the others draft positions base + q - nt).
@@ -176,11 +108,12 @@ __device__ __forceinline__ void load_batch(const Params &P, const RowGeom &G, in
 
 // Per-vector statistics of positions [base, base + nt) (target) and [base, base + nd)
 // (draft) of a row into LDS, every wave taking every fourth vector (first: this wave's
-// first batch, already loaded).
+// first batch, already loaded).  maxonly: every vector's records hold only a maximum
+// (a row whose temperature is unusable).
 template <int DT>
 __device__ __forceinline__ void scan_merge(const Params &P, const RowGeom &G, int64_t base, int nt, int nd,
                                            bool greedy, const TempConst &tc, ScanLds &sh, const ScanBatch &first,
-                                           bool have_first)
+                                           bool have_first, bool maxonly)
 {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nq = nt + nd;
@@ -195,7 +128,7 @@ __device__ __forceinline__ void scan_merge(const Params &P, const RowGeom &G, in
             float M;
             double S;
             int32_t idx;
-            wave_merge<DT>(P, B.rec[b], B.i0[b], B.i1[b], greedy && q < nt, tc, lane, M, S, idx);
+            wave_merge<DT>(P, B.rec[b], B.i0[b], B.i1[b], (greedy && q < nt) || maxonly, tc, lane, M, S, idx);
             if (lane == 0) {
                 const int side = q < nt ? 0 : 1, j = q < nt ? q : q - nt;
                 sh.m[side][j] = M;
@@ -247,7 +180,10 @@ __device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &s
     int32_t kidx = -1;
     int32_t x_keep = 0;                       // this lane's draft token (rows with gamma < 64)
 
-    if (rm != ROW_BAD_TEMP) {
+    // a row with an unusable temperature decides nothing, but every position is still
+    // checked for non-finite logits (from the maxima its records hold)
+    const bool bad = rm == ROW_BAD_TEMP;
+    {
         for (int64_t base = 0; base <= g; base += 64) {
             const int nt = (int)(g + 1 - base < 64 ? g + 1 - base : 64);
             const int nd = greedy ? 0 : (int)(g - base < 64 ? g - base : 64);
@@ -264,7 +200,7 @@ __device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &s
                     zd = P.zx[P.nD + G.d_off + j];
                 }
             }
-            scan_merge<DT>(P, G, base, nt, nd, greedy, tc, sh, first, base == 0);
+            scan_merge<DT>(P, G, base, nt, nd, greedy, tc, sh, first, base == 0, bad);
             __syncthreads();
             if (wave == 0) {
                 x_keep = x;
@@ -276,7 +212,10 @@ __device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &s
                 float md = -INFINITY;
                 double Sd = 0.0;
                 bool reject = false;
-                if (greedy) {
+                if (bad) {
+                    if (has_t && !(mt > -INFINITY && mt < INFINITY)) status |= ST_NONFINITE;
+                    if (has_d && !(sh.m[1][lane] > -INFINITY && sh.m[1][lane] < INFINITY)) status |= ST_NONFINITE;
+                } else if (greedy) {
                     if (has_t && !(mt > -INFINITY && mt < INFINITY)) status |= ST_NONFINITE;
                     if (has_d) reject = x != it;
                 } else {
@@ -487,16 +426,22 @@ __global__ __launch_bounds__(64) void ee_step_kernel(Params P)
     float mt = -INFINITY, md = -INFINITY;
     double St = 0.0, Sd = 0.0;
     int32_t at = INT32_MAX, unused;
-    if (!(status & ST_INVALID)) {
-        wave_merge<DT>(P, qt, ti0, ti1, greedy, tc, lane, mt, St, at);
-        if (greedy ? !(mt > -INFINITY && mt < INFINITY) : !(St > 0.0 && St < INFINITY)) status |= ST_NONFINITE;
+    // A row invalid from the start (a bad temperature or token) decides nothing, but
+    // like the full round it still reads every position for non-finite logits (its
+    // records hold maxima when the temperature is unusable).
+    const bool pre_invalid = (status & (ST_BAD_TEMP | ST_BAD_TOKEN)) != 0;
+    const bool maxonly = rm == ROW_BAD_TEMP;
+    if (!(status & ST_NONFINITE)) {
+        wave_merge<DT>(P, qt, ti0, ti1, greedy || maxonly, tc, lane, mt, St, at);
+        if ((greedy || maxonly) ? !(mt > -INFINITY && mt < INFINITY) : !(St > 0.0 && St < INFINITY))
+            status |= ST_NONFINITE;
         if (!greedy && j < g) {
-            wave_merge<DT>(P, qd, di0, di1, false, tc, lane, md, Sd, unused);
-            if (!(Sd > 0.0 && Sd < INFINITY)) status |= ST_NONFINITE;
+            wave_merge<DT>(P, qd, di0, di1, maxonly, tc, lane, md, Sd, unused);
+            if (maxonly ? !(md > -INFINITY && md < INFINITY) : !(Sd > 0.0 && Sd < INFINITY)) status |= ST_NONFINITE;
         }
     }
     const int64_t n_cache = P.cache_len ? P.cache_len[row] : 0;
-    if (status & ST_INVALID) {
+    if ((status & ST_NONFINITE) || (pre_invalid && j == g)) {
         for (int32_t k = lane; k <= g; k += 64) P.emitted[G.t_off + k] = -1;
         for (int32_t k = lane; k < g; k += 64) {
             if (P.p_x) P.p_x[G.d_off + k] = kQNaN;
@@ -513,7 +458,9 @@ __global__ __launch_bounds__(64) void ee_step_kernel(Params P)
     int32_t K = -1;
     RowDraw D{};
     D.kind = DRAW_NONE;
-    if (greedy) {
+    if (pre_invalid) {
+        // listed for the next position below
+    } else if (greedy) {
         if (j < g && x == at) {
             if (lane == 0) P.emitted[G.t_off + j] = x;
         } else {
@@ -581,151 +528,6 @@ __global__ __launch_bounds__(64) void ee_step_kernel(Params P)
 // ===========================================================================
 // draw: per-tile weight sums, then the inverse CDF
 // ===========================================================================
-// Bytes of the target (or draft) logit array.
-__device__ __forceinline__ uint64_t array_bytes(const Params &P, int DT, bool target)
-{
-    return (uint64_t)(target ? P.nT : P.nD) * (uint64_t)P.V * (DT == 0 ? 2u : 4u);
-}
-
-// A unit past the end of a vector, read as -inf logits.
-template <int DT>
-__device__ __forceinline__ RawUnit<DT> neg_inf_unit()
-{
-    RawUnit<DT> r;
-    if constexpr (DT == 0) {
-        r.a = make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
-    } else {
-        r.a = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        r.b = r.a;
-    }
-    return r;
-}
-
-template <int DT>
-struct DrawConst;
-
-// bf16 logits: fp32 weights 2^((z - m) c) / S.  The difference z - m of two bf16
-// values is exact in fp32, so the maximum gets exactly 1 / S: a distribution that
-// keeps one token (a top-k 1 filter) has weight exactly 1 there on both models.
-template <>
-struct DrawConst<0> {
-    float c, mt, md, Ft, Fd, tht, thd;
-    bool residual;
-
-    __device__ __forceinline__ void init(const RowDraw &D)
-    {
-        tht = D.theta_t;
-        thd = D.theta_d;
-        c = temp_const<0>(D.T).c_hi;
-        residual = D.kind == DRAW_RESIDUAL;
-        mt = D.m_t;
-        Ft = (float)(1.0 / D.S_t);
-        md = D.m_d;
-        Fd = residual ? (float)(1.0 / D.S_d) : 0.0f;
-    }
-    using W = float;
-    // weights of one unit: w (residual or p) and p
-    __device__ __forceinline__ void weights(const float *zt, const float *zd, float *w, float *p) const
-    {
-#pragma unroll
-        for (int e = 0; e < kUnitElems; ++e) {
-            // logits below a filter's threshold drop out
-            const float zte = zt[e] < tht ? -INFINITY : zt[e];
-            const float zde = zd[e] < thd ? -INFINITY : zd[e];
-            const float pe = hw_exp2((zte - mt) * c) * Ft;
-            float we = pe;
-            if (residual) we = fmaxf(0.0f, pe - hw_exp2((zde - md) * c) * Fd);
-            w[e] = we;
-            p[e] = pe;
-        }
-    }
-};
-
-// 1 - 2^y for y <= 0.  Near 0, where 2^y is close to 1 and the difference would
-// lose its relative accuracy, from the series -sum_k (y ln 2)^k / k! to degree 8
-// (y > -1/2: truncation below 1e-9 relative); below, from the hardware exp2.
-__device__ __forceinline__ float one_minus_exp2(float y)
-{
-    float s = (float)kExp2Coef[5];   // (ln 2)^8 / 8!; kExp2Coef[13 - k] = (ln 2)^k / k!
-#pragma unroll
-    for (int k = 7; k >= 1; --k) s = fmaf(s, y, (float)kExp2Coef[13 - k]);
-    return y > -0.5f ? -y * s : 1.0f - hw_exp2(y);
-}
-
-// The sum a + b as hi + lo exactly (Knuth's branch-free two-sum; finite inputs).
-__device__ __forceinline__ void two_sum(float a, float b, float &hi, float &lo)
-{
-    hi = a + b;
-    const float bb = hi - a;
-    lo = (a - (hi - bb)) + (b - bb);
-}
-
-// fp32 logits: fp32 weights from the hardware exp2, p = 2^(u c_hi + u c_lo - B) with the
-// vector's normalisation in the exponent: B = m c + log2 S held as two fp32 parts
-// (~2^-48 relative), so no per-vector factor is rounded to fp32.  When |fl(m c_hi)| <
-// 2^20, u = z; otherwise u = z - m, which is exact for every logit whose weight is not
-// 0 (it lies within a factor 2 of m), and B = log2 S.
-// The residual is taken as p (1 - 2^y) with y = log2(q/p) = ((z_d - z_t) + (m_t - m_d)) c
-// + log2(S_t / S_d), both differences carried exactly in two fp32 parts: y keeps its
-// relative accuracy where q is close to p (a difference p - q would keep only the
-// absolute accuracy of p and q), and it is exactly log2(S_t / S_d), 0 for equal sums,
-// wherever z_t - m_t = z_d - m_d, as for a distribution that keeps one token.
-template <>
-struct DrawConst<1> {
-    float ch, cl, ut, Bht, Blt, Mh, Ml, Lh, Ll, tht, thd;
-    bool residual;
-
-    __device__ __forceinline__ static void split(double x, float &hi, float &lo)
-    {
-        hi = (float)x;
-        lo = (float)(x - (double)hi);
-    }
-    __device__ __forceinline__ void init(const RowDraw &D)
-    {
-        tht = D.theta_t;
-        thd = D.theta_d;
-        const TempConst tc = temp_const<1>(D.T);
-        ch = tc.c_hi;
-        cl = tc.c_lo;
-        residual = D.kind == DRAW_RESIDUAL;
-        const double Lt = log2(D.S_t);
-        double B = Lt;
-        ut = D.m_t;
-        if (fabsf(D.m_t * tc.c_hi) < kFastRef) {
-            ut = 0.0f;
-            B += (double)D.m_t * tc.c_eff;
-        }
-        split(B, Bht, Blt);
-        Mh = Ml = Lh = Ll = 0.0f;
-        if (residual) {
-            split((double)D.m_t - (double)D.m_d, Mh, Ml);   // exact: both are fp32
-            split(Lt - log2(D.S_d), Lh, Ll);
-        }
-    }
-    using W = float;
-    __device__ __forceinline__ void weights(const float *zt, const float *zd, float *w, float *p) const
-    {
-#pragma unroll
-        for (int e = 0; e < kUnitElems; ++e) {
-            const float zte = zt[e] < tht ? -INFINITY : zt[e];
-            const float xt = zte - ut;
-            const float pe = hw_exp2(fmaf(xt, cl, fmaf(xt, ch, -Bht)) - Blt);
-            float we = pe;
-            if (residual) {
-                const float zde = zd[e] < thd ? -INFINITY : zd[e];
-                float dh, dl;
-                two_sum(zde, -zte, dh, dl);
-                const float g = (dh + Mh) + (dl + Ml);
-                const float y = fmaf(g, ch, Lh) + fmaf(g, cl, Ll);
-                // q = 0 keeps all of p; y >= 0 (q >= p) and NaN (p = 0) keep nothing
-                we = zde == -INFINITY ? pe : (y < 0.0f ? pe * one_minus_exp2(y) : 0.0f);
-            }
-            w[e] = we;
-            p[e] = pe;
-        }
-    }
-};
-
 // The accept scan, one workgroup per row; it stores the row's outputs and what the
 // draw needs.
 template <int DT>
@@ -828,69 +630,6 @@ __global__ __launch_bounds__(kBlock) void verify_kernel_f32(Params P)
 // running sum first exceeds t = u W, then re-reads that piece only: its tiles'
 // sums, the tile, the token.
 // ---------------------------------------------------------------------------
-
-// logits per draw piece (two halves of the streaming pass) and tiles per piece
-template <int DT> constexpr int kPieceTiles = 2 * kItemBytes / (DT == 0 ? 2 : 4) / kTileElems;
-
-// Sum of p over piece q of a vector whose maximum is m and sum 2^((z - m) c) is S.
-template <int DT>
-__device__ __forceinline__ double piece_weight(const Partial &q, const TempConst &tc, float m, double S)
-{
-    if (!(q.m > -INFINITY)) return 0.0;
-    return q.s * exp2_f64(rec_shift<DT>(q, tc) + ((double)q.m - (double)m) * tc.c_eff) / S;
-}
-
-// The bonus draw's piece from the pieces' p sums (lane j holds piece j): the first
-// piece where the running sum exceeds t = u W, else the last one with weight.
-template <int DT>
-__device__ __forceinline__ void bonus_piece(const Partial &q, const TempConst &tc, float m, double S, float u,
-                                            int lane, int32_t &piece, double &before, double &W)
-{
-    const double w = (m == m && S > 0.0) ? piece_weight<DT>(q, tc, m, S) : 0.0;
-    const double incl = wave_inclusive_sum(w, lane);
-    W = __shfl(incl, 63);
-    const double t = (double)u * W;
-    const unsigned long long hit = __ballot(incl > t && w > 0.0);
-    const unsigned long long pos = __ballot(w > 0.0);
-    const int l = hit ? __ffsll((long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : -1);
-    piece = l;
-    before = l >= 0 ? __shfl(incl - w, l) : 0.0;
-}
-
-// Totals over the 64 lanes of N per-lane values (N a power of two, at most 64), in
-// every lane: a butterfly where each exchange also halves the values a lane carries
-// (log2 N steps leave lane l the partial total of value bitrev(l mod N) over its
-// group of N lanes), then the groups are added, and the totals read back per value.
-template <int N>
-__device__ __forceinline__ void wave_totals(double (&v)[N], int lane)
-{
-    constexpr int LOGN = N == 1 ? 0 : N == 2 ? 1 : N == 4 ? 2 : N == 8 ? 3 : N == 16 ? 4 : N == 32 ? 5 : 6;
-    static_assert((1 << LOGN) == N, "N must be a power of two up to 64");
-    double x[N];
-#pragma unroll
-    for (int k = 0; k < N; ++k) x[k] = v[k];
-#pragma unroll
-    for (int st = 0; st < LOGN; ++st) {
-        const int half = N >> (st + 1);
-        const bool up = (lane >> st) & 1;
-#pragma unroll
-        for (int k = 0; k < half; ++k) {
-            const double send = up ? x[k] : x[k + half];
-            const double keep = up ? x[k + half] : x[k];
-            x[k] = keep + __shfl_xor(send, 1 << st);
-        }
-    }
-    double t = x[0];
-#pragma unroll
-    for (int m = N; m < 64; m <<= 1) t += __shfl_xor(t, m);
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-        int r = 0;   // the lane holding value k: k with its LOGN bits reversed
-#pragma unroll
-        for (int bit = 0; bit < LOGN; ++bit) r |= ((k >> bit) & 1) << (LOGN - 1 - bit);
-        v[k] = readlane_f64(t, r);
-    }
-}
 
 // The bonus draw by the workgroup's four waves: the piece (chosen by the scan, or
 // here for vectors of more than 64 pieces), each wave's quarter of its tiles summed,

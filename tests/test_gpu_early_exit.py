@@ -121,3 +121,16 @@ def test_c3_full(H):
 
 def test_c5_full(H):
     parity(H, workloads.c5(), seed=5)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_invalid_rows_read_to_the_end(H, dtype):
+    """A row invalid from the start (bad temperature or token) decides nothing, so the
+    early-exit round, like the full one, still reads its every position and reports
+    non-finite logits there."""
+    from test_gpu_parity import invalid_from_start
+    w = invalid_from_start(dtype)
+    g, ref = parity(H, w, seed=7)
+    st = g["row_status"]
+    assert st[0] == oracle.BAD_TEMP | oracle.NONFINITE and st[3] == oracle.BAD_TOKEN | oracle.NONFINITE
+    assert st[4] == oracle.BAD_TOKEN and st[5] == oracle.BAD_TEMP

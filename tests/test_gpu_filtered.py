@@ -238,3 +238,14 @@ def test_unaligned_vocabularies(H, vocab, dtype):
     kernel read them with aligned loads shifted into place."""
     w = workloads.small(seed=93, batch=5, vocab=vocab, dtype=dtype, gamma=[2, 3, 0, 1, 2])
     parity(H, w, *filters(w, seed=13))
+
+
+def test_invalid_rows_still_report_nonfinite(H):
+    """Rows with an unusable temperature or a bad token and non-finite logits further on,
+    in a filtered call (bf16 rows take the one-pass filter kernel)."""
+    from test_gpu_parity import invalid_from_start
+    for dtype in ("bf16", "f32"):
+        w = invalid_from_start(dtype, seed=56)
+        g, ref = parity(H, w, *filters(w, seed=14, kinds=("kp", "k", "p", "none")))
+        assert g["row_status"][0] == oracle.BAD_TEMP | oracle.NONFINITE
+        assert g["row_status"][3] == oracle.BAD_TOKEN | oracle.NONFINITE

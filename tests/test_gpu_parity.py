@@ -368,3 +368,38 @@ def test_binding_rejects_mismatched_draft_logits(H):
     with pytest.raises(ValueError, match="required in sampling mode"):
         sv.spec_verify(d["target"], None, d["tokens"], d["uniforms"], d["temperature"], d["gamma"])
     torch.cuda.synchronize()
+
+
+def invalid_from_start(dtype="f32", seed=55):
+    """Rows invalid from the start that also hold non-finite logits further on: an
+    unusable temperature (NaN, subnormal) with a NaN, +inf or all -inf position, and a
+    bad token with a NaN at the last position.  The round reads every position, so the
+    oracle reports the non-finite logits too."""
+    w = workloads.small(seed=seed, batch=8, vocab=3000, dtype=dtype, gamma=3)
+    tgt, drf, tok, T = w.target.copy(), w.draft.copy(), w.draft_tokens.copy(), w.temperature.copy()
+    nan = np.float32(np.nan) if dtype == "f32" else 0x7FC0
+    pinf = np.float32(np.inf) if dtype == "f32" else 0x7F80
+    ninf = np.float32(-np.inf) if dtype == "f32" else 0xFF80
+    T[0] = np.nan
+    drf[0 * 3 + 2, 11] = nan                   # row 0: bad T, NaN in the last draft position
+    T[1] = 1e-39
+    tgt[1 * 4 + 3, 5] = pinf                   # row 1: subnormal T, +inf at the bonus position
+    T[2] = np.inf
+    tgt[2 * 4 + 1, :] = ninf                   # row 2: infinite T, a position with all -inf
+    tok[3 * 3 + 0] = 3000
+    tgt[3 * 4 + 3, 7] = nan                    # row 3: bad token, NaN at the bonus position
+    tok[4 * 3 + 1] = -5                        # row 4: bad token only
+    T[5] = np.nan                              # row 5: bad T only
+    return workloads.Workload(**{**w.__dict__, "target": tgt, "draft": drf, "draft_tokens": tok, "temperature": T})
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_invalid_rows_still_report_nonfinite(H, dtype):
+    w = invalid_from_start(dtype)
+    gpu, ref, rep = _parity(H, w)
+    st = gpu["row_status"]
+    assert st[0] == oracle.BAD_TEMP | oracle.NONFINITE and st[1] == oracle.BAD_TEMP | oracle.NONFINITE
+    assert st[2] == oracle.BAD_TEMP | oracle.NONFINITE and st[3] == oracle.BAD_TOKEN | oracle.NONFINITE
+    assert st[4] == oracle.BAD_TOKEN and st[5] == oracle.BAD_TEMP
+    gg, rg, _ = _parity(H, w, mode="greedy")
+    assert gg["row_status"][3] == oracle.BAD_TOKEN | oracle.NONFINITE

@@ -135,3 +135,22 @@ def test_c2_target_full():
 def test_c5_draft_subset():
     """fp32 logits at V = 256000: the first 256 draft vectors."""
     parity(workloads.sample_inputs(workloads.c5(), seed=5, side="draft", limit=256))
+
+
+def test_bad_temperature_and_nonfinite_vector():
+    """A vector with an unusable temperature and a NaN, +inf or all -inf logits reports
+    both, as the oracle does."""
+    w = workloads.small(seed=63, batch=4, vocab=2000, dtype="f32", gamma=[1] * 4)
+    si = workloads.sample_inputs(w, seed=63, side="target")
+    z = si.logits.copy()
+    T = si.temperature.copy()
+    z[0, 3] = np.nan
+    T[0] = np.nan
+    z[1, 1999] = np.inf
+    T[1] = 1e-39
+    z[2, :] = -np.inf
+    T[2] = np.inf
+    T[3] = np.nan
+    si = workloads.SampleInputs("bad_t_nonfinite", "f32", si.vocab, z, T, si.uniforms)
+    tok, st, ref = parity(si)
+    assert list(st[:3]) == [oracle.BAD_TEMP | oracle.NONFINITE] * 3 and st[3] == oracle.BAD_TEMP
