@@ -223,7 +223,7 @@ struct DrawConst<1> {
 };
 
 // logits per draw piece (two halves of the streaming pass) and tiles per piece
-template <int DT> constexpr int kPieceTiles = 2 * kItemBytes / (DT == 0 ? 2 : 4) / kTileElems;
+template <int DT> constexpr int kPieceTiles = (int)(2 * kItemElems / kTileElems);
 
 // Sum of p over piece q of a vector whose maximum is m and sum 2^((z - m) c) is S.
 template <int DT>

@@ -13,18 +13,22 @@ namespace sv {
 // geometry constants
 // ---------------------------------------------------------------------------
 constexpr int kBlock = 256;              // threads per workgroup (4 wave64)
-constexpr int kStatsBlock = 768;         // streaming pass, aligned rows: 12 waves, one workgroup per CU
 constexpr int kWaves = kBlock / 64;
 constexpr int kUnitElems = 8;            // logits per draw-tile lane (one 16-byte bf16 load)
 constexpr int kTileUnits = 64;           // draw tile: one unit per lane of a wave
 constexpr int kTileElems = kTileUnits * kUnitElems;   // 512 logits
 constexpr int kTilesPerWave = 2;         // draw: tiles a wave sums with all loads in flight
 constexpr int kTilesPerDrawWg = kTilesPerWave * kWaves;   // 8 tiles = 4096 logits
-// Streaming pass: a wave reads a half piece of 8 KB as 8 loads of 16 bytes per lane
-// (lane l's k-th load at byte 1024 k + 16 l), so bf16 halves hold 4096 logits and
-// fp32 halves 2048.
-constexpr int kItemLoads = 8;
-constexpr int64_t kItemBytes = 64 * 16 * kItemLoads;
+// Streaming pass: a wave reads a half piece of 2048 logits, as loads of 16 bytes per
+// lane (lane l's k-th load at byte 1024 k + 16 l): 4 loads (4 KB) for bf16, 8 loads
+// (8 KB) for fp32.  (bf16 halves of 4 KB against 8 KB: the pass over 704 vectors of
+// 128256 logits took 34.6 against 36.7 us, over 4352 vectors of 152064 200.7 against
+// 202.9 us, the finer pieces spreading the end of the pass more evenly; the fp32
+// pass, bound by its arithmetic, was slower with 4 KB halves.)
+constexpr int64_t kItemElems = 2048;
+template <int DT> constexpr int kItemLoads = (int)(kItemElems * (DT == 0 ? 2 : 4) / 1024);
+// streaming-pass workgroups, one per CU: bf16 16 waves (4 per SIMD), fp32 12 waves
+template <int DT> constexpr int kStatsBlock = DT == 0 ? 1024 : 768;
 constexpr int kMaxStatsGrid = 16384;     // cap of the streaming-pass grid
 constexpr double kLog2e = 1.44269504088896340736;
 
@@ -90,7 +94,7 @@ struct RowDraw {           // what the draw needs about one row
 
 // Streaming pass.  The vectors it reads are the target rows (vectors 0 .. nT-1) and,
 // in sampling mode, the draft rows (vectors nT .. nT+nD-1).  Each vector is cut into
-// ipv pieces of two halves of kItemBytes (the last piece shorter); piece v ipv + j is
+// ipv pieces of two halves of kItemElems logits (the last piece shorter); piece v ipv + j is
 // piece j of vector v, and its record sits at parts[v ipv + j].  Wave w of the grid
 // reduces pieces w, w + nwaves, ... .
 struct Geometry {
@@ -113,7 +117,7 @@ struct Layout {
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-inline int64_t item_elems(int32_t dtype) { return kItemBytes / (dtype == 0 ? 2 : 4); }
+inline int64_t item_elems(int32_t) { return kItemElems; }
 
 inline Geometry make_geometry(int32_t B, int64_t nT, int64_t V, int32_t mode, int32_t dtype,
                               int32_t grid_cap)

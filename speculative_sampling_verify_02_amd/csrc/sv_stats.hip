@@ -1,9 +1,9 @@
 // The streaming pass of the speculative-sampling verification step for gfx950.
 //
 // Every logit of every target and draft vector is read exactly once.  The vectors
-// are cut into pieces of two 8 KB halves; one workgroup per CU owns a contiguous
+// are cut into pieces of two 4 KB halves; one workgroup per CU owns a contiguous
 // range of pieces and its waves take them in order from a counter in LDS, each half
-// as eight 16-byte loads per lane with the next half's loads in flight while one is
+// as four 16-byte loads per lane with the next half's loads in flight while one is
 // reduced.  Per piece a wave writes one record: the maximum and the sum of
 // 2^((z - m) c), c = log2(e)/T, over the piece (sampling rows) or the first argmax
 // (greedy rows).  The temperature softmax these summarize is the softened output of
@@ -55,7 +55,7 @@ __device__ __forceinline__ void stats_body(const Params &P)
     // the two halves of a piece in two register buffers: the next piece's first half
     // is loaded while this piece's second half is reduced, and so on (every load
     // unconditional, no copies between the buffers)
-    ItemRaw ra, rb;
+    ItemRaw<DT> ra, rb;
     half_begin<DT, AL>(P, v, j, 0, true, ra, lane);
     half_begin<DT, AL>(P, v, j, 1, true, rb, lane);
     VecCtx vc = vec_ctx(P, v);
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(64) void stats_list_kernel(Params P)
     if (slot >= 2 * (int64_t)P.ee_count[2 * buf]) return;
     const int64_t v = P.ee_vecs[buf][slot];
     if (v < 0) return;
-    ItemRaw ra, rb;
+    ItemRaw<DT> ra, rb;
     half_begin<DT, AL>(P, v, j, 0, true, ra, lane);
     half_begin<DT, AL>(P, v, j, 1, true, rb, lane);
     const VecCtx vc = vec_ctx(P, v);
@@ -130,18 +130,18 @@ __global__ __launch_bounds__(64) void stats_list_kernel(Params P)
     piece_finish<DT>(P, vc, rm, tc, v, j, acc);
 }
 
-// 16-byte aligned rows (the usual case): one workgroup of 12 waves per CU, 3 per SIMD
+// 16-byte aligned rows (the usual case): one workgroup per CU, of 16 waves (bf16) or 12
 template <int DT>
-__global__ __launch_bounds__(kStatsBlock) void stats_kernel(Params P)
+__global__ __launch_bounds__(kStatsBlock<DT>) void stats_kernel(Params P)
 {
     stats_body<DT, true>(P);
 }
 
-// rows that do not start 16-byte aligned: aligned loads, realigned in registers; 8
-// waves per CU (the realignment needs registers of its own)
-constexpr int kStatsBlockUnaligned = 512;
+// rows that do not start 16-byte aligned: aligned loads, realigned in registers; 12
+// waves per CU for bf16, 8 for fp32 (the realignment needs registers of its own)
+template <int DT> constexpr int kStatsBlockUnaligned = DT == 0 ? 768 : 512;
 template <int DT>
-__global__ __launch_bounds__(kStatsBlockUnaligned) void stats_kernel_unaligned(Params P)
+__global__ __launch_bounds__(kStatsBlockUnaligned<DT>) void stats_kernel_unaligned(Params P)
 {
     stats_body<DT, false>(P);
 }
@@ -157,7 +157,11 @@ static hipError_t launch(const void *fn, int64_t blocks, int threads, const Para
     return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(threads), args, 0, s);
 }
 
-static int stats_block(bool aligned) { return aligned ? kStatsBlock : kStatsBlockUnaligned; }
+static int stats_block(int dtype, bool aligned)
+{
+    if (dtype == 0) return aligned ? kStatsBlock<0> : kStatsBlockUnaligned<0>;
+    return aligned ? kStatsBlock<1> : kStatsBlockUnaligned<1>;
+}
 
 static const void *stats_fn(int dtype, bool aligned)
 {
@@ -178,7 +182,7 @@ int32_t stats_grid_cap(int dtype, bool aligned)
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stats_fn(dtype, aligned), stats_block(aligned), 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stats_fn(dtype, aligned), stats_block(dtype, aligned), 0) !=
             hipSuccess || per_cu <= 0)
         per_cu = 1;
     int64_t cap = (int64_t)cus * per_cu;
@@ -197,7 +201,7 @@ hipError_t launch_stats_list(const Params &P, hipStream_t s, int dtype, bool ali
 
 hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned, hipEvent_t start, hipEvent_t stop)
 {
-    return launch_timed(stats_fn(dtype, aligned), P.geo.G, stats_block(aligned), P, s, start, stop);
+    return launch_timed(stats_fn(dtype, aligned), P.geo.G, stats_block(dtype, aligned), P, s, start, stop);
 }
 
 }  // namespace sv

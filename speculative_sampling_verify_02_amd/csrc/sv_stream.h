@@ -24,8 +24,9 @@ namespace sv {
 // the half.  Rows that do not start 16-byte aligned are loaded from the aligned
 // address below the half's start: sb is the offset of the half's first byte there,
 // and e the aligned 16 bytes after the last load's (for lane 63 of that load).
+template <int DT>
 struct ItemRaw {
-    uint4 d[kItemLoads];
+    uint4 d[kItemLoads<DT>];
     uint4 e;
     uint32_t sb;
 };
@@ -48,7 +49,7 @@ __device__ __forceinline__ int32_t half_len(const Params &P, int64_t j, int h)
 // an empty window at the start of the vector (nothing to read, nothing used), which
 // keeps every load of the pipeline unconditional.
 template <int DT, bool AL>
-__device__ __forceinline__ void half_begin(const Params &P, int64_t v, int64_t j, int h, bool live, ItemRaw &r,
+__device__ __forceinline__ void half_begin(const Params &P, int64_t v, int64_t j, int h, bool live, ItemRaw<DT> &r,
                                            int lane)
 {
     constexpr int64_t esz = DT == 0 ? 2 : 4;
@@ -64,7 +65,7 @@ __device__ __forceinline__ void half_begin(const Params &P, int64_t v, int64_t j
             __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, (int)nbytes, kBufferWord3);
         const uint32_t last = nbytes > 16u ? nbytes - 16u : 0u;
 #pragma unroll
-        for (int k = 0; k < kItemLoads; ++k) {
+        for (int k = 0; k < kItemLoads<DT>; ++k) {
             uint32_t off = (uint32_t)k * 1024u + (uint32_t)lane * 16u;
             off = off < last ? off : last;
             r.d[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, kLoadNT));
@@ -82,12 +83,12 @@ __device__ __forceinline__ void half_begin(const Params &P, int64_t v, int64_t j
         const uint64_t last = (reinterpret_cast<uint64_t>(arr) + arr_bytes - 1) & ~(uint64_t)15;
         r.sb = (uint32_t)__builtin_amdgcn_readfirstlane((int)(a - a0));
 #pragma unroll
-        for (int k = 0; k < kItemLoads; ++k) {
+        for (int k = 0; k < kItemLoads<DT>; ++k) {
             uint64_t q = a0 + (uint64_t)(k * 64 + lane) * 16u;
             q = q < last ? q : last;
             r.d[k] = load_nt16(reinterpret_cast<const void *>(q));
         }
-        uint64_t qe = a0 + (uint64_t)kItemLoads * 1024u;
+        uint64_t qe = a0 + (uint64_t)kItemLoads<DT> * 1024u;
         qe = qe < last ? qe : last;
         r.e = load_nt16(reinterpret_cast<const void *>(qe));
     }
@@ -96,14 +97,14 @@ __device__ __forceinline__ void half_begin(const Params &P, int64_t v, int64_t j
 // Moves an unaligned half's bytes into the aligned layout: lane l of load k takes the
 // 16 bytes at offset sb of its own aligned block and the next one (lane l + 1's, or
 // for lane 63 lane 0's of load k + 1, or e after the last load).
-template <int Q>
-__device__ __forceinline__ void realign_q(ItemRaw &r, int lane, uint32_t rb)
+template <int DT, int Q>
+__device__ __forceinline__ void realign_q(ItemRaw<DT> &r, int lane, uint32_t rb)
 {
 #pragma unroll
-    for (int k = 0; k < kItemLoads; ++k) {
+    for (int k = 0; k < kItemLoads<DT>; ++k) {
         uint4 nx = make_uint4(wave_next_lane(r.d[k].x), wave_next_lane(r.d[k].y), wave_next_lane(r.d[k].z),
                               wave_next_lane(r.d[k].w));
-        const uint4 l0 = k + 1 < kItemLoads
+        const uint4 l0 = k + 1 < kItemLoads<DT>
             ? make_uint4((uint32_t)__builtin_amdgcn_readlane((int)r.d[k + 1].x, 0),
                          (uint32_t)__builtin_amdgcn_readlane((int)r.d[k + 1].y, 0),
                          (uint32_t)__builtin_amdgcn_readlane((int)r.d[k + 1].z, 0),
@@ -114,26 +115,27 @@ __device__ __forceinline__ void realign_q(ItemRaw &r, int lane, uint32_t rb)
     }
 }
 
-__device__ __forceinline__ void realign(ItemRaw &r, int lane)
+template <int DT>
+__device__ __forceinline__ void realign(ItemRaw<DT> &r, int lane)
 {
     const uint32_t rb = r.sb & 3u;
     switch (r.sb >> 2) {
-    case 0: if (rb != 0) realign_q<0>(r, lane, rb); break;
-    case 1: realign_q<1>(r, lane, rb); break;
-    case 2: realign_q<2>(r, lane, rb); break;
-    default: realign_q<3>(r, lane, rb); break;
+    case 0: if (rb != 0) realign_q<DT, 0>(r, lane, rb); break;
+    case 1: realign_q<DT, 1>(r, lane, rb); break;
+    case 2: realign_q<DT, 2>(r, lane, rb); break;
+    default: realign_q<DT, 3>(r, lane, rb); break;
     }
 }
 
 // Logits at half offsets n and beyond become -inf (the short end of a vector).  With
 // AL the rows hold whole 16-byte loads, so the test is per load.
 template <int DT, bool AL>
-__device__ __forceinline__ void mask_tail(ItemRaw &r, int lane, int n)
+__device__ __forceinline__ void mask_tail(ItemRaw<DT> &r, int lane, int n)
 {
     constexpr int E = kE<DT>;
     constexpr uint32_t kNinf = DT == 0 ? 0xff80ff80u : 0xff800000u;
 #pragma unroll
-    for (int k = 0; k < kItemLoads; ++k) {
+    for (int k = 0; k < kItemLoads<DT>; ++k) {
         if constexpr (AL) {
             if (k * 64 * E + lane * E >= n) r.d[k] = make_uint4(kNinf, kNinf, kNinf, kNinf);
         } else {
@@ -166,7 +168,7 @@ __device__ __forceinline__ float bf16_hi_f(uint32_t w)
 // The logits of load k on this lane (FORM picks the bf16 unpacking: 0 shifts and
 // masks, 1 and 2 byte permutes).
 template <int DT, int FORM = 0>
-__device__ __forceinline__ void lane_vals(const ItemRaw &r, int k, float *x)
+__device__ __forceinline__ void lane_vals(const ItemRaw<DT> &r, int k, float *x)
 {
     const uint4 w = r.d[k];
     if constexpr (DT == 0 && FORM != 0) {
@@ -186,12 +188,12 @@ __device__ __forceinline__ void lane_vals(const ItemRaw &r, int k, float *x)
 }
 
 template <int DT>
-__device__ __forceinline__ float lane_max(const ItemRaw &r)
+__device__ __forceinline__ float lane_max(const ItemRaw<DT> &r)
 {
     constexpr int E = kE<DT>;
     float m = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < kItemLoads; ++k) {
+    for (int k = 0; k < kItemLoads<DT>; ++k) {
         float x[E];
         lane_vals<DT>(r, k, x);
 #pragma unroll
@@ -252,7 +254,7 @@ __device__ __forceinline__ void set_ref(LaneSum &a, float R, float c)
 
 // add one bf16 half (first: the piece's first half, which sets the references); the
 // term of logit x is 2^(x c - Bhi), one fma and the hardware exp2
-__device__ __forceinline__ void sample_half(const ItemRaw &r, float c, LaneSum &a, bool first)
+__device__ __forceinline__ void sample_half(const ItemRaw<0> &r, float c, LaneSum &a, bool first)
 {
     constexpr int DT = 0;
     constexpr int E = kE<DT>;
@@ -268,9 +270,9 @@ __device__ __forceinline__ void sample_half(const ItemRaw &r, float c, LaneSum &
     }
     const float m_prev = a.m, s_prev = a.s;
     const double E_prev = a.E;
-    float acc[kItemLoads];
+    float acc[kItemLoads<DT>];
 #pragma unroll
-    for (int k = 0; k < kItemLoads; ++k) {
+    for (int k = 0; k < kItemLoads<DT>; ++k) {
         float x[E];
         lane_vals<DT, 1>(r, k, x);
 #pragma unroll
@@ -284,9 +286,9 @@ __device__ __forceinline__ void sample_half(const ItemRaw &r, float c, LaneSum &
         acc[k] = x[0];
     }
 #pragma unroll
-    for (int w = 1; w < kItemLoads; w <<= 1)
+    for (int w = 1; w < kItemLoads<DT>; w <<= 1)
 #pragma unroll
-        for (int k = 0; k + w < kItemLoads; k += 2 * w) acc[k] += acc[k + w];
+        for (int k = 0; k + w < kItemLoads<DT>; k += 2 * w) acc[k] += acc[k + w];
     // a lane whose logits are finite but whose sum is not, or a two-part reference: the
     // references move to the lanes' maxima, the earlier sum is rescaled, and the half is
     // summed again (from registers) with the two-part reference when needed
@@ -296,9 +298,9 @@ __device__ __forceinline__ void sample_half(const ItemRaw &r, float c, LaneSum &
         set_ref(a, R, c);
         a.s = m_prev == -INFINITY ? 0.0f : s_prev * (float)exp2_f64(E_prev - a.E);
         const float Blo = a.huge ? a.Blo : 0.0f;
-        float acc2[kItemLoads];
+        float acc2[kItemLoads<DT>];
 #pragma unroll
-        for (int k = 0; k < kItemLoads; ++k) {
+        for (int k = 0; k < kItemLoads<DT>; ++k) {
             float x[E];
             lane_vals<DT, 2>(r, k, x);
 #pragma unroll
@@ -310,9 +312,9 @@ __device__ __forceinline__ void sample_half(const ItemRaw &r, float c, LaneSum &
             acc2[k] = x[0];
         }
 #pragma unroll
-        for (int w = 1; w < kItemLoads; w <<= 1)
+        for (int w = 1; w < kItemLoads<DT>; w <<= 1)
 #pragma unroll
-            for (int k = 0; k + w < kItemLoads; k += 2 * w) acc2[k] += acc2[k + w];
+            for (int k = 0; k + w < kItemLoads<DT>; k += 2 * w) acc2[k] += acc2[k + w];
         acc[0] = acc2[0];
     }
     a.s += acc[0];
@@ -379,12 +381,13 @@ __device__ __forceinline__ void fill_exp2_tab(double *tab, int copies)
 // exponent from one fp64 fma (c the full scale), the power from the table.  The half's
 // lane maximum comes first and the reference follows the running lane maximum (the
 // sum so far rescaled), so every exponent is <= 0 up to rounding.
-__device__ __forceinline__ void sample_half_f32(const ItemRaw &r, double c_eff, LaneSum &a, bool first,
+__device__ __forceinline__ void sample_half_f32(const ItemRaw<1> &r, double c_eff, LaneSum &a, bool first,
                                                 const Exp2Tab &tab)
 {
+    constexpr int DT = 1;
     float mh = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < kItemLoads; ++k) {
+    for (int k = 0; k < kItemLoads<DT>; ++k) {
         float x[4];
         lane_vals<1>(r, k, x);
 #pragma unroll
@@ -408,7 +411,7 @@ __device__ __forceinline__ void sample_half_f32(const ItemRaw &r, double c_eff, 
     const double cs = (double)kTabLen * c_eff, Es = (double)kTabLen * a.E;
     double s = 0.0;
 #pragma unroll
-    for (int k = 0; k < kItemLoads; ++k) {
+    for (int k = 0; k < kItemLoads<DT>; ++k) {
         float x[4];
         lane_vals<1, 1>(r, k, x);
         TabTerm u[4];
@@ -458,7 +461,7 @@ struct LaneArg {
 };
 
 template <int DT>
-__device__ __forceinline__ void argmax_half(const ItemRaw &r, int lane, int base, LaneArg &a)
+__device__ __forceinline__ void argmax_half(const ItemRaw<DT> &r, int lane, int base, LaneArg &a)
 {
     constexpr int E = kE<DT>;
     // per load maximum, then the first load holding the half's lane maximum (strictly
@@ -467,7 +470,7 @@ __device__ __forceinline__ void argmax_half(const ItemRaw &r, int lane, int base
     int kb = 0;
     bool nan = false;
 #pragma unroll
-    for (int k = 0; k < kItemLoads; ++k) {
+    for (int k = 0; k < kItemLoads<DT>; ++k) {
         float x[E];
         lane_vals<DT>(r, k, x);
         float lm = x[0];
@@ -483,9 +486,9 @@ __device__ __forceinline__ void argmax_half(const ItemRaw &r, int lane, int base
     // the first logit of that load equal to it
     uint4 w = r.d[0];
 #pragma unroll
-    for (int k = 1; k < kItemLoads; ++k)
+    for (int k = 1; k < kItemLoads<DT>; ++k)
         if (k == kb) w = r.d[k];
-    ItemRaw one;
+    ItemRaw<DT> one;
     one.d[0] = w;
     float x[E];
     lane_vals<DT, 1>(one, 0, x);
@@ -512,13 +515,13 @@ __device__ __forceinline__ Partial argmax_record(const LaneArg &a)
 // The logit at half offset o (on the lane that loaded it): the raw word is picked
 // with constant indices (the half stays in registers) and unpacked alone.
 template <int DT>
-__device__ __forceinline__ float half_value(const ItemRaw &r, int lane, int o)
+__device__ __forceinline__ float half_value(const ItemRaw<DT> &r, int lane, int o)
 {
     constexpr int E = kE<DT>;
     uint32_t wsel = 0u;
     bool hi = false;
 #pragma unroll
-    for (int k = 0; k < kItemLoads; ++k) {
+    for (int k = 0; k < kItemLoads<DT>; ++k) {
         const uint32_t w[4] = {r.d[k].x, r.d[k].y, r.d[k].z, r.d[k].w};
 #pragma unroll
         for (int t = 0; t < E; ++t) {
@@ -541,7 +544,7 @@ struct PieceAcc {
 
 template <int DT, bool AL>
 __device__ __forceinline__ void piece_half(const Params &P, const VecCtx &vc, int32_t rm, const TempConst &tc,
-                                           int64_t j, int h, int n, ItemRaw &r, PieceAcc<DT> &acc, int lane,
+                                           int64_t j, int h, int n, ItemRaw<DT> &r, PieceAcc<DT> &acc, int lane,
                                            const Exp2Tab &tab)
 {
     constexpr int E = kE<DT>;
