@@ -133,8 +133,17 @@ static sv_status verify_impl(const void *target_logits, const void *draft_logits
         e = fused_units ? sv::launch_filter_stats(P, s, fused_units, g_prof_start, g_prof_stop)
                         : sv::launch_stats(P, s, dtype, aligned, g_prof_start, g_prof_stop);
     if (e == hipSuccess && filtered && !fused_units) e = sv::launch_filter(P, s, dtype, aligned);
-    if (e == hipSuccess) e = sv::launch_scan(P, s, dtype);
-    if (e == hipSuccess && mode == SV_SAMPLE) e = sv::launch_verify(P, s, dtype, aligned);
+    // bf16 sampling: the accept scan and the residual's tile sums in one kernel; otherwise
+    // the scan, then (sampling) the tile sums
+    if (e == hipSuccess) {
+        if (mode == SV_SAMPLE && dtype == 0) {
+            P.st_split = sv::scan_tiles_split(batch, P.geo.ntiles);
+            e = sv::launch_scan_tiles(P, s, aligned);
+        } else {
+            e = sv::launch_scan(P, s, dtype);
+            if (e == hipSuccess && mode == SV_SAMPLE) e = sv::launch_verify(P, s, dtype, aligned);
+        }
+    }
     if (e == hipSuccess && mode == SV_SAMPLE) e = sv::launch_draw_final(P, s, dtype, aligned);
     return e == hipSuccess ? SV_OK : SV_EHIP;
 }

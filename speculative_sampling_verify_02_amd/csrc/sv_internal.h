@@ -200,6 +200,8 @@ struct Params {
     int32_t *crop_len;        // [B] or null: cache entries to keep after it
     int32_t step;             // position being decided
     int32_t gamma_max;        // bound on gamma_i given by the caller
+    int32_t st_split;         // scan_tiles_kernel: workgroups per row
+    int32_t pad1;
     // top-k / top-p filtering of p and q
     const int32_t *top_k;     // [B] or null
     const float *top_p;       // [B] or null
@@ -669,6 +671,8 @@ hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned,
                         hipEvent_t stop = nullptr);
 hipError_t launch_scan(const Params &P, hipStream_t s, int dtype);
 hipError_t launch_verify(const Params &P, hipStream_t s, int dtype, bool aligned);
+int32_t scan_tiles_split(int32_t B, int32_t ntiles);
+hipError_t launch_scan_tiles(const Params &P, hipStream_t s, bool aligned);
 hipError_t launch_draw_final(const Params &P, hipStream_t s, int dtype, bool aligned);
 hipError_t launch_scan_draw(const Params &P, hipStream_t s, int dtype, bool aligned);
 hipError_t launch_tree(const TreeParams &T, hipStream_t s);

@@ -89,12 +89,13 @@ struct ScanBatch {
     int64_t i0[kScanBatch], i1[kScanBatch];
 };
 
+template <int NW>
 __device__ __forceinline__ void load_batch(const Params &P, const RowGeom &G, int64_t base, int nt, int nq, int q0,
                                            int lane, ScanBatch &B)
 {
 #pragma unroll
     for (int b = 0; b < kScanBatch; ++b) {
-        const int q = q0 + b * kWaves;
+        const int q = q0 + b * NW;
         B.rec[b] = Partial{-INFINITY, INT32_MAX, 0.0};
         B.i0[b] = 0;
         B.i1[b] = -1;
@@ -107,23 +108,23 @@ __device__ __forceinline__ void load_batch(const Params &P, const RowGeom &G, in
 }
 
 // Per-vector statistics of positions [base, base + nt) (target) and [base, base + nd)
-// (draft) of a row into LDS, every wave taking every fourth vector (first: this wave's
-// first batch, already loaded).  maxonly: every vector's records hold only a maximum
-// (a row whose temperature is unusable).
-template <int DT>
+// (draft) of a row into LDS, each of the NW waves taking every NW-th vector (first:
+// this wave's first batch, already loaded).  maxonly: every vector's records hold only
+// a maximum (a row whose temperature is unusable).
+template <int DT, int NW>
 __device__ __forceinline__ void scan_merge(const Params &P, const RowGeom &G, int64_t base, int nt, int nd,
                                            bool greedy, const TempConst &tc, ScanLds &sh, const ScanBatch &first,
                                            bool have_first, bool maxonly)
 {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nq = nt + nd;
-    for (int q0 = wave; q0 < nq; q0 += kWaves * kScanBatch) {
+    for (int q0 = wave; q0 < nq; q0 += NW * kScanBatch) {
         ScanBatch B;
         if (have_first && q0 == wave) B = first;
-        else load_batch(P, G, base, nt, nq, q0, lane, B);
+        else load_batch<NW>(P, G, base, nt, nq, q0, lane, B);
 #pragma unroll
         for (int b = 0; b < kScanBatch; ++b) {
-            const int q = q0 + b * kWaves;
+            const int q = q0 + b * NW;
             if (q >= nq) break;
             float M;
             double S;
@@ -140,9 +141,9 @@ __device__ __forceinline__ void scan_merge(const Params &P, const RowGeom &G, in
     }
 }
 
-// The accept scan of one row by the whole workgroup.  Returns what the draw needs
-// (on every thread); with `write`, wave 0 also stores the row's outputs.
-template <int DT>
+// The accept scan of one row by the whole workgroup of NW waves.  Returns what the draw
+// needs (on every thread); with `write`, wave 0 also stores the row's outputs.
+template <int DT, int NW = kWaves>
 __device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &sh)
 {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -167,7 +168,7 @@ __device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &s
     {
         const int nt0 = g + 1 < 64 ? g + 1 : 64;
         const int nd0 = P.mode == 1 ? 0 : (g < 64 ? g : 64);
-        load_batch(P, G, 0, nt0, nt0 + nd0, wave, lane, first);
+        load_batch<NW>(P, G, 0, nt0, nt0 + nd0, wave, lane, first);
     }
     const int32_t rm = row_mode(P.mode, T);
     const bool greedy = rm == ROW_GREEDY;
@@ -200,7 +201,7 @@ __device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &s
                     zd = P.zx[P.nD + G.d_off + j];
                 }
             }
-            scan_merge<DT>(P, G, base, nt, nd, greedy, tc, sh, first, base == 0, bad);
+            scan_merge<DT, NW>(P, G, base, nt, nd, greedy, tc, sh, first, base == 0, bad);
             __syncthreads();
             if (wave == 0) {
                 x_keep = x;
@@ -548,6 +549,59 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(Params P)
     scan_body<DT>(P);
 }
 
+// Sums of the draw weights w (the residual max(0, p - q), or p) and of p over the NTW
+// tiles t0 .. t0 + NTW - 1 of the row's position K, all their loads in flight together;
+// tiles at or past t_end add nothing and are not stored.
+template <int DT, bool AL, int NTW>
+__device__ __forceinline__ void tile_sums(const Params &P, const DrawConst<DT> &c, const RowDraw &D, int32_t row,
+                                          int64_t t0, int64_t t_end, int lane)
+{
+    const void *tb = vec_ptr(P.target, DT, D.t_row, P.V);
+    const void *db = c.residual ? vec_ptr(P.draft, DT, D.d_row, P.V) : nullptr;
+    RawUnit<DT> rt[NTW], rd[NTW];
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+        const int64_t unit = (t0 + i) * kTileUnits + lane;
+        const bool in = t0 + i < t_end && unit < P.geo.nunits;
+        if constexpr (AL) {
+            rt[i] = in ? load_raw<DT, AL>(tb, unit, P.V) : neg_inf_unit<DT>();
+            rd[i] = (in && c.residual) ? load_raw<DT, AL>(db, unit, P.V) : neg_inf_unit<DT>();
+        } else {
+            rt[i] = load_tile_unit<DT>(tb, t0 + i, P.V, P.target, array_bytes(P, DT, true), lane);
+            rd[i] = c.residual ? load_tile_unit<DT>(db, t0 + i, P.V, P.draft, array_bytes(P, DT, false), lane)
+                               : neg_inf_unit<DT>();
+        }
+    }
+    // per-lane sums of every tile first, then one interleaved cross-lane reduction
+    // (tiles past the end read -inf logits and sum to 0)
+    double lw[NTW], lp[NTW];
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+        float zt[kUnitElems], zd[kUnitElems];
+        unpack<DT>(rt[i], zt);
+        unpack<DT>(rd[i], zd);
+        typename DrawConst<DT>::W w[kUnitElems], p[kUnitElems];
+        c.weights(zt, zd, w, p);
+        lw[i] = 0.0;
+        lp[i] = 0.0;
+#pragma unroll
+        for (int e = 0; e < kUnitElems; ++e) { lw[i] += w[e]; lp[i] += p[e]; }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+#pragma unroll
+        for (int i = 0; i < NTW; ++i) {
+            lw[i] += __shfl_xor(lw[i], o);
+            lp[i] += __shfl_xor(lp[i], o);
+        }
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < NTW; ++i)
+            if (t0 + i < t_end) P.tiles[row * P.geo.ntiles + t0 + i] = Sum2{lw[i], lp[i]};
+    }
+}
+
 // The residual's tile sums: workgroup `piece` of a row that rejected sums its slice of
 // position K.
 template <int DT, bool AL>
@@ -563,52 +617,46 @@ __device__ __forceinline__ void verify_body(const Params &P)
     if (!(D.kind == DRAW_RESIDUAL || (P.theta && D.kind == DRAW_BONUS))) return;
     DrawConst<DT> c;
     c.init(D);
-    const void *tb = vec_ptr(P.target, DT, D.t_row, P.V);
-    const void *db = c.residual ? vec_ptr(P.draft, DT, D.d_row, P.V) : nullptr;
     const int64_t t0 = (int64_t)piece * kTilesPerDrawWg + (int64_t)wave * kTilesPerWave;
+    tile_sums<DT, AL, kTilesPerWave>(P, c, D, row, t0, P.geo.ntiles, lane);
+}
 
-    RawUnit<DT> rt[kTilesPerWave], rd[kTilesPerWave];
-#pragma unroll
-    for (int i = 0; i < kTilesPerWave; ++i) {
-        const int64_t unit = (t0 + i) * kTileUnits + lane;
-        const bool in = t0 + i < P.geo.ntiles && unit < P.geo.nunits;
-        if constexpr (AL) {
-            rt[i] = in ? load_raw<DT, AL>(tb, unit, P.V) : neg_inf_unit<DT>();
-            rd[i] = (in && c.residual) ? load_raw<DT, AL>(db, unit, P.V) : neg_inf_unit<DT>();
-        } else {
-            rt[i] = load_tile_unit<DT>(tb, t0 + i, P.V, P.target, array_bytes(P, DT, true), lane);
-            rd[i] = c.residual ? load_tile_unit<DT>(db, t0 + i, P.V, P.draft, array_bytes(P, DT, false), lane)
-                               : neg_inf_unit<DT>();
-        }
+// The accept scan and the residual's tile sums in one kernel: st_split workgroups of 16
+// waves per row.  Each runs the row's scan (the same arithmetic in each, so the same K
+// and draw record), the first also writes the row's outputs, and each then sums the
+// residual over its share of the row's tiles at position K, with no round trip through
+// memory between the decision and the loads of position K.
+constexpr int kScanTileBlock = 1024;
+constexpr int kScanTileWaves = kScanTileBlock / 64;
+constexpr int kScanTileBatch = 4;   // tiles per wave with all their loads in flight
+
+template <int DT, bool AL>
+__device__ __forceinline__ void scan_tiles_body(const Params &P)
+{
+    __shared__ ScanLds sh;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t S = P.st_split;
+    const int32_t row = (int32_t)(blockIdx.x / S);
+    const int32_t part = (int32_t)(blockIdx.x - (int64_t)row * S);
+    if (P.gamma != nullptr && P.hdr->status != 0) {
+        invalidate_call(P, row, part == 0 && threadIdx.x == 0);
+        return;
     }
-    // per-lane sums of every tile first, then one interleaved cross-lane reduction
-    // (tiles past the end read -inf logits and sum to 0)
-    double lw[kTilesPerWave], lp[kTilesPerWave];
-#pragma unroll
-    for (int i = 0; i < kTilesPerWave; ++i) {
-        float zt[kUnitElems], zd[kUnitElems];
-        unpack<DT>(rt[i], zt);
-        unpack<DT>(rd[i], zd);
-        typename DrawConst<DT>::W w[kUnitElems], p[kUnitElems];
-        c.weights(zt, zd, w, p);
-        lw[i] = 0.0;
-        lp[i] = 0.0;
-#pragma unroll
-        for (int e = 0; e < kUnitElems; ++e) { lw[i] += w[e]; lp[i] += p[e]; }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-#pragma unroll
-        for (int i = 0; i < kTilesPerWave; ++i) {
-            lw[i] += __shfl_xor(lw[i], o);
-            lp[i] += __shfl_xor(lp[i], o);
-        }
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int i = 0; i < kTilesPerWave; ++i)
-            if (t0 + i < P.geo.ntiles) P.tiles[row * P.geo.ntiles + t0 + i] = Sum2{lw[i], lp[i]};
-    }
+    const RowDraw D = scan_row<DT, kScanTileWaves>(P, row, part == 0, sh);
+    // bonus draws use the streaming pass's piece sums, except when p is filtered
+    if (!(D.kind == DRAW_RESIDUAL || (P.theta && D.kind == DRAW_BONUS))) return;
+    DrawConst<DT> c;
+    c.init(D);
+    const int64_t nt = P.geo.ntiles;
+    const int64_t a = nt * part / S, b = nt * (part + 1) / S;
+    for (int64_t t0 = a + (int64_t)wave * kScanTileBatch; t0 < b; t0 += (int64_t)kScanTileWaves * kScanTileBatch)
+        tile_sums<DT, AL, kScanTileBatch>(P, c, D, row, t0, b, lane);
+}
+
+template <int DT, bool AL>
+__global__ __launch_bounds__(kScanTileBlock) void scan_tiles_kernel(Params P)
+{
+    scan_tiles_body<DT, AL>(P);
 }
 
 template <bool AL>
@@ -930,6 +978,32 @@ hipError_t launch_scan(const Params &P, hipStream_t s, int dtype)
 {
     const void *fn = dtype == 0 ? (const void *)scan_kernel<0> : (const void *)scan_kernel<1>;
     return launch(fn, (int64_t)P.B, kBlock, P, s);
+}
+
+// Workgroups per row of scan_tiles_kernel: enough to give every CU a workgroup, each
+// with at least 32 tiles of the row.
+int32_t scan_tiles_split(int32_t B, int32_t ntiles)
+{
+    static int cus = 0;
+    if (cus <= 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+    }
+    int64_t S = B > 0 ? ((int64_t)cus + B - 1) / B : 1;
+    const int64_t cap = ntiles / 32;
+    if (S > cap) S = cap;
+    if (S < 1) S = 1;
+    return (int32_t)S;
+}
+
+// bf16 only: fp32 rows keep the separate scan and verify_kernel_f32, whose residual
+// weights come from the hardware exp2 and cost less than the fp64 terms of tile_sums
+hipError_t launch_scan_tiles(const Params &P, hipStream_t s, bool aligned)
+{
+    const void *fn = aligned ? (const void *)scan_tiles_kernel<0, true> : (const void *)scan_tiles_kernel<0, false>;
+    return launch(fn, (int64_t)P.B * P.st_split, kScanTileBlock, P, s);
 }
 
 hipError_t launch_verify(const Params &P, hipStream_t s, int dtype, bool aligned)
