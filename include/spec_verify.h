@@ -225,14 +225,16 @@ sv_status spec_tree_verify_greedy(const void *target_logits, int32_t dtype, int6
 /*
  * The verification round with early exit: positions are read left to right and,
  * for each row, nothing after its first rejection is read (rayaq.ca "Speculative
- * decoding", section "One round", step 3, which stops at the first rejection).  One
- * step per position: the rows still undecided read position j of both models, then
- * decide it.  Kept drafts, drawn tokens and the residual mass are those of
- * spec_verify on the same inputs; what differs is what a row can see: positions
- * after its rejection are not checked for non-finite logits (a NaN there leaves the
- * row valid) and their p(x_j), q(x_j) diagnostics are NaN.  Draft tokens are all
- * range-checked.  Fewer logits are read (2(K_i + 1) vectors of row i after a
- * rejection instead of 2 gamma_i + 1), at the price of gamma_max + 1 sequential steps.
+ * decoding", section "One round", step 3, which stops at the first rejection).  The
+ * positions go in chunks that double in length: step k reads positions
+ * [2^k - 1, 2^(k+1) - 1) of both models for the rows still undecided, then decides
+ * them in order, so ceil(log2(gamma_max + 2)) steps cover every row.  Kept drafts,
+ * drawn tokens and the residual mass are those of spec_verify on the same inputs;
+ * what differs is what a row can see: positions after its rejection are not checked
+ * for non-finite logits (a NaN there leaves the row valid) and their p(x_j), q(x_j)
+ * diagnostics are NaN.  Draft tokens are all range-checked.  Fewer logits are read: a
+ * row that rejects at position K_i reads the vectors of the chunks up to the one
+ * holding K_i (fewer than 4(K_i + 1) of them) instead of 2 gamma_i + 1.
  *
  * The cache rollback (rayaq.ca "Speculative decoding", section "Verification
  * attention and the cache"): a round that keeps K_i drafts over a cached prefix of
@@ -241,9 +243,10 @@ sv_status spec_tree_verify_greedy(const void *target_logits, int32_t dtype, int6
  *
  * Arguments as for spec_verify, plus:
  *   gamma_max   ragged batches (gamma_per_row != NULL): a host-side bound on every
- *               gamma_i, >= 0, the number of steps run is gamma_max + 1; a row with
- *               gamma_i > gamma_max is invalid (SV_ROW_BAD_GAMMA).  Ignored for dense
- *               batches (gamma_uniform is the bound).
+ *               gamma_i, >= 0, which sets the number of steps; a row with
+ *               gamma_i > gamma_max is invalid (SV_ROW_BAD_GAMMA, n_accepted and
+ *               crop_len -1, every emitted slot -1) and none of its logits is read.
+ *               Ignored for dense batches (gamma_uniform is the bound).
  *   cache_len   [batch] int32 device, or NULL for n_i = 0: cache entries before the round
  *   crop_len    [batch] int32 device out, or NULL: n_i + K_i + 1, or -1 for an invalid row
  *   workspace   >= spec_verify_early_exit_workspace_bytes(...) bytes, 256-byte aligned

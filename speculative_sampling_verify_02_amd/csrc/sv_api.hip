@@ -316,12 +316,12 @@ extern "C" size_t spec_verify_early_exit_workspace_bytes(int32_t batch, int64_t 
                                                          int32_t dtype)
 {
     const size_t base = spec_verify_workspace_bytes(batch, n_target_rows, vocab, dtype);
-    return base == 0 ? 0 : base + sv::early_exit_extra_bytes(batch);
+    return base == 0 ? 0 : base + sv::early_exit_extra_bytes(batch, n_target_rows);
 }
 
-// The round with early exit: step j reads position j of the rows still undecided
-// (a listed-vector streaming kernel), then decides it (one wave per listed row);
-// the draws follow as in spec_verify.
+// The round with early exit: step k reads positions [2^k - 1, 2^(k+1) - 1) of the
+// rows still undecided (a listed-vector streaming kernel), then decides them in order
+// (one wave per listed row); the draws follow as in spec_verify.
 extern "C" sv_status spec_verify_early_exit(const void *target_logits, const void *draft_logits, int32_t dtype,
                                             int64_t vocab, int32_t batch, int64_t n_target_rows,
                                             const int32_t *draft_tokens, const float *uniforms,
@@ -389,13 +389,14 @@ extern "C" sv_status spec_verify_early_exit(const void *target_logits, const voi
         P.geo.inv_d = gamma_uniform > 0 ? 1.0 / (double)gamma_uniform : 0.0;
     }
     char *ex = ws + L.total;
+    const size_t cap = sv::early_exit_list_cap(batch, n_target_rows);
     const size_t rows_b = sv::align256(sizeof(int32_t) * 2 * (size_t)batch);
-    const size_t vecs_b = sv::align256(sizeof(int32_t) * 4 * (size_t)batch);
+    const size_t vecs_b = sv::align256(sizeof(int32_t) * 2 * cap);
     const size_t cnt_b = sv::align256(sizeof(int32_t) * 4);
     P.ee_rows[0] = reinterpret_cast<int32_t *>(ex);
     P.ee_rows[1] = P.ee_rows[0] + batch;
     P.ee_vecs[0] = reinterpret_cast<int32_t *>(ex + rows_b);
-    P.ee_vecs[1] = P.ee_vecs[0] + 2 * (size_t)batch;
+    P.ee_vecs[1] = P.ee_vecs[0] + cap;
     P.ee_count = reinterpret_cast<int32_t *>(ex + rows_b + vecs_b);
     P.ee_status = reinterpret_cast<int32_t *>(ex + rows_b + vecs_b + cnt_b);
     P.cache_len = cache_len;
@@ -407,9 +408,20 @@ extern "C" sv_status spec_verify_early_exit(const void *target_logits, const voi
     if (gamma_per_row) e = sv::launch_prepare(P, s);
     if (e == hipSuccess) e = sv::launch_ee_init(P, s);
     if (e == hipSuccess && g_prof_start) e = hipEventRecord(g_prof_start, s);
-    for (int32_t j = 0; j <= gamma_max && e == hipSuccess; ++j) {
-        P.step = j;
-        e = sv::launch_stats_list(P, s, dtype, aligned);
+    // chunks of positions [2^k - 1, 2^(k+1) - 1) up to gamma_max
+    const int64_t vec_per_pos = mode == SV_SAMPLE ? 2 : 1;
+    const int64_t n_vecs = mode == SV_SAMPLE ? 2 * n_target_rows - batch : n_target_rows;
+    for (int k = 0; e == hipSuccess; ++k) {
+        const int64_t j0 = (int64_t(1) << k) - 1;
+        if (j0 > gamma_max) break;
+        const int64_t j1 = std::min<int64_t>((int64_t(1) << (k + 1)) - 1, (int64_t)gamma_max + 1);
+        const int64_t j2 = std::min<int64_t>((int64_t(1) << (k + 2)) - 1, (int64_t)gamma_max + 1);
+        P.step = k;
+        P.ee_j0 = (int32_t)j0;
+        P.ee_j1 = (int32_t)j1;
+        P.ee_j2 = (int32_t)j2;
+        const int64_t max_vecs = k == 0 ? vec_per_pos * batch : std::min(n_vecs, vec_per_pos * batch * (j1 - j0));
+        e = sv::launch_stats_list(P, s, dtype, aligned, max_vecs);
         if (e == hipSuccess) e = sv::launch_ee_step(P, s, dtype);
     }
     if (e == hipSuccess && g_prof_stop) e = hipEventRecord(g_prof_stop, s);

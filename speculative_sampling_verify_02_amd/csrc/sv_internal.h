@@ -190,28 +190,37 @@ struct Params {
     RowDraw *draws;
     Sum2 *tiles;
     Geometry geo;
-    // early exit (positions read left to right): the rows still undecided at the
-    // current step and the vectors they read there, double-buffered by step parity
+    // early exit (positions read left to right, in chunks): the rows still undecided
+    // at the current step and the vectors they read there, double-buffered by step
+    // parity
     int32_t *ee_rows[2];      // [B] row ids
-    int32_t *ee_vecs[2];      // [2 B] per listed row: its target vector, its draft vector or -1
-    int32_t *ee_count;        // [4]: rows listed in buffer 0, (unused), rows in buffer 1, (unused)
+    int32_t *ee_vecs[2];      // [max(2 B, nT + nD)] vector ids (-1: none)
+    int32_t *ee_count;        // [4]: rows, vectors listed in buffer 0; rows, vectors in buffer 1
     int32_t *ee_status;       // [B] status bits gathered so far
     const int32_t *cache_len; // [B] or null: cache entries before the round
     int32_t *crop_len;        // [B] or null: cache entries to keep after it
-    int32_t step;             // position being decided
+    int32_t step;             // chunk being read and decided
     int32_t gamma_max;        // bound on gamma_i given by the caller
     int32_t st_split;         // scan_tiles_kernel: workgroups per row
-    int32_t pad1;
+    int32_t ee_j0, ee_j1;     // this step's positions [ee_j0, ee_j1)
+    int32_t ee_j2;            // the next step's end (its positions [ee_j1, ee_j2))
     // top-k / top-p filtering of p and q
     const int32_t *top_k;     // [B] or null
     const float *top_p;       // [B] or null
     float *theta;             // [nT + nD] or null: per-vector logit threshold
 };
 
-// Early-exit scratch after the verification workspace.
-inline size_t early_exit_extra_bytes(int32_t B)
+// Early-exit scratch after the verification workspace: two row lists, two vector
+// lists (each vector is listed at most once, the first list holds two slots per row),
+// the counts and the per-row status.
+inline size_t early_exit_list_cap(int32_t B, int64_t nT)
 {
-    return align256(sizeof(int32_t) * 2 * (size_t)B) + align256(sizeof(int32_t) * 4 * (size_t)B) +
+    const int64_t all = 2 * nT - B;
+    return (size_t)(all > 2 * (int64_t)B ? all : 2 * (int64_t)B);
+}
+inline size_t early_exit_extra_bytes(int32_t B, int64_t nT)
+{
+    return align256(sizeof(int32_t) * 2 * (size_t)B) + align256(sizeof(int32_t) * 2 * early_exit_list_cap(B, nT)) +
            align256(sizeof(int32_t) * 4) + align256(sizeof(int32_t) * (size_t)B);
 }
 
@@ -676,7 +685,7 @@ hipError_t launch_scan_tiles(const Params &P, hipStream_t s, bool aligned);
 hipError_t launch_draw_final(const Params &P, hipStream_t s, int dtype, bool aligned);
 hipError_t launch_scan_draw(const Params &P, hipStream_t s, int dtype, bool aligned);
 hipError_t launch_tree(const TreeParams &T, hipStream_t s);
-hipError_t launch_stats_list(const Params &P, hipStream_t s, int dtype, bool aligned);
+hipError_t launch_stats_list(const Params &P, hipStream_t s, int dtype, bool aligned, int64_t max_vecs);
 hipError_t launch_ee_init(const Params &P, hipStream_t s);
 hipError_t launch_ee_step(const Params &P, hipStream_t s, int dtype);
 hipError_t launch_filter(const Params &P, hipStream_t s, int dtype, bool aligned);

@@ -333,19 +333,28 @@ __device__ void invalidate_call(const Params &P, int32_t row, bool row_writer)
 }
 
 // ===========================================================================
-// early exit: the positions of each row one at a time, left to right
+// early exit: the positions of each row left to right, in chunks
 // ===========================================================================
-// The first list: every row, with its position-0 vectors; every output slot
-// starts invalid (-1, NaN) and is filled as the steps decide.
+// Step k reads positions [2^k - 1, 2^(k+1) - 1) of the rows still undecided (the
+// vectors of the whole chunk in one streaming launch) and then decides them in order,
+// stopping at the first rejection: the first step reads position 0 of every row, and
+// a row that keeps accepting takes a step per doubling of its accepted length.
+
+// The first lists: every row, with its position-0 vectors (target in slot i, draft in
+// slot B + i or -1); every output slot starts invalid (-1, NaN) and is filled as the
+// steps decide.
 __global__ __launch_bounds__(kBlock) void ee_init_kernel(Params P)
 {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nth = (int64_t)gridDim.x * blockDim.x;
-    if (gid == 0) {
-        P.ee_count[0] = 0;
-        P.ee_count[2] = 0;
-    }
     const bool bad_call = P.gamma != nullptr && P.hdr->status != 0;
+    if (gid == 0) {
+        const bool sample = P.mode == 0;
+        P.ee_count[0] = bad_call ? 0 : P.B;
+        P.ee_count[1] = bad_call ? 0 : (sample ? 2 * P.B : P.B);
+        P.ee_count[2] = 0;
+        P.ee_count[3] = 0;
+    }
     if (bad_call) {
         for (int64_t s = gid; s < P.nT; s += nth) P.emitted[s] = -1;
         for (int64_t s = gid; s < P.nD; s += nth) {
@@ -364,57 +373,58 @@ __global__ __launch_bounds__(kBlock) void ee_init_kernel(Params P)
         }
         const RowGeom G = row_geom(P, (int32_t)i);
         const int32_t g = G.gamma;
-        P.ee_status[i] = g > P.gamma_max ? ST_BAD_GAMMA : 0;
+        // a row longer than the bound the steps cover is invalid and reads nothing
+        const bool over = g > P.gamma_max;
+        P.ee_status[i] = over ? ST_BAD_GAMMA : 0;
         P.ee_rows[0][i] = (int32_t)i;
-        P.ee_vecs[0][2 * i] = (int32_t)G.t_off;
-        P.ee_vecs[0][2 * i + 1] = (P.mode == 0 && g > 0) ? (int32_t)(P.nT + G.d_off) : -1;
+        P.ee_vecs[0][i] = over ? -1 : (int32_t)G.t_off;
+        if (P.mode == 0) P.ee_vecs[0][P.B + i] = (!over && g > 0) ? (int32_t)(P.nT + G.d_off) : -1;
         for (int32_t k = 0; k <= g; ++k) P.emitted[G.t_off + k] = -1;
         for (int32_t k = 0; k < g; ++k) {
             if (P.p_x) P.p_x[G.d_off + k] = kQNaN;
             if (P.q_x) P.q_x[G.d_off + k] = kQNaN;
         }
         if (P.resid) P.resid[i] = kQNaN;
+        if (over) {
+            P.n_accepted[i] = -1;
+            if (P.row_status) P.row_status[i] = ST_BAD_GAMMA;
+            if (P.crop_len) P.crop_len[i] = -1;
+        }
     }
-    if (gid == 0 && !bad_call) P.ee_count[0] = P.B;
 }
 
-// One wave per listed row decides position P.step from the records of the vectors
-// just read: the accept test of draft j (or its argmax match), else the bonus at
-// j = gamma.  A row that is kept going is listed for the next position.
+// One workgroup per listed row decides the positions of this step's chunk: its waves
+// merge the records of every vector of the chunk together, then wave 0 tests all the
+// positions at once (lane i: position j0 + i) and takes the first event, in position
+// order: non-finite logits (the row is invalid), the rejection of draft j (or its
+// argmax mismatch), or the bonus at j = gamma.  Positions before it are kept.  A row
+// invalid from the start (a bad temperature or token) has no event but non-finite
+// logits and its last position.  A row with no event in the chunk is listed for the
+// next chunk, with that chunk's vectors.
+constexpr int kEeWaves = 4;
+
 template <int DT>
-__global__ __launch_bounds__(64) void ee_step_kernel(Params P)
+__global__ __launch_bounds__(kEeWaves * 64) void ee_step_kernel(Params P)
 {
-    const int lane = threadIdx.x;
+    __shared__ ScanLds sh;
+    __shared__ int s_stop;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int buf = P.step & 1;
     if (P.gamma != nullptr && P.hdr->status != 0) return;
     const int32_t slot = (int32_t)blockIdx.x;
     if (slot >= P.ee_count[2 * buf]) return;
     const int32_t row = P.ee_rows[buf][slot];
-    const RowGeom G = row_geom(P, row);
-    const int32_t g = G.gamma, j = P.step;
-    const float T = P.temperature[row];
-    const int32_t rm = row_mode(P.mode, T);
-    const bool greedy = rm == ROW_GREEDY;
     int status = P.ee_status[row];
-    // this position's inputs and records, all loads first
-    int32_t x = -1;
-    float u = 0.0f, zt = 0.0f, zd = 0.0f;
-    if (j < g) {
-        x = P.tokens[G.d_off + j];
-        u = P.uniforms[G.t_off + j];
-        if (!greedy) {
-            zt = P.zx[G.d_off + j];
-            zd = P.zx[P.nD + G.d_off + j];
-        }
-    }
+    if (status & ST_BAD_GAMMA) return;   // invalid from the start, outputs already written
+    const RowGeom G = row_geom(P, row);
+    const int32_t g = G.gamma;
+    const int32_t j0 = P.ee_j0, j1 = P.ee_j1 <= g ? P.ee_j1 : g + 1;   // this step's positions
+    const float T = P.temperature[row];
     const float u_draw = P.uniforms[G.t_off + g];
-    int64_t ti0, ti1, di0 = 0, di1 = -1;
-    vec_records(P, G.t_off + j, ti0, ti1);
-    if (!greedy && j < g) vec_records(P, P.nT + G.d_off + j, di0, di1);
-    const Partial none{-INFINITY, INT32_MAX, 0.0};
-    const Partial qt = ti0 + lane <= ti1 ? P.parts[ti0 + lane] : none;
-    const Partial qd = di0 + lane <= di1 ? P.parts[di0 + lane] : none;
-    if (j == 0) {
+    const int32_t rm = row_mode(P.mode, T);
+    const bool greedy = rm == ROW_GREEDY, maxonly = rm == ROW_BAD_TEMP;
+    const int64_t n_cache = P.cache_len ? P.cache_len[row] : 0;
+    if (j0 == 0 && wave == 0) {
         if (rm == ROW_BAD_TEMP) status |= ST_BAD_TEMP;
         int bad = 0;
         for (int32_t k = lane; k < g; k += 64) {
@@ -423,107 +433,133 @@ __global__ __launch_bounds__(64) void ee_step_kernel(Params P)
         }
         if (wave_or_int(bad)) status |= ST_BAD_TOKEN;
     }
+    const bool pre_invalid = (status & (ST_BAD_TEMP | ST_BAD_TOKEN)) != 0;   // read on wave 0 only
     const TempConst tc = temp_const<DT>(rm == ROW_SAMPLE ? T : 1.0f);
-    float mt = -INFINITY, md = -INFINITY;
-    double St = 0.0, Sd = 0.0;
-    int32_t at = INT32_MAX, unused;
-    // A row invalid from the start (a bad temperature or token) decides nothing, but
-    // like the full round it still reads every position for non-finite logits (its
-    // records hold maxima when the temperature is unusable).
-    const bool pre_invalid = (status & (ST_BAD_TEMP | ST_BAD_TOKEN)) != 0;
-    const bool maxonly = rm == ROW_BAD_TEMP;
-    if (!(status & ST_NONFINITE)) {
-        wave_merge<DT>(P, qt, ti0, ti1, greedy || maxonly, tc, lane, mt, St, at);
-        if ((greedy || maxonly) ? !(mt > -INFINITY && mt < INFINITY) : !(St > 0.0 && St < INFINITY))
-            status |= ST_NONFINITE;
-        if (!greedy && j < g) {
-            wave_merge<DT>(P, qd, di0, di1, maxonly, tc, lane, md, Sd, unused);
-            if (maxonly ? !(md > -INFINITY && md < INFINITY) : !(Sd > 0.0 && Sd < INFINITY)) status |= ST_NONFINITE;
+    ScanBatch none;
+    for (int32_t base = j0; base < j1; base += 64) {
+        const int nt = j1 - base < 64 ? j1 - base : 64;
+        const int32_t dend = j1 < g ? j1 : g;
+        const int nd = greedy || dend <= base ? 0 : (dend - base < 64 ? dend - base : 64);
+        // wave 0: this sub-chunk's per-position inputs, in flight during the merge
+        const int32_t j = base + lane;
+        const bool in = lane < nt, has_d = in && j < g;
+        int32_t x = -1;
+        float u = 0.0f, zt = 0.0f, zd = 0.0f;
+        if (wave == 0 && has_d) {
+            x = P.tokens[G.d_off + j];
+            u = P.uniforms[G.t_off + j];
+            if (!greedy) {
+                zt = P.zx[G.d_off + j];
+                zd = P.zx[P.nD + G.d_off + j];
+            }
         }
+        scan_merge<DT, kEeWaves>(P, G, base, nt, nd, greedy, tc, sh, none, false, maxonly);
+        __syncthreads();
+        if (wave == 0) {
+            const float mt = in ? sh.m[0][lane] : -INFINITY;
+            const double St = in ? sh.S[0][lane] : 0.0;
+            const int32_t at = in ? sh.idx[lane] : INT32_MAX;
+            const float md = has_d && !greedy ? sh.m[1][lane] : -INFINITY;
+            const double Sd = has_d && !greedy ? sh.S[1][lane] : 0.0;
+            bool nonfinite = false, reject = false, qzero = false;
+            double px = kQNaN, qx = kQNaN;
+            if (in) {
+                nonfinite = (greedy || maxonly) ? !(mt > -INFINITY && mt < INFINITY) : !(St > 0.0 && St < INFINITY);
+                if (has_d && !greedy)
+                    nonfinite |= maxonly ? !(md > -INFINITY && md < INFINITY) : !(Sd > 0.0 && Sd < INFINITY);
+            }
+            if (in && !nonfinite && !pre_invalid && has_d) {
+                if (greedy) {
+                    reject = x != at;
+                } else {
+                    px = exp2_f64(((double)zt - (double)mt) * tc.c_eff) / St;
+                    qx = exp2_f64(((double)zd - (double)md) * tc.c_eff) / Sd;
+                    double ratio;
+                    if (qx > 0.0) {
+                        ratio = px / qx;
+                        if (ratio > 1.0) ratio = 1.0;
+                    } else {
+                        ratio = px > 0.0 ? 1.0 : 0.0;
+                        qzero = true;
+                    }
+                    reject = !((double)u < ratio);
+                }
+            }
+            const bool event = in && (nonfinite || j == g || reject);
+            const unsigned long long eb = __ballot(event);
+            const int e = eb ? __ffsll((long long)eb) - 1 : 64;   // first event's lane
+            status |= wave_or_int(lane <= e && qzero ? ST_Q_ZERO : 0);
+            const bool nf = e < 64 && __shfl(nonfinite ? 1 : 0, e) != 0;
+            if (e < 64 && (nf || pre_invalid)) {
+                if (nf) status |= ST_NONFINITE;
+                for (int32_t k = lane; k <= g; k += 64) P.emitted[G.t_off + k] = -1;
+                for (int32_t k = lane; k < g; k += 64) {
+                    if (P.p_x) P.p_x[G.d_off + k] = kQNaN;
+                    if (P.q_x) P.q_x[G.d_off + k] = kQNaN;
+                }
+                if (lane == 0) {
+                    P.n_accepted[row] = -1;
+                    if (P.row_status) P.row_status[row] = status & ST_INVALID;
+                    if (P.resid) P.resid[row] = kQNaN;
+                    if (P.crop_len) P.crop_len[row] = -1;
+                }
+            } else if (!pre_invalid) {
+                // positions before the event are kept; at the event a greedy row emits the
+                // argmax, a sampling row's token is drawn later
+                if (lane < e && in) P.emitted[G.t_off + j] = x;
+                if (greedy && lane == e) P.emitted[G.t_off + j] = at;
+                if (!greedy && lane <= e && has_d) {
+                    if (P.p_x) P.p_x[G.d_off + j] = px;
+                    if (P.q_x) P.q_x[G.d_off + j] = qx;
+                }
+                if (e < 64) {
+                    const int32_t K = base + e;
+                    RowDraw D{};
+                    D.kind = greedy ? DRAW_NONE : (K < g ? DRAW_RESIDUAL : DRAW_BONUS);
+                    const float kmt = __shfl(mt, e), kmd = __shfl(md, e);
+                    const double kSt = __shfl(St, e), kSd = __shfl(Sd, e);
+                    if (D.kind != DRAW_NONE) {
+                        D.K = K;
+                        D.t_row = (int32_t)(G.t_off + K);
+                        D.d_row = (int32_t)(G.d_off + K);
+                        D.u = u_draw;
+                        D.t_slot = (int32_t)(G.t_off + K);
+                        D.m_t = kmt;
+                        D.S_t = kSt;
+                        D.m_d = kmd;
+                        D.S_d = kSd;
+                        D.T = T;
+                        D.theta_t = -INFINITY;
+                        D.theta_d = -INFINITY;
+                    }
+                    if (lane == 0) {
+                        P.n_accepted[row] = K;
+                        if (P.row_status) P.row_status[row] = status;
+                        if (P.crop_len) P.crop_len[row] = (int32_t)(n_cache + K + 1);
+                        P.draws[row] = D;
+                    }
+                }
+            }
+            if (lane == 0) s_stop = e < 64 ? 1 : 0;
+        }
+        __syncthreads();
+        if (s_stop) return;
     }
-    const int64_t n_cache = P.cache_len ? P.cache_len[row] : 0;
-    if ((status & ST_NONFINITE) || (pre_invalid && j == g)) {
-        for (int32_t k = lane; k <= g; k += 64) P.emitted[G.t_off + k] = -1;
-        for (int32_t k = lane; k < g; k += 64) {
-            if (P.p_x) P.p_x[G.d_off + k] = kQNaN;
-            if (P.q_x) P.q_x[G.d_off + k] = kQNaN;
-        }
-        if (lane == 0) {
-            P.n_accepted[row] = -1;
-            if (P.row_status) P.row_status[row] = status & ST_INVALID;
-            if (P.resid) P.resid[row] = kQNaN;
-            if (P.crop_len) P.crop_len[row] = -1;
-        }
-        return;
-    }
-    int32_t K = -1;
-    RowDraw D{};
-    D.kind = DRAW_NONE;
-    if (pre_invalid) {
-        // listed for the next position below
-    } else if (greedy) {
-        if (j < g && x == at) {
-            if (lane == 0) P.emitted[G.t_off + j] = x;
-        } else {
-            K = j;
-            if (lane == 0) P.emitted[G.t_off + j] = at;
-        }
-    } else if (j < g) {
-        double px = kQNaN, qx = kQNaN, ratio = 0.0;
-        px = exp2_f64(((double)zt - (double)mt) * tc.c_eff) / St;
-        qx = exp2_f64(((double)zd - (double)md) * tc.c_eff) / Sd;
-        if (qx > 0.0) {
-            ratio = px / qx;
-            if (ratio > 1.0) ratio = 1.0;
-        } else {
-            ratio = px > 0.0 ? 1.0 : 0.0;
-            status |= ST_Q_ZERO;
-        }
-        if (lane == 0) {
-            if (P.p_x) P.p_x[G.d_off + j] = px;
-            if (P.q_x) P.q_x[G.d_off + j] = qx;
-        }
-        if (!((double)u < ratio)) {
-            K = j;
-            D.kind = DRAW_RESIDUAL;
-        } else if (lane == 0) {
-            P.emitted[G.t_off + j] = x;
-        }
-    } else {
-        K = g;
-        D.kind = DRAW_BONUS;
-    }
-    if (K >= 0) {
-        if (D.kind != DRAW_NONE) {
-            D.K = K;
-            D.t_row = (int32_t)(G.t_off + K);
-            D.d_row = (int32_t)(G.d_off + K);
-            D.u = u_draw;
-            D.t_slot = (int32_t)(G.t_off + K);
-            D.m_t = mt;
-            D.S_t = St;
-            D.m_d = md;
-            D.S_d = Sd;
-            D.T = T;
-            D.theta_t = -INFINITY;
-            D.theta_d = -INFINITY;
-        }
-        if (lane == 0) {
-            P.n_accepted[row] = K;
-            if (P.row_status) P.row_status[row] = status;
-            if (P.crop_len) P.crop_len[row] = (int32_t)(n_cache + K + 1);
-            P.draws[row] = D;
-        }
-        return;
-    }
-    // kept: listed for the next position
+    if (wave != 0) return;
+    // no event through the chunk (j1 <= g here): listed for the next chunk, positions
+    // [j1, min(ee_j2, g + 1)), with their target vectors, then their draft vectors
+    const int32_t a = j1, b = P.ee_j2 <= g ? P.ee_j2 : g + 1;
+    const int32_t nt = b - a, nd = greedy ? 0 : (b <= g ? b : g) - a;
+    int32_t base = 0;
     if (lane == 0) {
         P.ee_status[row] = status;
         const int32_t s2 = atomicAdd(&P.ee_count[2 * (buf ^ 1)], 1);
+        base = atomicAdd(&P.ee_count[2 * (buf ^ 1) + 1], nt + nd);
         P.ee_rows[buf ^ 1][s2] = row;
-        P.ee_vecs[buf ^ 1][2 * s2] = (int32_t)(G.t_off + j + 1);
-        P.ee_vecs[buf ^ 1][2 * s2 + 1] = (!greedy && j + 1 < g) ? (int32_t)(P.nT + G.d_off + j + 1) : -1;
     }
+    base = __shfl(base, 0);
+    for (int32_t q = lane; q < nt + nd; q += 64)
+        P.ee_vecs[buf ^ 1][base + q] = q < nt ? (int32_t)(G.t_off + a + q) : (int32_t)(P.nT + G.d_off + a + (q - nt));
 }
 
 // ===========================================================================
@@ -1025,7 +1061,7 @@ hipError_t launch_ee_init(const Params &P, hipStream_t s)
 hipError_t launch_ee_step(const Params &P, hipStream_t s, int dtype)
 {
     const void *fn = dtype == 0 ? (const void *)ee_step_kernel<0> : (const void *)ee_step_kernel<1>;
-    return launch(fn, P.B, 64, P, s);
+    return launch(fn, P.B, kEeWaves * 64, P, s);
 }
 
 hipError_t launch_scan_draw(const Params &P, hipStream_t s, int dtype, bool aligned)

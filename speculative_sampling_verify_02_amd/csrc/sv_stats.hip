@@ -89,11 +89,11 @@ __device__ __forceinline__ void stats_body(const Params &P)
     }
 }
 
-// One piece of a listed vector per wave: the early-exit steps read only the vectors
-// of the rows still undecided at the current position (two list slots per row).
-// Workgroup b takes piece b mod ipv of list slot b / ipv; slots past the list's
-// length, and holes (-1), do nothing.  Thread 0 of workgroup 0 also clears the other
-// list buffer's counts, which the step kernel after this one fills.
+// The early-exit steps' streaming: the pieces of the listed vectors (those of the
+// positions each undecided row reads at this step), grid-strided over one-wave
+// workgroups, each with its next piece's loads in flight while one is reduced.  Slots
+// holding -1 are skipped.  Thread 0 of workgroup 0 also clears the other list
+// buffer's counts, which the step kernel after this one fills.
 template <int DT, bool AL>
 __global__ __launch_bounds__(64) void stats_list_kernel(Params P)
 {
@@ -112,22 +112,53 @@ __global__ __launch_bounds__(64) void stats_list_kernel(Params P)
     }
     if (P.gamma != nullptr && P.hdr->status != 0) return;
     const int64_t ipv = P.geo.ipv;
-    const int64_t slot = (int64_t)blockIdx.x / ipv;
-    const int64_t j = (int64_t)blockIdx.x - slot * ipv;
-    if (slot >= 2 * (int64_t)P.ee_count[2 * buf]) return;
-    const int64_t v = P.ee_vecs[buf][slot];
-    if (v < 0) return;
+    const int64_t n = (int64_t)P.ee_count[2 * buf + 1] * ipv;   // pieces listed
+    const int64_t G = gridDim.x;
+    const int32_t *list = P.ee_vecs[buf];
+    int64_t p = blockIdx.x;
+    if (p >= n) return;
+    auto locate = [&](int64_t q, int64_t &v, int64_t &j) {
+        const int64_t s = qdiv(q, ipv, P.geo.inv_ipv);
+        j = q - s * ipv;
+        v = list[s];
+    };
+    int64_t v, j;
+    locate(p, v, j);
     ItemRaw<DT> ra, rb;
-    half_begin<DT, AL>(P, v, j, 0, true, ra, lane);
-    half_begin<DT, AL>(P, v, j, 1, true, rb, lane);
-    const VecCtx vc = vec_ctx(P, v);
-    const int32_t rm = row_mode(P.mode, vc.T);
-    const TempConst tc = rm == ROW_SAMPLE ? temp_const<DT>(vc.T) : TempConst{};
-    PieceAcc<DT> acc;
-    piece_half<DT, AL>(P, vc, rm, tc, j, 0, half_len(P, j, 0), ra, acc, lane, tab);
-    const int n1 = half_len(P, j, 1);
-    if (n1 > 0) piece_half<DT, AL>(P, vc, rm, tc, j, 1, n1, rb, acc, lane, tab);
-    piece_finish<DT>(P, vc, rm, tc, v, j, acc);
+    half_begin<DT, AL>(P, v, j, 0, v >= 0, ra, lane);
+    half_begin<DT, AL>(P, v, j, 1, v >= 0, rb, lane);
+    VecCtx vc = vec_ctx(P, v >= 0 ? v : 0);
+    float cached_T = __builtin_nanf("");
+    TempConst tc{};
+    for (;;) {
+        const int64_t cv = v, cj = j;
+        const int64_t pn = p + G;
+        const bool live = pn < n;
+        if (live) locate(pn, v, j);   // in flight while this piece is reduced
+        const bool next = live && v >= 0;
+        if (cv >= 0) {
+            const int32_t rm = row_mode(P.mode, vc.T);
+            if (rm == ROW_SAMPLE && vc.T != cached_T) {
+                tc = temp_const<DT>(vc.T);
+                cached_T = vc.T;
+            }
+            PieceAcc<DT> acc;
+            piece_half<DT, AL>(P, vc, rm, tc, cj, 0, half_len(P, cj, 0), ra, acc, lane, tab);
+            half_begin<DT, AL>(P, v, j, 0, next, ra, lane);
+            const int n1 = half_len(P, cj, 1);
+            if (n1 > 0) piece_half<DT, AL>(P, vc, rm, tc, cj, 1, n1, rb, acc, lane, tab);
+            half_begin<DT, AL>(P, v, j, 1, next, rb, lane);
+            const VecCtx vn = vec_ctx(P, next ? v : 0);
+            piece_finish<DT>(P, vc, rm, tc, cv, cj, acc);
+            vc = vn;
+        } else {
+            half_begin<DT, AL>(P, v, j, 0, next, ra, lane);
+            half_begin<DT, AL>(P, v, j, 1, next, rb, lane);
+            vc = vec_ctx(P, next ? v : 0);
+        }
+        if (!live) break;
+        p = pn;
+    }
 }
 
 // 16-byte aligned rows (the usual case): one workgroup per CU, of 16 waves (bf16) or 12
@@ -191,12 +222,43 @@ int32_t stats_grid_cap(int dtype, bool aligned)
     return (int32_t)cap;
 }
 
-hipError_t launch_stats_list(const Params &P, hipStream_t s, int dtype, bool aligned)
+static const void *stats_list_fn(int dtype, bool aligned)
 {
-    const void *fn = dtype == 0
+    return dtype == 0
         ? (aligned ? (const void *)stats_list_kernel<0, true> : (const void *)stats_list_kernel<0, false>)
         : (aligned ? (const void *)stats_list_kernel<1, true> : (const void *)stats_list_kernel<1, false>);
-    return launch(fn, 2 * (int64_t)P.B * P.geo.ipv, 64, P, s);
+}
+
+// One-wave workgroups of the list streaming kernel that fit on the current device at
+// once (cached per device and kernel variant).
+static int64_t stats_list_grid_cap(int dtype, bool aligned)
+{
+    constexpr int kMaxDev = 64;
+    static int64_t cache[kMaxDev][4] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 4096;
+    const int var = dtype * 2 + (aligned ? 1 : 0);
+    if (dev < kMaxDev && cache[dev][var] > 0) return cache[dev][var];
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stats_list_fn(dtype, aligned), 64, 0) != hipSuccess ||
+        per_cu <= 0)
+        per_cu = 8;
+    const int64_t cap = (int64_t)cus * per_cu;
+    if (dev < kMaxDev) cache[dev][var] = cap;
+    return cap;
+}
+
+// max_vecs: a bound on the vectors this step lists (the grid covers their pieces, up
+// to what fits on the device at once)
+hipError_t launch_stats_list(const Params &P, hipStream_t s, int dtype, bool aligned, int64_t max_vecs)
+{
+    int64_t blocks = max_vecs * P.geo.ipv;
+    const int64_t cap = stats_list_grid_cap(dtype, aligned);
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    return launch(stats_list_fn(dtype, aligned), blocks, 64, P, s);
 }
 
 hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned, hipEvent_t start, hipEvent_t stop)

@@ -25,13 +25,14 @@ def H():
     return gpu_harness
 
 
-def run_early(H, w, mode=None, dense=False, cache_len=None, tensors=None):
+def run_early(H, w, mode=None, dense=False, cache_len=None, tensors=None, gamma_max=None):
     import speculative_sampling_verify_02_amd as sv
     d = tensors or H.to_device(w)
     gamma = w.dense_gamma if dense else d["gamma"]
     cl = None if cache_len is None else torch.from_numpy(np.ascontiguousarray(cache_len, np.int32)).cuda()
+    gm = int(w.gamma.max()) if gamma_max is None else gamma_max
     n, e, crop, dg = sv.spec_verify_early_exit(d["target"], d["draft"], d["tokens"], d["uniforms"],
-                                               d["temperature"], gamma, gamma_max=int(w.gamma.max()),
+                                               d["temperature"], gamma, gamma_max=gm,
                                                cache_len=cl, mode=mode or w.mode, diag=True)
     torch.cuda.synchronize()
     out = dict(n_accepted=n.cpu().numpy(), emitted=e.cpu().numpy(), crop_len=crop.cpu().numpy())
@@ -134,3 +135,26 @@ def test_invalid_rows_read_to_the_end(H, dtype):
     st = g["row_status"]
     assert st[0] == oracle.BAD_TEMP | oracle.NONFINITE and st[3] == oracle.BAD_TOKEN | oracle.NONFINITE
     assert st[4] == oracle.BAD_TOKEN and st[5] == oracle.BAD_TEMP
+
+
+def test_rows_beyond_gamma_max(H):
+    """A ragged row longer than the caller's gamma_max is invalid (BAD_GAMMA): it emits
+    nothing and keeps no cache count, and the other rows decide exactly as in a call
+    whose bound covers every row (which the oracle checks)."""
+    w = workloads.small(seed=83, batch=6, vocab=3000, dtype="bf16", gamma=[2, 5, 1, 3, 0, 4], noise=0.05)
+    full, _ = parity(H, w, seed=83)
+    cache = np.random.default_rng(83).integers(0, 4096, w.batch).astype(np.int32)   # parity()'s
+    _say("[case] early exit with gamma_max 3 under row gammas up to 5")
+    cut = run_early(H, w, cache_len=cache, gamma_max=3)
+    t_off, _ = w.offsets()
+    assert np.any(w.gamma > 3) and np.any(full["n_accepted"][w.gamma <= 3] >= 1)
+    for i in range(w.batch):
+        a, b = t_off[i], t_off[i + 1]
+        if w.gamma[i] > 3:
+            assert cut["n_accepted"][i] == -1 and cut["crop_len"][i] == -1, i
+            assert cut["row_status"][i] == oracle.BAD_GAMMA and np.all(cut["emitted"][a:b] == -1), i
+            assert np.all(np.isnan(cut["p_x"][w.offsets()[1][i]:w.offsets()[1][i + 1]])), i
+        else:
+            for k in ("n_accepted", "crop_len", "row_status"):
+                assert cut[k][i] == full[k][i], (k, i)
+            assert np.array_equal(cut["emitted"][a:b], full["emitted"][a:b]), i
