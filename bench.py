@@ -404,6 +404,9 @@ def bench_verify(args, config: str, mode: str, dev, cpu: bool):
     else:
         ws = torch.empty(sv.workspace_bytes(B, nT, V, dt), dtype=torch.uint8, device=dev)
     gmax = int(w.gamma.max())
+    # the plan the round with early exit takes here by default (the library's choice
+    # for this shape with no acceptance hint)
+    ee_plan = sv.early_exit_plan(B, nT, V, dt, mode, gmax) if early else None
 
     def step(k, d=None):
         d = d or copies[k % len(copies)]
@@ -425,10 +428,18 @@ def bench_verify(args, config: str, mode: str, dev, cpu: bool):
     E = emitted.cpu().numpy()
     gam = w.gamma
     pass1_bytes = (nT + (nD if mode == "sample" else 0)) * V * esz
-    if early:
-        # positions 0..K of the target, and 0..min(K, gamma-1) of the draft in sampling mode
-        pass1_bytes = int(sum((K[i] + 1 + (min(K[i], gam_i - 1) + 1 if mode == "sample" else 0)) * V * esz
-                              for i, gam_i in enumerate(w.gamma) if K[i] >= 0))
+    if early and ee_plan == "steps":
+        # the chunks of positions [2^k - 1, 2^(k+1) - 1) up to the one holding K, of the
+        # target, and of the draft in sampling mode (positions below gamma)
+        def chunk_vectors(k_acc, g):
+            n, k = 0, 0
+            while (1 << k) - 1 <= k_acc:
+                a, b = (1 << k) - 1, (1 << (k + 1)) - 1
+                n += min(b, g + 1) - a + (max(0, min(b, g) - a) if mode == "sample" else 0)
+                k += 1
+            return n
+        pass1_bytes = int(sum(chunk_vectors(int(K[i]), int(g_i)) * V * esz
+                              for i, g_i in enumerate(w.gamma) if K[i] >= 0))
     pass2_bytes = 0
     if mode == "sample":
         # a rejection re-reads position K of both models; a bonus draw re-reads one
@@ -471,7 +482,7 @@ def bench_verify(args, config: str, mode: str, dev, cpu: bool):
         "dtype": w.dtype,
         "config": {"workload": w.name, "batch": B, "gamma": int(gam.max()) if dense is None else dense,
                    "ragged": dense is None, "vocab": V, "mode": mode,
-                   "variant": "early exit" if early else (
+                   "variant": f"early exit ({ee_plan.replace('_', ' ')})" if early else (
                        "top-k 50, top-p 0.9 on p and q" if filt else "all positions in parallel"),
                    "rotated_device_copies": len(copies)},
         "rows_per_s": B / sec_per_step,
@@ -482,7 +493,7 @@ def bench_verify(args, config: str, mode: str, dev, cpu: bool):
         "alpha_empirical": alpha_emp,
         "rows_rejected": int((valid & (K < gam)).sum()),
         "rows_bonus": int((valid & (K == gam)).sum()),
-        "roofline": {"kernel": "stats_list_kernel + ee_step_kernel steps" if early else (
+        "roofline": {"kernel": "stats_list_kernel + ee_step_kernel steps" if ee_plan == "steps" else (
                          "filter_stats_kernel" if fused else "stats_kernel"),
                      "bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,

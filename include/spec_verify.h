@@ -223,18 +223,27 @@ sv_status spec_tree_verify_greedy(const void *target_logits, int32_t dtype, int6
                                   void *hip_stream);
 
 /*
- * The verification round with early exit: positions are read left to right and,
- * for each row, nothing after its first rejection is read (rayaq.ca "Speculative
- * decoding", section "One round", step 3, which stops at the first rejection).  The
- * positions go in chunks that double in length: step k reads positions
- * [2^k - 1, 2^(k+1) - 1) of both models for the rows still undecided, then decides
- * them in order, so ceil(log2(gamma_max + 2)) steps cover every row.  Kept drafts,
- * drawn tokens and the residual mass are those of spec_verify on the same inputs;
- * what differs is what a row can see: positions after its rejection are not checked
- * for non-finite logits (a NaN there leaves the row valid) and their p(x_j), q(x_j)
- * diagnostics are NaN.  Draft tokens are all range-checked.  Fewer logits are read: a
- * row that rejects at position K_i reads the vectors of the chunks up to the one
- * holding K_i (fewer than 4(K_i + 1) of them) instead of 2 gamma_i + 1.
+ * The verification round with early exit: for each row, nothing after its first
+ * rejection counts (rayaq.ca "Speculative decoding", section "One round", step 3,
+ * which stops at the first rejection).  Kept drafts, drawn tokens and the residual
+ * mass are those of spec_verify on the same inputs; what differs is what a row can
+ * see: positions after its rejection are not checked for non-finite logits (a NaN
+ * there leaves the row valid) and their p(x_j), q(x_j) diagnostics are NaN; a bad
+ * draft token anywhere in a row still makes it invalid.  Two plans give identical
+ * outputs:
+ *   SV_EE_STEPS     positions are read left to right in chunks that double in length:
+ *                   step k reads positions [2^k - 1, 2^(k+1) - 1) of both models for
+ *                   the rows still undecided, then decides them in order, so
+ *                   ceil(log2(gamma_max + 2)) steps cover every row.  A row that
+ *                   rejects at K_i reads the vectors of the chunks up to the one
+ *                   holding K_i (fewer than 4(K_i + 1)) instead of 2 gamma_i + 1, at
+ *                   the price of a fixed cost per step.
+ *   SV_EE_ONE_PASS  spec_verify's single streaming pass over every position, with the
+ *                   decisions and status bits above: cheaper when the vectors of one
+ *                   position are too few to pay for a step.
+ *   SV_EE_AUTO      the plan with the smaller expected time for the shape, given the
+ *                   caller's per-position acceptance rate (accept_hint); see
+ *                   spec_verify_early_exit_plan.
  *
  * The cache rollback (rayaq.ca "Speculative decoding", section "Verification
  * attention and the cache"): a round that keeps K_i drafts over a cached prefix of
@@ -245,12 +254,20 @@ sv_status spec_tree_verify_greedy(const void *target_logits, int32_t dtype, int6
  *   gamma_max   ragged batches (gamma_per_row != NULL): a host-side bound on every
  *               gamma_i, >= 0, which sets the number of steps; a row with
  *               gamma_i > gamma_max is invalid (SV_ROW_BAD_GAMMA, n_accepted and
- *               crop_len -1, every emitted slot -1) and none of its logits is read.
- *               Ignored for dense batches (gamma_uniform is the bound).
+ *               crop_len -1, every emitted slot -1; the chunked plan reads none of its
+ *               logits).  Ignored for dense batches (gamma_uniform is the bound).
  *   cache_len   [batch] int32 device, or NULL for n_i = 0: cache entries before the round
  *   crop_len    [batch] int32 device out, or NULL: n_i + K_i + 1, or -1 for an invalid row
+ *   plan        SV_EE_AUTO, SV_EE_STEPS or SV_EE_ONE_PASS (else SV_EINVAL)
+ *   accept_hint SV_EE_AUTO only: the expected probability that a draft is kept (the
+ *               acceptance rate measured on recent rounds, rayaq.ca "Speculative
+ *               decoding", section "Tradeoffs"), clamped to [0, 1]; negative or NaN
+ *               for the default, 0.6
  *   workspace   >= spec_verify_early_exit_workspace_bytes(...) bytes, 256-byte aligned
  */
+#define SV_EE_AUTO 0
+#define SV_EE_STEPS 1
+#define SV_EE_ONE_PASS 2
 size_t spec_verify_early_exit_workspace_bytes(int32_t batch, int64_t n_target_rows, int64_t vocab,
                                               int32_t dtype);
 sv_status spec_verify_early_exit(const void *target_logits, const void *draft_logits, int32_t dtype,
@@ -260,7 +277,19 @@ sv_status spec_verify_early_exit(const void *target_logits, const void *draft_lo
                                  int32_t gamma_uniform, int32_t gamma_max, int32_t mode,
                                  const int32_t *cache_len, int32_t *n_accepted,
                                  int32_t *emitted_tokens, int32_t *crop_len, const sv_diag *diag,
-                                 void *workspace, size_t workspace_bytes, void *hip_stream);
+                                 int32_t plan, float accept_hint, void *workspace, size_t workspace_bytes,
+                                 void *hip_stream);
+
+/*
+ * The plan SV_EE_AUTO takes for a shape (SV_EE_STEPS or SV_EE_ONE_PASS), or a negative
+ * status for invalid arguments.  Host only, no GPU work.  It compares expected times
+ * from rates measured on MI355X: the streaming pass (~6.7 TB/s after ~13 us of fixed
+ * cost with its scan) against the steps (~6 TB/s, ~12.5 us fixed per step), where a
+ * row reaches chunk k with probability accept_hint^(2^k - 1) and the mean gamma is
+ * n_target_rows / batch - 1.
+ */
+int32_t spec_verify_early_exit_plan(int32_t batch, int64_t n_target_rows, int64_t vocab, int32_t dtype,
+                                    int32_t mode, int32_t gamma_max, float accept_hint);
 
 /*
  * The verification round on filtered distributions: each sampling row's top-k and

@@ -23,6 +23,7 @@ NOALLOC_SCRATCH_BYTES = 16 << 20
 # sv_dtype / sv_mode
 SV_BF16, SV_F32 = 0, 1
 SV_SAMPLE, SV_GREEDY = 0, 1
+SV_EE_AUTO, SV_EE_STEPS, SV_EE_ONE_PASS = 0, 1, 2
 # row status bits
 ROW_BAD_TOKEN = 1
 ROW_Q_ZERO = 2
@@ -38,7 +39,7 @@ EXPORTED = ("spec_verify", "spec_verify_workspace_bytes", "spec_verify_strerror"
             "spec_sample_workspace_bytes", "spec_tree_verify_greedy",
             "spec_tree_verify_greedy_workspace_bytes", "spec_verify_early_exit",
             "spec_verify_early_exit_workspace_bytes", "spec_verify_filtered",
-            "spec_verify_filtered_workspace_bytes", "spec_verify_noalloc")
+            "spec_verify_filtered_workspace_bytes", "spec_verify_noalloc", "spec_verify_early_exit_plan")
 
 
 class SpecVerifyError(RuntimeError):
@@ -81,8 +82,10 @@ def _load():
     L.spec_verify_early_exit_workspace_bytes.argtypes = [i32, i64, i64, i32]
     L.spec_verify_early_exit_workspace_bytes.restype = sz
     L.spec_verify_early_exit.argtypes = [vp, vp, i32, i64, i32, i64, vp, vp, vp, vp, i32, i32, i32, vp, vp,
-                                         vp, vp, ctypes.POINTER(Diag), vp, sz, vp]
+                                         vp, vp, ctypes.POINTER(Diag), i32, ctypes.c_float, vp, sz, vp]
     L.spec_verify_early_exit.restype = ctypes.c_int
+    L.spec_verify_early_exit_plan.argtypes = [i32, i64, i64, i32, i32, i32, ctypes.c_float]
+    L.spec_verify_early_exit_plan.restype = ctypes.c_int
     L.spec_verify_filtered_workspace_bytes.argtypes = [i32, i64, i64, i32]
     L.spec_verify_filtered_workspace_bytes.restype = sz
     L.spec_verify_filtered.argtypes = [vp, vp, i32, i64, i32, i64, vp, vp, vp, vp, i32, vp, vp, vp, vp,
@@ -168,18 +171,40 @@ def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature
                    mode=mode, diag=diag, workspace=workspace, out=out)
 
 
+EE_PLANS = {"auto": SV_EE_AUTO, "steps": SV_EE_STEPS, "one_pass": SV_EE_ONE_PASS}
+
+
 def spec_verify_early_exit(target_logits, draft_logits, draft_tokens, uniforms, temperature,
                            gamma_per_row=None, *, gamma_max: int | None = None, cache_len=None,
                            mode: str = "sample", diag: bool = False, workspace: torch.Tensor | None = None,
-                           out=None):
-    """spec_verify with early exit (positions read left to right, nothing after a row's
-    first rejection).  gamma_max bounds gamma_i of a ragged batch (default: read from
-    gamma_per_row, which synchronizes).  cache_len: int32 [B] device tensor of cached
-    prefix lengths (None: 0).  Returns (n_accepted, emitted, crop_len) and, with
-    diag=True, the diagnostics dict; crop_len[i] = cache_len[i] + n_accepted[i] + 1."""
+                           out=None, plan: str = "auto", accept_hint: float | None = None):
+    """spec_verify with early exit (nothing after a row's first rejection counts).
+    gamma_max bounds gamma_i of a ragged batch (default: read from gamma_per_row, which
+    synchronizes).  cache_len: int32 [B] device tensor of cached prefix lengths (None:
+    0).  plan: "steps" (positions read left to right in doubling chunks by the rows
+    still undecided), "one_pass" (one pass over every position) or "auto" (the one
+    expected faster for the shape, given accept_hint, the expected per-draft acceptance
+    rate; None for the library's default).  Every plan gives the same outputs.  Returns
+    (n_accepted, emitted, crop_len) and, with diag=True, the diagnostics dict;
+    crop_len[i] = cache_len[i] + n_accepted[i] + 1."""
+    if plan not in EE_PLANS:
+        raise ValueError(f"plan must be one of {sorted(EE_PLANS)}")
     return _verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, gamma_per_row,
                    mode=mode, diag=diag, workspace=workspace, out=out, early_exit=True,
-                   gamma_max=gamma_max, cache_len=cache_len)
+                   gamma_max=gamma_max, cache_len=cache_len, ee_plan=EE_PLANS[plan],
+                   accept_hint=-1.0 if accept_hint is None else float(accept_hint))
+
+
+def early_exit_plan(batch: int, n_target_rows: int, vocab: int, dtype: int, mode: str, gamma_max: int,
+                    accept_hint: float | None = None) -> str:
+    """The plan spec_verify_early_exit(plan="auto") takes for a shape: "steps" or
+    "one_pass" (host only)."""
+    rc = int(lib.spec_verify_early_exit_plan(batch, n_target_rows, vocab, dtype,
+                                             SV_SAMPLE if mode == "sample" else SV_GREEDY, gamma_max,
+                                             -1.0 if accept_hint is None else float(accept_hint)))
+    if rc < 0:
+        raise SpecVerifyError(rc, strerror(rc))
+    return {SV_EE_STEPS: "steps", SV_EE_ONE_PASS: "one_pass"}[rc]
 
 
 def spec_verify_filtered(target_logits, draft_logits, draft_tokens, uniforms, temperature,
@@ -195,7 +220,7 @@ def spec_verify_filtered(target_logits, draft_logits, draft_tokens, uniforms, te
 
 def _verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, gamma_per_row=None, *,
             mode="sample", diag=False, workspace=None, out=None, early_exit=False, gamma_max=None,
-            cache_len=None, top_k=None, top_p=None, filtered=False):
+            cache_len=None, top_k=None, top_p=None, filtered=False, ee_plan=0, accept_hint=-1.0):
     """Verify a batch of drafted rows on the GPU.
 
     target_logits  bf16/fp32 [n_target_rows, V] (packed) or [B, gamma+1, V] (dense)
@@ -328,8 +353,8 @@ def _verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, ga
     rc = lib.spec_verify_early_exit(_ptr(target_logits), _ptr(draft_logits), dtype, V, B, n_target_rows,
                                     _ptr(draft_tokens), _ptr(uniforms), _ptr(temperature), _ptr(gamma_t),
                                     gamma_uniform, int(gamma_max or 0), md, _ptr(cache_len), _ptr(n_acc),
-                                    _ptr(emitted), _ptr(crop), dptr, _ptr(workspace), workspace.numel(),
-                                    ctypes.c_void_p(stream))
+                                    _ptr(emitted), _ptr(crop), dptr, ee_plan, accept_hint, _ptr(workspace),
+                                    workspace.numel(), ctypes.c_void_p(stream))
     if rc != SV_OK:
         raise SpecVerifyError(rc, strerror(rc))
     return (n_acc, emitted, crop, dg) if diag else (n_acc, emitted, crop)

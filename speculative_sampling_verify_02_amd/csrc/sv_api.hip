@@ -4,6 +4,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+#include <cmath>
+
 #include "spec_verify.h"
 #include "sv_internal.h"
 
@@ -49,6 +52,14 @@ extern "C" sv_status spec_verify_set_profile_events(void *start_event, void *sto
     return SV_OK;
 }
 
+// The round with early exit run as one pass (its decisions from a pass that read
+// every position): what the scan needs besides spec_verify's arguments.
+struct EeArgs {
+    const int32_t *cache_len;
+    int32_t *crop_len;
+    int32_t gamma_max;
+};
+
 static sv_status verify_impl(const void *target_logits, const void *draft_logits, int32_t dtype,
                              int64_t vocab, int32_t batch, int64_t n_target_rows,
                              const int32_t *draft_tokens, const float *uniforms,
@@ -56,7 +67,7 @@ static sv_status verify_impl(const void *target_logits, const void *draft_logits
                              int32_t gamma_uniform, int32_t mode, int32_t *n_accepted,
                              int32_t *emitted_tokens, const sv_diag *diag, void *workspace,
                              size_t workspace_bytes, void *hip_stream, const int32_t *top_k,
-                             const float *top_p)
+                             const float *top_p, const EeArgs *ee = nullptr)
 {
     if (dtype != SV_BF16 && dtype != SV_F32) return SV_EDTYPE;
     if (mode != SV_SAMPLE && mode != SV_GREEDY) return SV_EINVAL;
@@ -122,6 +133,11 @@ static sv_status verify_impl(const void *target_logits, const void *draft_logits
         P.top_p = top_p;
         P.theta = reinterpret_cast<float *>(ws + L.total);
     }
+    if (ee) {
+        P.cache_len = ee->cache_len;
+        P.crop_len = ee->crop_len;
+        P.gamma_max = ee->gamma_max;
+    }
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     hipError_t e = hipSuccess;
@@ -138,9 +154,9 @@ static sv_status verify_impl(const void *target_logits, const void *draft_logits
     if (e == hipSuccess) {
         if (mode == SV_SAMPLE && dtype == 0) {
             P.st_split = sv::scan_tiles_split(batch, P.geo.ntiles);
-            e = sv::launch_scan_tiles(P, s, aligned);
+            e = sv::launch_scan_tiles(P, s, aligned, ee != nullptr);
         } else {
-            e = sv::launch_scan(P, s, dtype);
+            e = sv::launch_scan(P, s, dtype, ee != nullptr);
             if (e == hipSuccess && mode == SV_SAMPLE) e = sv::launch_verify(P, s, dtype, aligned);
         }
     }
@@ -319,9 +335,53 @@ extern "C" size_t spec_verify_early_exit_workspace_bytes(int32_t batch, int64_t 
     return base == 0 ? 0 : base + sv::early_exit_extra_bytes(batch, n_target_rows);
 }
 
-// The round with early exit: step k reads positions [2^k - 1, 2^(k+1) - 1) of the
-// rows still undecided (a listed-vector streaming kernel), then decides them in order
-// (one wave per listed row); the draws follow as in spec_verify.
+// Expected time of the two plans of the round with early exit, from rates measured on
+// MI355X: the streaming pass reads at ~6.7 TB/s after ~8 us of start-up, a step of the
+// chunked plan reads at ~6 TB/s and pays ~12.5 us for its two launches and their
+// dependent loads, and the one-pass plan's scan costs ~5 us more than the steps'
+// decisions do.  The residual's tile sums and the draw are the same in both.  With a
+// per-position acceptance rate alpha, chunk k (positions [2^k - 1, 2^(k+1) - 1)) is
+// reached by a row with probability alpha^(2^k - 1).
+static int32_t ee_choose(int32_t batch, int64_t n_target_rows, int64_t vocab, int32_t dtype, int32_t mode,
+                         int32_t gamma_max, float accept_hint)
+{
+    constexpr double kPassRate = 6.7e12, kPassFixed = 8e-6 + 5e-6;
+    constexpr double kStepRate = 6.0e12, kStepFixed = 12.5e-6;
+    constexpr double kDefaultAlpha = 0.6;
+    double alpha = accept_hint >= 0.0f ? (double)accept_hint : kDefaultAlpha;   // NaN: the default
+    if (alpha > 1.0) alpha = 1.0;
+    const double esz = dtype == SV_BF16 ? 2.0 : 4.0;
+    const double vec_bytes = (double)vocab * esz;
+    const bool sample = mode == SV_SAMPLE;
+    const double n_vecs = (double)n_target_rows + (sample ? (double)(n_target_rows - batch) : 0.0);
+    const double t_pass = kPassFixed + n_vecs * vec_bytes / kPassRate;
+    const double gbar = (double)n_target_rows / (double)batch - 1.0;   // mean drafts per row
+    double t_steps = 0.0;
+    for (int k = 0; k < 62; ++k) {
+        const double j0 = (double)((int64_t(1) << k) - 1);
+        if (j0 > (double)gamma_max) break;
+        const double j1 = (double)((int64_t(1) << (k + 1)) - 1);
+        const double nt = std::max(0.0, std::min(j1, gbar + 1.0) - j0);
+        const double nd = sample ? std::max(0.0, std::min(j1, gbar) - j0) : 0.0;
+        t_steps += kStepFixed + (double)batch * std::pow(alpha, j0) * (nt + nd) * vec_bytes / kStepRate;
+    }
+    return t_steps < t_pass ? SV_EE_STEPS : SV_EE_ONE_PASS;
+}
+
+extern "C" int32_t spec_verify_early_exit_plan(int32_t batch, int64_t n_target_rows, int64_t vocab, int32_t dtype,
+                                               int32_t mode, int32_t gamma_max, float accept_hint)
+{
+    if (dtype != SV_BF16 && dtype != SV_F32) return SV_EDTYPE;
+    if (mode != SV_SAMPLE && mode != SV_GREEDY) return SV_EINVAL;
+    if (batch <= 0 || vocab <= 0 || n_target_rows < batch || gamma_max < 0) return SV_EINVAL;
+    return ee_choose(batch, n_target_rows, vocab, dtype, mode, gamma_max, accept_hint);
+}
+
+// The round with early exit.  SV_EE_STEPS: step k reads positions
+// [2^k - 1, 2^(k+1) - 1) of the rows still undecided (a listed-vector streaming
+// kernel), then decides them in order (one workgroup per listed row).  SV_EE_ONE_PASS:
+// spec_verify's kernels, the scan with early-exit semantics.  The draws follow as in
+// spec_verify.
 extern "C" sv_status spec_verify_early_exit(const void *target_logits, const void *draft_logits, int32_t dtype,
                                             int64_t vocab, int32_t batch, int64_t n_target_rows,
                                             const int32_t *draft_tokens, const float *uniforms,
@@ -329,8 +389,10 @@ extern "C" sv_status spec_verify_early_exit(const void *target_logits, const voi
                                             int32_t gamma_uniform, int32_t gamma_max, int32_t mode,
                                             const int32_t *cache_len, int32_t *n_accepted,
                                             int32_t *emitted_tokens, int32_t *crop_len, const sv_diag *diag,
-                                            void *workspace, size_t workspace_bytes, void *hip_stream)
+                                            int32_t plan, float accept_hint, void *workspace,
+                                            size_t workspace_bytes, void *hip_stream)
 {
+    if (plan != SV_EE_AUTO && plan != SV_EE_STEPS && plan != SV_EE_ONE_PASS) return SV_EINVAL;
     if (dtype != SV_BF16 && dtype != SV_F32) return SV_EDTYPE;
     if (mode != SV_SAMPLE && mode != SV_GREEDY) return SV_EINVAL;
     if (batch < 0 || vocab <= 0 || vocab > INT32_MAX || n_target_rows < batch) return SV_EINVAL;
@@ -349,6 +411,13 @@ extern "C" sv_status spec_verify_early_exit(const void *target_logits, const voi
     if (n_draft_rows > 0 && (!draft_tokens || (mode == SV_SAMPLE && !draft_logits))) return SV_EINVAL;
     const size_t need = spec_verify_early_exit_workspace_bytes(batch, n_target_rows, vocab, dtype);
     if (workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) return SV_EWORKSPACE;
+    if (plan == SV_EE_AUTO) plan = ee_choose(batch, n_target_rows, vocab, dtype, mode, gamma_max, accept_hint);
+    if (plan == SV_EE_ONE_PASS) {
+        const EeArgs ee{cache_len, crop_len, gamma_max};
+        return verify_impl(target_logits, draft_logits, dtype, vocab, batch, n_target_rows, draft_tokens, uniforms,
+                           temperature, gamma_per_row, gamma_uniform, mode, n_accepted, emitted_tokens, diag,
+                           workspace, workspace_bytes, hip_stream, nullptr, nullptr, &ee);
+    }
 
     const int64_t esz = dtype == SV_BF16 ? 2 : 4;
     const bool aligned = (vocab * esz) % 16 == 0 && aligned16(target_logits) &&

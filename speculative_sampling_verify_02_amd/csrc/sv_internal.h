@@ -678,10 +678,10 @@ inline hipError_t launch_timed(const void *fn, int64_t blocks, int threads, cons
 hipError_t launch_prepare(const Params &P, hipStream_t s);
 hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned, hipEvent_t start = nullptr,
                         hipEvent_t stop = nullptr);
-hipError_t launch_scan(const Params &P, hipStream_t s, int dtype);
+hipError_t launch_scan(const Params &P, hipStream_t s, int dtype, bool ee = false);
 hipError_t launch_verify(const Params &P, hipStream_t s, int dtype, bool aligned);
 int32_t scan_tiles_split(int32_t B, int32_t ntiles);
-hipError_t launch_scan_tiles(const Params &P, hipStream_t s, bool aligned);
+hipError_t launch_scan_tiles(const Params &P, hipStream_t s, bool aligned, bool ee = false);
 hipError_t launch_draw_final(const Params &P, hipStream_t s, int dtype, bool aligned);
 hipError_t launch_scan_draw(const Params &P, hipStream_t s, int dtype, bool aligned);
 hipError_t launch_tree(const TreeParams &T, hipStream_t s);

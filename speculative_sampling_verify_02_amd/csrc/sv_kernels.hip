@@ -141,9 +141,33 @@ __device__ __forceinline__ void scan_merge(const Params &P, const RowGeom &G, in
     }
 }
 
+// Every output of an invalid row (one wave): nothing emitted, no diagnostics, no draw.
+__device__ void ee_invalid_row(const Params &P, int32_t row, const RowGeom &G, int status, int lane)
+{
+    const int32_t g = G.gamma;
+    for (int32_t k = lane; k <= g; k += 64) P.emitted[G.t_off + k] = -1;
+    for (int32_t k = lane; k < g; k += 64) {
+        if (P.p_x) P.p_x[G.d_off + k] = kQNaN;
+        if (P.q_x) P.q_x[G.d_off + k] = kQNaN;
+    }
+    if (lane == 0) {
+        P.n_accepted[row] = -1;
+        if (P.row_status) P.row_status[row] = status;
+        if (P.resid) P.resid[row] = kQNaN;
+        if (P.crop_len) P.crop_len[row] = -1;
+        P.draws[row].kind = DRAW_NONE;
+    }
+}
+
 // The accept scan of one row by the whole workgroup of NW waves.  Returns what the draw
 // needs (on every thread); with `write`, wave 0 also stores the row's outputs.
-template <int DT, int NW = kWaves>
+//
+// EE: what the round with early exit sees, from a pass that read every position.  A
+// row longer than that round's bound (gamma_max) is invalid outright.  A bad token
+// anywhere makes a row invalid from the start; such a row, like one with an unusable
+// temperature, still reports non-finite logits at any position.  Any other row counts
+// status bits, and reports p(x_j), q(x_j), only up to its first rejection.
+template <int DT, int NW = kWaves, bool EE = false>
 __device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &sh)
 {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -184,6 +208,23 @@ __device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &s
     // a row with an unusable temperature decides nothing, but every position is still
     // checked for non-finite logits (from the maxima its records hold)
     const bool bad = rm == ROW_BAD_TEMP;
+    bool pre_invalid = bad;   // (wave 0)
+    if constexpr (EE) {
+        if (g > P.gamma_max) {
+            if (write && wave == 0) ee_invalid_row(P, row, G, ST_BAD_GAMMA, lane);
+            RowDraw D{};
+            D.kind = DRAW_NONE;
+            return D;
+        }
+        if (wave == 0) {
+            int badx = 0;
+            for (int32_t k = lane; k < g; k += 64) {
+                const int32_t xk = k < 64 ? x0 : P.tokens[G.d_off + k];
+                if (xk < 0 || (int64_t)xk >= P.V) badx = 1;
+            }
+            if (wave_or_int(badx)) pre_invalid = true;
+        }
+    }
     {
         for (int64_t base = 0; base <= g; base += 64) {
             const int nt = (int)(g + 1 - base < 64 ? g + 1 - base : 64);
@@ -206,26 +247,27 @@ __device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &s
             if (wave == 0) {
                 x_keep = x;
                 const bool x_ok = x >= 0 && (int64_t)x < P.V;
-                if (has_d && !x_ok) status |= ST_BAD_TOKEN;
+                int cs = 0;   // this lane's status bits at position j
+                if (has_d && !x_ok) cs |= ST_BAD_TOKEN;
                 const float mt = has_t ? sh.m[0][lane] : -INFINITY;
                 const double St = has_t ? sh.S[0][lane] : 0.0;
                 const int32_t it = has_t ? sh.idx[lane] : INT32_MAX;
                 float md = -INFINITY;
                 double Sd = 0.0;
+                double px = kQNaN, qx = kQNaN;
                 bool reject = false;
                 if (bad) {
-                    if (has_t && !(mt > -INFINITY && mt < INFINITY)) status |= ST_NONFINITE;
-                    if (has_d && !(sh.m[1][lane] > -INFINITY && sh.m[1][lane] < INFINITY)) status |= ST_NONFINITE;
+                    if (has_t && !(mt > -INFINITY && mt < INFINITY)) cs |= ST_NONFINITE;
+                    if (has_d && !(sh.m[1][lane] > -INFINITY && sh.m[1][lane] < INFINITY)) cs |= ST_NONFINITE;
                 } else if (greedy) {
-                    if (has_t && !(mt > -INFINITY && mt < INFINITY)) status |= ST_NONFINITE;
+                    if (has_t && !(mt > -INFINITY && mt < INFINITY)) cs |= ST_NONFINITE;
                     if (has_d) reject = x != it;
                 } else {
-                    if (has_t && !(St > 0.0 && St < INFINITY)) status |= ST_NONFINITE;
+                    if (has_t && !(St > 0.0 && St < INFINITY)) cs |= ST_NONFINITE;
                     if (has_d) {
                         md = sh.m[1][lane];
                         Sd = sh.S[1][lane];
-                        if (!(Sd > 0.0 && Sd < INFINITY)) status |= ST_NONFINITE;
-                        double px = kQNaN, qx = kQNaN;
+                        if (!(Sd > 0.0 && Sd < INFINITY)) cs |= ST_NONFINITE;
                         if (x_ok && St > 0.0 && St < INFINITY && Sd > 0.0 && Sd < INFINITY) {
                             px = exp2_f64(((double)zt - (double)mt) * tc.c_eff) / St;
                             qx = exp2_f64(((double)zd - (double)md) * tc.c_eff) / Sd;
@@ -235,16 +277,13 @@ __device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &s
                                 if (ratio > 1.0) ratio = 1.0;
                             } else {
                                 ratio = px > 0.0 ? 1.0 : 0.0;
-                                status |= ST_Q_ZERO;
+                                cs |= ST_Q_ZERO;
                             }
                             reject = !((double)u < ratio);
                         }
-                        if (write) {
-                            if (P.p_x) P.p_x[G.d_off + j] = px;
-                            if (P.q_x) P.q_x[G.d_off + j] = qx;
-                        }
                     }
                 }
+                const bool was_found = found;
                 const unsigned long long rb = __ballot(reject);
                 int src = -1;
                 if (!found && rb != 0ull) {
@@ -253,6 +292,15 @@ __device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &s
                     found = true;
                 } else if (!found && g - base < 64) {
                     src = (int)(g - base);   // no rejection: the bonus position is in this chunk
+                }
+                // the positions that count: all of them, or (early exit) those up to the
+                // first rejection
+                bool counts = true;
+                if constexpr (EE) counts = pre_invalid || (!was_found && (!found || (int64_t)lane <= K - base));
+                if (counts) status |= cs;
+                if (write && has_d && !bad && !greedy) {
+                    if (P.p_x) P.p_x[G.d_off + j] = counts ? px : kQNaN;
+                    if (P.q_x) P.q_x[G.d_off + j] = counts ? qx : kQNaN;
                 }
                 if (src >= 0) {
                     kmt = __shfl(mt, src);
@@ -305,6 +353,8 @@ __device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &s
                 P.n_accepted[row] = invalid ? -1 : K;
                 if (P.row_status) P.row_status[row] = status;
                 if (D.kind == DRAW_NONE && P.resid) P.resid[row] = kQNaN;
+                if (P.crop_len)
+                    P.crop_len[row] = invalid ? -1 : (int32_t)((P.cache_len ? P.cache_len[row] : 0) + K + 1);
                 P.draws[row] = D;
             }
         }
@@ -328,6 +378,7 @@ __device__ void invalidate_call(const Params &P, int32_t row, bool row_writer)
         P.n_accepted[row] = -1;
         if (P.row_status) P.row_status[row] = ST_BAD_GAMMA;
         if (P.resid) P.resid[row] = kQNaN;
+        if (P.crop_len) P.crop_len[row] = -1;
         P.draws[row].kind = DRAW_NONE;
     }
 }
@@ -567,7 +618,7 @@ __global__ __launch_bounds__(kEeWaves * 64) void ee_step_kernel(Params P)
 // ===========================================================================
 // The accept scan, one workgroup per row; it stores the row's outputs and what the
 // draw needs.
-template <int DT>
+template <int DT, bool EE>
 __device__ __forceinline__ void scan_body(const Params &P)
 {
     __shared__ ScanLds sh;
@@ -576,13 +627,14 @@ __device__ __forceinline__ void scan_body(const Params &P)
         invalidate_call(P, row, threadIdx.x == 0);
         return;
     }
-    scan_row<DT>(P, row, true, sh);
+    scan_row<DT, kWaves, EE>(P, row, true, sh);
 }
 
-template <int DT>
+// EE: the decisions of the round with early exit (see scan_row)
+template <int DT, bool EE>
 __global__ __launch_bounds__(kBlock) void scan_kernel(Params P)
 {
-    scan_body<DT>(P);
+    scan_body<DT, EE>(P);
 }
 
 // Sums of the draw weights w (the residual max(0, p - q), or p) and of p over the NTW
@@ -666,7 +718,7 @@ constexpr int kScanTileBlock = 1024;
 constexpr int kScanTileWaves = kScanTileBlock / 64;
 constexpr int kScanTileBatch = 4;   // tiles per wave with all their loads in flight
 
-template <int DT, bool AL>
+template <int DT, bool AL, bool EE>
 __device__ __forceinline__ void scan_tiles_body(const Params &P)
 {
     __shared__ ScanLds sh;
@@ -678,7 +730,7 @@ __device__ __forceinline__ void scan_tiles_body(const Params &P)
         invalidate_call(P, row, part == 0 && threadIdx.x == 0);
         return;
     }
-    const RowDraw D = scan_row<DT, kScanTileWaves>(P, row, part == 0, sh);
+    const RowDraw D = scan_row<DT, kScanTileWaves, EE>(P, row, part == 0, sh);
     // bonus draws use the streaming pass's piece sums, except when p is filtered
     if (!(D.kind == DRAW_RESIDUAL || (P.theta && D.kind == DRAW_BONUS))) return;
     DrawConst<DT> c;
@@ -689,10 +741,10 @@ __device__ __forceinline__ void scan_tiles_body(const Params &P)
         tile_sums<DT, AL, kScanTileBatch>(P, c, D, row, t0, b, lane);
 }
 
-template <int DT, bool AL>
+template <int DT, bool AL, bool EE>
 __global__ __launch_bounds__(kScanTileBlock) void scan_tiles_kernel(Params P)
 {
-    scan_tiles_body<DT, AL>(P);
+    scan_tiles_body<DT, AL, EE>(P);
 }
 
 template <bool AL>
@@ -1010,9 +1062,10 @@ hipError_t launch_prepare(const Params &P, hipStream_t s)
     return launch((const void *)prepare_kernel, 1, 1024, P, s);
 }
 
-hipError_t launch_scan(const Params &P, hipStream_t s, int dtype)
+hipError_t launch_scan(const Params &P, hipStream_t s, int dtype, bool ee)
 {
-    const void *fn = dtype == 0 ? (const void *)scan_kernel<0> : (const void *)scan_kernel<1>;
+    const void *fn = dtype == 0 ? (ee ? (const void *)scan_kernel<0, true> : (const void *)scan_kernel<0, false>)
+                                : (ee ? (const void *)scan_kernel<1, true> : (const void *)scan_kernel<1, false>);
     return launch(fn, (int64_t)P.B, kBlock, P, s);
 }
 
@@ -1036,9 +1089,12 @@ int32_t scan_tiles_split(int32_t B, int32_t ntiles)
 
 // bf16 only: fp32 rows keep the separate scan and verify_kernel_f32, whose residual
 // weights come from the hardware exp2 and cost less than the fp64 terms of tile_sums
-hipError_t launch_scan_tiles(const Params &P, hipStream_t s, bool aligned)
+hipError_t launch_scan_tiles(const Params &P, hipStream_t s, bool aligned, bool ee)
 {
-    const void *fn = aligned ? (const void *)scan_tiles_kernel<0, true> : (const void *)scan_tiles_kernel<0, false>;
+    const void *fn = ee ? (aligned ? (const void *)scan_tiles_kernel<0, true, true>
+                                   : (const void *)scan_tiles_kernel<0, false, true>)
+                        : (aligned ? (const void *)scan_tiles_kernel<0, true, false>
+                                   : (const void *)scan_tiles_kernel<0, false, false>);
     return launch(fn, (int64_t)P.B * P.st_split, kScanTileBlock, P, s);
 }
 

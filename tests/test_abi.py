@@ -149,13 +149,14 @@ def test_early_exit_host_argument_errors(sv):
     def call(**kw):
         a = dict(target=1 << 20, draft=1 << 21, dtype=sv.SV_BF16, vocab=32, batch=2, nT=6, tokens=1 << 22,
                  uniforms=1 << 23, temperature=1 << 24, gamma=None, gamma_u=2, gamma_max=2, mode=sv.SV_SAMPLE,
-                 cache=None, n_acc=1 << 25, emitted=1 << 26, crop=None, ws=1 << 27, ws_bytes=1 << 30)
+                 cache=None, n_acc=1 << 25, emitted=1 << 26, crop=None, plan=sv.SV_EE_AUTO, hint=-1.0,
+                 ws=1 << 27, ws_bytes=1 << 30)
         a.update(kw)
         return sv.lib.spec_verify_early_exit(vp(a["target"]), vp(a["draft"]), a["dtype"], a["vocab"], a["batch"],
                                              a["nT"], vp(a["tokens"]), vp(a["uniforms"]), vp(a["temperature"]),
                                              vp(a["gamma"]), a["gamma_u"], a["gamma_max"], a["mode"],
                                              vp(a["cache"]), vp(a["n_acc"]), vp(a["emitted"]), vp(a["crop"]),
-                                             None, vp(a["ws"]), a["ws_bytes"], None)
+                                             None, a["plan"], a["hint"], vp(a["ws"]), a["ws_bytes"], None)
     assert call(dtype=4) == sv.SV_EDTYPE
     assert call(mode=2) == sv.SV_EINVAL
     assert call(nT=7) == sv.SV_EINVAL
@@ -165,6 +166,7 @@ def test_early_exit_host_argument_errors(sv):
     assert call(draft=None) == sv.SV_EINVAL
     assert call(ws_bytes=64) == sv.SV_EWORKSPACE
     assert call(ws=(1 << 27) + 16) == sv.SV_EWORKSPACE
+    assert call(plan=3) == sv.SV_EINVAL and call(plan=-1) == sv.SV_EINVAL
     assert call(batch=0, nT=0) == sv.SV_OK
     a = sv.early_exit_workspace_bytes(64, 384, 128256, sv.SV_BF16)
     assert a > sv.workspace_bytes(64, 384, 128256, sv.SV_BF16) and a % 256 == 0
@@ -221,3 +223,26 @@ def test_noalloc_host_argument_errors(sv):
     assert call(7, 1000, 2, 6, 2) == sv.SV_EDTYPE
     assert call(sv.SV_BF16, 0, 2, 6, 2) == sv.SV_EINVAL
     assert call(sv.SV_BF16, 1000, 2, 1, 2) == sv.SV_EINVAL
+
+
+def test_early_exit_plan_choice(sv):
+    """The automatic plan of the round with early exit (host only).  Few, short vectors
+    per position (64 rows of 128256 bf16 logits, 5 drafts) cannot pay for the steps'
+    fixed cost, so one pass is taken; 256 rows of 152064 logits with 8 drafts read a
+    third of their logits at the default acceptance rate, so the steps are taken.  A
+    draft that is never kept makes the steps read position 0 only; one that is always
+    kept makes them read everything, so one pass.  (Even then the small shape keeps one
+    pass: its three steps' fixed cost exceeds what they save.)"""
+    plan = sv.early_exit_plan
+    assert plan(64, 64 * 6, 128256, sv.SV_BF16, "sample", 5) == "one_pass"
+    assert plan(64, 64 * 6, 128256, sv.SV_BF16, "greedy", 5) == "one_pass"
+    assert plan(256, 256 * 9, 152064, sv.SV_BF16, "sample", 8) == "steps"
+    assert plan(256, 256 * 9, 152064, sv.SV_BF16, "sample", 8, accept_hint=0.0) == "steps"
+    assert plan(256, 256 * 9, 152064, sv.SV_BF16, "sample", 8, accept_hint=1.0) == "one_pass"
+    assert plan(256, 256 * 9, 152064, sv.SV_BF16, "sample", 8, accept_hint=float("nan")) == "steps"
+    assert plan(64, 64 * 6, 128256, sv.SV_BF16, "sample", 5, accept_hint=0.0) == "one_pass"
+    for bad in (dict(batch=0), dict(gamma_max=-1), dict(dtype=7), dict(mode=5)):
+        a = dict(batch=4, nT=8, vocab=100, dtype=sv.SV_F32, mode=sv.SV_SAMPLE, gamma_max=1)
+        a.update(bad)
+        assert sv.lib.spec_verify_early_exit_plan(a["batch"], a["nT"], a["vocab"], a["dtype"], a["mode"],
+                                                  a["gamma_max"], -1.0) < 0, bad

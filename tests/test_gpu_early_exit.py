@@ -25,7 +25,7 @@ def H():
     return gpu_harness
 
 
-def run_early(H, w, mode=None, dense=False, cache_len=None, tensors=None, gamma_max=None):
+def run_early(H, w, mode=None, dense=False, cache_len=None, tensors=None, gamma_max=None, plan="steps"):
     import speculative_sampling_verify_02_amd as sv
     d = tensors or H.to_device(w)
     gamma = w.dense_gamma if dense else d["gamma"]
@@ -33,7 +33,7 @@ def run_early(H, w, mode=None, dense=False, cache_len=None, tensors=None, gamma_
     gm = int(w.gamma.max()) if gamma_max is None else gamma_max
     n, e, crop, dg = sv.spec_verify_early_exit(d["target"], d["draft"], d["tokens"], d["uniforms"],
                                                d["temperature"], gamma, gamma_max=gm,
-                                               cache_len=cl, mode=mode or w.mode, diag=True)
+                                               cache_len=cl, mode=mode or w.mode, diag=True, plan=plan)
     torch.cuda.synchronize()
     out = dict(n_accepted=n.cpu().numpy(), emitted=e.cpu().numpy(), crop_len=crop.cpu().numpy())
     for k, v in dg.items():
@@ -41,11 +41,20 @@ def run_early(H, w, mode=None, dense=False, cache_len=None, tensors=None, gamma_
     return out
 
 
+def same_outputs(a, b):
+    """Every output of two early-exit calls is identical (NaN diagnostics included)."""
+    for k in a:
+        assert np.array_equal(a[k], b[k], equal_nan=a[k].dtype.kind == "f"), k
+
+
 def parity(H, w, mode=None, dense=False, seed=0):
+    """The steps plan against the oracle's early-exit round; the one-pass plan gives
+    identical outputs."""
     mode = mode or w.mode
     _say(f"[case] early exit {w.name} mode={mode} dense={dense} B={w.batch} V={w.vocab}")
     cache = np.random.default_rng(seed).integers(0, 4096, w.batch).astype(np.int32)
     g = run_early(H, w, mode=mode, dense=dense, cache_len=cache)
+    same_outputs(g, run_early(H, w, mode=mode, dense=dense, cache_len=cache, plan="one_pass"))
     ref = oracle.verify_workload(w, mode=mode, early_exit=True, cache_len=cache)
     # compare() also holds crop_len to cache_len + K + 1 of the (possibly re-run) oracle row
     rep = H.compare(w, g, ref, mode=mode, oracle_kw=dict(early_exit=True, cache_len=cache))
@@ -146,6 +155,7 @@ def test_rows_beyond_gamma_max(H):
     cache = np.random.default_rng(83).integers(0, 4096, w.batch).astype(np.int32)   # parity()'s
     _say("[case] early exit with gamma_max 3 under row gammas up to 5")
     cut = run_early(H, w, cache_len=cache, gamma_max=3)
+    same_outputs(cut, run_early(H, w, cache_len=cache, gamma_max=3, plan="one_pass"))
     t_off, _ = w.offsets()
     assert np.any(w.gamma > 3) and np.any(full["n_accepted"][w.gamma <= 3] >= 1)
     for i in range(w.batch):
@@ -158,3 +168,31 @@ def test_rows_beyond_gamma_max(H):
             for k in ("n_accepted", "crop_len", "row_status"):
                 assert cut[k][i] == full[k][i], (k, i)
             assert np.array_equal(cut["emitted"][a:b], full["emitted"][a:b]), i
+
+
+def test_auto_plan(H):
+    """plan="auto" takes one of the two plans and so gives their outputs.  On 64 rows
+    of 131072 bf16 logits with 12 drafts each (inputs drawn on the GPU, drafts sampled
+    from q), a hint of 0 makes it take the steps and a hint of 1 the one pass."""
+    import speculative_sampling_verify_02_amd as sv
+    B, g, V = 64, 12, 131072
+    gen = torch.Generator(device="cuda").manual_seed(85)
+    tgt = (torch.randn(B, g + 1, V, device="cuda", generator=gen) * 3.0).to(torch.bfloat16)
+    drf = (tgt[:, :g].float() + 0.3 * torch.randn(B, g, V, device="cuda", generator=gen)).to(torch.bfloat16)
+    tok = torch.multinomial(torch.softmax(drf.float().reshape(B * g, V), -1), 1, generator=gen)
+    tok = tok.reshape(B, g).to(torch.int32)
+    uni = torch.rand(B, g + 1, device="cuda", generator=gen)
+    T = torch.ones(B, device="cuda")
+    outs, chosen = [], []
+    for plan, hint in (("steps", None), ("one_pass", None), ("auto", 0.0), ("auto", 1.0)):
+        if plan == "auto":
+            chosen.append(sv.early_exit_plan(B, B * (g + 1), V, sv.SV_BF16, "sample", g, accept_hint=hint))
+        _say(f"[case] early exit plan={plan} hint={hint} B={B} gamma={g} V={V}")
+        n, e, crop, dg = sv.spec_verify_early_exit(tgt, drf, tok, uni, T, diag=True, plan=plan, accept_hint=hint)
+        torch.cuda.synchronize()
+        outs.append(dict(n_accepted=n.cpu().numpy(), emitted=e.cpu().numpy(), crop_len=crop.cpu().numpy(),
+                         **{k: v.cpu().numpy() for k, v in dg.items()}))
+    assert chosen == ["steps", "one_pass"]
+    assert np.all(outs[0]["row_status"] & oracle.INVALID_MASK == 0) and 0 < outs[0]["n_accepted"].mean() < g
+    for o in outs[1:]:
+        same_outputs(outs[0], o)
