@@ -5,9 +5,11 @@ residual sign, the wrong uniform for the draw, ...), applied textually to a
 temporary copy of oracle.c and compiled on the CPU.  The committed oracle is never
 modified.
 """
+import concurrent.futures
 import os
 import shutil
 import subprocess
+import sys
 
 import pytest
 
@@ -61,32 +63,55 @@ MUTANTS = {
 }
 
 
-@pytest.fixture(scope="module")
-def mutant_dir(tmp_path_factory):
-    return tmp_path_factory.mktemp("oracle_mutants")
+# Each mutant is compiled and run against the pins in a worker process of its own (one
+# OpenMP thread each), all of them at once, so the suite's wall time stays a few
+# minutes; a worker prints the name of the first pin that fails, or nothing.
+_WORKER = """
+import sys
+sys.path[:0] = [sys.argv[2], sys.argv[3]]
+import oracle, pins
+with oracle.using(sys.argv[1]):
+    for pin in pins.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            print(pin.__name__)
+            break
+"""
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_mutant_is_caught(name, mutant_dir):
+def _run_mutant(name, root):
     old, new = MUTANTS[name]
     src = open(oracle.SRC_PATH).read()
-    assert src.count(old) == 1, f"mutation site for {name} not unique/found"
-    d = mutant_dir / name
+    if src.count(old) != 1:
+        return f"!site: mutation site for {name} not unique/found"
+    d = root / name
     d.mkdir()
     shutil.copy(os.path.join(os.path.dirname(oracle.SRC_PATH), "oracle.h"), d / "oracle.h")
     (d / "oracle.c").write_text(src.replace(old, new))
     so = str(d / "liboracle.so")
     subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", str(d / "oracle.c"),
                     "-o", so, "-lm"], check=True)
-    failed = []
-    with oracle.using(so):
-        for pin in pins.ALL_PINS:
-            try:
-                pin()
-            except AssertionError:
-                failed.append(pin.__name__)
-            except ValueError:
-                failed.append(pin.__name__)
-            if failed:
-                break
-    assert failed, f"mutant {name} passes every pin"
+    here = os.path.dirname(os.path.abspath(__file__))
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", _WORKER, so, os.path.dirname(here), here], env=env,
+                       capture_output=True, text=True, timeout=1200)
+    if r.returncode != 0:
+        return f"!worker: {r.stderr[-2000:]}"
+    return r.stdout.strip()
+
+
+@pytest.fixture(scope="module")
+def mutant_results(tmp_path_factory):
+    root = tmp_path_factory.mktemp("oracle_mutants")
+    workers = max(1, min(8, os.cpu_count() or 1))
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        futs = {name: ex.submit(_run_mutant, name, root) for name in MUTANTS}
+        return {name: f.result() for name, f in futs.items()}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, mutant_results):
+    caught = mutant_results[name]
+    assert not caught.startswith("!"), caught
+    assert caught, f"mutant {name} passes every pin"
