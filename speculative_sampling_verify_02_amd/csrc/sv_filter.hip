@@ -692,12 +692,12 @@ __global__ __launch_bounds__(kFilterBlock) void filter_stats_kernel(Params P)
                 const uint32_t ncand = gather_candidates<16>(gather_ge, tmx, mx, k, use_k, c64, sh);
                 if (ncand <= (uint32_t)(kWaveCand * 64)) {
                     // the registers are free from here on: the next vector's loads go
-                    // out while one wave finishes this one
-                    if (has_next) {
-                        load_vector<NU>(P, vn, nunits, r);
-                        issued = true;
-                    }
+                    // out while wave 0 finishes this one (its own loads after, so that
+                    // they do not queue ahead of its select)
+                    if (has_next && (tid >> 6) != 0) load_vector<NU>(P, vn, nunits, r);
                     one_wave_thresholds<16>(ncand, mx, k, tp, use_p, c64, sh, theta, S);
+                    if (has_next && (tid >> 6) == 0) load_vector<NU>(P, vn, nunits, r);
+                    issued = true;
                 } else {
                     finish_thresholds<16>(from_hbm, part_sum, ncand, mx, k, tp, use_k, use_p, c64, sh, theta, S);
                 }
