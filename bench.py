@@ -33,7 +33,7 @@ PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, published
 PIECE_BYTES = 8192       # a piece of the streaming pass: two halves of 4 KB
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "stats_kernel_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "speculative_sampling_verify_02_amd", "csrc", f)
-                  for f in ("sv_stats.hip", "sv_internal.h")]
+                  for f in ("sv_stats.hip", "sv_stream.h", "sv_internal.h")]
 # filtered calls on aligned bf16 rows of up to 163840 logits: one fused kernel
 PROFILE_TRAFFIC_FILTER = os.path.join(ROOT, "profiles", "filter_stats_kernel_traffic.json")
 FILTER_SOURCES = [os.path.join(ROOT, "speculative_sampling_verify_02_amd", "csrc", f)
