@@ -133,6 +133,17 @@ def test_c5_full(H):
     parity(H, workloads.c5(), seed=5)
 
 
+def test_c4_full(H):
+    """The shape where the automatic plan takes the steps: four chunks of positions
+    over 256 rows of 152064 logits."""
+    import speculative_sampling_verify_02_amd as sv
+    w = workloads.c4()
+    assert sv.early_exit_plan(w.batch, w.n_target_rows, w.vocab, sv.SV_BF16, "sample", int(w.gamma.max())) == "steps"
+    g, _ = parity(H, w, dense=True, seed=4)
+    assert np.all(g["row_status"] & oracle.INVALID_MASK == 0)
+    assert len(set(g["n_accepted"].tolist())) >= 4   # rows decided in several different chunks
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_invalid_rows_read_to_the_end(H, dtype):
     """A row invalid from the start (bad temperature or token) decides nothing, so the
