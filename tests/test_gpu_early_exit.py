@@ -81,6 +81,16 @@ def test_small_greedy(H, case):
     parity(H, w, mode="greedy", seed=case)
 
 
+def test_long_rows(H):
+    """Rows of up to 250 drafts with drafts close to the target: the chunk of positions
+    [127, 255) is longer than a wave, so its positions are decided 64 at a time, and
+    rows are decided in both of its parts (K = 250 and 200 at the bonus, 136 by a
+    rejection)."""
+    w = workloads.small(seed=89, batch=4, vocab=64, dtype="f32", gamma=[250, 200, 5, 140], noise=0.004)
+    g, ref = parity(H, w, seed=89)
+    assert sorted(g["n_accepted"].tolist()) == [5, 136, 200, 250]
+
+
 def test_dense(H):
     parity(H, workloads.small(seed=71, batch=24, vocab=8192, dtype="bf16", gamma=4, noise=0.4), dense=True)
 
