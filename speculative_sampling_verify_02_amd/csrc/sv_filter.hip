@@ -551,6 +551,8 @@ template <int NU>
 __global__ __launch_bounds__(kFilterBlock) void filter_stats_kernel(Params P)
 {
     __shared__ FilterLds sh;
+    // unit maxima of the thread's units beyond what registers hold (two bf16 to a word)
+    __shared__ uint32_t s_um[NU > 16 ? (NU + 1) / 2 : 1][kFilterBlock];
     const int tid = tid_now(), lane = tid & 63, wave = tid >> 6;
     const int64_t nvec = P.nT + P.nD;
     const int32_t nunits = (int32_t)(P.V / kUnitElems);   // aligned rows: V is a multiple of 8
@@ -598,12 +600,13 @@ __global__ __launch_bounds__(kFilterBlock) void filter_stats_kernel(Params P)
             }
         };
 
-        // the maximum, NaN if any logit is, and (up to 16 units per thread, where the
-        // registers allow) the maximum of every unit (bf16 values, two to a register)
-        // for the top-k gather
+        // the maximum, NaN if any logit is, and the maximum of every unit (bf16
+        // values, two to a word) for the top-k gather: in registers up to 16 units per
+        // thread, in LDS beyond (where the registers do not allow)
         constexpr bool kKeepUnitMax = NU <= 16;
         float tmx = -INFINITY;
         uint32_t um2[(NU + 1) / 2];
+        uint32_t pend = 0u;   // (LDS) an even unit's maximum, stored with the odd one's
 #pragma unroll
         for (int i = 0; i < NU; ++i) {
             uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
@@ -612,12 +615,16 @@ __global__ __launch_bounds__(kFilterBlock) void filter_stats_kernel(Params P)
 #pragma unroll
             for (int t = 0; t < 4; ++t) um = nmax(um, nmax(bf16_lo(w[t]), bf16_hi(w[t])));
             tmx = nmax(tmx, um);
+            const uint32_t ub = __float_as_uint(um) >> 16;
             if constexpr (kKeepUnitMax) {
-                const uint32_t ub = __float_as_uint(um) >> 16;
                 if (i & 1) um2[i / 2] |= ub << 16;
                 else um2[i / 2] = ub;
+            } else {
+                if (i & 1) s_um[i / 2][tid] = pend | (ub << 16);
+                else pend = ub;
             }
         }
+        if constexpr (!kKeepUnitMax && (NU & 1)) s_um[NU / 2][tid] = pend;
         const float mx = block_nmax(tmx, sh);
 
         float theta = -INFINITY;
@@ -667,9 +674,8 @@ __global__ __launch_bounds__(kFilterBlock) void filter_stats_kernel(Params P)
                         if constexpr (kKeepUnitMax) {
                             um = (i & 1) ? bf16_hi(um2[i / 2]) : bf16_lo(um2[i / 2]);
                         } else {
-                            um = -INFINITY;
-#pragma unroll
-                            for (int t = 0; t < 4; ++t) um = fmaxf(um, fmaxf(bf16_lo(w[t]), bf16_hi(w[t])));
+                            const uint32_t uw = s_um[i / 2][tid];
+                            um = (i & 1) ? bf16_hi(uw) : bf16_lo(uw);
                         }
                         if (um >= L) {
 #pragma unroll
