@@ -92,6 +92,7 @@ struct FilterLds {
     double rd[kFilterWaves];
     float rf[kFilterWaves];
     uint32_t ru[kFilterWaves];
+    float rL[kFilterWaves];
     uint32_t rsel;          // radix select: key prefix so far
     double rabove;          // and the metric above it
     float wtheta;           // one-wave select results
@@ -506,6 +507,50 @@ __global__ __launch_bounds__(kFilterBlock) void filter_kernel(Params P)
 // at the position's draft token (-inf when it falls below theta).
 // ---------------------------------------------------------------------------
 
+// What the register-resident kernel needs from its threads' maxima, in one barrier:
+// the block maximum (NaN if any logit is), the number of threads whose maximum is
+// finite (each such maximum is a different logit), and, with m > 0, each wave's m-th
+// largest finite thread maximum, the least of them being L (nw such waves hold at
+// least nw m logits >= L, so L bounds the k-th largest logit from below when
+// nw m >= k).  Also clears the candidate count.
+struct MaxStats {
+    float mx;
+    int nfin;
+    float L;
+    int nw;
+};
+
+__device__ __forceinline__ MaxStats block_max_stats(float tmx, int64_t m, FilterLds &sh)
+{
+    const int tid = tid_now(), lane = tid & 63, wave = tid >> 6;
+    const float wm = wave_umax_f32(tmx);
+    const int wf = __popcll(__ballot(tmx > -INFINITY));
+    float Lw = INFINITY;
+    if (m > 0 && wf >= m) {
+        const uint32_t key[1] = {tmx > -INFINITY ? fkey(tmx) : 0u};
+        Lw = key_val<16>(wave_select_count<16, 1>(key, m));
+    }
+    if (lane == 0) {
+        sh.rf[wave] = wm;
+        sh.ru[wave] = (uint32_t)wf;
+        sh.rL[wave] = Lw;
+    }
+    if (tid == 0) sh.ncand = 0u;
+    __syncthreads();
+    MaxStats r{-INFINITY, 0, INFINITY, 0};
+    for (int w = 0; w < kFilterWaves; ++w) {
+        r.mx = nmax(r.mx, sh.rf[w]);
+        r.nfin += (int)sh.ru[w];
+        const float lw = sh.rL[w];
+        if (lw < INFINITY) {
+            r.L = fminf(r.L, lw);
+            ++r.nw;
+        }
+    }
+    __syncthreads();   // sh.rf, sh.ru are written again by the greedy argmax
+    return r;
+}
+
 // The raw words of a unit as the compiler must assume them changed: a pass over the
 // register-resident vector unpacks its logits where it uses them, instead of keeping
 // the unpacked values of every unit live across passes.
@@ -625,7 +670,11 @@ __global__ __launch_bounds__(kFilterBlock) void filter_stats_kernel(Params P)
             }
         }
         if constexpr (!kKeepUnitMax && (NU & 1)) s_um[NU / 2][tid] = pend;
-        const float mx = block_nmax(tmx, sh);
+        // top-k rows: each wave's m-th largest thread maximum (m = ceil(k / 16)) rides
+        // on the maximum's barrier
+        const int64_t m = (rm == ROW_SAMPLE && k > 0 && k < P.V) ? (k + kFilterWaves - 1) / kFilterWaves : 0;
+        const MaxStats ms = block_max_stats(tmx, m, sh);
+        const float mx = ms.mx;
 
         float theta = -INFINITY;
         Partial rec{-INFINITY, INT32_MAX, 0.0};
@@ -695,7 +744,22 @@ __global__ __launch_bounds__(kFilterBlock) void filter_stats_kernel(Params P)
                     });
                     return s;
                 };
-                const uint32_t ncand = gather_candidates<16>(gather_ge, tmx, mx, k, use_k, c64, sh);
+                // top-k candidates: the logits >= L (fewer waves holding m finite
+                // maxima: L is the k-th largest thread maximum, by a block-wide select)
+                uint32_t ncand = kNoCand;
+                if (use_k && k <= ms.nfin) {
+                    float L = ms.L;
+                    if ((int64_t)ms.nw * m < k) {
+                        auto from_tmax = [&](auto &&f) __attribute__((always_inline)) { f(tmx); };
+                        L = key_val<16>(radix_select<false, 16>(from_tmax, (double)k, mx, c64, sh));
+                    }
+                    gather_ge(L, [&](float z) __attribute__((always_inline)) {
+                        const uint32_t i = atomicAdd(&sh.ncand, 1u);
+                        if (i < (uint32_t)kMaxCand) sh.cand[i] = z;
+                    });
+                    __syncthreads();
+                    ncand = sh.ncand;
+                }
                 if (ncand <= (uint32_t)(kWaveCand * 64)) {
                     // the registers are free from here on: the next vector's loads go
                     // out while wave 0 finishes this one (its own loads after, so that
