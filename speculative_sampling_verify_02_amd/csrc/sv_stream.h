@@ -322,12 +322,12 @@ __device__ __forceinline__ void sample_half(const ItemRaw<0> &r, float c, LaneSu
 }
 
 // 2^(a/L) in fp64 from a table of the L = 64 values 2^(j/L) in LDS (exp2_tab_read,
-// then exp2_tab_finish): a = k + r with
+// then exp2_tab_add): a = k + r with
 // k = rint(a), so |r| <= 1/2 and 2^(a/L) = 2^floor(k/L) 2^((k mod L)/L) 2^(r/L), with
 // 2^(r/L) from its Taylor series in r ln 2 / L to degree 3 (truncation below 4e-11
-// relative).  The power 2^floor(k/L) is added to the exponent field of the product,
-// which lies in [0.99, 2.02): the caller keeps a >= -1000 L (2^-1000, a term that
-// cannot register next to the maximum's 1), so the result stays normal.  Entry j of
+// relative).  The power 2^floor(k/L) scales the table entry (ldexp, exact): the
+// caller keeps a >= -1000 L (2^-1000, a term that cannot register next to the
+// maximum's 1), so the scaled entry stays normal.  Entry j of
 // the lane's copy is at col[j << sh] (sh = 6: one column per lane, which no two lanes
 // of a wave share, so the reads meet no bank conflicts; sh = 0: a single shared copy).
 constexpr int kTabBits = 6;
@@ -361,11 +361,12 @@ __device__ __forceinline__ TabTerm exp2_tab_read(double a, const Exp2Tab &t)
     return u;
 }
 
-__device__ __forceinline__ double exp2_tab_finish(const TabTerm &u)
+// s + 2^(a/L): the table entry scaled by 2^floor(k/L) (ldexp: a term down to 2^-1000
+// stays exact), times the series, added to s in one fma.
+__device__ __forceinline__ double exp2_tab_add(const TabTerm &u, double s)
 {
     const double q = fma(fma(fma(kTabC3, u.r, kTabC2), u.r, kTabC1), u.r, 1.0);
-    const double v = u.T * q;
-    return __hiloint2double(__double2hiint(v) + (u.ki >> kTabBits) * 1048576, __double2loint(v));
+    return fma(ldexp(u.T, u.ki >> kTabBits), q, s);
 }
 
 // Fill a table of 2^(j/L) for exp2_tab_read: kTabLen entries, each repeated `copies`
@@ -418,7 +419,7 @@ __device__ __forceinline__ void sample_half_f32(const ItemRaw<1> &r, double c_ef
 #pragma unroll
         for (int t = 0; t < 4; ++t) u[t] = exp2_tab_read(fmax(fma((double)x[t], cs, -Es), -1000.0 * kTabLen), tab);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) s += exp2_tab_finish(u[t]);
+        for (int t = 0; t < 4; ++t) s = exp2_tab_add(u[t], s);
     }
     a.s64 += s;
 }
