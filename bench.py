@@ -34,10 +34,9 @@ PIECE_BYTES = 8192       # a piece of the streaming pass: two halves of 4 KB
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "stats_kernel_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "speculative_sampling_verify_02_amd", "csrc", f)
                   for f in ("sv_stats.hip", "sv_stream.h", "sv_internal.h")]
-# filtered calls on aligned bf16 rows of up to 163840 logits: one fused kernel
-PROFILE_TRAFFIC_FILTER = os.path.join(ROOT, "profiles", "filter_stats_kernel_traffic.json")
-FILTER_SOURCES = [os.path.join(ROOT, "speculative_sampling_verify_02_amd", "csrc", f)
-                  for f in ("sv_filter.hip", "sv_internal.h")]
+# filtered calls: the streaming kernel's variant that also stores the 64-logit unit
+# maxima of the rows that filter (and skips their sums)
+PROFILE_TRAFFIC_FILTER = os.path.join(ROOT, "profiles", "stats_kernel_filtered_traffic.json")
 
 
 def kernel_source_hash(sources=None) -> str:
@@ -447,7 +446,6 @@ def bench_verify(args, config: str, mode: str, dev, cpu: bool):
         # of p_gamma when p is filtered
         pass2_bytes = int(sum(2 * V * esz if K[i] < gam[i] else (V * esz if filt else min(PIECE_BYTES, V * esz))
                               for i in range(B) if K[i] >= 0))
-    fused = filt and w.dtype == "bf16" and V % 8 == 0 and V <= 163840
     small_bytes = nT * 4 * 2 + nD * 4 + B * 8
     valid = K >= 0
     tests_made = np.where(K < gam, K + 1, gam)[valid].sum()
@@ -465,12 +463,12 @@ def bench_verify(args, config: str, mode: str, dev, cpu: bool):
     achieved = stats_bytes / (stats_avg_ms * 1e-3) / 1e9
 
     traffic = None
-    prof_path, sources = (PROFILE_TRAFFIC_FILTER, FILTER_SOURCES) if fused else (PROFILE_TRAFFIC, KERNEL_SOURCES)
-    if os.path.exists(prof_path) and not early and (fused or not filt):
+    prof_path = PROFILE_TRAFFIC_FILTER if filt else PROFILE_TRAFFIC
+    if os.path.exists(prof_path) and not early:
         try:
             prof = json.load(open(prof_path))
             entry = prof.get("workloads", {}).get(f"{config}_{mode}")
-            if entry and prof.get("kernel_source_hash") == kernel_source_hash(sources):
+            if entry and prof.get("kernel_source_hash") == kernel_source_hash():
                 traffic = entry["hbm_bytes_per_launch"]
         except Exception:
             traffic = None
@@ -494,7 +492,7 @@ def bench_verify(args, config: str, mode: str, dev, cpu: bool):
         "rows_rejected": int((valid & (K < gam)).sum()),
         "rows_bonus": int((valid & (K == gam)).sum()),
         "roofline": {"kernel": "stats_list_kernel + ee_step_kernel steps" if ee_plan == "steps" else (
-                         "filter_stats_kernel" if fused else "stats_kernel"),
+                         "stats_kernel (unit maxima of filtering rows)" if filt else "stats_kernel"),
                      "bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic, "avg_launch_ms": stats_avg_ms,

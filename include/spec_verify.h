@@ -356,8 +356,8 @@ const char *spec_verify_strerror(int32_t status);
 /*
  * Profiling aid: when both are non-NULL hipEvent_t handles, every following
  * spec_verify, spec_sample, spec_verify_filtered or spec_tree_verify_greedy call
- * attaches them to the dispatch of its streaming kernel (the pass over every logit:
- * the streaming statistics kernel, or the fused filter kernel), so that
+ * attaches them to the dispatch of its streaming kernel (the statistics pass over
+ * every logit), so that
  * hipEventElapsedTime(start_event, stop_event) gives that kernel's own duration;
  * spec_verify_early_exit records them on its stream around its position steps.
  * Pass NULL, NULL to stop.  Process-wide setting, not thread-safe.

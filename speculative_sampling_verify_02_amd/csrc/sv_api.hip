@@ -86,8 +86,12 @@ static sv_status verify_impl(const void *target_logits, const void *draft_logits
     const sv::Layout L = sv::make_layout(batch, n_target_rows, vocab, dtype);
     const bool filtered = top_k != nullptr || top_p != nullptr;
     const size_t theta_bytes = filtered ? sv::align256(sizeof(float) * (size_t)(2 * n_target_rows - batch)) : 0;
+    // the maxima of 64-logit units, when the threshold search can take them
+    const bool units = filtered && sv::filter_units_num(vocab) != 0;
+    const size_t umax_bytes = units ? sv::filter_umax_bytes(batch, n_target_rows, vocab) : 0;
     if (filtered && mode != SV_SAMPLE) return SV_EINVAL;
-    if (workspace_bytes < L.total + theta_bytes || ((uintptr_t)workspace & 255u) != 0) return SV_EWORKSPACE;
+    if (workspace_bytes < L.total + theta_bytes + umax_bytes || ((uintptr_t)workspace & 255u) != 0)
+        return SV_EWORKSPACE;
 
     // 16-byte vector loads need every logit row to start 16-byte aligned
     const int64_t esz = dtype == SV_BF16 ? 2 : 4;
@@ -132,6 +136,7 @@ static sv_status verify_impl(const void *target_logits, const void *draft_logits
         P.top_k = top_k;
         P.top_p = top_p;
         P.theta = reinterpret_cast<float *>(ws + L.total);
+        if (units) P.umax = reinterpret_cast<uint16_t *>(ws + L.total + theta_bytes);
     }
     if (ee) {
         P.cache_len = ee->cache_len;
@@ -142,13 +147,12 @@ static sv_status verify_impl(const void *target_logits, const void *draft_logits
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     hipError_t e = hipSuccess;
     if (gamma_per_row) e = sv::launch_prepare(P, s);
-    // filtered calls on aligned bf16 rows: one kernel reads each vector once and does
-    // both the streaming pass and the threshold search
-    const int fused_units = filtered ? sv::filter_stats_units(dtype, aligned, vocab) : 0;
-    if (e == hipSuccess)
-        e = fused_units ? sv::launch_filter_stats(P, s, fused_units, g_prof_start, g_prof_stop)
-                        : sv::launch_stats(P, s, dtype, aligned, g_prof_start, g_prof_stop);
-    if (e == hipSuccess && filtered && !fused_units) e = sv::launch_filter(P, s, dtype, aligned);
+    // filtered calls: the streaming pass also stores the maximum of every 64 consecutive
+    // logits, from which the threshold search bounds the top-k and reads only the units
+    // that can hold it
+    if (e == hipSuccess) e = sv::launch_stats(P, s, dtype, aligned, g_prof_start, g_prof_stop);
+    if (e == hipSuccess && filtered)
+        e = units ? sv::launch_filter_units(P, s, dtype, aligned) : sv::launch_filter(P, s, dtype, aligned);
     // bf16 sampling: the accept scan and the residual's tile sums in one kernel; otherwise
     // the scan, then (sampling) the tile sums
     if (e == hipSuccess) {
@@ -181,14 +185,16 @@ extern "C" size_t spec_verify_filtered_workspace_bytes(int32_t batch, int64_t n_
                                                        int32_t dtype)
 {
     const size_t base = spec_verify_workspace_bytes(batch, n_target_rows, vocab, dtype);
-    return base == 0 ? 0 : base + sv::align256(sizeof(float) * (size_t)(2 * n_target_rows - batch));
+    if (base == 0) return 0;
+    const size_t umax = sv::filter_units_num(vocab) ? sv::filter_umax_bytes(batch, n_target_rows, vocab) : 0;
+    return base + sv::align256(sizeof(float) * (size_t)(2 * n_target_rows - batch)) + umax;
 }
 
-// The round on filtered distributions: the vectors of rows that filter get their
-// thresholds and filtered statistics, in the same pass as every vector's statistics
-// for 16-byte-aligned bf16 rows of up to 163840 logits (filter_stats_kernel), else
-// after the streaming pass (filter_kernel); the scan and the draws then see the
-// filtered p and q.
+// The round on filtered distributions: the streaming pass also stores the maximum of
+// every 64 consecutive logits of the vectors whose rows filter (and skips their sums),
+// and the threshold search then gives each such vector its threshold and its record
+// over the kept logits (filter_units_kernel; filter_kernel beyond 524288 logits); the
+// scan and the draws then see the filtered p and q.
 extern "C" sv_status spec_verify_filtered(const void *target_logits, const void *draft_logits, int32_t dtype,
                                           int64_t vocab, int32_t batch, int64_t n_target_rows,
                                           const int32_t *draft_tokens, const float *uniforms,

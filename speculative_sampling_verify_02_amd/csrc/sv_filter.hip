@@ -22,18 +22,17 @@
 // for fp32.  Since the metric over {key >= t} only changes at keys of logits, the
 // key found is a logit's.
 //
-// With top-k (k at most the number of threads holding a finite logit) a lower bound
-// L of theta_k comes from the threads' own maxima (per wave, with ballots); the
-// logits >= L, at least k of them and usually a few times k, are gathered in LDS and
-// every later select runs there, in one wave when they are at most 256 (the same
-// selects a key bit at a time, with ballots).  Otherwise the selects run over the
-// whole vector.
+// With top-k, a lower bound L of theta_k comes from maxima that are different logits
+// of the vector (k of them reaching L hold k logits >= L); the logits >= L, at least
+// k of them and usually a few times k, are gathered in LDS and every later select
+// runs there, in one wave when they are at most 256 (the same selects a key bit at a
+// time, with ballots).  Otherwise the selects run over the whole vector.
 //
-// filter_stats_kernel (16-byte-aligned bf16 rows of up to 163840 logits) holds the
-// vector in registers and produces the vector's statistics record, theta and the
-// logit at the position's draft token in one pass; filter_kernel runs after the
-// streaming pass otherwise, reading the vector from memory in every pass, and
-// replaces the record of each vector that filters.
+// filter_units_kernel takes those maxima from the streaming pass, which in filtered
+// calls stores the maximum of every 64 consecutive logits, and reads again only the
+// units that can hold the top-k; filter_kernel (vocabularies beyond its budget) takes
+// them from the threads' own maxima, reading the vector from memory in every pass.
+// Both replace the record of each vector that filters.
 #include <float.h>
 #include <limits.h>
 
@@ -47,8 +46,8 @@ constexpr int kBins = 256;       // one 8-bit digit
 constexpr int kMaxCand = 4096;   // logits kept in LDS by the top-k candidate path
 
 // The thread index as a value the compiler must take as new at every call: what the
-// helpers derive from it (lane, wave, LDS offsets) is recomputed where used, not kept
-// in registers across the loop of filter_stats_kernel.
+// helpers derive from it (lane, wave, LDS offsets) is recomputed where used rather
+// than kept in registers.
 __device__ __forceinline__ int tid_now()
 {
     int t = threadIdx.x;
@@ -56,9 +55,8 @@ __device__ __forceinline__ int tid_now()
     return t;
 }
 
-// 2^x in fp64 (exp2_f64) with the series' coefficients read from constant memory:
-// scalar registers, rather than vector registers held across the loop of
-// filter_stats_kernel.
+// 2^x in fp64 (exp2_f64) with the series' coefficients read from constant memory
+// (scalar registers rather than vector registers).
 static __constant__ double kExp2Table[14] = {kExp2Coef[0], kExp2Coef[1], kExp2Coef[2],  kExp2Coef[3],  kExp2Coef[4],
                                              kExp2Coef[5], kExp2Coef[6], kExp2Coef[7],  kExp2Coef[8],  kExp2Coef[9],
                                              kExp2Coef[10], kExp2Coef[11], kExp2Coef[12], kExp2Coef[13]};
@@ -85,6 +83,7 @@ __device__ __forceinline__ float key_val(uint32_t t)
 }
 
 struct FilterLds {
+    static constexpr uint32_t kCap = kMaxCand;
     float cand[kMaxCand];   // logits at or above a lower bound of theta_k
     uint32_t ncand;
     uint32_t cnt[kBins];
@@ -92,14 +91,16 @@ struct FilterLds {
     double rd[kFilterWaves];
     float rf[kFilterWaves];
     uint32_t ru[kFilterWaves];
-    float rL[kFilterWaves];
     uint32_t rsel;          // radix select: key prefix so far
     double rabove;          // and the metric above it
     float wtheta;           // one-wave select results
     double wS;
 };
 
-__device__ __forceinline__ double fblock_sum(double v, FilterLds &sh)
+// Block-wide helpers for a workgroup of NT threads; Lds is the kernel's LDS layout
+// (FilterLds, or the smaller one of filter_units_kernel).
+template <int NT = kFilterBlock, class Lds>
+__device__ __forceinline__ double fblock_sum(double v, Lds &sh)
 {
     const int tid = tid_now(), lane = tid & 63, wave = tid >> 6;
 #pragma unroll
@@ -109,19 +110,20 @@ __device__ __forceinline__ double fblock_sum(double v, FilterLds &sh)
     __syncthreads();
     double t = 0.0;
 #pragma unroll
-    for (int w = 0; w < kFilterWaves; ++w) t += sh.rd[w];
+    for (int w = 0; w < NT / 64; ++w) t += sh.rd[w];
     return t;
 }
 
 // Block-wide maximum of the threads' values, NaN if any is NaN.
-__device__ __forceinline__ float block_nmax(float v, FilterLds &sh)
+template <int NT = kFilterBlock, class Lds>
+__device__ __forceinline__ float block_nmax(float v, Lds &sh)
 {
     const int tid = tid_now(), lane = tid & 63, wave = tid >> 6;
     v = wave_umax_f32(v);
     if (lane == 0) sh.rf[wave] = v;
     __syncthreads();
     float m = -INFINITY;
-    for (int w = 0; w < kFilterWaves; ++w) m = nmax(m, sh.rf[w]);
+    for (int w = 0; w < NT / 64; ++w) m = nmax(m, sh.rf[w]);
     __syncthreads();
     return m;
 }
@@ -130,12 +132,12 @@ __device__ __forceinline__ float block_nmax(float v, FilterLds &sh)
 // 16-byte aligned are read a 512-logit tile per wave with aligned loads shifted into
 // place (load_tile_unit), the logits past V as -inf (arr, arr_bytes: the array the
 // row lies in).
-template <int DT, bool AL, class F>
+template <int DT, bool AL, int NT = kFilterBlock, class F>
 __device__ __forceinline__ void each_logit(const void *base, int64_t V, int64_t nunits, const void *arr,
                                            uint64_t arr_bytes, F &&f)
 {
     if constexpr (AL) {
-        for (int64_t u = tid_now(); u < nunits; u += kFilterBlock) {
+        for (int64_t u = tid_now(); u < nunits; u += NT) {
             const RawUnit<DT> r = load_raw<DT, AL>(base, u, V);
             float z[kUnitElems];
             unpack<DT>(r, z);
@@ -144,7 +146,7 @@ __device__ __forceinline__ void each_logit(const void *base, int64_t V, int64_t 
         }
     } else {
         const int tid = tid_now(), lane = tid & 63, wave = tid >> 6;
-        for (int64_t tile = wave; tile * kTileUnits < nunits; tile += kFilterWaves) {
+        for (int64_t tile = wave; tile * kTileUnits < nunits; tile += NT / 64) {
             const RawUnit<DT> r = load_tile_unit<DT>(base, tile, V, arr, arr_bytes, lane);
             float z[kUnitElems];
             unpack<DT>(r, z);
@@ -157,8 +159,8 @@ __device__ __forceinline__ void each_logit(const void *base, int64_t V, int64_t 
 // The largest key t (bits >= LOW) whose metric over {key >= t} reaches target > 0:
 // the count of the logits `each` passes (MASS false), or the sum of their weights
 // 2^((z - m) c64) (MASS true).  The total metric must reach the target.
-template <bool MASS, int LOW, class Src>
-__device__ __forceinline__ uint32_t radix_select(Src &&each, double target, float m, double c64, FilterLds &sh)
+template <bool MASS, int LOW, class Src, class Lds>
+__device__ __forceinline__ uint32_t radix_select(Src &&each, double target, float m, double c64, Lds &sh)
 {
     const int tid = tid_now(), lane = tid & 63;
     uint32_t prefix = 0u;
@@ -259,9 +261,9 @@ constexpr int kWaveCand = 4;   // candidates per lane of the one-wave path (256 
 
 // theta and the kept sum from at most 256 candidates in LDS, in one wave (the other
 // waves wait at the barrier).
-template <int LOW>
+template <int LOW, class Lds>
 __device__ __forceinline__ void one_wave_thresholds(uint32_t ncand, float mx, int64_t k, float tp, bool use_p,
-                                                    double c64, FilterLds &sh, float &theta_out, double &S_out)
+                                                    double c64, Lds &sh, float &theta_out, double &S_out)
 {
     const int tid = tid_now(), lane = tid & 63, wave = tid >> 6;
     if (wave == 0) {
@@ -358,10 +360,10 @@ __device__ __forceinline__ uint32_t gather_candidates(GatherGe &&gather_ge, floa
 // logits of 2^((z - mx) c64), from the candidates when they fit in LDS, else from the
 // whole vector (`each(f)` passes every logit to f, spread over the threads;
 // `part_sum(lower)` is this thread's share of the sum over the logits >= lower).
-template <int LOW, class Each, class PartSum>
+template <int LOW, int NT = kFilterBlock, class Each, class PartSum, class Lds>
 __device__ __forceinline__ void finish_thresholds(Each &&each, PartSum &&part_sum, uint32_t ncand, float mx,
                                                   int64_t k, float tp, bool use_k, bool use_p, double c64,
-                                                  FilterLds &sh, float &theta_out, double &S_out)
+                                                  Lds &sh, float &theta_out, double &S_out)
 {
     const int tid = tid_now(), lane = tid & 63, wave = tid >> 6;
     if (ncand != kNoCand) {
@@ -369,9 +371,9 @@ __device__ __forceinline__ void finish_thresholds(Each &&each, PartSum &&part_su
             one_wave_thresholds<LOW>(ncand, mx, k, tp, use_p, c64, sh, theta_out, S_out);
             return;
         }
-        if (ncand <= (uint32_t)kMaxCand) {
+        if (ncand <= Lds::kCap) {
             auto from_cand = [&](auto &&f) __attribute__((always_inline)) {
-                for (uint32_t i = tid; i < ncand; i += kFilterBlock) f(sh.cand[i]);
+                for (uint32_t i = tid; i < ncand; i += NT) f(sh.cand[i]);
             };
             float theta = key_val<LOW>(radix_select<false, LOW>(from_cand, (double)k, mx, c64, sh));
             auto cand_sum = [&](float lower) {
@@ -379,7 +381,7 @@ __device__ __forceinline__ void finish_thresholds(Each &&each, PartSum &&part_su
                 from_cand([&](float z) {
                     if (z >= lower) s += fexp2(((double)z - (double)mx) * c64);
                 });
-                return fblock_sum(s, sh);
+                return fblock_sum<NT>(s, sh);
             };
             double S = cand_sum(theta);
             if (use_p) {
@@ -405,10 +407,10 @@ __device__ __forceinline__ void finish_thresholds(Each &&each, PartSum &&part_su
     each([&](float z) {
         if (z > -INFINITY) ++nfin;
     });
-    nfin = (uint32_t)fblock_sum((double)nfin, sh);
+    nfin = (uint32_t)fblock_sum<NT>((double)nfin, sh);
     float theta = -INFINITY;
     if (use_k && (uint64_t)k <= nfin) theta = key_val<LOW>(radix_select<false, LOW>(each, (double)k, mx, c64, sh));
-    double S = fblock_sum(part_sum(theta), sh);
+    double S = fblock_sum<NT>(part_sum(theta), sh);
     if (use_p) {
         const float lk = theta;
         auto kept = [&](auto &&f) {
@@ -419,7 +421,7 @@ __device__ __forceinline__ void finish_thresholds(Each &&each, PartSum &&part_su
         const float tp_val = key_val<LOW>(radix_select<true, LOW>(kept, (double)tp * S, mx, c64, sh));
         if (tp_val > theta) {
             theta = tp_val;
-            S = fblock_sum(part_sum(theta), sh);
+            S = fblock_sum<NT>(part_sum(theta), sh);
         }
     }
     theta_out = theta;
@@ -427,16 +429,16 @@ __device__ __forceinline__ void finish_thresholds(Each &&each, PartSum &&part_su
 }
 
 // Record 0 of vector v is rec0, its other records are empty.
+template <int NT = kFilterBlock>
 __device__ __forceinline__ void write_records(const Params &P, int64_t v, const Partial &rec0)
 {
     const int64_t ipv = P.geo.ipv;
-    for (int64_t j = tid_now(); j < ipv; j += kFilterBlock)
+    for (int64_t j = tid_now(); j < ipv; j += NT)
         P.parts[v * ipv + j] = j == 0 ? rec0 : Partial{-INFINITY, INT32_MAX, 0.0};
 }
 
-// Thresholds after the streaming pass (fp32 logits, rows that are not 16-byte
-// aligned, vocabularies beyond what filter_stats_kernel holds in registers): the
-// vector is read from memory by every pass.
+// Thresholds after the streaming pass for vocabularies beyond filter_units_kernel's
+// budget: the vector is read from memory by every pass.
 template <int DT, bool AL>
 __global__ __launch_bounds__(kFilterBlock) void filter_kernel(Params P)
 {
@@ -499,317 +501,230 @@ __global__ __launch_bounds__(kFilterBlock) void filter_kernel(Params P)
 }
 
 // ---------------------------------------------------------------------------
-// The whole pass of a filtered call in one kernel, for 16-byte-aligned bf16 rows of
-// at most NU * 8192 logits: the workgroup loads its vector once into registers (NU
-// 16-byte units per thread) and computes from there what the streaming pass and the
-// threshold search compute together otherwise: the vector's record (maximum and sum
-// over the kept logits, or the first argmax of a greedy row), theta, and the logit
-// at the position's draft token (-inf when it falls below theta).
+// Thresholds after a streaming pass that stored the maximum of every unit of 64
+// consecutive logits (umax, as 16-bit keys; each maximum a different logit).  With
+// top-k, any value that k unit maxima reach is a lower bound L of theta_k, so only
+// the units whose maximum reaches L are read again (one 128-byte line per bf16
+// unit), and the selects run on their logits >= L in LDS.  L as in the other
+// kernels, from maxima over the threads: each wave's m-th largest lane maximum
+// (m = ceil(k / waves); a lane maximum covers the lane's units), and L their least
+// (a block-wide select over all unit maxima when fewer waves hold m finite lanes).
+// Rows without top-k, or whose candidates do not fit, take the selects over the
+// whole vector.  One 4-wave workgroup per vector: the work is a chain of small
+// dependent reads, so many vectors are in flight per CU.
 // ---------------------------------------------------------------------------
+constexpr int kUnitsBlock = 256;
+constexpr int kUnitsWaves = kUnitsBlock / 64;
+constexpr int kMaxUnitList = 1024;   // units read again
 
-// What the register-resident kernel needs from its threads' maxima, in one barrier:
-// the block maximum (NaN if any logit is), the number of threads whose maximum is
-// finite (each such maximum is a different logit), and, with m > 0, each wave's m-th
-// largest finite thread maximum, the least of them being L (nw such waves hold at
-// least nw m logits >= L, so L bounds the k-th largest logit from below when
-// nw m >= k).  Also clears the candidate count.
-struct MaxStats {
-    float mx;
-    int nfin;
-    float L;
-    int nw;
+struct UnitsLds {
+    static constexpr uint32_t kCap = 2048;
+    float cand[kCap];
+    uint32_t ncand;
+    uint32_t cnt[kBins];
+    double mass[kBins];
+    double rd[kUnitsWaves];
+    float rf[kUnitsWaves];
+    uint32_t ru[kUnitsWaves];
+    uint32_t rL[kUnitsWaves];
+    uint32_t rsel;
+    double rabove;
+    float wtheta;
+    double wS;
+    uint32_t nlist;
+    uint16_t list[kMaxUnitList];
 };
 
-__device__ __forceinline__ MaxStats block_max_stats(float tmx, int64_t m, FilterLds &sh)
+// NUM: units per thread (the vector's ipv * 64 units, at most NUM * kUnitsBlock).
+template <int DT, bool AL, int NUM>
+__global__ __launch_bounds__(kUnitsBlock) void filter_units_kernel(Params P)
 {
-    const int tid = tid_now(), lane = tid & 63, wave = tid >> 6;
-    const float wm = wave_umax_f32(tmx);
-    const int wf = __popcll(__ballot(tmx > -INFINITY));
-    float Lw = INFINITY;
-    if (m > 0 && wf >= m) {
-        const uint32_t key[1] = {tmx > -INFINITY ? fkey(tmx) : 0u};
-        Lw = key_val<16>(wave_select_count<16, 1>(key, m));
-    }
-    if (lane == 0) {
-        sh.rf[wave] = wm;
-        sh.ru[wave] = (uint32_t)wf;
-        sh.rL[wave] = Lw;
-    }
-    if (tid == 0) sh.ncand = 0u;
-    __syncthreads();
-    MaxStats r{-INFINITY, 0, INFINITY, 0};
-    for (int w = 0; w < kFilterWaves; ++w) {
-        r.mx = nmax(r.mx, sh.rf[w]);
-        r.nfin += (int)sh.ru[w];
-        const float lw = sh.rL[w];
-        if (lw < INFINITY) {
-            r.L = fminf(r.L, lw);
-            ++r.nw;
-        }
-    }
-    __syncthreads();   // sh.rf, sh.ru are written again by the greedy argmax
-    return r;
-}
-
-// The raw words of a unit as the compiler must assume them changed: a pass over the
-// register-resident vector unpacks its logits where it uses them, instead of keeping
-// the unpacked values of every unit live across passes.
-__device__ __forceinline__ void opaque(uint32_t (&w)[4])
-{
-    asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
-}
-
-// NU units of vector v into registers, every load unconditional (a unit past the end
-// reads the last unit); land_vector then waits for them and makes those units -inf.
-template <int NU>
-__device__ __forceinline__ void load_vector(const Params &P, int64_t v, int32_t nunits, uint4 (&r)[NU])
-{
-    const bool target = v < P.nT;
-    const uint4 *base =
-        static_cast<const uint4 *>(vec_ptr(target ? P.target : P.draft, 0, target ? v : v - P.nT, P.V));
-    // the lane's unit offsets are recomputed here on every call (32-bit, from a thread
-    // index the compiler must take as new), not kept live across the calls
-    const uint32_t tid = (uint32_t)tid_now();
+    constexpr int NT = kUnitsBlock;
+    constexpr int E = DT == 0 ? 8 : 4;                  // logits per 16 bytes
+    constexpr int kChunks = kPieceUnits / E;            // 16-byte chunks of a unit
+    constexpr int LOW = DT == 0 ? 16 : 0;
+    constexpr uint32_t kBad = 0xffff0000u;              // a NaN or +inf unit maximum
+    __shared__ UnitsLds sh;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t v = blockIdx.x;
+    // the thread's units tid, tid + NT, ...: keys in the upper half-word, 0 for -inf
+    // (loaded first, so that the row's context loads overlap them)
+    const int32_t nu = (int32_t)(P.geo.ipv * kPieceUnits);
+    const uint16_t *um = P.umax + v * (int64_t)nu;
+    uint32_t key[NUM];
 #pragma unroll
-    for (int i = 0; i < NU; ++i) {
-        const uint32_t u = tid + (uint32_t)(i * kFilterBlock);
-        r[i] = load_nt16(base + (u < (uint32_t)nunits ? u : (uint32_t)nunits - 1u));
+    for (int i = 0; i < NUM; ++i) {
+        const int32_t u = tid + i * NT;
+        key[i] = u < nu ? (uint32_t)um[u] << 16 : 0u;
     }
-}
-
-template <int NU>
-__device__ __forceinline__ void land_vector(int32_t nunits, uint4 (&r)[NU], int32_t tid)
-{
-#pragma unroll
-    for (int i = 0; i < NU; ++i) {
-        uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
-        opaque(w);
-        const bool in = tid + i * kFilterBlock < nunits;
-        r[i] = in ? make_uint4(w[0], w[1], w[2], w[3]) : make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
-    }
-}
-
-// One workgroup per CU takes vectors blockIdx.x, + gridDim.x, ...; the loads of its
-// next vector are issued as soon as the current one's registers are no longer read
-// (after the top-k gather, usually), so they overlap the rest of its work.
-template <int NU>
-__global__ __launch_bounds__(kFilterBlock) void filter_stats_kernel(Params P)
-{
-    __shared__ FilterLds sh;
-    // unit maxima of the thread's units beyond what registers hold (two bf16 to a word)
-    __shared__ uint32_t s_um[NU > 16 ? (NU + 1) / 2 : 1][kFilterBlock];
-    const int tid = tid_now(), lane = tid & 63, wave = tid >> 6;
-    const int64_t nvec = P.nT + P.nD;
-    const int32_t nunits = (int32_t)(P.V / kUnitElems);   // aligned rows: V is a multiple of 8
-    int64_t v = blockIdx.x;
-    if (v >= nvec) return;
-    uint4 r[NU];
-    load_vector<NU>(P, v, nunits, r);
     if (P.gamma != nullptr && P.hdr->status != 0) return;
-    for (;;) {
-        const int64_t vn = v + gridDim.x;
-        const bool has_next = vn < nvec;
-        bool issued = false;   // the next vector's loads are in flight
-        // the thread index as a new value in every iteration: what derives from it is
-        // recomputed where used instead of held in registers across the loop
-        const int32_t tid = tid_now();
-        land_vector<NU>(nunits, r, tid);
-        const bool target = v < P.nT;
-        const uint16_t *base =
-            static_cast<const uint16_t *>(vec_ptr(target ? P.target : P.draft, 0, target ? v : v - P.nT, P.V));
-        // the vector's context, the same on every thread: kept in scalar registers
-        VecCtx vc = vec_ctx(P, v);
-        vc.row = __builtin_amdgcn_readfirstlane(vc.row);
-        vc.slot = __builtin_amdgcn_readfirstlane(vc.slot);
-        vc.x = __builtin_amdgcn_readfirstlane(vc.x);
-        vc.T = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(vc.T)));
-        const bool has_x = vc.slot >= 0 && vc.x >= 0 && (int64_t)vc.x < P.V;
-        const float zx = (tid == 0 && has_x) ? load_logit<0>(base, vc.x) : -INFINITY;
-        const int32_t rm = row_mode(P.mode, vc.T);
-        const int64_t k = __builtin_amdgcn_readfirstlane(P.top_k ? P.top_k[vc.row] : 0);
-        const float tp =
-            __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(P.top_p ? P.top_p[vc.row] : 1.0f)));
-
-        // f(z, i) for every logit z of this thread, i its index in the vector
-        auto each_idx = [&](auto &&f) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i = 0; i < NU; ++i) {
-                uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
-                opaque(w);
-                const int32_t e0 = (tid + i * kFilterBlock) * kUnitElems;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    f(bf16_lo(w[t]), e0 + 2 * t);
-                    f(bf16_hi(w[t]), e0 + 2 * t + 1);
-                }
-            }
-        };
-
-        // the maximum, NaN if any logit is, and the maximum of every unit (bf16
-        // values, two to a word) for the top-k gather: in registers up to 16 units per
-        // thread, in LDS beyond (where the registers do not allow)
-        constexpr bool kKeepUnitMax = NU <= 16;
-        float tmx = -INFINITY;
-        uint32_t um2[(NU + 1) / 2];
-        uint32_t pend = 0u;   // (LDS) an even unit's maximum, stored with the odd one's
-#pragma unroll
-        for (int i = 0; i < NU; ++i) {
-            uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
-            opaque(w);
-            float um = -INFINITY;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) um = nmax(um, nmax(bf16_lo(w[t]), bf16_hi(w[t])));
-            tmx = nmax(tmx, um);
-            const uint32_t ub = __float_as_uint(um) >> 16;
-            if constexpr (kKeepUnitMax) {
-                if (i & 1) um2[i / 2] |= ub << 16;
-                else um2[i / 2] = ub;
-            } else {
-                if (i & 1) s_um[i / 2][tid] = pend | (ub << 16);
-                else pend = ub;
-            }
-        }
-        if constexpr (!kKeepUnitMax && (NU & 1)) s_um[NU / 2][tid] = pend;
-        // top-k rows: each wave's m-th largest thread maximum (m = ceil(k / 16)) rides
-        // on the maximum's barrier
-        const int64_t m = (rm == ROW_SAMPLE && k > 0 && k < P.V) ? (k + kFilterWaves - 1) / kFilterWaves : 0;
-        const MaxStats ms = block_max_stats(tmx, m, sh);
-        const float mx = ms.mx;
-
-        float theta = -INFINITY;
-        Partial rec{-INFINITY, INT32_MAX, 0.0};
-        if (rm != ROW_SAMPLE) {
-            // greedy rows: the target vectors' first argmax (NaN: no index); bad
-            // temperatures: the maximum alone (which tells the row non-finite)
-            if (rm == ROW_BAD_TEMP) rec.m = mx;
-            if (rm == ROW_GREEDY && target) {
-                rec.m = mx;
-                if (mx > -INFINITY) {   // not NaN, not -inf
-                    int32_t first = INT32_MAX;
-                    if (tmx == mx) {
-                        each_idx([&](float z, int32_t i) __attribute__((always_inline)) {
-                            if (z == mx && i < first) first = i;
-                        });
-                    }
-                    first = wave_umin_i32(first);
-                    if (lane == 0) sh.ru[wave] = (uint32_t)first;
-                    __syncthreads();
-                    for (int w = 0; w < kFilterWaves; ++w) first = min(first, (int32_t)sh.ru[w]);
-                    rec.idx = first;
-                }
-            }
-        } else if (!(mx < INFINITY)) {
-            // a NaN or +inf logit: the row is reported non-finite
-            rec = Partial{mx, __float_as_int(__builtin_nanf("")), (double)__builtin_nanf("")};
-        } else if (mx == -INFINITY) {
-            rec = Partial{-INFINITY, 0, 0.0};
-        } else {
-            const double c64 = kLog2e / (double)vc.T;
-            const float c32 = (float)c64;
-            const bool use_k = k > 0 && k < P.V, use_p = tp > 0.0f && tp < 1.0f;
-            double S;
-            if (use_k || use_p) {
-                // the candidates come from the registers, a unit at a time (units whose
-                // maximum is below L are skipped); selects that do not run on
-                // candidates in LDS read the vector from memory again, in fp64 like
-                // filter_kernel
-                auto gather_ge = [&](float L, auto &&f) __attribute__((always_inline)) {
-                    if (!(tmx >= L)) return;   // no logit of this thread reaches L
-#pragma unroll
-                    for (int i = 0; i < NU; ++i) {
-                        uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
-                        opaque(w);
-                        float um;
-                        if constexpr (kKeepUnitMax) {
-                            um = (i & 1) ? bf16_hi(um2[i / 2]) : bf16_lo(um2[i / 2]);
-                        } else {
-                            const uint32_t uw = s_um[i / 2][tid];
-                            um = (i & 1) ? bf16_hi(uw) : bf16_lo(uw);
-                        }
-                        if (um >= L) {
-#pragma unroll
-                            for (int t = 0; t < 4; ++t) {
-                                const float zl = bf16_lo(w[t]), zh = bf16_hi(w[t]);
-                                if (zl >= L) f(zl);
-                                if (zh >= L) f(zh);
-                            }
-                        }
-                    }
-                };
-                auto from_hbm = [&](auto &&f) { each_logit<0, true>(base, P.V, nunits, nullptr, 0, f); };
-                auto part_sum = [&](float lower) {
-                    double s = 0.0;
-                    from_hbm([&](float z) {
-                        if (z >= lower) s += fexp2(((double)z - (double)mx) * c64);
-                    });
-                    return s;
-                };
-                // top-k candidates: the logits >= L (fewer waves holding m finite
-                // maxima: L is the k-th largest thread maximum, by a block-wide select)
-                uint32_t ncand = kNoCand;
-                if (use_k && k <= ms.nfin) {
-                    float L = ms.L;
-                    if ((int64_t)ms.nw * m < k) {
-                        auto from_tmax = [&](auto &&f) __attribute__((always_inline)) { f(tmx); };
-                        L = key_val<16>(radix_select<false, 16>(from_tmax, (double)k, mx, c64, sh));
-                    }
-                    gather_ge(L, [&](float z) __attribute__((always_inline)) {
-                        const uint32_t i = atomicAdd(&sh.ncand, 1u);
-                        if (i < (uint32_t)kMaxCand) sh.cand[i] = z;
-                    });
-                    __syncthreads();
-                    ncand = sh.ncand;
-                }
-                if (ncand <= (uint32_t)(kWaveCand * 64)) {
-                    // the registers are free from here on: the next vector's loads go
-                    // out while wave 0 finishes this one (its own loads after, so that
-                    // they do not queue ahead of its select)
-                    if (has_next && (tid >> 6) != 0) load_vector<NU>(P, vn, nunits, r);
-                    one_wave_thresholds<16>(ncand, mx, k, tp, use_p, c64, sh, theta, S);
-                    if (has_next && (tid >> 6) == 0) load_vector<NU>(P, vn, nunits, r);
-                    issued = true;
-                } else {
-                    finish_thresholds<16>(from_hbm, part_sum, ncand, mx, k, tp, use_k, use_p, c64, sh, theta, S);
-                }
-            } else {
-                // this thread's sum over all logits: fp32 per unit, fp64 across units
-                double s = 0.0;
-#pragma unroll
-                for (int i = 0; i < NU; ++i) {
-                    uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
-                    opaque(w);
-                    float a = 0.0f;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        a += hw_exp2((bf16_lo(w[t]) - mx) * c32);
-                        a += hw_exp2((bf16_hi(w[t]) - mx) * c32);
-                    }
-                    s += (double)a;
-                }
-                S = fblock_sum(s, sh);
-            }
-            rec = Partial{mx, __float_as_int(__builtin_nanf("")), S};
-        }
-        write_records(P, v, rec);
-        if (tid == 0) {
-            P.theta[v] = theta;
-            if (rm == ROW_SAMPLE && has_x) P.zx[(target ? 0 : P.nD) + vc.slot] = zx < theta ? -INFINITY : zx;
-        }
-        if (!has_next) break;
-        if (!issued) load_vector<NU>(P, vn, nunits, r);
-        v = vn;
+    const VecCtx vc = vec_ctx(P, v);
+    const int32_t rm = row_mode(P.mode, vc.T);
+    const int64_t k = P.top_k ? P.top_k[vc.row] : 0;
+    const float tp = P.top_p ? P.top_p[vc.row] : 1.0f;
+    const bool use_k = k > 0 && k < P.V, use_p = tp > 0.0f && tp < 1.0f;
+    if (rm != ROW_SAMPLE || (!use_k && !use_p)) {
+        if (tid == 0) P.theta[v] = -INFINITY;
+        return;
     }
-}
+    const bool target = v < P.nT;
+    const void *arr = target ? P.target : P.draft;
+    const void *base = vec_ptr(arr, DT, target ? v : v - P.nT, P.V);
+    const int64_t nunits = (P.V + kUnitElems - 1) / kUnitElems;
+    const uint64_t arr_bytes = (uint64_t)(target ? P.nT : P.nD) * (uint64_t)P.V * (DT == 0 ? 2u : 4u);
 
-// Workgroups of filter_stats_kernel<nu> that fit on the current device at once.
-static int32_t filter_grid_cap(const void *fn)
-{
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kFilterBlock, 0) != hipSuccess || per_cu <= 0)
-        per_cu = 1;
-    return cus * per_cu;
+    // per wave, in one barrier: a non-finite maximum, the finite units, and with top-k
+    // the m-th largest lane maximum (lanes hold different units, so m lanes whose
+    // maximum reaches it hold m logits >= it)
+    const int64_t m = use_k ? (k + kUnitsWaves - 1) / kUnitsWaves : 0;
+    {
+        bool bad = false;
+        int wf = 0;
+        uint32_t kmax = 0u;
+#pragma unroll
+        for (int i = 0; i < NUM; ++i) {
+            bad |= key[i] == kBad;
+            wf += __popcll(__ballot(key[i] != 0u));
+            kmax = key[i] > kmax ? key[i] : kmax;
+        }
+        uint32_t Lw = 0xffffffffu;   // none
+        if (m > 0 && m <= 64 && __popcll(__ballot(kmax != 0u)) >= m) {
+            const uint32_t lk[1] = {kmax};
+            Lw = wave_select_count<16, 1>(lk, m);
+        }
+        const bool wbad = __any(bad);
+        if (lane == 0) {
+            sh.ru[wave] = (uint32_t)wf | (wbad ? 0x80000000u : 0u);
+            sh.rL[wave] = Lw;
+        }
+        if (tid == 0) {
+            sh.nlist = 0u;
+            sh.ncand = 0u;
+        }
+    }
+    __syncthreads();
+    int64_t nfin = 0;
+    bool bad = false;
+    uint32_t L32 = 0xffffffffu;
+    int nw = 0;
+#pragma unroll
+    for (int w = 0; w < kUnitsWaves; ++w) {
+        const uint32_t r = sh.ru[w];
+        bad |= (r & 0x80000000u) != 0u;
+        nfin += (int64_t)(r & 0x7fffffffu);
+        const uint32_t lw = sh.rL[w];
+        if (lw != 0xffffffffu) {
+            L32 = lw < L32 ? lw : L32;
+            ++nw;
+        }
+    }
+    // a NaN or +inf logit (the row is reported non-finite) or no finite logit: the
+    // vector stays unfiltered
+    if (bad || nfin == 0) {
+        if (tid == 0) P.theta[v] = -INFINITY;
+        return;
+    }
+    const double c64 = kLog2e / (double)vc.T;
+    uint32_t ncand = kNoCand;
+    float mx = -INFINITY;
+    if (use_k && k <= nfin) {
+        if ((int64_t)nw * m < k) {
+            auto from_keys = [&](auto &&f) __attribute__((always_inline)) {
+#pragma unroll
+                for (int i = 0; i < NUM; ++i)
+                    if (key[i] != 0u) f(key_val<0>(key[i]));
+            };
+            L32 = radix_select<false, 16>(from_keys, (double)k, 0.0f, c64, sh);
+        }
+        // the units whose maximum reaches L
+#pragma unroll
+        for (int i = 0; i < NUM; ++i) {
+            if (key[i] >= L32) {
+                const uint32_t at = atomicAdd(&sh.nlist, 1u);
+                if (at < (uint32_t)kMaxUnitList) sh.list[at] = (uint16_t)(tid + i * NT);
+            }
+        }
+        __syncthreads();
+        const uint32_t nlist = sh.nlist;
+        if (nlist <= (uint32_t)kMaxUnitList) {
+            // their logits >= L (L the least float of its key, so a lower bound for
+            // fp32 maxima rounded down to 16 bits, exact for bf16), four 16-byte chunks
+            // per thread in flight (consecutive threads read consecutive chunks)
+            const float L = key_val<0>(L32);
+            const int32_t nch = (int32_t)nlist * kChunks;
+            float tmx = -INFINITY;
+            for (int32_t c0 = 0; c0 < nch; c0 += 4 * NT) {
+                uint32_t w[4][4];
+                int64_t e0[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int32_t c = c0 + q * NT + tid;
+                    e0[q] = P.V;   // nothing to read
+                    if (c < nch) e0[q] = (int64_t)sh.list[c / kChunks] * kPieceUnits + (c % kChunks) * E;
+                    if (e0[q] < P.V) {
+                        if constexpr (AL) {
+                            const uint4 x = *reinterpret_cast<const uint4 *>(
+                                static_cast<const char *>(base) + e0[q] * (DT == 0 ? 2 : 4));
+                            w[q][0] = x.x; w[q][1] = x.y; w[q][2] = x.z; w[q][3] = x.w;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (!(e0[q] < P.V)) continue;
+#pragma unroll
+                    for (int t = 0; t < E; ++t) {
+                        float z;
+                        if constexpr (AL) {
+                            z = DT == 0 ? ((t & 1) ? bf16_hi(w[q][t / 2]) : bf16_lo(w[q][t / 2]))
+                                        : __uint_as_float(w[q][t]);
+                        } else {
+                            if (e0[q] + t >= P.V) break;
+                            z = load_logit<DT>(base, e0[q] + t);
+                        }
+                        if (z >= L) {
+                            const uint32_t at = atomicAdd(&sh.ncand, 1u);
+                            if (at < UnitsLds::kCap) sh.cand[at] = z;
+                            tmx = nmax(tmx, z);
+                        }
+                    }
+                }
+            }
+            // the maximum is among them
+            tmx = wave_umax_f32(tmx);
+            if (lane == 0) sh.rf[wave] = tmx;
+            __syncthreads();
+            ncand = sh.ncand;
+#pragma unroll
+            for (int w = 0; w < kUnitsWaves; ++w) mx = nmax(mx, sh.rf[w]);
+        }
+    }
+    auto from_hbm = [&](auto &&f) { each_logit<DT, AL, NT>(base, P.V, nunits, arr, arr_bytes, f); };
+    if (ncand == kNoCand || ncand > UnitsLds::kCap) {
+        // the selects over the whole vector: its maximum first
+        float t = -INFINITY;
+        from_hbm([&](float z) { t = nmax(t, z); });
+        mx = block_nmax<NT>(t, sh);
+    }
+    auto part_sum = [&](float lower) {
+        double s = 0.0;
+        from_hbm([&](float z) {
+            if (z >= lower) s += fexp2(((double)z - (double)mx) * c64);
+        });
+        return s;
+    };
+    float theta;
+    double S;
+    finish_thresholds<LOW, NT>(from_hbm, part_sum, ncand, mx, k, tp, use_k, use_p, c64, sh, theta, S);
+    write_records<NT>(P, v, Partial{mx, __float_as_int(__builtin_nanf("")), S});
+    if (tid == 0) {
+        P.theta[v] = theta;
+        if (vc.slot >= 0 && vc.x >= 0 && (int64_t)vc.x < P.V) {
+            float *zx = P.zx + (target ? 0 : P.nD) + vc.slot;
+            const float zv = *zx;
+            if (zv < theta) *zx = -INFINITY;
+        }
+    }
 }
 
 hipError_t launch_filter(const Params &P, hipStream_t s, int dtype, bool aligned)
@@ -824,41 +739,39 @@ hipError_t launch_filter(const Params &P, hipStream_t s, int dtype, bool aligned
     return hipLaunchKernel(fn, dim3((unsigned)nvec), dim3(kFilterBlock), args, 0, s);
 }
 
-// Units per thread of filter_stats_kernel for this call, 0 when it does not apply.
-int filter_stats_units(int dtype, bool aligned, int64_t V)
+// Units per thread of filter_units_kernel for a vocabulary, 0 beyond what it holds.
+int filter_units_num(int64_t V)
 {
-    if (dtype != 0 || !aligned) return 0;
-    const int64_t per = (V / kUnitElems + kFilterBlock - 1) / kFilterBlock;
-    for (int nu : {4, 8, 12, 16, 20})
-        if (per <= nu) return nu;
+    const int64_t nu = ceil_div(V, 2 * kItemElems) * kPieceUnits;
+    for (int n : {2, 8, 12, 16, 32})
+        if (nu <= (int64_t)n * kUnitsBlock) return n;
     return 0;
 }
 
-hipError_t launch_filter_stats(const Params &P, hipStream_t s, int nu, hipEvent_t start, hipEvent_t stop)
+template <int DT, bool AL>
+static const void *filter_units_fn(int num)
+{
+    switch (num) {
+    case 2: return (const void *)filter_units_kernel<DT, AL, 2>;
+    case 8: return (const void *)filter_units_kernel<DT, AL, 8>;
+    case 12: return (const void *)filter_units_kernel<DT, AL, 12>;
+    case 16: return (const void *)filter_units_kernel<DT, AL, 16>;
+    case 32: return (const void *)filter_units_kernel<DT, AL, 32>;
+    default: return nullptr;
+    }
+}
+
+hipError_t launch_filter_units(const Params &P, hipStream_t s, int dtype, bool aligned)
 {
     const int64_t nvec = P.nT + P.nD;
-    if (nvec <= 0) return launch_timed(nullptr, 0, kFilterBlock, P, s, start, stop);
-    if (nvec > INT32_MAX) return hipErrorInvalidConfiguration;
-    const void *fn = nullptr;
-    switch (nu) {
-    case 4: fn = (const void *)filter_stats_kernel<4>; break;
-    case 8: fn = (const void *)filter_stats_kernel<8>; break;
-    case 12: fn = (const void *)filter_stats_kernel<12>; break;
-    case 16: fn = (const void *)filter_stats_kernel<16>; break;
-    case 20: fn = (const void *)filter_stats_kernel<20>; break;
-    default: return hipErrorInvalidValue;
-    }
-    static int32_t cap[5][64] = {};   // per kernel variant and device
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-    const int var = nu / 4 - 1;
-    int32_t grid = dev < 64 ? cap[var][dev] : 0;
-    if (grid <= 0) {
-        grid = filter_grid_cap(fn);
-        if (dev < 64) cap[var][dev] = grid;
-    }
-    const int64_t blocks = nvec < grid ? nvec : grid;
-    return launch_timed(fn, blocks, kFilterBlock, P, s, start, stop);
+    if (nvec <= 0) return hipSuccess;
+    if (nvec > INT32_MAX || P.umax == nullptr) return hipErrorInvalidConfiguration;
+    const int num = filter_units_num(P.V);
+    const void *fn = dtype == 0 ? (aligned ? filter_units_fn<0, true>(num) : filter_units_fn<0, false>(num))
+                                : (aligned ? filter_units_fn<1, true>(num) : filter_units_fn<1, false>(num));
+    if (fn == nullptr) return hipErrorInvalidValue;
+    void *args[] = {const_cast<Params *>(&P)};
+    return hipLaunchKernel(fn, dim3((unsigned)nvec), dim3(kUnitsBlock), args, 0, s);
 }
 
 }  // namespace sv

@@ -72,6 +72,7 @@ struct VecInfo {           // one streamed vector of a ragged batch (filled by p
     int32_t x;             // that draft token (when slot >= 0)
     float T;               // the row's temperature
 };
+static_assert(sizeof(VecInfo) == 16, "vec_ctx_uniform reads a VecInfo as four words");
 
 struct Sum2 {              // draw sums over one tile
     double w;              // draw weights (residual or bonus)
@@ -208,7 +209,18 @@ struct Params {
     const int32_t *top_k;     // [B] or null
     const float *top_p;       // [B] or null
     float *theta;             // [nT + nD] or null: per-vector logit threshold
+    // filtered calls: the maximum of every unit of 64 consecutive logits, as a 16-bit
+    // key (unit_key), [nT + nD][ipv * 64] (unit u: logits [64 u, 64 u + 64))
+    uint16_t *umax;
 };
+
+// Units of 64 consecutive logits, 64 to a piece of the streaming pass.
+constexpr int kPieceUnits = 64;
+inline size_t filter_umax_bytes(int32_t B, int64_t nT, int64_t V)
+{
+    const int64_t nvec = 2 * nT - B;
+    return align256(sizeof(uint16_t) * (size_t)nvec * (size_t)ceil_div(V, 2 * kItemElems) * kPieceUnits);
+}
 
 // Early-exit scratch after the verification workspace: two row lists, two vector
 // lists (each vector is listed at most once, the first list holds two slots per row),
@@ -567,6 +579,24 @@ struct VecCtx {
 };
 
 // v: global vector index (target rows first, then draft rows)
+// Element i (wave-uniform) of an input that no kernel writes, read as a scalar load
+// (through the constant address space).  Scalar loads complete apart from the wave's
+// vector loads: waiting for one does not wait for the vector loads in flight.
+template <class T>
+__device__ __forceinline__ T load_uniform(const T *p, int64_t i)
+{
+    return ((const __attribute__((address_space(4))) T *)p)[i];
+}
+
+// Whether a row of a filtered call has a filter to apply (top-k with 0 < k < V, or
+// top-p with 0 < p < 1); row wave-uniform.
+__device__ __forceinline__ bool row_filters(const Params &P, int32_t row)
+{
+    const int64_t k = P.top_k ? load_uniform(P.top_k, row) : 0;
+    const float tp = P.top_p ? load_uniform(P.top_p, row) : 1.0f;
+    return (k > 0 && k < P.V) || (tp > 0.0f && tp < 1.0f);
+}
+
 __device__ __forceinline__ VecCtx vec_ctx(const Params &P, int64_t v)
 {
     VecCtx c;
@@ -588,6 +618,34 @@ __device__ __forceinline__ VecCtx vec_ctx(const Params &P, int64_t v)
         c.slot = P.mode == 0 ? vi.slot : -1;
         c.x = vi.x;
         c.T = vi.T;
+    }
+    return c;
+}
+
+// vec_ctx for a wave-uniform v, with scalar loads (load_uniform): for the streaming
+// loops, whose context reads would otherwise wait behind the pieces' loads in flight.
+__device__ __forceinline__ VecCtx vec_ctx_uniform(const Params &P, int64_t v)
+{
+    v = __builtin_amdgcn_readfirstlane((int32_t)v);   // v < nT + nD <= INT32_MAX
+    VecCtx c;
+    c.target = v < P.nT;
+    if (P.gamma == nullptr) {
+        const bool target = c.target;
+        const int64_t vloc = target ? v : v - P.nT;
+        const int64_t g = P.gamma_uniform;
+        const int64_t per = target ? g + 1 : g;
+        const int64_t row = __builtin_amdgcn_readfirstlane((int32_t)qdiv(vloc, per, target ? P.geo.inv_t : P.geo.inv_d));
+        const int64_t j = vloc - row * per;
+        c.row = (int32_t)row;
+        c.slot = (P.mode == 0 && j < g) ? (int32_t)(row * g + j) : -1;
+        c.x = c.slot >= 0 ? load_uniform(P.tokens, c.slot) : -1;
+        c.T = P.mode == 0 ? load_uniform(P.temperature, row) : 0.0f;
+    } else {
+        const int32_t *w = reinterpret_cast<const int32_t *>(P.vinfo + v);   // {row, slot, x, T}
+        c.row = load_uniform(w, 0);
+        c.slot = P.mode == 0 ? load_uniform(w, 1) : -1;
+        c.x = load_uniform(w, 2);
+        c.T = __int_as_float(load_uniform(w, 3));
     }
     return c;
 }
@@ -627,6 +685,19 @@ __device__ __forceinline__ double readlane_f64(double v, int l)
 
 // maximum that propagates NaN
 __device__ __forceinline__ float nmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// A unit maximum as a 16-bit key that sorts like it, rounded down: the upper half of
+// the float's order-preserving key (exact for bf16 values); 0 for -inf, 0xffff for
+// NaN or +inf (finite values take 0x0080 to 0xff7f).
+__device__ __forceinline__ uint16_t unit_key(float x)
+{
+    // selects only: a branch here would split the streaming loop's control flow
+    const uint32_t b = __float_as_uint(x);
+    uint32_t k = ((b & 0x80000000u) ? ~b : (b | 0x80000000u)) >> 16;
+    k = x == -INFINITY ? 0u : k;
+    k = x < INFINITY ? k : 0xffffu;
+    return (uint16_t)k;
+}
 
 __device__ __forceinline__ float wave_umax_f32(float v)
 {
@@ -689,8 +760,7 @@ hipError_t launch_stats_list(const Params &P, hipStream_t s, int dtype, bool ali
 hipError_t launch_ee_init(const Params &P, hipStream_t s);
 hipError_t launch_ee_step(const Params &P, hipStream_t s, int dtype);
 hipError_t launch_filter(const Params &P, hipStream_t s, int dtype, bool aligned);
-int filter_stats_units(int dtype, bool aligned, int64_t V);
-hipError_t launch_filter_stats(const Params &P, hipStream_t s, int nu, hipEvent_t start = nullptr,
-                               hipEvent_t stop = nullptr);
+int filter_units_num(int64_t V);
+hipError_t launch_filter_units(const Params &P, hipStream_t s, int dtype, bool aligned);
 
 }  // namespace sv

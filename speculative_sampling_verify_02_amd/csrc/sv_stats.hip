@@ -23,8 +23,9 @@ namespace sv {
 // Workgroup b owns pieces [b N / G, (b + 1) N / G) of the N pieces.  Its waves take
 // them in order from a counter in LDS (each wave's first piece is fixed), so a wave
 // the CU's arbiter serves less takes fewer pieces and the workgroup's waves finish
-// together; with one workgroup per CU the CUs finish together too.
-template <int DT, bool AL>
+// together; with one workgroup per CU the CUs finish together too.  UM: filtered
+// calls, which also store the maximum of every 64 consecutive logits (piece_finish).
+template <int DT, bool AL, bool UM>
 __device__ __forceinline__ void stats_body(const Params &P)
 {
     __shared__ uint32_t s_next;
@@ -58,7 +59,10 @@ __device__ __forceinline__ void stats_body(const Params &P)
     ItemRaw<DT> ra, rb;
     half_begin<DT, AL>(P, v, j, 0, true, ra, lane);
     half_begin<DT, AL>(P, v, j, 1, true, rb, lane);
-    VecCtx vc = vec_ctx(P, v);
+    // the vector's context by scalar loads (vec_ctx_uniform): as vector loads, reading
+    // it would wait for every load in flight, the next piece's included
+    VecCtx vc = vec_ctx_uniform(P, v);
+    bool filt = UM && row_filters(P, vc.row);   // UM: the row filters (then the maxima only)
     float cached_T = __builtin_nanf("");
     TempConst tc{};
     for (;;) {
@@ -76,15 +80,17 @@ __device__ __forceinline__ void stats_body(const Params &P)
             cached_T = vc.T;
         }
         PieceAcc<DT> acc;
-        piece_half<DT, AL>(P, vc, rm, tc, cj, 0, half_len(P, cj, 0), ra, acc, lane, tab);
+        piece_half<DT, AL, UM>(P, vc, rm, tc, cj, 0, half_len(P, cj, 0), ra, acc, lane, tab, filt);
         half_begin<DT, AL>(P, v, j, 0, live, ra, lane);
         const int n1 = half_len(P, cj, 1);
-        if (n1 > 0) piece_half<DT, AL>(P, vc, rm, tc, cj, 1, n1, rb, acc, lane, tab);
+        if (n1 > 0) piece_half<DT, AL, UM>(P, vc, rm, tc, cj, 1, n1, rb, acc, lane, tab, filt);
         half_begin<DT, AL>(P, v, j, 1, live, rb, lane);
-        const VecCtx vn = vec_ctx(P, live ? v : 0);
-        piece_finish<DT>(P, vc, rm, tc, cv, cj, acc);
+        const VecCtx vn = vec_ctx_uniform(P, live ? v : 0);
+        const bool fn = UM && row_filters(P, vn.row);
+        piece_finish<DT, UM>(P, vc, rm, tc, cv, cj, acc, filt);
         if (!live) break;
         vc = vn;
+        filt = fn;
         pn = pnn;
     }
 }
@@ -162,19 +168,19 @@ __global__ __launch_bounds__(64) void stats_list_kernel(Params P)
 }
 
 // 16-byte aligned rows (the usual case): one workgroup per CU, of 16 waves (bf16) or 12
-template <int DT>
+template <int DT, bool UM>
 __global__ __launch_bounds__(kStatsBlock<DT>) void stats_kernel(Params P)
 {
-    stats_body<DT, true>(P);
+    stats_body<DT, true, UM>(P);
 }
 
 // rows that do not start 16-byte aligned: aligned loads, realigned in registers; 12
 // waves per CU for bf16, 8 for fp32 (the realignment needs registers of its own)
 template <int DT> constexpr int kStatsBlockUnaligned = DT == 0 ? 768 : 512;
-template <int DT>
+template <int DT, bool UM>
 __global__ __launch_bounds__(kStatsBlockUnaligned<DT>) void stats_kernel_unaligned(Params P)
 {
-    stats_body<DT, false>(P);
+    stats_body<DT, false, UM>(P);
 }
 
 // ===========================================================================
@@ -194,10 +200,15 @@ static int stats_block(int dtype, bool aligned)
     return aligned ? kStatsBlock<1> : kStatsBlockUnaligned<1>;
 }
 
-static const void *stats_fn(int dtype, bool aligned)
+static const void *stats_fn(int dtype, bool aligned, bool um = false)
 {
-    return dtype == 0 ? (aligned ? (const void *)stats_kernel<0> : (const void *)stats_kernel_unaligned<0>)
-                      : (aligned ? (const void *)stats_kernel<1> : (const void *)stats_kernel_unaligned<1>);
+    if (um)
+        return dtype == 0
+            ? (aligned ? (const void *)stats_kernel<0, true> : (const void *)stats_kernel_unaligned<0, true>)
+            : (aligned ? (const void *)stats_kernel<1, true> : (const void *)stats_kernel_unaligned<1, true>);
+    return dtype == 0
+        ? (aligned ? (const void *)stats_kernel<0, false> : (const void *)stats_kernel_unaligned<0, false>)
+        : (aligned ? (const void *)stats_kernel<1, false> : (const void *)stats_kernel_unaligned<1, false>);
 }
 
 // Workgroups of the streaming kernel that fit on the current device at once
@@ -263,7 +274,8 @@ hipError_t launch_stats_list(const Params &P, hipStream_t s, int dtype, bool ali
 
 hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned, hipEvent_t start, hipEvent_t stop)
 {
-    return launch_timed(stats_fn(dtype, aligned), P.geo.G, stats_block(dtype, aligned), P, s, start, stop);
+    return launch_timed(stats_fn(dtype, aligned, P.umax != nullptr), P.geo.G, stats_block(dtype, aligned), P, s,
+                        start, stop);
 }
 
 }  // namespace sv

@@ -541,19 +541,71 @@ template <int DT>
 struct PieceAcc {
     LaneSum ls;
     LaneArg la;
+    float um = -INFINITY;   // UM: the maximum of the 64-logit unit this lane stores
 };
 
-template <int DT, bool AL>
+// Filtered calls cut every vector into units of 64 consecutive logits: one load of G
+// neighbouring lanes (G E = 64).  Each lane's load maxima are reduced over its group
+// (butterfly within rows of 16 lanes), and lane l = G g + r keeps the maximum of load
+// r of the piece (half r / loads, load r % loads) for group g: unit r E + g of the
+// piece, logits [64 (r E + g), +64).
+template <int DT>
+__device__ __forceinline__ void unit_max_half(const float *lmk, int h, int lane, float &um)
+{
+    constexpr int E = kE<DT>, G = 64 / E, NL = kItemLoads<DT>;
+    const int r = lane & (G - 1);
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+        float v = lmk[k];
+        v = nmax(v, dpp_f32<0xB1>(v));    // quad_perm [1,0,3,2]
+        v = nmax(v, dpp_f32<0x4E>(v));    // quad_perm [2,3,0,1]
+        v = nmax(v, dpp_f32<0x141>(v));   // row_half_mirror: 8 lanes
+        if constexpr (G == 16) v = nmax(v, dpp_f32<0x140>(v));   // row_mirror: 16 lanes
+        if (r == h * NL + k) um = v;
+    }
+}
+
+// The maximum of each load's logits (lmk), and the lane maximum m updated with them.
+template <int DT>
+__device__ __forceinline__ void max_half(const ItemRaw<DT> &r, float *lmk, float &m)
+{
+    constexpr int E = kE<DT>;
+#pragma unroll
+    for (int k = 0; k < kItemLoads<DT>; ++k) {
+        float x[E];
+        lane_vals<DT>(r, k, x);
+        float lm = x[0];
+#pragma unroll
+        for (int t = 1; t < E; ++t) lm = nmax(lm, x[t]);
+        lmk[k] = lm;
+        m = nmax(m, lm);
+    }
+}
+
+// UM with filt (a row of a filtered call that filters): the vector's sums are not
+// needed, since the threshold search replaces its record by the exact sum over the
+// kept logits; the half gives only the maxima (the lane's, and its unit's).
+template <int DT, bool AL, bool UM = false>
 __device__ __forceinline__ void piece_half(const Params &P, const VecCtx &vc, int32_t rm, const TempConst &tc,
                                            int64_t j, int h, int n, ItemRaw<DT> &r, PieceAcc<DT> &acc, int lane,
-                                           const Exp2Tab &tab)
+                                           const Exp2Tab &tab, bool filt = false)
 {
     constexpr int E = kE<DT>;
     if constexpr (!AL) realign(r, lane);
     if (n != (int)P.geo.ie) mask_tail<DT, AL>(r, lane, n);
     if (rm == ROW_SAMPLE) {
-        if constexpr (DT == 0) sample_half(r, tc.c_hi, acc.ls, h == 0);
-        else sample_half_f32(r, tc.c_eff, acc.ls, h == 0, tab);
+        if (UM && filt) {
+            float lmk[kItemLoads<DT>];
+            if (h == 0) {
+                acc.ls.m = -INFINITY;
+                acc.um = -INFINITY;   // (a piece without a second half: its units are past the end)
+            }
+            max_half<DT>(r, lmk, acc.ls.m);
+            unit_max_half<DT>(lmk, h, lane, acc.um);
+        } else {
+            if constexpr (DT == 0) sample_half(r, tc.c_hi, acc.ls, h == 0);
+            else sample_half_f32(r, tc.c_eff, acc.ls, h == 0, tab);
+        }
         // the logit at the position's draft token, if this half holds it
         if (vc.slot >= 0 && vc.x >= 0 && (int64_t)vc.x < P.V) {
             const int64_t o = (int64_t)vc.x - (2 * j + h) * P.geo.ie;
@@ -578,10 +630,16 @@ __device__ __forceinline__ void piece_half(const Params &P, const VecCtx &vc, in
 // is unusable.
 template <int DT>
 __device__ __forceinline__ Partial piece_record(const Params &P, const VecCtx &vc, int32_t rm, const TempConst &tc,
-                                                int64_t j, const PieceAcc<DT> &acc)
+                                                int64_t j, const PieceAcc<DT> &acc, bool filt = false)
 {
     Partial rec{-INFINITY, INT32_MAX, 0.0};
-    if (rm == ROW_SAMPLE) {
+    if (rm == ROW_SAMPLE && filt) {
+        // the maximum alone (its sum comes from the threshold search); a NaN or +inf
+        // logit makes the record non-finite as in sample_record
+        const float M = wave_umax_f32(acc.ls.m);
+        rec = Partial{M, 0, 0.0};
+        if (M == INFINITY || M != M) rec = Partial{M, __float_as_int(__builtin_nanf("")), (double)__builtin_nanf("")};
+    } else if (rm == ROW_SAMPLE) {
         rec = sample_record<DT>(acc.ls, tc.c_hi, tc.c_lo);
     } else if ((rm == ROW_GREEDY && vc.target) || rm == ROW_BAD_TEMP) {
         rec = argmax_record(acc.la);
@@ -590,12 +648,21 @@ __device__ __forceinline__ Partial piece_record(const Params &P, const VecCtx &v
     return rec;
 }
 
-template <int DT>
+// UM (filtered calls): a sampling row that filters also stores the maximum of each of
+// the piece's 64 units as a 16-bit key (unit_max_half), from which the threshold
+// search bounds the top-k.
+template <int DT, bool UM = false>
 __device__ __forceinline__ void piece_finish(const Params &P, const VecCtx &vc, int32_t rm, const TempConst &tc,
-                                             int64_t v, int64_t j, PieceAcc<DT> &acc)
+                                             int64_t v, int64_t j, PieceAcc<DT> &acc, bool filt = false)
 {
-    const Partial rec = piece_record<DT>(P, vc, rm, tc, j, acc);
-    if ((threadIdx.x & 63) == 0) P.parts[v * P.geo.ipv + j] = rec;
+    const Partial rec = piece_record<DT>(P, vc, rm, tc, j, acc, UM && filt);
+    const int lane = threadIdx.x & 63;
+    if constexpr (UM) {
+        constexpr int E = kE<DT>, G = 64 / E;
+        if (rm == ROW_SAMPLE && filt)
+            P.umax[(v * P.geo.ipv + j) * kPieceUnits + (lane % G) * E + lane / G] = unit_key(acc.um);
+    }
+    if (lane == 0) P.parts[v * P.geo.ipv + j] = rec;
 }
 
 }  // namespace sv

@@ -164,12 +164,15 @@ def test_large_k_and_crowded_tops(H):
                np.array([0.9, 1.0, 0.5, 0.99, 1.0, 0.7], np.float32))
 
 
-def test_vocab_sizes_around_the_register_budget(H):
-    """Aligned bf16 vocabularies at several register budgets of the one-pass kernel
-    (up to 163840 logits per vector) and just beyond it (streaming pass, then the
-    threshold kernel), with top-k, top-p, both and neither."""
-    for i, V in enumerate((90000, 152064, 163840, 163848)):
-        w = workloads.small(seed=90 + i, batch=4, vocab=V, dtype="bf16", gamma=[2, 0, 3, 1],
+def test_vocab_sizes_around_the_unit_budgets(H):
+    """Vocabularies at the edges of the threshold kernel's unit budgets (2, 8, 12, 16
+    and 32 unit maxima of 64 logits per thread: up to 32768, 131072, 196608, 262144
+    and 524288 logits) and just beyond the last (the threshold kernel that reads the
+    whole vector), bf16 and fp32, with top-k, top-p, both and neither."""
+    cases = ((32768, "bf16"), (32776, "bf16"), (131080, "f32"), (196608, "bf16"),
+             (196616, "bf16"), (262152, "f32"), (524288, "bf16"), (524296, "bf16"))
+    for i, (V, dt) in enumerate(cases):
+        w = workloads.small(seed=90 + i, batch=4, vocab=V, dtype=dt, gamma=[2, 0, 3, 1],
                             temperature=[1.0, 0.7, 1.3, 0.0])
         parity(H, w, *filters(w, seed=300 + i, kinds=("kp", "p", "k", "none")))
 
