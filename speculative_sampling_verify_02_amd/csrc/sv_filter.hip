@@ -167,9 +167,9 @@ __device__ __forceinline__ uint32_t radix_select(Src &&each, double target, floa
     double above = 0.0;
 #pragma unroll
     for (int shift = 24; shift >= LOW; shift -= 8) {
-        if (tid < kBins) {
-            if constexpr (MASS) sh.mass[tid] = 0.0;
-            else sh.cnt[tid] = 0u;
+        for (int i = tid; i < kBins; i += blockDim.x) {
+            if constexpr (MASS) sh.mass[i] = 0.0;
+            else sh.cnt[i] = 0u;
         }
         __syncthreads();
         // keys whose digits above this one are the prefix's
@@ -511,18 +511,22 @@ __global__ __launch_bounds__(kFilterBlock) void filter_kernel(Params P)
 // (a block-wide select over all unit maxima when fewer waves hold m finite lanes).
 // Rows without top-k, or whose candidates do not fit, take the selects over the
 // whole vector.  One 4-wave workgroup per vector: the work is a chain of small
-// dependent reads, so many vectors are in flight per CU.
+// dependent reads, so many vectors are in flight per CU: two-wave workgroups, 16 per
+// CU when their registers allow.
 // ---------------------------------------------------------------------------
-constexpr int kUnitsBlock = 256;
+constexpr int kUnitsBlock = 128;
 constexpr int kUnitsWaves = kUnitsBlock / 64;
-constexpr int kMaxUnitList = 1024;   // units read again
+constexpr int kMaxUnitList = 768;   // units read again
 
+// Under 10 KB, so that 16 workgroups fit a CU's LDS.
 struct UnitsLds {
-    static constexpr uint32_t kCap = 2048;
+    static constexpr uint32_t kCap = 1536;
     float cand[kCap];
     uint32_t ncand;
-    uint32_t cnt[kBins];
-    double mass[kBins];
+    union {   // a select's histogram: counts or masses, never both at once
+        uint32_t cnt[kBins];
+        double mass[kBins];
+    };
     double rd[kUnitsWaves];
     float rf[kUnitsWaves];
     uint32_t ru[kUnitsWaves];
@@ -534,8 +538,11 @@ struct UnitsLds {
     uint32_t nlist;
     uint16_t list[kMaxUnitList];
 };
+static_assert(sizeof(UnitsLds) <= 10240, "16 select workgroups per CU");
 
-// NUM: units per thread (the vector's ipv * 64 units, at most NUM * kUnitsBlock).
+// NUM: units per thread, a multiple of 8 (the vector's ipv * 64 units, at most
+// NUM * kUnitsBlock); thread t holds units 8 (t + q NT) + i, i < 8, read 16 bytes at a
+// time.
 template <int DT, bool AL, int NUM>
 __global__ __launch_bounds__(kUnitsBlock) void filter_units_kernel(Params P)
 {
@@ -547,21 +554,29 @@ __global__ __launch_bounds__(kUnitsBlock) void filter_units_kernel(Params P)
     __shared__ UnitsLds sh;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t v = blockIdx.x;
-    // the thread's units tid, tid + NT, ...: keys in the upper half-word, 0 for -inf
-    // (loaded first, so that the row's context loads overlap them)
-    const int32_t nu = (int32_t)(P.geo.ipv * kPieceUnits);
-    const uint16_t *um = P.umax + v * (int64_t)nu;
-    uint32_t key[NUM];
+    // the thread's units: keys in the upper half-word, 0 for -inf (loaded first, so
+    // that the row's context loads overlap them)
+    const int32_t nu = (int32_t)(P.geo.ipv * kPieceUnits);   // a multiple of 64
+    const uint4 *um = reinterpret_cast<const uint4 *>(P.umax + v * (int64_t)nu);
+    // (two to a word: key(i) unpacks unit i's)
+    uint32_t kw[NUM / 2];
 #pragma unroll
-    for (int i = 0; i < NUM; ++i) {
-        const int32_t u = tid + i * NT;
-        key[i] = u < nu ? (uint32_t)um[u] << 16 : 0u;
+    for (int q = 0; q < NUM / 8; ++q) {
+        const int32_t g = tid + q * NT;
+        const uint4 w = 8 * g < nu ? um[g] : make_uint4(0u, 0u, 0u, 0u);
+        kw[4 * q] = w.x;
+        kw[4 * q + 1] = w.y;
+        kw[4 * q + 2] = w.z;
+        kw[4 * q + 3] = w.w;
     }
+    auto key = [&](int i) __attribute__((always_inline)) -> uint32_t {
+        return (i & 1) ? (kw[i / 2] & 0xffff0000u) : (kw[i / 2] << 16);
+    };
     if (P.gamma != nullptr && P.hdr->status != 0) return;
-    const VecCtx vc = vec_ctx(P, v);
+    const VecCtx vc = vec_ctx_uniform(P, v);
     const int32_t rm = row_mode(P.mode, vc.T);
-    const int64_t k = P.top_k ? P.top_k[vc.row] : 0;
-    const float tp = P.top_p ? P.top_p[vc.row] : 1.0f;
+    const int64_t k = P.top_k ? load_uniform(P.top_k, vc.row) : 0;
+    const float tp = P.top_p ? load_uniform(P.top_p, vc.row) : 1.0f;
     const bool use_k = k > 0 && k < P.V, use_p = tp > 0.0f && tp < 1.0f;
     if (rm != ROW_SAMPLE || (!use_k && !use_p)) {
         if (tid == 0) P.theta[v] = -INFINITY;
@@ -583,9 +598,10 @@ __global__ __launch_bounds__(kUnitsBlock) void filter_units_kernel(Params P)
         uint32_t kmax = 0u;
 #pragma unroll
         for (int i = 0; i < NUM; ++i) {
-            bad |= key[i] == kBad;
-            wf += __popcll(__ballot(key[i] != 0u));
-            kmax = key[i] > kmax ? key[i] : kmax;
+            const uint32_t ki = key(i);
+            bad |= ki == kBad;
+            wf += __popcll(__ballot(ki != 0u));
+            kmax = ki > kmax ? ki : kmax;
         }
         uint32_t Lw = 0xffffffffu;   // none
         if (m > 0 && m <= 64 && __popcll(__ballot(kmax != 0u)) >= m) {
@@ -602,6 +618,10 @@ __global__ __launch_bounds__(kUnitsBlock) void filter_units_kernel(Params P)
             sh.ncand = 0u;
         }
     }
+    // later uses unpack the keys again from their words, rather than keep them
+    // unpacked across the barrier
+#pragma unroll
+    for (int i = 0; i < NUM / 2; ++i) asm volatile("" : "+v"(kw[i]));
     __syncthreads();
     int64_t nfin = 0;
     bool bad = false;
@@ -632,35 +652,36 @@ __global__ __launch_bounds__(kUnitsBlock) void filter_units_kernel(Params P)
             auto from_keys = [&](auto &&f) __attribute__((always_inline)) {
 #pragma unroll
                 for (int i = 0; i < NUM; ++i)
-                    if (key[i] != 0u) f(key_val<0>(key[i]));
+                    if (key(i) != 0u) f(key_val<0>(key(i)));
             };
             L32 = radix_select<false, 16>(from_keys, (double)k, 0.0f, c64, sh);
         }
         // the units whose maximum reaches L
 #pragma unroll
         for (int i = 0; i < NUM; ++i) {
-            if (key[i] >= L32) {
+            if (key(i) >= L32) {
                 const uint32_t at = atomicAdd(&sh.nlist, 1u);
-                if (at < (uint32_t)kMaxUnitList) sh.list[at] = (uint16_t)(tid + i * NT);
+                if (at < (uint32_t)kMaxUnitList) sh.list[at] = (uint16_t)(8 * (tid + (i / 8) * NT) + i % 8);
             }
         }
         __syncthreads();
         const uint32_t nlist = sh.nlist;
         if (nlist <= (uint32_t)kMaxUnitList) {
             // their logits >= L (L the least float of its key, so a lower bound for
-            // fp32 maxima rounded down to 16 bits, exact for bf16), four 16-byte chunks
+            // fp32 maxima rounded down to 16 bits, exact for bf16), eight 16-byte chunks
             // per thread in flight (consecutive threads read consecutive chunks)
+            constexpr int kQ = 8;
             const float L = key_val<0>(L32);
             const int32_t nch = (int32_t)nlist * kChunks;
             float tmx = -INFINITY;
-            for (int32_t c0 = 0; c0 < nch; c0 += 4 * NT) {
-                uint32_t w[4][4];
-                int64_t e0[4];
+            for (int32_t c0 = 0; c0 < nch; c0 += kQ * NT) {
+                uint32_t w[kQ][4];
+                int32_t e0[kQ];   // (V < 2^31)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int q = 0; q < kQ; ++q) {
                     const int32_t c = c0 + q * NT + tid;
-                    e0[q] = P.V;   // nothing to read
-                    if (c < nch) e0[q] = (int64_t)sh.list[c / kChunks] * kPieceUnits + (c % kChunks) * E;
+                    e0[q] = (int32_t)P.V;   // nothing to read
+                    if (c < nch) e0[q] = (int32_t)sh.list[c / kChunks] * kPieceUnits + (c % kChunks) * E;
                     if (e0[q] < P.V) {
                         if constexpr (AL) {
                             const uint4 x = *reinterpret_cast<const uint4 *>(
@@ -670,7 +691,7 @@ __global__ __launch_bounds__(kUnitsBlock) void filter_units_kernel(Params P)
                     }
                 }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int q = 0; q < kQ; ++q) {
                     if (!(e0[q] < P.V)) continue;
 #pragma unroll
                     for (int t = 0; t < E; ++t) {
@@ -743,7 +764,7 @@ hipError_t launch_filter(const Params &P, hipStream_t s, int dtype, bool aligned
 int filter_units_num(int64_t V)
 {
     const int64_t nu = ceil_div(V, 2 * kItemElems) * kPieceUnits;
-    for (int n : {2, 8, 12, 16, 32})
+    for (int n : {8, 16, 24, 32, 64})
         if (nu <= (int64_t)n * kUnitsBlock) return n;
     return 0;
 }
@@ -752,11 +773,11 @@ template <int DT, bool AL>
 static const void *filter_units_fn(int num)
 {
     switch (num) {
-    case 2: return (const void *)filter_units_kernel<DT, AL, 2>;
     case 8: return (const void *)filter_units_kernel<DT, AL, 8>;
-    case 12: return (const void *)filter_units_kernel<DT, AL, 12>;
     case 16: return (const void *)filter_units_kernel<DT, AL, 16>;
+    case 24: return (const void *)filter_units_kernel<DT, AL, 24>;
     case 32: return (const void *)filter_units_kernel<DT, AL, 32>;
+    case 64: return (const void *)filter_units_kernel<DT, AL, 64>;
     default: return nullptr;
     }
 }

@@ -165,11 +165,12 @@ def test_large_k_and_crowded_tops(H):
 
 
 def test_vocab_sizes_around_the_unit_budgets(H):
-    """Vocabularies at the edges of the threshold kernel's unit budgets (2, 8, 12, 16
-    and 32 unit maxima of 64 logits per thread: up to 32768, 131072, 196608, 262144
-    and 524288 logits) and just beyond the last (the threshold kernel that reads the
-    whole vector), bf16 and fp32, with top-k, top-p, both and neither."""
-    cases = ((32768, "bf16"), (32776, "bf16"), (131080, "f32"), (196608, "bf16"),
+    """Vocabularies at the edges of the threshold kernel's unit budgets (8, 16, 24, 32
+    and 64 unit maxima of 64 logits per thread of a 128-thread workgroup: up to 65536,
+    131072, 196608, 262144 and 524288 logits) and just beyond the last (the threshold
+    kernel that reads the whole vector), bf16 and fp32, with top-k, top-p, both and
+    neither."""
+    cases = ((65536, "bf16"), (65544, "bf16"), (131080, "f32"), (196608, "bf16"),
              (196616, "bf16"), (262152, "f32"), (524288, "bf16"), (524296, "bf16"))
     for i, (V, dt) in enumerate(cases):
         w = workloads.small(seed=90 + i, batch=4, vocab=V, dtype=dt, gamma=[2, 0, 3, 1],
