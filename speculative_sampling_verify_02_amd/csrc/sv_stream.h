@@ -321,16 +321,17 @@ __device__ __forceinline__ void sample_half(const ItemRaw<0> &r, float c, LaneSu
     if (a.m == -INFINITY) a.s = 0.0f;
 }
 
-// 2^(a/L) in fp64 from a table of the L = 64 values 2^(j/L) in LDS (exp2_tab_read,
-// then exp2_tab_add): a = k + r with
-// k = rint(a), so |r| <= 1/2 and 2^(a/L) = 2^floor(k/L) 2^((k mod L)/L) 2^(r/L), with
-// 2^(r/L) from its Taylor series in r ln 2 / L to degree 3 (truncation below 4e-11
-// relative).  The power 2^floor(k/L) scales the table entry (ldexp, exact): the
-// caller keeps a >= -1000 L (2^-1000, a term that cannot register next to the
-// maximum's 1), so the scaled entry stays normal.  Entry j of
-// the lane's copy is at col[j << sh] (sh = 6: one column per lane, which no two lanes
-// of a wave share, so the reads meet no bank conflicts; sh = 0: a single shared copy).
-constexpr int kTabBits = 6;
+// 2^(a/L) in fp64 from a table of the L = 256 values 2^(j/L) in LDS (exp2_tab_read,
+// then exp2_tab_add): a = k + r with k = rint(a), so |r| <= 1/2 and
+// 2^(a/L) = 2^floor(k/L) 2^((k mod L)/L) 2^(r/L), with 2^(r/L) from its Taylor series
+// in r ln 2 / L to degree 2 (truncation below (ln 2 / 512)^3 / 6 = 4.2e-10 relative).
+// The power 2^floor(k/L) scales the table entry (ldexp, exact): the caller keeps
+// a >= -1000 L (2^-1000, a term that cannot register next to the maximum's 1), so the
+// scaled entry stays normal.  Entry j of the lane's copy is at col[j << sh] (sh = 6:
+// one column per lane, which no two lanes of a wave share, so the reads meet no bank
+// conflicts; sh = 0: a single shared copy).  With 64 columns the table takes 128 KB
+// of LDS, which the streaming kernel's one workgroup per CU can hold.
+constexpr int kTabBits = 8;
 constexpr int kTabLen = 1 << kTabBits;
 
 struct Exp2Tab {
@@ -341,7 +342,6 @@ struct Exp2Tab {
 // (ln 2 / L)^j / j!  (kExp2Coef[13 - j] = (ln 2)^j / j!, scaled by L^-j exactly)
 constexpr double kTabC1 = kExp2Coef[12] / kTabLen;
 constexpr double kTabC2 = kExp2Coef[11] / kTabLen / kTabLen;
-constexpr double kTabC3 = kExp2Coef[10] / kTabLen / kTabLen / kTabLen;
 
 // The two halves of exp2_tab, so that a caller can issue the table reads of several
 // terms before it waits for the first: the rounding and the read, then the series.
@@ -351,7 +351,7 @@ struct TabTerm {
     int ki;     // rint(a)
 };
 
-__device__ __forceinline__ TabTerm exp2_tab_read(double a, const Exp2Tab &t)
+__host__ __device__ __forceinline__ TabTerm exp2_tab_read(double a, const Exp2Tab &t)
 {
     const double k = rint(a);
     TabTerm u;
@@ -363,18 +363,23 @@ __device__ __forceinline__ TabTerm exp2_tab_read(double a, const Exp2Tab &t)
 
 // s + 2^(a/L): the table entry scaled by 2^floor(k/L) (ldexp: a term down to 2^-1000
 // stays exact), times the series, added to s in one fma.
-__device__ __forceinline__ double exp2_tab_add(const TabTerm &u, double s)
+__host__ __device__ __forceinline__ double exp2_tab_add(const TabTerm &u, double s)
 {
-    const double q = fma(fma(fma(kTabC3, u.r, kTabC2), u.r, kTabC1), u.r, 1.0);
+    const double q = fma(fma(kTabC2, u.r, kTabC1), u.r, 1.0);
     return fma(ldexp(u.T, u.ki >> kTabBits), q, s);
+}
+
+// Entry j of the table, 2^(j/L).
+__host__ __device__ __forceinline__ double exp2_tab_entry(int j)
+{
+    return exp2_f64((double)j * (1.0 / kTabLen));
 }
 
 // Fill a table of 2^(j/L) for exp2_tab_read: kTabLen entries, each repeated `copies`
 // times (64: one column per lane; 1: a single copy).  The caller synchronises after it.
 __device__ __forceinline__ void fill_exp2_tab(double *tab, int copies)
 {
-    for (int i = threadIdx.x; i < kTabLen * copies; i += blockDim.x)
-        tab[i] = exp2_f64((double)(i / copies) * (1.0 / kTabLen));
+    for (int i = threadIdx.x; i < kTabLen * copies; i += blockDim.x) tab[i] = exp2_tab_entry(i / copies);
 }
 
 // fp32 logits: the sums feed log2(S_t / S_d), which the residual mass of a draft close
