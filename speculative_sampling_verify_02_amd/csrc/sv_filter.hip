@@ -132,26 +132,44 @@ __device__ __forceinline__ float block_nmax(float v, Lds &sh)
 // 16-byte aligned are read a 512-logit tile per wave with aligned loads shifted into
 // place (load_tile_unit), the logits past V as -inf (arr, arr_bytes: the array the
 // row lies in).
+// Four loads per thread are issued before the first is reduced.
 template <int DT, bool AL, int NT = kFilterBlock, class F>
 __device__ __forceinline__ void each_logit(const void *base, int64_t V, int64_t nunits, const void *arr,
                                            uint64_t arr_bytes, F &&f)
 {
+    constexpr int U = 4;
     if constexpr (AL) {
-        for (int64_t u = tid_now(); u < nunits; u += NT) {
-            const RawUnit<DT> r = load_raw<DT, AL>(base, u, V);
-            float z[kUnitElems];
-            unpack<DT>(r, z);
+        for (int64_t u0 = tid_now(); u0 < nunits; u0 += U * NT) {
+            RawUnit<DT> r[U];
 #pragma unroll
-            for (int e = 0; e < kUnitElems; ++e) f(z[e]);
+            for (int i = 0; i < U; ++i)
+                if (u0 + (int64_t)i * NT < nunits) r[i] = load_raw<DT, AL>(base, u0 + (int64_t)i * NT, V);
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                if (u0 + (int64_t)i * NT >= nunits) break;
+                float z[kUnitElems];
+                unpack<DT>(r[i], z);
+#pragma unroll
+                for (int e = 0; e < kUnitElems; ++e) f(z[e]);
+            }
         }
     } else {
         const int tid = tid_now(), lane = tid & 63, wave = tid >> 6;
-        for (int64_t tile = wave; tile * kTileUnits < nunits; tile += NT / 64) {
-            const RawUnit<DT> r = load_tile_unit<DT>(base, tile, V, arr, arr_bytes, lane);
-            float z[kUnitElems];
-            unpack<DT>(r, z);
+        constexpr int64_t step = NT / 64;
+        for (int64_t t0 = wave; t0 * kTileUnits < nunits; t0 += U * step) {
+            RawUnit<DT> r[U];
 #pragma unroll
-            for (int e = 0; e < kUnitElems; ++e) f(z[e]);
+            for (int i = 0; i < U; ++i)
+                if ((t0 + i * step) * kTileUnits < nunits)
+                    r[i] = load_tile_unit<DT>(base, t0 + i * step, V, arr, arr_bytes, lane);
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                if ((t0 + i * step) * kTileUnits >= nunits) break;
+                float z[kUnitElems];
+                unpack<DT>(r[i], z);
+#pragma unroll
+                for (int e = 0; e < kUnitElems; ++e) f(z[e]);
+            }
         }
     }
 }
@@ -360,18 +378,19 @@ __device__ __forceinline__ uint32_t gather_candidates(GatherGe &&gather_ge, floa
 // logits of 2^((z - mx) c64), from the candidates when they fit in LDS, else from the
 // whole vector (`each(f)` passes every logit to f, spread over the threads;
 // `part_sum(lower)` is this thread's share of the sum over the logits >= lower).
-template <int LOW, int NT = kFilterBlock, class Each, class PartSum, class Lds>
-__device__ __forceinline__ void finish_thresholds(Each &&each, PartSum &&part_sum, uint32_t ncand, float mx,
-                                                  int64_t k, float tp, bool use_k, bool use_p, double c64,
-                                                  Lds &sh, float &theta_out, double &S_out)
+// The thresholds and the kept sum from ncand <= Lds::kCap top-k candidates in LDS:
+// in one wave up to 256 of them, else by block-wide radix selects.
+template <int LOW, int NT = kFilterBlock, class Lds>
+__device__ __forceinline__ void cand_thresholds(uint32_t ncand, float mx, int64_t k, float tp, bool use_p,
+                                                double c64, Lds &sh, float &theta_out, double &S_out)
 {
-    const int tid = tid_now(), lane = tid & 63, wave = tid >> 6;
-    if (ncand != kNoCand) {
-        if (ncand <= (uint32_t)(kWaveCand * 64)) {
-            one_wave_thresholds<LOW>(ncand, mx, k, tp, use_p, c64, sh, theta_out, S_out);
-            return;
-        }
-        if (ncand <= Lds::kCap) {
+    const int tid = tid_now();
+    if (ncand <= (uint32_t)(kWaveCand * 64)) {
+        one_wave_thresholds<LOW>(ncand, mx, k, tp, use_p, c64, sh, theta_out, S_out);
+        return;
+    }
+    {
+        {
             auto from_cand = [&](auto &&f) __attribute__((always_inline)) {
                 for (uint32_t i = tid; i < ncand; i += NT) f(sh.cand[i]);
             };
@@ -399,8 +418,18 @@ __device__ __forceinline__ void finish_thresholds(Each &&each, PartSum &&part_su
             }
             theta_out = theta;
             S_out = S;
-            return;
         }
+    }
+}
+
+template <int LOW, int NT = kFilterBlock, class Each, class PartSum, class Lds>
+__device__ __forceinline__ void finish_thresholds(Each &&each, PartSum &&part_sum, uint32_t ncand, float mx,
+                                                  int64_t k, float tp, bool use_k, bool use_p, double c64,
+                                                  Lds &sh, float &theta_out, double &S_out)
+{
+    if (ncand != kNoCand && ncand <= Lds::kCap) {
+        cand_thresholds<LOW, NT>(ncand, mx, k, tp, use_p, c64, sh, theta_out, S_out);
+        return;
     }
     // selects over the whole vector; theta_k needs at least k finite logits
     uint32_t nfin = 0u;
@@ -437,15 +466,12 @@ __device__ __forceinline__ void write_records(const Params &P, int64_t v, const 
         P.parts[v * ipv + j] = j == 0 ? rec0 : Partial{-INFINITY, INT32_MAX, 0.0};
 }
 
-// Thresholds after the streaming pass for vocabularies beyond filter_units_kernel's
-// budget: the vector is read from memory by every pass.
+// Thresholds of vector v after the streaming pass, reading the vector from memory in
+// every pass (1024 threads): for vocabularies beyond filter_units_kernel's budget.
 template <int DT, bool AL>
-__global__ __launch_bounds__(kFilterBlock) void filter_kernel(Params P)
+__device__ __forceinline__ void filter_vector(const Params &P, int64_t v, FilterLds &sh)
 {
-    __shared__ FilterLds sh;
     const int tid = tid_now();
-    const int64_t v = blockIdx.x;
-    if (P.gamma != nullptr && P.hdr->status != 0) return;
     const VecCtx vc = vec_ctx(P, v);
     const int32_t rm = row_mode(P.mode, vc.T);
     const int64_t k = P.top_k ? P.top_k[vc.row] : 0;
@@ -498,6 +524,15 @@ __global__ __launch_bounds__(kFilterBlock) void filter_kernel(Params P)
             if (zv < theta) *zx = -INFINITY;
         }
     }
+}
+
+// One workgroup per vector.
+template <int DT, bool AL>
+__global__ __launch_bounds__(kFilterBlock) void filter_kernel(Params P)
+{
+    __shared__ FilterLds sh;
+    if (P.gamma != nullptr && P.hdr->status != 0) return;
+    filter_vector<DT, AL>(P, blockIdx.x, sh);
 }
 
 // ---------------------------------------------------------------------------
