@@ -545,9 +545,8 @@ __global__ __launch_bounds__(kFilterBlock) void filter_kernel(Params P)
 // (m = ceil(k / waves); a lane maximum covers the lane's units), and L their least
 // (a block-wide select over all unit maxima when fewer waves hold m finite lanes).
 // Rows without top-k, or whose candidates do not fit, take the selects over the
-// whole vector.  One 4-wave workgroup per vector: the work is a chain of small
-// dependent reads, so many vectors are in flight per CU: two-wave workgroups, 16 per
-// CU when their registers allow.
+// whole vector.  One two-wave workgroup per vector, 16 per CU: the work is a chain of
+// small dependent reads, so many vectors are kept in flight.
 // ---------------------------------------------------------------------------
 constexpr int kUnitsBlock = 128;
 constexpr int kUnitsWaves = kUnitsBlock / 64;
