@@ -164,6 +164,31 @@ def test_large_k_and_crowded_tops(H):
                np.array([0.9, 1.0, 0.5, 0.99, 1.0, 0.7], np.float32))
 
 
+def test_fp32_key_buckets(H):
+    """fp32 logits whose largest values share one 16-bit key bucket: the top of each
+    vector is a cluster -4 - j 2^-20 (j <= 40, negative, so the bucket's least float
+    is its most negative one), spread over different 64-logit units, everything else
+    below -5, and top-k cuts inside the cluster.  The threshold search's bound from
+    the units' 16-bit keys must be the least float of the bucket for all of the
+    cluster to be among the candidates."""
+    rng = np.random.default_rng(95)
+    w = workloads.small(seed=95, batch=6, vocab=8192, dtype="f32", gamma=2)
+
+    def clustered(shape):
+        x = (-10.0 + 0.5 * rng.standard_normal(shape)).astype(np.float32)
+        x = np.minimum(x, np.float32(-5.0))
+        for r in range(shape[0]):
+            units = rng.choice(shape[1] // 64, size=41, replace=False)
+            pos = units * 64 + rng.integers(0, 64, size=41)
+            x[r, pos] = (np.float32(-4.0) - np.arange(41, dtype=np.float32) * np.float32(2.0 ** -20))
+        return x
+
+    w2 = workloads.Workload(**{**w.__dict__, "target": clustered(w.target.shape), "draft": clustered(w.draft.shape)})
+    k = np.array([10, 5, 30, 40, 1, 10], np.int32)
+    p = np.array([1.0, 0.9, 1.0, 0.5, 1.0, 0.99], np.float32)
+    parity(H, w2, k, p)
+
+
 def test_vocab_sizes_around_the_unit_budgets(H):
     """Vocabularies at the edges of the threshold kernel's unit budgets (8, 16, 24, 32
     and 64 unit maxima of 64 logits per thread of a 128-thread workgroup: up to 65536,
