@@ -205,6 +205,9 @@ struct Params {
     int32_t st_split;         // scan_tiles_kernel: workgroups per row
     int32_t ee_j0, ee_j1;     // this step's positions [ee_j0, ee_j1)
     int32_t ee_j2;            // the next step's end (its positions [ee_j1, ee_j2))
+    // streaming pass: relative piece shares of the workgroups on each XCD (workgroup b
+    // runs on XCD b mod 8); all zero: equal shares
+    int32_t xcd_w[8];
     // top-k / top-p filtering of p and q
     const int32_t *top_k;     // [B] or null
     const float *top_p;       // [B] or null

@@ -16,6 +16,8 @@
 // fma) and added across lanes in fp64.  fp32 logits are summed term by term in fp64
 // (a table-driven exp2): the residual mass of a draft close to the target depends on
 // the ratio of the two sums to ~1e-9 relative, below what an fp32 exp can give.
+#include <algorithm>
+
 #include "sv_stream.h"
 
 namespace sv {
@@ -42,7 +44,27 @@ __device__ __forceinline__ void stats_body(const Params &P)
     const int64_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nwb = blockDim.x >> 6;
     const int64_t N = P.geo.nitems, G = gridDim.x;
-    const int64_t p0 = (int64_t)blockIdx.x * N / G, p1 = ((int64_t)blockIdx.x + 1) * N / G;
+    int64_t p0, p1;
+    if (P.xcd_w[0] > 0) {
+        // weighted shares: workgroup b's share is w[b mod 8], its range starts at
+        // N W(b) / W(G) with W(b) the weights of the workgroups before it (exact in
+        // integers, so the ranges still cover every piece once)
+        int64_t wsum = 0, pre[9];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            pre[x] = wsum;
+            wsum += P.xcd_w[x];
+        }
+        pre[8] = wsum;
+        auto W = [&](int64_t b) { return (b / 8) * wsum + pre[b % 8]; };
+        const int64_t wt = W(G);
+        auto start = [&](int64_t b) { const int64_t w = W(b); return (N / wt) * w + (N % wt) * w / wt; };
+        p0 = start(blockIdx.x);
+        p1 = start((int64_t)blockIdx.x + 1);
+    } else {
+        p0 = (int64_t)blockIdx.x * N / G;
+        p1 = ((int64_t)blockIdx.x + 1) * N / G;
+    }
     int64_t p = p0 + wave;
     if (p >= p1) return;
     auto grab = [&]() -> int64_t {
@@ -272,9 +294,31 @@ hipError_t launch_stats_list(const Params &P, hipStream_t s, int dtype, bool ali
     return launch(stats_list_fn(dtype, aligned), blocks, 64, P, s);
 }
 
+// Shares of the streaming pass's workgroups by XCD, from clocks of the pass on MI355X
+// (device-wide timestamps per workgroup): the workgroups of XCDs 0 and 1 start about
+// 0.1-0.3 us after the launch and those of XCDs 2 to 7 about 1.6-2.6 us after it, and
+// the odd XCDs stream about 6.5 % slower than the even ones.  With equal shares the
+// pass ends with the odd XCDs while the even ones idle (C4: ~197 against ~184 us of
+// work).  Each XCD gets work in proportion to its rate times the time it has, T - s,
+// for a pass of T = the bytes at 6.4 TB/s.  The fp32 pass is bound by arithmetic and
+// keeps equal shares.
+static void set_xcd_weights(Params &P, int dtype)
+{
+    if (dtype != 0 || P.geo.G < 64) return;
+    constexpr double kStart[8] = {0.12e-6, 0.25e-6, 1.57e-6, 2.06e-6, 2.5e-6, 2.6e-6, 2.5e-6, 2.5e-6};
+    constexpr double kOddRate = 0.935;
+    const double T = (double)P.geo.nitems * 2.0 * (double)kItemElems * 2.0 / 6.4e12;
+    for (int x = 0; x < 8; ++x) {
+        const double w = ((x & 1) ? kOddRate : 1.0) * std::max(T - kStart[x], 0.5 * T) / T;
+        P.xcd_w[x] = (int32_t)(w * 4096.0 + 0.5);
+    }
+}
+
 hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned, hipEvent_t start, hipEvent_t stop)
 {
-    return launch_timed(stats_fn(dtype, aligned, P.umax != nullptr), P.geo.G, stats_block(dtype, aligned), P, s,
+    Params Q = P;
+    set_xcd_weights(Q, dtype);
+    return launch_timed(stats_fn(dtype, aligned, P.umax != nullptr), P.geo.G, stats_block(dtype, aligned), Q, s,
                         start, stop);
 }
 
