@@ -2,8 +2,9 @@
 around the streaming pass's piece and half boundaries (4096 and 2048 logits) and at
 odd sizes (rows that are not 16-byte aligned), ragged gammas, per-row temperatures
 that include greedy rows (T <= 0) and unusable ones (NaN, inf, subnormal), and draft
-noise from near-equal to unrelated distributions; the full round, the filtered round
-and both early-exit plans."""
+noise from near-equal to unrelated distributions; the full round, the filtered round,
+both early-exit plans, the drafter's draw and greedy tree verification (random tree
+shapes and depths)."""
 from __future__ import annotations
 
 import numpy as np
@@ -66,3 +67,26 @@ def test_random_filtered_rounds(H, case):
 @pytest.mark.parametrize("case", range(20))
 def test_random_early_exit_rounds(H, case):
     ee.parity(H, workloads.small(**random_case(4000 + case)), seed=4100 + case)
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_drafter_draws(case):
+    import test_gpu_sample as samp
+    w = workloads.small(**random_case(5000 + case))
+    side = "target" if case % 3 == 0 else "draft"
+    if side == "draft" and w.draft.shape[0] == 0:
+        side = "target"
+    samp.parity(workloads.sample_inputs(w, seed=5100 + case, side=side))
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_trees(case):
+    import test_gpu_tree as tree
+    rng = np.random.default_rng(6000 + case)
+    vocab = int(rng.choice(BOUNDARY_V)) if rng.random() < 0.5 else int(rng.integers(2, 40001))
+    top_k = int(rng.integers(1, 4))
+    tree.parity(workloads.trees(seed=6100 + case, batch=int(rng.integers(1, 9)), vocab=vocab,
+                                dtype=str(rng.choice(["bf16", "f32"])), top_k=top_k,
+                                heads=int(rng.integers(0, 7 if top_k < 3 else 6)),
+                                accept=float(rng.choice([0.3, 0.7, 0.95])),
+                                random_shape=bool(rng.random() < 0.4)))
