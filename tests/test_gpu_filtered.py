@@ -126,8 +126,8 @@ def test_c3_full_near_target_bonus(H):
 
 
 def test_c4_full(H):
-    """The V = 152064 bf16 batch (B = 256, gamma = 8) with top-k 50 and top-p 0.9: the
-    one-pass kernel at 20 units per thread, looping over 4352 vectors; drafts from the
+    """The V = 152064 bf16 batch (B = 256, gamma = 8) with top-k 50 and top-p 0.9: 4352
+    vectors, more than the select workgroups that fit at once; drafts from the
     drafter's 20 largest logits."""
     w = workloads.c4(draft_top_k=20)
     g, ref = parity(H, w, np.full(w.batch, 50, np.int32), np.full(w.batch, 0.9, np.float32), dense=True)
@@ -247,8 +247,7 @@ def test_bad_gamma(H):
 
 
 def test_many_vectors_mixed_rows(H):
-    """More vectors than workgroups, so each workgroup of the one-pass kernel takes
-    several in turn, with rows of every kind interleaved: top-k, top-p, both, neither,
+    """Many vectors with rows of every kind interleaved: top-k, top-p, both, neither,
     top-k 1, greedy (T = 0), a bad temperature and a NaN logit."""
     w = workloads.small(seed=91, batch=100, vocab=32000, dtype="bf16", gamma=4)
     T = w.temperature.copy()
@@ -259,6 +258,25 @@ def test_many_vectors_mixed_rows(H):
     w2 = workloads.Workload(**{**w.__dict__, "temperature": T, "target": tgt})
     g, ref = parity(H, w2, *filters(w2, seed=12))
     assert g["row_status"][5] & oracle.NONFINITE and g["row_status"][13] & oracle.BAD_TEMP
+
+
+@pytest.mark.parametrize("vocab,dtype", [(8192, "bf16"), (6001, "f32"), (4101, "bf16")])
+def test_more_vectors_than_resident_selects(H, vocab, dtype):
+    """More vectors (5100) than the select workgroups that fit on the device at once
+    (16 a CU), so the last ones start in a second round, on rows of every kind: top-k
+    from 1 to 300 (above 128 the per-wave bound does not apply and the select runs over
+    every unit key), top-p, both, neither, greedy (T = 0) and a bad temperature;
+    aligned and unaligned rows, bf16 and fp32."""
+    w = workloads.small(seed=94, batch=300, vocab=vocab, dtype=dtype, gamma=8)
+    T = w.temperature.copy()
+    T[11::17] = 0.0
+    T[5] = np.inf
+    w2 = workloads.Workload(**{**w.__dict__, "temperature": T})
+    assert 2 * w2.target.shape[0] - w2.batch > 16 * 256
+    k, p = filters(w2, seed=14)
+    k[3::20] = 300
+    k[8::20] = 65
+    parity(H, w2, k, p, dense=True)
 
 
 @pytest.mark.parametrize("vocab,dtype", [(50257, "bf16"), (32001, "f32"), (128257, "bf16")])
