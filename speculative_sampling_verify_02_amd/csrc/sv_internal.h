@@ -208,6 +208,9 @@ struct Params {
     // streaming pass: relative piece shares of the workgroups on each XCD (workgroup b
     // runs on XCD b mod 8); all zero: equal shares
     int32_t xcd_w[8];
+    // streaming pass: N / G and N % G (equal shares), 1 / W(G) (weighted shares)
+    int64_t share_q, share_r;
+    double share_inv;
     // top-k / top-p filtering of p and q
     const int32_t *top_k;     // [B] or null
     const float *top_p;       // [B] or null

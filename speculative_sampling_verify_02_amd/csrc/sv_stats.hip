@@ -22,11 +22,13 @@
 
 namespace sv {
 
-// Workgroup b owns pieces [b N / G, (b + 1) N / G) of the N pieces.  Its waves take
-// them in order from a counter in LDS (each wave's first piece is fixed), so a wave
-// the CU's arbiter serves less takes fewer pieces and the workgroup's waves finish
-// together; with one workgroup per CU the CUs finish together too.  UM: filtered
-// calls, which also store the maximum of every 64 consecutive logits (piece_finish).
+// Workgroup b owns pieces [b q + min(b, r), (b + 1) q + min(b + 1, r)) of the N
+// pieces, q = N / G and r = N % G (from the host: a division here would delay every
+// wave's first load by hundreds of scalar instructions).  Its waves take them in order
+// from a counter in LDS (each wave's first piece is fixed), so a wave the CU's arbiter
+// serves less takes fewer pieces and the workgroup's waves finish together; with one
+// workgroup per CU the CUs finish together too.  UM: filtered calls, which also store
+// the maximum of every 64 consecutive logits (piece_finish).
 template <int DT, bool AL, bool UM>
 __device__ __forceinline__ void stats_body(const Params &P)
 {
@@ -47,23 +49,26 @@ __device__ __forceinline__ void stats_body(const Params &P)
     int64_t p0, p1;
     if (P.xcd_w[0] > 0) {
         // weighted shares: workgroup b's share is w[b mod 8], its range starts at
-        // N W(b) / W(G) with W(b) the weights of the workgroups before it (exact in
-        // integers, so the ranges still cover every piece once)
-        int64_t wsum = 0, pre[9];
+        // floor(N W(b) / W(G)) with W(b) the weights of the workgroups before it (the
+        // rounding is monotone in W(b) and the last range ends at N, so the ranges
+        // still cover every piece once)
+        int32_t wsum = 0, pre[8];
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
             pre[x] = wsum;
             wsum += P.xcd_w[x];
         }
-        pre[8] = wsum;
-        auto W = [&](int64_t b) { return (b / 8) * wsum + pre[b % 8]; };
-        const int64_t wt = W(G);
-        auto start = [&](int64_t b) { const int64_t w = W(b); return (N / wt) * w + (N % wt) * w / wt; };
+        auto start = [&](int64_t b) -> int64_t {
+            if (b >= G) return N;
+            const double w = (double)((b >> 3) * (int64_t)wsum + pre[b & 7]);
+            return (int64_t)((double)N * w * P.share_inv);
+        };
         p0 = start(blockIdx.x);
         p1 = start((int64_t)blockIdx.x + 1);
     } else {
-        p0 = (int64_t)blockIdx.x * N / G;
-        p1 = ((int64_t)blockIdx.x + 1) * N / G;
+        const int64_t b = blockIdx.x;
+        p0 = b * P.share_q + (b < P.share_r ? b : P.share_r);
+        p1 = p0 + P.share_q + (b < P.share_r ? 1 : 0);
     }
     int64_t p = p0 + wave;
     if (p >= p1) return;
@@ -321,6 +326,17 @@ hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned,
 {
     Params Q = P;
     set_xcd_weights(Q, dtype);
+    const int64_t N = Q.geo.nitems, G = Q.geo.G > 0 ? Q.geo.G : 1;
+    Q.share_q = N / G;
+    Q.share_r = N % G;
+    if (Q.xcd_w[0] > 0) {
+        int64_t wsum = 0, pre[8];
+        for (int x = 0; x < 8; ++x) {
+            pre[x] = wsum;
+            wsum += Q.xcd_w[x];
+        }
+        Q.share_inv = 1.0 / (double)((G >> 3) * wsum + pre[G & 7]);
+    }
     return launch_timed(stats_fn(dtype, aligned, P.umax != nullptr), P.geo.G, stats_block(dtype, aligned), Q, s,
                         start, stop);
 }
