@@ -364,11 +364,13 @@ __device__ RowDraw scan_row(const Params &P, int32_t row, bool write, ScanLds &s
     return sh.D;
 }
 
-// Ragged batch whose gamma array is inconsistent: every row and slot is invalid.
+// Ragged batch whose gamma array is inconsistent: every row and slot is invalid (NT:
+// the workgroup's threads).
+template <int NT>
 __device__ void invalidate_call(const Params &P, int32_t row, bool row_writer)
 {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+    const int64_t gid = (int64_t)blockIdx.x * NT + threadIdx.x;
+    const int64_t nthreads = (int64_t)gridDim.x * NT;
     for (int64_t s = gid; s < P.nT; s += nthreads) P.emitted[s] = -1;
     for (int64_t s = gid; s < P.nD; s += nthreads) {
         if (P.p_x) P.p_x[s] = kQNaN;
@@ -396,8 +398,8 @@ __device__ void invalidate_call(const Params &P, int32_t row, bool row_writer)
 // steps decide.
 __global__ __launch_bounds__(kBlock) void ee_init_kernel(Params P)
 {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const int64_t nth = (int64_t)gridDim.x * kBlock;
     const bool bad_call = P.gamma != nullptr && P.hdr->status != 0;
     if (gid == 0) {
         const bool sample = P.mode == 0;
@@ -624,7 +626,7 @@ __device__ __forceinline__ void scan_body(const Params &P)
     __shared__ ScanLds sh;
     const int32_t row = (int32_t)blockIdx.x;
     if (P.gamma != nullptr && P.hdr->status != 0) {
-        invalidate_call(P, row, threadIdx.x == 0);
+        invalidate_call<kBlock>(P, row, threadIdx.x == 0);
         return;
     }
     scan_row<DT, kWaves, EE>(P, row, true, sh);
@@ -727,7 +729,7 @@ __device__ __forceinline__ void scan_tiles_body(const Params &P)
     const int32_t row = (int32_t)(blockIdx.x / S);
     const int32_t part = (int32_t)(blockIdx.x - (int64_t)row * S);
     if (P.gamma != nullptr && P.hdr->status != 0) {
-        invalidate_call(P, row, part == 0 && threadIdx.x == 0);
+        invalidate_call<kScanTileBlock>(P, row, part == 0 && threadIdx.x == 0);
         return;
     }
     const RowDraw D = scan_row<DT, kScanTileWaves, EE>(P, row, part == 0, sh);

@@ -29,7 +29,9 @@ namespace sv {
 // serves less takes fewer pieces and the workgroup's waves finish together; with one
 // workgroup per CU the CUs finish together too.  UM: filtered calls, which also store
 // the maximum of every 64 consecutive logits (piece_finish).
-template <int DT, bool AL, bool UM>
+// NT: the workgroup's threads (a constant: blockDim would be read from the dispatch
+// packet, a memory round trip before the first load).
+template <int DT, bool AL, bool UM, int NT>
 __device__ __forceinline__ void stats_body(const Params &P)
 {
     __shared__ uint32_t s_next;
@@ -37,15 +39,15 @@ __device__ __forceinline__ void stats_body(const Params &P)
     Exp2Tab tab{nullptr, 6};
     if constexpr (DT == 1) {
         __shared__ double s_tab[kTabLen * 64];
-        fill_exp2_tab(s_tab, 64);
+        fill_exp2_tab<NT>(s_tab, 64);
         tab.col = s_tab + lane;
     }
     if (threadIdx.x == 0) s_next = 0u;
     __syncthreads();
     if (P.gamma != nullptr && P.hdr->status != 0) return;
     const int64_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t nwb = blockDim.x >> 6;
-    const int64_t N = P.geo.nitems, G = gridDim.x;
+    constexpr int64_t nwb = NT / 64;
+    const int64_t N = P.geo.nitems, G = P.geo.G;   // (the grid)
     int64_t p0, p1;
     if (P.xcd_w[0] > 0) {
         // weighted shares: workgroup b's share is w[b mod 8], its range starts at
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(64) void stats_list_kernel(Params P)
     Exp2Tab tab{nullptr, 0};
     if constexpr (DT == 1) {   // one shared copy: 64 copies would limit the one-wave workgroups per CU
         __shared__ double s_tab[kTabLen];
-        fill_exp2_tab(s_tab, 1);
+        fill_exp2_tab<64>(s_tab, 1);
         __syncthreads();
         tab.col = s_tab;
     }
@@ -198,7 +200,7 @@ __global__ __launch_bounds__(64) void stats_list_kernel(Params P)
 template <int DT, bool UM>
 __global__ __launch_bounds__(kStatsBlock<DT>) void stats_kernel(Params P)
 {
-    stats_body<DT, true, UM>(P);
+    stats_body<DT, true, UM, kStatsBlock<DT>>(P);
 }
 
 // rows that do not start 16-byte aligned: aligned loads, realigned in registers; 12
@@ -207,7 +209,7 @@ template <int DT> constexpr int kStatsBlockUnaligned = DT == 0 ? 768 : 512;
 template <int DT, bool UM>
 __global__ __launch_bounds__(kStatsBlockUnaligned<DT>) void stats_kernel_unaligned(Params P)
 {
-    stats_body<DT, false, UM>(P);
+    stats_body<DT, false, UM, kStatsBlockUnaligned<DT>>(P);
 }
 
 // ===========================================================================

@@ -376,10 +376,12 @@ __host__ __device__ __forceinline__ double exp2_tab_entry(int j)
 }
 
 // Fill a table of 2^(j/L) for exp2_tab_read: kTabLen entries, each repeated `copies`
-// times (64: one column per lane; 1: a single copy).  The caller synchronises after it.
+// times (64: one column per lane; 1: a single copy), by a workgroup of NT threads.  The
+// caller synchronises after it.
+template <int NT>
 __device__ __forceinline__ void fill_exp2_tab(double *tab, int copies)
 {
-    for (int i = threadIdx.x; i < kTabLen * copies; i += blockDim.x) tab[i] = exp2_tab_entry(i / copies);
+    for (int i = threadIdx.x; i < kTabLen * copies; i += NT) tab[i] = exp2_tab_entry(i / copies);
 }
 
 // fp32 logits: the sums feed log2(S_t / S_d), which the residual mass of a draft close
