@@ -698,9 +698,9 @@ template <int DT, bool AL>
 __device__ __forceinline__ void verify_body(const Params &P)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t per_row = P.geo.ndraw;
+    const uint32_t per_row = (uint32_t)P.geo.ndraw;
     const int32_t row = (int32_t)(blockIdx.x / per_row);
-    const int32_t piece = (int32_t)(blockIdx.x - (int64_t)row * per_row);
+    const int32_t piece = (int32_t)(blockIdx.x - (uint32_t)row * per_row);
     const RowDraw D = P.draws[row];   // loaded together with the status word
     if (P.gamma != nullptr && P.hdr->status != 0) return;
     // bonus draws use the streaming pass's piece sums, except when p is filtered
@@ -725,9 +725,9 @@ __device__ __forceinline__ void scan_tiles_body(const Params &P)
 {
     __shared__ ScanLds sh;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t S = P.st_split;
+    const uint32_t S = (uint32_t)P.st_split;   // (32-bit: a 64-bit division costs ~100 instructions)
     const int32_t row = (int32_t)(blockIdx.x / S);
-    const int32_t part = (int32_t)(blockIdx.x - (int64_t)row * S);
+    const int32_t part = (int32_t)(blockIdx.x - (uint32_t)row * S);
     if (P.gamma != nullptr && P.hdr->status != 0) {
         invalidate_call<kScanTileBlock>(P, row, part == 0 && threadIdx.x == 0);
         return;
@@ -737,8 +737,8 @@ __device__ __forceinline__ void scan_tiles_body(const Params &P)
     if (!(D.kind == DRAW_RESIDUAL || (P.theta && D.kind == DRAW_BONUS))) return;
     DrawConst<DT> c;
     c.init(D);
-    const int64_t nt = P.geo.ntiles;
-    const int64_t a = nt * part / S, b = nt * (part + 1) / S;
+    const uint32_t nt = (uint32_t)P.geo.ntiles;   // (nt S < 2^32: 32-bit divisions)
+    const int64_t a = nt * (uint32_t)part / S, b = nt * (uint32_t)(part + 1) / S;
     for (int64_t t0 = a + (int64_t)wave * kScanTileBatch; t0 < b; t0 += (int64_t)kScanTileWaves * kScanTileBatch)
         tile_sums<DT, AL, kScanTileBatch>(P, c, D, row, t0, b, lane);
 }
@@ -919,19 +919,54 @@ __device__ __forceinline__ void draw_bonus_row(const Params &P, const RowDraw &D
     }
 }
 
-// The residual draw from the tile sums of the row's position K.
-template <int DT, bool AL>
-__device__ __forceinline__ void draw_residual_row(const Params &P, const RowDraw &D, int32_t row, int lane)
+// A lane's tile sums of the residual walk, R at a time with all R loads in flight
+// together (one round trip for vocabularies up to 64 R tiles); the lane holds the
+// contiguous tiles [l0, l1) of its row, and tiles past l1 read as 0.
+constexpr int kWalkChunk = 8;
+struct TileChunk {
+    double w[kWalkChunk], p[kWalkChunk];
+};
+
+__device__ __forceinline__ void walk_range(const Params &P, int lane, int &per, int &l0, int &l1)
 {
     const int32_t nt = P.geo.ntiles;
-    const Sum2 *tiles = P.tiles + (int64_t)row * nt;
-    const int per = (nt + 63) / 64;        // tiles per lane, contiguous
-    const int l0 = lane * per;
-    const int l1 = min(l0 + per, nt);
+    per = (nt + 63) / 64;
+    l0 = lane * per;
+    l1 = min(l0 + per, nt);
+}
+
+__device__ __forceinline__ void load_tile_chunk(const Sum2 *tiles, int c0, int l1, TileChunk &c)
+{
+#pragma unroll
+    for (int i = 0; i < kWalkChunk; ++i) {
+        const Sum2 x = c0 + i < l1 ? tiles[c0 + i] : Sum2{0.0, 0.0};
+        c.w[i] = x.w;
+        c.p[i] = x.p;
+    }
+}
+
+// The residual draw from the tile sums of the row's position K; `ch` holds the lane's
+// first chunk of them (load_tile_chunk at l0).
+template <int DT, bool AL>
+__device__ __forceinline__ void draw_residual_row(const Params &P, const RowDraw &D, int32_t row, int lane,
+                                                  TileChunk &ch)
+{
+    const Sum2 *tiles = P.tiles + (int64_t)row * P.geo.ntiles;
+    int per, l0, l1;
+    walk_range(P, lane, per, l0, l1);
+    constexpr int R = kWalkChunk;
+    double *rw = ch.w, *rp = ch.p;
 
     // total weight (residual, or p when the residual is empty)
     double lw = 0.0, lp = 0.0;
-    for (int t = l0; t < l1; ++t) { lw += tiles[t].w; lp += tiles[t].p; }
+    for (int c0 = l0; c0 < l1; c0 += R) {
+        if (c0 != l0) load_tile_chunk(tiles, c0, l1, ch);
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            lw += rw[i];
+            lp += rp[i];
+        }
+    }
     const double iw = wave_inclusive_sum(lw, lane), ip = wave_inclusive_sum(lp, lane);
     double W = __shfl(iw, 63);
     bool use_p = false;
@@ -943,11 +978,17 @@ __device__ __forceinline__ void draw_residual_row(const Params &P, const RowDraw
     double cum = use_p ? ip - lp : iw - lw;
     int cand = -1, lastpos = -1;
     double cand_before = 0.0, last_before = 0.0;
-    for (int k = l0; k < l1; ++k) {
-        const double v = use_p ? tiles[k].p : tiles[k].w;
-        if (cand < 0 && cum + v > t) { cand = k; cand_before = cum; }
-        if (v > 0.0) { lastpos = k; last_before = cum; }
-        cum += v;
+    for (int c0 = l0; c0 < l1; c0 += R) {
+        if (per > R) load_tile_chunk(tiles, c0, l1, ch);   // (else ch still holds the lane's tiles)
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int k = c0 + i;
+            if (k >= l1) break;
+            const double v = use_p ? rp[i] : rw[i];
+            if (cand < 0 && cum + v > t) { cand = k; cand_before = cum; }
+            if (v > 0.0) { lastpos = k; last_before = cum; }
+            cum += v;
+        }
     }
     int tile = -1;
     double before = 0.0;
@@ -1027,9 +1068,17 @@ __global__ __launch_bounds__(kBlock) void draw_final_kernel(Params P)
     __shared__ double s_ts[kPieceTiles<DT>];
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int32_t row = blockIdx.x;
+    // the residual walk's first tile sums need only the row: their loads overlap the
+    // draw record's (for rows that draw otherwise they go unused)
+    TileChunk ch;
+    if (wave == 0) {
+        int per, l0, l1;
+        walk_range(P, lane, per, l0, l1);
+        load_tile_chunk(P.tiles + (int64_t)row * P.geo.ntiles, l0, l1, ch);
+    }
     const RowDraw D = P.draws[row];
     if (D.kind == DRAW_RESIDUAL || (P.theta && D.kind == DRAW_BONUS)) {
-        if (wave == 0) draw_residual_row<DT, AL>(P, D, row, lane);
+        if (wave == 0) draw_residual_row<DT, AL>(P, D, row, lane, ch);
     } else if (D.kind == DRAW_BONUS) {
         draw_bonus_row<DT, AL>(P, D, row, lane, wave, s_ts);
     }
