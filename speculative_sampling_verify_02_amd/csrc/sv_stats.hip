@@ -31,7 +31,9 @@ namespace sv {
 // the maximum of every 64 consecutive logits (piece_finish).
 // NT: the workgroup's threads (a constant: blockDim would be read from the dispatch
 // packet, a memory round trip before the first load).
-template <int DT, bool AL, bool UM, int NT>
+constexpr int kKeyPieces = 1024;   // 128 KB of staged keys
+
+template <int DT, bool AL, bool UM, int NT, bool ST = false>
 __device__ __forceinline__ void stats_body(const Params &P)
 {
     __shared__ uint32_t s_next;
@@ -72,8 +74,23 @@ __device__ __forceinline__ void stats_body(const Params &P)
         p0 = b * P.share_q + (b < P.share_r ? b : P.share_r);
         p1 = p0 + P.share_q + (b < P.share_r ? 1 : 0);
     }
+    // long bf16 filtered passes stage the unit keys of the range's first kKeyPieces
+    // pieces in LDS and write them out at the end in one contiguous burst (keys written
+    // piece by piece, interleaved with the stream's reads, made the C4 pass ~12 %
+    // slower); a bit per piece marks those that have keys (rows that filter)
+    constexpr bool kStage = DT == 0 && UM && ST;
+    uint16_t *keys = nullptr;
+    uint32_t *kflag = nullptr;
+    if constexpr (kStage) {
+        __shared__ uint4 s_keys[kKeyPieces * kPieceUnits / 8];
+        __shared__ uint32_t s_kflag[kKeyPieces / 32];
+        keys = reinterpret_cast<uint16_t *>(s_keys);
+        kflag = s_kflag;
+        for (int i = threadIdx.x; i < kKeyPieces / 32; i += NT) s_kflag[i] = 0u;
+        __syncthreads();
+    }
     int64_t p = p0 + wave;
-    if (p >= p1) return;
+    if (p < p1) {
     auto grab = [&]() -> int64_t {
         uint32_t t = 0u;
         if (lane == 0) t = atomicAdd(&s_next, 1u);
@@ -116,11 +133,31 @@ __device__ __forceinline__ void stats_body(const Params &P)
         half_begin<DT, AL>(P, v, j, 1, live, rb, lane);
         const VecCtx vn = vec_ctx_uniform(P, live ? v : 0);
         const bool fn = UM && row_filters(P, vn.row);
-        piece_finish<DT, UM>(P, vc, rm, tc, cv, cj, acc, filt);
+        uint16_t *slot = nullptr;
+        if (kStage && keys) {
+            const int64_t r = cv * ipv + cj - p0;
+            if (filt && r < kKeyPieces) {
+                slot = keys + r * kPieceUnits;
+                if (lane == 0) atomicOr(&kflag[r >> 5], 1u << (r & 31));
+            }
+        }
+        piece_finish<DT, UM>(P, vc, rm, tc, cv, cj, acc, filt, slot);
         if (!live) break;
         vc = vn;
         filt = fn;
         pn = pnn;
+    }
+    }
+    if (kStage && keys) {
+        // the staged keys: 8 16-byte words per piece, to [p0, p0 + kKeyPieces) of umax
+        __syncthreads();
+        const int64_t n = (p1 - p0 < kKeyPieces ? p1 - p0 : kKeyPieces) * (kPieceUnits / 8);
+        uint4 *dst = reinterpret_cast<uint4 *>(P.umax + p0 * kPieceUnits);
+        const uint4 *src = reinterpret_cast<const uint4 *>(keys);
+        for (int64_t i = threadIdx.x; i < n; i += NT) {
+            const int64_t r = i / (kPieceUnits / 8);
+            if (kflag[r >> 5] & (1u << (r & 31))) dst[i] = src[i];
+        }
     }
 }
 
@@ -197,19 +234,19 @@ __global__ __launch_bounds__(64) void stats_list_kernel(Params P)
 }
 
 // 16-byte aligned rows (the usual case): one workgroup per CU, of 16 waves (bf16) or 12
-template <int DT, bool UM>
+template <int DT, bool UM, bool ST = false>
 __global__ __launch_bounds__(kStatsBlock<DT>) void stats_kernel(Params P)
 {
-    stats_body<DT, true, UM, kStatsBlock<DT>>(P);
+    stats_body<DT, true, UM, kStatsBlock<DT>, ST>(P);
 }
 
 // rows that do not start 16-byte aligned: aligned loads, realigned in registers; 12
 // waves per CU for bf16, 8 for fp32 (the realignment needs registers of its own)
 template <int DT> constexpr int kStatsBlockUnaligned = DT == 0 ? 768 : 512;
-template <int DT, bool UM>
+template <int DT, bool UM, bool ST = false>
 __global__ __launch_bounds__(kStatsBlockUnaligned<DT>) void stats_kernel_unaligned(Params P)
 {
-    stats_body<DT, false, UM, kStatsBlockUnaligned<DT>>(P);
+    stats_body<DT, false, UM, kStatsBlockUnaligned<DT>, ST>(P);
 }
 
 // ===========================================================================
@@ -229,8 +266,11 @@ static int stats_block(int dtype, bool aligned)
     return aligned ? kStatsBlock<1> : kStatsBlockUnaligned<1>;
 }
 
-static const void *stats_fn(int dtype, bool aligned, bool um = false)
+// um: filtered calls; stage: bf16 filtered calls whose unit keys are staged in LDS
+static const void *stats_fn(int dtype, bool aligned, bool um = false, bool stage = false)
 {
+    if (um && stage && dtype == 0)
+        return aligned ? (const void *)stats_kernel<0, true, true> : (const void *)stats_kernel_unaligned<0, true, true>;
     if (um)
         return dtype == 0
             ? (aligned ? (const void *)stats_kernel<0, true> : (const void *)stats_kernel_unaligned<0, true>)
@@ -328,6 +368,9 @@ hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned,
 {
     Params Q = P;
     set_xcd_weights(Q, dtype);
+    // bf16 filtered passes of 100 us or more stage the unit keys in LDS (C4: 226 ->
+    // 201 us; shorter passes keep the kernel that stores them piece by piece)
+    const bool stage = P.umax != nullptr && (double)P.geo.nitems * 2.0 * (double)kItemElems * 2.0 / 6.4e12 >= 100e-6;
     const int64_t N = Q.geo.nitems, G = Q.geo.G > 0 ? Q.geo.G : 1;
     Q.share_q = N / G;
     Q.share_r = N % G;
@@ -339,7 +382,7 @@ hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned,
         }
         Q.share_inv = 1.0 / (double)((G >> 3) * wsum + pre[G & 7]);
     }
-    return launch_timed(stats_fn(dtype, aligned, P.umax != nullptr), P.geo.G, stats_block(dtype, aligned), Q, s,
+    return launch_timed(stats_fn(dtype, aligned, P.umax != nullptr, stage), P.geo.G, stats_block(dtype, aligned), Q, s,
                         start, stop);
 }
 

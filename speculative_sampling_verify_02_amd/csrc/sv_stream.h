@@ -658,16 +658,23 @@ __device__ __forceinline__ Partial piece_record(const Params &P, const VecCtx &v
 // UM (filtered calls): a sampling row that filters also stores the maximum of each of
 // the piece's 64 units as a 16-bit key (unit_max_half), from which the threshold
 // search bounds the top-k.
+// lds_keys: where the piece's 64 keys go instead of memory (the workgroup writes them
+// out later), or null.
 template <int DT, bool UM = false>
 __device__ __forceinline__ void piece_finish(const Params &P, const VecCtx &vc, int32_t rm, const TempConst &tc,
-                                             int64_t v, int64_t j, PieceAcc<DT> &acc, bool filt = false)
+                                             int64_t v, int64_t j, PieceAcc<DT> &acc, bool filt = false,
+                                             uint16_t *lds_keys = nullptr)
 {
     const Partial rec = piece_record<DT>(P, vc, rm, tc, j, acc, UM && filt);
     const int lane = threadIdx.x & 63;
     if constexpr (UM) {
         constexpr int E = kE<DT>, G = 64 / E;
-        if (rm == ROW_SAMPLE && filt)
-            P.umax[(v * P.geo.ipv + j) * kPieceUnits + (lane % G) * E + lane / G] = unit_key(acc.um);
+        if (rm == ROW_SAMPLE && filt) {
+            const uint16_t key = unit_key(acc.um);
+            const int u = (lane % G) * E + lane / G;
+            if (lds_keys) lds_keys[u] = key;
+            else P.umax[(v * P.geo.ipv + j) * kPieceUnits + u] = key;
+        }
     }
     if (lane == 0) P.parts[v * P.geo.ipv + j] = rec;
 }

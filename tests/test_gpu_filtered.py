@@ -260,6 +260,17 @@ def test_many_vectors_mixed_rows(H):
     assert g["row_status"][5] & oracle.NONFINITE and g["row_status"][13] & oracle.BAD_TEMP
 
 
+@pytest.mark.parametrize("vocab", [152064, 152063])
+def test_long_pass_staged_keys(H, vocab):
+    """A bf16 pass long enough (82688 pieces) for the streaming kernel to keep the unit
+    keys of its pieces in LDS and write them out at the end, on rows of every kind
+    (top-k, top-p, both, neither, top-k 1), with 16-byte aligned rows and with rows
+    that are not (the kernel that realigns its loads)."""
+    w = workloads.small(seed=96, batch=128, vocab=vocab, dtype="bf16", gamma=8, n_boost=5)
+    assert (2 * w.target.shape[0] - w.batch) * ((vocab + 4095) // 4096) >= 78125
+    parity(H, w, *filters(w, seed=15), dense=True)
+
+
 @pytest.mark.parametrize("vocab,dtype", [(8192, "bf16"), (6001, "f32"), (4101, "bf16")])
 def test_more_vectors_than_resident_selects(H, vocab, dtype):
     """More vectors (5100) than the select workgroups that fit on the device at once
