@@ -74,10 +74,12 @@ __device__ __forceinline__ void stats_body(const Params &P)
         p0 = b * P.share_q + (b < P.share_r ? b : P.share_r);
         p1 = p0 + P.share_q + (b < P.share_r ? 1 : 0);
     }
-    // long bf16 filtered passes stage the unit keys of the range's first kKeyPieces
-    // pieces in LDS and write them out at the end in one contiguous burst (keys written
-    // piece by piece, interleaved with the stream's reads, made the C4 pass ~12 %
-    // slower); a bit per piece marks those that have keys (rows that filter)
+    // ST (long bf16 passes): what the pass writes besides its reads is staged in LDS
+    // and written out after the workgroup's last piece, in contiguous bursts, instead
+    // of piece by piece amid the stream's reads (which made C4's pass 3 % slower for
+    // the records, 12 % for the filtered calls' unit keys).  The unit keys of the
+    // range's first kKeyPieces pieces (a bit per piece marks those of rows that
+    // filter), and the records of its first kRecPieces pieces.
     constexpr bool kStage = DT == 0 && UM && ST;
     uint16_t *keys = nullptr;
     uint32_t *kflag = nullptr;
@@ -88,6 +90,13 @@ __device__ __forceinline__ void stats_body(const Params &P)
         kflag = s_kflag;
         for (int i = threadIdx.x; i < kKeyPieces / 32; i += NT) s_kflag[i] = 0u;
         __syncthreads();
+    }
+    constexpr bool kRecStage = DT == 0 && ST;
+    constexpr int64_t kRecPieces = kStage ? 1024 : 2048;   // 16 or 32 KB
+    Partial *recs = nullptr;
+    if constexpr (kRecStage) {
+        __shared__ Partial s_rec[kRecPieces];
+        recs = s_rec;
     }
     int64_t p = p0 + wave;
     if (p < p1) {
@@ -141,12 +150,22 @@ __device__ __forceinline__ void stats_body(const Params &P)
                 if (lane == 0) atomicOr(&kflag[r >> 5], 1u << (r & 31));
             }
         }
-        piece_finish<DT, UM>(P, vc, rm, tc, cv, cj, acc, filt, slot);
+        Partial *rslot = nullptr;
+        if constexpr (kRecStage) {
+            const int64_t r = cv * ipv + cj - p0;
+            if (r < kRecPieces) rslot = recs + r;
+        }
+        piece_finish<DT, UM>(P, vc, rm, tc, cv, cj, acc, filt, slot, rslot);
         if (!live) break;
         vc = vn;
         filt = fn;
         pn = pnn;
     }
+    }
+    if constexpr (kRecStage) {
+        __syncthreads();
+        const int64_t n = p1 - p0 < kRecPieces ? p1 - p0 : kRecPieces;
+        for (int64_t i = threadIdx.x; i < n; i += NT) P.parts[p0 + i] = recs[i];
     }
     if (kStage && keys) {
         // the staged keys: 8 16-byte words per piece, to [p0, p0 + kKeyPieces) of umax
@@ -266,11 +285,15 @@ static int stats_block(int dtype, bool aligned)
     return aligned ? kStatsBlock<1> : kStatsBlockUnaligned<1>;
 }
 
-// um: filtered calls; stage: bf16 filtered calls whose unit keys are staged in LDS
+// um: filtered calls; stage: long bf16 passes, which stage their writes in LDS
 static const void *stats_fn(int dtype, bool aligned, bool um = false, bool stage = false)
 {
-    if (um && stage && dtype == 0)
-        return aligned ? (const void *)stats_kernel<0, true, true> : (const void *)stats_kernel_unaligned<0, true, true>;
+    if (stage && dtype == 0) {
+        if (um)
+            return aligned ? (const void *)stats_kernel<0, true, true>
+                           : (const void *)stats_kernel_unaligned<0, true, true>;
+        return aligned ? (const void *)stats_kernel<0, false, true> : (const void *)stats_kernel_unaligned<0, false, true>;
+    }
     if (um)
         return dtype == 0
             ? (aligned ? (const void *)stats_kernel<0, true> : (const void *)stats_kernel_unaligned<0, true>)
@@ -368,9 +391,10 @@ hipError_t launch_stats(const Params &P, hipStream_t s, int dtype, bool aligned,
 {
     Params Q = P;
     set_xcd_weights(Q, dtype);
-    // bf16 filtered passes of 100 us or more stage the unit keys in LDS (C4: 226 ->
-    // 201 us; shorter passes keep the kernel that stores them piece by piece)
-    const bool stage = P.umax != nullptr && (double)P.geo.nitems * 2.0 * (double)kItemElems * 2.0 / 6.4e12 >= 100e-6;
+    // bf16 passes of 60 us or more (at 6.4 TB/s) stage their writes in LDS: C4 202.6 ->
+    // 197.1 us, filtered 226.6 -> 202.2 us; on C3 (~35 us) the end-of-pass barrier
+    // and burst cost 0.4 us, so shorter passes store piece by piece
+    const bool stage = (double)P.geo.nitems * 2.0 * (double)kItemElems * 2.0 / 6.4e12 >= 60e-6;
     const int64_t N = Q.geo.nitems, G = Q.geo.G > 0 ? Q.geo.G : 1;
     Q.share_q = N / G;
     Q.share_r = N % G;

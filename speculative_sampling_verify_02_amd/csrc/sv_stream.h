@@ -658,12 +658,12 @@ __device__ __forceinline__ Partial piece_record(const Params &P, const VecCtx &v
 // UM (filtered calls): a sampling row that filters also stores the maximum of each of
 // the piece's 64 units as a 16-bit key (unit_max_half), from which the threshold
 // search bounds the top-k.
-// lds_keys: where the piece's 64 keys go instead of memory (the workgroup writes them
-// out later), or null.
+// lds_keys, lds_rec: where the piece's 64 keys and its record go instead of memory
+// (the workgroup writes them out later), or null.
 template <int DT, bool UM = false>
 __device__ __forceinline__ void piece_finish(const Params &P, const VecCtx &vc, int32_t rm, const TempConst &tc,
                                              int64_t v, int64_t j, PieceAcc<DT> &acc, bool filt = false,
-                                             uint16_t *lds_keys = nullptr)
+                                             uint16_t *lds_keys = nullptr, Partial *lds_rec = nullptr)
 {
     const Partial rec = piece_record<DT>(P, vc, rm, tc, j, acc, UM && filt);
     const int lane = threadIdx.x & 63;
@@ -676,7 +676,10 @@ __device__ __forceinline__ void piece_finish(const Params &P, const VecCtx &vc, 
             else P.umax[(v * P.geo.ipv + j) * kPieceUnits + u] = key;
         }
     }
-    if (lane == 0) P.parts[v * P.geo.ipv + j] = rec;
+    if (lane == 0) {
+        if (lds_rec) *lds_rec = rec;
+        else P.parts[v * P.geo.ipv + j] = rec;
+    }
 }
 
 }  // namespace sv

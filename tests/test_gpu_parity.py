@@ -293,6 +293,17 @@ def test_c3_more_seeds(H, seed):
     _parity(H, workloads.c3(seed=seed), dense=True, assert_strict=True)
 
 
+def test_long_pass_staged_records(H):
+    """A bf16 pass long enough (51680 pieces) for the streaming kernel to keep its
+    records in LDS and write them out at the end, with rows that are not 16-byte
+    aligned (the kernel that realigns its loads) and greedy rows (T = 0, argmax
+    records) among the sampling rows."""
+    w = workloads.small(seed=97, batch=80, vocab=152063, dtype="bf16", gamma=8, n_boost=5,
+                        temperature=[0.0 if i % 7 == 3 else 0.9 for i in range(80)])
+    assert (2 * w.target.shape[0] - w.batch) * ((w.vocab + 4095) // 4096) * 8192 / 6.4e12 >= 60e-6
+    _parity(H, w, dense=True)
+
+
 def test_c4_second_seed(H):
     _parity(H, workloads.c4(seed=14), dense=True, assert_strict=True)
 
