@@ -464,9 +464,12 @@ __global__ __launch_bounds__(kEeWaves * 64) void ee_step_kernel(Params P)
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int buf = P.step & 1;
     if (P.gamma != nullptr && P.hdr->status != 0) return;
+    // the row id is read together with the count (slot < B, so in the list's buffer),
+    // one dependent read fewer before the row's own
     const int32_t slot = (int32_t)blockIdx.x;
-    if (slot >= P.ee_count[2 * buf]) return;
+    const int32_t listed = P.ee_count[2 * buf];
     const int32_t row = P.ee_rows[buf][slot];
+    if (slot >= listed) return;
     int status = P.ee_status[row];
     if (status & ST_BAD_GAMMA) return;   // invalid from the start, outputs already written
     const RowGeom G = row_geom(P, row);
