@@ -370,9 +370,11 @@ hipError_t launch_stats_list(const Params &P, hipStream_t s, int dtype, bool ali
 // the odd XCDs stream about 6.5 % slower than the even ones.  With equal shares the
 // pass ends with the odd XCDs while the even ones idle (C4: ~197 against ~184 us of
 // work).  Each XCD gets work in proportion to its rate times the time it has, T - s,
-// for a pass of T = the bytes at 6.4 TB/s.  Only passes of at least 150 us are
-// weighted: on C4 (~205 us) the pass took 1.6 % less time, while shorter ones (13-44 us:
-// greedy C3, the drafter's draw, the tree) took 1-7 % more time over the whole step.
+// for a pass of T = the bytes at 6.4 TB/s.  Only passes of at least 80 us are
+// weighted: C4's pass took 1.6 % less time (3.3 us with its records staged), the
+// drafter's draw of 2048 vectors (~100 us) 1.3 % less, while shorter ones (13-44 us:
+// greedy C3, the drafter's draw of 320 vectors, the tree) took 1-7 % more time over
+// the whole step.
 // The fp32 pass is bound by arithmetic and keeps equal shares.
 static void set_xcd_weights(Params &P, int dtype)
 {
@@ -380,7 +382,7 @@ static void set_xcd_weights(Params &P, int dtype)
     constexpr double kStart[8] = {0.12e-6, 0.25e-6, 1.57e-6, 2.06e-6, 2.5e-6, 2.6e-6, 2.5e-6, 2.5e-6};
     constexpr double kOddRate = 0.935;
     const double T = (double)P.geo.nitems * 2.0 * (double)kItemElems * 2.0 / 6.4e12;
-    if (T < 150e-6) return;
+    if (T < 80e-6) return;
     for (int x = 0; x < 8; ++x) {
         const double w = ((x & 1) ? kOddRate : 1.0) * std::max(T - kStart[x], 0.5 * T) / T;
         P.xcd_w[x] = (int32_t)(w * 4096.0 + 0.5);
