@@ -293,13 +293,15 @@ def test_c3_more_seeds(H, seed):
     _parity(H, workloads.c3(seed=seed), dense=True, assert_strict=True)
 
 
-def test_long_pass_staged_records(H):
-    """A bf16 pass long enough (51680 pieces) for the streaming kernel to keep its
+@pytest.mark.parametrize("vocab,dtype,batch", [(152063, "bf16", 80), (65537, "f32", 164)])
+def test_long_pass_staged_records(H, vocab, dtype, batch):
+    """A pass long enough (over 46875 pieces) for the bf16 streaming kernel to keep its
     records in LDS and write them out at the end, with rows that are not 16-byte
     aligned (the kernel that realigns its loads) and greedy rows (T = 0, argmax
-    records) among the sampling rows."""
-    w = workloads.small(seed=97, batch=80, vocab=152063, dtype="bf16", gamma=8, n_boost=5,
-                        temperature=[0.0 if i % 7 == 3 else 0.9 for i in range(80)])
+    records) among the sampling rows; and an fp32 pass of that length (bound by its
+    arithmetic, it stores its records piece by piece)."""
+    w = workloads.small(seed=97, batch=batch, vocab=vocab, dtype=dtype, gamma=8, n_boost=5 if dtype == "bf16" else 0,
+                        temperature=[0.0 if i % 7 == 3 else 0.9 for i in range(batch)])
     assert (2 * w.target.shape[0] - w.batch) * ((w.vocab + 4095) // 4096) * 8192 / 6.4e12 >= 60e-6
     _parity(H, w, dense=True)
 
