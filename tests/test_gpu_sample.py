@@ -128,6 +128,15 @@ def test_c3_draft_full():
     parity(workloads.sample_inputs(workloads.c3(), seed=3, side="draft"))
 
 
+def test_c4_draft_long_pass():
+    """1300 draft vectors of the V = 152064 bf16 batch: 49400 pieces, a pass long
+    enough for the streaming kernel to keep its records in LDS and write them out
+    after its last piece."""
+    si = workloads.sample_inputs(workloads.c4(), seed=4, side="draft", limit=1300)
+    assert si.n * ((si.vocab + 4095) // 4096) * 8192 / 6.4e12 >= 60e-6
+    parity(si)
+
+
 def test_c2_target_full():
     parity(workloads.sample_inputs(workloads.c2(), seed=2, side="target"))
 

@@ -135,3 +135,12 @@ def test_oversized_tree_is_rejected():
 def test_medusa_full():
     """16 Medusa trees of 63 nodes at V = 128256 bf16 (the measured workload)."""
     parity(workloads.trees(21, 16, 128256, "bf16", top_k=2, heads=5))
+
+
+def test_medusa_long_pass():
+    """24 Medusa trees of 63 nodes at V = 128256 bf16: 48384 pieces, a pass long enough
+    for the streaming kernel to keep its argmax records in LDS and write them out
+    after its last piece."""
+    tr = workloads.trees(22, 24, 128256, "bf16", top_k=2, heads=5)
+    assert tr.n_nodes * ((tr.vocab + 4095) // 4096) * 8192 / 6.4e12 >= 60e-6
+    parity(tr)
