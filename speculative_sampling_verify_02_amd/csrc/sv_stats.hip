@@ -1,12 +1,13 @@
 // The streaming pass of the speculative-sampling verification step for gfx950.
 //
 // Every logit of every target and draft vector is read exactly once.  The vectors
-// are cut into pieces of two 4 KB halves; one workgroup per CU owns a contiguous
-// range of pieces and its waves take them in order from a counter in LDS, each half
-// as four 16-byte loads per lane with the next half's loads in flight while one is
-// reduced.  Per piece a wave writes one record: the maximum and the sum of
-// 2^((z - m) c), c = log2(e)/T, over the piece (sampling rows) or the first argmax
-// (greedy rows).  The temperature softmax these summarize is the softened output of
+// are cut into pieces of two halves of 2048 logits; one workgroup per CU owns a
+// contiguous range of pieces and its waves take them in order from a counter in LDS,
+// each half as four (bf16) or eight (fp32) 16-byte loads per lane with the next
+// half's loads in flight while one is reduced.  Per piece a wave writes one record:
+// the maximum and the sum of 2^((z - m) c), c = log2(e)/T, over the piece (sampling
+// rows) or the first argmax (greedy rows); long bf16 passes collect the records (and
+// a filtered call's unit keys) in LDS and write them out after their last piece.  The temperature softmax these summarize is the softened output of
 // brunomaga.github.io "inference-distillation-speculative-decoding", section
 // "Knowledge distillation", with one T for both models (rayaq.ca "Speculative
 // decoding", section "Why the output is exactly the target's").  The wave also keeps
