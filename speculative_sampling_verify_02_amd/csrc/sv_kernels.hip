@@ -8,9 +8,12 @@
 // argmax in greedy mode (section "The greedy case"), writes the row's outputs and
 // what its draw needs.  After a rejection verify_kernel re-reads position K of the
 // row and sums the residual max(0, p - q) (step 4) per 512-logit tile, and
-// draw_final_kernel walks the tile sums and one tile to the inverse-CDF token.  The
-// bonus token (step 5) is drawn from p, whose sums per piece the streaming pass
-// already holds: draw_final_kernel walks those and re-reads one piece.
+// draw_final_kernel walks the tile sums and one tile to the inverse-CDF token.  For
+// bf16 sampling scan_tiles_kernel does the scan and the tile sums in one launch:
+// several workgroups per row each run the row's scan (the same arithmetic, so the
+// same K) and then sum their share of the row's tiles.  The bonus token (step 5) is
+// drawn from p, whose sums per piece the streaming pass already holds:
+// draw_final_kernel walks those and re-reads one piece.
 //
 // The draw's weights are fp32 from the hardware exp2 for both logit types (fp32
 // logits form the exponent in two parts to keep fp32-level accuracy), with fp64 sums
