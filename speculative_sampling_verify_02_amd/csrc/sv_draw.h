@@ -107,6 +107,7 @@ template <>
 struct DrawConst<0> {
     float c, mt, md, Ft, Fd, tht, thd;
     bool residual;
+    bool filt;   // a threshold applies (filtered call): logits below it drop out
 
     __device__ __forceinline__ void init(const RowDraw &D)
     {
@@ -118,16 +119,19 @@ struct DrawConst<0> {
         Ft = (float)(1.0 / D.S_t);
         md = D.m_d;
         Fd = residual ? (float)(1.0 / D.S_d) : 0.0f;
+        filt = tht > -INFINITY || thd > -INFINITY;
     }
     using W = float;
-    // weights of one unit: w (residual or p) and p
+    // weights of one unit: w (residual or p) and p; FILT false: no threshold applies
+    // (the comparisons skipped)
+    template <bool FILT = true>
     __device__ __forceinline__ void weights(const float *zt, const float *zd, float *w, float *p) const
     {
 #pragma unroll
         for (int e = 0; e < kUnitElems; ++e) {
             // logits below a filter's threshold drop out
-            const float zte = zt[e] < tht ? -INFINITY : zt[e];
-            const float zde = zd[e] < thd ? -INFINITY : zd[e];
+            const float zte = (FILT && zt[e] < tht) ? -INFINITY : zt[e];
+            const float zde = (FILT && zd[e] < thd) ? -INFINITY : zd[e];
             const float pe = hw_exp2((zte - mt) * c) * Ft;
             float we = pe;
             if (residual) we = fmaxf(0.0f, pe - hw_exp2((zde - md) * c) * Fd);

@@ -18,6 +18,8 @@
 // The draw's weights are fp32 from the hardware exp2 for both logit types (fp32
 // logits form the exponent in two parts to keep fp32-level accuracy), with fp64 sums
 // across lanes and tiles; the merges of the streaming pass's records are fp64.
+#include <type_traits>
+
 #include "sv_draw.h"
 
 namespace sv {
@@ -671,17 +673,40 @@ __device__ __forceinline__ void tile_sums(const Params &P, const DrawConst<DT> &
     // per-lane sums of every tile first, then one interleaved cross-lane reduction
     // (tiles past the end read -inf logits and sum to 0)
     double lw[NTW], lp[NTW];
+    if constexpr (DT == 0) {
+        // bf16: a lane's 8 weights of a tile summed in fp32 (relative error below
+        // 1e-6, against the 1e-5 W at which a draw counts as near), the comparisons
+        // with the thresholds only in filtered calls: the reduction is bound by its
+        // arithmetic once the loads are in
+        auto units = [&](auto filt) {
 #pragma unroll
-    for (int i = 0; i < NTW; ++i) {
-        float zt[kUnitElems], zd[kUnitElems];
-        unpack<DT>(rt[i], zt);
-        unpack<DT>(rd[i], zd);
-        typename DrawConst<DT>::W w[kUnitElems], p[kUnitElems];
-        c.weights(zt, zd, w, p);
-        lw[i] = 0.0;
-        lp[i] = 0.0;
+            for (int i = 0; i < NTW; ++i) {
+                float zt[kUnitElems], zd[kUnitElems], w[kUnitElems], p[kUnitElems];
+                unpack<DT>(rt[i], zt);
+                unpack<DT>(rd[i], zd);
+                c.template weights<decltype(filt)::value>(zt, zd, w, p);
+                float sw = 0.0f, sp = 0.0f;
 #pragma unroll
-        for (int e = 0; e < kUnitElems; ++e) { lw[i] += w[e]; lp[i] += p[e]; }
+                for (int e = 0; e < kUnitElems; ++e) { sw += w[e]; sp += p[e]; }
+                lw[i] = sw;
+                lp[i] = sp;
+            }
+        };
+        if (c.filt) units(std::true_type{});
+        else units(std::false_type{});
+    } else {
+#pragma unroll
+        for (int i = 0; i < NTW; ++i) {
+            float zt[kUnitElems], zd[kUnitElems];
+            unpack<DT>(rt[i], zt);
+            unpack<DT>(rd[i], zd);
+            typename DrawConst<DT>::W w[kUnitElems], p[kUnitElems];
+            c.weights(zt, zd, w, p);
+            lw[i] = 0.0;
+            lp[i] = 0.0;
+#pragma unroll
+            for (int e = 0; e < kUnitElems; ++e) { lw[i] += w[e]; lp[i] += p[e]; }
+        }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
