@@ -123,8 +123,9 @@ struct DrawConst<0> {
     }
     using W = float;
     // weights of one unit: w (residual or p) and p; FILT false: no threshold applies
-    // (the comparisons skipped)
-    template <bool FILT = true>
+    // (the comparisons skipped); RES 0 or 1 fixes the kind of draw at compile time (the
+    // draft's exponentials skipped, or taken without a branch), -1 reads it from the row
+    template <bool FILT = true, int RES = -1>
     __device__ __forceinline__ void weights(const float *zt, const float *zd, float *w, float *p) const
     {
 #pragma unroll
@@ -134,7 +135,7 @@ struct DrawConst<0> {
             const float zde = (FILT && zd[e] < thd) ? -INFINITY : zd[e];
             const float pe = hw_exp2((zte - mt) * c) * Ft;
             float we = pe;
-            if (residual) we = fmaxf(0.0f, pe - hw_exp2((zde - md) * c) * Fd);
+            if (RES == 1 || (RES < 0 && residual)) we = fmaxf(0.0f, pe - hw_exp2((zde - md) * c) * Fd);
             w[e] = we;
             p[e] = pe;
         }

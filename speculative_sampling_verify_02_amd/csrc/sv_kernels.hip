@@ -676,15 +676,16 @@ __device__ __forceinline__ void tile_sums(const Params &P, const DrawConst<DT> &
     if constexpr (DT == 0) {
         // bf16: a lane's 8 weights of a tile summed in fp32 (relative error below
         // 1e-6, against the 1e-5 W at which a draw counts as near), the comparisons
-        // with the thresholds only in filtered calls: the reduction is bound by its
-        // arithmetic once the loads are in
-        auto units = [&](auto filt) {
+        // with the thresholds only in filtered calls and the kind of draw fixed per
+        // variant (straight-line code): the reduction is bound by its arithmetic once
+        // the loads are in
+        auto units = [&](auto filt, auto res) {
 #pragma unroll
             for (int i = 0; i < NTW; ++i) {
                 float zt[kUnitElems], zd[kUnitElems], w[kUnitElems], p[kUnitElems];
                 unpack<DT>(rt[i], zt);
                 unpack<DT>(rd[i], zd);
-                c.template weights<decltype(filt)::value>(zt, zd, w, p);
+                c.template weights<decltype(filt)::value, decltype(res)::value>(zt, zd, w, p);
                 float sw = 0.0f, sp = 0.0f;
 #pragma unroll
                 for (int e = 0; e < kUnitElems; ++e) { sw += w[e]; sp += p[e]; }
@@ -692,8 +693,15 @@ __device__ __forceinline__ void tile_sums(const Params &P, const DrawConst<DT> &
                 lp[i] = sp;
             }
         };
-        if (c.filt) units(std::true_type{});
-        else units(std::false_type{});
+        using R0 = std::integral_constant<int, 0>;
+        using R1 = std::integral_constant<int, 1>;
+        if (c.filt) {
+            if (c.residual) units(std::true_type{}, R1{});
+            else units(std::true_type{}, R0{});
+        } else {
+            if (c.residual) units(std::false_type{}, R1{});
+            else units(std::false_type{}, R0{});
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < NTW; ++i) {
