@@ -106,6 +106,8 @@ struct DrawConst;
 template <>
 struct DrawConst<0> {
     float c, mt, md, Ft, Fd, tht, thd;
+    float r;       // S_t / S_d: q's weights 2^((z - m_d) c) on p's scale (residual draws)
+    double Ftd;    // 1 / S_t in fp64, the scale of unit_sums
     bool residual;
     bool filt;   // a threshold applies (filtered call): logits below it drop out
 
@@ -119,7 +121,29 @@ struct DrawConst<0> {
         Ft = (float)(1.0 / D.S_t);
         md = D.m_d;
         Fd = residual ? (float)(1.0 / D.S_d) : 0.0f;
+        r = residual ? (float)(D.S_t / D.S_d) : 0.0f;
+        Ftd = 1.0 / D.S_t;
         filt = tht > -INFINITY || thd > -INFINITY;
+    }
+    // A unit's sums of w and of p before the common factor 1 / S_t (Ftd): p's terms
+    // 2^((z_t - m_t) c), w's max(0, 2^((z_t - m_t) c) - r 2^((z_d - m_d) c)) for a
+    // residual draw, else p's.  Equal p and q (S_t = S_d, so r = 1) still cancel to 0.
+    template <bool FILT, int RES>
+    __device__ __forceinline__ void unit_sums(const float *zt, const float *zd, float &sw, float &sp) const
+    {
+        sw = 0.0f;
+        sp = 0.0f;
+#pragma unroll
+        for (int e = 0; e < kUnitElems; ++e) {
+            const float zte = (FILT && zt[e] < tht) ? -INFINITY : zt[e];
+            const float a = hw_exp2((zte - mt) * c);
+            sp += a;
+            if (RES) {
+                const float zde = (FILT && zd[e] < thd) ? -INFINITY : zd[e];
+                sw += fmaxf(0.0f, fmaf(-r, hw_exp2((zde - md) * c), a));
+            }
+        }
+        if (!RES) sw = sp;
     }
     using W = float;
     // weights of one unit: w (residual or p) and p; FILT false: no threshold applies

@@ -670,27 +670,27 @@ __device__ __forceinline__ void tile_sums(const Params &P, const DrawConst<DT> &
                                : neg_inf_unit<DT>();
         }
     }
-    // per-lane sums of every tile first, then one interleaved cross-lane reduction
+    // per-lane sums of every tile first, then one cross-lane reduction of all of them
     // (tiles past the end read -inf logits and sum to 0)
-    double lw[NTW], lp[NTW];
+    constexpr int NV = 2 * NTW;   // w and p of each tile: value 2 i + 1 is tile i's p
+    static_assert(NV >= 2 && NV <= 64 && (NV & (NV - 1)) == 0, "tile batch");
+    double v[NV];
+    double scale = 1.0;
     if constexpr (DT == 0) {
         // bf16: a lane's 8 weights of a tile summed in fp32 (relative error below
-        // 1e-6, against the 1e-5 W at which a draw counts as near), the comparisons
-        // with the thresholds only in filtered calls and the kind of draw fixed per
-        // variant (straight-line code): the reduction is bound by its arithmetic once
-        // the loads are in
+        // 1e-6, against the 1e-5 W at which a draw counts as near) without their
+        // common factor 1 / S_t, the comparisons with the thresholds only in filtered
+        // calls and the kind of draw fixed per variant (straight-line code): the
+        // reduction is bound by its arithmetic once the loads are in
         auto units = [&](auto filt, auto res) {
 #pragma unroll
             for (int i = 0; i < NTW; ++i) {
-                float zt[kUnitElems], zd[kUnitElems], w[kUnitElems], p[kUnitElems];
+                float zt[kUnitElems], zd[kUnitElems], sw, sp;
                 unpack<DT>(rt[i], zt);
                 unpack<DT>(rd[i], zd);
-                c.template weights<decltype(filt)::value, decltype(res)::value>(zt, zd, w, p);
-                float sw = 0.0f, sp = 0.0f;
-#pragma unroll
-                for (int e = 0; e < kUnitElems; ++e) { sw += w[e]; sp += p[e]; }
-                lw[i] = sw;
-                lp[i] = sp;
+                c.template unit_sums<decltype(filt)::value, decltype(res)::value>(zt, zd, sw, sp);
+                v[2 * i] = sw;
+                v[2 * i + 1] = sp;
             }
         };
         using R0 = std::integral_constant<int, 0>;
@@ -702,6 +702,7 @@ __device__ __forceinline__ void tile_sums(const Params &P, const DrawConst<DT> &
             if (c.residual) units(std::false_type{}, R1{});
             else units(std::false_type{}, R0{});
         }
+        scale = c.Ftd;
     } else {
 #pragma unroll
         for (int i = 0; i < NTW; ++i) {
@@ -710,24 +711,35 @@ __device__ __forceinline__ void tile_sums(const Params &P, const DrawConst<DT> &
             unpack<DT>(rd[i], zd);
             typename DrawConst<DT>::W w[kUnitElems], p[kUnitElems];
             c.weights(zt, zd, w, p);
-            lw[i] = 0.0;
-            lp[i] = 0.0;
+            v[2 * i] = 0.0;
+            v[2 * i + 1] = 0.0;
 #pragma unroll
-            for (int e = 0; e < kUnitElems; ++e) { lw[i] += w[e]; lp[i] += p[e]; }
+            for (int e = 0; e < kUnitElems; ++e) { v[2 * i] += w[e]; v[2 * i + 1] += p[e]; }
         }
     }
+    // Reduce-scatter over the wave: each exchange halves the values a lane holds (the
+    // lane whose bit o is set keeps the upper half and sends the lower), so after
+    // log2 NV exchanges lane l holds a partial sum of value l >> (6 - log2 NV); the
+    // remaining exchanges sum that one value over the lanes that share it.
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
+    for (int n = NV, o = 32; n > 1; n >>= 1, o >>= 1) {
+        const bool hi = (lane & o) != 0;
 #pragma unroll
-        for (int i = 0; i < NTW; ++i) {
-            lw[i] += __shfl_xor(lw[i], o);
-            lp[i] += __shfl_xor(lp[i], o);
+        for (int k = 0; k < n / 2; ++k) {
+            const double keep = hi ? v[k + n / 2] : v[k];
+            const double send = hi ? v[k] : v[k + n / 2];
+            v[k] = keep + __shfl_xor(send, o);
         }
     }
-    if (lane == 0) {
+    constexpr int kGroup = 64 / NV;   // lanes that hold one value
 #pragma unroll
-        for (int i = 0; i < NTW; ++i)
-            if (t0 + i < t_end) P.tiles[row * P.geo.ntiles + t0 + i] = Sum2{lw[i], lp[i]};
+    for (int o = kGroup / 2; o > 0; o >>= 1) v[0] += __shfl_xor(v[0], o);
+    if ((lane & (kGroup - 1)) == 0) {
+        const int idx = lane / kGroup, i = idx >> 1;
+        if (t0 + i < t_end) {
+            Sum2 *d = &P.tiles[row * P.geo.ntiles + t0 + i];
+            *((idx & 1) ? &d->p : &d->w) = v[0] * scale;
+        }
     }
 }
 
