@@ -188,10 +188,11 @@ def test_status_rules(H):
     assert not gg["row_status"][1] & oracle.INVALID_MASK
 
 
-def test_q_zero_and_zero_residual(H):
+@pytest.mark.parametrize("V,dtype", [(16, "f32"), (16, "bf16"), (5000, "f32"), (5000, "bf16")])
+def test_q_zero_and_zero_residual(H, V, dtype):
     """q(x) = 0 with p(x) > 0 keeps the draft (ratio 1); q(x) = p(x) = 0 with p = q
-    elsewhere rejects with zero residual mass and draws from p."""
-    V = 16
+    elsewhere rejects with zero residual mass and draws from p (over several tiles at
+    V = 5000: the residual's terms cancel to exactly 0 in every tile)."""
     z = np.zeros((2, V), np.float32)
     tgt1 = z.copy()
     drf1 = z[:1].copy()
@@ -200,8 +201,9 @@ def test_q_zero_and_zero_residual(H):
     tgt2[:, 9] = -np.inf
     drf2 = z[:1].copy()
     drf2[0, 9] = -np.inf
-    w = workloads.Workload("qzero", "f32", V, np.array([1, 1], np.int32), np.concatenate([tgt1, tgt2]),
-                           np.concatenate([drf1, drf2]), np.array([5, 9], np.int32),
+    store = (lambda a: workloads.to_bf16_bits(a)) if dtype == "bf16" else (lambda a: a)
+    w = workloads.Workload("qzero", dtype, V, np.array([1, 1], np.int32), store(np.concatenate([tgt1, tgt2])),
+                           store(np.concatenate([drf1, drf2])), np.array([5, 9], np.int32),
                            np.array([0.999, 0.3, 0.2, 0.55], np.float32), np.ones(2, np.float32))
     gpu, ref, rep = _parity(H, w)
     assert gpu["row_status"][0] == oracle.Q_ZERO and gpu["n_accepted"][0] == 1
