@@ -199,6 +199,7 @@ template <>
 struct DrawConst<1> {
     float ch, cl, ut, Bht, Blt, Mh, Ml, Lh, Ll, tht, thd;
     bool residual;
+    bool filt;   // a threshold applies (filtered call): logits below it drop out
 
     __device__ __forceinline__ static void split(double x, float &hi, float &lo)
     {
@@ -213,6 +214,7 @@ struct DrawConst<1> {
         ch = tc.c_hi;
         cl = tc.c_lo;
         residual = D.kind == DRAW_RESIDUAL;
+        filt = tht > -INFINITY || thd > -INFINITY;
         const double Lt = log2(D.S_t);
         double B = Lt;
         ut = D.m_t;
@@ -228,16 +230,19 @@ struct DrawConst<1> {
         }
     }
     using W = float;
+    // FILT false: no threshold applies (the comparisons skipped); RES 0 or 1 fixes the
+    // kind of draw at compile time, -1 reads it from the row
+    template <bool FILT = true, int RES = -1>
     __device__ __forceinline__ void weights(const float *zt, const float *zd, float *w, float *p) const
     {
 #pragma unroll
         for (int e = 0; e < kUnitElems; ++e) {
-            const float zte = zt[e] < tht ? -INFINITY : zt[e];
+            const float zte = (FILT && zt[e] < tht) ? -INFINITY : zt[e];
             const float xt = zte - ut;
             const float pe = hw_exp2(fmaf(xt, cl, fmaf(xt, ch, -Bht)) - Blt);
             float we = pe;
-            if (residual) {
-                const float zde = zd[e] < thd ? -INFINITY : zd[e];
+            if (RES == 1 || (RES < 0 && residual)) {
+                const float zde = (FILT && zd[e] < thd) ? -INFINITY : zd[e];
                 float dh, dl;
                 two_sum(zde, -zte, dh, dl);
                 const float g = (dh + Mh) + (dl + Ml);

@@ -675,48 +675,45 @@ __device__ __forceinline__ void tile_sums(const Params &P, const DrawConst<DT> &
     constexpr int NV = 2 * NTW;   // w and p of each tile: value 2 i + 1 is tile i's p
     static_assert(NV >= 2 && NV <= 64 && (NV & (NV - 1)) == 0, "tile batch");
     double v[NV];
-    double scale = 1.0;
-    if constexpr (DT == 0) {
-        // bf16: a lane's 8 weights of a tile summed in fp32 (relative error below
-        // 1e-6, against the 1e-5 W at which a draw counts as near) without their
-        // common factor 1 / S_t, the comparisons with the thresholds only in filtered
-        // calls and the kind of draw fixed per variant (straight-line code): the
-        // reduction is bound by its arithmetic once the loads are in
-        auto units = [&](auto filt, auto res) {
-#pragma unroll
-            for (int i = 0; i < NTW; ++i) {
-                float zt[kUnitElems], zd[kUnitElems], sw, sp;
-                unpack<DT>(rt[i], zt);
-                unpack<DT>(rd[i], zd);
-                c.template unit_sums<decltype(filt)::value, decltype(res)::value>(zt, zd, sw, sp);
-                v[2 * i] = sw;
-                v[2 * i + 1] = sp;
-            }
-        };
-        using R0 = std::integral_constant<int, 0>;
-        using R1 = std::integral_constant<int, 1>;
-        if (c.filt) {
-            if (c.residual) units(std::true_type{}, R1{});
-            else units(std::true_type{}, R0{});
-        } else {
-            if (c.residual) units(std::false_type{}, R1{});
-            else units(std::false_type{}, R0{});
-        }
-        scale = c.Ftd;
-    } else {
+    // A lane's 8 terms of a tile summed in fp32 (bf16: in order and without their
+    // common factor 1 / S_t, relative error at most 7 units of 2^-24; fp32 logits:
+    // pairwise, at most 3 units, within the 1e-6 to which their residual mass is
+    // held; both well below the 1e-5 W at which a draw counts as near), the
+    // comparisons with the thresholds only in filtered calls and the kind of draw
+    // fixed per variant (straight-line code): the reduction is bound by its
+    // arithmetic once the loads are in.
+    static_assert(kUnitElems == 8, "unit of 8 logits");
+    auto units = [&](auto filt, auto res) {
+        constexpr bool F = decltype(filt)::value;
+        constexpr int R = decltype(res)::value;
 #pragma unroll
         for (int i = 0; i < NTW; ++i) {
-            float zt[kUnitElems], zd[kUnitElems];
+            float zt[kUnitElems], zd[kUnitElems], sw, sp;
             unpack<DT>(rt[i], zt);
             unpack<DT>(rd[i], zd);
-            typename DrawConst<DT>::W w[kUnitElems], p[kUnitElems];
-            c.weights(zt, zd, w, p);
-            v[2 * i] = 0.0;
-            v[2 * i + 1] = 0.0;
-#pragma unroll
-            for (int e = 0; e < kUnitElems; ++e) { v[2 * i] += w[e]; v[2 * i + 1] += p[e]; }
+            if constexpr (DT == 0) {
+                c.template unit_sums<F, R>(zt, zd, sw, sp);
+            } else {
+                float w[kUnitElems], p[kUnitElems];
+                c.template weights<F, R>(zt, zd, w, p);
+                sw = ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
+                sp = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+            }
+            v[2 * i] = sw;
+            v[2 * i + 1] = sp;
         }
+    };
+    using R0 = std::integral_constant<int, 0>;
+    using R1 = std::integral_constant<int, 1>;
+    if (c.filt) {
+        if (c.residual) units(std::true_type{}, R1{});
+        else units(std::true_type{}, R0{});
+    } else {
+        if (c.residual) units(std::false_type{}, R1{});
+        else units(std::false_type{}, R0{});
     }
+    double scale = 1.0;
+    if constexpr (DT == 0) scale = c.Ftd;
     // Reduce-scatter over the wave: each exchange halves the values a lane holds (the
     // lane whose bit o is set keeps the upper half and sends the lower), so after
     // log2 NV exchanges lane l holds a partial sum of value l >> (6 - log2 NV); the
