@@ -177,27 +177,22 @@ __device__ __forceinline__ float one_minus_exp2(float y)
     return y > -0.5f ? -y * s : 1.0f - hw_exp2(y);
 }
 
-// The sum a + b as hi + lo exactly (Knuth's branch-free two-sum; finite inputs).
-__device__ __forceinline__ void two_sum(float a, float b, float &hi, float &lo)
-{
-    hi = a + b;
-    const float bb = hi - a;
-    lo = (a - (hi - bb)) + (b - bb);
-}
-
 // fp32 logits: fp32 weights from the hardware exp2, p = 2^(u c_hi + u c_lo - B) with the
 // vector's normalisation in the exponent: B = m c + log2 S held as two fp32 parts
 // (~2^-48 relative), so no per-vector factor is rounded to fp32.  When |fl(m c_hi)| <
 // 2^20, u = z; otherwise u = z - m, which is exact for every logit whose weight is not
 // 0 (it lies within a factor 2 of m), and B = log2 S.
 // The residual is taken as p (1 - 2^y) with y = log2(q/p) = ((z_d - z_t) + (m_t - m_d)) c
-// + log2(S_t / S_d), both differences carried exactly in two fp32 parts: y keeps its
-// relative accuracy where q is close to p (a difference p - q would keep only the
-// absolute accuracy of p and q), and it is exactly log2(S_t / S_d), 0 for equal sums,
-// wherever z_t - m_t = z_d - m_d, as for a distribution that keeps one token.
+// + log2(S_t / S_d) evaluated in fp64 (full rate on this GPU, fewer operations than
+// carrying the differences in two fp32 parts): y keeps its relative accuracy where q
+// is close to p (a difference p - q would keep only the absolute accuracy of p and q),
+// and it is exactly log2(S_t / S_d), 0 for equal sums, wherever z_t - m_t = z_d - m_d,
+// as for a distribution that keeps one token (both differences of fp32 values are
+// then exact in fp64 and cancel).
 template <>
 struct DrawConst<1> {
-    float ch, cl, ut, Bht, Blt, Mh, Ml, Lh, Ll, tht, thd;
+    float ch, cl, ut, Bht, Blt, tht, thd;
+    double c64, M64, L64;   // c, m_t - m_d (exact) and log2(S_t / S_d): the residual's y
     bool residual;
     bool filt;   // a threshold applies (filtered call): logits below it drop out
 
@@ -223,11 +218,9 @@ struct DrawConst<1> {
             B += (double)D.m_t * tc.c_eff;
         }
         split(B, Bht, Blt);
-        Mh = Ml = Lh = Ll = 0.0f;
-        if (residual) {
-            split((double)D.m_t - (double)D.m_d, Mh, Ml);   // exact: both are fp32
-            split(Lt - log2(D.S_d), Lh, Ll);
-        }
+        c64 = tc.c_eff;
+        M64 = residual ? (double)D.m_t - (double)D.m_d : 0.0;   // exact: both are fp32
+        L64 = residual ? Lt - log2(D.S_d) : 0.0;
     }
     using W = float;
     // FILT false: no threshold applies (the comparisons skipped); RES 0 or 1 fixes the
@@ -243,12 +236,11 @@ struct DrawConst<1> {
             float we = pe;
             if (RES == 1 || (RES < 0 && residual)) {
                 const float zde = (FILT && zd[e] < thd) ? -INFINITY : zd[e];
-                float dh, dl;
-                two_sum(zde, -zte, dh, dl);
-                const float g = (dh + Mh) + (dl + Ml);
-                const float y = fmaf(g, ch, Lh) + fmaf(g, cl, Ll);
-                // q = 0 keeps all of p; y >= 0 (q >= p) and NaN (p = 0) keep nothing
-                we = zde == -INFINITY ? pe : (y < 0.0f ? pe * one_minus_exp2(y) : 0.0f);
+                const float y = (float)fma(((double)zde - (double)zte) + M64, c64, L64);
+                // without a branch: q = 0 gives y = -inf and keeps all of p (1 - 2^-inf
+                // = 1); y >= 0 (q >= p) and NaN (p = q = 0) become y = 0 (minNum) and
+                // keep nothing
+                we = pe * one_minus_exp2(fminf(y, 0.0f));
             }
             w[e] = we;
             p[e] = pe;
