@@ -58,14 +58,25 @@ __global__ __launch_bounds__(1024) void prepare_kernel(Params P)
         const int64_t t_off = pt + it - vt, d_off = pd + id - vd;
         if (in) {
             P.rows[i] = RowInfo{(int32_t)t_off, (int32_t)d_off, g, 0};
-            // the row's vectors (bounds-checked: the totals are validated below)
+            // the row's vectors (bounds-checked: the totals are validated below), 8 at a
+            // time with their token loads issued together before the stores
             const float T = P.temperature[i];
-            for (int64_t k = 0; k <= g && t_off + k < P.nT; ++k) {
-                const bool has_x = k < g && d_off + k < P.nD;
-                const int32_t slot = has_x ? (int32_t)(d_off + k) : -1;
-                P.vinfo[t_off + k] = VecInfo{(int32_t)i, slot, has_x ? P.tokens[d_off + k] : -1, T};
-                if (P.mode == 0 && has_x)
-                    P.vinfo[P.nT + d_off + k] = VecInfo{(int32_t)i, slot, P.tokens[d_off + k], T};
+            for (int64_t k0 = 0; k0 <= g && t_off + k0 < P.nT; k0 += 8) {
+                int32_t x[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int64_t k = k0 + j;
+                    x[j] = (k < g && d_off + k < P.nD) ? P.tokens[d_off + k] : -1;
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int64_t k = k0 + j;
+                    if (k > g || t_off + k >= P.nT) break;
+                    const bool has_x = k < g && d_off + k < P.nD;
+                    const int32_t slot = has_x ? (int32_t)(d_off + k) : -1;
+                    P.vinfo[t_off + k] = VecInfo{(int32_t)i, slot, x[j], T};
+                    if (P.mode == 0 && has_x) P.vinfo[P.nT + d_off + k] = VecInfo{(int32_t)i, slot, x[j], T};
+                }
             }
         }
         __syncthreads();
